@@ -1,0 +1,87 @@
+"""Integer bookkeeping of the schedule path, written from its definitions
+(test infrastructure only).
+
+* Degree histogram: the input features the AutoSAGE page's scheduler reads
+  (Abstract: performance varies with degree skew and feature width).  Row i has
+  degree d_i = row_ptr[i+1] - row_ptr[i]; bucket 0 holds the empty rows and
+  bucket b >= 1 the rows with 2^(b-1) <= d_i < 2^b.  Per bucket: the number of
+  rows and the sum of their degrees; plus the maximum degree.
+
+* Merge-path partition: the nnz-balanced split of the work.  Walk the rows'
+  entries and the rows' ends as one merged sequence in which the end of row i
+  comes right after the row's last entry; chunk c owns the items
+  [c * D, (c + 1) * D) of that sequence.  Its start is the pair (x, y) = (row
+  ends, entries) that precede item c * D.
+
+* FNV-1a 64: the published Fowler-Noll-Vo hash (offset basis
+  0xcbf29ce484222325, prime 0x100000001b3; per byte: xor, then multiply).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+N_BUCKETS = 33
+
+
+def degree_histogram(row_ptr):
+    """Returns (counts int64[33], nnz int64[33], max_degree)."""
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    deg = rp[1:] - rp[:-1]
+    counts = np.zeros(N_BUCKETS, dtype=np.int64)
+    sums = np.zeros(N_BUCKETS, dtype=np.int64)
+    # bucket = number of powers of two 1, 2, 4, ... that are <= d (0 for d = 0)
+    b = np.zeros(len(deg), dtype=np.int64)
+    for k in range(N_BUCKETS - 1):
+        b += deg >= (1 << k)
+    counts = np.bincount(b, minlength=N_BUCKETS).astype(np.int64)
+    sums = np.bincount(b, weights=deg, minlength=N_BUCKETS).astype(np.int64)
+    mx = int(deg.max()) if len(deg) else 0
+    return counts, sums, mx
+
+
+def merge_path_partition(row_ptr, items_per_chunk: int):
+    """(x, y) int32 arrays of length n_chunks + 1.
+
+    x(d) = number of rows i whose end precedes item d, i.e. whose
+    (i + 1) + row_ptr[i + 1] <= d; y(d) = d - x(d).
+    """
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    n, nnz = len(rp) - 1, int(rp[-1])
+    total = n + nnz
+    n_chunks = max(1, -(-total // items_per_chunk))
+    d = np.minimum(np.arange(n_chunks + 1, dtype=np.int64) * items_per_chunk, total)
+    key = rp[1:] + np.arange(1, n + 1, dtype=np.int64)  # strictly increasing
+    x = np.searchsorted(key, d, side="right")
+    y = d - x
+    return x.astype(np.int32), y.astype(np.int32)
+
+
+def merge_path_bruteforce(row_ptr, items_per_chunk: int):
+    """Same partition by walking the merged sequence item by item (tiny inputs)."""
+    rp = [int(v) for v in row_ptr]
+    n, nnz = len(rp) - 1, rp[-1]
+    xs, ys = [0], [0]
+    x = y = 0
+    count = 0
+    while x < n or y < nnz:
+        if x < n and y >= rp[x + 1]:
+            x += 1  # every entry of row x has been consumed: its end comes next
+        else:
+            y += 1
+        count += 1
+        if count % items_per_chunk == 0:
+            xs.append(x)
+            ys.append(y)
+    if count % items_per_chunk or count == 0:
+        xs.append(x)
+        ys.append(y)
+    return np.array(xs, dtype=np.int32), np.array(ys, dtype=np.int32)
+
+
+def fnv1a64(data: bytes) -> int:
+    h = 0xCBF29CE484222325
+    for byte in data:
+        h ^= byte
+        h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h

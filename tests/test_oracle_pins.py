@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each check below follows from the definitions of the operations (AutoSAGE
+page, Abstract: CSR SpMM, CSR SDDMM and the attention pipeline SDDMM ->
+row-softmax -> SpMM; POPCORNBENCH trace page, task statement and kernels:
+softmax over each destination's incoming edge scores, zero output for a
+destination with no edge) or from mathematics, and none reuses the oracle's own
+code: dense matrix algebra with numpy/scipy, hand-worked values, closed forms
+and invariants.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.special import softmax as sp_softmax
+
+import oracle
+from synth import random_small_graph, to_bf16_bits, bf16_bits_to_f32
+from synth.graphs import CSR
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def dense_of(csr, vals):
+    """Dense matrix of a CSR pattern; duplicate entries add."""
+    A = np.zeros((csr.n_rows, csr.n_cols))
+    np.add.at(A, (csr.row_of_edge(), csr.col_idx.astype(np.int64)), vals)
+    return A
+
+
+def dense_attention(csr, scores, V, scale=1.0):
+    """Softmax attention written over the edge list: one column per stored
+    entry, masked rows -> 0, then a dense product."""
+    n, nnz = csr.n_rows, csr.nnz
+    rows = csr.row_of_edge()
+    S = np.full((n, nnz), -np.inf)
+    S[rows, np.arange(nnz)] = scale * np.asarray(scores, dtype=np.float64)
+    P = np.zeros_like(S)
+    live = csr.degrees() > 0
+    if live.any():
+        P[live] = sp_softmax(S[live], axis=1)
+    return P @ np.asarray(V, dtype=np.float64)[csr.col_idx], P[rows, np.arange(nnz)]
+
+
+def rel_err(a, b, mag):
+    mag = np.asarray(mag)
+    diff = np.abs(np.asarray(a) - np.asarray(b))
+    return float(np.max(diff / np.maximum(mag, 1e-300))) if diff.size else 0.0
+
+
+# --------------------------------------------------------------------------
+# hand-worked example
+# --------------------------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "worked_4node.json")) as f:
+        g = json.load(f)
+    csr = CSR(4, 4, np.array(g["row_ptr"], np.int32), np.array(g["col_idx"], np.int32))
+    return g, csr
+
+
+def test_golden_spmm(oracle_lib):
+    g, csr = _golden()
+    X = np.array(g["features"], np.float32)
+    Y, _ = oracle.spmm(csr.row_ptr, csr.col_idx, np.array(g["spmm"]["vals"], np.float32), X)
+    assert np.array_equal(Y, np.array(g["spmm"]["expected"], float))
+
+
+def test_golden_sddmm(oracle_lib):
+    g, csr = _golden()
+    out, _ = oracle.sddmm(csr.row_ptr, csr.col_idx, np.array(g["sddmm"]["U"], np.float32),
+                          np.array(g["sddmm"]["V"], np.float32))
+    assert np.array_equal(out, np.array(g["sddmm"]["expected"], float))
+
+
+def test_golden_attention(oracle_lib):
+    g, csr = _golden()
+    table = {"0": 0.0, "ln 2": np.log(2.0), "ln 3": np.log(3.0)}
+    sc = np.array([table.get(s, None) if s in table else float(s) for s in g["attention"]["scores"]],
+                  np.float32)
+    out, _, p = oracle.attention(csr.row_ptr, csr.col_idx, sc, np.array(g["features"], np.float32),
+                                 want_probs=True)
+    assert np.max(np.abs(out - np.array(g["attention"]["expected"]))) < 1e-6
+    assert np.max(np.abs(p - np.array(g["attention"]["expected_probs"]))) < 1e-6
+    assert out[2].tolist() == [0.0, 0.0]
+
+
+# --------------------------------------------------------------------------
+# dense brute force on random small graphs
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_spmm_dense_bruteforce(oracle_lib, seed):
+    rng = np.random.default_rng(seed)
+    n, m, F = int(rng.integers(1, 60)), int(rng.integers(1, 70)), int(rng.integers(1, 20))
+    csr = random_small_graph(n, m, rng.random() * 0.4, rng, empty_frac=0.2, allow_dup=True)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((m, F)).astype(np.float32)
+    Y, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X)
+    ref = dense_of(csr, vals) @ X.astype(np.float64)
+    refmag = dense_of(csr, np.abs(vals)) @ np.abs(X.astype(np.float64))
+    assert np.allclose(Y, ref, rtol=0, atol=1e-12 * max(1.0, refmag.max()))
+    assert np.allclose(mag, refmag, rtol=1e-13, atol=0)
+    # missing values mean a_e = 1
+    Y1, _ = oracle.spmm(csr.row_ptr, csr.col_idx, None, X)
+    assert np.allclose(Y1, dense_of(csr, np.ones(csr.nnz)) @ X, atol=1e-12 * max(1, np.abs(X).sum()))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sddmm_dense_bruteforce(oracle_lib, seed):
+    rng = np.random.default_rng(100 + seed)
+    n, m, K = int(rng.integers(1, 60)), int(rng.integers(1, 70)), int(rng.integers(1, 40))
+    csr = random_small_graph(n, m, rng.random() * 0.4, rng, empty_frac=0.2, allow_dup=True)
+    U = rng.standard_normal((n, K)).astype(np.float32)
+    V = rng.standard_normal((m, K)).astype(np.float32)
+    out, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V)
+    full = U.astype(np.float64) @ V.astype(np.float64).T
+    assert np.allclose(out, full[csr.row_of_edge(), csr.col_idx], rtol=0, atol=1e-12 * K)
+    fullmag = np.abs(U.astype(np.float64)) @ np.abs(V.astype(np.float64)).T
+    assert np.allclose(mag, fullmag[csr.row_of_edge(), csr.col_idx], rtol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attention_dense_bruteforce(oracle_lib, seed):
+    rng = np.random.default_rng(200 + seed)
+    n, m, F = int(rng.integers(1, 60)), int(rng.integers(1, 70)), int(rng.integers(1, 20))
+    csr = random_small_graph(n, m, rng.random() * 0.5, rng, empty_frac=0.25, allow_dup=seed % 2 == 1)
+    scores = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    V = rng.standard_normal((m, F)).astype(np.float32)
+    scale = [1.0, 0.125, 2.5][seed % 3]
+    out, mag, p = oracle.attention(csr.row_ptr, csr.col_idx, scores, V, scale, want_probs=True)
+    ref, refp = dense_attention(csr, scores, V, scale)
+    assert np.allclose(out, ref, rtol=0, atol=1e-13)
+    assert np.allclose(p, refp, rtol=0, atol=1e-14)
+
+
+def _bf16(rng, shape):
+    return to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_mha_dense_bruteforce(oracle_lib, seed):
+    rng = np.random.default_rng(300 + seed)
+    n, H, D = int(rng.integers(1, 40)), int(rng.integers(1, 5)), int(rng.integers(1, 17))
+    csr = random_small_graph(n, n, rng.random() * 0.5, rng, empty_frac=0.2)
+    Q, K, Vb = _bf16(rng, (n, H, D)), _bf16(rng, (n, H, D)), _bf16(rng, (n, H, D))
+    scale = 1.0 / np.sqrt(D)
+    out, mag, p = oracle.mha(csr.row_ptr, csr.col_idx, Q, K, Vb, scale, want_probs=True)
+    Qf, Kf, Vf = (bf16_bits_to_f32(a).astype(np.float64) for a in (Q, K, Vb))
+    for h in range(H):
+        S = Qf[:, h, :] @ Kf[:, h, :].T  # dense scores, then sampled on the pattern
+        sc = S[csr.row_of_edge(), csr.col_idx]
+        ref, refp = dense_attention(csr, sc, Vf[:, h, :], scale)
+        assert np.allclose(out[:, h, :], ref, rtol=0, atol=1e-12)
+        assert np.allclose(p[:, h], refp, rtol=0, atol=1e-13)
+
+
+def test_exhaustive_3x3_patterns(oracle_lib):
+    """Every one of the 512 patterns of a 3 x 3 matrix."""
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((3, 4)).astype(np.float32)
+    U = rng.standard_normal((3, 4)).astype(np.float32)
+    for mask in range(512):
+        M = np.array([(mask >> k) & 1 for k in range(9)], bool).reshape(3, 3)
+        rows, cols = np.nonzero(M)
+        rp = np.zeros(4, np.int32)
+        np.cumsum(M.sum(1), out=rp[1:])
+        csr = CSR(3, 3, rp, cols.astype(np.int32))
+        vals = rng.standard_normal(len(rows)).astype(np.float32)
+        sc = rng.standard_normal(len(rows)).astype(np.float32)
+        Y, _ = oracle.spmm(rp, csr.col_idx, vals, X)
+        assert np.allclose(Y, dense_of(csr, vals) @ X, atol=1e-12)
+        out, _ = oracle.sddmm(rp, csr.col_idx, U, X)
+        assert np.allclose(out, (U.astype(float) @ X.astype(float).T)[rows, cols], atol=1e-12)
+        att, _, _ = oracle.attention(rp, csr.col_idx, sc, X)
+        ref, _ = dense_attention(csr, sc, X)
+        assert np.allclose(att, ref, atol=1e-13)
+        for r in range(3):
+            if not M[r].any():
+                assert att[r].tolist() == [0.0] * 4 and Y[r].tolist() == [0.0] * 4
+
+
+# --------------------------------------------------------------------------
+# special cases and closed forms
+# --------------------------------------------------------------------------
+
+def _full_pattern(n, m):
+    rp = (np.arange(n + 1) * m).astype(np.int32)
+    return CSR(n, m, rp, np.tile(np.arange(m, dtype=np.int32), n))
+
+
+def test_full_pattern_is_dense_softmax_attention(oracle_lib):
+    rng = np.random.default_rng(11)
+    n, m, F = 17, 23, 9
+    csr = _full_pattern(n, m)
+    S = rng.standard_normal((n, m)).astype(np.float32)
+    V = rng.standard_normal((m, F)).astype(np.float32)
+    out, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, S.ravel(), V, scale=0.5)
+    ref = sp_softmax(0.5 * S.astype(np.float64), axis=1) @ V.astype(np.float64)
+    assert np.allclose(out, ref, rtol=0, atol=1e-13)
+    Y, _ = oracle.spmm(csr.row_ptr, csr.col_idx, S.ravel(), V)
+    assert np.allclose(Y, S.astype(np.float64) @ V.astype(np.float64), atol=1e-12)
+
+
+def test_identity_pattern_exact(oracle_lib):
+    rng = np.random.default_rng(12)
+    n, F = 50, 7
+    csr = CSR(n, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32))
+    V = rng.standard_normal((n, F)).astype(np.float32)
+    sc = rng.standard_normal(n).astype(np.float32) * 30
+    out, _, p = oracle.attention(csr.row_ptr, csr.col_idx, sc, V, want_probs=True)
+    assert np.array_equal(out, V.astype(np.float64))
+    assert np.array_equal(p, np.ones(n))
+    Y, _ = oracle.spmm(csr.row_ptr, csr.col_idx, None, V)
+    assert np.array_equal(Y, V.astype(np.float64))
+
+
+def test_empty_rows_are_positive_zero(oracle_lib):
+    rng = np.random.default_rng(13)
+    csr = random_small_graph(40, 40, 0.2, rng, empty_frac=0.5)
+    V = rng.standard_normal((40, 5)).astype(np.float32)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    out, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V)
+    Y, _ = oracle.spmm(csr.row_ptr, csr.col_idx, sc, V)
+    empty = csr.degrees() == 0
+    assert empty.any()
+    for arr in (out, mag, Y):
+        assert np.all(arr[empty] == 0) and not np.signbit(arr[empty]).any()
+
+
+def test_uniform_scores_give_neighbour_mean(oracle_lib):
+    rng = np.random.default_rng(14)
+    csr = random_small_graph(60, 80, 0.15, rng, empty_frac=0.1)
+    V = rng.standard_normal((80, 6)).astype(np.float32)
+    sc = np.repeat(rng.standard_normal(60).astype(np.float32) * 5, csr.degrees())
+    out, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V)
+    for i in range(60):
+        cols = csr.col_idx[csr.row_ptr[i]:csr.row_ptr[i + 1]]
+        want = V[cols].astype(np.float64).mean(0) if len(cols) else np.zeros(6)
+        assert np.allclose(out[i], want, atol=1e-14)
+
+
+def test_constant_values(oracle_lib):
+    rng = np.random.default_rng(15)
+    csr = random_small_graph(60, 80, 0.2, rng, empty_frac=0.1)
+    c = np.float32(-1.75)
+    V = np.full((80, 3), c, np.float32)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    out, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V)
+    live = csr.degrees() > 0
+    assert np.allclose(out[live], c, atol=1e-14)
+    # mean aggregation (values 1/deg) of a constant feature gives the constant
+    inv = np.repeat(1.0 / np.maximum(csr.degrees(), 1), csr.degrees())
+    Y, _ = oracle.spmm(csr.row_ptr, csr.col_idx, inv.astype(np.float32), V)
+    assert np.allclose(Y[live], c, rtol=1e-6)
+
+
+def test_softmax_rows_sum_to_one(oracle_lib):
+    rng = np.random.default_rng(16)
+    csr = random_small_graph(100, 100, 0.3, rng, empty_frac=0.1)
+    sc = (10 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    _, _, p = oracle.attention(csr.row_ptr, csr.col_idx, sc, np.ones((100, 1), np.float32),
+                               want_probs=True)
+    sums = np.add.reduceat(p, csr.row_ptr[:-1][csr.degrees() > 0])
+    assert np.allclose(sums, 1.0, rtol=0, atol=1e-15 * 100)
+    assert (p > 0).all() and (p <= 1).all()
+
+
+def test_shift_invariance_and_overflow(oracle_lib):
+    """Adding a constant to every score of a row leaves its output unchanged;
+    with a shift of 1000 the exponentials would overflow without subtracting
+    the row maximum.  Scores are multiples of 2^-10 so the shifted fp32 values
+    are exact."""
+    rng = np.random.default_rng(17)
+    csr = random_small_graph(50, 60, 0.3, rng, empty_frac=0.1)
+    base = (np.round(rng.standard_normal(csr.nnz) * 1024) / 1024).astype(np.float32)
+    V = rng.standard_normal((60, 4)).astype(np.float32)
+    shift = np.repeat(rng.choice([-1000.0, 80.0, 0.0, 1000.0], 50), csr.degrees()).astype(np.float32)
+    a, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, base, V)
+    b, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, base + shift, V)
+    assert np.all(np.isfinite(b))
+    assert np.array_equal(a, b)
+
+
+def test_hard_attention_limit(oracle_lib):
+    rng = np.random.default_rng(18)
+    csr = random_small_graph(60, 60, 0.3, rng, empty_frac=0.0)
+    V = rng.standard_normal((60, 5)).astype(np.float32)
+    # a unique maximum per row, at least 0.05 above every other score
+    sc = np.empty(csr.nnz, np.float32)
+    for i in range(60):
+        b, e = csr.row_ptr[i], csr.row_ptr[i + 1]
+        k = e - b
+        if k:
+            s = rng.permutation(k).astype(np.float32) * 0.05
+            sc[b:e] = s
+    out, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V, scale=1000.0)
+    for i in range(60):
+        b, e = csr.row_ptr[i], csr.row_ptr[i + 1]
+        if e > b:
+            j = csr.col_idx[b + int(np.argmax(sc[b:e]))]
+            assert np.allclose(out[i], V[j], atol=1e-6)
+
+
+def test_spmm_linearity(oracle_lib):
+    rng = np.random.default_rng(19)
+    csr = random_small_graph(40, 50, 0.3, rng)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.integers(-8, 8, (50, 6)).astype(np.float32)
+    Z = rng.integers(-8, 8, (50, 6)).astype(np.float32)
+    a, b = 3.0, -0.5  # small integers and halves keep every sum exact-ish
+    lhs, _ = oracle.spmm(csr.row_ptr, csr.col_idx, vals, (a * X + b * Z).astype(np.float32))
+    rx, _ = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X)
+    rz, _ = oracle.spmm(csr.row_ptr, csr.col_idx, vals, Z)
+    assert np.allclose(lhs, a * rx + b * rz, atol=1e-12)
+
+
+def test_sddmm_spmm_duality(oracle_lib):
+    """sum_e <U_row(e), V_col(e)> = sum_i <U_i, (A1 V)_i>, A1 the 0/1 pattern."""
+    rng = np.random.default_rng(20)
+    csr = random_small_graph(45, 55, 0.3, rng, empty_frac=0.1)
+    U = rng.standard_normal((45, 8)).astype(np.float32)
+    V = rng.standard_normal((55, 8)).astype(np.float32)
+    out, _ = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V)
+    Y, _ = oracle.spmm(csr.row_ptr, csr.col_idx, None, V)
+    assert np.isclose(out.sum(), np.sum(U.astype(np.float64) * Y), rtol=1e-12)
+
+
+def test_relabeling_equivariance(oracle_lib):
+    rng = np.random.default_rng(21)
+    n = 50
+    csr = random_small_graph(n, n, 0.2, rng, empty_frac=0.1)
+    V = rng.standard_normal((n, 4)).astype(np.float32)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    perm = rng.permutation(n)  # new id of old node i is perm[i]
+    inv = np.argsort(perm)
+    rows = csr.row_of_edge()
+    new_rows, new_cols = perm[rows], perm[csr.col_idx]
+    order = np.lexsort((new_cols, new_rows))
+    rp = np.zeros(n + 1, np.int32)
+    np.cumsum(np.bincount(new_rows, minlength=n), out=rp[1:])
+    V2 = V[inv]
+    out, _, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V)
+    out2, _, _ = oracle.attention(rp, new_cols[order].astype(np.int32), sc[order], V2)
+    assert np.allclose(out2[perm], out, atol=1e-14)
+
+
+def test_thread_count_does_not_change_results(oracle_lib):
+    rng = np.random.default_rng(22)
+    csr = random_small_graph(300, 200, 0.1, rng, empty_frac=0.2)
+    V = rng.standard_normal((200, 5)).astype(np.float32)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    a = oracle.attention(csr.row_ptr, csr.col_idx, sc, V, threads=1)[0]
+    b = oracle.attention(csr.row_ptr, csr.col_idx, sc, V, threads=7)[0]
+    assert np.array_equal(a, b)
+    c = oracle.spmm(csr.row_ptr, csr.col_idx, sc, V, r0=100, r1=250, threads=3)[0]
+    assert np.array_equal(c, oracle.spmm(csr.row_ptr, csr.col_idx, sc, V)[0][100:250])
+
+
+# --------------------------------------------------------------------------
+# integer bookkeeping
+# --------------------------------------------------------------------------
+
+def test_fnv1a64_published_vectors():
+    assert oracle.fnv1a64(b"") == 0xCBF29CE484222325
+    assert oracle.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert oracle.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_degree_histogram_bruteforce(seed):
+    rng = np.random.default_rng(400 + seed)
+    deg = rng.integers(0, 3000, size=500) * (rng.random(500) < 0.8)
+    deg[:4] = [0, 1, 2**11, 2**11 - 1]
+    rp = np.zeros(501, np.int64)
+    np.cumsum(deg, out=rp[1:])
+    counts, sums, mx = oracle.degree_histogram(rp)
+    c2, s2 = [0] * 33, [0] * 33
+    for d in deg.tolist():
+        b = int(d).bit_length()  # 0 for d = 0, else floor(log2 d) + 1
+        c2[b] += 1
+        s2[b] += int(d)
+    assert counts.tolist() == c2 and sums.tolist() == s2 and mx == int(deg.max())
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_merge_path_counting_equals_walk(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(0, 60))
+    deg = rng.integers(0, 12, size=n) * (rng.random(n) < 0.7)
+    rp = np.zeros(n + 1, np.int32)
+    np.cumsum(deg, out=rp[1:])
+    for D in (1, 2, 3, 7, 16, 64, 1000):
+        x, y = oracle.merge_path_partition(rp, D)
+        bx, by = oracle.merge_path_bruteforce(rp, D)
+        assert x.tolist() == bx.tolist() and y.tolist() == by.tolist()
+        # every chunk holds exactly D items except the last
+        items = (x[1:] + y[1:]) - (x[:-1] + y[:-1])
+        assert (items[:-1] == D).all() and 0 <= items[-1] <= D
