@@ -1,0 +1,38 @@
+"""MI355X-native CSR sparse aggregation: SpMM, SDDMM and fused CSR softmax
+attention with an input-aware schedule selector and a persistent cache.
+
+The computation lives in ``libcsrsa.so`` (hand-written HIP kernels for gfx950
+behind the C ABI of ``include/csrsa.h``); this package is a thin ctypes
+binding over it and raises ImportError when the library has not been built.
+"""
+
+from ._ffi import (  # noqa: F401
+    CsrError,
+    CsrProblem,
+    CsrSchedule,
+    EXPORTS,
+    LIB_PATH,
+    MAP_MERGEPATH,
+    MAP_ROWGROUP,
+    CTX_NO_PROBE,
+    CTX_VALIDATE,
+    load as load_library,
+)
+
+load_library()
+
+from .ops import (  # noqa: E402,F401
+    Context,
+    attention,
+    default_context,
+    default_schedule,
+    degree_histogram,
+    make_problem,
+    merge_path_partition,
+    mha_attention,
+    sddmm,
+    select,
+    signature,
+    spmm,
+    workspace_size,
+)

@@ -1,0 +1,692 @@
+// C ABI of the library (declared in include/csrsa.h): contexts, argument
+// checks, schedule execution, the auto-select path (degree histogram,
+// signature, cache, cost model, micro-probes, guarded fallback) and the
+// persistent cache log.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/csrsa.h"
+#include "host.h"
+#include "launch.h"
+
+struct CacheEntry {
+    csr_schedule_t sched;
+    double probe_us;
+    bool persisted;
+};
+
+struct csr_context_s {
+    std::mutex mu;
+    int device = -1;  // -1: host-only context (cache and host logic only)
+    csrh::DeviceInfo dev;
+    uint32_t flags = 0;
+    std::string cache_path;
+    std::map<uint64_t, CacheEntry> cache;
+    int64_t skipped_lines = 0;
+    int64_t io_errors = 0;
+    int64_t* pinned = nullptr;  // 4 KiB pinned host buffer
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    std::string last_error;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (dev < 0) return;
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev) {
+            changed = hipSetDevice(dev) == hipSuccess;
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+int set_err(csr_context_t ctx, int code, const std::string& msg)
+{
+    if (ctx) ctx->last_error = msg;
+    return code;
+}
+
+int hip_err(csr_context_t ctx, hipError_t e, const char* what)
+{
+    return set_err(ctx, CSR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define CSR_HIP(ctx, call)                                   \
+    do {                                                     \
+        hipError_t e_ = (call);                              \
+        if (e_ != hipSuccess) return hip_err(ctx, e_, #call); \
+    } while (0)
+
+// Appends one line; if the log ends in a partial line (an interrupted
+// writer), a newline is written first so that the new line stays intact.
+bool append_line(const std::string& path, const std::string& line)
+{
+    bool need_nl = false;
+    if (FILE* r = std::fopen(path.c_str(), "rb")) {
+        if (std::fseek(r, -1, SEEK_END) == 0) need_nl = std::fgetc(r) != '\n';
+        std::fclose(r);
+    }
+    FILE* f = std::fopen(path.c_str(), "a");
+    if (!f) return false;
+    bool ok = true;
+    if (need_nl) ok = std::fputc('\n', f) != EOF;
+    ok = ok && std::fwrite(line.data(), 1, line.size(), f) == line.size();
+    return (std::fclose(f) == 0) && ok;
+}
+
+void load_cache(csr_context_t ctx)
+{
+    std::ifstream in(ctx->cache_path);
+    if (!in) return;  // a missing log is an empty cache
+    std::string line;
+    while (std::getline(in, line)) {
+        if (line.empty() || line[0] == '#') continue;
+        uint64_t sig;
+        csr_schedule_t s;
+        double us;
+        if (!csrh::parse_cache_line(line, &sig, &s, &us)) {
+            ++ctx->skipped_lines;
+            continue;
+        }
+        ctx->cache[sig] = CacheEntry{s, us, true};  // a later line for a signature replaces an earlier one
+    }
+}
+
+int store_entry(csr_context_t ctx, uint64_t sig, const csr_schedule_t& s, double us)
+{
+    ctx->cache[sig] = CacheEntry{s, us, false};
+    if (ctx->cache_path.empty()) {
+        ctx->cache[sig].persisted = true;
+        return CSR_OK;
+    }
+    if (append_line(ctx->cache_path, csrh::format_cache_line(sig, s, us))) {
+        ctx->cache[sig].persisted = true;
+        return CSR_OK;
+    }
+    ++ctx->io_errors;
+    return set_err(ctx, CSR_ERR_CACHE_IO, "cannot append to the cache log " + ctx->cache_path);
+}
+
+bool env_flag(const char* name)
+{
+    const char* v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+// ---------------------------------------------------------------------------
+// Execution of one schedule
+// ---------------------------------------------------------------------------
+
+int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st)
+{
+    char* ws = static_cast<char*>(p.workspace);
+    if (ctx->flags & CSR_CTX_VALIDATE) {
+        int64_t* bad = reinterpret_cast<int64_t*>(ws);
+        CSR_HIP(ctx, csrk::launch_validate(p.row_ptr, p.col_idx, p.n_rows, p.n_cols, p.nnz, bad, st));
+        CSR_HIP(ctx, hipMemcpyAsync(ctx->pinned, bad, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        CSR_HIP(ctx, hipStreamSynchronize(st));
+        if (ctx->pinned[0] != 0) return set_err(ctx, CSR_ERR_INVALID_CSR, "row_ptr / col_idx fail CSR validation");
+    }
+    if (p.n_rows == 0) return CSR_OK;
+    if (p.op == CSR_OP_SDDMM && p.nnz == 0) return CSR_OK;
+
+    const csrh::WsLayout L = csrh::ws_layout(p, s);
+    int32_t* coords = reinterpret_cast<int32_t*>(ws + L.coords);
+    if (s.mapping == CSR_MAP_MERGEPATH) {
+        CSR_HIP(ctx, csrk::launch_merge_path(p.row_ptr, p.n_rows, p.nnz, s.chunk_items, L.n_chunks, coords, st));
+    }
+
+    if (p.op == CSR_OP_MHA) {
+        csrk::MhaArgs a{};
+        a.row_ptr = p.row_ptr;
+        a.col_idx = p.col_idx;
+        a.n_rows = p.n_rows;
+        a.Q = static_cast<const uint16_t*>(p.a);
+        a.K = static_cast<const uint16_t*>(p.b);
+        a.V = static_cast<const uint16_t*>(p.c);
+        a.H = p.heads;
+        a.Dh = p.head_dim;
+        a.scale = p.scale;
+        a.out = static_cast<float*>(p.out);
+        a.part = coords;
+        a.n_chunks = L.n_chunks;
+        a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
+        a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
+        a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
+        const int lph = p.head_dim / 8;
+        CSR_HIP(ctx, csrk::launch_mha(s.mapping, lph, s.chunk_items, a, st));
+        if (s.mapping == CSR_MAP_MERGEPATH) CSR_HIP(ctx, csrk::launch_mha_fixup(lph, a, st));
+        return CSR_OK;
+    }
+
+    csrk::Fp32Args a{};
+    a.row_ptr = p.row_ptr;
+    a.col_idx = p.col_idx;
+    a.n_rows = p.n_rows;
+    a.F = (int32_t)p.width;
+    a.W = s.group_lanes;
+    a.scale = p.scale;
+    a.long_row = s.long_row;
+    a.part = coords;
+    a.n_chunks = L.n_chunks;
+    a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
+    a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
+    a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
+    if (p.op == CSR_OP_SDDMM) {
+        a.U = static_cast<const float*>(p.a);
+        a.ldu = p.ld_a;
+        a.X = static_cast<const float*>(p.b);
+        a.ldx = p.ld_b;
+        a.Y = static_cast<float*>(p.out);
+        CSR_HIP(ctx, csrk::launch_sddmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        return CSR_OK;
+    }
+    a.ev = static_cast<const float*>(p.a);
+    a.X = static_cast<const float*>(p.b);
+    a.ldx = p.ld_b;
+    a.Y = static_cast<float*>(p.out);
+    a.ldy = p.ld_out;
+    if (p.op == CSR_OP_SPMM) {
+        CSR_HIP(ctx, csrk::launch_spmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        if (s.mapping == CSR_MAP_MERGEPATH) CSR_HIP(ctx, csrk::launch_spmm_fixup(s.vec, s.passes, a, st));
+    } else {
+        CSR_HIP(ctx, csrk::launch_attention(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        if (s.mapping == CSR_MAP_MERGEPATH) CSR_HIP(ctx, csrk::launch_attention_fixup(s.vec, s.passes, a, st));
+    }
+    return CSR_OK;
+}
+
+size_t auto_workspace(const csr_problem_t& p)
+{
+    size_t need = csrh::kHeadBytes;
+    for (const auto& c : csrh::candidates(p, nullptr)) need = std::max(need, csrh::workspace_bytes(p, c));
+    csr_schedule_t rg = csrh::default_schedule(p);
+    rg.mapping = CSR_MAP_ROWGROUP;
+    rg.chunk_items = rg.long_row = 0;
+    return std::max(need, csrh::workspace_bytes(p, rg));
+}
+
+int check_workspace(csr_context_t ctx, const csr_problem_t& p, size_t need)
+{
+    if (need > 0 && !p.workspace) return set_err(ctx, CSR_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)p.workspace % csrh::kAlign) return set_err(ctx, CSR_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (p.workspace_bytes < need)
+        return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+    return CSR_OK;
+}
+
+int histogram(csr_context_t ctx, const csr_problem_t& p, hipStream_t st, int64_t* out)
+{
+    int64_t* dev = static_cast<int64_t*>(p.workspace);
+    CSR_HIP(ctx, csrk::launch_degree_hist(p.row_ptr, p.n_rows, dev, st));
+    CSR_HIP(ctx, hipMemcpyAsync(ctx->pinned, dev, csrh::kHistInts * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    CSR_HIP(ctx, hipStreamSynchronize(st));
+    std::memcpy(out, ctx->pinned, csrh::kHistInts * sizeof(int64_t));
+    return CSR_OK;
+}
+
+// Times schedule s on p: one untimed run, then `reps` timed runs; returns
+// the median in microseconds, or a negative value if a run failed.
+double probe(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st, int reps)
+{
+    if (env_flag("CSRSA_FAIL_PROBE")) return -1.0;
+    if (run_schedule(ctx, p, s, st) != CSR_OK) return -1.0;
+    if (!ctx->ev0) {
+        if (hipEventCreate(&ctx->ev0) != hipSuccess || hipEventCreate(&ctx->ev1) != hipSuccess) return -1.0;
+    }
+    std::vector<double> t;
+    for (int r = 0; r < reps; ++r) {
+        if (hipEventRecord(ctx->ev0, st) != hipSuccess) return -1.0;
+        if (run_schedule(ctx, p, s, st) != CSR_OK) return -1.0;
+        if (hipEventRecord(ctx->ev1, st) != hipSuccess) return -1.0;
+        if (hipEventSynchronize(ctx->ev1) != hipSuccess) return -1.0;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ctx->ev0, ctx->ev1) != hipSuccess) return -1.0;
+        t.push_back(ms * 1000.0);
+    }
+    std::sort(t.begin(), t.end());
+    return t[t.size() / 2];
+}
+
+int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_schedule_t* out, uint64_t* sig_out)
+{
+    std::string why;
+    const bool need_ptrs = (mode == CSR_SELECT_AUTO || mode == CSR_SELECT_FORCE_PROBE);
+    int rc = csrh::check_problem(p, need_ptrs, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    if (!p.row_ptr) return set_err(ctx, CSR_ERR_NULL, "row_ptr is NULL");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    rc = check_workspace(ctx, p, need_ptrs ? auto_workspace(p) : csrh::kHeadBytes);
+    if (rc != CSR_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+
+    int64_t hist[csrh::kHistInts];
+    rc = histogram(ctx, p, st, hist);
+    if (rc != CSR_OK) return rc;
+    const uint64_t sig = csrh::signature(p, hist, ctx->dev);
+    if (sig_out) *sig_out = sig;
+
+    if (mode == CSR_SELECT_AUTO || mode == CSR_SELECT_REPLAY_ONLY) {
+        auto it = ctx->cache.find(sig);
+        if (it != ctx->cache.end() && csrh::check_schedule(p, it->second.sched, nullptr) == CSR_OK) {
+            *out = it->second.sched;
+            return CSR_OK;
+        }
+        if (mode == CSR_SELECT_REPLAY_ONLY) return set_err(ctx, CSR_ERR_NO_CACHE_ENTRY, "no cached schedule for this input");
+    }
+
+    std::vector<csr_schedule_t> cand = csrh::candidates(p, hist);
+    // rank by the cost model; probe the best few
+    std::vector<std::pair<double, size_t>> order;
+    for (size_t i = 0; i < cand.size(); ++i) order.push_back({csrh::estimate(p, cand[i], hist, ctx->dev), i});
+    std::stable_sort(order.begin(), order.end(),
+                     [](const std::pair<double, size_t>& x, const std::pair<double, size_t>& y) { return x.first < y.first; });
+    if (mode == CSR_SELECT_ESTIMATE || (ctx->flags & CSR_CTX_NO_PROBE)) {
+        *out = cand[order[0].second];
+        if (mode != CSR_SELECT_ESTIMATE) store_entry(ctx, sig, *out, 0.0);
+        return CSR_OK;
+    }
+    const int max_probe = std::max(1, env_int("CSRSA_PROBE_CANDIDATES", 6));
+    const int reps = std::max(1, env_int("CSRSA_PROBE_REPS", 5));
+    std::vector<size_t> probe_set;
+    for (size_t k = 0; k < order.size() && (int)probe_set.size() < max_probe; ++k) probe_set.push_back(order[k].second);
+    std::sort(probe_set.begin(), probe_set.end());  // fixed candidate order for tie-breaking
+    double best = -1.0;
+    size_t best_i = 0;
+    for (size_t i : probe_set) {
+        const double t = probe(ctx, p, cand[i], st, reps);
+        if (t < 0) continue;  // guardrail: a failing candidate is never chosen
+        if (best < 0 || t < best * 0.99) {
+            best = t;
+            best_i = i;
+        }
+    }
+    if (best < 0) {
+        // every probe failed: fall back to the default schedule
+        (void)hipGetLastError();
+        *out = csrh::default_schedule(p);
+        return CSR_OK;
+    }
+    *out = cand[best_i];
+    (void)store_entry(ctx, sig, *out, best);  // a log write failure keeps the entry in memory
+    return CSR_OK;
+}
+
+// Shared body of the four operation calls.
+int op_call(csr_context_t ctx, csr_problem_t& p, const csr_schedule_t* sched)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        std::string why;
+        int rc = csrh::check_problem(p, true, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+        DeviceGuard g(ctx->device);
+        csr_schedule_t s;
+        if (sched) {
+            rc = csrh::check_schedule(p, *sched, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            rc = check_workspace(ctx, p, csrh::workspace_bytes(p, *sched));
+            if (rc != CSR_OK) return rc;
+            s = *sched;
+        } else {
+            rc = select_locked(ctx, p, CSR_SELECT_AUTO, &s, nullptr);
+            if (rc != CSR_OK) return rc;
+        }
+        return run_schedule(ctx, p, s, static_cast<hipStream_t>(p.stream));
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+csr_problem_t blank_problem()
+{
+    csr_problem_t p;
+    std::memset(&p, 0, sizeof p);
+    p.scale = 1.0f;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csr_status_string(int status)
+{
+    switch (status) {
+    case CSR_OK: return "ok";
+    case CSR_ERR_NULL: return "null pointer";
+    case CSR_ERR_SHAPE: return "invalid or unsupported shape";
+    case CSR_ERR_DTYPE: return "unsupported dtype";
+    case CSR_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case CSR_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSR_ERR_INVALID_CSR: return "CSR validation failed";
+    case CSR_ERR_SCHEDULE: return "schedule invalid for this problem";
+    case CSR_ERR_NO_CACHE_ENTRY: return "no cached schedule";
+    case CSR_ERR_CACHE_IO: return "cache file I/O error";
+    case CSR_ERR_HIP: return "HIP runtime error";
+    case CSR_ERR_DEVICE: return "no usable gfx950 device";
+    case CSR_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+    }
+}
+
+const char* csr_last_error(csr_context_t ctx) { return ctx ? ctx->last_error.c_str() : ""; }
+
+int csr_context_create(csr_context_t* out, int device, const char* cache_path, uint32_t flags)
+{
+    if (!out) return CSR_ERR_NULL;
+    *out = nullptr;
+    csr_context_t ctx = nullptr;
+    try {
+        ctx = new csr_context_s();
+        ctx->flags = flags;
+        ctx->device = device;
+        if (cache_path) ctx->cache_path = cache_path;
+        if (device >= 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+                delete ctx;
+                return CSR_ERR_DEVICE;
+            }
+            if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+                delete ctx;
+                return CSR_ERR_DEVICE;
+            }
+            ctx->dev.cu_count = prop.multiProcessorCount;
+            ctx->dev.arch = 950;
+            DeviceGuard g(device);
+            if (hipHostMalloc(reinterpret_cast<void**>(&ctx->pinned), 4096, hipHostMallocDefault) != hipSuccess) {
+                delete ctx;
+                return CSR_ERR_HIP;
+            }
+        } else {
+            ctx->pinned = static_cast<int64_t*>(std::calloc(512, sizeof(int64_t)));
+        }
+        if (!ctx->cache_path.empty()) load_cache(ctx);
+    } catch (...) {
+        delete ctx;
+        return CSR_ERR_INTERNAL;
+    }
+    *out = ctx;
+    return CSR_OK;
+}
+
+int csr_context_destroy(csr_context_t ctx)
+{
+    if (!ctx) return CSR_OK;
+    int rc = csr_cache_flush(ctx);
+    if (ctx->device >= 0) {
+        DeviceGuard g(ctx->device);
+        if (ctx->ev0) (void)hipEventDestroy(ctx->ev0);
+        if (ctx->ev1) (void)hipEventDestroy(ctx->ev1);
+        if (ctx->pinned) (void)hipHostFree(ctx->pinned);
+    } else {
+        std::free(ctx->pinned);
+    }
+    delete ctx;
+    return rc;
+}
+
+int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+             const int32_t* col_idx, const float* vals, const float* X, int64_t F, int64_t ldx, float* Y,
+             int64_t ldy, const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
+{
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_SPMM;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = n_rows;
+    p.n_cols = n_cols;
+    p.nnz = nnz;
+    p.width = F;
+    p.ld_b = ldx;
+    p.ld_out = ldy;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.a = vals;
+    p.b = X;
+    p.out = Y;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
+int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+              const int32_t* col_idx, const float* U, int64_t ldu, const float* V, int64_t ldv, int64_t K,
+              float* out, const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
+{
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_SDDMM;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = n_rows;
+    p.n_cols = n_cols;
+    p.nnz = nnz;
+    p.width = K;
+    p.ld_a = ldu;
+    p.ld_b = ldv;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.a = U;
+    p.b = V;
+    p.out = out;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
+int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                  const int32_t* col_idx, const float* edge_scores, const float* node_value, int64_t F, int64_t ldv,
+                  float scale, float* out, int64_t ldo, const csr_schedule_t* sched, void* workspace,
+                  size_t ws_bytes, void* stream)
+{
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_ATTENTION;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = n_rows;
+    p.n_cols = n_cols;
+    p.nnz = nnz;
+    p.width = F;
+    p.ld_b = ldv;
+    p.ld_out = ldo;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.a = edge_scores;
+    p.b = node_value;
+    p.out = out;
+    p.scale = scale;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
+int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                      const int32_t* col_idx, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                      int32_t heads, int32_t head_dim, float scale, float* out, const csr_schedule_t* sched,
+                      void* workspace, size_t ws_bytes, void* stream)
+{
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_MHA;
+    p.dtype = CSR_DTYPE_BF16;
+    p.n_rows = n_rows;
+    p.n_cols = n_cols;
+    p.nnz = nnz;
+    p.heads = heads;
+    p.head_dim = head_dim;
+    p.width = (int64_t)heads * head_dim;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.a = Q;
+    p.b = K;
+    p.c = V;
+    p.out = out;
+    p.scale = scale;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
+int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_schedule_t* out, uint64_t* signature)
+{
+    if (!ctx || !p || !out) return CSR_ERR_NULL;
+    if (mode > CSR_SELECT_ESTIMATE) return set_err(ctx, CSR_ERR_SHAPE, "unknown selection mode");
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        DeviceGuard g(ctx->device);
+        return select_locked(ctx, *p, mode, out, signature);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule_t* out)
+{
+    if (!p || !out) return CSR_ERR_NULL;
+    std::string why;
+    int rc = csrh::check_problem(*p, false, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    *out = csrh::default_schedule(*p);
+    return CSR_OK;
+}
+
+int csr_workspace_size(csr_context_t ctx, const csr_problem_t* p, const csr_schedule_t* sched, size_t* bytes)
+{
+    if (!p || !bytes) return CSR_ERR_NULL;
+    std::string why;
+    int rc = csrh::check_problem(*p, false, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    if (sched) {
+        rc = csrh::check_schedule(*p, *sched, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+        *bytes = csrh::workspace_bytes(*p, *sched);
+    } else {
+        *bytes = auto_workspace(*p);
+    }
+    return CSR_OK;
+}
+
+int csr_cache_flush(csr_context_t ctx)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (ctx->cache_path.empty()) return CSR_OK;
+    int rc = CSR_OK;
+    for (auto& kv : ctx->cache) {
+        if (kv.second.persisted) continue;
+        if (append_line(ctx->cache_path, csrh::format_cache_line(kv.first, kv.second.sched, kv.second.probe_us)))
+            kv.second.persisted = true;
+        else
+            rc = CSR_ERR_CACHE_IO;
+    }
+    return rc;
+}
+
+int csr_cache_info(csr_context_t ctx, int64_t* entries, int64_t* skipped_lines, int64_t* io_errors)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (entries) *entries = (int64_t)ctx->cache.size();
+    if (skipped_lines) *skipped_lines = ctx->skipped_lines;
+    if (io_errors) *io_errors = ctx->io_errors;
+    return CSR_OK;
+}
+
+int csr_cache_lookup(csr_context_t ctx, uint64_t signature, csr_schedule_t* out)
+{
+    if (!ctx || !out) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    auto it = ctx->cache.find(signature);
+    if (it == ctx->cache.end()) return CSR_ERR_NO_CACHE_ENTRY;
+    *out = it->second.sched;
+    return CSR_OK;
+}
+
+int csr_cache_store(csr_context_t ctx, uint64_t signature, const csr_schedule_t* sched)
+{
+    if (!ctx || !sched) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_MHA)
+        return set_err(ctx, CSR_ERR_SCHEDULE, "not a schedule of this library version");
+    return store_entry(ctx, signature, *sched, 0.0);
+}
+
+int csr_degree_histogram(csr_context_t ctx, int64_t n_rows, const int32_t* row_ptr, int64_t* out_host,
+                         void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx || !row_ptr || !out_host) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        if (n_rows < 0 || n_rows >= ((int64_t)1 << 31) - 1) return set_err(ctx, CSR_ERR_SHAPE, "bad n_rows");
+        csr_problem_t p = blank_problem();
+        p.n_rows = n_rows;
+        p.row_ptr = row_ptr;
+        p.workspace = workspace;
+        p.workspace_bytes = ws_bytes;
+        int rc = check_workspace(ctx, p, csrh::kHeadBytes);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        return histogram(ctx, p, static_cast<hipStream_t>(stream), out_host);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_merge_path_partition(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
+                             int32_t items_per_chunk, int32_t* coords, void* stream)
+{
+    if (!ctx || !row_ptr || !coords) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    const int64_t lim = (int64_t)1 << 31;
+    if (n_rows < 0 || nnz < 0 || n_rows >= lim - 1 || nnz >= lim || items_per_chunk < 1)
+        return set_err(ctx, CSR_ERR_SHAPE, "bad sizes");
+    DeviceGuard g(ctx->device);
+    const int64_t total = n_rows + nnz;
+    int64_t nc = (total + items_per_chunk - 1) / items_per_chunk;
+    if (nc < 1) nc = 1;
+    CSR_HIP(ctx, csrk::launch_merge_path(row_ptr, n_rows, nnz, items_per_chunk, nc, coords,
+                                         static_cast<hipStream_t>(stream)));
+    return CSR_OK;
+}
+
+int csr_signature(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, uint64_t* signature)
+{
+    if (!p || !histogram || !signature) return CSR_ERR_NULL;
+    csrh::DeviceInfo dev;
+    if (ctx) dev = ctx->dev;
+    *signature = csrh::signature(*p, histogram, dev);
+    return CSR_OK;
+}
+
+}  // extern "C"

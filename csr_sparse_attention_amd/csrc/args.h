@@ -1,0 +1,47 @@
+// Kernel argument blocks (plain data, passed by value as kernel arguments).
+#pragma once
+
+#include <stdint.h>
+
+namespace csrk {
+
+struct Fp32Args {
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    int64_t n_rows;
+    const float* ev;   // per-entry input: SpMM values (may be null = 1) or attention scores
+    const float* U;    // SDDMM row operand
+    int64_t ldu;
+    const float* X;    // gathered operand: SpMM X, attention node_value, SDDMM V
+    int64_t ldx;
+    float* Y;          // output rows (SpMM, attention) or per-entry output (SDDMM)
+    int64_t ldy;
+    int32_t F;         // feature width (K for SDDMM)
+    int32_t W;         // lanes per group, power of two
+    float scale;       // attention score scale
+    int32_t long_row;  // merge path: whole-wave threshold
+    const int32_t* part;  // merge path: (x, y) per chunk boundary
+    int64_t n_chunks;
+    int32_t* carry_row;   // [2 n_chunks]: row of slot A / slot B, -1 if empty
+    float* carry_ml;      // [2 n_chunks][2]: attention piece (max, sum of exp)
+    float* carry_val;     // [2 n_chunks][F]
+};
+
+struct MhaArgs {
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    int64_t n_rows;
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    int32_t H, Dh;
+    float scale;
+    float* out;
+    const int32_t* part;
+    int64_t n_chunks;
+    int32_t* carry_row;  // [2 n_chunks]
+    float* carry_ml;     // [2 n_chunks][H][2]
+    float* carry_val;    // [2 n_chunks][H * Dh]
+};
+
+}  // namespace csrk

@@ -1,0 +1,107 @@
+// Device-side building blocks shared by the CSR kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csrsa.h"
+
+#define CSR_WAVE 64
+#define CSR_BLOCK 256
+#define CSR_WAVES_PER_BLOCK (CSR_BLOCK / CSR_WAVE)
+
+namespace csrk {
+
+// ---------------------------------------------------------------------------
+// fp32 vectors of 1, 2 or 4 lanes (one global load / store instruction each)
+// ---------------------------------------------------------------------------
+template <int VEC> struct vtype;
+template <> struct vtype<1> { typedef float t; };
+template <> struct vtype<2> { typedef float2 t; };
+template <> struct vtype<4> { typedef float4 t; };
+
+template <int VEC>
+__device__ __forceinline__ void vload(float (&d)[VEC], const float* p)
+{
+    typedef typename vtype<VEC>::t T;
+    T v = *reinterpret_cast<const T*>(p);
+    if constexpr (VEC == 1) {
+        d[0] = v;
+    } else if constexpr (VEC == 2) {
+        d[0] = v.x; d[1] = v.y;
+    } else {
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void vstore(float* p, const float (&s)[VEC])
+{
+    typedef typename vtype<VEC>::t T;
+    T v;
+    if constexpr (VEC == 1) {
+        v = s[0];
+    } else if constexpr (VEC == 2) {
+        v.x = s[0]; v.y = s[1];
+    } else {
+        v.x = s[0]; v.y = s[1]; v.z = s[2]; v.w = s[3];
+    }
+    *reinterpret_cast<T*>(p) = v;
+}
+
+// Streamed (read-once) loads of the CSR arrays: non-temporal so that they do
+// not push the gathered feature rows out of the caches.
+__device__ __forceinline__ int ld_stream(const int32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float ld_stream(const float* p) { return __builtin_nontemporal_load(p); }
+
+// exp(x) for x <= 0 as 2^(x log2 e) on the hardware exp2 unit.
+__device__ __forceinline__ float exp_neg(float x)
+{
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, CSR_WAVE); }
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Sum over the lanes l, l ^ from, l ^ 2 from, ... (from a power of two < 64):
+// afterwards every lane holds the sum over its coset.
+__device__ __forceinline__ float xor_sum_from(float v, int from)
+{
+    for (int s = from; s < CSR_WAVE; s <<= 1) v += shfl_xor(v, s);
+    return v;
+}
+
+// Sum over the lanes of an aligned group of W lanes.
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int s = 1; s < W; s <<= 1) v += shfl_xor(v, s);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int s = 1; s < W; s <<= 1) v = fmaxf(v, shfl_xor(v, s));
+    return v;
+}
+
+// Online softmax state (m = running maximum, l = sum of exp(t - m)) merged
+// across the lanes l ^ s for s = from .. 32.  The lanes of one group must
+// hold identical states on entry when from > 1.
+__device__ __forceinline__ void softmax_merge_xor(float& m, float& l, int from, int to)
+{
+    for (int s = from; s < to; s <<= 1) {
+        float m2 = shfl_xor(m, s);
+        float l2 = shfl_xor(l, s);
+        float mm = fmaxf(m, m2);
+        float a = (l > 0.f) ? l * exp_neg(m - mm) : 0.f;
+        float b = (l2 > 0.f) ? l2 * exp_neg(m2 - mm) : 0.f;
+        m = mm;
+        l = a + b;
+    }
+}
+
+} // namespace csrk

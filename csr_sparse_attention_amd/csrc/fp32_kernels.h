@@ -1,0 +1,461 @@
+// Templated fp32 kernels: SpMM, scores-given softmax attention and SDDMM, in
+// the row-group mapping and the merge-path mapping.
+//
+// Lane layout (both mappings).  A wavefront of 64 lanes is cut into G = 64/W
+// groups of W lanes.  Within a group, lane lg covers the features
+// (j * W + lg) * VEC .. + VEC - 1 for passes j < NV, so a row of F features is
+// read with W * NV vector loads of VEC floats each.  W, VEC and NV are chosen
+// on the host from F and the alignment of the operands.
+//
+// Row-group mapping: group k of the grid owns row k and walks its entries.
+//
+// Merge-path mapping: the rows and entries are merged into one sequence (the
+// end of a row follows the row's last entry) and cut into chunks of D items,
+// one chunk per wavefront, so every wavefront gets the same amount of work
+// whatever the degree skew.  A wave stages its chunk's row_ptr, col_idx and
+// per-entry values in LDS, then
+//   pass 1: every row segment with at least `long_row` entries is processed
+//           by the whole wave, the G groups taking interleaved entries, and
+//           reduced across the groups;
+//   pass 2: the remaining short rows are dealt round-robin to the groups.
+// Rows whose entries are cut by a chunk boundary leave pieces in a carry
+// buffer (slot A: the end of a row that began in an earlier chunk, slot B:
+// the beginning or middle of a row that continues into the next chunk), and a
+// fix-up kernel combines each such row's pieces in chunk order.  No atomics:
+// results are bitwise reproducible for a given schedule.
+#pragma once
+
+#include "args.h"
+#include "common.h"
+
+namespace csrk {
+
+enum class Op { Spmm, Attention, Sddmm };
+
+
+template <int VEC, int NV>
+struct Lanes {
+    int W, lg, g, G;
+    __device__ __forceinline__ Lanes(int w) : W(w)
+    {
+        int lane = lane_id();
+        lg = lane & (w - 1);
+        g = lane / w;
+        G = CSR_WAVE / w;
+    }
+    __device__ __forceinline__ int off(int j) const { return (j * W + lg) * VEC; }
+    __device__ __forceinline__ bool valid(int j, int F) const { return off(j) < F; }
+};
+
+template <int VEC, int NV>
+__device__ __forceinline__ void zero(float (&a)[NV][VEC])
+{
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) a[j][v] = 0.f;
+}
+
+// Edge weight: SpMM value (1 if absent) or unnormalised softmax weight.
+template <Op OP>
+__device__ __forceinline__ float edge_weight(const float* ev, int e, float scale, float m)
+{
+    if constexpr (OP == Op::Spmm) {
+        return ev ? ev[e] : 1.f;
+    } else {
+        return exp_neg(ev[e] * scale - m);
+    }
+}
+
+// acc += sum over entries e = kb, kb + step, ... < ke of w_e * X[col[e], lane features].
+// col / ev are indexed directly by e (they may point into LDS or global memory).
+template <Op OP, int VEC, int NV, int U>
+__device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t* col, const float* ev,
+                                           int kb, int ke, int step, const float* X, int64_t ldx,
+                                           const Lanes<VEC, NV>& L, int F, float scale, float m)
+{
+    for (int k = kb; k < ke; k += step * U) {
+        float xv[U][NV][VEC];
+        float w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int e = k + u * step;
+            bool ok = e < ke;
+            int c = ok ? col[e] : 0;
+            w[u] = ok ? edge_weight<OP>(ev, e, scale, m) : 0.f;
+            const float* xr = X + (int64_t)c * ldx;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (ok && L.valid(j, F)) {
+                    vload<VEC>(xv[u][j], xr + L.off(j));
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) xv[u][j][v] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[j][v] = fmaf(w[u], xv[u][j][v], acc[j][v]);
+    }
+}
+
+// Softmax statistics (max, sum of exp) of scale * ev[e] over e = kb + t, kb + t + n, ...
+// for this lane's t, merged over the n lanes (an aligned power-of-two set).
+__device__ __forceinline__ void seg_softmax_stats(const float* ev, int kb, int ke, int t, int n,
+                                                  float scale, float& m, float& l)
+{
+    m = -INFINITY;
+    l = 0.f;
+    for (int e = kb + t; e < ke; e += n) {
+        float x = ev[e] * scale;
+        if (x > m) {
+            l = l * exp_neg(m - x) + 1.f;
+            m = x;
+        } else {
+            l += exp_neg(x - m);
+        }
+    }
+    // merge lanes t ^ 1, t ^ 2, ... within the n-lane set
+    for (int s = 1; s < n; s <<= 1) {
+        float m2 = shfl_xor(m, s), l2 = shfl_xor(l, s);
+        float mm = fmaxf(m, m2);
+        float a = (l > 0.f) ? l * exp_neg(m - mm) : 0.f;
+        float b = (l2 > 0.f) ? l2 * exp_neg(m2 - mm) : 0.f;
+        m = mm;
+        l = a + b;
+    }
+}
+
+template <int VEC, int NV>
+__device__ __forceinline__ void store_row(float* dst, const float (&acc)[NV][VEC], const Lanes<VEC, NV>& L,
+                                          int F, float mul)
+{
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (L.valid(j, F)) {
+            float o[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) o[v] = acc[j][v] * mul;
+            vstore<VEC>(dst + L.off(j), o);
+        }
+    }
+}
+
+template <int VEC, int NV>
+__device__ __forceinline__ void store_row_div(float* dst, const float (&acc)[NV][VEC], const Lanes<VEC, NV>& L,
+                                              int F, float den)
+{
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (L.valid(j, F)) {
+            float o[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) o[v] = acc[j][v] / den;
+            vstore<VEC>(dst + L.off(j), o);
+        }
+    }
+}
+
+// SDDMM: out[e] = <u, X[col[e]]> for e = kb, kb + step, ... < ke; the W lanes
+// of the group reduce the partial dot products and lane 0 of the group writes.
+template <int VEC, int NV, int U>
+__device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int32_t* col, int kb, int ke,
+                                            int step, const float* X, int64_t ldx, const Lanes<VEC, NV>& L,
+                                            int F, float* out)
+{
+    for (int k = kb; k < ke; k += step * U) {
+        float xv[U][NV][VEC];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            int e = k + uu * step;
+            bool ok = e < ke;
+            int c = ok ? col[e] : 0;
+            const float* xr = X + (int64_t)c * ldx;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (ok && L.valid(j, F)) {
+                    vload<VEC>(xv[uu][j], xr + L.off(j));
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) xv[uu][j][v] = 0.f;
+                }
+            }
+        }
+        float d[U];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) s = fmaf(u[j][v], xv[uu][j][v], s);
+            d[uu] = s;
+        }
+        for (int s = 1; s < L.W; s <<= 1) {
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) d[uu] += shfl_xor(d[uu], s);
+        }
+        if (L.lg == 0) {
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                int e = k + uu * step;
+                if (e < ke) out[e] = d[uu];
+            }
+        }
+    }
+}
+
+template <int VEC, int NV>
+__device__ __forceinline__ void load_row(float (&u)[NV][VEC], const float* src, const Lanes<VEC, NV>& L, int F)
+{
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (L.valid(j, F)) {
+            vload<VEC>(u[j], src + L.off(j));
+        } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) u[j][v] = 0.f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-group mapping
+// ---------------------------------------------------------------------------
+template <Op OP, int VEC, int NV, int U>
+__global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
+{
+    Lanes<VEC, NV> L(a.W);
+    int64_t row = ((int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x) / a.W;
+    if (row >= a.n_rows) return;  // groups are whole: no group is split by this test
+    int b = a.row_ptr[row], e = a.row_ptr[row + 1];
+
+    if constexpr (OP == Op::Sddmm) {
+        float u[NV][VEC];
+        load_row<VEC, NV>(u, a.U + row * a.ldu, L, a.F);
+        sddmm_edges<VEC, NV, U>(u, a.col_idx, b, e, 1, a.X, a.ldx, L, a.F, a.Y);
+    } else {
+        float acc[NV][VEC];
+        zero(acc);
+        float m = 0.f, l = 1.f;
+        if constexpr (OP == Op::Attention) {
+            seg_softmax_stats(a.ev, b, e, L.lg, a.W, a.scale, m, l);
+        }
+        gather_acc<OP, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, a.X, a.ldx, L, a.F, a.scale, m);
+        float* dst = a.Y + row * a.ldy;
+        if (OP == Op::Attention && e > b)
+            store_row_div<VEC, NV>(dst, acc, L, a.F, l);
+        else
+            store_row<VEC, NV>(dst, acc, L, a.F, 1.f);  // empty rows: acc == 0
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge-path mapping
+// ---------------------------------------------------------------------------
+template <int D>
+struct MpShared {
+    int32_t rp[CSR_WAVES_PER_BLOCK][D + 2];
+    int32_t col[CSR_WAVES_PER_BLOCK][D];
+    float ev[CSR_WAVES_PER_BLOCK][D];
+};
+
+template <Op OP, int VEC, int NV, int U, int D>
+__global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
+{
+    __shared__ MpShared<D> sh;
+    const int wave = threadIdx.x / CSR_WAVE;
+    const int lane = lane_id();
+    const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
+    const bool active = chunk < a.n_chunks;
+
+    int x0 = 0, y0 = 0, x1 = 0, y1 = 0, nrow = 0;
+    bool slotA = false, slotB = false;
+    if (active) {
+        x0 = a.part[2 * chunk];
+        y0 = a.part[2 * chunk + 1];
+        x1 = a.part[2 * chunk + 2];
+        y1 = a.part[2 * chunk + 3];
+        // rows x0 .. x1-1 end in this chunk; row x1 may own entries [.., y1)
+        int rpx1 = (x1 < a.n_rows) ? a.row_ptr[x1] : y1;
+        slotB = (x1 < a.n_rows) && (max(rpx1, y0) < y1);
+        nrow = x1 - x0 + (slotB ? 1 : 0);
+        for (int i = lane; i <= nrow; i += CSR_WAVE) sh.rp[wave][i] = a.row_ptr[x0 + i];
+        const int ne = y1 - y0;
+        for (int i = lane; i < ne; i += CSR_WAVE) {
+            sh.col[wave][i] = ld_stream(a.col_idx + y0 + i);
+            if constexpr (OP != Op::Sddmm) sh.ev[wave][i] = a.ev ? ld_stream(a.ev + y0 + i) : 1.f;
+        }
+    }
+    __syncthreads();
+    if (!active) return;
+
+    const int32_t* rp = sh.rp[wave];
+    const int32_t* col = sh.col[wave] - y0;  // indexed by absolute entry id
+    const float* ev = sh.ev[wave] - y0;
+    slotA = (x0 < x1) && (rp[0] < y0);
+    if (lane == 0) {
+        a.carry_row[2 * chunk] = slotA ? x0 : -1;
+        a.carry_row[2 * chunk + 1] = slotB ? x1 : -1;
+    }
+
+    Lanes<VEC, NV> L(a.W);
+    const int G = L.G;
+    const int long_row = (G == 1) ? 0 : a.long_row;
+
+    // Emits the result of row index i (row x0 + i) of this chunk: rows
+    // x0 .. x1-1 end here and are final unless they began before y0 (slot A,
+    // only possible for i == 0); row x1, when present, continues (slot B).
+    const int nend = x1 - x0;
+    auto emit = [&](int i, float (&acc)[NV][VEC], float m, float l, bool whole_wave) {
+        const int rs = rp[i], re = rp[i + 1];
+        const int64_t row = (int64_t)x0 + i;
+        if (whole_wave && L.g != 0) return;
+        if (i < nend && rs >= y0) {
+            float* dst = a.Y + row * a.ldy;
+            if (OP == Op::Attention && re > rs)
+                store_row_div<VEC, NV>(dst, acc, L, a.F, l);
+            else
+                store_row<VEC, NV>(dst, acc, L, a.F, 1.f);
+        } else {
+            const int64_t slot = 2 * chunk + ((i == nend) ? 1 : 0);
+            store_row<VEC, NV>(a.carry_val + slot * a.F, acc, L, a.F, 1.f);
+            if (OP == Op::Attention && L.lg == 0) {
+                a.carry_ml[2 * slot] = m;
+                a.carry_ml[2 * slot + 1] = l;
+            }
+        }
+    };
+
+    if constexpr (OP == Op::Sddmm) {
+        // pass 1: long segments, whole wave
+        for (int i = 0; i < nrow; ++i) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb < long_row || se <= sb) continue;
+            float u[NV][VEC];
+            load_row<VEC, NV>(u, a.U + ((int64_t)x0 + i) * a.ldu, L, a.F);
+            sddmm_edges<VEC, NV, U>(u, col, sb + L.g, se, G, a.X, a.ldx, L, a.F, a.Y);
+        }
+        // pass 2: short segments, one group each
+        for (int i = L.g; i < nrow; i += G) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb >= long_row || se <= sb) continue;
+            float u[NV][VEC];
+            load_row<VEC, NV>(u, a.U + ((int64_t)x0 + i) * a.ldu, L, a.F);
+            sddmm_edges<VEC, NV, U>(u, col, sb, se, 1, a.X, a.ldx, L, a.F, a.Y);
+        }
+    } else {
+        for (int i = 0; i < nrow; ++i) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb < long_row) continue;
+            float acc[NV][VEC];
+            zero(acc);
+            float m = 0.f, l = 1.f;
+            if constexpr (OP == Op::Attention) seg_softmax_stats(ev, sb, se, lane, CSR_WAVE, a.scale, m, l);
+            gather_acc<OP, VEC, NV, U>(acc, col, ev, sb + L.g, se, G, a.X, a.ldx, L, a.F, a.scale, m);
+            if (G > 1) {
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[j][v] = xor_sum_from(acc[j][v], a.W);
+            }
+            emit(i, acc, m, l, true);
+        }
+        if (G > 1) {
+            for (int i = L.g; i < nrow; i += G) {
+                const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+                if (se - sb >= long_row) continue;
+                float acc[NV][VEC];
+                zero(acc);
+                float m = 0.f, l = 1.f;
+                if constexpr (OP == Op::Attention) seg_softmax_stats(ev, sb, se, L.lg, a.W, a.scale, m, l);
+                gather_acc<OP, VEC, NV, U>(acc, col, ev, sb, se, 1, a.X, a.ldx, L, a.F, a.scale, m);
+                emit(i, acc, m, l, false);
+            }
+        }
+    }
+}
+
+// Fix-up of rows split across chunks.  One wave per chunk c whose slot A holds
+// a row r: the pieces of r are slot B of chunks k0 .. c-1 (the run of chunks
+// right before c whose slot B holds r) and slot A of c.  SpMM adds them;
+// attention rescales each piece by exp(m_k - M), M the largest piece maximum.
+// The groups of the wave take interleaved pieces and are reduced in a fixed
+// order, so the result is reproducible.
+template <Op OP, int VEC, int NV>
+__global__ __launch_bounds__(CSR_BLOCK) void k_fixup(Fp32Args a)
+{
+    const int wave = threadIdx.x / CSR_WAVE;
+    const int lane = lane_id();
+    const int64_t c = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
+    if (c >= a.n_chunks) return;
+    const int r = a.carry_row[2 * c];
+    if (r < 0) return;
+
+    // k0: first chunk of the run of slot-B pieces of row r ending at c - 1
+    int64_t k0 = c;
+    while (true) {
+        int64_t idx = k0 - 1 - lane;
+        bool ok = idx >= 0 && a.carry_row[2 * idx + 1] == r;
+        uint64_t mask = __ballot(ok);
+        int n = (~mask == 0) ? 64 : __builtin_ctzll(~mask);
+        k0 -= n;
+        if (n < 64) break;
+    }
+    // pieces: p = 0 .. np-1 -> slot index 2*(k0+p)+1 for p < np-1, 2*c for the last
+    const int64_t np = c - k0 + 1;
+    auto slot_of = [&](int64_t p) -> int64_t { return (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c; };
+
+    Lanes<VEC, NV> L(a.W);
+    float M = 0.f;
+    if constexpr (OP == Op::Attention) {
+        float mm = -INFINITY;
+        for (int64_t p = lane; p < np; p += CSR_WAVE) {
+            int64_t s = slot_of(p);
+            if (a.carry_ml[2 * s + 1] > 0.f) mm = fmaxf(mm, a.carry_ml[2 * s]);
+        }
+        for (int s = 1; s < CSR_WAVE; s <<= 1) mm = fmaxf(mm, shfl_xor(mm, s));
+        M = mm;
+    }
+    float acc[NV][VEC];
+    zero(acc);
+    float lsum = 0.f;
+    for (int64_t p = L.g; p < np; p += L.G) {
+        int64_t s = slot_of(p);
+        float w = 1.f;
+        if constexpr (OP == Op::Attention) {
+            float lp = a.carry_ml[2 * s + 1];
+            w = (lp > 0.f) ? exp_neg(a.carry_ml[2 * s] - M) : 0.f;
+            lsum = fmaf(w, lp, lsum);
+        }
+        const float* src = a.carry_val + s * a.F;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (L.valid(j, a.F)) {
+                float x[VEC];
+                vload<VEC>(x, src + L.off(j));
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[j][v] = fmaf(w, x[v], acc[j][v]);
+            }
+        }
+    }
+    if (L.G > 1) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[j][v] = xor_sum_from(acc[j][v], a.W);
+        lsum = xor_sum_from(lsum, a.W);
+    }
+    if (L.g != 0) return;
+    float* dst = a.Y + (int64_t)r * a.ldy;
+    if constexpr (OP == Op::Attention)
+        store_row_div<VEC, NV>(dst, acc, L, a.F, lsum);
+    else
+        store_row<VEC, NV>(dst, acc, L, a.F, 1.f);
+}
+
+} // namespace csrk

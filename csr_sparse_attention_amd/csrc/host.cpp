@@ -1,0 +1,362 @@
+// Host-side runtime logic that needs no GPU: problem and schedule checks,
+// lane layouts, workspace layout, default schedule, candidate list, cost
+// model, input signature and the cache log format.
+#include "host.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+namespace csrh {
+
+namespace {
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int64_t next_pow2(int64_t v)
+{
+    int64_t p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+bool nv_ok(int nv)
+{
+    switch (nv) {
+    case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 12: case 16: return true;
+    default: return false;
+    }
+}
+
+int nv_up(int64_t nv)
+{
+    static const int s[] = {1, 2, 3, 4, 5, 6, 8, 12, 16};
+    for (int v : s)
+        if (v >= nv) return v;
+    return -1;
+}
+
+int unroll_for(int vec, int nv) { return (vec * nv <= 2) ? 8 : (vec * nv <= 8) ? 4 : (vec * nv <= 16) ? 2 : 1; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_fp32_op(int op) { return op == CSR_OP_SPMM || op == CSR_OP_SDDMM || op == CSR_OP_ATTENTION; }
+
+void fnv(uint64_t& h, int64_t v)
+{
+    for (int i = 0; i < 8; ++i) {
+        h ^= (uint64_t)((uint64_t)v >> (8 * i)) & 0xffu;
+        h *= 0x100000001b3ull;
+    }
+}
+
+}  // namespace
+
+int max_vec_f32(const csr_problem_t& p)
+{
+    for (int v : {4, 2, 1}) {
+        if (p.width % v) continue;
+        const size_t bytes = 4u * v;
+        bool ok = true;
+        if (p.op == CSR_OP_SPMM || p.op == CSR_OP_ATTENTION) {
+            ok = (p.ld_b % v == 0) && (p.ld_out % v == 0) && aligned(p.b, bytes) && aligned(p.out, bytes);
+        } else if (p.op == CSR_OP_SDDMM) {
+            ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && aligned(p.a, bytes) && aligned(p.b, bytes);
+        }
+        if (ok) return v;
+    }
+    return 1;
+}
+
+bool natural_layout(int64_t width, int vec, int* W, int* nv)
+{
+    if (width <= 0 || vec <= 0 || width % vec) return false;
+    const int64_t L = width / vec;
+    if (L <= 64) {
+        *W = (int)next_pow2(L);
+        *nv = 1;
+        return true;
+    }
+    const int n = nv_up((L + 63) / 64);
+    if (n < 0) return false;
+    *W = 64;
+    *nv = n;
+    return true;
+}
+
+int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
+{
+    auto fail = [&](int code, const char* msg) {
+        if (why) *why = msg;
+        return code;
+    };
+    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_MHA) return fail(CSR_ERR_SHAPE, "unknown op");
+    if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "this op takes fp32 operands");
+    if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
+    const int64_t lim = (int64_t)1 << 31;
+    if (p.n_rows < 0 || p.n_cols < 0 || p.nnz < 0) return fail(CSR_ERR_SHAPE, "negative size");
+    if (p.n_rows >= lim - 1 || p.n_cols >= lim || p.nnz >= lim) return fail(CSR_ERR_SHAPE, "sizes must fit int32 indices");
+    if (p.nnz > 0 && p.n_cols == 0) return fail(CSR_ERR_SHAPE, "entries but no columns");
+    if (p.nnz > 0 && p.n_rows == 0) return fail(CSR_ERR_SHAPE, "entries but no rows");
+    if (is_fp32_op(p.op)) {
+        if (p.width < 1 || p.width > 4096) return fail(CSR_ERR_SHAPE, "feature width must be in [1, 4096]");
+        int W, nv;
+        if (!natural_layout(p.width, 1, &W, &nv) && !natural_layout(p.width, 2, &W, &nv) &&
+            !natural_layout(p.width, 4, &W, &nv))
+            return fail(CSR_ERR_SHAPE, "feature width not supported");
+        if (!natural_layout(p.width, max_vec_f32(p), &W, &nv))
+            return fail(CSR_ERR_SHAPE, "feature width too large for the operands' alignment");
+        if (p.op == CSR_OP_SDDMM) {
+            if (p.ld_a < p.width || p.ld_b < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < K");
+        } else {
+            if (p.ld_b < p.width || p.ld_out < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < F");
+        }
+        if (!aligned(p.a, 4) || !aligned(p.b, 4) || !aligned(p.out, 4))
+            return fail(CSR_ERR_ALIGN, "fp32 operands must be 4-byte aligned");
+    } else {
+        if (p.heads < 1) return fail(CSR_ERR_SHAPE, "heads must be >= 1");
+        if (!pow2(p.head_dim) || p.head_dim < 8 || p.head_dim > 512) return fail(CSR_ERR_SHAPE, "head_dim must be a power of two in [8, 512]");
+        if ((int64_t)p.heads * p.head_dim > 512) return fail(CSR_ERR_SHAPE, "heads * head_dim must be <= 512");
+        if (p.width != (int64_t)p.heads * p.head_dim) return fail(CSR_ERR_SHAPE, "width must equal heads * head_dim");
+        if (!aligned(p.a, 16) || !aligned(p.b, 16) || !aligned(p.c, 16) || !aligned(p.out, 16))
+            return fail(CSR_ERR_ALIGN, "Q, K, V and out must be 16-byte aligned");
+    }
+    if ((p.op == CSR_OP_ATTENTION || p.op == CSR_OP_MHA) && !std::isfinite(p.scale))
+        return fail(CSR_ERR_SHAPE, "scale must be finite");
+    if (need_ptrs) {
+        if (!p.row_ptr) return fail(CSR_ERR_NULL, "row_ptr is NULL");
+        if (p.nnz > 0 && !p.col_idx) return fail(CSR_ERR_NULL, "col_idx is NULL");
+        if (p.op != CSR_OP_SPMM && p.nnz > 0 && !p.a) return fail(CSR_ERR_NULL, "operand a is NULL");
+        if (p.nnz > 0 && !p.b) return fail(CSR_ERR_NULL, "operand b is NULL");
+        if (p.op == CSR_OP_MHA && p.nnz > 0 && !p.c) return fail(CSR_ERR_NULL, "V is NULL");
+        if (p.op == CSR_OP_SDDMM ? (p.nnz > 0 && !p.out) : (p.n_rows > 0 && !p.out))
+            return fail(CSR_ERR_NULL, "output is NULL");
+    }
+    return CSR_OK;
+}
+
+int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string* why)
+{
+    auto fail = [&](const char* msg) {
+        if (why) *why = msg;
+        return CSR_ERR_SCHEDULE;
+    };
+    if (s.version != CSR_SCHEDULE_VERSION) return fail("schedule version mismatch");
+    if (s.op != p.op) return fail("schedule is for another op");
+    if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH) return fail("unknown mapping");
+    if (s.flags != 0) return fail("unknown schedule flags");
+    for (int r : s.reserved)
+        if (r != 0) return fail("reserved schedule fields must be 0");
+    if (s.mapping == CSR_MAP_MERGEPATH) {
+        if (s.chunk_items != 256 && s.chunk_items != 512 && s.chunk_items != 1024) return fail("chunk_items must be 256, 512 or 1024");
+        if (s.long_row < 0) return fail("long_row must be >= 0");
+    } else if (s.chunk_items != 0 || s.long_row != 0) {
+        return fail("row-group schedules take chunk_items = long_row = 0");
+    }
+    if (p.op == CSR_OP_MHA) {
+        if (s.vec != 8 || s.passes != 1 || s.group_lanes != p.head_dim / 8) return fail("multi-head layout must be vec 8, W = head_dim / 8, 1 pass");
+        return CSR_OK;
+    }
+    if (s.vec != 1 && s.vec != 2 && s.vec != 4) return fail("vec must be 1, 2 or 4");
+    if (s.vec > max_vec_f32(p) || p.width % s.vec) return fail("vec not allowed by the operands' width or alignment");
+    if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
+    if (!nv_ok(s.passes)) return fail("unsupported pass count");
+    const int64_t per_pass = (int64_t)s.group_lanes * s.vec;
+    if (per_pass * s.passes < p.width) return fail("layout does not cover the feature width");
+    if (s.passes > 1 && per_pass * (s.passes - 1) >= p.width) return fail("layout has an empty pass");
+    return CSR_OK;
+}
+
+int64_t n_chunks_for(const csr_problem_t& p, int items)
+{
+    const int64_t total = p.n_rows + p.nnz;
+    const int64_t n = (total + items - 1) / items;
+    return n < 1 ? 1 : n;
+}
+
+WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
+{
+    WsLayout w{};
+    w.coords = kHeadBytes;
+    w.total = kHeadBytes;
+    if (s.mapping != CSR_MAP_MERGEPATH) return w;
+    const int64_t nc = n_chunks_for(p, s.chunk_items);
+    w.n_chunks = nc;
+    w.carry_row = w.coords + up((size_t)(nc + 1) * 2 * 4);
+    w.carry_ml = w.carry_row + up((size_t)nc * 2 * 4);
+    size_t ml = 0, val = 0;
+    if (p.op == CSR_OP_ATTENTION) {
+        ml = (size_t)nc * 2 * 2 * 4;
+        val = (size_t)nc * 2 * p.width * 4;
+    } else if (p.op == CSR_OP_SPMM) {
+        val = (size_t)nc * 2 * p.width * 4;
+    } else if (p.op == CSR_OP_MHA) {
+        ml = (size_t)nc * 2 * p.heads * 2 * 4;
+        val = (size_t)nc * 2 * p.width * 4;
+    }
+    w.carry_val = w.carry_ml + up(ml);
+    w.total = w.carry_val + up(val);
+    return w;
+}
+
+size_t workspace_bytes(const csr_problem_t& p, const csr_schedule_t& s) { return ws_layout(p, s).total; }
+
+static csr_schedule_t blank(const csr_problem_t& p)
+{
+    csr_schedule_t s;
+    std::memset(&s, 0, sizeof s);
+    s.version = CSR_SCHEDULE_VERSION;
+    s.op = p.op;
+    return s;
+}
+
+csr_schedule_t default_schedule(const csr_problem_t& p)
+{
+    csr_schedule_t s = blank(p);
+    s.mapping = CSR_MAP_MERGEPATH;
+    if (p.op == CSR_OP_MHA) {
+        s.vec = 8;
+        s.group_lanes = p.head_dim / 8;
+        s.passes = 1;
+        s.chunk_items = 256;
+        s.long_row = 0;
+        return s;
+    }
+    s.vec = max_vec_f32(p);
+    int W = 1, nv = 1;
+    natural_layout(p.width, s.vec, &W, &nv);
+    s.group_lanes = W;
+    s.passes = nv;
+    s.chunk_items = 512;
+    const int G = 64 / W;
+    s.long_row = (G > 1) ? G * unroll_for(s.vec, nv) : 0;
+    return s;
+}
+
+std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hist)
+{
+    std::vector<csr_schedule_t> out;
+    const csr_schedule_t d = default_schedule(p);
+    out.push_back(d);
+    const int64_t max_deg = hist ? hist[66] : 0;
+    auto add = [&](csr_schedule_t s) {
+        if (check_schedule(p, s, nullptr) != CSR_OK) return;
+        for (const auto& o : out)
+            if (std::memcmp(&o, &s, sizeof s) == 0) return;
+        out.push_back(s);
+    };
+    csr_schedule_t s = d;
+    s.chunk_items = 256;
+    add(s);
+    s.chunk_items = 1024;
+    add(s);
+    // row-group: one group per row, no partition or fix-up; only when no row
+    // is long enough to leave a tail or a long fp32 accumulation chain
+    if (hist && max_deg <= 4096) {
+        s = d;
+        s.mapping = CSR_MAP_ROWGROUP;
+        s.chunk_items = 0;
+        s.long_row = 0;
+        add(s);
+    }
+    if (p.op != CSR_OP_MHA) {
+        // half the lanes per row, twice the passes: more rows in flight
+        if (d.group_lanes >= 2 && nv_ok(d.passes * 2)) {
+            s = d;
+            s.group_lanes = d.group_lanes / 2;
+            s.passes = d.passes * 2;
+            const int G = 64 / s.group_lanes;
+            s.long_row = G * unroll_for(s.vec, s.passes);
+            add(s);
+        }
+        if (64 / d.group_lanes > 1) {
+            s = d;
+            s.long_row = d.long_row * 4;
+            add(s);
+        }
+    }
+    return out;
+}
+
+double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* hist, const DeviceInfo& dev)
+{
+    // Coarse ranking model: time = HBM bytes / bandwidth (lanes left idle by
+    // the layout inflate the gather traffic) + a latency-bound tail for the
+    // longest row when rows are not split + launch overheads.
+    const double bw = 5.0e12, wave_bw = 8.0e9, launch = 4e-6;
+    const double esize = (p.op == CSR_OP_MHA) ? 2.0 : 4.0;
+    const double gathers = (p.op == CSR_OP_MHA) ? 2.0 : 1.0;
+    const double row_bytes = p.width * esize * gathers;
+    const double lanes_used = (p.op == CSR_OP_MHA) ? 1.0
+        : (double)p.width / ((double)s.group_lanes * s.vec * s.passes);
+    const double bytes = p.nnz * (8.0 + row_bytes / (lanes_used > 0 ? lanes_used : 1.0)) + p.n_rows * p.width * 4.0;
+    double t = bytes / bw;
+    const double max_deg = hist ? (double)hist[66] : 0.0;
+    if (s.mapping == CSR_MAP_ROWGROUP) {
+        t += max_deg * row_bytes / wave_bw;  // one group walks the longest row alone
+        t += launch;
+    } else {
+        const double nc = (double)n_chunks_for(p, s.chunk_items);
+        const double cus = dev.cu_count > 0 ? dev.cu_count : 256.0;
+        t += 3 * launch + nc * 2.0e-9 * 64.0 / cus;  // per-chunk staging and bookkeeping
+        t += s.chunk_items * row_bytes / wave_bw * 0.25;  // chunk-granularity tail
+    }
+    return t;
+}
+
+uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev)
+{
+    uint64_t h = 0xcbf29ce484222325ull;
+    fnv(h, 0x43535253);  // 'CSRS'
+    fnv(h, kLibVersion);
+    fnv(h, p.op);
+    fnv(h, p.dtype);
+    fnv(h, p.n_rows);
+    fnv(h, p.n_cols);
+    fnv(h, p.nnz);
+    fnv(h, p.width);
+    fnv(h, p.op == CSR_OP_MHA ? p.heads : 0);
+    fnv(h, p.op == CSR_OP_MHA ? p.head_dim : 0);
+    fnv(h, p.op == CSR_OP_MHA ? 8 : max_vec_f32(p));
+    fnv(h, dev.cu_count);
+    fnv(h, dev.arch);
+    for (int i = 0; i < kHistInts; ++i) fnv(h, hist ? hist[i] : 0);
+    return h;
+}
+
+std::string format_cache_line(uint64_t sig, const csr_schedule_t& s, double probe_us)
+{
+    char buf[256];
+    std::snprintf(buf, sizeof buf,
+                  "csrsa-cache v%d %016llx op=%d map=%d vec=%d w=%d nv=%d chunk=%d long=%d flags=%d us=%.3f\n",
+                  CSR_SCHEDULE_VERSION, (unsigned long long)sig, s.op, s.mapping, s.vec, s.group_lanes, s.passes,
+                  s.chunk_items, s.long_row, s.flags, probe_us);
+    return buf;
+}
+
+bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s, double* probe_us)
+{
+    int ver = 0, n = 0;
+    unsigned long long sg = 0;
+    csr_schedule_t t;
+    std::memset(&t, 0, sizeof t);
+    double us = 0;
+    const int got = std::sscanf(line.c_str(),
+                                "csrsa-cache v%d %16llx op=%d map=%d vec=%d w=%d nv=%d chunk=%d long=%d flags=%d us=%lf%n",
+                                &ver, &sg, &t.op, &t.mapping, &t.vec, &t.group_lanes, &t.passes, &t.chunk_items,
+                                &t.long_row, &t.flags, &us, &n);
+    if (got != 11 || ver != CSR_SCHEDULE_VERSION) return false;
+    for (size_t i = (size_t)n; i < line.size(); ++i)
+        if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
+    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_MHA) return false;
+    if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH) return false;
+    t.version = CSR_SCHEDULE_VERSION;
+    *sig = sg;
+    *s = t;
+    if (probe_us) *probe_us = us;
+    return true;
+}
+
+}  // namespace csrh

@@ -1,0 +1,71 @@
+// Host-side runtime: problem checks, lane layouts, workspace layout, schedule
+// validation, signature and cost model.  Nothing here touches the GPU, so the
+// selector logic can be exercised on a machine without one.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/csrsa.h"
+
+namespace csrh {
+
+constexpr int kLibVersion = 1;
+constexpr int kHistInts = 67;    // counts[33], sums[33], max degree
+constexpr size_t kAlign = 256;   // workspace region alignment
+constexpr size_t kHeadBytes = 1024;  // workspace head: histogram / validation scratch
+
+struct DeviceInfo {
+    int cu_count = 0;   // 0 for a host-only context
+    int arch = 0;       // 950 for gfx950, 0 unknown
+};
+
+// Largest fp32 vector width (1, 2, 4) that the operands' alignment allows.
+int max_vec_f32(const csr_problem_t& p);
+
+// Checks the shape, dtype and pointer fields of p for its op.  need_ptrs:
+// operand pointers must be non-null.  Returns CSR_OK or an error code and a
+// message in *why.
+int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why);
+
+// The natural lane layout of a row of `width` fp32 values read `vec` at a
+// time: W = lanes per group, nv = passes.  Returns false if unsupported.
+bool natural_layout(int64_t width, int vec, int* W, int* nv);
+
+// Validates schedule s against problem p (CSR_OK or CSR_ERR_SCHEDULE + why).
+int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string* why);
+
+// Bytes of workspace needed by schedule s (s must be valid for p).
+size_t workspace_bytes(const csr_problem_t& p, const csr_schedule_t& s);
+
+// Merge-path chunk count for items_per_chunk.
+int64_t n_chunks_for(const csr_problem_t& p, int items_per_chunk);
+
+// Workspace regions of a merge-path schedule.
+struct WsLayout {
+    size_t coords, carry_row, carry_ml, carry_val, total;
+    int64_t n_chunks;
+};
+WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s);
+
+// The safe default schedule (the guardrail's fallback).
+csr_schedule_t default_schedule(const csr_problem_t& p);
+
+// Candidate schedules for the auto path, in fixed priority order (the first
+// is the default).  hist may be null (no degree information).
+std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hist);
+
+// Cost-model estimate (arbitrary time units, lower is better) of schedule s
+// on problem p with degree histogram hist.
+double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* hist, const DeviceInfo& dev);
+
+// FNV-1a 64 signature of (problem shape, alignment class, histogram, device).
+uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev);
+
+// Cache log line format.
+std::string format_cache_line(uint64_t sig, const csr_schedule_t& s, double probe_us);
+bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s, double* probe_us);
+
+}  // namespace csrh

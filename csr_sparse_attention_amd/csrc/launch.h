@@ -1,0 +1,51 @@
+// Host-side launchers of the templated kernels (one translation unit per op).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "args.h"
+
+namespace csrk {
+
+// Feature passes per lane that have a kernel instantiation.
+inline bool nv_supported(int nv)
+{
+    switch (nv) {
+    case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 12: case 16: return true;
+    default: return false;
+    }
+}
+inline int nv_round_up(int nv)
+{
+    static const int s[] = {1, 2, 3, 4, 5, 6, 8, 12, 16};
+    for (int v : s)
+        if (v >= nv) return v;
+    return -1;
+}
+inline bool chunk_supported(int d) { return d == 256 || d == 512 || d == 1024; }
+
+// Entries in flight per lane group, from the registers one entry needs.
+constexpr int unroll_for(int vec, int nv)
+{
+    return (vec * nv <= 2) ? 8 : (vec * nv <= 8) ? 4 : (vec * nv <= 16) ? 2 : 1;
+}
+
+// Returns hipSuccess or the launch error.  mapping: 1 row-group, 2 merge path
+// (main pass; the fix-up is launched separately).
+hipError_t launch_spmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_spmm_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
+hipError_t launch_attention(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_attention_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
+hipError_t launch_sddmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_mha(int mapping, int lph, int chunk, const MhaArgs& a, hipStream_t s);
+hipError_t launch_mha_fixup(int lph, const MhaArgs& a, hipStream_t s);
+
+// Structure kernels.
+hipError_t launch_fill_i64(int64_t* p, int64_t n, int64_t value, hipStream_t s);
+hipError_t launch_degree_hist(const int32_t* row_ptr, int64_t n_rows, int64_t* out, hipStream_t s);
+hipError_t launch_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz, int64_t items,
+                             int64_t n_chunks, int32_t* coords, hipStream_t s);
+hipError_t launch_validate(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows,
+                           int64_t n_cols, int64_t nnz, int64_t* bad, hipStream_t s);
+
+} // namespace csrk

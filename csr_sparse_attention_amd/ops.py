@@ -1,0 +1,380 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Tensors are passed to the library as device pointers together with their
+sizes and leading dimensions; torch provides the memory (outputs and the
+workspace) and the current HIP stream.  Every computation happens in
+libcsrsa.so; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+from . import _ffi
+from ._ffi import CsrError, CsrProblem, CsrSchedule
+
+_lock = threading.Lock()
+_contexts: dict = {}
+_workspaces: dict = {}
+
+
+def _lib():
+    return _ffi.load()
+
+
+def _check(rc: int, where: str, ctx=None):
+    if rc != _ffi.CSR_OK:
+        msg = ""
+        if ctx is not None:
+            m = _lib().csr_last_error(ctx.handle)
+            msg = m.decode() if m else ""
+        raise CsrError(rc, where, msg)
+
+
+class Context:
+    """A library context on one device: schedule cache (optionally persisted
+    to ``cache_path``) and the pinned buffer of the auto-select path."""
+
+    def __init__(self, device: int = 0, cache_path: Optional[str] = None, flags: int = 0):
+        self.device = device
+        self.cache_path = cache_path
+        h = ctypes.c_void_p()
+        path = cache_path.encode() if cache_path else None
+        rc = _lib().csr_context_create(ctypes.byref(h), device, path, flags)
+        if rc != _ffi.CSR_OK:
+            raise CsrError(rc, "csr_context_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _lib().csr_context_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover - interpreter shutdown order
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def cache_info(self):
+        e, s, io = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(_lib().csr_cache_info(self.handle, ctypes.byref(e), ctypes.byref(s), ctypes.byref(io)),
+               "csr_cache_info", self)
+        return {"entries": e.value, "skipped_lines": s.value, "io_errors": io.value}
+
+    def cache_lookup(self, signature: int) -> Optional[CsrSchedule]:
+        s = CsrSchedule()
+        rc = _lib().csr_cache_lookup(self.handle, ctypes.c_uint64(signature), ctypes.byref(s))
+        if rc == _ffi.CSR_ERR_NO_CACHE_ENTRY:
+            return None
+        _check(rc, "csr_cache_lookup", self)
+        return s
+
+    def cache_store(self, signature: int, sched: CsrSchedule):
+        _check(_lib().csr_cache_store(self.handle, ctypes.c_uint64(signature), ctypes.byref(sched)),
+               "csr_cache_store", self)
+
+    def cache_flush(self):
+        _check(_lib().csr_cache_flush(self.handle), "csr_cache_flush", self)
+
+
+def default_context(device: Optional[int] = None) -> Context:
+    """The per-device context used when none is given.  Its cache log is the
+    file named by the environment variable CSRSA_CACHE (in memory if unset)."""
+    if device is None:
+        device = torch.cuda.current_device()
+    with _lock:
+        ctx = _contexts.get(device)
+        if ctx is None:
+            ctx = Context(device, os.environ.get("CSRSA_CACHE") or None)
+            _contexts[device] = ctx
+        return ctx
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A cached device buffer of at least nbytes (256-byte aligned)."""
+    key = device.index
+    with _lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes + 256:
+            ws = torch.empty(max(nbytes + 256, 1 << 20), dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+    off = (-ws.data_ptr()) % 256
+    return ws[off:]
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dense(t: torch.Tensor, name: str, dtype) -> int:
+    """Leading dimension of a row-major 2-D operand (inner stride 1)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit inner stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _pattern(row_ptr: torch.Tensor, col_idx: torch.Tensor):
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    return row_ptr.numel() - 1, col_idx.numel()
+
+
+def _sched_arg(schedule: Optional[CsrSchedule]):
+    return None if schedule is None else ctypes.byref(schedule)
+
+
+# ---------------------------------------------------------------------------
+# problems (shared by the calls, select() and workspace_size())
+# ---------------------------------------------------------------------------
+
+def _problem(op: int, row_ptr, col_idx, a, b, c, out, *, n_cols, width, ld_a=0, ld_b=0, ld_out=0,
+             heads=0, head_dim=0, scale=1.0) -> CsrProblem:
+    p = CsrProblem()
+    p.op = op
+    p.dtype = _ffi.DTYPE_BF16 if op == _ffi.OP_MHA else _ffi.DTYPE_F32
+    p.n_rows = row_ptr.numel() - 1
+    p.n_cols = n_cols
+    p.nnz = col_idx.numel()
+    p.width = width
+    p.heads, p.head_dim = heads, head_dim
+    p.ld_a, p.ld_b, p.ld_out = ld_a, ld_b, ld_out
+    p.row_ptr, p.col_idx = _ptr(row_ptr), _ptr(col_idx)
+    p.a, p.b, p.c, p.out = _ptr(a), _ptr(b), _ptr(c), _ptr(out)
+    p.scale = scale
+    return p
+
+
+def _spmm_problem(row_ptr, col_idx, vals, X, out):
+    ldx = _dense(X, "X", torch.float32)
+    ldy = _dense(out, "out", torch.float32)
+    return _problem(_ffi.OP_SPMM, row_ptr, col_idx, vals, X, None, out, n_cols=X.shape[0],
+                    width=X.shape[1], ld_b=ldx, ld_out=ldy)
+
+
+def _sddmm_problem(row_ptr, col_idx, U, V, out):
+    ldu = _dense(U, "U", torch.float32)
+    ldv = _dense(V, "V", torch.float32)
+    if U.shape[1] != V.shape[1]:
+        raise ValueError("U and V must have the same width")
+    return _problem(_ffi.OP_SDDMM, row_ptr, col_idx, U, V, None, out, n_cols=V.shape[0],
+                    width=U.shape[1], ld_a=ldu, ld_b=ldv)
+
+
+def _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale):
+    ldv = _dense(node_value, "node_value", torch.float32)
+    ldo = _dense(out, "out", torch.float32)
+    return _problem(_ffi.OP_ATTENTION, row_ptr, col_idx, edge_scores, node_value, None, out,
+                    n_cols=node_value.shape[0], width=node_value.shape[1], ld_b=ldv, ld_out=ldo,
+                    scale=scale)
+
+
+def _mha_problem(row_ptr, col_idx, Q, K, V, out, scale):
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor [n, heads, head_dim]")
+    H, D = Q.shape[1], Q.shape[2]
+    if K.shape[1:] != (H, D) or V.shape[1:] != (H, D) or K.shape[0] != V.shape[0]:
+        raise ValueError("Q, K, V shapes do not match")
+    return _problem(_ffi.OP_MHA, row_ptr, col_idx, Q, K, V, out, n_cols=K.shape[0], width=H * D,
+                    heads=H, head_dim=D, scale=scale)
+
+
+def _run(problem: CsrProblem, device, schedule, ctx, call):
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    nbytes = ctypes.c_size_t()
+    _check(lib.csr_workspace_size(ctx.handle, ctypes.byref(problem), _sched_arg(schedule), ctypes.byref(nbytes)),
+           "csr_workspace_size", ctx)
+    ws = _workspace(device, nbytes.value)
+    rc = call(ctx, ws, nbytes.value, _stream(device))
+    _check(rc, "csr call", ctx)
+
+
+# ---------------------------------------------------------------------------
+# public calls
+# ---------------------------------------------------------------------------
+
+def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule] = None,
+         ctx: Optional[Context] = None) -> torch.Tensor:
+    """Y = A X for the CSR matrix A (row_ptr, col_idx, vals; vals=None means 1)."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    if out is None:
+        out = torch.empty((n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
+    if vals is not None and (vals.dtype != torch.float32 or vals.numel() != nnz or not vals.is_contiguous()):
+        raise ValueError("vals must be a contiguous fp32 tensor with one value per entry")
+    p = _spmm_problem(row_ptr, col_idx, vals, X, out)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_spmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
+                               p.width, p.ld_b, p.out, p.ld_out, _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _run(p, X.device, schedule, ctx, call)
+    return out
+
+
+def sddmm(row_ptr, col_idx, U, V, *, out=None, schedule: Optional[CsrSchedule] = None,
+          ctx: Optional[Context] = None) -> torch.Tensor:
+    """out[e] = <U[row(e)], V[col_idx[e]]> for every stored entry e."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    if out is None:
+        out = torch.empty(nnz, dtype=torch.float32, device=U.device)
+    if out.dtype != torch.float32 or out.numel() != nnz or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor with one value per entry")
+    p = _sddmm_problem(row_ptr, col_idx, U, V, out)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_sddmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.ld_a,
+                                p.b, p.ld_b, p.width, p.out, _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _run(p, U.device, schedule, ctx, call)
+    return out
+
+
+def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, out=None,
+              schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None) -> torch.Tensor:
+    """Fused CSR attention with given scores: per row, softmax over the row's
+    entries of scale * edge_scores, then the weighted sum of node_value rows
+    (zero for rows without entries).  Arguments in the order row_ptr,
+    col_idx, edge_scores, node_value."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    if edge_scores.dtype != torch.float32 or edge_scores.numel() != nnz or not edge_scores.is_contiguous():
+        raise ValueError("edge_scores must be a contiguous fp32 tensor with one score per entry")
+    if out is None:
+        out = torch.empty((n_rows, node_value.shape[1]), dtype=torch.float32, device=node_value.device)
+    p = _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_attention(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
+                                    p.width, p.ld_b, ctypes.c_float(scale), p.out, p.ld_out,
+                                    _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _run(p, node_value.device, schedule, ctx, call)
+    return out
+
+
+def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, out=None,
+                  schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None) -> torch.Tensor:
+    """Multi-head fused CSR attention: bf16 Q [n_rows, H, D], K, V [n_cols, H, D];
+    per head, softmax over the row's entries of scale * <Q_i, K_j>, times V.
+    Returns fp32 [n_rows, H, D].  scale defaults to 1/sqrt(D)."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    H, D = Q.shape[1], Q.shape[2]
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((n_rows, H, D), dtype=torch.float32, device=Q.device)
+    p = _mha_problem(row_ptr, col_idx, Q, K, V, out, scale)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_mha_attention(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
+                                        p.c, H, D, ctypes.c_float(scale), p.out, _sched_arg(schedule),
+                                        ws.data_ptr(), nb, st)
+
+    _run(p, Q.device, schedule, ctx, call)
+    return out
+
+
+def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0) -> CsrProblem:
+    """The csr_problem_t of a call, for select() / workspace_size() /
+    default_schedule(): op is 'spmm' (vals, X), 'sddmm' (U, V), 'attention'
+    (edge_scores, node_value) or 'mha' (Q, K, V)."""
+    _pattern(row_ptr, col_idx)
+    n_rows = row_ptr.numel() - 1
+    if op == "spmm":
+        vals, X = operands
+        out = out if out is not None else torch.empty((n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
+        return _spmm_problem(row_ptr, col_idx, vals, X, out), out
+    if op == "sddmm":
+        U, V = operands
+        out = out if out is not None else torch.empty(col_idx.numel(), dtype=torch.float32, device=U.device)
+        return _sddmm_problem(row_ptr, col_idx, U, V, out), out
+    if op == "attention":
+        s, nv = operands
+        out = out if out is not None else torch.empty((n_rows, nv.shape[1]), dtype=torch.float32, device=nv.device)
+        return _attention_problem(row_ptr, col_idx, s, nv, out, scale), out
+    if op == "mha":
+        Q, K, V = operands
+        out = out if out is not None else torch.empty((n_rows,) + tuple(Q.shape[1:]), dtype=torch.float32,
+                                                       device=Q.device)
+        return _mha_problem(row_ptr, col_idx, Q, K, V, out, scale), out
+    raise ValueError(op)
+
+
+def select(op: str, row_ptr, col_idx, *operands, mode: str = "auto", scale: float = 1.0, out=None,
+           ctx: Optional[Context] = None):
+    """Runs the selector for a call; returns (schedule, signature).  With
+    mode 'auto' or 'probe' the candidates run on the given operands and write
+    ``out``."""
+    p, out = make_problem(op, row_ptr, col_idx, *operands, out=out, scale=scale)
+    device = row_ptr.device
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    nbytes = ctypes.c_size_t()
+    _check(lib.csr_workspace_size(ctx.handle, ctypes.byref(p), None, ctypes.byref(nbytes)), "csr_workspace_size", ctx)
+    ws = _workspace(device, nbytes.value)
+    p.workspace, p.workspace_bytes, p.stream = ws.data_ptr(), nbytes.value, _stream(device)
+    s, sig = CsrSchedule(), ctypes.c_uint64()
+    _check(lib.csr_select(ctx.handle, ctypes.byref(p), _ffi.SELECT_MODES[mode], ctypes.byref(s), ctypes.byref(sig)),
+           "csr_select", ctx)
+    return s, sig.value
+
+
+def default_schedule(problem: CsrProblem) -> CsrSchedule:
+    s = CsrSchedule()
+    _check(_lib().csr_default_schedule(None, ctypes.byref(problem), ctypes.byref(s)), "csr_default_schedule")
+    return s
+
+
+def workspace_size(problem: CsrProblem, schedule: Optional[CsrSchedule] = None) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib().csr_workspace_size(None, ctypes.byref(problem), _sched_arg(schedule), ctypes.byref(n)),
+           "csr_workspace_size")
+    return n.value
+
+
+def signature(problem: CsrProblem, histogram, ctx: Optional[Context] = None) -> int:
+    h = (ctypes.c_int64 * 67)(*[int(v) for v in histogram])
+    out = ctypes.c_uint64()
+    _check(_lib().csr_signature(ctx.handle if ctx else None, ctypes.byref(problem), h, ctypes.byref(out)),
+           "csr_signature")
+    return out.value
+
+
+def degree_histogram(row_ptr, *, ctx: Optional[Context] = None):
+    """(counts[33], degree sums[33], max degree) of a device CSR row_ptr."""
+    _pattern(row_ptr, row_ptr)
+    device = row_ptr.device
+    ctx = ctx or default_context(device.index)
+    out = (ctypes.c_int64 * 67)()
+    ws = _workspace(device, 1024)
+    _check(_lib().csr_degree_histogram(ctx.handle, row_ptr.numel() - 1, row_ptr.data_ptr(), out, ws.data_ptr(),
+                                       1024, _stream(device)), "csr_degree_histogram", ctx)
+    vals = list(out)
+    return vals[:33], vals[33:66], vals[66]
+
+
+def merge_path_partition(row_ptr, nnz: int, items_per_chunk: int, *, ctx: Optional[Context] = None):
+    """Device int32 tensor [n_chunks + 1, 2] of (rows ended, entries consumed)."""
+    device = row_ptr.device
+    ctx = ctx or default_context(device.index)
+    n_rows = row_ptr.numel() - 1
+    n_chunks = max(1, -(-(n_rows + nnz) // items_per_chunk))
+    coords = torch.empty((n_chunks + 1, 2), dtype=torch.int32, device=device)
+    _check(_lib().csr_merge_path_partition(ctx.handle, n_rows, nnz, row_ptr.data_ptr(), items_per_chunk,
+                                           coords.data_ptr(), _stream(device)), "csr_merge_path_partition", ctx)
+    return coords

@@ -1,0 +1,325 @@
+/*
+ * csrsa.h - C ABI of an MI355X (gfx950) library for CSR sparse aggregation:
+ * SpMM, SDDMM and softmax attention over a CSR pattern, with an input-aware
+ * schedule selector and a persistent schedule cache.
+ *
+ * The operations are those of "AutoSAGE: Input-Aware CUDA Scheduling for
+ * Sparse GNN Aggregation (SpMM/SDDMM) and CSR Attention" (Abstract): CSR SpMM,
+ * CSR SDDMM, and their composition into a CSR attention pipeline
+ * SDDMM -> row-softmax -> SpMM; a scheduler picks tiling and mapping per input
+ * from a cheap estimate refined by on-device micro-probes, falls back to a
+ * safe default, and keeps its choices in a persistent cache so that runs
+ * replay deterministically.  The argument order and the edge-case rules of
+ * the attention call follow the fused sparse attention-value aggregation task
+ * on the POPCORNBENCH trace page (task statement; its host wrapper and final
+ * kernel): row_ptr, col_idx, edge_scores, node_value; rows are destination
+ * nodes, col_idx holds the source node of each incoming edge, the number of
+ * nodes is len(row_ptr) - 1, the feature width is node_value's second
+ * dimension, and a node without incoming edges gets a zero output row.
+ *
+ * Conventions for every call below
+ *  - Pointers named row_ptr, col_idx, vals, X, U, V, Q, K, edge_scores,
+ *    node_value, out, Y and workspace are DEVICE pointers (memory of the GPU
+ *    the context was created on).  Every other pointer is a host pointer.
+ *  - row_ptr: int32 [n_rows + 1], row_ptr[0] = 0, non-decreasing,
+ *    row_ptr[n_rows] = nnz.  col_idx: int32 [nnz], each in [0, n_cols).
+ *    Columns need not be sorted or unique; every stored entry counts once
+ *    (duplicates add in SpMM and are separate terms of a row's softmax).
+ *    The library never writes row_ptr or col_idx (they pass through bit-exact).
+ *  - Dense matrices are row-major with a leading dimension (elements between
+ *    consecutive rows) >= their width.  Index arithmetic is 64-bit, so a
+ *    dense operand may exceed 2^31 elements; nnz must be < 2^31.
+ *  - Outputs are fully overwritten (including zero rows for rows without
+ *    entries); no pre-zeroing is needed.  Inputs are never modified.
+ *  - The caller owns all memory.  The library allocates no device memory on
+ *    the call path; temporary storage comes from the caller's workspace,
+ *    sized with csr_workspace_size().  The auto-select path also uses a small
+ *    pinned host buffer owned by the context.
+ *  - stream is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously.  Only the auto-select path (sched == NULL) and the
+ *    calls marked "synchronous" wait on the stream.
+ *  - Every call returns a csr_status (0 = CSR_OK).  No C++ exception or abort
+ *    crosses the ABI.  On error nothing has been written to the outputs
+ *    unless stated; csr_last_error() gives a message.
+ *  - Calls on one context are serialised by an internal mutex.
+ */
+#ifndef CSRSA_H
+#define CSRSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSRSA_ABI_VERSION 1
+#define CSR_SCHEDULE_VERSION 1
+
+typedef struct csr_context_s* csr_context_t;
+
+enum csr_status {
+    CSR_OK = 0,
+    CSR_ERR_NULL = -1,           /* a required pointer is NULL */
+    CSR_ERR_SHAPE = -2,          /* a size or leading dimension is invalid or unsupported */
+    CSR_ERR_DTYPE = -3,          /* unsupported element type */
+    CSR_ERR_ALIGN = -4,          /* misaligned pointer or leading dimension */
+    CSR_ERR_WORKSPACE = -5,      /* workspace missing or too small */
+    CSR_ERR_INVALID_CSR = -6,    /* CSR validation failed (context flag CSR_CTX_VALIDATE) */
+    CSR_ERR_SCHEDULE = -7,       /* schedule invalid for this problem */
+    CSR_ERR_NO_CACHE_ENTRY = -8, /* CSR_SELECT_REPLAY_ONLY and no cached schedule */
+    CSR_ERR_CACHE_IO = -9,       /* cache file could not be read or written */
+    CSR_ERR_HIP = -10,           /* a HIP runtime call failed */
+    CSR_ERR_DEVICE = -11,        /* no usable gfx950 device */
+    CSR_ERR_INTERNAL = -12
+};
+
+enum csr_op {
+    CSR_OP_SPMM = 1,      /* Y = A X */
+    CSR_OP_SDDMM = 2,     /* out_e = <U[row_e], V[col_e]> */
+    CSR_OP_ATTENTION = 3, /* scores given: out = softmax_row(scale * S) V */
+    CSR_OP_MHA = 4        /* multi-head, scores = scale * <Q_i, K_j> per head */
+};
+
+enum csr_dtype { CSR_DTYPE_F32 = 0, CSR_DTYPE_BF16 = 1 };
+
+/* Row mappings (the "mapping" half of a schedule). */
+enum csr_mapping {
+    CSR_MAP_ROWGROUP = 1,  /* a group of W lanes per row, lanes across the feature width */
+    CSR_MAP_MERGEPATH = 2  /* nnz-balanced merge-path chunks per wavefront; col_idx and
+                              edge values staged in LDS; split rows combined by a
+                              deterministic fix-up pass */
+};
+
+/* Context flags. */
+enum csr_ctx_flags {
+    CSR_CTX_VALIDATE = 1u,   /* check row_ptr / col_idx on every call (one extra pass) */
+    CSR_CTX_NO_PROBE = 2u    /* never run micro-probes: cost model only */
+};
+
+/* Selection modes for csr_select(). */
+enum csr_select_mode {
+    CSR_SELECT_AUTO = 0,        /* cache hit -> replay; miss -> estimate + probes, then store */
+    CSR_SELECT_REPLAY_ONLY = 1, /* cache only; CSR_ERR_NO_CACHE_ENTRY on a miss */
+    CSR_SELECT_FORCE_PROBE = 2, /* ignore the cache, probe, store (replaces the entry) */
+    CSR_SELECT_ESTIMATE = 3     /* cost model only, nothing stored */
+};
+
+/*
+ * A schedule: plain data, 64 bytes, safe to copy, store and compare with
+ * memcmp.  Obtain one from csr_select() or csr_default_schedule(); passing
+ * a schedule back replays it without any host-side work beyond argument
+ * checks.  Fields are validated against the problem on every call
+ * (CSR_ERR_SCHEDULE if they do not fit).
+ */
+typedef struct csr_schedule_s {
+    int32_t version;     /* CSR_SCHEDULE_VERSION */
+    int32_t op;          /* enum csr_op */
+    int32_t mapping;     /* enum csr_mapping */
+    int32_t vec;         /* elements per lane access: 1, 2, 4 (fp32), 8 (bf16) */
+    int32_t group_lanes; /* W: lanes per row group, power of two in [1, 64] */
+    int32_t passes;      /* feature passes per lane (width = W * vec * passes, rounded) */
+    int32_t chunk_items; /* merge-path: rows + entries per wavefront chunk (256, 512, 1024) */
+    int32_t long_row;    /* merge-path: a row segment this long is shared by the whole wave */
+    int32_t flags;       /* reserved, 0 */
+    int32_t reserved[7]; /* 0 */
+} csr_schedule_t;
+
+/*
+ * A problem description: the same fields as the operation calls, used by
+ * csr_select() and csr_workspace_size().  Unused pointers may be NULL for
+ * csr_workspace_size().
+ *   op = CSR_OP_SPMM:      a = vals (fp32 [nnz], NULL = all ones), b = X, width = F,
+ *                          ld_b = ldx, out = Y, ld_out = ldy
+ *   op = CSR_OP_SDDMM:     a = U [n_rows, K], ld_a = ldu, b = V [n_cols, K], ld_b = ldv,
+ *                          width = K, out = fp32 [nnz]
+ *   op = CSR_OP_ATTENTION: a = edge_scores fp32 [nnz], b = node_value [n_cols, F],
+ *                          ld_b, width = F, out [n_rows, F], ld_out, scale
+ *   op = CSR_OP_MHA:       a = Q, b = K, c = V (bf16 [n, heads, head_dim]), heads,
+ *                          head_dim, width = heads * head_dim, out fp32 [n_rows, width],
+ *                          scale
+ */
+typedef struct csr_problem_s {
+    int32_t op;
+    int32_t dtype;
+    int64_t n_rows, n_cols, nnz;
+    int64_t width;
+    int32_t heads, head_dim;
+    int64_t ld_a, ld_b, ld_out;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const void* a;
+    const void* b;
+    const void* c;
+    void* out;
+    float scale;
+    int32_t pad_;
+    void* workspace;
+    size_t workspace_bytes;
+    void* stream;
+} csr_problem_t;
+
+/* ---------------------------------------------------------------------------
+ * Context
+ * ------------------------------------------------------------------------- */
+
+/* Creates a context on HIP device `device` (must be gfx950), or a host-only
+ * context for device = -1 (cache and host-side calls only; operations return
+ * CSR_ERR_DEVICE).  cache_path:
+ * the persistent schedule cache, an append-only text log (NULL = in-memory
+ * only).  An existing log is loaded; malformed or foreign-version lines are
+ * skipped.  flags: enum csr_ctx_flags.  The context owns a 4 KiB pinned host
+ * buffer and the in-memory cache. */
+int csr_context_create(csr_context_t* ctx, int device, const char* cache_path, uint32_t flags);
+
+/* Flushes the cache log and frees the context.  NULL is accepted. */
+int csr_context_destroy(csr_context_t ctx);
+
+/* Static message for a status code. */
+const char* csr_status_string(int status);
+
+/* Message of the last failed call on this context (valid until the next call). */
+const char* csr_last_error(csr_context_t ctx);
+
+/* ---------------------------------------------------------------------------
+ * Operations
+ *
+ * sched: NULL selects a schedule automatically (degree histogram on the device,
+ * a stream synchronisation to read it, cache lookup, and on a miss cost model
+ * plus micro-probes that run the operation itself on the caller's operands);
+ * otherwise the given schedule is replayed with no synchronisation.
+ * workspace / ws_bytes: device scratch of at least csr_workspace_size() bytes
+ * for this problem and schedule (for sched == NULL: the size reported for a
+ * NULL schedule, which covers every candidate).  256-byte alignment required.
+ * ------------------------------------------------------------------------- */
+
+/* SpMM (AutoSAGE page, Abstract: CSR SpMM):
+ *   Y[i, f] = sum over stored entries e of row i of vals[e] * X[col_idx[e], f]
+ * vals: fp32 [nnz] or NULL (all ones).  X: fp32 [n_cols, ldx], F <= ldx.
+ * Y: fp32 [n_rows, ldy], F <= ldy.  1 <= F <= 4096. */
+int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+             const int32_t* row_ptr, const int32_t* col_idx, const float* vals,
+             const float* X, int64_t F, int64_t ldx, float* Y, int64_t ldy,
+             const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
+
+/* SDDMM (AutoSAGE page, Abstract: CSR SDDMM):
+ *   out[e] = sum over k < K of U[i, k] * V[col_idx[e], k] for every stored
+ *   entry e of row i, in CSR order.
+ * U: fp32 [n_rows, ldu], V: fp32 [n_cols, ldv], out: fp32 [nnz].  1 <= K <= 4096. */
+int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+              const int32_t* row_ptr, const int32_t* col_idx,
+              const float* U, int64_t ldu, const float* V, int64_t ldv, int64_t K,
+              float* out, const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
+              void* stream);
+
+/* Fused CSR attention with given edge scores (AutoSAGE page, Abstract: the
+ * SDDMM -> row-softmax -> SpMM pipeline; POPCORNBENCH trace page, task
+ * statement: argument order row_ptr, col_idx, edge_scores, node_value):
+ *   for row i with entries E_i: t_e = scale * edge_scores[e],
+ *   p_e = exp(t_e - max t) / sum over E_i of exp(t - max t),
+ *   out[i, f] = sum over e in E_i of p_e * node_value[col_idx[e], f];
+ *   out[i, :] = 0 when E_i is empty.
+ * edge_scores: fp32 [nnz].  node_value: fp32 [n_cols, ldv].  out: fp32
+ * [n_rows, ldo].  scale: finite (1.0 = no scaling).  1 <= F <= 4096. */
+int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                  const int32_t* row_ptr, const int32_t* col_idx, const float* edge_scores,
+                  const float* node_value, int64_t F, int64_t ldv, float scale,
+                  float* out, int64_t ldo, const csr_schedule_t* sched,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Multi-head fused CSR attention, SDDMM -> row-softmax -> SpMM in one pass
+ * (AutoSAGE page, Abstract: CSR attention pipeline), bf16 inputs, fp32
+ * accumulation and output.  For each head h and row i:
+ *   t_e = scale * sum over d of Q[i, h, d] * K[col_idx[e], h, d],
+ *   p_e = softmax over the row's entries of t,
+ *   out[i, h, d] = sum over e of p_e * V[col_idx[e], h, d]; zero for empty rows.
+ * Q: bf16 [n_rows, heads, head_dim]; K, V: bf16 [n_cols, heads, head_dim]
+ * (raw bfloat16 bit patterns, contiguous); out: fp32 [n_rows, heads, head_dim].
+ * head_dim in {8, 16, 32, 64, 128, 256, 512}, heads * head_dim <= 512,
+ * 16-byte aligned pointers. */
+int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                      const int32_t* row_ptr, const int32_t* col_idx,
+                      const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                      int32_t heads, int32_t head_dim, float scale, float* out,
+                      const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Schedule selection and cache (AutoSAGE page, Abstract: input-aware choice
+ * refined by on-device micro-probes, guarded fallback, persistent cache for
+ * deterministic replay).
+ * ------------------------------------------------------------------------- */
+
+/* Selects a schedule for problem p (all operand pointers, workspace and stream
+ * must be set unless mode == CSR_SELECT_REPLAY_ONLY or CSR_SELECT_ESTIMATE).
+ * Probing runs the operation on p's operands and writes p->out.
+ * signature (may be NULL) receives the 64-bit input signature: FNV-1a over
+ * the problem shape, the degree histogram and the device identity.
+ * Synchronous. */
+int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode,
+               csr_schedule_t* out, uint64_t* signature);
+
+/* The library's safe default schedule for p (the fallback when probing fails):
+ * needs only the shape fields (and the operand pointers for their alignment).
+ * Host-only; ctx may be NULL. */
+int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule_t* out);
+
+/* Workspace bytes needed for p under schedule sched (NULL = automatic
+ * selection, covering every candidate).  Host-only; ctx may be NULL; needs
+ * only the shape fields of p (and the operand pointers for their alignment). */
+int csr_workspace_size(csr_context_t ctx, const csr_problem_t* p, const csr_schedule_t* sched,
+                       size_t* bytes);
+
+/* Appends to the log every in-memory entry that is not yet in it (entries
+ * whose earlier append failed).  CSR_ERR_CACHE_IO if an append fails again. */
+int csr_cache_flush(csr_context_t ctx);
+
+/* Cache statistics (host-only; any pointer may be NULL): number of entries,
+ * log lines skipped at load (malformed, truncated or of another schema
+ * version), failed log appends. */
+int csr_cache_info(csr_context_t ctx, int64_t* entries, int64_t* skipped_lines, int64_t* io_errors);
+
+/* Looks up / stores the schedule cached for a signature (host-only).  A store
+ * replaces the in-memory entry and appends one log line; on reload the last
+ * valid line of a signature wins.  Store returns CSR_ERR_CACHE_IO when the
+ * append fails (the entry is kept in memory). */
+int csr_cache_lookup(csr_context_t ctx, uint64_t signature, csr_schedule_t* out);
+int csr_cache_store(csr_context_t ctx, uint64_t signature, const csr_schedule_t* sched);
+
+/* ---------------------------------------------------------------------------
+ * Building blocks, exposed for testing and reuse
+ * ------------------------------------------------------------------------- */
+
+/* Degree histogram of a CSR pattern (the selector's input features).  Row i
+ * has degree d = row_ptr[i+1] - row_ptr[i]; bucket 0 counts empty rows and
+ * bucket b in 1..32 the rows with 2^(b-1) <= d < 2^b.
+ * out_host: int64 [67] = counts[33], degree sums[33], max degree.
+ * workspace: >= 1024 bytes.  Synchronous. */
+int csr_degree_histogram(csr_context_t ctx, int64_t n_rows, const int32_t* row_ptr,
+                         int64_t* out_host, void* workspace, size_t ws_bytes, void* stream);
+
+/* Merge-path partition of rows + entries into chunks of items_per_chunk
+ * items (items = row ends + stored entries, the end of a row following its
+ * last entry).  coords: device int32 [2 * (n_chunks + 1)], (x, y) pairs =
+ * (rows ended, entries consumed) before each chunk; the last pair is
+ * (n_rows, nnz).  n_chunks = ceil((n_rows + nnz) / items_per_chunk), at least
+ * 1.  Asynchronous. */
+int csr_merge_path_partition(csr_context_t ctx, int64_t n_rows, int64_t nnz,
+                             const int32_t* row_ptr, int32_t items_per_chunk,
+                             int32_t* coords, void* stream);
+
+/* Signature of problem p given its degree histogram (int64 [67] as returned
+ * by csr_degree_histogram): FNV-1a 64 over the little-endian int64 sequence
+ * 0x43535253, library version 1, op, dtype, n_rows, n_cols, nnz, width,
+ * heads, head_dim (0, 0 for the fp32 ops), the widest vector access the
+ * operands allow (1, 2, 4; 8 for multi-head), the device's CU count and
+ * architecture number (950; both 0 when ctx is NULL or host-only), then the
+ * 67 histogram values.  Host-only. */
+int csr_signature(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram,
+                  uint64_t* signature);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSRSA_H */

@@ -1,0 +1,47 @@
+"""Helpers of the GPU parity tests: device transfer and the error measure.
+
+Error measure: for each output element, |gpu - ref| / mag where mag is the
+oracle's sum of absolute terms (sum |a||x|, sum |u||v|, sum p|v|); an element
+with mag = 0 must be exactly 0 on the GPU.  For non-negative data mag equals
+the value itself, so this is then the plain relative error.
+"""
+
+import numpy as np
+import torch
+
+TOL_F32 = 1e-5
+TOL_BF16 = 1e-2
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def bf16_dev(bits):
+    """uint16 bf16 bit patterns -> device bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def max_err(gpu, ref, mag):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    m = np.asarray(mag, dtype=np.float64)
+    assert g.shape == r.shape == m.shape, (g.shape, r.shape, m.shape)
+    if g.size == 0:
+        return 0.0
+    zero = m == 0
+    if zero.any():
+        assert np.all(g[zero] == 0), "elements with an all-zero oracle sum must be exactly 0"
+    nz = ~zero
+    if not nz.any():
+        return 0.0
+    return float(np.max(np.abs(g[nz] - r[nz]) / m[nz]))
+
+
+def assert_close(gpu, ref, mag, tol=TOL_F32, what=""):
+    e = max_err(gpu, ref, mag)
+    assert e <= tol, f"{what}: max error {e:.3e} > {tol:.0e}"
+    return e

@@ -1,0 +1,238 @@
+"""The C ABI on a machine without a GPU: the library loads and exports every
+declared symbol, and its host-side logic (problem and schedule checks, lane
+layouts, workspace sizes, signature, schedule cache log) behaves as the
+header documents."""
+
+import ctypes
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import csr_sparse_attention_amd as csa
+import oracle
+
+_ffi = csa._ffi
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "csrsa.h")).read()
+    return set(re.findall(r"^(?:int|const char\*)\s+(csr_\w+)\(", src, re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = csa.load_library()
+    declared = header_symbols()
+    assert declared == set(_ffi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = csa.load_library()
+    for code in range(0, -13, -1):
+        s = lib.csr_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.csr_status_string(-99).decode() == "unknown status"
+
+
+def problem(op, n_rows=1000, n_cols=1000, nnz=5000, width=64, heads=0, head_dim=0, ld=None, ptr=0x1000):
+    p = _ffi.CsrProblem()
+    p.op = op
+    p.dtype = _ffi.DTYPE_BF16 if op == _ffi.OP_MHA else _ffi.DTYPE_F32
+    p.n_rows, p.n_cols, p.nnz, p.width = n_rows, n_cols, nnz, width
+    p.heads, p.head_dim = heads, head_dim
+    ld = width if ld is None else ld
+    p.ld_a = p.ld_b = p.ld_out = ld
+    p.a = p.b = p.c = p.out = ptr
+    p.scale = 1.0
+    return p
+
+
+@pytest.mark.parametrize("F,vec,W,nv", [
+    (1, 1, 1, 1), (2, 2, 1, 1), (3, 1, 4, 1), (4, 4, 1, 1), (6, 2, 4, 1), (32, 4, 8, 1), (64, 4, 16, 1),
+    (100, 4, 32, 1), (128, 4, 32, 1), (256, 4, 64, 1), (300, 4, 64, 2), (602, 2, 64, 5), (1024, 4, 64, 4),
+    (4096, 4, 64, 16),
+])
+def test_default_layout(F, vec, W, nv):
+    s = csa.default_schedule(problem(_ffi.OP_SPMM, width=F))
+    assert (s.vec, s.group_lanes, s.passes) == (vec, W, nv)
+    assert s.mapping == _ffi.MAP_MERGEPATH and s.version == _ffi.SCHEDULE_VERSION
+
+
+def test_alignment_limits_vector_width():
+    s = csa.default_schedule(problem(_ffi.OP_SPMM, width=64, ld=66))
+    assert s.vec == 2
+    s = csa.default_schedule(problem(_ffi.OP_SPMM, width=64, ptr=0x1004))
+    assert s.vec == 1
+
+
+def test_problem_errors():
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+
+    def rc(p):
+        return lib.csr_workspace_size(None, ctypes.byref(p), None, ctypes.byref(n))
+
+    assert rc(problem(_ffi.OP_SPMM)) == 0
+    assert rc(problem(_ffi.OP_SPMM, width=0)) == -2
+    assert rc(problem(_ffi.OP_SPMM, width=4097)) == -2
+    assert rc(problem(_ffi.OP_SPMM, width=64, ld=32)) == -2
+    assert rc(problem(_ffi.OP_SPMM, nnz=-1)) == -2
+    assert rc(problem(_ffi.OP_SPMM, nnz=2**31)) == -2
+    p = problem(_ffi.OP_SPMM)
+    p.dtype = _ffi.DTYPE_BF16
+    assert rc(p) == -3
+    assert rc(problem(_ffi.OP_MHA, width=512, heads=8, head_dim=64)) == 0
+    assert rc(problem(_ffi.OP_MHA, width=1024, heads=8, head_dim=128)) == -2
+    assert rc(problem(_ffi.OP_MHA, width=8 * 48, heads=8, head_dim=48)) == -2
+    assert rc(problem(_ffi.OP_MHA, width=512, heads=8, head_dim=64, ptr=0x1008)) == -4
+    p = problem(_ffi.OP_ATTENTION)
+    p.scale = float("inf")
+    assert rc(p) == -2
+
+
+def test_workspace_layout_sizes():
+    # merge path: 1 KiB head, coords, slot rows, (max, sum) pieces, value pieces
+    def up(v):
+        return (v + 255) // 256 * 256
+
+    for op, ml_per, val in ((_ffi.OP_SPMM, 0, True), (_ffi.OP_ATTENTION, 2, True), (_ffi.OP_SDDMM, 0, False)):
+        p = problem(op, n_rows=10_000, nnz=123_457, width=100)
+        s = csa.default_schedule(p)
+        nc = -(-(10_000 + 123_457) // s.chunk_items)
+        want = 1024 + up((nc + 1) * 8) + up(nc * 8) + up(nc * 2 * ml_per * 4) + (up(nc * 2 * 100 * 4) if val else 0)
+        assert csa.workspace_size(p, s) == want
+        rg = csa.CsrSchedule.from_buffer_copy(bytes(s))
+        rg.mapping, rg.chunk_items, rg.long_row = _ffi.MAP_ROWGROUP, 0, 0
+        assert csa.workspace_size(p, rg) == 1024
+        assert csa.workspace_size(p) >= csa.workspace_size(p, s)
+
+
+def test_invalid_schedules_rejected():
+    lib = csa.load_library()
+    p = problem(_ffi.OP_SPMM, width=64)
+    n = ctypes.c_size_t()
+    base = csa.default_schedule(p)
+
+    def rc(**kw):
+        s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+        for k, v in kw.items():
+            setattr(s, k, v)
+        return lib.csr_workspace_size(None, ctypes.byref(p), ctypes.byref(s), ctypes.byref(n))
+
+    assert rc() == 0
+    assert rc(version=2) == -7
+    assert rc(op=_ffi.OP_SDDMM) == -7
+    assert rc(mapping=3) == -7
+    assert rc(chunk_items=300) == -7
+    assert rc(group_lanes=3) == -7
+    assert rc(group_lanes=128) == -7
+    assert rc(passes=7) == -7
+    assert rc(group_lanes=4, passes=1) == -7   # does not cover F
+    assert rc(group_lanes=16, passes=2) == -7  # empty second pass
+    assert rc(group_lanes=8, passes=2) == 0
+    assert rc(flags=1) == -7
+    assert rc(mapping=_ffi.MAP_ROWGROUP) == -7  # row-group takes chunk = long = 0
+    assert rc(mapping=_ffi.MAP_ROWGROUP, chunk_items=0, long_row=0) == 0
+
+
+def test_signature_is_fnv1a_of_documented_fields():
+    p = problem(_ffi.OP_SPMM, n_rows=232_965, n_cols=232_965, nnz=114_600_002, width=602, ptr=0x10000)
+    hist = np.arange(67, dtype=np.int64) * 1234567
+    sig = csa.signature(p, hist)
+    fields = [0x43535253, 1, p.op, p.dtype, p.n_rows, p.n_cols, p.nnz, p.width, 0, 0, 2, 0, 0] + hist.tolist()
+    want = oracle.fnv1a64(b"".join(struct.pack("<q", v) for v in fields))
+    assert sig == want
+    hist2 = hist.copy()
+    hist2[5] += 1
+    assert csa.signature(p, hist2) != sig
+    q = problem(_ffi.OP_MHA, width=512, heads=8, head_dim=64, ptr=0x10000)
+    fields = [0x43535253, 1, q.op, q.dtype, q.n_rows, q.n_cols, q.nnz, 512, 8, 64, 8, 0, 0] + hist.tolist()
+    assert csa.signature(q, hist) == oracle.fnv1a64(b"".join(struct.pack("<q", v) for v in fields))
+
+
+def test_device_context_needs_gfx950():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = csa.load_library()
+    h = ctypes.c_void_p()
+    assert lib.csr_context_create(ctypes.byref(h), 0, None, 0) == -11
+
+
+def _sched(**kw):
+    s = csa.CsrSchedule()
+    s.version, s.op, s.mapping, s.vec, s.group_lanes, s.passes, s.chunk_items, s.long_row = 1, 1, 2, 4, 16, 1, 512, 64
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_cache_log_robustness(tmp_path):
+    path = tmp_path / "cache.log"
+    good = "csrsa-cache v1 00000000000000ab op=1 map=2 vec=4 w=16 nv=1 chunk=512 long=64 flags=0 us=12.500\n"
+    newer = "csrsa-cache v1 00000000000000ab op=1 map=2 vec=4 w=16 nv=1 chunk=1024 long=64 flags=0 us=10.000\n"
+    other = "csrsa-cache v1 00000000000000cd op=3 map=1 vec=2 w=8 nv=1 chunk=0 long=0 flags=0 us=1.000\n"
+    lines = [
+        "# comment\n",
+        good,
+        "csrsa-cache v2 00000000000000ef op=1 map=2 vec=4 w=16 nv=1 chunk=512 long=64 flags=0 us=1.0\n",  # schema
+        "garbage line\n",
+        "csrsa-cache v1 zz op=1\n",
+        other,
+        newer,
+        "csrsa-cache v1 0000000000000011 op=9 map=2 vec=4 w=16 nv=1 chunk=512 long=64 flags=0 us=1.0\n",  # bad op
+        "csrsa-cache v1 0000000000000012 op=1 map=2 vec=4 w=16 nv=1 chunk=512 long=64 flags=0 us=1.0 extra\n",
+        "csrsa-cache v1 0000000000000013 op=1 map=2 vec=4 w=16 nv=1 chu",  # truncated
+    ]
+    path.write_text("".join(lines))
+    ctx = csa.Context(-1, str(path))
+    info = ctx.cache_info()
+    assert info["entries"] == 2 and info["skipped_lines"] == 6
+    s = ctx.cache_lookup(0xAB)
+    assert s.chunk_items == 1024  # the last valid line of a signature wins
+    s2 = ctx.cache_lookup(0xCD)
+    assert (s2.op, s2.mapping, s2.vec, s2.group_lanes) == (3, 1, 2, 8)
+    assert ctx.cache_lookup(0x13) is None
+    # store appends one line; a fresh context replays it byte for byte
+    t = _sched(chunk_items=256)
+    ctx.cache_store(0x77, t)
+    ctx.close()
+    ctx2 = csa.Context(-1, str(path))
+    assert bytes(ctx2.cache_lookup(0x77)) == bytes(t)
+    assert bytes(ctx2.cache_lookup(0xAB)) == bytes(_sched(chunk_items=1024))
+    ctx2.close()
+
+
+def test_cache_missing_and_unwritable(tmp_path):
+    ctx = csa.Context(-1, str(tmp_path / "does-not-exist-yet.log"))
+    assert ctx.cache_info()["entries"] == 0
+    ctx.cache_store(1, _sched())
+    assert (tmp_path / "does-not-exist-yet.log").exists()
+    ctx.close()
+    bad = tmp_path / "no-such-dir" / "cache.log"
+    ctx = csa.Context(-1, str(bad))
+    with pytest.raises(csa.CsrError) as ei:
+        ctx.cache_store(2, _sched())
+    assert ei.value.code == -9
+    assert bytes(ctx.cache_lookup(2)) == bytes(_sched())  # kept in memory
+    assert ctx.cache_info()["io_errors"] == 1
+    with pytest.raises(csa.CsrError):
+        ctx.cache_flush()
+    (tmp_path / "no-such-dir").mkdir()
+    ctx.cache_flush()  # retried and persisted now
+    assert "0000000000000002" in bad.read_text()
+    ctx.close()
+
+
+def test_host_only_context_refuses_operations():
+    lib = csa.load_library()
+    ctx = csa.Context(-1, None)
+    assert lib.csr_spmm(ctx.handle, 1, 1, 0, 0x1000, None, None, 0x1000, 4, 4, 0x1000, 4, None, 0x1000, 4096,
+                        None) == -11
+    ctx.close()

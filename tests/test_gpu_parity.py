@@ -1,0 +1,477 @@
+"""GPU parity: every mapping and lane layout of every op against the CPU
+oracle on seeded graphs that span many chunks, with skew, empty rows, a row
+long enough to be split over more than 64 merge-path chunks, ragged widths and
+strided operands; plus the bit-exact cases (identity pattern, empty rows,
+pass-through of row_ptr / col_idx, replay determinism, integer bookkeeping)."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import csr_sparse_attention_amd as csa  # noqa: E402
+import oracle  # noqa: E402
+from synth import graphs, to_bf16_bits  # noqa: E402
+from synth.graphs import CSR  # noqa: E402
+from gpu_util import TOL_BF16, TOL_F32, assert_close, bf16_dev, dev  # noqa: E402
+
+_ffi = csa._ffi
+
+
+def skew_graph(seed, n_rows=3000, n_cols=100_000, giant=80_000):
+    """30% empty rows, short Poisson rows, medium rows, a few long rows and one
+    giant row (split over > 64 chunks of 1024 items)."""
+    rng = np.random.default_rng(seed)
+    kind = rng.random(n_rows)
+    deg = np.where(kind < 0.3, 0, rng.poisson(3, n_rows))
+    mid = (kind > 0.8) & (kind < 0.95)
+    deg[mid] = rng.integers(50, 300, mid.sum())
+    longr = rng.choice(n_rows, 5, replace=False)
+    deg[longr] = rng.integers(2000, 5000, 5)
+    deg[rng.integers(0, n_rows)] = giant
+    deg = np.minimum(deg, n_cols)
+    return graphs.csr_from_degrees(deg, n_cols, rng)
+
+
+def dup_graph(seed):
+    """Unsorted columns with duplicate entries."""
+    rng = np.random.default_rng(seed)
+    return graphs.random_small_graph(700, 900, 0.02, rng, empty_frac=0.2, allow_dup=True)
+
+
+def pattern_dev(csr):
+    return dev(csr.row_ptr), dev(csr.col_idx)
+
+
+def schedules(problem, thorough=True):
+    """The default schedule and its variants: both mappings, every chunk size,
+    whole-wave / per-group / default long-row thresholds, halved group width."""
+    base = csa.default_schedule(problem)
+    layouts = [(base.group_lanes, base.passes)]
+    W2, nv2 = base.group_lanes // 2, base.passes * 2
+    if W2 >= 1 and nv2 in (2, 4, 6, 8, 12, 16) and W2 * base.vec * (nv2 - 1) < problem.width:
+        layouts.append((W2, nv2))
+    out = []
+    for W, nv in layouts:
+        s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+        s.group_lanes, s.passes = W, nv
+        s.mapping, s.chunk_items, s.long_row = csa.MAP_ROWGROUP, 0, 0
+        out.append(s)
+        chunks = (256, 512, 1024) if thorough else (512,)
+        G = 64 // W
+        lrs = sorted({0, G * 4, 1 << 30}) if thorough else [G * 4]
+        for D in chunks:
+            for lr in lrs:
+                s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+                s.group_lanes, s.passes = W, nv
+                s.mapping, s.chunk_items, s.long_row = csa.MAP_MERGEPATH, D, lr
+                out.append(s)
+    return out
+
+
+def sched_id(s):
+    return f"m{s.mapping}-w{s.group_lanes}-nv{s.passes}-v{s.vec}-d{s.chunk_items}-lr{s.long_row}"
+
+
+# ---------------------------------------------------------------------------
+# SpMM
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def skew():
+    return skew_graph(1)
+
+
+@pytest.mark.parametrize("F", [1, 4, 32, 64, 602])
+def test_spmm_every_schedule(skew, F):
+    csr = skew
+    rng = np.random.default_rng(F)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    v, Xd = dev(vals), dev(X)
+    p, out = csa.make_problem("spmm", rp, ci, v, Xd)
+    for s in schedules(p):
+        Y = csa.spmm(rp, ci, v, Xd, schedule=s)
+        torch.cuda.synchronize()
+        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+    Y = csa.spmm(rp, ci, v, Xd)  # automatic selection
+    assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, "auto")
+
+
+@pytest.mark.parametrize("F", [2, 3, 5, 7, 8, 16, 17, 100, 128, 256, 300, 1024])
+def test_spmm_widths(F):
+    csr = skew_graph(2, n_rows=1500, n_cols=20_000, giant=9000)
+    rng = np.random.default_rng(100 + F)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("spmm", rp, ci, dev(vals), dev(X))
+    for s in schedules(p, thorough=False):
+        Y = csa.spmm(rp, ci, dev(vals), dev(X), schedule=s)
+        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+
+
+def test_spmm_strided_and_unit_values():
+    csr = skew_graph(3, n_rows=800, n_cols=5000, giant=3000)
+    rng = np.random.default_rng(3)
+    F, ldx, ldy = 24, 40, 36
+    Xbig = rng.standard_normal((csr.n_cols, ldx)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, None, Xbig[:, :F])
+    rp, ci = pattern_dev(csr)
+    Xd = dev(Xbig)[:, :F]
+    Ybig = torch.full((csr.n_rows, ldy), 7.0, device="cuda")
+    Y = Ybig[:, :F]
+    p, _ = csa.make_problem("spmm", rp, ci, None, Xd, out=Y)
+    for s in schedules(p, thorough=False):
+        csa.spmm(rp, ci, None, Xd, out=Y, schedule=s)
+        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+        assert torch.all(Ybig[:, F:] == 7.0), "columns beyond F must not be written"
+
+
+def test_spmm_duplicates_unsorted():
+    csr = dup_graph(4)
+    rng = np.random.default_rng(4)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, 33)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X)
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("spmm", rp, ci, dev(vals), dev(X))
+    for s in schedules(p, thorough=False):
+        Y = csa.spmm(rp, ci, dev(vals), dev(X), schedule=s)
+        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+
+
+# ---------------------------------------------------------------------------
+# attention (scores given)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("F", [1, 4, 32, 64, 100])
+def test_attention_every_schedule(skew, F):
+    csr = skew
+    rng = np.random.default_rng(200 + F)
+    sc = (2 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    V = rng.uniform(-1, 1, (csr.n_cols, F)).astype(np.float32)
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V, 1.0, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    s_d, V_d = dev(sc), dev(V)
+    p, _ = csa.make_problem("attention", rp, ci, s_d, V_d)
+    for s in schedules(p):
+        out = csa.attention(rp, ci, s_d, V_d, schedule=s)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+    out = csa.attention(rp, ci, s_d, V_d)
+    assert_close(out.cpu().numpy(), ref, mag, TOL_F32, "auto")
+
+
+@pytest.mark.parametrize("scale", [0.125, 3.0])
+def test_attention_scale_and_duplicates(scale):
+    csr = dup_graph(5)
+    rng = np.random.default_rng(5)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, 16)).astype(np.float32)
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, sc, V, scale)
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("attention", rp, ci, dev(sc), dev(V), scale=scale)
+    for s in schedules(p, thorough=False):
+        out = csa.attention(rp, ci, dev(sc), dev(V), scale=scale, schedule=s)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+
+
+def test_attention_shift_invariance_large_offsets(skew):
+    """+-1000 added per row (exact in fp32 for scores on a 2^-10 grid): the
+    max subtraction keeps exp finite and the result matches the oracle."""
+    csr = skew
+    rng = np.random.default_rng(6)
+    base = (np.round(rng.standard_normal(csr.nnz) * 1024) / 1024).astype(np.float32)
+    shift = np.repeat(rng.choice([-1000.0, 0.0, 1000.0], csr.n_rows), csr.degrees()).astype(np.float32)
+    sc = base + shift
+    V = rng.standard_normal((csr.n_cols, 8)).astype(np.float32)
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, base, V)
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("attention", rp, ci, dev(sc), dev(V))
+    for s in schedules(p, thorough=False):
+        out = csa.attention(rp, ci, dev(sc), dev(V), schedule=s)
+        o = out.cpu().numpy()
+        assert np.all(np.isfinite(o))
+        assert_close(o, ref, mag, TOL_F32, sched_id(s))
+
+
+def test_c1_attention_workload():
+    from synth import configs
+
+    c = configs.make_config("c1")
+    csr = c["csr"]
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, c["scores"], c["V"])
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("attention", rp, ci, dev(c["scores"]), dev(c["V"]))
+    for s in schedules(p):
+        out = csa.attention(rp, ci, dev(c["scores"]), dev(c["V"]), schedule=s)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+
+
+def test_p4_size_attention():
+    from synth import configs
+
+    c = configs.make_config("p4")
+    csr = c["csr"]
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, c["scores"], c["V"])
+    rp, ci = pattern_dev(csr)
+    out = csa.attention(rp, ci, dev(c["scores"]), dev(c["V"]))
+    assert_close(out.cpu().numpy(), ref, mag, TOL_F32)
+
+
+# ---------------------------------------------------------------------------
+# SDDMM
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [1, 4, 32, 64, 128, 602])
+def test_sddmm_every_schedule(K):
+    csr = skew_graph(7, n_rows=2000, n_cols=30_000, giant=25_000)
+    rng = np.random.default_rng(300 + K)
+    U = rng.standard_normal((csr.n_rows, K)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, K)).astype(np.float32)
+    ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    Ud, Vd = dev(U), dev(V)
+    p, _ = csa.make_problem("sddmm", rp, ci, Ud, Vd)
+    for s in schedules(p):
+        out = csa.sddmm(rp, ci, Ud, Vd, schedule=s)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_F32, sched_id(s))
+    out = csa.sddmm(rp, ci, Ud, Vd)
+    assert_close(out.cpu().numpy(), ref, mag, TOL_F32, "auto")
+
+
+# ---------------------------------------------------------------------------
+# multi-head attention (bf16 in, fp32 accumulate)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,D", [(8, 64), (2, 8), (1, 512), (4, 32), (3, 16)])
+def test_mha_schedules(H, D):
+    csr = skew_graph(8, n_rows=1200, n_cols=30_000, giant=20_000)
+    rng = np.random.default_rng(400 + H * D)
+    Q = to_bf16_bits(rng.standard_normal((csr.n_rows, H, D)).astype(np.float32))
+    K = to_bf16_bits(rng.standard_normal((csr.n_cols, H, D)).astype(np.float32))
+    V = to_bf16_bits(rng.standard_normal((csr.n_cols, H, D)).astype(np.float32))
+    scale = 1.0 / np.sqrt(D)
+    ref, mag, _ = oracle.mha(csr.row_ptr, csr.col_idx, Q, K, V, scale, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    Qd, Kd, Vd = bf16_dev(Q), bf16_dev(K), bf16_dev(V)
+    p, _ = csa.make_problem("mha", rp, ci, Qd, Kd, Vd, scale=scale)
+    base = csa.default_schedule(p)
+    scheds = []
+    for mapping, D_items in ((csa.MAP_ROWGROUP, 0), (csa.MAP_MERGEPATH, 256), (csa.MAP_MERGEPATH, 512),
+                             (csa.MAP_MERGEPATH, 1024)):
+        s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+        s.mapping, s.chunk_items = mapping, D_items
+        scheds.append(s)
+    for s in scheds:
+        out = csa.mha_attention(rp, ci, Qd, Kd, Vd, scale=scale, schedule=s)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_BF16, sched_id(s))
+        # fp32 accumulation keeps the error far below the bf16 tolerance
+        assert_close(out.cpu().numpy(), ref, mag, 1e-4, sched_id(s))
+    out = csa.mha_attention(rp, ci, Qd, Kd, Vd, scale=scale)
+    assert_close(out.cpu().numpy(), ref, mag, TOL_BF16, "auto")
+
+
+# ---------------------------------------------------------------------------
+# exact cases
+# ---------------------------------------------------------------------------
+
+def test_identity_pattern_bit_exact():
+    n, F = 5000, 64
+    rng = np.random.default_rng(9)
+    rp = np.arange(n + 1, dtype=np.int32)
+    ci = np.arange(n, dtype=np.int32)
+    V = rng.standard_normal((n, F)).astype(np.float32)
+    sc = (30 * rng.standard_normal(n)).astype(np.float32)
+    rpd, cid, Vd = dev(rp), dev(ci), dev(V)
+    p, _ = csa.make_problem("attention", rpd, cid, dev(sc), Vd)
+    for s in schedules(p):
+        out = csa.attention(rpd, cid, dev(sc), Vd, schedule=s).cpu().numpy()
+        assert np.array_equal(out.view(np.uint32), V.view(np.uint32)), sched_id(s)
+        Y = csa.spmm(rpd, cid, None, Vd, schedule=_as_op(s, 1)).cpu().numpy()
+        assert np.array_equal(Y.view(np.uint32), V.view(np.uint32)), sched_id(s)
+    Q = to_bf16_bits(rng.standard_normal((n, 8, 64)).astype(np.float32))
+    Vb = to_bf16_bits(rng.standard_normal((n, 8, 64)).astype(np.float32))
+    out = csa.mha_attention(rpd, cid, bf16_dev(Q), bf16_dev(Q), bf16_dev(Vb)).cpu().numpy()
+    want = (Vb.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(out, want)
+
+
+def _as_op(s, op):
+    t = csa.CsrSchedule.from_buffer_copy(bytes(s))
+    t.op = op
+    return t
+
+
+def test_empty_rows_positive_zero_and_empty_graph():
+    n = 4000
+    rng = np.random.default_rng(10)
+    deg = np.where(rng.random(n) < 0.5, 0, rng.integers(1, 9, n))
+    csr = graphs.csr_from_degrees(deg, 3000, rng)
+    V = rng.standard_normal((3000, 20)).astype(np.float32)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("attention", rp, ci, dev(sc), dev(V))
+    empty = csr.degrees() == 0
+    for s in schedules(p, thorough=False):
+        out = torch.full((n, 20), float("nan"), device="cuda")
+        csa.attention(rp, ci, dev(sc), dev(V), out=out, schedule=s)
+        o = out.cpu().numpy()
+        assert np.all(o[empty].view(np.uint32) == 0), sched_id(s)
+        Y = torch.full((n, 20), float("nan"), device="cuda")
+        csa.spmm(rp, ci, dev(sc), dev(V), out=Y, schedule=_as_op(s, 1))
+        assert np.all(Y.cpu().numpy()[empty].view(np.uint32) == 0)
+    # no entries at all
+    rp0 = dev(np.zeros(n + 1, np.int32))
+    ci0 = torch.empty(0, dtype=torch.int32, device="cuda")
+    for fn, args in ((csa.spmm, (None, dev(V))), (csa.attention, (torch.empty(0, device="cuda"), dev(V)))):
+        out = torch.full((n, 20), float("nan"), device="cuda")
+        fn(rp0, ci0, *args, out=out)
+        assert torch.all(out == 0) and not torch.any(torch.signbit(out))
+    out = csa.sddmm(rp0, ci0, dev(V[:n // 2]), dev(V))
+    assert out.numel() == 0
+    # no rows at all
+    Y = csa.spmm(dev(np.zeros(1, np.int32)), ci0, None, dev(V))
+    assert Y.shape == (0, 20)
+
+
+def test_inputs_pass_through_and_replay_determinism(skew):
+    csr = skew
+    rng = np.random.default_rng(11)
+    sc = rng.standard_normal(csr.nnz).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, 32)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    sd, Vd = dev(sc), dev(V)
+    p, _ = csa.make_problem("attention", rp, ci, sd, Vd)
+    for s in schedules(p, thorough=False):
+        a = csa.attention(rp, ci, sd, Vd, schedule=s).cpu().numpy()
+        b = csa.attention(rp, ci, sd, Vd, schedule=s).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), sched_id(s)
+    assert np.array_equal(rp.cpu().numpy(), csr.row_ptr)
+    assert np.array_equal(ci.cpu().numpy(), csr.col_idx)
+    assert np.array_equal(sd.cpu().numpy(), sc) and np.array_equal(Vd.cpu().numpy(), V)
+
+
+# ---------------------------------------------------------------------------
+# integer bookkeeping, selector and cache
+# ---------------------------------------------------------------------------
+
+def test_degree_histogram_and_partition_bit_exact(skew):
+    csr = skew
+    rp = dev(csr.row_ptr)
+    counts, sums, mx = csa.degree_histogram(rp)
+    oc, osum, omx = oracle.degree_histogram(csr.row_ptr)
+    assert counts == oc.tolist() and sums == osum.tolist() and mx == omx
+    for D in (1, 7, 256, 1024, 5000):
+        coords = csa.merge_path_partition(rp, csr.nnz, D).cpu().numpy()
+        x, y = oracle.merge_path_partition(csr.row_ptr, D)
+        assert np.array_equal(coords[:, 0], x) and np.array_equal(coords[:, 1], y)
+
+
+def test_select_replay_and_cache_file(tmp_path, skew):
+    csr = skew
+    rng = np.random.default_rng(12)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, 64)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    vd, Xd = dev(vals), dev(X)
+    path = str(tmp_path / "cache.log")
+    ctx = csa.Context(0, path)
+    s1, sig1 = csa.select("spmm", rp, ci, vd, Xd, ctx=ctx)
+    s2, sig2 = csa.select("spmm", rp, ci, vd, Xd, ctx=ctx)  # cache hit
+    s3, sig3 = csa.select("spmm", rp, ci, vd, Xd, mode="replay", ctx=ctx)
+    assert sig1 == sig2 == sig3 and bytes(s1) == bytes(s2) == bytes(s3)
+    assert ctx.cache_info()["entries"] == 1
+    ctx.close()
+    ctx2 = csa.Context(0, path)  # reload from the log
+    s4, sig4 = csa.select("spmm", rp, ci, vd, Xd, mode="replay", ctx=ctx2)
+    assert sig4 == sig1 and bytes(s4) == bytes(s1)
+    Y = csa.spmm(rp, ci, vd, Xd, schedule=s4, ctx=ctx2)
+    assert_close(Y.cpu().numpy(), ref, mag, TOL_F32)
+    # a different width is a different signature: replay-only misses
+    X2 = dev(rng.standard_normal((csr.n_cols, 48)).astype(np.float32))
+    with pytest.raises(csa.CsrError) as ei:
+        csa.select("spmm", rp, ci, vd, X2, mode="replay", ctx=ctx2)
+    assert ei.value.code == _ffi.CSR_ERR_NO_CACHE_ENTRY
+    ctx2.close()
+
+
+def test_probe_failure_falls_back_to_default(monkeypatch, skew):
+    csr = skew
+    rp, ci = pattern_dev(csr)
+    X = dev(np.ones((csr.n_cols, 16), np.float32))
+    monkeypatch.setenv("CSRSA_FAIL_PROBE", "1")
+    ctx = csa.Context(0, None)
+    s, _ = csa.select("spmm", rp, ci, None, X, ctx=ctx)
+    p, _ = csa.make_problem("spmm", rp, ci, None, X)
+    assert bytes(s) == bytes(csa.default_schedule(p))
+    assert ctx.cache_info()["entries"] == 0  # a fallback is not cached
+    ctx.close()
+
+
+def test_error_codes(skew):
+    csr = skew
+    lib = csa.load_library()
+    ctx = csa.default_context(0)
+    rp, ci = pattern_dev(csr)
+    X = dev(np.ones((csr.n_cols, 16), np.float32))
+    Y = torch.empty((csr.n_rows, 16), device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    n, m, nnz = csr.n_rows, csr.n_cols, csr.nnz
+
+    def call(**kw):
+        a = dict(rp=rp.data_ptr(), ci=ci.data_ptr(), X=X.data_ptr(), F=16, ldx=16, Y=Y.data_ptr(), ldy=16,
+                 ws=ws.data_ptr(), wsb=ws.numel(), n=n, m=m, nnz=nnz, sched=None)
+        a.update(kw)
+        return lib.csr_spmm(ctx.handle, a["n"], a["m"], a["nnz"], a["rp"], a["ci"], None, a["X"], a["F"], a["ldx"],
+                            a["Y"], a["ldy"], a["sched"], a["ws"], a["wsb"], st)
+
+    assert call() == 0
+    assert call(rp=None) == -1
+    assert call(X=None) == -1
+    assert call(F=0) == -2
+    assert call(ldx=8) == -2
+    assert call(n=-1) == -2
+    assert call(X=X.data_ptr() + 2) == -4
+    assert call(wsb=16) == -5
+    assert call(ws=ws.data_ptr() + 64) == -4
+    p, _ = csa.make_problem("spmm", rp, ci, None, X, out=Y)
+    s = csa.default_schedule(p)
+    s.op = _ffi.OP_ATTENTION
+    assert call(sched=ctypes.byref(s)) == -7
+    s = csa.default_schedule(p)
+    s.chunk_items = 300
+    assert call(sched=ctypes.byref(s)) == -7
+    s = csa.default_schedule(p)
+    s.vec = 4
+    assert call(F=6, ldx=6, ldy=6, sched=ctypes.byref(s)) == -7
+    torch.cuda.synchronize()
+
+
+def test_validation_flag_rejects_bad_columns():
+    rng = np.random.default_rng(13)
+    csr = graphs.random_small_graph(200, 300, 0.05, rng)
+    bad = csr.col_idx.copy()
+    bad[len(bad) // 2] = 300  # out of range
+    rp, ci = dev(csr.row_ptr), dev(bad)
+    X = dev(np.ones((300, 8), np.float32))
+    ctx = csa.Context(0, None, flags=csa.CTX_VALIDATE)
+    with pytest.raises(csa.CsrError) as ei:
+        csa.spmm(rp, ci, None, X, ctx=ctx)
+    assert ei.value.code == -6
+    Y = csa.spmm(rp, dev(csr.col_idx), None, X, ctx=ctx)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, None, np.ones((300, 8), np.float32))
+    assert_close(Y.cpu().numpy(), ref, mag)
+    ctx.close()
