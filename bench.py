@@ -115,6 +115,65 @@ def build_workload(name, torch, csa):
     return calls, time.time() - t0
 
 
+def committed_traffic(config, call, schedule):
+    """HBM traffic per launch of the dominant kernel from the committed counter
+    summary (profiles/traffic.json), or None when the kernel's sources or the
+    selected schedule differ from those the counters were taken with."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(config)
+    if not rec or rec.get("call") != call.name:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    sd = schedule.as_dict()
+    if any(sd.get(k) != v for k, v in rec["schedule"].items()):
+        return None
+    return rec["traffic_bytes"]
+
+
+def selector_study(calls, torch, csa, reps=5):
+    """Times every candidate schedule of each call (the fixed mappings of the
+    selector's search space) and the selected one, same protocol for all:
+    one untimed run, then the median of `reps` HIP-event timed runs."""
+    stream = torch.cuda.current_stream()
+
+    def med(call, sched):
+        call.fn(*call.args, schedule=sched, **call.kwargs)
+        t = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call.fn(*call.args, schedule=sched, **call.kwargs)
+            b.record(stream)
+            b.synchronize()
+            t.append(a.elapsed_time(b))
+        return float(np.median(t))
+
+    out = {}
+    for c in calls:
+        scale = c.kwargs.get("scale", 1.0)
+        p, _ = csa.make_problem(c.op, *c.args, out=c.kwargs.get("out"), scale=scale)
+        counts, sums, mx = csa.degree_histogram(c.args[0])
+        cands = csa.candidates(p, counts + sums + [mx])
+        times = [med(c, s) for s in cands]
+        t_sel = med(c, c.schedule)
+        best = int(np.argmin(times))
+        out[c.name] = {"selected_ms": round(t_sel, 4), "best_fixed_ms": round(times[best], 4),
+                       "best_fixed": cands[best].as_dict(), "n_candidates": len(cands),
+                       "selected_over_best": round(t_sel / times[best], 4),
+                       "candidate_ms": [round(t, 4) for t in times]}
+    return out
+
+
 def cpu_baseline(calls, target_s=15.0):
     """Times the oracle (as it is) on a bounded sample of the step: the same
     contiguous block of leading rows for every call, sized so that the whole
@@ -138,17 +197,20 @@ def cpu_baseline(calls, target_s=15.0):
 
     csr = calls[0].oracle_fn[1]
     rp = csr.row_ptr.astype(np.int64)
-    # calibrate on ~0.2% of the entries, then scale the row block
-    probe_rows = int(np.searchsorted(rp, max(1, csr.nnz // 500))) or 1
-    probe_rows = min(probe_rows, csr.n_rows)
-    t_probe = sum(run(c, probe_rows) for c in calls)
-    frac = min(1.0, (rp[probe_rows] / max(1, csr.nnz)) * target_s / max(t_probe, 1e-3))
-    r1 = int(np.searchsorted(rp, int(frac * csr.nnz))) or 1
-    r1 = min(max(r1, probe_rows), csr.n_rows)
-    total_t, total_b = 0.0, 0.0
-    for c in calls:
-        total_t += run(c, r1)
-        total_b += b_alg(c.op, r1, int(rp[r1]), c.width)
+
+    def sample(r1):
+        t, b = 0.0, 0.0
+        for c in calls:
+            t += run(c, r1)
+            b += b_alg(c.op, r1, int(rp[r1]), c.width)
+        return t, b
+
+    # calibrate on ~1% of the entries, then size the row block for target_s
+    r1 = min(csr.n_rows, max(1, int(np.searchsorted(rp, max(1, csr.nnz // 100)))))
+    t_cal, _ = sample(r1)
+    frac = (rp[r1] / max(1, csr.nnz)) * target_s / max(t_cal, 1e-3)
+    r1 = min(csr.n_rows, max(r1, int(np.searchsorted(rp, int(min(1.0, frac) * csr.nnz)))))
+    total_t, total_b = sample(r1)
     return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"rows [0, {r1}) ({int(rp[r1])} entries, {100.0 * rp[r1] / max(1, csr.nnz):.2f}% of nnz) "
                       f"of every call of the step, float64 oracle, {total_t:.1f} s"}
@@ -162,6 +224,9 @@ def main():
     ap.add_argument("--config", default="c2", help="c2 (default), c1, p4, c3, c4, c5a, c5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one device copy of 1 GiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's hot path runs on a single MI355X "
@@ -173,6 +238,14 @@ def main():
     import csr_sparse_attention_amd as csa
 
     torch.cuda.init()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     calls, gen_s = build_workload(args.config, torch, csa)
     print(f"[bench] workload {args.config}: {len(calls)} calls, generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
 
@@ -256,10 +329,15 @@ def main():
                    "widths": [c.width for c in calls], "parallelism": "1 GPU"},
         "gnnzf_per_s": round(gnnzf, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom.name,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": committed_traffic(args.config, dom, dom.schedule), "kernel": dom.name,
                      "launch_ms": round(dom_ms, 4), "bytes_per_launch": dom.bytes},
         "kernels": kernels,
     }
+    if not args.no_study:
+        print("[bench] selector study: every candidate schedule of every call", file=sys.stderr, flush=True)
+        result["selector"] = selector_study(calls, torch, csa)
+        result["selector_worst_ratio"] = max(v["selected_over_best"] for v in result["selector"].values())
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(calls, args.cpu_seconds)

@@ -24,6 +24,7 @@ load_library()
 from .ops import (  # noqa: E402,F401
     Context,
     attention,
+    candidates,
     default_context,
     default_schedule,
     degree_histogram,

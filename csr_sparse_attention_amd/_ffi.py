@@ -28,7 +28,7 @@ SCHEDULE_VERSION = 1
 EXPORTS = (
     "csr_context_create", "csr_context_destroy", "csr_status_string", "csr_last_error",
     "csr_spmm", "csr_sddmm", "csr_attention", "csr_mha_attention",
-    "csr_select", "csr_default_schedule", "csr_workspace_size", "csr_cache_flush",
+    "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
 )
@@ -112,7 +112,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m csr_sparse_attention_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python csr_sparse_attention_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, U32, F, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
@@ -129,6 +129,7 @@ def load() -> ctypes.CDLL:
         "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, SP, P, SZ, P],
         "csr_select": [P, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
         "csr_default_schedule": [P, PP, SP],
+        "csr_candidates": [P, PP, ctypes.POINTER(I64), SP, I32, ctypes.POINTER(I32)],
         "csr_workspace_size": [P, PP, SP, ctypes.POINTER(SZ)],
         "csr_cache_flush": [P],
         "csr_cache_info": [P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)],

@@ -1,6 +1,6 @@
 """Builds libcsrsa.so (HIP kernels + C ABI) for gfx950 with hipcc.
 
-    python -m csr_sparse_attention_amd.build
+    python csr_sparse_attention_amd/build.py
 
 Every source under csrc/ is compiled in parallel into _build/ at the repository
 root, then linked into csr_sparse_attention_amd/libcsrsa.so.

@@ -579,6 +579,19 @@ int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule
     return CSR_OK;
 }
 
+int csr_candidates(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, csr_schedule_t* out,
+                   int32_t max, int32_t* n)
+{
+    if (!p || !n || (max > 0 && !out)) return CSR_ERR_NULL;
+    std::string why;
+    int rc = csrh::check_problem(*p, false, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    const std::vector<csr_schedule_t> c = csrh::candidates(*p, histogram);
+    *n = (int32_t)c.size();
+    for (int32_t i = 0; i < max && i < (int32_t)c.size(); ++i) out[i] = c[i];
+    return CSR_OK;
+}
+
 int csr_workspace_size(csr_context_t ctx, const csr_problem_t* p, const csr_schedule_t* sched, size_t* bytes)
 {
     if (!p || !bytes) return CSR_ERR_NULL;

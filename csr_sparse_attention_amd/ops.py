@@ -340,6 +340,16 @@ def default_schedule(problem: CsrProblem) -> CsrSchedule:
     return s
 
 
+def candidates(problem: CsrProblem, histogram=None):
+    """The selector's candidate schedules for a problem (and degree histogram)."""
+    h = None if histogram is None else (ctypes.c_int64 * 67)(*[int(v) for v in histogram])
+    n = ctypes.c_int32()
+    _check(_lib().csr_candidates(None, ctypes.byref(problem), h, None, 0, ctypes.byref(n)), "csr_candidates")
+    arr = (CsrSchedule * max(1, n.value))()
+    _check(_lib().csr_candidates(None, ctypes.byref(problem), h, arr, n.value, ctypes.byref(n)), "csr_candidates")
+    return [CsrSchedule.from_buffer_copy(bytes(arr[i])) for i in range(n.value)]
+
+
 def workspace_size(problem: CsrProblem, schedule: Optional[CsrSchedule] = None) -> int:
     n = ctypes.c_size_t()
     _check(_lib().csr_workspace_size(None, ctypes.byref(problem), _sched_arg(schedule), ctypes.byref(n)),

@@ -264,6 +264,13 @@ int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode,
  * Host-only; ctx may be NULL. */
 int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule_t* out);
 
+/* The candidate schedules the selector considers for p given its degree
+ * histogram (int64 [67], or NULL), in the fixed order used for tie-breaking;
+ * the first is csr_default_schedule().  Writes at most max entries to out and
+ * the full count to *n.  Host-only; ctx may be NULL. */
+int csr_candidates(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram,
+                   csr_schedule_t* out, int32_t max, int32_t* n);
+
 /* Workspace bytes needed for p under schedule sched (NULL = automatic
  * selection, covering every candidate).  Host-only; ctx may be NULL; needs
  * only the shape fields of p (and the operand pointers for their alignment). */

@@ -46,22 +46,46 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def _declare(lib):
+    P, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
+    lib.oracle_spmm.argtypes = [P, P, P, P, I, I, I, I, P, P]
+    lib.oracle_sddmm.argtypes = [P, P, P, I, P, I, I, I, I, P, P]
+    lib.oracle_attention.argtypes = [P, P, P, P, I, I, D, I, I, P, P, P]
+    lib.oracle_mha.argtypes = [P, P, P, P, P, I, I, D, I, I, P, P, P]
+    for f in (lib.oracle_spmm, lib.oracle_sddmm, lib.oracle_attention, lib.oracle_mha):
+        f.restype = None
+    return lib
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
                 build(force=True)
-            lib = ctypes.CDLL(_LIB)
-            P, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
-            lib.oracle_spmm.argtypes = [P, P, P, P, I, I, I, I, P, P]
-            lib.oracle_sddmm.argtypes = [P, P, P, I, P, I, I, I, I, P, P]
-            lib.oracle_attention.argtypes = [P, P, P, P, I, I, D, I, I, P, P, P]
-            lib.oracle_mha.argtypes = [P, P, P, P, P, I, I, D, I, I, P, P, P]
-            for f in (lib.oracle_spmm, lib.oracle_sddmm, lib.oracle_attention, lib.oracle_mha):
-                f.restype = None
-            _lib = lib
+            _lib = _declare(ctypes.CDLL(_LIB))
     return _lib
+
+
+class use_library:
+    """Context manager that routes the functions of this module through
+    another build of oracle.c (the pin tests use it to check that planted
+    mistakes are caught)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        _load()
+        self.saved = _lib
+        _lib = _declare(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def default_threads() -> int:
