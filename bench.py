@@ -43,6 +43,8 @@ def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64):
         return 4 * (n_rows + 1) + nnz * 8 + n_rows * width * 4 + nnz * width * 4
     if op == "attention":
         return 4 * (n_rows + 1) + nnz * 8 + nnz * width * 4 + n_rows * width * 4
+    if op == "row_softmax":
+        return 4 * (n_rows + 1) + nnz * 8
     if op == "mha":
         hd = heads * head_dim
         return 4 * (n_rows + 1) + nnz * 4 + n_rows * hd * 2 + 2 * nnz * hd * 2 + n_rows * hd * 4
@@ -94,6 +96,29 @@ def build_workload(name, torch, csa):
             out = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
             calls.append(Call(f"sddmm_K{K}", "sddmm", csa.sddmm, (rp, ci, d(U), d(V)), {"out": out}, csr.n_rows,
                               csr.nnz, K, ("sddmm", csr, U, V)))
+    elif name in ("c3pipe", "c3fused"):
+        # single-head fp32 attention on the c3 graph from Q, K, V of width 64:
+        # SDDMM -> row softmax -> SpMM as three calls, or SDDMM -> fused
+        # softmax-aggregation as two
+        csr = configs.config_pattern("c3")
+        rp, ci = d(csr.row_ptr), d(csr.col_idx)
+        Q = configs.config_dense("c3", "U", csr, 64)
+        K = configs.config_dense("c3", "V", csr, 64)
+        V = configs.config_dense("c3", "X", csr, 64)
+        S = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+        P = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+        Y = torch.empty((csr.n_rows, 64), dtype=torch.float32, device="cuda")
+        Vd = d(V)
+        calls.append(Call("sddmm_K64", "sddmm", csa.sddmm, (rp, ci, d(Q), d(K)), {"out": S}, csr.n_rows, csr.nnz,
+                          64, ("sddmm", csr, Q, K)))
+        if name == "c3pipe":
+            calls.append(Call("row_softmax", "row_softmax", csa.row_softmax, (rp, S), {"out": P, "scale": 0.125},
+                              csr.n_rows, csr.nnz, 1, None))
+            calls.append(Call("spmm_F64", "spmm", csa.spmm, (rp, ci, P, Vd), {"out": Y}, csr.n_rows, csr.nnz, 64,
+                              None))
+        else:
+            calls.append(Call("attention_F64", "attention", csa.attention, (rp, ci, S, Vd),
+                              {"out": Y, "scale": 0.125}, csr.n_rows, csr.nnz, 64, None))
     elif name in ("c1", "p4"):
         c = configs.make_config(name)
         csr = c["csr"]
@@ -113,6 +138,30 @@ def build_workload(name, torch, csa):
     else:
         raise SystemExit(f"unknown config {name}")
     return calls, time.time() - t0
+
+
+def stream_bandwidth(torch, gib=4):
+    """Streaming reference on this GPU: best of 5 device copies (read + write)
+    and of 5 full reductions (read only) of a `gib` GiB fp32 buffer."""
+    n = gib * (1 << 28)
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn, nbytes in (("copy", lambda: y.copy_(x), 2 * 4 * n), ("read", lambda: x.sum(), 4 * n)):
+        best = None
+        for _ in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+        res[f"{name}_GB_s"] = round(nbytes / (best * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def committed_traffic(config, call, schedule):
@@ -140,37 +189,49 @@ def committed_traffic(config, call, schedule):
     return rec["traffic_bytes"]
 
 
-def selector_study(calls, torch, csa, reps=5):
+def selector_study(calls, torch, csa, rounds=5, per_round=3):
     """Times every candidate schedule of each call (the fixed mappings of the
-    selector's search space) and the selected one, same protocol for all:
-    one untimed run, then the median of `reps` HIP-event timed runs."""
+    selector's search space) and the selected one under one protocol: the
+    distinct schedules are run in interleaved rounds (so clock and thermal
+    drift bias none of them), `per_round` HIP-event timed runs each, and the
+    median over all rounds is kept.  The selected schedule is one of the
+    candidates, so its time is that candidate's time."""
     stream = torch.cuda.current_stream()
 
-    def med(call, sched):
+    def timed(call, sched):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         call.fn(*call.args, schedule=sched, **call.kwargs)
-        t = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            call.fn(*call.args, schedule=sched, **call.kwargs)
-            b.record(stream)
-            b.synchronize()
-            t.append(a.elapsed_time(b))
-        return float(np.median(t))
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b)
 
     out = {}
     for c in calls:
         scale = c.kwargs.get("scale", 1.0)
-        p, _ = csa.make_problem(c.op, *c.args, out=c.kwargs.get("out"), scale=scale)
+        args = (c.args[0], None) + tuple(c.args[1:]) if c.op == "row_softmax" else c.args
+        p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale)
         counts, sums, mx = csa.degree_histogram(c.args[0])
         cands = csa.candidates(p, counts + sums + [mx])
-        times = [med(c, s) for s in cands]
-        t_sel = med(c, c.schedule)
-        best = int(np.argmin(times))
-        out[c.name] = {"selected_ms": round(t_sel, 4), "best_fixed_ms": round(times[best], 4),
-                       "best_fixed": cands[best].as_dict(), "n_candidates": len(cands),
-                       "selected_over_best": round(t_sel / times[best], 4),
-                       "candidate_ms": [round(t, 4) for t in times]}
+        keys = [bytes(s) for s in cands]
+        if bytes(c.schedule) not in keys:
+            cands.append(c.schedule)
+            keys.append(bytes(c.schedule))
+        times = [[] for _ in cands]
+        for s in cands:
+            timed(c, s)
+        for _ in range(rounds):
+            for i, s in enumerate(cands):
+                for _ in range(per_round):
+                    times[i].append(timed(c, s))
+        med = [float(np.median(t)) for t in times]
+        n_cand = len(keys) if bytes(c.schedule) in keys[:-1] or len(cands) == len(keys) else len(keys) - 1
+        sel = med[keys.index(bytes(c.schedule))]
+        best = int(np.argmin(med))
+        out[c.name] = {"selected_ms": round(sel, 4), "best_fixed_ms": round(med[best], 4),
+                       "best_fixed": cands[best].as_dict(), "n_candidates": n_cand,
+                       "selected_over_best": round(sel / med[best], 4),
+                       "candidate_ms": [round(t, 4) for t in med]}
     return out
 
 
@@ -181,6 +242,7 @@ def cpu_baseline(calls, target_s=15.0):
     import oracle
 
     threads = oracle.default_threads()
+    calls = [c for c in calls if c.oracle_fn is not None]
 
     def run(call, r1):
         kind, csr, *ops = call.oracle_fn
@@ -221,7 +283,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2", help="c2 (default), c1, p4, c3, c4, c5a, c5b")
+    ap.add_argument("--config", default="c2", help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -246,6 +308,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    stream_ref = stream_bandwidth(torch)
     calls, gen_s = build_workload(args.config, torch, csa)
     print(f"[bench] workload {args.config}: {len(calls)} calls, generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
 
@@ -254,12 +317,13 @@ def main():
     for c in calls:
         torch.cuda.synchronize()
         t = time.perf_counter()
-        s, sig = csa.select(c.op if c.op != "mha" else "mha", *c.args, **(
-            {"scale": c.kwargs["scale"]} if c.op == "mha" else {}))
+        sel_args = (c.args[0], None) + tuple(c.args[1:]) if c.op == "row_softmax" else c.args
+        kw = {"scale": c.kwargs["scale"]} if "scale" in c.kwargs else {}
+        s, sig = csa.select(c.op, *sel_args, **kw)
         torch.cuda.synchronize()
         first = time.perf_counter() - t
         t = time.perf_counter()
-        s2, sig2 = csa.select(c.op, *c.args, mode="replay", **({"scale": c.kwargs["scale"]} if c.op == "mha" else {}))
+        s2, sig2 = csa.select(c.op, *sel_args, mode="replay", **kw)
         torch.cuda.synchronize()
         replay = time.perf_counter() - t
         assert bytes(s) == bytes(s2) and sig == sig2
@@ -324,7 +388,11 @@ def main():
                                 "c3": "CSR SpMM F in {100,128} + SDDMM K=128, log-normal graph 2,449,029 rows ~123.7M nnz",
                                 "c4": "skew stress SpMM + SDDMM, 1M rows 32M nnz Zipf(1.5), F in {4,8,16,32}",
                                 "c5a": "8-head bf16 CSR attention on the 2,449,029-row log-normal graph",
-                                "c5b": "8-head bf16 CSR attention, 16,384 tokens, window 512 + 64 global"}[args.config],
+                                "c5b": "8-head bf16 CSR attention, 16,384 tokens, window 512 + 64 global",
+                                "c3pipe": "unfused single-head fp32 attention on the log-normal graph: "
+                                          "SDDMM K=64 -> row softmax -> SpMM F=64",
+                                "c3fused": "single-head fp32 attention on the log-normal graph: "
+                                           "SDDMM K=64 -> fused softmax-SpMM F=64"}[args.config],
                    "name": args.config, "n_rows": calls[0].n_rows, "nnz": calls[0].nnz,
                    "widths": [c.width for c in calls], "parallelism": "1 GPU"},
         "gnnzf_per_s": round(gnnzf, 2),
@@ -333,7 +401,9 @@ def main():
                      "traffic": committed_traffic(args.config, dom, dom.schedule), "kernel": dom.name,
                      "launch_ms": round(dom_ms, 4), "bytes_per_launch": dom.bytes},
         "kernels": kernels,
+        "stream_measured": stream_ref,
     }
+    result["roofline"]["frac_of_measured_copy"] = round(achieved / stream_ref["copy_GB_s"], 4)
     if not args.no_study:
         print("[bench] selector study: every candidate schedule of every call", file=sys.stderr, flush=True)
         result["selector"] = selector_study(calls, torch, csa)

@@ -6,7 +6,13 @@ behind the C ABI of ``include/csrsa.h``); this package is a thin ctypes
 binding over it and raises ImportError when the library has not been built.
 """
 
-from ._ffi import (  # noqa: F401
+# torch first: its bundled HIP runtime carries the same soname as ROCm's, so
+# loading it before libcsrsa.so makes the library bind to that one runtime
+# (torch's streams and allocations are then valid in library calls); the
+# other order would put two HIP runtimes in the process.
+import torch  # noqa: F401
+
+from ._ffi import (  # noqa: F401,E402
     CsrError,
     CsrProblem,
     CsrSchedule,
@@ -24,6 +30,7 @@ load_library()
 from .ops import (  # noqa: E402,F401
     Context,
     attention,
+    attention_pipeline,
     candidates,
     default_context,
     default_schedule,
@@ -31,6 +38,7 @@ from .ops import (  # noqa: E402,F401
     make_problem,
     merge_path_partition,
     mha_attention,
+    row_softmax,
     sddmm,
     select,
     signature,

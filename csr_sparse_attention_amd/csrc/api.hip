@@ -160,6 +160,24 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         CSR_HIP(ctx, csrk::launch_merge_path(p.row_ptr, p.n_rows, p.nnz, s.chunk_items, L.n_chunks, coords, st));
     }
 
+    if (p.op == CSR_OP_ROW_SOFTMAX) {
+        if (p.nnz == 0) return CSR_OK;
+        csrk::SoftmaxArgs a{};
+        a.row_ptr = p.row_ptr;
+        a.n_rows = p.n_rows;
+        a.scores = static_cast<const float*>(p.a);
+        a.scale = p.scale;
+        a.probs = static_cast<float*>(p.out);
+        a.W = s.group_lanes;
+        a.long_row = (s.group_lanes == 64) ? 0 : s.long_row;
+        a.part = coords;
+        a.n_chunks = L.n_chunks;
+        a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
+        a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
+        a.stats = reinterpret_cast<float*>(ws + L.carry_val);
+        CSR_HIP(ctx, csrk::launch_row_softmax(s.chunk_items, a, st));
+        return CSR_OK;
+    }
     if (p.op == CSR_OP_MHA) {
         csrk::MhaArgs a{};
         a.row_ptr = p.row_ptr;
@@ -249,27 +267,65 @@ int histogram(csr_context_t ctx, const csr_problem_t& p, hipStream_t st, int64_t
     return CSR_OK;
 }
 
-// Times schedule s on p: one untimed run, then `reps` timed runs; returns
-// the median in microseconds, or a negative value if a run failed.
-double probe(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st, int reps)
+// One timed run of schedule s on p (milliseconds), or a negative value if it failed.
+double timed_run(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st)
 {
     if (env_flag("CSRSA_FAIL_PROBE")) return -1.0;
-    if (run_schedule(ctx, p, s, st) != CSR_OK) return -1.0;
     if (!ctx->ev0) {
         if (hipEventCreate(&ctx->ev0) != hipSuccess || hipEventCreate(&ctx->ev1) != hipSuccess) return -1.0;
     }
-    std::vector<double> t;
-    for (int r = 0; r < reps; ++r) {
-        if (hipEventRecord(ctx->ev0, st) != hipSuccess) return -1.0;
-        if (run_schedule(ctx, p, s, st) != CSR_OK) return -1.0;
-        if (hipEventRecord(ctx->ev1, st) != hipSuccess) return -1.0;
-        if (hipEventSynchronize(ctx->ev1) != hipSuccess) return -1.0;
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, ctx->ev0, ctx->ev1) != hipSuccess) return -1.0;
-        t.push_back(ms * 1000.0);
+    if (hipEventRecord(ctx->ev0, st) != hipSuccess) return -1.0;
+    if (run_schedule(ctx, p, s, st) != CSR_OK) return -1.0;
+    if (hipEventRecord(ctx->ev1, st) != hipSuccess) return -1.0;
+    if (hipEventSynchronize(ctx->ev1) != hipSuccess) return -1.0;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ctx->ev0, ctx->ev1) != hipSuccess) return -1.0;
+    return ms;
+}
+
+// Micro-probes: median run time (ms) of every candidate, or a negative
+// value for a candidate that failed.  The GPU is first warmed up on the
+// first candidate (clocks ramp up from idle), then the candidates are timed
+// in interleaved rounds so that slow drifts (clocks, temperature) bias none
+// of them; the number of runs per round adapts to the kernel's duration.
+std::vector<double> probe_all(csr_context_t ctx, const csr_problem_t& p, const std::vector<csr_schedule_t>& cand,
+                              const std::vector<size_t>& which, hipStream_t st)
+{
+    std::vector<double> med(cand.size(), -1.0);
+    std::vector<std::vector<double>> t(cand.size());
+    std::vector<bool> failed(cand.size(), false);
+    double warm = 0.0, last = -1.0;
+    for (int k = 0; k < 20 && warm < 20.0; ++k) {
+        last = timed_run(ctx, p, cand[which[0]], st);
+        if (last < 0) break;
+        warm += last;
     }
-    std::sort(t.begin(), t.end());
-    return t[t.size() / 2];
+    const int reps = std::max(1, env_int("CSRSA_PROBE_REPS", 0));
+    const int per_round = env_int("CSRSA_PROBE_REPS", 0) > 0 ? 1
+                          : (last > 0 ? std::max(1, std::min(3, (int)(10.0 / last))) : 1);
+    const int rounds = env_int("CSRSA_PROBE_REPS", 0) > 0 ? reps : 3;
+    for (size_t i : which) {  // one untimed run each (code loading, caches)
+        if (timed_run(ctx, p, cand[i], st) < 0) failed[i] = true;
+    }
+    for (int r = 0; r < rounds; ++r) {
+        for (size_t i : which) {
+            if (failed[i]) continue;
+            for (int k = 0; k < per_round; ++k) {
+                const double ms = timed_run(ctx, p, cand[i], st);
+                if (ms < 0) {
+                    failed[i] = true;
+                    break;
+                }
+                t[i].push_back(ms);
+            }
+        }
+    }
+    for (size_t i : which) {
+        if (failed[i] || t[i].empty()) continue;
+        std::sort(t[i].begin(), t[i].end());
+        med[i] = t[i][t[i].size() / 2];
+    }
+    return med;
 }
 
 int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_schedule_t* out, uint64_t* sig_out)
@@ -305,26 +361,30 @@ int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_
     for (size_t i = 0; i < cand.size(); ++i) order.push_back({csrh::estimate(p, cand[i], hist, ctx->dev), i});
     std::stable_sort(order.begin(), order.end(),
                      [](const std::pair<double, size_t>& x, const std::pair<double, size_t>& y) { return x.first < y.first; });
-    if (mode == CSR_SELECT_ESTIMATE || (ctx->flags & CSR_CTX_NO_PROBE)) {
+    // an in-place row softmax cannot be probed: every probe would overwrite
+    // its own input
+    const bool in_place = (p.op == CSR_OP_ROW_SOFTMAX) && (p.a == p.out) && p.a;
+    if (mode == CSR_SELECT_ESTIMATE || (ctx->flags & CSR_CTX_NO_PROBE) || in_place) {
         *out = cand[order[0].second];
-        if (mode != CSR_SELECT_ESTIMATE) store_entry(ctx, sig, *out, 0.0);
+        if (mode != CSR_SELECT_ESTIMATE && !in_place) store_entry(ctx, sig, *out, 0.0);
         return CSR_OK;
     }
     const int max_probe = std::max(1, env_int("CSRSA_PROBE_CANDIDATES", 6));
-    const int reps = std::max(1, env_int("CSRSA_PROBE_REPS", 5));
     std::vector<size_t> probe_set;
     for (size_t k = 0; k < order.size() && (int)probe_set.size() < max_probe; ++k) probe_set.push_back(order[k].second);
     std::sort(probe_set.begin(), probe_set.end());  // fixed candidate order for tie-breaking
+    const std::vector<double> med = probe_all(ctx, p, cand, probe_set, st);
     double best = -1.0;
     size_t best_i = 0;
     for (size_t i : probe_set) {
-        const double t = probe(ctx, p, cand[i], st, reps);
+        const double t = med[i];
         if (t < 0) continue;  // guardrail: a failing candidate is never chosen
-        if (best < 0 || t < best * 0.99) {
+        if (best < 0 || t < best * 0.99) {  // within 1 %: the lower candidate index wins
             best = t;
             best_i = i;
         }
     }
+    best *= 1000.0;  // microseconds in the cache log
     if (best < 0) {
         // every probe failed: fall back to the default schedule
         (void)hipGetLastError();
@@ -555,6 +615,27 @@ int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t
     return op_call(ctx, p, sched);
 }
 
+int csr_row_softmax(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr, const float* scores,
+                    float scale, float* probs, const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
+                    void* stream)
+{
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_ROW_SOFTMAX;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = n_rows;
+    p.n_cols = 0;
+    p.nnz = nnz;
+    p.width = 1;
+    p.row_ptr = row_ptr;
+    p.a = scores;
+    p.out = probs;
+    p.scale = scale;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
 int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_schedule_t* out, uint64_t* signature)
 {
     if (!ctx || !p || !out) return CSR_ERR_NULL;
@@ -648,7 +729,7 @@ int csr_cache_store(csr_context_t ctx, uint64_t signature, const csr_schedule_t*
 {
     if (!ctx || !sched) return CSR_ERR_NULL;
     std::lock_guard<std::mutex> lk(ctx->mu);
-    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_MHA)
+    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_ROW_SOFTMAX)
         return set_err(ctx, CSR_ERR_SCHEDULE, "not a schedule of this library version");
     return store_entry(ctx, signature, *sched, 0.0);
 }

@@ -44,4 +44,19 @@ struct MhaArgs {
     float* carry_val;    // [2 n_chunks][H * Dh]
 };
 
+struct SoftmaxArgs {
+    const int32_t* row_ptr;
+    int64_t n_rows;
+    const float* scores;  // [nnz]
+    float scale;
+    float* probs;         // [nnz]
+    int32_t W;            // lanes per group for short rows
+    int32_t long_row;     // whole-wave threshold
+    const int32_t* part;
+    int64_t n_chunks;
+    int32_t* carry_row;   // [2 n_chunks]
+    float* carry_ml;      // [2 n_chunks][2]
+    float* stats;         // [n_rows][2]: row maximum, sum of exponentials
+};
+
 }  // namespace csrk

@@ -92,9 +92,23 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (why) *why = msg;
         return code;
     };
-    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_MHA) return fail(CSR_ERR_SHAPE, "unknown op");
+    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_ROW_SOFTMAX) return fail(CSR_ERR_SHAPE, "unknown op");
     if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "this op takes fp32 operands");
     if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
+    if (p.op == CSR_OP_ROW_SOFTMAX) {
+        const int64_t lim = (int64_t)1 << 31;
+        if (p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "row softmax takes fp32 scores");
+        if (p.n_rows < 0 || p.nnz < 0) return fail(CSR_ERR_SHAPE, "negative size");
+        if (p.n_rows >= lim - 1 || p.nnz >= lim) return fail(CSR_ERR_SHAPE, "sizes must fit int32 indices");
+        if (p.nnz > 0 && p.n_rows == 0) return fail(CSR_ERR_SHAPE, "entries but no rows");
+        if (!std::isfinite(p.scale)) return fail(CSR_ERR_SHAPE, "scale must be finite");
+        if (!aligned(p.a, 4) || !aligned(p.out, 4)) return fail(CSR_ERR_ALIGN, "fp32 arrays must be 4-byte aligned");
+        if (need_ptrs) {
+            if (!p.row_ptr) return fail(CSR_ERR_NULL, "row_ptr is NULL");
+            if (p.nnz > 0 && (!p.a || !p.out)) return fail(CSR_ERR_NULL, "scores or probs is NULL");
+        }
+        return CSR_OK;
+    }
     const int64_t lim = (int64_t)1 << 31;
     if (p.n_rows < 0 || p.n_cols < 0 || p.nnz < 0) return fail(CSR_ERR_SHAPE, "negative size");
     if (p.n_rows >= lim - 1 || p.n_cols >= lim || p.nnz >= lim) return fail(CSR_ERR_SHAPE, "sizes must fit int32 indices");
@@ -159,6 +173,12 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
         if (s.vec != 8 || s.passes != 1 || s.group_lanes != p.head_dim / 8) return fail("multi-head layout must be vec 8, W = head_dim / 8, 1 pass");
         return CSR_OK;
     }
+    if (p.op == CSR_OP_ROW_SOFTMAX) {
+        if (s.mapping != CSR_MAP_MERGEPATH) return fail("row softmax runs on the merge-path mapping");
+        if (s.vec != 1 || s.passes != 1) return fail("row softmax layout must be vec 1, 1 pass");
+        if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
+        return CSR_OK;
+    }
     if (s.vec != 1 && s.vec != 2 && s.vec != 4) return fail("vec must be 1, 2 or 4");
     if (s.vec > max_vec_f32(p) || p.width % s.vec) return fail("vec not allowed by the operands' width or alignment");
     if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
@@ -195,6 +215,9 @@ WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
     } else if (p.op == CSR_OP_MHA) {
         ml = (size_t)nc * 2 * p.heads * 2 * 4;
         val = (size_t)nc * 2 * p.width * 4;
+    } else if (p.op == CSR_OP_ROW_SOFTMAX) {
+        ml = (size_t)nc * 2 * 2 * 4;
+        val = (size_t)p.n_rows * 2 * 4;  // per-row statistics
     }
     w.carry_val = w.carry_ml + up(ml);
     w.total = w.carry_val + up(val);
@@ -222,6 +245,15 @@ csr_schedule_t default_schedule(const csr_problem_t& p)
         s.passes = 1;
         s.chunk_items = 256;
         s.long_row = 0;
+        return s;
+    }
+    if (p.op == CSR_OP_ROW_SOFTMAX) {
+        // one lane per short row: no cross-lane merge on the common path
+        s.vec = 1;
+        s.group_lanes = 1;
+        s.passes = 1;
+        s.chunk_items = 1024;
+        s.long_row = 32;
         return s;
     }
     s.vec = max_vec_f32(p);
@@ -252,6 +284,15 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
     add(s);
     s.chunk_items = 1024;
     add(s);
+    if (p.op == CSR_OP_ROW_SOFTMAX) {
+        for (int w : {4, 16, 64}) {
+            s = d;
+            s.group_lanes = w;
+            s.long_row = (w == 64) ? 0 : 8 * w;
+            add(s);
+        }
+        return out;
+    }
     // row-group: one group per row, no partition or fix-up; only when no row
     // is long enough to leave a tail or a long fp32 accumulation chain
     if (hist && max_deg <= 4096) {
@@ -350,7 +391,7 @@ bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s,
     if (got != 11 || ver != CSR_SCHEDULE_VERSION) return false;
     for (size_t i = (size_t)n; i < line.size(); ++i)
         if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
-    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_MHA) return false;
+    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_ROW_SOFTMAX) return false;
     if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH) return false;
     t.version = CSR_SCHEDULE_VERSION;
     *sig = sg;

@@ -7,7 +7,7 @@ namespace csrk {
 template <int LPH>
 static hipError_t run_mha(int mapping, int chunk, const MhaArgs& a, hipStream_t s)
 {
-    constexpr int U = 4;
+    constexpr int U = 8;  // entries in flight per wavefront
     if (mapping == 1) {
         const int64_t blocks = (a.n_rows + CSR_WAVES_PER_BLOCK - 1) / CSR_WAVES_PER_BLOCK;
         if (blocks == 0) return hipSuccess;

@@ -1,0 +1,32 @@
+// Standalone CSR row softmax (statistics, split-row merge, normalisation).
+#include "launch.h"
+#include "softmax_kernels.h"
+
+namespace csrk {
+
+template <int D>
+static hipError_t run_softmax(const SoftmaxArgs& a, hipStream_t s)
+{
+    const int64_t blocks = (a.n_chunks + CSR_WAVES_PER_BLOCK - 1) / CSR_WAVES_PER_BLOCK;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_softmax_stats<D>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_softmax_fixup, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_softmax_norm<D>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_softmax(int chunk, const SoftmaxArgs& a, hipStream_t s)
+{
+    switch (chunk) {
+    case 256: return run_softmax<256>(a, s);
+    case 512: return run_softmax<512>(a, s);
+    case 1024: return run_softmax<1024>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace csrk

@@ -50,57 +50,74 @@ __device__ __forceinline__ float head_sum(float v)
     return v;
 }
 
+// Gathers the K and V rows of entries k .. k+U-1 (< ke) of a row.
+template <int LPH, int U>
+__device__ __forceinline__ void mha_issue(const MhaArgs& a, const MhaLanes<LPH>& L, const int32_t* col, int k, int ke,
+                                          uint4 (&kr)[U], uint4 (&vr)[U])
+{
+    const int64_t ld = (int64_t)a.H * a.Dh;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = k + u;
+        const bool ok = (e < ke) && L.valid;
+        const int c = (e < ke) ? col[e] : 0;
+        const int64_t base = (int64_t)c * ld + L.off;
+        if (ok) {
+            kr[u] = *reinterpret_cast<const uint4*>(a.K + base);
+            vr[u] = *reinterpret_cast<const uint4*>(a.V + base);
+        } else {
+            kr[u] = make_uint4(0, 0, 0, 0);
+            vr[u] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Folds entries k .. k+U-1 (< ke), whose K and V rows are in kr / vr, into the
+// online softmax state (m, l, acc) of the row whose query is q.
+template <int LPH, int U>
+__device__ __forceinline__ void mha_fold(const MhaArgs& a, const float (&q)[8], int k, int ke, const uint4 (&kr)[U],
+                                         const uint4 (&vr)[U], float& m, float& l, float (&acc)[8])
+{
+    float t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float kf[8];
+        bf16x8_to_f32(kf, kr[u]);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(q[i], kf[i], s);
+        s = head_sum<LPH>(s) * a.scale;
+        t[u] = (k + u < ke) ? s : -INFINITY;
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, t[u]);
+    const float corr = (l > 0.f) ? exp_neg(m - mn) : 0.f;
+    l *= corr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float p = (k + u < ke) ? exp_neg(t[u] - mn) : 0.f;
+        l += p;
+        float vf[8];
+        bf16x8_to_f32(vf, vr[u]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
+    }
+    m = mn;
+}
+
 // Online-softmax walk over entries [kb, ke) of one row (col indexed by entry id).
 template <int LPH, int U>
 __device__ __forceinline__ void mha_walk(const MhaArgs& a, const MhaLanes<LPH>& L, const float (&q)[8],
                                          const int32_t* col, int kb, int ke, float& m, float& l,
                                          float (&acc)[8])
 {
-    const int64_t ld = (int64_t)a.H * a.Dh;
     for (int k = kb; k < ke; k += U) {
         uint4 kr[U], vr[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int e = k + u;
-            bool ok = (e < ke) && L.valid;
-            int c = (e < ke) ? col[e] : 0;
-            const int64_t base = (int64_t)c * ld + L.off;
-            if (ok) {
-                kr[u] = *reinterpret_cast<const uint4*>(a.K + base);
-                vr[u] = *reinterpret_cast<const uint4*>(a.V + base);
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
-            }
-        }
-        float t[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kf[8];
-            bf16x8_to_f32(kf, kr[u]);
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s = fmaf(q[i], kf[i], s);
-            s = head_sum<LPH>(s) * a.scale;
-            t[u] = (k + u < ke) ? s : -INFINITY;
-        }
-        float mn = m;
-#pragma unroll
-        for (int u = 0; u < U; ++u) mn = fmaxf(mn, t[u]);
-        const float corr = (l > 0.f) ? exp_neg(m - mn) : 0.f;
-        l *= corr;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= corr;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float p = (k + u < ke) ? exp_neg(t[u] - mn) : 0.f;
-            l += p;
-            float vf[8];
-            bf16x8_to_f32(vf, vr[u]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
-        }
-        m = mn;
+        mha_issue<LPH, U>(a, L, col, k, ke, kr, vr);
+        mha_fold<LPH, U>(a, q, k, ke, kr, vr, m, l, acc);
     }
 }
 

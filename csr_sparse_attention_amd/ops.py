@@ -194,6 +194,18 @@ def _mha_problem(row_ptr, col_idx, Q, K, V, out, scale):
                     heads=H, head_dim=D, scale=scale)
 
 
+def _softmax_problem(row_ptr, scores, out, scale):
+    p = CsrProblem()
+    p.op = _ffi.OP_ROW_SOFTMAX
+    p.dtype = _ffi.DTYPE_F32
+    p.n_rows = row_ptr.numel() - 1
+    p.nnz = scores.numel()
+    p.width = 1
+    p.row_ptr, p.a, p.out = _ptr(row_ptr), _ptr(scores), _ptr(out)
+    p.scale = scale
+    return p
+
+
 def _run(problem: CsrProblem, device, schedule, ctx, call):
     ctx = ctx or default_context(device.index)
     lib = _lib()
@@ -289,11 +301,43 @@ def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, o
     return out
 
 
+def row_softmax(row_ptr, scores, *, scale: float = 1.0, out=None, schedule: Optional[CsrSchedule] = None,
+                ctx: Optional[Context] = None) -> torch.Tensor:
+    """Per-row softmax over the stored entries: out[e] = exp(scale * s_e - m_i) /
+    sum over row i of exp(scale * s - m_i).  ``out`` may be ``scores`` (in place)."""
+    _pattern(row_ptr, row_ptr)
+    if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous 1-D fp32 tensor")
+    if out is None:
+        out = torch.empty_like(scores)
+    p = _softmax_problem(row_ptr, scores, out, scale)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_row_softmax(ctx.handle, p.n_rows, p.nnz, p.row_ptr, p.a, ctypes.c_float(scale), p.out,
+                                      _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _run(p, scores.device, schedule, ctx, call)
+    return out
+
+
+def attention_pipeline(row_ptr, col_idx, Q, K, V, *, scale: float = 1.0, fused: bool = True,
+                       ctx: Optional[Context] = None) -> torch.Tensor:
+    """Single-head fp32 CSR attention from Q [n_rows, d], K [n_cols, d],
+    V [n_cols, F] as the composition of library calls SDDMM -> row-softmax ->
+    SpMM.  fused=True runs SDDMM then the fused softmax-aggregation
+    (``attention``); fused=False runs the three stages separately."""
+    scores = sddmm(row_ptr, col_idx, Q, K, ctx=ctx)
+    if fused:
+        return attention(row_ptr, col_idx, scores, V, scale=scale, ctx=ctx)
+    probs = row_softmax(row_ptr, scores, scale=scale, out=scores, ctx=ctx)
+    return spmm(row_ptr, col_idx, probs, V, ctx=ctx)
+
+
 def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0) -> CsrProblem:
     """The csr_problem_t of a call, for select() / workspace_size() /
     default_schedule(): op is 'spmm' (vals, X), 'sddmm' (U, V), 'attention'
     (edge_scores, node_value) or 'mha' (Q, K, V)."""
-    _pattern(row_ptr, col_idx)
+    _pattern(row_ptr, row_ptr if col_idx is None else col_idx)
     n_rows = row_ptr.numel() - 1
     if op == "spmm":
         vals, X = operands
@@ -307,6 +351,10 @@ def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 
         s, nv = operands
         out = out if out is not None else torch.empty((n_rows, nv.shape[1]), dtype=torch.float32, device=nv.device)
         return _attention_problem(row_ptr, col_idx, s, nv, out, scale), out
+    if op == "row_softmax":
+        (scores,) = operands
+        out = out if out is not None else torch.empty_like(scores)
+        return _softmax_problem(row_ptr, scores, out, scale), out
     if op == "mha":
         Q, K, V = operands
         out = out if out is not None else torch.empty((n_rows,) + tuple(Q.shape[1:]), dtype=torch.float32,

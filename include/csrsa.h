@@ -78,7 +78,8 @@ enum csr_op {
     CSR_OP_SPMM = 1,      /* Y = A X */
     CSR_OP_SDDMM = 2,     /* out_e = <U[row_e], V[col_e]> */
     CSR_OP_ATTENTION = 3, /* scores given: out = softmax_row(scale * S) V */
-    CSR_OP_MHA = 4        /* multi-head, scores = scale * <Q_i, K_j> per head */
+    CSR_OP_MHA = 4,       /* multi-head, scores = scale * <Q_i, K_j> per head */
+    CSR_OP_ROW_SOFTMAX = 5 /* p_e = softmax over the row's entries of scale * s */
 };
 
 enum csr_dtype { CSR_DTYPE_F32 = 0, CSR_DTYPE_BF16 = 1 };
@@ -138,6 +139,8 @@ typedef struct csr_schedule_s {
  *   op = CSR_OP_MHA:       a = Q, b = K, c = V (bf16 [n, heads, head_dim]), heads,
  *                          head_dim, width = heads * head_dim, out fp32 [n_rows, width],
  *                          scale
+ *   op = CSR_OP_ROW_SOFTMAX: a = scores fp32 [nnz], out = probabilities fp32 [nnz],
+ *                          width = 1, scale (n_cols is not used)
  */
 typedef struct csr_problem_s {
     int32_t op;
@@ -243,6 +246,19 @@ int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t
                       int32_t heads, int32_t head_dim, float scale, float* out,
                       const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/* CSR row softmax, the middle stage of the unfused pipeline SDDMM ->
+ * row-softmax -> SpMM (AutoSAGE page, Abstract): for every stored entry e of
+ * row i, probs[e] = exp(scale * scores[e] - m_i) / sum over the row's entries
+ * of exp(scale * scores - m_i), m_i the row maximum of scale * scores.
+ * scores, probs: fp32 [nnz] (may alias for an in-place update; an in-place
+ * call with sched == NULL then picks its schedule by the cost model alone,
+ * since a micro-probe would overwrite its own input).  Rows without entries
+ * have nothing to write.  Schedules: merge-path mapping only
+ * (vec 1, passes 1, group_lanes = lanes per short row). */
+int csr_row_softmax(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
+                    const float* scores, float scale, float* probs, const csr_schedule_t* sched,
+                    void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Schedule selection and cache (AutoSAGE page, Abstract: input-aware choice

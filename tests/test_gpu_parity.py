@@ -475,3 +475,52 @@ def test_validation_flag_rejects_bad_columns():
     ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, None, np.ones((300, 8), np.float32))
     assert_close(Y.cpu().numpy(), ref, mag)
     ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# unfused pipeline: row softmax and SDDMM -> row-softmax -> SpMM
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scale", [1.0, 0.125])
+def test_row_softmax_every_schedule(skew, scale):
+    csr = skew
+    rng = np.random.default_rng(500)
+    sc = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    _, _, ref = oracle.attention(csr.row_ptr, csr.col_idx, sc, np.zeros((csr.n_cols, 1), np.float32), scale,
+                                 want_probs=True, threads=oracle.default_threads())
+    rp = dev(csr.row_ptr)
+    sd = dev(sc)
+    p, _ = csa.make_problem("row_softmax", rp, None, sd, scale=scale)
+    base = csa.default_schedule(p)
+    scheds = csa.candidates(p)
+    for D in (256, 512):
+        s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+        s.chunk_items = D
+        scheds.append(s)
+    for s in scheds:
+        out = csa.row_softmax(rp, sd, scale=scale, schedule=s).cpu().numpy()
+        err = np.max(np.abs(out.astype(np.float64) - ref) / ref)
+        assert err < 1e-5, (sched_id(s), err)
+        sums = np.add.reduceat(out.astype(np.float64), csr.row_ptr[:-1][csr.degrees() > 0])
+        assert np.max(np.abs(sums - 1)) < 1e-5
+    # in place
+    x = dev(sc)
+    csa.row_softmax(rp, x, scale=scale, out=x)
+    assert np.max(np.abs(x.cpu().numpy() - ref) / ref) < 1e-5
+
+
+def test_attention_pipeline_unfused_equals_fused():
+    csr = skew_graph(14, n_rows=2000, n_cols=20_000, giant=12_000)
+    rng = np.random.default_rng(14)
+    d, F = 32, 48
+    Q = rng.standard_normal((csr.n_rows, d)).astype(np.float32)
+    K = rng.standard_normal((csr.n_cols, d)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    scale = 1.0 / np.sqrt(d)
+    # oracle: SDDMM then softmax attention over those scores, in float64
+    scores, _ = oracle.sddmm(csr.row_ptr, csr.col_idx, Q, K, threads=oracle.default_threads())
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, scores, V, scale, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    for fused in (True, False):
+        out = csa.attention_pipeline(rp, ci, dev(Q), dev(K), dev(V), scale=scale, fused=fused)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_F32, f"fused={fused}")
