@@ -20,6 +20,7 @@ from ._ffi import (  # noqa: F401,E402
     LIB_PATH,
     MAP_MERGEPATH,
     MAP_ROWGROUP,
+    MAP_SEGSCAN,
     CTX_NO_PROBE,
     CTX_VALIDATE,
     load as load_library,

@@ -21,7 +21,7 @@ CSR_ERR_NO_CACHE_ENTRY = -8
 
 OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX = 1, 2, 3, 4, 5
 DTYPE_F32, DTYPE_BF16 = 0, 1
-MAP_ROWGROUP, MAP_MERGEPATH = 1, 2
+MAP_ROWGROUP, MAP_MERGEPATH, MAP_SEGSCAN = 1, 2, 3
 CTX_VALIDATE, CTX_NO_PROBE = 1, 2
 SELECT_MODES = {"auto": 0, "replay": 1, "probe": 2, "estimate": 3}
 SCHEDULE_VERSION = 1

@@ -156,7 +156,7 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
 
     const csrh::WsLayout L = csrh::ws_layout(p, s);
     int32_t* coords = reinterpret_cast<int32_t*>(ws + L.coords);
-    if (s.mapping == CSR_MAP_MERGEPATH) {
+    if (s.mapping != CSR_MAP_ROWGROUP) {
         CSR_HIP(ctx, csrk::launch_merge_path(p.row_ptr, p.n_rows, p.nnz, s.chunk_items, L.n_chunks, coords, st));
     }
 
@@ -197,7 +197,7 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
         const int lph = p.head_dim / 8;
         CSR_HIP(ctx, csrk::launch_mha(s.mapping, lph, s.chunk_items, a, st));
-        if (s.mapping == CSR_MAP_MERGEPATH) CSR_HIP(ctx, csrk::launch_mha_fixup(lph, a, st));
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_mha_fixup(lph, a, st));
         return CSR_OK;
     }
 
@@ -230,10 +230,10 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     a.ldy = p.ld_out;
     if (p.op == CSR_OP_SPMM) {
         CSR_HIP(ctx, csrk::launch_spmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
-        if (s.mapping == CSR_MAP_MERGEPATH) CSR_HIP(ctx, csrk::launch_spmm_fixup(s.vec, s.passes, a, st));
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_spmm_fixup(s.vec, s.passes, a, st));
     } else {
         CSR_HIP(ctx, csrk::launch_attention(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
-        if (s.mapping == CSR_MAP_MERGEPATH) CSR_HIP(ctx, csrk::launch_attention_fixup(s.vec, s.passes, a, st));
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_attention_fixup(s.vec, s.passes, a, st));
     }
     return CSR_OK;
 }

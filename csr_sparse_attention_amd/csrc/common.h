@@ -54,6 +54,47 @@ __device__ __forceinline__ void vstore(float* p, const float (&s)[VEC])
 __device__ __forceinline__ int ld_stream(const int32_t* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float ld_stream(const float* p) { return __builtin_nontemporal_load(p); }
 
+// Stages a merge-path chunk in LDS with the 64 lanes of a wave: row_ptr
+// entries rp_src[0 .. nr) (nr <= NR * 64) and, for the chunk's entries,
+// col_src[0 .. ne) and optionally val_src[0 .. ne) (ne <= NE * 64; a null
+// val_src with FILL set stores 1.0).  Every global load is issued before the
+// first LDS store, so the loads of one wave overlap instead of each waiting
+// for the previous one.  The per-entry arrays are read once: non-temporal.
+template <int NR, int NE, bool VALS, typename V>
+__device__ __forceinline__ void stage_chunk(int32_t* rp_dst, const int32_t* rp_src, int nr, int32_t* col_dst,
+                                            const int32_t* col_src, V* val_dst, const V* val_src, int ne)
+{
+    const int lane = __lane_id();
+    int32_t r[NR], c[NE];
+    V v[NE];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const int i = lane + k * 64;
+        if (i < nr) r[k] = rp_src[i];
+    }
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int i = lane + k * 64;
+        if (i < ne) {
+            if (col_src) c[k] = __builtin_nontemporal_load(col_src + i);
+            if constexpr (VALS) v[k] = val_src ? __builtin_nontemporal_load(val_src + i) : V(1);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const int i = lane + k * 64;
+        if (i < nr) rp_dst[i] = r[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int i = lane + k * 64;
+        if (i < ne) {
+            if (col_src) col_dst[i] = c[k];
+            if constexpr (VALS) val_dst[i] = v[k];
+        }
+    }
+}
+
 // exp(x) for x <= 0 as 2^(x log2 e) on the hardware exp2 unit.
 __device__ __forceinline__ float exp_neg(float x)
 {
@@ -102,6 +143,16 @@ __device__ __forceinline__ void softmax_merge_xor(float& m, float& l, int from, 
         m = mm;
         l = a + b;
     }
+}
+
+// The fix-up kernels give each wavefront a window of 64 consecutive chunks:
+// one coalesced load tells which of them hold work (a split row ending
+// there), and the wave then handles those one after the other.  Returns the
+// window's first chunk, or -1 when the window is past the last chunk.
+__device__ __forceinline__ int64_t fixup_window(int64_t n_chunks)
+{
+    const int64_t base = ((int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + threadIdx.x / CSR_WAVE) * CSR_WAVE;
+    return base < n_chunks ? base : -1;
 }
 
 } // namespace csrk

@@ -280,16 +280,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
         y0 = a.part[2 * chunk + 1];
         x1 = a.part[2 * chunk + 2];
         y1 = a.part[2 * chunk + 3];
-        // rows x0 .. x1-1 end in this chunk; row x1 may own entries [.., y1)
-        int rpx1 = (x1 < a.n_rows) ? a.row_ptr[x1] : y1;
-        slotB = (x1 < a.n_rows) && (max(rpx1, y0) < y1);
-        nrow = x1 - x0 + (slotB ? 1 : 0);
-        for (int i = lane; i <= nrow; i += CSR_WAVE) sh.rp[wave][i] = a.row_ptr[x0 + i];
-        const int ne = y1 - y0;
-        for (int i = lane; i < ne; i += CSR_WAVE) {
-            sh.col[wave][i] = ld_stream(a.col_idx + y0 + i);
-            if constexpr (OP != Op::Sddmm) sh.ev[wave][i] = a.ev ? ld_stream(a.ev + y0 + i) : 1.f;
-        }
+        // rows x0 .. x1-1 end in this chunk; row x1 may own entries [.., y1).
+        // Rows x0 .. x1 (x1 only if it exists): row_ptr[x0 .. min(x1, n_rows - 1) + 1]
+        const int nr = (x1 < a.n_rows ? x1 : (int)a.n_rows - 1) - x0 + 2;
+        stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, D / CSR_WAVE, OP != Op::Sddmm, float>(
+            sh.rp[wave], a.row_ptr + x0, nr, sh.col[wave], a.col_idx + y0, sh.ev[wave],
+            a.ev ? a.ev + y0 : nullptr, y1 - y0);
     }
     __syncthreads();
     if (!active) return;
@@ -297,6 +293,8 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
     const int32_t* rp = sh.rp[wave];
     const int32_t* col = sh.col[wave] - y0;  // indexed by absolute entry id
     const float* ev = sh.ev[wave] - y0;
+    slotB = (x1 < a.n_rows) && (max(rp[x1 - x0], y0) < y1);
+    nrow = x1 - x0 + (slotB ? 1 : 0);
     slotA = (x0 < x1) && (rp[0] < y0);
     if (lane == 0) {
         a.carry_row[2 * chunk] = slotA ? x0 : -1;
@@ -380,6 +378,184 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Entry-parallel mapping for small widths (segmented scan)
+// ---------------------------------------------------------------------------
+// The chunk is staged as in the merge-path mapping, but its entries are
+// dealt to the lanes in order: lane l takes entries b + l, b + 64 + l, ...,
+// and each lane gathers the whole (small) feature row of its entry, so a
+// batch of 64 entries costs one round of gathers whatever the row lengths.
+// SpMM then sums the products of each row with an inclusive segmented scan
+// across the lanes (segments = runs of lanes holding the same row) and a
+// carry between batches; the last lane of a row's run writes the row.  SDDMM
+// needs no reduction across entries: each lane forms its entry's dot product.
+template <Op OP, int VEC, int NV, int U, int D>
+__global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
+{
+    __shared__ MpShared<D> sh;
+    const int wave = threadIdx.x / CSR_WAVE;
+    const int lane = lane_id();
+    const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
+    const bool active = chunk < a.n_chunks;
+    int x0 = 0, y0 = 0, x1 = 0, y1 = 0;
+    if (active) {
+        x0 = a.part[2 * chunk];
+        y0 = a.part[2 * chunk + 1];
+        x1 = a.part[2 * chunk + 2];
+        y1 = a.part[2 * chunk + 3];
+        const int nr = (x1 < a.n_rows ? x1 : (int)a.n_rows - 1) - x0 + 2;
+        stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, D / CSR_WAVE, OP != Op::Sddmm, float>(
+            sh.rp[wave], a.row_ptr + x0, nr, sh.col[wave], a.col_idx + y0, sh.ev[wave],
+            a.ev ? a.ev + y0 : nullptr, y1 - y0);
+    }
+    __syncthreads();
+    if (!active) return;
+    const int32_t* rp = sh.rp[wave];
+    const int32_t* col = sh.col[wave] - y0;
+    const float* ev = sh.ev[wave] - y0;
+    const bool slotB = (x1 < a.n_rows) && (max(rp[x1 - x0], y0) < y1);
+    const int nrow = x1 - x0 + (slotB ? 1 : 0);
+    const bool slotA = (x0 < x1) && (rp[0] < y0);
+    if (lane == 0) {
+        a.carry_row[2 * chunk] = slotA ? x0 : -1;
+        a.carry_row[2 * chunk + 1] = slotB ? x1 : -1;
+    }
+    const int nend = x1 - x0;
+    const int F = a.F;
+
+    // chunk row index of entry e: the largest i < nrow with rp[i] <= e
+    auto row_of = [&](int e) {
+        int lo = 0, hi = nrow - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (rp[mid] <= e)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        return lo;
+    };
+    auto load_row = [&](float (&v)[NV][VEC], const float* src) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (j * VEC < F) {
+                vload<VEC>(v[j], src + j * VEC);
+            } else {
+#pragma unroll
+                for (int t = 0; t < VEC; ++t) v[j][t] = 0.f;
+            }
+        }
+    };
+
+    if constexpr (OP == Op::Sddmm) {
+        for (int b = y0; b < y1; b += CSR_WAVE * U) {
+            float uv[U][NV][VEC], xv[U][NV][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = b + u * CSR_WAVE + lane;
+                if (e < y1) {
+                    load_row(uv[u], a.U + ((int64_t)x0 + row_of(e)) * a.ldu);
+                    load_row(xv[u], a.X + (int64_t)col[e] * a.ldx);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = b + u * CSR_WAVE + lane;
+                if (e < y1) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int j = 0; j < NV; ++j)
+#pragma unroll
+                        for (int t = 0; t < VEC; ++t) d = fmaf(uv[u][j][t], xv[u][j][t], d);
+                    a.Y[e] = d;
+                }
+            }
+        }
+    } else {
+        // a row's result, written by one lane: final row, or a piece of a split row
+        auto emit = [&](int i, const float (&v)[NV][VEC]) {
+            float* dst;
+            if (i < nend && rp[i] >= y0)
+                dst = a.Y + ((int64_t)x0 + i) * a.ldy;
+            else
+                dst = a.carry_val + (2 * chunk + ((i == nend) ? 1 : 0)) * F;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                if (j * VEC < F) vstore<VEC>(dst + j * VEC, v[j]);
+        };
+        // rows without entries in this chunk: zero rows (or zero pieces)
+        for (int i = lane; i < nrow; i += CSR_WAVE) {
+            if (max(rp[i], y0) == min(rp[i + 1], y1)) {
+                float z[NV][VEC];
+                zero(z);
+                emit(i, z);
+            }
+        }
+        float carry[NV][VEC];
+        zero(carry);
+        int carry_row = -1;
+        for (int b = y0; b < y1; b += CSR_WAVE * U) {
+            float xv[U][NV][VEC];
+            float w[U];
+            int ri[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = b + u * CSR_WAVE + lane;
+                const bool ok = e < y1;
+                w[u] = ok ? ev[e] : 0.f;
+                ri[u] = ok ? row_of(e) : -1 - lane;  // a lane past the end forms no segment
+                if (ok) {
+                    load_row(xv[u], a.X + (int64_t)col[e] * a.ldx);
+                } else {
+                    zero(xv[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = b + u * CSR_WAVE + lane;
+                const int i = ri[u];
+                float v[NV][VEC];
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int t = 0; t < VEC; ++t) v[j][t] = w[u] * xv[u][j][t];
+                // inclusive segmented scan across lanes
+#pragma unroll
+                for (int off = 1; off < CSR_WAVE; off <<= 1) {
+                    const int io = __shfl_up(i, off, CSR_WAVE);
+                    const bool join = lane >= off && io == i;
+#pragma unroll
+                    for (int j = 0; j < NV; ++j)
+#pragma unroll
+                        for (int t = 0; t < VEC; ++t) {
+                            const float o = __shfl_up(v[j][t], off, CSR_WAVE);
+                            if (join) v[j][t] += o;
+                        }
+                }
+                if (i == carry_row) {
+#pragma unroll
+                    for (int j = 0; j < NV; ++j)
+#pragma unroll
+                        for (int t = 0; t < VEC; ++t) v[j][t] += carry[j][t];
+                }
+                const int inext = __shfl_down(i, 1, CSR_WAVE);
+                const bool ok = e < y1;
+                const bool tail = ok && (lane == CSR_WAVE - 1 || inext != i);
+                const bool row_last = ok && (e == min(rp[i + 1], y1) - 1);
+                if (tail && row_last) emit(i, v);
+                // the run of the last lane continues into the next batch unless its row ended
+                const int last_i = __shfl(i, CSR_WAVE - 1, CSR_WAVE);
+                const bool last_done = __shfl((int)row_last, CSR_WAVE - 1, CSR_WAVE) != 0;
+                carry_row = last_done ? -1 : last_i;
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int t = 0; t < VEC; ++t) carry[j][t] = __shfl(v[j][t], CSR_WAVE - 1, CSR_WAVE);
+            }
+        }
+    }
+}
+
 // Fix-up of rows split across chunks.  One wave per chunk c whose slot A holds
 // a row r: the pieces of r are slot B of chunks k0 .. c-1 (the run of chunks
 // right before c whose slot B holds r) and slot A of c.  SpMM adds them;
@@ -387,14 +563,9 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
 // The groups of the wave take interleaved pieces and are reduced in a fixed
 // order, so the result is reproducible.
 template <Op OP, int VEC, int NV>
-__global__ __launch_bounds__(CSR_BLOCK) void k_fixup(Fp32Args a)
+__device__ __forceinline__ void fixup_one(const Fp32Args& a, int64_t c, int r)
 {
-    const int wave = threadIdx.x / CSR_WAVE;
     const int lane = lane_id();
-    const int64_t c = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
-    if (c >= a.n_chunks) return;
-    const int r = a.carry_row[2 * c];
-    if (r < 0) return;
 
     // k0: first chunk of the run of slot-B pieces of row r ending at c - 1
     int64_t k0 = c;
@@ -456,6 +627,22 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_fixup(Fp32Args a)
         store_row_div<VEC, NV>(dst, acc, L, a.F, lsum);
     else
         store_row<VEC, NV>(dst, acc, L, a.F, 1.f);
+}
+
+template <Op OP, int VEC, int NV>
+__global__ __launch_bounds__(CSR_BLOCK) void k_fixup(Fp32Args a)
+{
+    const int64_t base = fixup_window(a.n_chunks);
+    if (base < 0) return;
+    const int lane = lane_id();
+    const int64_t mine = base + lane;
+    const int rl = (mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
+    uint64_t todo = __ballot(rl >= 0);
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        fixup_one<OP, VEC, NV>(a, base + j, __shfl(rl, j, CSR_WAVE));
+    }
 }
 
 } // namespace csrk

@@ -159,11 +159,17 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
     };
     if (s.version != CSR_SCHEDULE_VERSION) return fail("schedule version mismatch");
     if (s.op != p.op) return fail("schedule is for another op");
-    if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH) return fail("unknown mapping");
+    if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH && s.mapping != CSR_MAP_SEGSCAN)
+        return fail("unknown mapping");
+    if (s.mapping == CSR_MAP_SEGSCAN) {
+        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return fail("the segmented-scan mapping serves SpMM and SDDMM");
+        if (s.group_lanes != 1 || s.passes > 4 || s.long_row != 0)
+            return fail("segmented-scan schedules take group_lanes 1, passes <= 4, long_row 0");
+    }
     if (s.flags != 0) return fail("unknown schedule flags");
     for (int r : s.reserved)
         if (r != 0) return fail("reserved schedule fields must be 0");
-    if (s.mapping == CSR_MAP_MERGEPATH) {
+    if (s.mapping != CSR_MAP_ROWGROUP) {
         if (s.chunk_items != 256 && s.chunk_items != 512 && s.chunk_items != 1024) return fail("chunk_items must be 256, 512 or 1024");
         if (s.long_row < 0) return fail("long_row must be >= 0");
     } else if (s.chunk_items != 0 || s.long_row != 0) {
@@ -175,6 +181,7 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
     }
     if (p.op == CSR_OP_ROW_SOFTMAX) {
         if (s.mapping != CSR_MAP_MERGEPATH) return fail("row softmax runs on the merge-path mapping");
+        if (s.chunk_items > 512) return fail("row softmax chunks hold at most 512 items");
         if (s.vec != 1 || s.passes != 1) return fail("row softmax layout must be vec 1, 1 pass");
         if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
         return CSR_OK;
@@ -201,7 +208,7 @@ WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
     WsLayout w{};
     w.coords = kHeadBytes;
     w.total = kHeadBytes;
-    if (s.mapping != CSR_MAP_MERGEPATH) return w;
+    if (s.mapping == CSR_MAP_ROWGROUP) return w;
     const int64_t nc = n_chunks_for(p, s.chunk_items);
     w.n_chunks = nc;
     w.carry_row = w.coords + up((size_t)(nc + 1) * 2 * 4);
@@ -252,7 +259,7 @@ csr_schedule_t default_schedule(const csr_problem_t& p)
         s.vec = 1;
         s.group_lanes = 1;
         s.passes = 1;
-        s.chunk_items = 1024;
+        s.chunk_items = 512;
         s.long_row = 32;
         return s;
     }
@@ -316,6 +323,18 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
             s = d;
             s.long_row = d.long_row * 4;
             add(s);
+        }
+        // small widths: lanes over entries, segmented scan
+        if (p.op != CSR_OP_ATTENTION && p.width <= 4 * d.vec) {
+            for (int D : {512, 256}) {
+                s = d;
+                s.mapping = CSR_MAP_SEGSCAN;
+                s.group_lanes = 1;
+                s.passes = (int)((p.width + d.vec - 1) / d.vec);
+                s.chunk_items = D;
+                s.long_row = 0;
+                add(s);
+            }
         }
     }
     return out;
@@ -392,7 +411,7 @@ bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s,
     for (size_t i = (size_t)n; i < line.size(); ++i)
         if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
     if (t.op < CSR_OP_SPMM || t.op > CSR_OP_ROW_SOFTMAX) return false;
-    if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH) return false;
+    if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH && t.mapping != CSR_MAP_SEGSCAN) return false;
     t.version = CSR_SCHEDULE_VERSION;
     *sig = sg;
     *s = t;

@@ -28,7 +28,7 @@ static hipError_t run_mha(int mapping, int chunk, const MhaArgs& a, hipStream_t 
 template <int LPH>
 static hipError_t run_mha_fixup(const MhaArgs& a, hipStream_t s)
 {
-    const int64_t blocks = (a.n_chunks + CSR_WAVES_PER_BLOCK - 1) / CSR_WAVES_PER_BLOCK;
+    const int64_t blocks = (a.n_chunks + CSR_WAVE * CSR_WAVES_PER_BLOCK - 1) / (CSR_WAVE * CSR_WAVES_PER_BLOCK);
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_mha_fixup<LPH>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
     return hipGetLastError();

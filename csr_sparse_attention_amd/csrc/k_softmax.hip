@@ -1,4 +1,5 @@
-// Standalone CSR row softmax (statistics, split-row merge, normalisation).
+// Standalone CSR row softmax (statistics and in-chunk normalisation,
+// split-row merge, split-row normalisation).
 #include "launch.h"
 #include "softmax_kernels.h"
 
@@ -9,13 +10,14 @@ static hipError_t run_softmax(const SoftmaxArgs& a, hipStream_t s)
 {
     const int64_t blocks = (a.n_chunks + CSR_WAVES_PER_BLOCK - 1) / CSR_WAVES_PER_BLOCK;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_softmax_stats<D>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    hipLaunchKernelGGL((k_softmax_main<D>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_softmax_fixup, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    const int64_t fblocks = (a.n_chunks + CSR_WAVE * CSR_WAVES_PER_BLOCK - 1) / (CSR_WAVE * CSR_WAVES_PER_BLOCK);
+    hipLaunchKernelGGL(k_softmax_fixup, dim3((unsigned)fblocks), dim3(CSR_BLOCK), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_softmax_norm<D>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    hipLaunchKernelGGL(k_softmax_split, dim3((unsigned)fblocks), dim3(CSR_BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
@@ -24,7 +26,6 @@ hipError_t launch_row_softmax(int chunk, const SoftmaxArgs& a, hipStream_t s)
     switch (chunk) {
     case 256: return run_softmax<256>(a, s);
     case 512: return run_softmax<512>(a, s);
-    case 1024: return run_softmax<1024>(a, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -185,16 +185,17 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mha_mergepath(MhaArgs a)
         y0 = a.part[2 * chunk + 1];
         x1 = a.part[2 * chunk + 2];
         y1 = a.part[2 * chunk + 3];
-        int rpx1 = (x1 < a.n_rows) ? a.row_ptr[x1] : y1;
-        slotB = (x1 < a.n_rows) && (max(rpx1, y0) < y1);
-        nrow = x1 - x0 + (slotB ? 1 : 0);
-        for (int i = lane; i <= nrow; i += CSR_WAVE) sh.rp[wave][i] = a.row_ptr[x0 + i];
-        for (int i = lane; i < y1 - y0; i += CSR_WAVE) sh.col[wave][i] = ld_stream(a.col_idx + y0 + i);
+        // rows x0 .. x1 (x1 only if it exists): row_ptr[x0 .. min(x1, n_rows - 1) + 1]
+        const int nr = (x1 < a.n_rows ? x1 : (int)a.n_rows - 1) - x0 + 2;
+        stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, D / CSR_WAVE, false, int32_t>(
+            sh.rp[wave], a.row_ptr + x0, nr, sh.col[wave], a.col_idx + y0, nullptr, nullptr, y1 - y0);
     }
     __syncthreads();
     if (!active) return;
     const int32_t* rp = sh.rp[wave];
     const int32_t* col = sh.col[wave] - y0;
+    slotB = (x1 < a.n_rows) && (max(rp[x1 - x0], y0) < y1);
+    nrow = x1 - x0 + (slotB ? 1 : 0);
     const bool slotA = (x0 < x1) && (rp[0] < y0);
     if (lane == 0) {
         a.carry_row[2 * chunk] = slotA ? x0 : -1;
@@ -231,14 +232,9 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mha_mergepath(MhaArgs a)
 
 // Fix-up: merge the (m, l, acc) pieces of each split row in chunk order.
 template <int LPH>
-__global__ __launch_bounds__(CSR_BLOCK) void k_mha_fixup(MhaArgs a)
+__device__ __forceinline__ void mha_fixup_one(const MhaArgs& a, int64_t c, int r)
 {
-    const int wave = threadIdx.x / CSR_WAVE;
     const int lane = lane_id();
-    const int64_t c = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
-    if (c >= a.n_chunks) return;
-    const int r = a.carry_row[2 * c];
-    if (r < 0) return;
     int64_t k0 = c;
     while (true) {
         int64_t idx = k0 - 1 - lane;
@@ -271,6 +267,22 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mha_fixup(MhaArgs a)
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
     }
     store8(a.out + (int64_t)r * ld + L.off, acc, lsum);
+}
+
+template <int LPH>
+__global__ __launch_bounds__(CSR_BLOCK) void k_mha_fixup(MhaArgs a)
+{
+    const int64_t base = fixup_window(a.n_chunks);
+    if (base < 0) return;
+    const int lane = lane_id();
+    const int64_t mine = base + lane;
+    const int rl = (mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
+    uint64_t todo = __ballot(rl >= 0);
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        mha_fixup_one<LPH>(a, base + j, __shfl(rl, j, CSR_WAVE));
+    }
 }
 
 } // namespace csrk

@@ -4,12 +4,17 @@
 // l_i the sum of exponentials.
 //
 // Three kernels over the merge-path chunks of the fp32 kernels:
-//   k_softmax_stats  - (m, l) of every row segment of a chunk (a long segment
-//                      by the whole wave, short ones by groups of W lanes);
-//                      complete rows write their statistics, split rows leave
-//                      (m, l) pieces in the carry slots;
-//   k_softmax_fixup  - merges the pieces of each split row in chunk order;
-//   k_softmax_norm   - writes p_e for every entry of the chunk.
+//   k_softmax_main   - stages the chunk's row_ptr and scores in LDS, forms
+//                      (m, l) of every row segment (a long segment by the
+//                      whole wave, short ones by groups of W lanes) into LDS,
+//                      then writes p_e for every entry of the rows that lie
+//                      wholly in the chunk, lanes over consecutive entries
+//                      (coalesced); the segments of rows cut by a chunk
+//                      boundary leave (m, l) pieces in the carry slots;
+//   k_softmax_fixup  - merges the pieces of each split row in chunk order into
+//                      that row's statistics;
+//   k_softmax_split  - writes p_e for the entries of split rows only.
+// The scores are read once (plus the entries of split rows a second time).
 #pragma once
 
 #include "args.h"
@@ -21,107 +26,99 @@ template <int D>
 struct SmShared {
     int32_t rp[CSR_WAVES_PER_BLOCK][D + 2];
     float s[CSR_WAVES_PER_BLOCK][D];
+    float m[CSR_WAVES_PER_BLOCK][D + 2];
+    float l[CSR_WAVES_PER_BLOCK][D + 2];
+    uint16_t ri[CSR_WAVES_PER_BLOCK][D];  // row index (within the chunk) of each entry
 };
 
-// (m, l) of scale * s[e] over e = kb + t, kb + t + n, ... merged over the n
-// lanes of an aligned lane set.
+// (m, l) of scale * s[e] over e = kb + t, kb + t + n, ... for the n lanes of
+// an aligned lane set: the maximum first (butterfly of max), then the sum of
+// exponentials (butterfly of sums), so the cross-lane steps need no rescaling.
 __device__ __forceinline__ void sm_stats(const float* s, int kb, int ke, int t, int n, float scale, float& m, float& l)
 {
     m = -INFINITY;
+    for (int e = kb + t; e < ke; e += n) m = fmaxf(m, s[e] * scale);
+    for (int k = 1; k < n; k <<= 1) m = fmaxf(m, shfl_xor(m, k));
     l = 0.f;
-    for (int e = kb + t; e < ke; e += n) {
-        const float x = s[e] * scale;
-        if (x > m) {
-            l = l * exp_neg(m - x) + 1.f;
-            m = x;
-        } else {
-            l += exp_neg(x - m);
-        }
-    }
-    for (int k = 1; k < n; k <<= 1) {
-        const float m2 = shfl_xor(m, k), l2 = shfl_xor(l, k);
-        const float mm = fmaxf(m, m2);
-        const float a = (l > 0.f) ? l * exp_neg(m - mm) : 0.f;
-        const float b = (l2 > 0.f) ? l2 * exp_neg(m2 - mm) : 0.f;
-        m = mm;
-        l = a + b;
-    }
+    for (int e = kb + t; e < ke; e += n) l += exp_neg(s[e] * scale - m);
+    for (int k = 1; k < n; k <<= 1) l += shfl_xor(l, k);
 }
 
 template <int D>
-__device__ __forceinline__ bool sm_stage(const SoftmaxArgs& a, SmShared<D>& sh, int wave, int lane, int64_t chunk,
-                                         int& x0, int& y0, int& x1, int& y1, int& nrow, bool& slotB)
+__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_main(SoftmaxArgs a)
 {
+    __shared__ SmShared<D> sh;
+    const int wave = threadIdx.x / CSR_WAVE, lane = lane_id();
+    const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
     const bool active = chunk < a.n_chunks;
+    int x0 = 0, y0 = 0, x1 = 0, y1 = 0, nrow = 0;
+    bool slotB = false;
     if (active) {
         x0 = a.part[2 * chunk];
         y0 = a.part[2 * chunk + 1];
         x1 = a.part[2 * chunk + 2];
         y1 = a.part[2 * chunk + 3];
-        const int rpx1 = (x1 < a.n_rows) ? a.row_ptr[x1] : y1;
-        slotB = (x1 < a.n_rows) && (max(rpx1, y0) < y1);
-        nrow = x1 - x0 + (slotB ? 1 : 0);
-        for (int i = lane; i <= nrow; i += CSR_WAVE) sh.rp[wave][i] = a.row_ptr[x0 + i];
-        for (int i = lane; i < y1 - y0; i += CSR_WAVE) sh.s[wave][i] = ld_stream(a.scores + y0 + i);
+        // rows x0 .. x1 (x1 only if it exists): row_ptr[x0 .. min(x1, n_rows - 1) + 1]
+        const int nr = (x1 < a.n_rows ? x1 : (int)a.n_rows - 1) - x0 + 2;
+        stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, D / CSR_WAVE, true, float>(
+            sh.rp[wave], a.row_ptr + x0, nr, nullptr, nullptr, sh.s[wave], a.scores + y0, y1 - y0);
     }
     __syncthreads();
-    return active;
-}
-
-template <int D>
-__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_stats(SoftmaxArgs a)
-{
-    __shared__ SmShared<D> sh;
-    const int wave = threadIdx.x / CSR_WAVE, lane = lane_id();
-    const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
-    int x0 = 0, y0 = 0, x1 = 0, y1 = 0, nrow = 0;
-    bool slotB = false;
-    if (!sm_stage<D>(a, sh, wave, lane, chunk, x0, y0, x1, y1, nrow, slotB)) return;
     const int32_t* rp = sh.rp[wave];
     const float* s = sh.s[wave] - y0;
-    const bool slotA = (x0 < x1) && (rp[0] < y0);
-    if (lane == 0) {
-        a.carry_row[2 * chunk] = slotA ? x0 : -1;
-        a.carry_row[2 * chunk + 1] = slotB ? x1 : -1;
-    }
     const int nend = x1 - x0;
     const int W = a.W, G = CSR_WAVE / W, g = lane / W, lg = lane & (W - 1);
-    auto emit = [&](int i, float m, float l) {
-        if (i < nend && rp[i] >= y0) {
-            a.stats[2 * ((int64_t)x0 + i)] = m;
-            a.stats[2 * ((int64_t)x0 + i) + 1] = l;
-        } else {
-            const int64_t slot = 2 * chunk + ((i == nend) ? 1 : 0);
-            a.carry_ml[2 * slot] = m;
-            a.carry_ml[2 * slot + 1] = l;
+    if (active) {
+        slotB = (x1 < a.n_rows) && (max(rp[x1 - x0], y0) < y1);
+        nrow = x1 - x0 + (slotB ? 1 : 0);
+        const bool slotA = (x0 < x1) && (rp[0] < y0);
+        if (lane == 0) {
+            a.carry_row[2 * chunk] = slotA ? x0 : -1;
+            a.carry_row[2 * chunk + 1] = slotB ? x1 : -1;
         }
-    };
-    for (int i = 0; i < nrow; ++i) {
-        const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
-        if (se - sb < a.long_row) continue;
-        float m, l;
-        sm_stats(s, sb, se, lane, CSR_WAVE, a.scale, m, l);
-        if (lane == 0) emit(i, m, l);
+        // statistics of every segment; split segments also leave a piece
+        auto keep = [&](int i, int sb, int se, float m, float l, bool writer, int t, int n) {
+            if (writer) {
+                sh.m[wave][i] = m;
+                sh.l[wave][i] = l;
+                if (!(i < nend && rp[i] >= y0)) {
+                    const int64_t slot = 2 * chunk + ((i == nend) ? 1 : 0);
+                    a.carry_ml[2 * slot] = m;
+                    a.carry_ml[2 * slot + 1] = l;
+                }
+            }
+            for (int e = sb + t; e < se; e += n) sh.ri[wave][e - y0] = (uint16_t)i;
+        };
+        for (int i = 0; i < nrow; ++i) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb < a.long_row) continue;
+            float m, l;
+            sm_stats(s, sb, se, lane, CSR_WAVE, a.scale, m, l);
+            keep(i, sb, se, m, l, lane == 0, lane, CSR_WAVE);
+        }
+        for (int i = g; i < nrow; i += G) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb >= a.long_row) continue;
+            float m, l;
+            sm_stats(s, sb, se, lg, W, a.scale, m, l);
+            keep(i, sb, se, m, l, lg == 0, lg, W);
+        }
     }
-    for (int i = g; i < nrow; i += G) {
-        const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
-        if (se - sb >= a.long_row) continue;
-        float m, l;
-        sm_stats(s, sb, se, lg, W, a.scale, m, l);
-        if (lg == 0) emit(i, m, l);
+    __syncthreads();
+    if (!active) return;
+    // probabilities of the rows wholly inside the chunk, lanes over entries
+    for (int e = y0 + lane; e < y1; e += CSR_WAVE) {
+        const int i = sh.ri[wave][e - y0];
+        if (i < nend && rp[i] >= y0) a.probs[e] = exp_neg(s[e] * a.scale - sh.m[wave][i]) / sh.l[wave][i];
     }
 }
 
 // Merges the (m, l) pieces of rows split across chunks (one wave per chunk
 // whose slot A holds a row; the pieces are slot B of the run of chunks before
 // it, then slot A).
-__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
+__device__ __forceinline__ void softmax_fixup_one(const SoftmaxArgs& a, int64_t c, int r)
 {
-    const int wave = threadIdx.x / CSR_WAVE, lane = lane_id();
-    const int64_t c = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
-    if (c >= a.n_chunks) return;
-    const int r = a.carry_row[2 * c];
-    if (r < 0) return;
+    const int lane = lane_id();
     int64_t k0 = c;
     while (true) {
         const int64_t idx = k0 - 1 - lane;
@@ -156,32 +153,46 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_norm(SoftmaxArgs a)
+__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
 {
-    __shared__ SmShared<D> sh;
-    const int wave = threadIdx.x / CSR_WAVE, lane = lane_id();
-    const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
-    int x0 = 0, y0 = 0, x1 = 0, y1 = 0, nrow = 0;
-    bool slotB = false;
-    if (!sm_stage<D>(a, sh, wave, lane, chunk, x0, y0, x1, y1, nrow, slotB)) return;
-    const int32_t* rp = sh.rp[wave];
-    const float* s = sh.s[wave] - y0;
-    const int W = a.W, G = CSR_WAVE / W, g = lane / W, lg = lane & (W - 1);
-    auto write = [&](int i, int sb, int se, int t, int n) {
-        const int64_t row = (int64_t)x0 + i;
-        const float m = a.stats[2 * row], inv = 1.f / a.stats[2 * row + 1];
-        for (int e = sb + t; e < se; e += n) a.probs[e] = exp_neg(s[e] * a.scale - m) * inv;
-    };
-    for (int i = 0; i < nrow; ++i) {
-        const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
-        if (se - sb < a.long_row || se <= sb) continue;
-        write(i, sb, se, lane, CSR_WAVE);
+    const int64_t base = fixup_window(a.n_chunks);
+    if (base < 0) return;
+    const int lane = lane_id();
+    const int64_t mine = base + lane;
+    const int rl = (mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
+    uint64_t todo = __ballot(rl >= 0);
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        softmax_fixup_one(a, base + j, __shfl(rl, j, CSR_WAVE));
     }
-    for (int i = g; i < nrow; i += G) {
-        const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
-        if (se - sb >= a.long_row || se <= sb) continue;
-        write(i, sb, se, lg, W);
+}
+
+// Probabilities of the entries of split rows: lane j of a wave handles chunk
+// base + j of the wave's window, writing the entries of its slot A segment
+// [y0, end of row x0) and of its slot B segment [start of row x1, y1).
+__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split(SoftmaxArgs a)
+{
+    const int64_t base = fixup_window(a.n_chunks);
+    if (base < 0) return;
+    const int64_t c = base + lane_id();
+    if (c >= a.n_chunks) return;
+    const int y0 = a.part[2 * c + 1], y1 = a.part[2 * c + 3];
+    for (int slot = 0; slot < 2; ++slot) {
+        const int r = a.carry_row[2 * c + slot];
+        if (r < 0) continue;
+        const int sb = slot == 0 ? y0 : max(a.row_ptr[r], y0);
+        const int se = slot == 0 ? min(a.row_ptr[r + 1], y1) : y1;
+        const float m = a.stats[2 * (int64_t)r], l = a.stats[2 * (int64_t)r + 1];
+        int e = sb;
+        for (; e + 4 <= se; e += 4) {
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = a.scores[e + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a.probs[e + u] = exp_neg(x[u] * a.scale - m) / l;
+        }
+        for (; e < se; ++e) a.probs[e] = exp_neg(a.scores[e] * a.scale - m) / l;
     }
 }
 

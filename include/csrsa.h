@@ -87,9 +87,14 @@ enum csr_dtype { CSR_DTYPE_F32 = 0, CSR_DTYPE_BF16 = 1 };
 /* Row mappings (the "mapping" half of a schedule). */
 enum csr_mapping {
     CSR_MAP_ROWGROUP = 1,  /* a group of W lanes per row, lanes across the feature width */
-    CSR_MAP_MERGEPATH = 2  /* nnz-balanced merge-path chunks per wavefront; col_idx and
+    CSR_MAP_MERGEPATH = 2, /* nnz-balanced merge-path chunks per wavefront; col_idx and
                               edge values staged in LDS; split rows combined by a
                               deterministic fix-up pass */
+    CSR_MAP_SEGSCAN = 3    /* small widths (SpMM, SDDMM): merge-path chunks staged in LDS,
+                              lanes over consecutive entries, each lane gathering a whole
+                              feature row; SpMM rows summed by a cross-lane segmented
+                              scan.  group_lanes = 1, vec * passes covers the width,
+                              passes <= 4, long_row = 0 */
 };
 
 /* Context flags. */
@@ -255,7 +260,7 @@ int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t
  * call with sched == NULL then picks its schedule by the cost model alone,
  * since a micro-probe would overwrite its own input).  Rows without entries
  * have nothing to write.  Schedules: merge-path mapping only
- * (vec 1, passes 1, group_lanes = lanes per short row). */
+ * (vec 1, passes 1, group_lanes = lanes per short row, chunk_items 256 or 512). */
 int csr_row_softmax(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
                     const float* scores, float scale, float* probs, const csr_schedule_t* sched,
                     void* workspace, size_t ws_bytes, void* stream);

@@ -73,6 +73,13 @@ def schedules(problem, thorough=True):
                 s.group_lanes, s.passes = W, nv
                 s.mapping, s.chunk_items, s.long_row = csa.MAP_MERGEPATH, D, lr
                 out.append(s)
+    # entry-parallel segmented scan for small widths (SpMM, SDDMM)
+    if problem.op in (_ffi.OP_SPMM, _ffi.OP_SDDMM) and problem.width <= 4 * base.vec:
+        for D in ((256, 512, 1024) if thorough else (512,)):
+            s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+            s.mapping, s.group_lanes, s.chunk_items, s.long_row = csa.MAP_SEGSCAN, 1, D, 0
+            s.passes = -(-problem.width // base.vec)
+            out.append(s)
     return out
 
 
