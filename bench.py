@@ -174,19 +174,20 @@ def committed_traffic(config, call, schedule):
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(config)
-    if not rec or rec.get("call") != call.name:
-        return None
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec["sources_sha256"]:
-        return None
+        recs = json.load(f).get(config) or []
+    if isinstance(recs, dict):
+        recs = [recs]
     sd = schedule.as_dict()
-    if any(sd.get(k) != v for k, v in rec["schedule"].items()):
-        return None
-    return rec["traffic_bytes"]
+    for rec in recs:
+        if rec.get("call") != call.name or any(sd.get(k) != v for k, v in rec["schedule"].items()):
+            continue
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() == rec["sources_sha256"]:
+            return rec["traffic_bytes"]
+    return None
 
 
 def selector_study(calls, torch, csa, rounds=5, per_round=3):
