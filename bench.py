@@ -236,6 +236,30 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
     return out
 
 
+def cold_times(calls, torch, reps=5, flush_gib=1):
+    """Per-call time with cold caches: before each HIP-event timed call a
+    kernel writes a 1 GiB buffer (four times the 256 MB Infinity Cache and far
+    beyond L2), so the call finds none of its operands cached.  Median of
+    `reps`."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(flush_gib << 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    for c in calls:
+        ts = []
+        for r in range(reps):
+            scratch.fill_(r & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            c.run()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[c.name] = float(np.median(ts))
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(calls, target_s=15.0):
     """Times the oracle (as it is) on a bounded sample of the step: the same
     contiguous block of leading rows for every call, sized so that the whole
@@ -288,6 +312,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of every call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one device copy of 1 GiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -360,6 +385,7 @@ def main():
     value = step_bytes / (wall / args.steps) / 1e9
     gnnzf = sum(c.nnz * c.width for c in calls) / (wall / args.steps) / 1e9
 
+    cold = {} if args.no_cold else cold_times(calls, torch)
     kernels = {}
     for c in calls:
         ms = float(np.mean(per_call[c.name]))
@@ -368,6 +394,10 @@ def main():
             "GNNZF_s": round(c.nnz * c.width / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(c.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_alg": c.bytes, **sel[c.name]}
+        if c.name in cold:
+            mc = cold[c.name]
+            kernels[c.name].update({"ms_cold": round(mc, 4), "GB_s_cold": round(c.bytes / (mc * 1e-3) / 1e9, 1),
+                                    "frac_hbm_cold": round(c.bytes / (mc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     dom_ms = float(np.mean(per_call[dom.name]))
     achieved = dom.bytes / (dom_ms * 1e-3) / 1e9
     result = {

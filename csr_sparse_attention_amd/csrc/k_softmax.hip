@@ -17,7 +17,7 @@ static hipError_t run_softmax(const SoftmaxArgs& a, hipStream_t s)
     hipLaunchKernelGGL(k_softmax_fixup, dim3((unsigned)fblocks), dim3(CSR_BLOCK), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_softmax_split, dim3((unsigned)fblocks), dim3(CSR_BLOCK), 0, s, a);
+    hipLaunchKernelGGL(k_softmax_split, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
     return hipGetLastError();
 }
 

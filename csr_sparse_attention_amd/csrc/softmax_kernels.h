@@ -13,7 +13,8 @@
 //                      boundary leave (m, l) pieces in the carry slots;
 //   k_softmax_fixup  - merges the pieces of each split row in chunk order into
 //                      that row's statistics;
-//   k_softmax_split  - writes p_e for the entries of split rows only.
+//   k_softmax_split  - writes p_e for the entries of split rows only, a wave
+//                      per chunk, lanes over entries.
 // The scores are read once (plus the entries of split rows a second time).
 #pragma once
 
@@ -168,32 +169,40 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
     }
 }
 
-// Probabilities of the entries of split rows: lane j of a wave handles chunk
-// base + j of the wave's window, writing the entries of its slot A segment
-// [y0, end of row x0) and of its slot B segment [start of row x1, y1).
+// Probabilities of the entries of split rows, one wave per chunk: the chunk's
+// slot A segment (the end of a row begun earlier: [y0, end of row x0)) and
+// slot B segment (the start or middle of a row that continues: [start of row
+// x1, y1)) are written with the lanes over consecutive entries (coalesced).
+// A wave per chunk keeps every chunk's few dependent loads (slot rows, bounds,
+// row statistics, scores) in flight at once across the chip.
+__device__ __forceinline__ void softmax_write_segment(const SoftmaxArgs& a, int r, int sb, int se)
+{
+    const int lane = lane_id();
+    const float m = a.stats[2 * (int64_t)r], l = a.stats[2 * (int64_t)r + 1];
+    for (int e0 = sb; e0 < se; e0 += 4 * CSR_WAVE) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * CSR_WAVE + lane;
+            x[u] = (e < se) ? a.scores[e] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * CSR_WAVE + lane;
+            if (e < se) a.probs[e] = exp_neg(x[u] * a.scale - m) / l;
+        }
+    }
+}
+
 __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split(SoftmaxArgs a)
 {
-    const int64_t base = fixup_window(a.n_chunks);
-    if (base < 0) return;
-    const int64_t c = base + lane_id();
+    const int64_t c = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + threadIdx.x / CSR_WAVE;
     if (c >= a.n_chunks) return;
+    const int ra = a.carry_row[2 * c], rb = a.carry_row[2 * c + 1];
+    if (ra < 0 && rb < 0) return;
     const int y0 = a.part[2 * c + 1], y1 = a.part[2 * c + 3];
-    for (int slot = 0; slot < 2; ++slot) {
-        const int r = a.carry_row[2 * c + slot];
-        if (r < 0) continue;
-        const int sb = slot == 0 ? y0 : max(a.row_ptr[r], y0);
-        const int se = slot == 0 ? min(a.row_ptr[r + 1], y1) : y1;
-        const float m = a.stats[2 * (int64_t)r], l = a.stats[2 * (int64_t)r + 1];
-        int e = sb;
-        for (; e + 4 <= se; e += 4) {
-            float x[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) x[u] = a.scores[e + u];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) a.probs[e + u] = exp_neg(x[u] * a.scale - m) / l;
-        }
-        for (; e < se; ++e) a.probs[e] = exp_neg(a.scores[e] * a.scale - m) / l;
-    }
+    if (ra >= 0) softmax_write_segment(a, ra, y0, min(a.row_ptr[ra + 1], y1));
+    if (rb >= 0) softmax_write_segment(a, rb, max(a.row_ptr[rb], y0), y1);
 }
 
 }  // namespace csrk
