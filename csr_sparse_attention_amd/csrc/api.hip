@@ -157,7 +157,8 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     const csrh::WsLayout L = csrh::ws_layout(p, s);
     int32_t* coords = reinterpret_cast<int32_t*>(ws + L.coords);
     if (s.mapping != CSR_MAP_ROWGROUP) {
-        CSR_HIP(ctx, csrk::launch_merge_path(p.row_ptr, p.n_rows, p.nnz, s.chunk_items, L.n_chunks, coords, st));
+        int32_t* bounds = L.bounds ? reinterpret_cast<int32_t*>(ws + L.bounds) : nullptr;
+        CSR_HIP(ctx, csrk::launch_merge_path(p.row_ptr, p.n_rows, p.nnz, s.chunk_items, L.n_chunks, coords, st, bounds));
     }
 
     if (p.op == CSR_OP_ROW_SOFTMAX) {
@@ -171,11 +172,12 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         a.W = s.group_lanes;
         a.long_row = (s.group_lanes == 64) ? 0 : s.long_row;
         a.part = coords;
+        a.bounds = L.bounds ? reinterpret_cast<const int32_t*>(ws + L.bounds) : nullptr;
         a.n_chunks = L.n_chunks;
         a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
         a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
         a.stats = reinterpret_cast<float*>(ws + L.carry_val);
-        CSR_HIP(ctx, csrk::launch_row_softmax(s.chunk_items, a, st));
+        CSR_HIP(ctx, csrk::launch_row_softmax(s.mapping, s.chunk_items, a, st));
         return CSR_OK;
     }
     if (p.op == CSR_OP_MHA) {

@@ -53,6 +53,7 @@ struct SoftmaxArgs {
     int32_t W;            // lanes per group for short rows
     int32_t long_row;     // whole-wave threshold
     const int32_t* part;
+    const int32_t* bounds;  // [n_chunks + 1][2]: entry range of the row at each chunk boundary
     int64_t n_chunks;
     int32_t* carry_row;   // [2 n_chunks]
     float* carry_ml;      // [2 n_chunks][2]

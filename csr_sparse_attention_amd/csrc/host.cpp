@@ -162,7 +162,8 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
     if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH && s.mapping != CSR_MAP_SEGSCAN)
         return fail("unknown mapping");
     if (s.mapping == CSR_MAP_SEGSCAN) {
-        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return fail("the segmented-scan mapping serves SpMM and SDDMM");
+        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM && p.op != CSR_OP_ROW_SOFTMAX)
+            return fail("the segmented-scan mapping serves SpMM, SDDMM and row softmax");
         if (s.group_lanes != 1 || s.passes > 4 || s.long_row != 0)
             return fail("segmented-scan schedules take group_lanes 1, passes <= 4, long_row 0");
     }
@@ -180,9 +181,14 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
         return CSR_OK;
     }
     if (p.op == CSR_OP_ROW_SOFTMAX) {
-        if (s.mapping != CSR_MAP_MERGEPATH) return fail("row softmax runs on the merge-path mapping");
-        if (s.chunk_items > 512) return fail("row softmax chunks hold at most 512 items");
         if (s.vec != 1 || s.passes != 1) return fail("row softmax layout must be vec 1, 1 pass");
+        if (s.mapping == CSR_MAP_SEGSCAN) {
+            if (s.group_lanes != 1 || s.long_row != 0) return fail("entry-run row softmax takes group_lanes 1, long_row 0");
+            if (s.chunk_items > 512) return fail("entry-run row softmax chunks hold at most 512 items");
+            return CSR_OK;
+        }
+        if (s.mapping != CSR_MAP_MERGEPATH) return fail("row softmax runs on the merge-path chunks");
+        if (s.chunk_items > 512) return fail("row-segment softmax chunks hold at most 512 items");
         if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
         return CSR_OK;
     }
@@ -228,6 +234,11 @@ WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
     }
     w.carry_val = w.carry_ml + up(ml);
     w.total = w.carry_val + up(val);
+    if (p.op == CSR_OP_ROW_SOFTMAX && s.mapping == CSR_MAP_SEGSCAN) {
+        // entry range of the row at every chunk boundary
+        w.bounds = w.total;
+        w.total = w.bounds + up((size_t)(nc + 1) * 2 * 4);
+    }
     return w;
 }
 
@@ -255,12 +266,13 @@ csr_schedule_t default_schedule(const csr_problem_t& p)
         return s;
     }
     if (p.op == CSR_OP_ROW_SOFTMAX) {
-        // one lane per short row: no cross-lane merge on the common path
+        // lane-owned entry runs, one cross-lane scan per chunk
+        s.mapping = CSR_MAP_SEGSCAN;
         s.vec = 1;
         s.group_lanes = 1;
         s.passes = 1;
-        s.chunk_items = 512;
-        s.long_row = 32;
+        s.chunk_items = 256;
+        s.long_row = 0;
         return s;
     }
     s.vec = max_vec_f32(p);
@@ -287,19 +299,24 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
         out.push_back(s);
     };
     csr_schedule_t s = d;
-    s.chunk_items = 256;
-    add(s);
-    s.chunk_items = 1024;
-    add(s);
     if (p.op == CSR_OP_ROW_SOFTMAX) {
-        for (int w : {4, 16, 64}) {
+        s.chunk_items = 512;  // lane-owned runs twice as long
+        add(s);
+        // row segments by groups of W lanes (a whole wave for the long ones)
+        for (int w : {1, 4, 16, 64}) {
             s = d;
+            s.mapping = CSR_MAP_MERGEPATH;
+            s.chunk_items = 512;
             s.group_lanes = w;
-            s.long_row = (w == 64) ? 0 : 8 * w;
+            s.long_row = (w == 64) ? 0 : (w == 1 ? 32 : 8 * w);
             add(s);
         }
         return out;
     }
+    s.chunk_items = 256;
+    add(s);
+    s.chunk_items = 1024;
+    add(s);
     // row-group: one group per row, no partition or fix-up; only when no row
     // is long enough to leave a tail or a long fp32 accumulation chain
     if (hist && max_deg <= 4096) {
@@ -346,6 +363,14 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
     // the layout inflate the gather traffic) + a latency-bound tail for the
     // longest row when rows are not split + launch overheads.
     const double bw = 5.0e12, wave_bw = 8.0e9, launch = 4e-6;
+    if (p.op == CSR_OP_ROW_SOFTMAX) {
+        // scores in, probabilities out; the row-segment mapping pays about
+        // twice the per-chunk instruction work of the entry runs
+        const double nc = (double)n_chunks_for(p, s.chunk_items);
+        const double per_chunk = (s.mapping == CSR_MAP_SEGSCAN ? 0.75e-6 : 1.5e-6) * s.chunk_items / 256.0;
+        const double cus = dev.cu_count > 0 ? dev.cu_count : 256.0;
+        return p.nnz * 8.0 / bw + 3 * launch + nc * per_chunk / (cus * 8.0);
+    }
     const double esize = (p.op == CSR_OP_MHA) ? 2.0 : 4.0;
     const double gathers = (p.op == CSR_OP_MHA) ? 2.0 : 1.0;
     const double row_bytes = p.width * esize * gathers;

@@ -45,7 +45,7 @@ int64_t n_chunks_for(const csr_problem_t& p, int items_per_chunk);
 
 // Workspace regions of a merge-path schedule.
 struct WsLayout {
-    size_t coords, carry_row, carry_ml, carry_val, total;
+    size_t coords, carry_row, carry_ml, carry_val, bounds, total;
     int64_t n_chunks;
 };
 WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s);

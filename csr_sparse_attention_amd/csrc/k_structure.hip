@@ -44,9 +44,11 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_degree_hist(const int32_t* row_pt
 
 // Chunk boundary c sits at item d = min(c * items, n_rows + nnz) of the merged
 // sequence; x = number of rows i whose end precedes it, i.e. with
-// row_ptr[i + 1] + i + 1 <= d (a strictly increasing key), y = d - x.
+// row_ptr[i + 1] + i + 1 <= d (a strictly increasing key), y = d - x.  With
+// bounds set, also the entry range of row x: bounds[2c] = row_ptr[x],
+// bounds[2c + 1] = row_ptr[x + 1] (both nnz when x = n_rows).
 __global__ void k_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz, int64_t items,
-                             int64_t n_chunks, int32_t* coords)
+                             int64_t n_chunks, int32_t* coords, int32_t* bounds)
 {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c > n_chunks) return;
@@ -62,6 +64,10 @@ __global__ void k_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz
     }
     coords[2 * c] = (int32_t)lo;
     coords[2 * c + 1] = (int32_t)(d - lo);
+    if (bounds) {
+        bounds[2 * c] = lo < n_rows ? row_ptr[lo] : (int32_t)nnz;
+        bounds[2 * c + 1] = lo < n_rows ? row_ptr[lo + 1] : (int32_t)nnz;
+    }
 }
 
 // Counts violations of the CSR invariants into *bad (zeroed beforehand).
@@ -104,10 +110,10 @@ hipError_t launch_degree_hist(const int32_t* row_ptr, int64_t n_rows, int64_t* o
 }
 
 hipError_t launch_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz, int64_t items,
-                             int64_t n_chunks, int32_t* coords, hipStream_t s)
+                             int64_t n_chunks, int32_t* coords, hipStream_t s, int32_t* bounds)
 {
     hipLaunchKernelGGL(k_merge_path, dim3(grid_for(n_chunks + 1, 1 << 30)), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows,
-                       nnz, items, n_chunks, coords);
+                       nnz, items, n_chunks, coords, bounds);
     return hipGetLastError();
 }
 

@@ -40,13 +40,13 @@ hipError_t launch_sddmm(int mapping, int vec, int nv, int chunk, const Fp32Args&
 hipError_t launch_mha(int mapping, int lph, int chunk, const MhaArgs& a, hipStream_t s);
 hipError_t launch_mha_fixup(int lph, const MhaArgs& a, hipStream_t s);
 
-hipError_t launch_row_softmax(int chunk, const SoftmaxArgs& a, hipStream_t s);
+hipError_t launch_row_softmax(int mapping, int chunk, const SoftmaxArgs& a, hipStream_t s);
 
 // Structure kernels.
 hipError_t launch_fill_i64(int64_t* p, int64_t n, int64_t value, hipStream_t s);
 hipError_t launch_degree_hist(const int32_t* row_ptr, int64_t n_rows, int64_t* out, hipStream_t s);
 hipError_t launch_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz, int64_t items,
-                             int64_t n_chunks, int32_t* coords, hipStream_t s);
+                             int64_t n_chunks, int32_t* coords, hipStream_t s, int32_t* bounds = nullptr);
 hipError_t launch_validate(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows,
                            int64_t n_cols, int64_t nnz, int64_t* bad, hipStream_t s);
 

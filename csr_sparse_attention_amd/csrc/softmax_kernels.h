@@ -114,6 +114,209 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_main(SoftmaxArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Entry-run variant (mapping "segmented scan").  Chunks are the merge-path
+// chunks, re-cut at row starts: a row of at most D entries belongs wholly to
+// the chunk that holds its end (its entries before the chunk's start are
+// staged too, so a chunk stages fewer than 2 D entries), and only rows of more
+// than D entries are cut into pieces, merged by k_softmax_fixup and written by
+// k_softmax_split as before.  Lane l of a wave owns the run of R consecutive
+// entries [l R, l R + R) of the chunk's range, R = ceil(entries / 64), loads
+// its scores straight into registers (between them the wave's lanes read
+// whole lines) and walks them alone with an online (m, l) of the row it is in;
+// a row that crosses lanes is completed by one inclusive segmented scan of the
+// lanes' open pieces (keyed by row), so the cross-lane work is one scan per
+// chunk.  Only row_ptr and the per-row statistics go through LDS.  Every lane
+// then reads the statistics of its rows and writes its p_e.
+// ---------------------------------------------------------------------------
+template <int D>
+struct SmRunShared {
+    // chunk row_ptr, then the rows' maxima (float bits); 64 trailing slots take
+    // the lanes' writes that have no row to go to
+    int32_t rp[CSR_WAVES_PER_BLOCK][D + 4 + CSR_WAVE];
+    float l[CSR_WAVES_PER_BLOCK][D + 4 + CSR_WAVE];  // row-start marks (uint16), then the rows' sums
+};
+
+// (m1, l1) <- (m1, l1) merged with (m2, l2); maxima in log2 units, an empty
+// piece has m = -inf and l = 0.  One of the two exponentials is exp2(0) = 1.
+__device__ __forceinline__ void sm_merge2(float& m1, float& l1, float m2, float l2)
+{
+    const float d = m1 - m2;
+    const float e = (fminf(l1, l2) > 0.f) ? __builtin_amdgcn_exp2f(-fabsf(d)) : 0.f;
+    const bool first_big = d >= 0.f;
+    l1 = first_big ? fmaf(l2, e, l1) : fmaf(l1, e, l2);
+    m1 = first_big ? m1 : m2;
+}
+
+// largest i in [lo, hi] with rp[i] <= e, given rp[lo] <= e
+__device__ __forceinline__ int sm_row_search(const int32_t* rp, int lo, int hi, int e)
+{
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rp[mid] <= e)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
+{
+    constexpr int RMAX = 2 * D / CSR_WAVE;
+    constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
+    __shared__ SmRunShared<D> sh;
+    // the wave index is the same for all of a wave's lanes: in a scalar register,
+    // everything derived from the chunk's coordinates is uniform too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / CSR_WAVE), lane = lane_id();
+    const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
+    const bool active = chunk < a.n_chunks;
+    int x0 = 0, y0 = 0, x1 = 0, y1 = 0, a_beg = 0, a_end = 0, b_beg = 0, b_end = 0;
+    if (active) {
+        x0 = a.part[2 * chunk];
+        y0 = a.part[2 * chunk + 1];
+        x1 = a.part[2 * chunk + 2];
+        y1 = a.part[2 * chunk + 3];
+        a_beg = a.bounds[2 * chunk];  // entries of row x0
+        a_end = a.bounds[2 * chunk + 1];
+        b_beg = a.bounds[2 * chunk + 2];  // entries of row x1
+        b_end = a.bounds[2 * chunk + 3];
+    }
+    // row x0 ends here: whole if short, its last piece if long (begun earlier);
+    // row x1 goes on past the chunk: its first or middle piece if long, left to
+    // a later chunk if short
+    const bool slotA = active && x0 < x1 && a_end - a_beg > D;
+    const bool slotB = active && x1 < a.n_rows && b_end - b_beg > D && max(b_beg, y0) < y1;
+    const int lo = (active && x0 < x1 && !slotA) ? a_beg : y0;
+    const int hi = slotB ? y1 : max(b_beg, lo);
+    const int ne = active ? hi - lo : 0;
+    const int nend = x1 - x0, nrow = nend + (slotB ? 1 : 0);
+    int32_t* rp = sh.rp[wave];
+    uint16_t* mark = reinterpret_cast<uint16_t*>(sh.l[wave]);
+    // lane-owned run of R staged entries [k0, k0 + kn); R is the same for the
+    // whole wave, so loops over k stop at R uniformly
+    const int R = (ne + CSR_WAVE - 1) / CSR_WAVE;
+    const int k0 = lane * R;
+    const int kn = max(0, min(R, ne - k0));
+    const float c = a.scale * LOG2E;
+    float t[RMAX];
+    // the run's scores, straight from HBM (the wave's loads cover whole lines
+    // between them); read once, so non-temporal
+    const float* srun = a.scores + lo + k0;
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k) {
+        if (k >= R) break;
+        t[k] = (k < kn) ? __builtin_nontemporal_load(srun + k) : 0.f;
+    }
+    if (active) {
+        // row_ptr[x0 .. x0 + nrow]: nrow + 1 <= D + 2 values
+        stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, 1, false, float>(rp, a.row_ptr + x0, nrow + 1, nullptr,
+                                                                       nullptr, nullptr, nullptr, 0);
+        for (int j = lane; j < ne; j += CSR_WAVE) mark[j] = 0;
+    }
+    __syncthreads();
+    // mark the first staged entry of every non-empty row after row 0 with its index + 1
+    for (int i = 1 + lane; i < nrow; i += CSR_WAVE) {
+        const int b = rp[i];
+        if (b < rp[i + 1]) mark[b - lo] = (uint16_t)(i + 1);
+    }
+    __syncthreads();
+    // rows of the run's entries and scores in log2 units
+    int ri[RMAX];
+    {
+        int cur = (kn > 0) ? sm_row_search(rp, 0, nrow - 1, lo + k0) : 0;
+#pragma unroll
+        for (int k = 0; k < RMAX; ++k) {
+            if (k >= R) break;
+            const bool ok = k < kn;
+            const int mk = ok ? mark[k0 + k] : 0;
+            cur = mk ? mk - 1 : cur;
+            ri[k] = cur;  // past the run: the last row again, with t = -inf
+            t[k] = ok ? t[k] * c : -INFINITY;
+        }
+    }
+    __syncthreads();  // rp and the marks are rewritten below
+    float* sl = sh.l[wave];
+    const int dummy = D + 4 + lane;  // this lane's slot for writes that go nowhere
+    const int64_t slot_base = 2 * chunk;
+    // the total of row i over this chunk: LDS statistics for a row completed
+    // here, a carry piece (natural-log maximum) for a long row
+    auto finish = [&](int i, float m, float l) {
+        if (i == nend && slotB) {
+            a.carry_ml[2 * (slot_base + 1)] = m * LN2;
+            a.carry_ml[2 * (slot_base + 1) + 1] = l;
+        } else if (i == 0 && slotA) {
+            a.carry_ml[2 * slot_base] = m * LN2;
+            a.carry_ml[2 * slot_base + 1] = l;
+        } else {
+            rp[i] = __float_as_int(m);
+            sl[i] = l;
+        }
+    };
+    // online (max, sum) of the run's row segments; a segment closed inside the
+    // run goes to LDS at its row (the first one is finished after the scan)
+    const int first = (kn > 0) ? ri[0] : -1;
+    int tail = (kn > 0) ? first : -2 - lane;  // row of the open piece
+    float m = -INFINITY, l = 0.f;
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k) {
+        if (k >= R) break;
+        const bool close = ri[k] != tail && kn > 0;
+        const int w = close ? tail : dummy;
+        rp[w] = __float_as_int(m);
+        sl[w] = l;
+        tail = close ? ri[k] : tail;
+        m = close ? -INFINITY : m;
+        l = close ? 0.f : l;
+        const float mm = (t[k] > m) ? t[k] : m;
+        l = fmaf(l, __builtin_amdgcn_exp2f(m - mm), __builtin_amdgcn_exp2f(t[k] - mm));
+        m = mm;
+    }
+    if (active && lane == 0) {
+        a.carry_row[2 * chunk] = slotA ? x0 : -1;
+        a.carry_row[2 * chunk + 1] = slotB ? x1 : -1;
+        if (slotA && a_end == y0) {  // long row without entries here: empty piece
+            a.carry_ml[2 * slot_base] = -INFINITY;
+            a.carry_ml[2 * slot_base + 1] = 0.f;
+        }
+    }
+    // inclusive segmented scan of the open pieces over the lanes, keyed by row
+    float sm = m, sq = l;
+#pragma unroll
+    for (int off = 1; off < CSR_WAVE; off <<= 1) {
+        const int r2 = __shfl_up(tail, off, CSR_WAVE);
+        const float m2 = __shfl_up(sm, off, CSR_WAVE);
+        const float l2 = __shfl_up(sq, off, CSR_WAVE);
+        if (lane >= off && r2 == tail) sm_merge2(sm, sq, m2, l2);
+    }
+    // what the lanes before this one hold of this run's first row
+    const int prev_tail = __shfl_up(tail, 1, CSR_WAVE);
+    const float cm = __shfl_up(sm, 1, CSR_WAVE), cl = __shfl_up(sq, 1, CSR_WAVE);
+    const int next_first = __shfl_down(first, 1, CSR_WAVE);
+    if (active && kn > 0) {
+        if (tail != first) {  // the first row closed inside the run
+            float fm = __int_as_float(rp[first]), fl = sl[first];
+            if (lane > 0 && prev_tail == first) sm_merge2(fm, fl, cm, cl);
+            finish(first, fm, fl);
+        }
+        // the open piece is the row's total over the chunk when no later lane continues it
+        if (k0 + kn >= ne || next_first != tail) finish(tail, sm, sq);
+    }
+    __syncthreads();
+    // entries of the rows completed here: [ya, yb), run positions [ks, ke)
+    const int ya = slotA ? a_end : lo;
+    const int yb = slotB ? max(b_beg, y0) : hi;
+    const int ks = max(0, ya - lo - k0), ke = min(kn, yb - lo - k0);
+    float* prun = a.probs + lo + k0;
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k) {
+        if (k >= R) break;
+        if (k >= ks && k < ke)
+            prun[k] = __builtin_amdgcn_exp2f(t[k] - __int_as_float(rp[ri[k]])) * __builtin_amdgcn_rcpf(sl[ri[k]]);
+    }
+}
+
 // Merges the (m, l) pieces of rows split across chunks (one wave per chunk
 // whose slot A holds a row; the pieces are slot B of the run of chunks before
 // it, then slot A).
@@ -203,6 +406,71 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split(SoftmaxArgs a)
     const int y0 = a.part[2 * c + 1], y1 = a.part[2 * c + 3];
     if (ra >= 0) softmax_write_segment(a, ra, y0, min(a.row_ptr[ra + 1], y1));
     if (rb >= 0) softmax_write_segment(a, rb, max(a.row_ptr[rb], y0), y1);
+}
+
+// Probabilities of the long rows' entries after the entry-run kernel: a wave
+// per window of 64 chunks.  Lane j reads chunk base + j's slot rows, bounds
+// (from the row-bound records, no row_ptr reads) and the slot rows' merged
+// statistics in two rounds of independent loads; a ballot then lists the
+// window's segments and the whole wave writes each one, lanes over
+// consecutive entries (at most D entries, one pass of 4 loads per lane for
+// D = 256).  Only chunks inside or at the ends of rows longer than D hold
+// segments, so a window usually has few.
+__global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split_runs(SoftmaxArgs a)
+{
+    const int64_t base = ((int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x / CSR_WAVE)) * CSR_WAVE;
+    if (base >= a.n_chunks) return;
+    const int lane = lane_id();
+    const int64_t c = base + lane;
+    int ra = -1, rb = -1, a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+    if (c < a.n_chunks) {
+        ra = a.carry_row[2 * c];
+        rb = a.carry_row[2 * c + 1];
+        const int y0 = a.part[2 * c + 1], y1 = a.part[2 * c + 3];
+        a0 = y0;
+        a1 = a.bounds[2 * c + 1];                // end of row x0
+        b0 = max(a.bounds[2 * c + 2], y0);       // start of row x1
+        b1 = y1;
+    }
+    float ma = 0.f, la = 1.f, mb = 0.f, lb = 1.f;
+    if (ra >= 0) {
+        ma = a.stats[2 * (int64_t)ra];
+        la = a.stats[2 * (int64_t)ra + 1];
+    }
+    if (rb >= 0) {
+        mb = a.stats[2 * (int64_t)rb];
+        lb = a.stats[2 * (int64_t)rb + 1];
+    }
+    const float c2 = a.scale * 1.44269504088896341f;
+    auto segment = [&](int sb, int se, float m, float l) {
+        const float m2 = m * 1.44269504088896341f, il = 1.f / l;
+        for (int e0 = sb; e0 < se; e0 += 4 * CSR_WAVE) {
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * CSR_WAVE + lane;
+                x[u] = (e < se) ? __builtin_nontemporal_load(a.scores + e) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * CSR_WAVE + lane;
+                if (e < se) a.probs[e] = __builtin_amdgcn_exp2f(x[u] * c2 - m2) * il;
+            }
+        }
+    };
+    uint64_t todo = __ballot(ra >= 0);
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        segment(__shfl(a0, j, CSR_WAVE), __shfl(a1, j, CSR_WAVE), __shfl(ma, j, CSR_WAVE), __shfl(la, j, CSR_WAVE));
+    }
+    todo = __ballot(rb >= 0);
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        segment(__shfl(b0, j, CSR_WAVE), __shfl(b1, j, CSR_WAVE), __shfl(mb, j, CSR_WAVE), __shfl(lb, j, CSR_WAVE));
+    }
 }
 
 }  // namespace csrk

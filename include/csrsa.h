@@ -94,7 +94,10 @@ enum csr_mapping {
                               lanes over consecutive entries, each lane gathering a whole
                               feature row; SpMM rows summed by a cross-lane segmented
                               scan.  group_lanes = 1, vec * passes covers the width,
-                              passes <= 4, long_row = 0 */
+                              passes <= 4, long_row = 0.  Row softmax: each lane owns a
+                              run of chunk_items / 64 consecutive entries, rows crossing
+                              lanes completed by one segmented scan per chunk
+                              (group_lanes 1, long_row 0, chunk_items 256, 512, 1024) */
 };
 
 /* Context flags. */
@@ -259,8 +262,10 @@ int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t
  * scores, probs: fp32 [nnz] (may alias for an in-place update; an in-place
  * call with sched == NULL then picks its schedule by the cost model alone,
  * since a micro-probe would overwrite its own input).  Rows without entries
- * have nothing to write.  Schedules: merge-path mapping only
- * (vec 1, passes 1, group_lanes = lanes per short row, chunk_items 256 or 512). */
+ * have nothing to write.  Schedules (vec 1, passes 1): the merge-path mapping
+ * with group_lanes = lanes per short row and chunk_items 256 or 512, or the
+ * segmented-scan mapping (lane-owned entry runs) with group_lanes 1, long_row 0
+ * and chunk_items 256, 512 or 1024. */
 int csr_row_softmax(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
                     const float* scores, float scale, float* probs, const csr_schedule_t* sched,
                     void* workspace, size_t ws_bytes, void* stream);

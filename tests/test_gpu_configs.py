@@ -176,3 +176,50 @@ def test_c1_attention_selected():
     out = csa.attention(rp, ci, sd, Vd, schedule=s).cpu().numpy()
     ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, c["scores"], c["V"])
     print(f"c1: {s} max err {assert_close(out, ref, mag, TOL_F32, 'c1'):.2e}")
+
+
+# ---------------------------------------------------------------------------
+# row softmax (the unfused pipeline's middle stage) on the c3 and c4 patterns
+# ---------------------------------------------------------------------------
+
+def _softmax_case(name, seed):
+    csr = pattern(name)
+    rp, _ = pattern_dev(name)
+    sc = (3 * np.random.default_rng(seed).standard_normal(csr.nnz)).astype(np.float32)
+    sd = dev(sc)
+    s = selected("row_softmax", rp, None, sd, scale=0.125)
+    out = csa.row_softmax(rp, sd, scale=0.125, schedule=s).cpu().numpy()
+    return csr, sc, s, out
+
+
+def _row_sums_ok(csr, out):
+    live = csr.degrees() > 0
+    sums = np.add.reduceat(out.astype(np.float64), csr.row_ptr[:-1][live])
+    return np.max(np.abs(sums - 1))
+
+
+def test_c3_row_softmax():
+    csr, sc, s, out = _softmax_case("c3", 31)
+    rows = sample_rows(csr, seed=31)
+    got = np.concatenate([out[csr.row_ptr[r]:csr.row_ptr[r + 1]] for r in rows])
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+
+    def one(r):
+        p = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, 0.125, r, r + 1, want_probs=True)[2]
+        return p, p
+
+    ref, _ = oracle_rows(one, rows)
+    err = np.max(np.abs(got.astype(np.float64) - ref) / ref)
+    assert err < TOL_F32, err
+    assert _row_sums_ok(csr, out) < 1e-5
+    print(f"c3 row softmax: {s} max err {err:.2e}")
+
+
+def test_c4_row_softmax_full():
+    csr, sc, s, out = _softmax_case("c4", 41)
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+    ref = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, 0.125, threads=16, want_probs=True)[2]
+    err = np.max(np.abs(out.astype(np.float64) - ref) / ref)
+    assert err < TOL_F32, err
+    assert _row_sums_ok(csr, out) < 1e-5
+    print(f"c4 row softmax: {s} max err {err:.2e}")

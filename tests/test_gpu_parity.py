@@ -488,9 +488,31 @@ def test_validation_flag_rejects_bad_columns():
 # unfused pipeline: row softmax and SDDMM -> row-softmax -> SpMM
 # ---------------------------------------------------------------------------
 
+def short_rows_graph(seed):
+    """Mostly empty and one-entry rows with a few long ones: hundreds of rows
+    per merge-path chunk, runs of empty rows inside a lane's entries."""
+    rng = np.random.default_rng(seed)
+    n = 20_000
+    deg = np.where(rng.random(n) < 0.4, 0, 1 + rng.poisson(0.3, n))
+    deg[rng.choice(n, 4, replace=False)] = rng.integers(700, 3000, 4)
+    return graphs.csr_from_degrees(deg, 50_000, rng)
+
+
+def chunk_edge_graph(seed):
+    """Rows of 255, 256, 257, 511, 512, 513 and 1024 entries (either side of
+    the chunk sizes, where a row stops being kept whole by one chunk) between
+    runs of short and empty rows."""
+    rng = np.random.default_rng(seed)
+    deg = []
+    for L in (255, 256, 257, 511, 512, 513, 1024) * 6:
+        deg += [L] + list(rng.integers(0, 6, rng.integers(0, 40)))
+    return graphs.csr_from_degrees(np.array(deg), 5000, rng)
+
+
+@pytest.mark.parametrize("graph", ["skew", "short", "edges"])
 @pytest.mark.parametrize("scale", [1.0, 0.125])
-def test_row_softmax_every_schedule(skew, scale):
-    csr = skew
+def test_row_softmax_every_schedule(skew, graph, scale):
+    csr = {"skew": lambda: skew, "short": lambda: short_rows_graph(501), "edges": lambda: chunk_edge_graph(502)}[graph]()
     rng = np.random.default_rng(500)
     sc = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
     _, _, ref = oracle.attention(csr.row_ptr, csr.col_idx, sc, np.zeros((csr.n_cols, 1), np.float32), scale,
@@ -502,8 +524,13 @@ def test_row_softmax_every_schedule(skew, scale):
     scheds = csa.candidates(p)
     for D in (256, 512):
         s = csa.CsrSchedule.from_buffer_copy(bytes(base))
-        s.chunk_items = D
+        s.mapping, s.group_lanes, s.long_row, s.chunk_items = csa.MAP_MERGEPATH, 1, 32, D
         scheds.append(s)
+    for D in (256, 512):
+        s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+        s.mapping, s.group_lanes, s.long_row, s.chunk_items = csa.MAP_SEGSCAN, 1, 0, D
+        scheds.append(s)
+    assert {s.mapping for s in scheds} == {csa.MAP_MERGEPATH, csa.MAP_SEGSCAN}
     for s in scheds:
         out = csa.row_softmax(rp, sd, scale=scale, schedule=s).cpu().numpy()
         err = np.max(np.abs(out.astype(np.float64) - ref) / ref)
