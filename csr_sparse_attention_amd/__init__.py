@@ -13,6 +13,7 @@ binding over it and raises ImportError when the library has not been built.
 import torch  # noqa: F401
 
 from ._ffi import (  # noqa: F401,E402
+    OP_SOFTMAX_BWD,
     CsrError,
     CsrProblem,
     CsrSchedule,
@@ -30,19 +31,26 @@ load_library()
 
 from .ops import (  # noqa: E402,F401
     Context,
+    Transposed,
     attention,
+    attention_backward,
     attention_pipeline,
     candidates,
     default_context,
     default_schedule,
     degree_histogram,
+    gather_values,
     make_problem,
     merge_path_partition,
     mha_attention,
     row_softmax,
+    row_softmax_backward,
     sddmm,
+    sddmm_backward,
     select,
     signature,
     spmm,
+    spmm_backward,
+    transpose,
     workspace_size,
 )

@@ -19,7 +19,7 @@ STATUS = {
 }
 CSR_ERR_NO_CACHE_ENTRY = -8
 
-OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX = 1, 2, 3, 4, 5
+OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX, OP_SOFTMAX_BWD = 1, 2, 3, 4, 5, 6
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAP_ROWGROUP, MAP_MERGEPATH, MAP_SEGSCAN = 1, 2, 3
 CTX_VALIDATE, CTX_NO_PROBE = 1, 2
@@ -30,6 +30,7 @@ SCHEDULE_VERSION = 1
 EXPORTS = (
     "csr_context_create", "csr_context_destroy", "csr_status_string", "csr_last_error",
     "csr_spmm", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
+    "csr_row_softmax_backward", "csr_transpose_workspace_size", "csr_transpose", "csr_gather_values",
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
@@ -130,6 +131,10 @@ def load() -> ctypes.CDLL:
         "csr_attention": [P, I64, I64, I64, P, P, P, P, I64, I64, F, P, I64, SP, P, SZ, P],
         "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, SP, P, SZ, P],
         "csr_row_softmax": [P, I64, I64, P, P, F, P, SP, P, SZ, P],
+        "csr_row_softmax_backward": [P, I64, I64, P, P, P, F, P, SP, P, SZ, P],
+        "csr_transpose_workspace_size": [P, I64, I64, I64, ctypes.POINTER(SZ)],
+        "csr_transpose": [P, I64, I64, I64, P, P, P, P, P, P, SZ, P],
+        "csr_gather_values": [P, I64, P, P, P, P],
         "csr_select": [P, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
         "csr_default_schedule": [P, PP, SP],
         "csr_candidates": [P, PP, ctypes.POINTER(I64), SP, I32, ctypes.POINTER(I32)],

@@ -161,12 +161,13 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         CSR_HIP(ctx, csrk::launch_merge_path(p.row_ptr, p.n_rows, p.nnz, s.chunk_items, L.n_chunks, coords, st, bounds));
     }
 
-    if (p.op == CSR_OP_ROW_SOFTMAX) {
+    if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         if (p.nnz == 0) return CSR_OK;
         csrk::SoftmaxArgs a{};
         a.row_ptr = p.row_ptr;
         a.n_rows = p.n_rows;
         a.scores = static_cast<const float*>(p.a);
+        a.grad = static_cast<const float*>(p.b);
         a.scale = p.scale;
         a.probs = static_cast<float*>(p.out);
         a.W = s.group_lanes;
@@ -177,7 +178,10 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
         a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
         a.stats = reinterpret_cast<float*>(ws + L.carry_val);
-        CSR_HIP(ctx, csrk::launch_row_softmax(s.mapping, s.chunk_items, a, st));
+        if (p.op == CSR_OP_SOFTMAX_BWD)
+            CSR_HIP(ctx, csrk::launch_row_softmax_backward(s.chunk_items, a, st));
+        else
+            CSR_HIP(ctx, csrk::launch_row_softmax(s.mapping, s.chunk_items, a, st));
         return CSR_OK;
     }
     if (p.op == CSR_OP_MHA) {
@@ -363,9 +367,10 @@ int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_
     for (size_t i = 0; i < cand.size(); ++i) order.push_back({csrh::estimate(p, cand[i], hist, ctx->dev), i});
     std::stable_sort(order.begin(), order.end(),
                      [](const std::pair<double, size_t>& x, const std::pair<double, size_t>& y) { return x.first < y.first; });
-    // an in-place row softmax cannot be probed: every probe would overwrite
-    // its own input
-    const bool in_place = (p.op == CSR_OP_ROW_SOFTMAX) && (p.a == p.out) && p.a;
+    // an in-place row softmax (or backward) cannot be probed: every probe
+    // would overwrite its own input
+    const bool in_place = (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) && p.out &&
+                          (p.a == p.out || p.b == p.out);
     if (mode == CSR_SELECT_ESTIMATE || (ctx->flags & CSR_CTX_NO_PROBE) || in_place) {
         *out = cand[order[0].second];
         if (mode != CSR_SELECT_ESTIMATE && !in_place) store_entry(ctx, sig, *out, 0.0);
@@ -638,6 +643,95 @@ int csr_row_softmax(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_
     return op_call(ctx, p, sched);
 }
 
+int csr_row_softmax_backward(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
+                             const float* probs, const float* grad_probs, float scale, float* grad_scores,
+                             const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
+{
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_SOFTMAX_BWD;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = n_rows;
+    p.n_cols = 0;
+    p.nnz = nnz;
+    p.width = 1;
+    p.row_ptr = row_ptr;
+    p.a = probs;
+    p.b = grad_probs;
+    p.out = grad_scores;
+    p.scale = scale;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
+static int transpose_args(int64_t n_rows, int64_t n_cols, int64_t nnz)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    if (n_rows < 0 || n_cols < 0 || nnz < 0) return CSR_ERR_SHAPE;
+    if (n_rows >= lim - 1 || n_cols >= lim - 1 || nnz >= lim) return CSR_ERR_SHAPE;
+    if (nnz > 0 && (n_rows == 0 || n_cols == 0)) return CSR_ERR_SHAPE;
+    return CSR_OK;
+}
+
+int csr_transpose_workspace_size(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, size_t* bytes)
+{
+    if (!ctx || !bytes) return CSR_ERR_NULL;
+    const int rc = transpose_args(n_rows, n_cols, nnz);
+    if (rc != CSR_OK) return set_err(ctx, rc, "bad sizes");
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    hipError_t e = csrk::transpose_workspace(n_cols, nnz, bytes);
+    if (e != hipSuccess) return hip_err(ctx, e, "transpose workspace");
+    return CSR_OK;
+}
+
+int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                  const int32_t* col_idx, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm,
+                  void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx || !row_ptr || !t_row_ptr) return CSR_ERR_NULL;
+    if (nnz > 0 && (!col_idx || !t_col_idx || !t_perm || !workspace)) return CSR_ERR_NULL;
+    const int rc = transpose_args(n_rows, n_cols, nnz);
+    if (rc != CSR_OK) return set_err(ctx, rc, "bad sizes");
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        DeviceGuard g(ctx->device);
+        size_t need = 0;
+        CSR_HIP(ctx, csrk::transpose_workspace(n_cols, nnz, &need));
+        if (ws_bytes < need) return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small for the transpose");
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        if ((ctx->flags & CSR_CTX_VALIDATE) && nnz > 0) {
+            int64_t* bad = reinterpret_cast<int64_t*>(workspace);
+            CSR_HIP(ctx, csrk::launch_validate(row_ptr, col_idx, n_rows, n_cols, nnz, bad, st));
+            CSR_HIP(ctx, hipMemcpyAsync(ctx->pinned, bad, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+            CSR_HIP(ctx, hipStreamSynchronize(st));
+            if (ctx->pinned[0] != 0) return set_err(ctx, CSR_ERR_INVALID_CSR, "row_ptr / col_idx fail CSR validation");
+        }
+        CSR_HIP(ctx, csrk::launch_transpose(row_ptr, col_idx, n_rows, n_cols, nnz, t_row_ptr, t_col_idx, t_perm,
+                                            workspace, ws_bytes, st));
+        return CSR_OK;
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const float* src, float* dst, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    if (n < 0 || n >= ((int64_t)1 << 31)) return set_err(ctx, CSR_ERR_SHAPE, "bad size");
+    if (n > 0 && (!perm || !src || !dst)) return CSR_ERR_NULL;
+    if (n > 0 && src == dst) return set_err(ctx, CSR_ERR_SHAPE, "src and dst must not alias");
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    CSR_HIP(ctx, csrk::launch_gather_values(perm, src, dst, n, static_cast<hipStream_t>(stream)));
+    return CSR_OK;
+}
+
 int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_schedule_t* out, uint64_t* signature)
 {
     if (!ctx || !p || !out) return CSR_ERR_NULL;
@@ -731,7 +825,7 @@ int csr_cache_store(csr_context_t ctx, uint64_t signature, const csr_schedule_t*
 {
     if (!ctx || !sched) return CSR_ERR_NULL;
     std::lock_guard<std::mutex> lk(ctx->mu);
-    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_ROW_SOFTMAX)
+    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_SOFTMAX_BWD)
         return set_err(ctx, CSR_ERR_SCHEDULE, "not a schedule of this library version");
     return store_entry(ctx, signature, *sched, 0.0);
 }

@@ -47,7 +47,8 @@ struct MhaArgs {
 struct SoftmaxArgs {
     const int32_t* row_ptr;
     int64_t n_rows;
-    const float* scores;  // [nnz]
+    const float* scores;  // [nnz] (the backward: the probabilities p)
+    const float* grad;    // [nnz] the backward's incoming gradient g, else unused
     float scale;
     float* probs;         // [nnz]
     int32_t W;            // lanes per group for short rows

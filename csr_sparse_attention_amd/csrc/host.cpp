@@ -92,12 +92,15 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (why) *why = msg;
         return code;
     };
-    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_ROW_SOFTMAX) return fail(CSR_ERR_SHAPE, "unknown op");
+    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_SOFTMAX_BWD) return fail(CSR_ERR_SHAPE, "unknown op");
     if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "this op takes fp32 operands");
     if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
-    if (p.op == CSR_OP_ROW_SOFTMAX) {
+    if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         const int64_t lim = (int64_t)1 << 31;
         if (p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "row softmax takes fp32 scores");
+        if (p.op == CSR_OP_SOFTMAX_BWD && !aligned(p.b, 4)) return fail(CSR_ERR_ALIGN, "fp32 arrays must be 4-byte aligned");
+        if (need_ptrs && p.op == CSR_OP_SOFTMAX_BWD && p.nnz > 0 && !p.b)
+            return fail(CSR_ERR_NULL, "grad_probs is NULL");
         if (p.n_rows < 0 || p.nnz < 0) return fail(CSR_ERR_SHAPE, "negative size");
         if (p.n_rows >= lim - 1 || p.nnz >= lim) return fail(CSR_ERR_SHAPE, "sizes must fit int32 indices");
         if (p.nnz > 0 && p.n_rows == 0) return fail(CSR_ERR_SHAPE, "entries but no rows");
@@ -162,8 +165,8 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
     if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH && s.mapping != CSR_MAP_SEGSCAN)
         return fail("unknown mapping");
     if (s.mapping == CSR_MAP_SEGSCAN) {
-        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM && p.op != CSR_OP_ROW_SOFTMAX)
-            return fail("the segmented-scan mapping serves SpMM, SDDMM and row softmax");
+        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM && p.op != CSR_OP_ROW_SOFTMAX && p.op != CSR_OP_SOFTMAX_BWD)
+            return fail("the segmented-scan mapping serves SpMM, SDDMM and the row softmax and its backward");
         if (s.group_lanes != 1 || s.passes > 4 || s.long_row != 0)
             return fail("segmented-scan schedules take group_lanes 1, passes <= 4, long_row 0");
     }
@@ -180,7 +183,9 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
         if (s.vec != 8 || s.passes != 1 || s.group_lanes != p.head_dim / 8) return fail("multi-head layout must be vec 8, W = head_dim / 8, 1 pass");
         return CSR_OK;
     }
-    if (p.op == CSR_OP_ROW_SOFTMAX) {
+    if (p.op == CSR_OP_SOFTMAX_BWD && s.mapping != CSR_MAP_SEGSCAN)
+        return fail("the softmax backward runs on lane-owned entry runs (segmented-scan mapping)");
+    if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         if (s.vec != 1 || s.passes != 1) return fail("row softmax layout must be vec 1, 1 pass");
         if (s.mapping == CSR_MAP_SEGSCAN) {
             if (s.group_lanes != 1 || s.long_row != 0) return fail("entry-run row softmax takes group_lanes 1, long_row 0");
@@ -228,13 +233,13 @@ WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
     } else if (p.op == CSR_OP_MHA) {
         ml = (size_t)nc * 2 * p.heads * 2 * 4;
         val = (size_t)nc * 2 * p.width * 4;
-    } else if (p.op == CSR_OP_ROW_SOFTMAX) {
+    } else if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         ml = (size_t)nc * 2 * 2 * 4;
         val = (size_t)p.n_rows * 2 * 4;  // per-row statistics
     }
     w.carry_val = w.carry_ml + up(ml);
     w.total = w.carry_val + up(val);
-    if (p.op == CSR_OP_ROW_SOFTMAX && s.mapping == CSR_MAP_SEGSCAN) {
+    if ((p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) && s.mapping == CSR_MAP_SEGSCAN) {
         // entry range of the row at every chunk boundary
         w.bounds = w.total;
         w.total = w.bounds + up((size_t)(nc + 1) * 2 * 4);
@@ -265,7 +270,7 @@ csr_schedule_t default_schedule(const csr_problem_t& p)
         s.long_row = 0;
         return s;
     }
-    if (p.op == CSR_OP_ROW_SOFTMAX) {
+    if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         // lane-owned entry runs, one cross-lane scan per chunk
         s.mapping = CSR_MAP_SEGSCAN;
         s.vec = 1;
@@ -299,6 +304,11 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
         out.push_back(s);
     };
     csr_schedule_t s = d;
+    if (p.op == CSR_OP_SOFTMAX_BWD) {
+        s.chunk_items = 512;
+        add(s);
+        return out;
+    }
     if (p.op == CSR_OP_ROW_SOFTMAX) {
         s.chunk_items = 512;  // lane-owned runs twice as long
         add(s);
@@ -363,7 +373,7 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
     // the layout inflate the gather traffic) + a latency-bound tail for the
     // longest row when rows are not split + launch overheads.
     const double bw = 5.0e12, wave_bw = 8.0e9, launch = 4e-6;
-    if (p.op == CSR_OP_ROW_SOFTMAX) {
+    if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         // scores in, probabilities out; the row-segment mapping pays about
         // twice the per-chunk instruction work of the entry runs
         const double nc = (double)n_chunks_for(p, s.chunk_items);
@@ -435,7 +445,7 @@ bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s,
     if (got != 11 || ver != CSR_SCHEDULE_VERSION) return false;
     for (size_t i = (size_t)n; i < line.size(); ++i)
         if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
-    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_ROW_SOFTMAX) return false;
+    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_SOFTMAX_BWD) return false;
     if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH && t.mapping != CSR_MAP_SEGSCAN) return false;
     t.version = CSR_SCHEDULE_VERSION;
     *sig = sg;

@@ -41,6 +41,15 @@ hipError_t launch_mha(int mapping, int lph, int chunk, const MhaArgs& a, hipStre
 hipError_t launch_mha_fixup(int lph, const MhaArgs& a, hipStream_t s);
 
 hipError_t launch_row_softmax(int mapping, int chunk, const SoftmaxArgs& a, hipStream_t s);
+hipError_t launch_row_softmax_backward(int chunk, const SoftmaxArgs& a, hipStream_t s);
+
+// CSR of A^T (entries of each column in row order) and its entry permutation;
+// the workspace holds two int32 [nnz] arrays and the sort's temporary storage.
+hipError_t transpose_workspace(int64_t n_cols, int64_t nnz, size_t* bytes);
+hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_cols,
+                            int64_t nnz, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm, void* ws,
+                            size_t ws_bytes, hipStream_t s);
+hipError_t launch_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n, hipStream_t s);
 
 // Structure kernels.
 hipError_t launch_fill_i64(int64_t* p, int64_t n, int64_t value, hipStream_t s);

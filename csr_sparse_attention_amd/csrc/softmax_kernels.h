@@ -161,7 +161,10 @@ __device__ __forceinline__ int sm_row_search(const int32_t* rp, int lo, int hi, 
     return lo;
 }
 
-template <int D>
+// BWD: the softmax backward instead, grad_scores_e = scale p_e (g_e - S_i)
+// with S_i the row sum of p g; scores holds p, grad holds g, probs receives
+// the result, and the per-row reduction is that plain sum (a piece is (0, S)).
+template <int D, bool BWD>
 __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
 {
     constexpr int RMAX = 2 * D / CSR_WAVE;
@@ -201,13 +204,16 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     const int kn = max(0, min(R, ne - k0));
     const float c = a.scale * LOG2E;
     float t[RMAX];
+    float g[BWD ? RMAX : 1];
     // the run's scores, straight from HBM (the wave's loads cover whole lines
     // between them); read once, so non-temporal
     const float* srun = a.scores + lo + k0;
+    const float* grun = BWD ? a.grad + lo + k0 : nullptr;
 #pragma unroll
     for (int k = 0; k < RMAX; ++k) {
         if (k >= R) break;
         t[k] = (k < kn) ? __builtin_nontemporal_load(srun + k) : 0.f;
+        if constexpr (BWD) g[k] = (k < kn) ? __builtin_nontemporal_load(grun + k) : 0.f;
     }
     if (active) {
         // row_ptr[x0 .. x0 + nrow]: nrow + 1 <= D + 2 values
@@ -232,8 +238,8 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
             const bool ok = k < kn;
             const int mk = ok ? mark[k0 + k] : 0;
             cur = mk ? mk - 1 : cur;
-            ri[k] = cur;  // past the run: the last row again, with t = -inf
-            t[k] = ok ? t[k] * c : -INFINITY;
+            ri[k] = cur;  // past the run: the last row again, adding nothing
+            if constexpr (!BWD) t[k] = ok ? t[k] * c : -INFINITY;
         }
     }
     __syncthreads();  // rp and the marks are rewritten below
@@ -243,11 +249,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     // the total of row i over this chunk: LDS statistics for a row completed
     // here, a carry piece (natural-log maximum) for a long row
     auto finish = [&](int i, float m, float l) {
+        const float mn = BWD ? 0.f : m * LN2;
         if (i == nend && slotB) {
-            a.carry_ml[2 * (slot_base + 1)] = m * LN2;
+            a.carry_ml[2 * (slot_base + 1)] = mn;
             a.carry_ml[2 * (slot_base + 1) + 1] = l;
         } else if (i == 0 && slotA) {
-            a.carry_ml[2 * slot_base] = m * LN2;
+            a.carry_ml[2 * slot_base] = mn;
             a.carry_ml[2 * slot_base + 1] = l;
         } else {
             rp[i] = __float_as_int(m);
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     // run goes to LDS at its row (the first one is finished after the scan)
     const int first = (kn > 0) ? ri[0] : -1;
     int tail = (kn > 0) ? first : -2 - lane;  // row of the open piece
-    float m = -INFINITY, l = 0.f;
+    float m = BWD ? 0.f : -INFINITY, l = 0.f;
 #pragma unroll
     for (int k = 0; k < RMAX; ++k) {
         if (k >= R) break;
@@ -267,17 +274,22 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
         rp[w] = __float_as_int(m);
         sl[w] = l;
         tail = close ? ri[k] : tail;
-        m = close ? -INFINITY : m;
-        l = close ? 0.f : l;
-        const float mm = (t[k] > m) ? t[k] : m;
-        l = fmaf(l, __builtin_amdgcn_exp2f(m - mm), __builtin_amdgcn_exp2f(t[k] - mm));
-        m = mm;
+        if constexpr (BWD) {
+            l = close ? 0.f : l;
+            if (k < kn) l = fmaf(t[k], g[k], l);
+        } else {
+            m = close ? -INFINITY : m;
+            l = close ? 0.f : l;
+            const float mm = (t[k] > m) ? t[k] : m;
+            l = fmaf(l, __builtin_amdgcn_exp2f(m - mm), __builtin_amdgcn_exp2f(t[k] - mm));
+            m = mm;
+        }
     }
     if (active && lane == 0) {
         a.carry_row[2 * chunk] = slotA ? x0 : -1;
         a.carry_row[2 * chunk + 1] = slotB ? x1 : -1;
         if (slotA && a_end == y0) {  // long row without entries here: empty piece
-            a.carry_ml[2 * slot_base] = -INFINITY;
+            a.carry_ml[2 * slot_base] = BWD ? 0.f : -INFINITY;
             a.carry_ml[2 * slot_base + 1] = 0.f;
         }
     }
@@ -288,7 +300,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
         const int r2 = __shfl_up(tail, off, CSR_WAVE);
         const float m2 = __shfl_up(sm, off, CSR_WAVE);
         const float l2 = __shfl_up(sq, off, CSR_WAVE);
-        if (lane >= off && r2 == tail) sm_merge2(sm, sq, m2, l2);
+        if (lane >= off && r2 == tail) {
+            if constexpr (BWD)
+                sq += l2;
+            else
+                sm_merge2(sm, sq, m2, l2);
+        }
     }
     // what the lanes before this one hold of this run's first row
     const int prev_tail = __shfl_up(tail, 1, CSR_WAVE);
@@ -297,7 +314,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     if (active && kn > 0) {
         if (tail != first) {  // the first row closed inside the run
             float fm = __int_as_float(rp[first]), fl = sl[first];
-            if (lane > 0 && prev_tail == first) sm_merge2(fm, fl, cm, cl);
+            if (lane > 0 && prev_tail == first) {
+                if constexpr (BWD)
+                    fl += cl;
+                else
+                    sm_merge2(fm, fl, cm, cl);
+            }
             finish(first, fm, fl);
         }
         // the open piece is the row's total over the chunk when no later lane continues it
@@ -312,14 +334,19 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
 #pragma unroll
     for (int k = 0; k < RMAX; ++k) {
         if (k >= R) break;
-        if (k >= ks && k < ke)
-            prun[k] = __builtin_amdgcn_exp2f(t[k] - __int_as_float(rp[ri[k]])) * __builtin_amdgcn_rcpf(sl[ri[k]]);
+        if (k >= ks && k < ke) {
+            if constexpr (BWD)
+                prun[k] = a.scale * t[k] * (g[k] - sl[ri[k]]);
+            else
+                prun[k] = __builtin_amdgcn_exp2f(t[k] - __int_as_float(rp[ri[k]])) * __builtin_amdgcn_rcpf(sl[ri[k]]);
+        }
     }
 }
 
 // Merges the (m, l) pieces of rows split across chunks (one wave per chunk
 // whose slot A holds a row; the pieces are slot B of the run of chunks before
 // it, then slot A).
+template <bool BWD>
 __device__ __forceinline__ void softmax_fixup_one(const SoftmaxArgs& a, int64_t c, int r)
 {
     const int lane = lane_id();
@@ -333,6 +360,20 @@ __device__ __forceinline__ void softmax_fixup_one(const SoftmaxArgs& a, int64_t 
         if (n < 64) break;
     }
     const int64_t np = c - k0 + 1;
+    if constexpr (BWD) {
+        // pieces are (0, partial sum of p g): add them
+        float sum = 0.f;
+        for (int64_t p = lane; p < np; p += CSR_WAVE) {
+            const int64_t s = (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c;
+            sum += a.carry_ml[2 * s + 1];
+        }
+        sum = xor_sum_from(sum, 1);
+        if (lane == 0) {
+            a.stats[2 * (int64_t)r] = 0.f;
+            a.stats[2 * (int64_t)r + 1] = sum;
+        }
+        return;
+    }
     float m = -INFINITY, l = 0.f;
     for (int64_t p = lane; p < np; p += CSR_WAVE) {
         const int64_t s = (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c;
@@ -357,6 +398,7 @@ __device__ __forceinline__ void softmax_fixup_one(const SoftmaxArgs& a, int64_t 
     }
 }
 
+template <bool BWD>
 __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
 {
     const int64_t base = fixup_window(a.n_chunks);
@@ -368,7 +410,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
     while (todo) {
         const int j = __builtin_ctzll(todo);
         todo &= todo - 1;
-        softmax_fixup_one(a, base + j, __shfl(rl, j, CSR_WAVE));
+        softmax_fixup_one<BWD>(a, base + j, __shfl(rl, j, CSR_WAVE));
     }
 }
 
@@ -416,6 +458,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split(SoftmaxArgs a)
 // consecutive entries (at most D entries, one pass of 4 loads per lane for
 // D = 256).  Only chunks inside or at the ends of rows longer than D hold
 // segments, so a window usually has few.
+template <bool BWD>
 __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split_runs(SoftmaxArgs a)
 {
     const int64_t base = ((int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK +
@@ -444,18 +487,24 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split_runs(SoftmaxArgs a)
     }
     const float c2 = a.scale * 1.44269504088896341f;
     auto segment = [&](int sb, int se, float m, float l) {
-        const float m2 = m * 1.44269504088896341f, il = 1.f / l;
+        const float m2 = m * 1.44269504088896341f, il = BWD ? 0.f : 1.f / l;
         for (int e0 = sb; e0 < se; e0 += 4 * CSR_WAVE) {
-            float x[4];
+            float x[4], y[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = e0 + u * CSR_WAVE + lane;
                 x[u] = (e < se) ? __builtin_nontemporal_load(a.scores + e) : 0.f;
+                if constexpr (BWD) y[u] = (e < se) ? __builtin_nontemporal_load(a.grad + e) : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = e0 + u * CSR_WAVE + lane;
-                if (e < se) a.probs[e] = __builtin_amdgcn_exp2f(x[u] * c2 - m2) * il;
+                if (e < se) {
+                    if constexpr (BWD)
+                        a.probs[e] = a.scale * x[u] * (y[u] - l);
+                    else
+                        a.probs[e] = __builtin_amdgcn_exp2f(x[u] * c2 - m2) * il;
+                }
             }
         }
     };

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
-from typing import Optional
+from typing import NamedTuple, Optional
 
 import torch
 
@@ -333,6 +333,120 @@ def attention_pipeline(row_ptr, col_idx, Q, K, V, *, scale: float = 1.0, fused: 
     return spmm(row_ptr, col_idx, probs, V, ctx=ctx)
 
 
+# ---------------------------------------------------------------------------
+# backward operations
+# ---------------------------------------------------------------------------
+
+def _softmax_bwd_problem(row_ptr, probs, grad, out, scale):
+    p = _softmax_problem(row_ptr, probs, out, scale)
+    p.op = _ffi.OP_SOFTMAX_BWD
+    p.b = _ptr(grad)
+    return p
+
+
+def _flat_f32(t, name, n):
+    if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous 1-D fp32 tensor of {n} values")
+
+
+def row_softmax_backward(row_ptr, probs, grad, *, scale: float = 1.0, out=None,
+                         schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None) -> torch.Tensor:
+    """Gradient of the row softmax: out[e] = scale * p_e * (g_e - sum over the
+    row of p g), for p = row_softmax(s, scale) and g = dL/dp.  ``out`` may be
+    ``probs`` or ``grad`` (in place)."""
+    _pattern(row_ptr, row_ptr)
+    _flat_f32(probs, "probs", probs.numel())
+    _flat_f32(grad, "grad", probs.numel())
+    if out is None:
+        out = torch.empty_like(probs)
+    p = _softmax_bwd_problem(row_ptr, probs, grad, out, scale)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_row_softmax_backward(ctx.handle, p.n_rows, p.nnz, p.row_ptr, p.a, p.b,
+                                               ctypes.c_float(scale), p.out, _sched_arg(schedule), ws.data_ptr(),
+                                               nb, st)
+
+    _run(p, probs.device, schedule, ctx, call)
+    return out
+
+
+class Transposed(NamedTuple):
+    """The CSR pattern of A^T: row_ptr [n_cols + 1], col_idx [nnz] (rows of A)
+    and perm [nnz] (the entry of A behind each entry of A^T)."""
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    perm: torch.Tensor
+
+
+def transpose(row_ptr, col_idx, n_cols: int, *, ctx: Optional[Context] = None) -> Transposed:
+    """CSR of A^T for the pattern (row_ptr, col_idx) with n_cols columns; the
+    entries of each column keep their row order (deterministic)."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    device = row_ptr.device
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    nbytes = ctypes.c_size_t()
+    _check(lib.csr_transpose_workspace_size(ctx.handle, n_rows, n_cols, nnz, ctypes.byref(nbytes)),
+           "csr_transpose_workspace_size", ctx)
+    ws = _workspace(device, nbytes.value)
+    t_rp = torch.empty(n_cols + 1, dtype=torch.int32, device=device)
+    t_ci = torch.empty(nnz, dtype=torch.int32, device=device)
+    perm = torch.empty(nnz, dtype=torch.int32, device=device)
+    _check(lib.csr_transpose(ctx.handle, n_rows, n_cols, nnz, row_ptr.data_ptr(), col_idx.data_ptr(),
+                             t_rp.data_ptr(), t_ci.data_ptr(), perm.data_ptr(), ws.data_ptr(), nbytes.value,
+                             _stream(device)), "csr_transpose", ctx)
+    return Transposed(t_rp, t_ci, perm)
+
+
+def gather_values(perm, src, *, out=None, ctx: Optional[Context] = None) -> torch.Tensor:
+    """out[k] = src[perm[k]] (per-entry values into a transposed pattern's order)."""
+    if perm.dtype != torch.int32 or perm.dim() != 1 or not perm.is_contiguous() or not perm.is_cuda:
+        raise ValueError("perm must be a contiguous 1-D int32 GPU tensor")
+    if src.dtype != torch.float32 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous fp32 tensor")
+    if out is None:
+        out = torch.empty(perm.numel(), dtype=torch.float32, device=perm.device)
+    ctx = ctx or default_context(perm.device.index)
+    _check(_lib().csr_gather_values(ctx.handle, perm.numel(), perm.data_ptr(), src.data_ptr(), out.data_ptr(),
+                                    _stream(perm.device)), "csr_gather_values", ctx)
+    return out
+
+
+def spmm_backward(row_ptr, col_idx, vals, X, dY, *, transposed: Optional[Transposed] = None,
+                  ctx: Optional[Context] = None):
+    """Gradients of Y = A X: (d vals, dX) with d vals_e = <dY[row_e], X[col_e]>
+    (SDDMM; None when vals is None) and dX = A^T dY (SpMM on the transposed
+    pattern).  ``transposed`` (from transpose()) is reused when given."""
+    At = transposed or transpose(row_ptr, col_idx, X.shape[0], ctx=ctx)
+    vt = None if vals is None else gather_values(At.perm, vals, ctx=ctx)
+    dX = spmm(At.row_ptr, At.col_idx, vt, dY, ctx=ctx)
+    dvals = None if vals is None else sddmm(row_ptr, col_idx, dY, X, ctx=ctx)
+    return dvals, dX
+
+
+def sddmm_backward(row_ptr, col_idx, U, V, dout, *, transposed: Optional[Transposed] = None,
+                   ctx: Optional[Context] = None):
+    """Gradients of out_e = <U[row_e], V[col_e]>: dU = A_g V and dV = A_g^T U,
+    A_g the pattern carrying dout."""
+    At = transposed or transpose(row_ptr, col_idx, V.shape[0], ctx=ctx)
+    dU = spmm(row_ptr, col_idx, dout, V, ctx=ctx)
+    dV = spmm(At.row_ptr, At.col_idx, gather_values(At.perm, dout, ctx=ctx), U, ctx=ctx)
+    return dU, dV
+
+
+def attention_backward(row_ptr, col_idx, edge_scores, node_value, d_out, *, scale: float = 1.0, probs=None,
+                       transposed: Optional[Transposed] = None, ctx: Optional[Context] = None):
+    """Gradients of out = softmax_row(scale * S) V (scores given): returns
+    (d edge_scores, d node_value).  P is recomputed by row_softmax unless given;
+    dP = SDDMM(d_out, V); d scores = row_softmax_backward(P, dP); dV = P^T d_out."""
+    At = transposed or transpose(row_ptr, col_idx, node_value.shape[0], ctx=ctx)
+    P = probs if probs is not None else row_softmax(row_ptr, edge_scores, scale=scale, ctx=ctx)
+    dP = sddmm(row_ptr, col_idx, d_out, node_value, ctx=ctx)
+    dS = row_softmax_backward(row_ptr, P, dP, scale=scale, out=dP, ctx=ctx)
+    dV = spmm(At.row_ptr, At.col_idx, gather_values(At.perm, P, ctx=ctx), d_out, ctx=ctx)
+    return dS, dV
+
+
 def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0) -> CsrProblem:
     """The csr_problem_t of a call, for select() / workspace_size() /
     default_schedule(): op is 'spmm' (vals, X), 'sddmm' (U, V), 'attention'
@@ -355,6 +469,10 @@ def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 
         (scores,) = operands
         out = out if out is not None else torch.empty_like(scores)
         return _softmax_problem(row_ptr, scores, out, scale), out
+    if op == "row_softmax_backward":
+        probs, grad = operands
+        out = out if out is not None else torch.empty_like(probs)
+        return _softmax_bwd_problem(row_ptr, probs, grad, out, scale), out
     if op == "mha":
         Q, K, V = operands
         out = out if out is not None else torch.empty((n_rows,) + tuple(Q.shape[1:]), dtype=torch.float32,

@@ -79,7 +79,8 @@ enum csr_op {
     CSR_OP_SDDMM = 2,     /* out_e = <U[row_e], V[col_e]> */
     CSR_OP_ATTENTION = 3, /* scores given: out = softmax_row(scale * S) V */
     CSR_OP_MHA = 4,       /* multi-head, scores = scale * <Q_i, K_j> per head */
-    CSR_OP_ROW_SOFTMAX = 5 /* p_e = softmax over the row's entries of scale * s */
+    CSR_OP_ROW_SOFTMAX = 5, /* p_e = softmax over the row's entries of scale * s */
+    CSR_OP_SOFTMAX_BWD = 6  /* ds_e = scale * p_e * (g_e - sum over the row of p g) */
 };
 
 enum csr_dtype { CSR_DTYPE_F32 = 0, CSR_DTYPE_BF16 = 1 };
@@ -269,6 +270,50 @@ int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t
 int csr_row_softmax(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
                     const float* scores, float scale, float* probs, const csr_schedule_t* sched,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward operations (the gradients of the three products, for training the
+ * GNN layers the AutoSAGE page's SpMM / SDDMM serve).  With Y = A X:
+ * dX = A^T dY (csr_transpose + csr_gather_values + csr_spmm) and
+ * d(edge values) = SDDMM(dY, X).  With out_e = <U_i, V_j>: dU = A_g V and
+ * dV = A_g^T U.  For the attention, dV = P^T dOut, dP = SDDMM(dOut, V) and
+ * d(scores) = csr_row_softmax_backward(P, dP).
+ * ------------------------------------------------------------------------- */
+
+/* Softmax backward over each row's stored entries: with p the row softmax of
+ * scale * s and g = dL/dp, dL/ds_e = scale * p_e * (g_e - sum over the row of
+ * p * g).  probs, grad_probs, grad_scores: fp32 [nnz] (grad_scores may alias
+ * either input for an in-place update; an in-place call with sched == NULL
+ * picks its schedule by the cost model alone).  Rows without entries have
+ * nothing to write.  Schedules: the segmented-scan mapping (lane-owned entry
+ * runs), vec 1, passes 1, group_lanes 1, long_row 0, chunk_items 256 or 512.
+ * Errors as for csr_row_softmax. */
+int csr_row_softmax_backward(csr_context_t ctx, int64_t n_rows, int64_t nnz, const int32_t* row_ptr,
+                             const float* probs, const float* grad_probs, float scale, float* grad_scores,
+                             const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
+
+/* Device workspace (bytes) that csr_transpose needs for these sizes.
+ * Returns CSR_ERR_SHAPE for negative sizes or sizes beyond int32 indices,
+ * CSR_ERR_DEVICE on a host-only context. */
+int csr_transpose_workspace_size(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, size_t* bytes);
+
+/* The CSR pattern of A^T (A in CSC form): t_row_ptr int32 [n_cols + 1],
+ * t_col_idx int32 [nnz] (the original row of each entry), t_perm int32 [nnz]
+ * (the original entry index of each transposed entry, so that a value array v
+ * of A becomes v[t_perm[k]] for A^T; see csr_gather_values).  The entries of
+ * each column keep their original order (a stable sort by column): the result
+ * is deterministic.  All arrays are caller-allocated device memory; the inputs
+ * are not modified; workspace of csr_transpose_workspace_size bytes.  col_idx
+ * must lie in [0, n_cols) (checked only with CSR_CTX_VALIDATE:
+ * CSR_ERR_INVALID_CSR).  CSR_ERR_WORKSPACE when ws_bytes is too small. */
+int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                  const int32_t* col_idx, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* dst[k] = src[perm[k]] for k < n (fp32; dst must not alias src): moves
+ * per-entry values (edge values, probabilities, gradients) into the order of
+ * a transposed pattern. */
+int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const float* src, float* dst, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Schedule selection and cache (AutoSAGE page, Abstract: input-aware choice

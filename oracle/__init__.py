@@ -22,6 +22,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from .structure import (  # noqa: F401
+    transpose,
     degree_histogram,
     merge_path_partition,
     merge_path_bruteforce,
@@ -52,7 +53,11 @@ def _declare(lib):
     lib.oracle_sddmm.argtypes = [P, P, P, I, P, I, I, I, I, P, P]
     lib.oracle_attention.argtypes = [P, P, P, P, I, I, D, I, I, P, P, P]
     lib.oracle_mha.argtypes = [P, P, P, P, P, I, I, D, I, I, P, P, P]
-    for f in (lib.oracle_spmm, lib.oracle_sddmm, lib.oracle_attention, lib.oracle_mha):
+    lib.oracle_softmax_backward.argtypes = [P, P, P, D, I, I, P, P]
+    lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, D, I, I, P, P]
+    lib.oracle_spmm_transpose.argtypes = [P, P, P, P, I, I, I, P, P]
+    for f in (lib.oracle_spmm, lib.oracle_sddmm, lib.oracle_attention, lib.oracle_mha,
+              lib.oracle_softmax_backward, lib.oracle_attention_backward, lib.oracle_spmm_transpose):
         f.restype = None
     return lib
 
@@ -209,3 +214,59 @@ def mha(row_ptr, col_idx, Q, K, V, scale, r0=0, r1=None, threads=1, want_probs=F
     return out, mag, probs
 
 
+
+
+def softmax_backward(row_ptr, probs, grad, scale=1.0, r0=0, r1=None, threads=1):
+    """Softmax backward of the entries of rows [r0, r1) from fp32 probabilities
+    and incoming gradient: (values, magnitudes), float64."""
+    lib = _load()
+    rp = _c(row_ptr, np.int32)
+    pc, gc = _c(probs, np.float32), _c(grad, np.float32)
+    r1 = len(rp) - 1 if r1 is None else r1
+    base = int(rp[r0])
+    n = int(rp[r1]) - base
+    out, mag = np.zeros(n), np.zeros(n)
+
+    def fn(a, b):
+        off = int(rp[a]) - base
+        lib.oracle_softmax_backward(_ptr(rp), _ptr(pc), _ptr(gc), float(scale), a, b,
+                                    out[off:].ctypes.data, mag[off:].ctypes.data)
+
+    _run(_ranges(rp, r0, r1, threads), fn)
+    return out, mag
+
+
+def attention_backward_scores(row_ptr, col_idx, scores, V, d_out, scale=1.0, r0=0, r1=None, threads=1):
+    """Gradient of softmax_row(scale * S) V with respect to the scores for the
+    incoming gradient d_out [n_rows, F], entries of rows [r0, r1)."""
+    lib = _load()
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    sc, Vc, dc = _c(scores, np.float32), _c(V, np.float32), _c(d_out, np.float32)
+    F = Vc.shape[1]
+    assert dc.shape[1] == F
+    r1 = len(rp) - 1 if r1 is None else r1
+    base = int(rp[r0])
+    n = int(rp[r1]) - base
+    ds, mag = np.zeros(n), np.zeros(n)
+
+    def fn(a, b):
+        off = int(rp[a]) - base
+        lib.oracle_attention_backward(_ptr(rp), _ptr(ci), _ptr(sc), _ptr(Vc), _ptr(dc), F, float(scale), a, b,
+                                      ds[off:].ctypes.data, mag[off:].ctypes.data)
+
+    _run(_ranges(rp, r0, r1, threads), fn)
+    return ds, mag
+
+
+def spmm_transpose(row_ptr, col_idx, vals, dY, n_cols):
+    """A^T dY over the whole matrix (float64 values a_e, None = 1): (dX, mag),
+    single-threaded (the columns gather from every row)."""
+    lib = _load()
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    va = None if vals is None else np.ascontiguousarray(vals, dtype=np.float64)
+    yc = _c(dY, np.float32)
+    F = yc.shape[1]
+    dX, mag = np.zeros((n_cols, F)), np.zeros((n_cols, F))
+    lib.oracle_spmm_transpose(_ptr(rp), _ptr(ci), _ptr(va), _ptr(yc), len(rp) - 1, n_cols, F,
+                              dX.ctypes.data, mag.ctypes.data)
+    return dX, mag

@@ -25,6 +25,16 @@
  *    t_e = scale * sum_d Q[i, h, d] * K[col_e, h, d] from bfloat16 inputs read
  *    exactly.
  *
+ *  - Backward (the gradients of the three products; prior art's GNN training,
+ *    SparseTIR page, Abstract): the softmax backward over a row's entries,
+ *    ds_e = scale * p_e * (g_e - sum over the row of p g), which is the chain
+ *    rule through p_e = exp(t_e - m) / l with t = scale * s; the attention's
+ *    score gradient from its inputs (probabilities by the two-pass softmax
+ *    above, dp_e = sum_f dOut[i, f] V[col_e, f], then the softmax backward);
+ *    and the product with the transpose, dX[j, f] = sum over the entries e
+ *    with col_e = j of a_e * dY[row_e, f], accumulated row by row in storage
+ *    order.
+ *
  * Besides each value the oracle returns its magnitude, the same sum taken over
  * absolute values (sum |a_e| |X[col_e, f]|, sum |U| |V|, sum p_e |V|).  Tests
  * divide the GPU's error by it, which stays meaningful where random signs
@@ -174,6 +184,97 @@ void oracle_mha(const int32_t *row_ptr, const int32_t *col_idx,
                     y[h * D + d] += p * bf16_to_double(v[d]);
                     if (g) g[h * D + d] += p * fabs(bf16_to_double(v[d]));
                 }
+            }
+        }
+    }
+}
+
+/* Softmax backward from given probabilities and incoming gradient (fp32 arrays
+ * read exactly): out_e = scale * p_e * (g_e - S_i), S_i = sum over row i of
+ * p g; mag_e = |scale| * p_e * (|g_e| + sum over the row of p |g|).  out and
+ * mag are indexed from row_ptr[r0]. */
+void oracle_softmax_backward(const int32_t *row_ptr, const float *probs, const float *grad, double scale,
+                             int64_t r0, int64_t r1, double *out, double *mag)
+{
+    const int64_t base = row_ptr[r0];
+    for (int64_t i = r0; i < r1; ++i) {
+        double S = 0.0, A = 0.0;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            S += (double)probs[e] * (double)grad[e];
+            A += (double)probs[e] * fabs((double)grad[e]);
+        }
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            double p = (double)probs[e];
+            out[e - base] = scale * p * ((double)grad[e] - S);
+            if (mag) mag[e - base] = fabs(scale) * p * (fabs((double)grad[e]) + A);
+        }
+    }
+}
+
+/* Gradient of the scores-given attention out = softmax_row(scale * s) V with
+ * respect to the scores, for the incoming gradient dOut [n_rows, F]:
+ * ds_e = scale * p_e * (dp_e - sum over the row of p dp), dp_e = <dOut_i,
+ * V[col_e]>.  Probabilities by the two-pass softmax.  mag_e = |scale| * p_e *
+ * (|dp|_e + sum over the row of p |dp|), |dp|_e = sum_f |dOut| |V|.  ds and
+ * mag are indexed from row_ptr[r0]. */
+void oracle_attention_backward(const int32_t *row_ptr, const int32_t *col_idx, const float *scores,
+                               const float *Vv, const float *dOut, int64_t F, double scale, int64_t r0,
+                               int64_t r1, double *ds, double *mag)
+{
+    const int64_t base = row_ptr[r0];
+    for (int64_t i = r0; i < r1; ++i) {
+        const int64_t b = row_ptr[i], end = row_ptr[i + 1];
+        if (b == end) continue;
+        double m = -INFINITY;
+        for (int64_t e = b; e < end; ++e) {
+            double t = scale * (double)scores[e];
+            if (t > m) m = t;
+        }
+        double l = 0.0;
+        for (int64_t e = b; e < end; ++e) l += exp(scale * (double)scores[e] - m);
+        const float *go = dOut + i * F;
+        double S = 0.0, A = 0.0;
+        for (int64_t e = b; e < end; ++e) {
+            const float *v = Vv + (int64_t)col_idx[e] * F;
+            double dp = 0.0, ap = 0.0;
+            for (int64_t f = 0; f < F; ++f) {
+                dp += (double)go[f] * (double)v[f];
+                ap += fabs((double)go[f]) * fabs((double)v[f]);
+            }
+            double p = exp(scale * (double)scores[e] - m) / l;
+            ds[e - base] = dp;  /* dp for now */
+            if (mag) mag[e - base] = ap;
+            S += p * dp;
+            A += p * ap;
+        }
+        for (int64_t e = b; e < end; ++e) {
+            double p = exp(scale * (double)scores[e] - m) / l;
+            ds[e - base] = scale * p * (ds[e - base] - S);
+            if (mag) mag[e - base] = fabs(scale) * p * (mag[e - base] + A);
+        }
+    }
+}
+
+/* dX = A^T dY over the whole matrix: dX[j, f] = sum over entries e with
+ * col_e = j of a_e dY[row_e, f] (a_e = vals[e], double; vals NULL means 1),
+ * visiting the rows in order and each row's entries in storage order.
+ * dX, mag: [n_cols, F], zeroed here. */
+void oracle_spmm_transpose(const int32_t *row_ptr, const int32_t *col_idx, const double *vals, const float *dY,
+                           int64_t n_rows, int64_t n_cols, int64_t F, double *dX, double *mag)
+{
+    for (int64_t k = 0; k < n_cols * F; ++k) {
+        dX[k] = 0.0;
+        if (mag) mag[k] = 0.0;
+    }
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const float *y = dY + i * F;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            double a = vals ? vals[e] : 1.0;
+            double *x = dX + (int64_t)col_idx[e] * F;
+            double *g = mag ? mag + (int64_t)col_idx[e] * F : 0;
+            for (int64_t f = 0; f < F; ++f) {
+                x[f] += a * (double)y[f];
+                if (g) g[f] += fabs(a) * fabs((double)y[f]);
             }
         }
     }

@@ -13,6 +13,9 @@
   [c * D, (c + 1) * D) of that sequence.  Its start is the pair (x, y) = (row
   ends, entries) that precede item c * D.
 
+* Transpose: the CSR pattern of A^T, i.e. the entries regrouped by column,
+  each column listing its rows in increasing order (a stable sort by column).
+
 * FNV-1a 64: the published Fowler-Noll-Vo hash (offset basis
   0xcbf29ce484222325, prime 0x100000001b3; per byte: xor, then multiply).
 """
@@ -85,3 +88,19 @@ def fnv1a64(data: bytes) -> int:
         h ^= byte
         h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
     return h
+
+
+def transpose(row_ptr, col_idx, n_cols):
+    """The CSR pattern of A^T by its definition: the entries sorted by column
+    with a stable sort (so each column lists its rows in order), the row of
+    each entry as the new column index, and per-column counts accumulated into
+    the new row_ptr.  Returns (t_row_ptr, t_col_idx, perm) with perm[k] the
+    original entry index of transposed entry k."""
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    rows = np.repeat(np.arange(len(rp) - 1, dtype=np.int64), np.diff(rp))
+    perm = np.argsort(ci, kind="stable")
+    counts = np.bincount(ci, minlength=n_cols)[:n_cols]
+    t_rp = np.zeros(n_cols + 1, dtype=np.int64)
+    np.cumsum(counts, out=t_rp[1:])
+    return t_rp.astype(np.int32), rows[perm].astype(np.int32), perm.astype(np.int32)

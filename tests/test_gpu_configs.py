@@ -223,3 +223,45 @@ def test_c4_row_softmax_full():
     assert err < TOL_F32, err
     assert _row_sums_ok(csr, out) < 1e-5
     print(f"c4 row softmax: {s} max err {err:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# backward operations at full size
+# ---------------------------------------------------------------------------
+
+def test_c3_row_softmax_backward():
+    csr = pattern("c3")
+    rp, _ = pattern_dev("c3")
+    rng = np.random.default_rng(33)
+    sc = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+    p = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, 0.125, threads=16, want_probs=True)[2].astype(np.float32)
+    g = rng.standard_normal(csr.nnz).astype(np.float32)
+    s = selected("row_softmax_backward", rp, None, dev(p), dev(g), scale=0.125)
+    out = csa.row_softmax_backward(rp, dev(p), dev(g), scale=0.125, schedule=s).cpu().numpy()
+    rows = sample_rows(csr, seed=33)
+    got = np.concatenate([out[csr.row_ptr[r]:csr.row_ptr[r + 1]] for r in rows])
+    ref, mag = oracle_rows(lambda r: oracle.softmax_backward(csr.row_ptr, p, g, 0.125, r, r + 1), rows)
+    print(f"c3 softmax backward: {s} max err {assert_close(got, ref, mag, TOL_F32, 'c3 softmax bwd'):.2e}")
+
+
+def test_c4_attention_backward_full():
+    csr = pattern("c4")
+    rp, ci = pattern_dev("c4")
+    rng = np.random.default_rng(44)
+    F = 8
+    sc = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    want = oracle.transpose(csr.row_ptr, csr.col_idx, csr.n_cols)
+    for got, exp, name in zip(t, want, ("row_ptr", "col_idx", "perm")):
+        assert np.array_equal(got.cpu().numpy(), exp), name
+    dS, dV = csa.attention_backward(rp, ci, dev(sc), dev(V), dev(dO), scale=0.125, transposed=t)
+    ref, mag = oracle.attention_backward_scores(csr.row_ptr, csr.col_idx, sc, V, dO, 0.125, threads=16)
+    e1 = assert_close(dS.cpu().numpy(), ref, mag, TOL_F32, "c4 d scores")
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+    P = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, 0.125, threads=16, want_probs=True)[2]
+    ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P, dO, csr.n_cols)
+    e2 = assert_close(dV.cpu().numpy(), ref, mag, TOL_F32, "c4 dV")
+    print(f"c4 attention backward: max err d scores {e1:.2e}, dV {e2:.2e}")

@@ -558,3 +558,118 @@ def test_attention_pipeline_unfused_equals_fused():
     for fused in (True, False):
         out = csa.attention_pipeline(rp, ci, dev(Q), dev(K), dev(V), scale=scale, fused=fused)
         assert_close(out.cpu().numpy(), ref, mag, TOL_F32, f"fused={fused}")
+
+
+# ---------------------------------------------------------------------------
+# backward operations: transpose, value gather, softmax backward and the
+# gradients of SpMM, SDDMM and the attention
+# ---------------------------------------------------------------------------
+
+def _graphs_for_backward():
+    return {"skew": skew_graph(1), "dup": dup_graph(3), "short": short_rows_graph(503),
+            "edges": chunk_edge_graph(504)}
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges", "empty"])
+def test_transpose_bit_exact(graph):
+    if graph == "empty":
+        csr = CSR(5, 7, np.zeros(6, np.int32), np.zeros(0, np.int32))
+    else:
+        csr = _graphs_for_backward()[graph]
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    want = oracle.transpose(csr.row_ptr, csr.col_idx, csr.n_cols)
+    for got, exp, name in zip(t, want, ("row_ptr", "col_idx", "perm")):
+        assert np.array_equal(got.cpu().numpy(), exp), name
+    # values follow their entries
+    vals = np.random.default_rng(5).standard_normal(csr.nnz).astype(np.float32)
+    if csr.nnz:
+        got = csa.gather_values(t.perm, dev(vals)).cpu().numpy()
+        assert np.array_equal(got, vals[want[2]])
+
+
+def _probs_and_grad(csr, seed, scale):
+    rng = np.random.default_rng(seed)
+    sc = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+    p = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, scale, want_probs=True,
+                         threads=oracle.default_threads())[2].astype(np.float32)
+    g = rng.standard_normal(csr.nnz).astype(np.float32)
+    return p, g
+
+
+@pytest.mark.parametrize("graph", ["skew", "short", "edges"])
+@pytest.mark.parametrize("scale", [1.0, 0.125])
+def test_row_softmax_backward_every_schedule(graph, scale):
+    csr = _graphs_for_backward()[graph]
+    p, g = _probs_and_grad(csr, 600, scale)
+    ref, mag = oracle.softmax_backward(csr.row_ptr, p, g, scale, threads=oracle.default_threads())
+    rp, pd, gd = dev(csr.row_ptr), dev(p), dev(g)
+    prob, _ = csa.make_problem("row_softmax_backward", rp, None, pd, gd, scale=scale)
+    scheds = csa.candidates(prob)
+    assert {s.chunk_items for s in scheds} == {256, 512}
+    for s in scheds:
+        out = csa.row_softmax_backward(rp, pd, gd, scale=scale, schedule=s).cpu().numpy()
+        assert_close(out, ref, mag, TOL_F32, sched_id(s))
+    out = csa.row_softmax_backward(rp, pd, gd, scale=scale).cpu().numpy()  # automatic selection
+    assert_close(out, ref, mag, TOL_F32, "auto")
+    x = dev(g)
+    csa.row_softmax_backward(rp, pd, x, scale=scale, out=x)  # in place over the gradient
+    assert_close(x.cpu().numpy(), ref, mag, TOL_F32, "in place")
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup"])
+def test_spmm_backward(graph):
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(610)
+    F = 24
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dY = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    dvals, dX = csa.spmm_backward(rp, ci, dev(vals), dev(X), dev(dY))
+    ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, dY, X, threads=oracle.default_threads())
+    assert_close(dvals.cpu().numpy(), ref, mag, TOL_F32, "d vals")
+    ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, vals.astype(np.float64), dY, csr.n_cols)
+    assert_close(dX.cpu().numpy(), ref, mag, TOL_F32, "dX")
+    # no edge values: A = pattern of ones, no value gradient
+    dv0, dX1 = csa.spmm_backward(rp, ci, None, dev(X), dev(dY))
+    assert dv0 is None
+    ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, None, dY, csr.n_cols)
+    assert_close(dX1.cpu().numpy(), ref, mag, TOL_F32, "dX, unit values")
+
+
+def test_sddmm_backward():
+    csr = skew_graph(7, n_rows=1200, n_cols=9000, giant=5000)
+    rng = np.random.default_rng(620)
+    K = 20
+    U = rng.standard_normal((csr.n_rows, K)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, K)).astype(np.float32)
+    g = rng.standard_normal(csr.nnz).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    dU, dV = csa.sddmm_backward(rp, ci, dev(U), dev(V), dev(g), transposed=t)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, g, V, threads=oracle.default_threads())
+    assert_close(dU.cpu().numpy(), ref, mag, TOL_F32, "dU")
+    ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, g.astype(np.float64), U, csr.n_cols)
+    assert_close(dV.cpu().numpy(), ref, mag, TOL_F32, "dV")
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("scale", [1.0, 0.125])
+def test_attention_backward(graph, scale):
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(630)
+    F = 16
+    sc = (2 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    dS, dV = csa.attention_backward(rp, ci, dev(sc), dev(V), dev(dO), scale=scale)
+    ref, mag = oracle.attention_backward_scores(csr.row_ptr, csr.col_idx, sc, V, dO, scale,
+                                                threads=oracle.default_threads())
+    assert_close(dS.cpu().numpy(), ref, mag, TOL_F32, "d scores")
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+    P = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, scale, want_probs=True)[2]
+    ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P, dO, csr.n_cols)
+    assert_close(dV.cpu().numpy(), ref, mag, TOL_F32, "dV")

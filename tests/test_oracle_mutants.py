@@ -53,6 +53,21 @@ MUTANTS = [
                                       "const uint16_t *v = V + (int64_t)col_idx[e] * HD;", None)]),
     ("bfloat16 widened with the wrong shift", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;",
                                                 None)]),
+    ("softmax backward drops the row sum", [("out[e - base] = scale * p * ((double)grad[e] - S);",
+                                             "out[e - base] = scale * p * (double)grad[e];", None)]),
+    ("softmax backward drops the scale", [("out[e - base] = scale * p * ((double)grad[e] - S);",
+                                           "out[e - base] = p * ((double)grad[e] - S);", None)]),
+    ("softmax backward sums g instead of p g", [("S += (double)probs[e] * (double)grad[e];",
+                                                 "S += (double)grad[e];", None)]),
+    ("attention backward dots with the wrong value row", [(
+        "const float *v = Vv + (int64_t)col_idx[e] * F;\n            double dp",
+        "const float *v = Vv + (int64_t)col_idx[b] * F;\n            double dp", None)]),
+    ("attention backward flips the sign", [("ds[e - base] = scale * p * (ds[e - base] - S);",
+                                            "ds[e - base] = scale * p * (S - ds[e - base]);", None)]),
+    ("transpose product gathers by column", [("const float *y = dY + i * F;",
+                                              "const float *y = dY + (i % n_cols) * F;", None)]),
+    ("transpose product scatters to the row", [("double *x = dX + (int64_t)col_idx[e] * F;",
+                                                "double *x = dX + (i % n_cols) * F;", None)]),
 ]
 
 

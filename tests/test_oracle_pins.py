@@ -399,3 +399,136 @@ def test_merge_path_counting_equals_walk(seed):
         # every chunk holds exactly D items except the last
         items = (x[1:] + y[1:]) - (x[:-1] + y[:-1])
         assert (items[:-1] == D).all() and 0 <= items[-1] <= D
+
+
+# --------------------------------------------------------------------------
+# backward operations: finite differences of the (pinned) forward, closed
+# forms, invariants, dense algebra
+# --------------------------------------------------------------------------
+
+def _grid_scores(rng, n, lim=2.0):
+    """Scores on a 2^-8 grid in [-lim, lim]: s +- 2^-10 is exact in fp32, so a
+    central difference perturbs exactly one score by exactly h."""
+    return (np.round(rng.uniform(-lim, lim, n) * 256) / 256).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_softmax_backward_finite_differences(oracle_lib, seed):
+    rng = np.random.default_rng(700 + seed)
+    csr = random_small_graph(9, 11, 0.4, rng, empty_frac=0.2, allow_dup=True)
+    scale = [1.0, 0.5, 0.125, 2.0][seed]
+    s = _grid_scores(rng, csr.nnz)
+    g = rng.standard_normal(csr.nnz).astype(np.float32)
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+
+    def loss(sv):
+        p = oracle_lib.attention(csr.row_ptr, csr.col_idx, sv, zero, scale, want_probs=True)[2]
+        return float(np.dot(g.astype(np.float64), p))
+
+    p32 = oracle_lib.attention(csr.row_ptr, csr.col_idx, s, zero, scale, want_probs=True)[2].astype(np.float32)
+    ds, mag = oracle_lib.softmax_backward(csr.row_ptr, p32, g, scale)
+    h = 2.0 ** -10
+    fd = np.empty(csr.nnz)
+    for e in range(csr.nnz):
+        sp, sm = s.copy(), s.copy()
+        sp[e] += np.float32(h)
+        sm[e] -= np.float32(h)
+        fd[e] = (loss(sp) - loss(sm)) / (2 * h)
+    assert rel_err(ds, fd, mag) < 1e-4
+
+
+def test_softmax_backward_two_entry_closed_form(oracle_lib):
+    # p1 = logistic(t1 - t2): dL/ds1 = scale p1 p2 (g1 - g2) = -dL/ds2
+    rp = np.array([0, 2], np.int32)
+    for t1, t2, g1, g2, scale in ((0.5, -1.0, 2.0, -0.5, 1.0), (3.0, 3.0, 1.0, 4.0, 0.25), (-2.0, 1.5, 0.0, 1.0, 2.0)):
+        p1 = 1.0 / (1.0 + np.exp(-scale * (t1 - t2)))
+        p = np.array([p1, 1 - p1], np.float32)
+        ds, _ = oracle_lib.softmax_backward(rp, p, np.array([g1, g2], np.float32), scale)
+        want = scale * float(p[0]) * float(p[1]) * (g1 - g2)
+        assert abs(ds[0] - want) < 1e-6 and abs(ds[1] + want) < 1e-6
+
+
+def test_softmax_backward_invariants(oracle_lib):
+    rng = np.random.default_rng(710)
+    csr = random_small_graph(40, 30, 0.3, rng, empty_frac=0.2)
+    zero = np.zeros((csr.n_cols, 1), np.float32)
+    p = oracle_lib.attention(csr.row_ptr, csr.col_idx, rng.standard_normal(csr.nnz).astype(np.float32), zero,
+                             1.0, want_probs=True)[2].astype(np.float32)
+    g = rng.standard_normal(csr.nnz).astype(np.float32)
+    ds, _ = oracle_lib.softmax_backward(csr.row_ptr, p, g, 0.7)
+    live = csr.degrees() > 0
+    starts = csr.row_ptr[:-1][live]
+    # over each row the gradient sums to scale * S * (1 - sum p): zero for an
+    # exact softmax, here the rounding of p to fp32
+    S = np.add.reduceat(p.astype(np.float64) * g, starts)
+    psum = np.add.reduceat(p.astype(np.float64), starts)
+    assert np.max(np.abs(np.add.reduceat(ds, starts) - 0.7 * S * (1 - psum))) < 1e-12
+    assert np.max(np.abs(1 - psum)) < 1e-6
+    # a gradient constant over a row has no effect beyond that rounding:
+    # ds_e = scale * p_e * c_i * (1 - sum p)
+    crow = rng.standard_normal(csr.n_rows)
+    c = np.repeat(crow, csr.degrees()).astype(np.float32)
+    dc, _ = oracle_lib.softmax_backward(csr.row_ptr, p, c, 0.7)
+    psum_all = np.bincount(csr.row_of_edge(), weights=p.astype(np.float64), minlength=csr.n_rows)
+    left = np.repeat(1 - psum_all, csr.degrees())
+    assert np.max(np.abs(dc - 0.7 * p * c.astype(np.float64) * left)) < 1e-12
+    assert np.max(np.abs(dc)) < 1e-6
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_backward_finite_differences(oracle_lib, seed):
+    rng = np.random.default_rng(720 + seed)
+    csr = random_small_graph(8, 10, 0.45, rng, empty_frac=0.2, allow_dup=seed == 2)
+    F, scale = 3, [1.0, 0.125, 0.5][seed]
+    s = _grid_scores(rng, csr.nnz)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+
+    def loss(sv):
+        out = oracle_lib.attention(csr.row_ptr, csr.col_idx, sv, V, scale)[0]
+        return float(np.sum(dO.astype(np.float64) * out))
+
+    ds, mag = oracle_lib.attention_backward_scores(csr.row_ptr, csr.col_idx, s, V, dO, scale)
+    h = 2.0 ** -10
+    fd = np.empty(csr.nnz)
+    for e in range(csr.nnz):
+        sp, sm = s.copy(), s.copy()
+        sp[e] += np.float32(h)
+        sm[e] -= np.float32(h)
+        fd[e] = (loss(sp) - loss(sm)) / (2 * h)
+    assert rel_err(ds, fd, mag) < 1e-4
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_spmm_transpose_dense(oracle_lib, seed):
+    rng = np.random.default_rng(730 + seed)
+    csr = random_small_graph(25, 18, 0.2, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
+    vals = rng.standard_normal(csr.nnz)
+    dY = rng.standard_normal((csr.n_rows, 4)).astype(np.float32)
+    dX, mag = oracle_lib.spmm_transpose(csr.row_ptr, csr.col_idx, vals, dY, csr.n_cols)
+    want = dense_of(csr, vals).T @ dY.astype(np.float64)
+    assert rel_err(dX, want, mag) < 1e-12
+    ones, _ = oracle_lib.spmm_transpose(csr.row_ptr, csr.col_idx, None, dY, csr.n_cols)
+    assert np.allclose(ones, dense_of(csr, np.ones(csr.nnz)).T @ dY.astype(np.float64), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_transpose_definition(seed):
+    rng = np.random.default_rng(740 + seed)
+    csr = random_small_graph(30, 23, 0.15, rng, empty_frac=0.3, allow_dup=seed % 2 == 1)
+    t_rp, t_ci, perm = oracle.transpose(csr.row_ptr, csr.col_idx, csr.n_cols)
+    assert sorted(perm.tolist()) == list(range(csr.nnz))
+    At = CSR(csr.n_cols, csr.n_rows, t_rp, t_ci)
+    vals = rng.standard_normal(csr.nnz)
+    assert np.array_equal(dense_of(At, vals[perm]), dense_of(csr, vals).T)
+    # each column lists its rows in increasing order, ties in entry order
+    for j in range(csr.n_cols):
+        seg = perm[t_rp[j]:t_rp[j + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all(csr.col_idx[seg] == j)
+    # transposing twice gives back the pattern with each row's entries ordered
+    # by (column, original position): the original order when it was sorted
+    rp2, ci2, perm2 = oracle.transpose(t_rp, t_ci, csr.n_rows)
+    order = np.lexsort((np.arange(csr.nnz), csr.col_idx, csr.row_of_edge()))
+    assert np.array_equal(rp2, csr.row_ptr) and np.array_equal(ci2, csr.col_idx[order])
+    assert np.array_equal(perm[perm2], order)
