@@ -45,6 +45,10 @@ def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64):
         return 4 * (n_rows + 1) + nnz * 8 + nnz * width * 4 + n_rows * width * 4
     if op == "row_softmax":
         return 4 * (n_rows + 1) + nnz * 8
+    if op == "row_softmax_backward":
+        return 4 * (n_rows + 1) + nnz * 12
+    if op == "gather":
+        return nnz * 12
     if op == "mha":
         hd = heads * head_dim
         return 4 * (n_rows + 1) + nnz * 4 + n_rows * hd * 2 + 2 * nnz * hd * 2 + n_rows * hd * 4
@@ -119,6 +123,35 @@ def build_workload(name, torch, csa):
         else:
             calls.append(Call("attention_F64", "attention", csa.attention, (rp, ci, S, Vd),
                               {"out": Y, "scale": 0.125}, csr.n_rows, csr.nnz, 64, None))
+    elif name == "c3bwd":
+        # backward of the single-head fp32 attention on the c3 graph (scores
+        # given, F = 64): P = row softmax, dP = SDDMM(dOut, V), d scores =
+        # softmax backward (in place), P^T order by gather, dV = SpMM on A^T.
+        # The transposed pattern is built once, outside the step.
+        csr = configs.config_pattern("c3")
+        rp, ci = d(csr.row_ptr), d(csr.col_idx)
+        S = d(configs.config_dense("c3", "scores", csr) * 3.0)
+        Vd = d(configs.config_dense("c3", "X", csr, 64))
+        dO = d(configs.config_dense("c3", "V", csr, 64))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        At = csa.transpose(rp, ci, csr.n_cols)
+        torch.cuda.synchronize()
+        build_workload.transpose_ms = (time.perf_counter() - t0) * 1e3
+        P = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+        dP = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+        Pt = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+        dV = torch.empty((csr.n_cols, 64), dtype=torch.float32, device="cuda")
+        calls.append(Call("row_softmax", "row_softmax", csa.row_softmax, (rp, S), {"out": P, "scale": 0.125},
+                          csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("sddmm_dP", "sddmm", csa.sddmm, (rp, ci, dO, Vd), {"out": dP}, csr.n_rows, csr.nnz, 64,
+                          None))
+        calls.append(Call("softmax_bwd", "row_softmax_backward", csa.row_softmax_backward, (rp, P, dP),
+                          {"out": dP, "scale": 0.125}, csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("gather_Pt", "gather", lambda perm, src, out, schedule=None: csa.gather_values(
+            perm, src, out=out), (At.perm, P, Pt), {}, csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("spmm_dV", "spmm", csa.spmm, (At.row_ptr, At.col_idx, Pt, dO), {"out": dV}, csr.n_cols,
+                          csr.nnz, 64, None))
     elif name in ("c1", "p4"):
         c = configs.make_config(name)
         csr = c["csr"]
@@ -138,6 +171,27 @@ def build_workload(name, torch, csa):
     else:
         raise SystemExit(f"unknown config {name}")
     return calls, time.time() - t0
+
+
+def check_shapes(calls):
+    """Host-side check, before any launch, that every operand has the size its
+    call implies (per-entry arrays: nnz values; pattern arrays: rows + 1 and
+    nnz), so that no kernel is handed a buffer shorter than it reads."""
+    for c in calls:
+        a = c.args
+        if c.op == "gather":
+            assert all(t.numel() == c.nnz for t in a), (c.name, "gather operands")
+            continue
+        assert a[0].numel() == c.n_rows + 1, (c.name, "row_ptr")
+        if c.op in ("row_softmax", "row_softmax_backward"):
+            for t in a[1:]:
+                assert t.numel() == c.nnz, (c.name, "per-entry operand")
+            out = c.kwargs.get("out")
+            assert out is None or out.numel() == c.nnz, (c.name, "out")
+        else:
+            assert a[1].numel() == c.nnz, (c.name, "col_idx")
+            if c.op in ("spmm", "attention") and a[2] is not None:
+                assert a[2].numel() == c.nnz, (c.name, "per-entry values")
 
 
 def stream_bandwidth(torch, gib=4):
@@ -209,8 +263,10 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
 
     out = {}
     for c in calls:
+        if c.op == "gather":
+            continue
         scale = c.kwargs.get("scale", 1.0)
-        args = (c.args[0], None) + tuple(c.args[1:]) if c.op == "row_softmax" else c.args
+        args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
         p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale)
         counts, sums, mx = csa.degree_histogram(c.args[0])
         cands = csa.candidates(p, counts + sums + [mx])
@@ -308,7 +364,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2", help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused")
+    ap.add_argument("--config", default="c2",
+                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -336,6 +393,7 @@ def main():
         del src, dst
     stream_ref = stream_bandwidth(torch)
     calls, gen_s = build_workload(args.config, torch, csa)
+    check_shapes(calls)
     print(f"[bench] workload {args.config}: {len(calls)} calls, generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
 
     # selection (histogram, signature, cost model, probes) once per call
@@ -343,7 +401,9 @@ def main():
     for c in calls:
         torch.cuda.synchronize()
         t = time.perf_counter()
-        sel_args = (c.args[0], None) + tuple(c.args[1:]) if c.op == "row_softmax" else c.args
+        if c.op == "gather":  # no schedule
+            continue
+        sel_args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
         kw = {"scale": c.kwargs["scale"]} if "scale" in c.kwargs else {}
         s, sig = csa.select(c.op, *sel_args, **kw)
         torch.cuda.synchronize()
@@ -393,7 +453,7 @@ def main():
             "ms": round(ms, 4), "GB_s": round(c.bytes / (ms * 1e-3) / 1e9, 1),
             "GNNZF_s": round(c.nnz * c.width / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(c.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_alg": c.bytes, **sel[c.name]}
+            "bytes_alg": c.bytes, **sel.get(c.name, {})}
         if c.name in cold:
             mc = cold[c.name]
             kernels[c.name].update({"ms_cold": round(mc, 4), "GB_s_cold": round(c.bytes / (mc * 1e-3) / 1e9, 1),
@@ -423,7 +483,10 @@ def main():
                                 "c3pipe": "unfused single-head fp32 attention on the log-normal graph: "
                                           "SDDMM K=64 -> row softmax -> SpMM F=64",
                                 "c3fused": "single-head fp32 attention on the log-normal graph: "
-                                           "SDDMM K=64 -> fused softmax-SpMM F=64"}[args.config],
+                                           "SDDMM K=64 -> fused softmax-SpMM F=64",
+                                "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "
+                                         "row softmax, SDDMM dP, softmax backward, gather P^T, SpMM dV on A^T"
+                                }[args.config],
                    "name": args.config, "n_rows": calls[0].n_rows, "nnz": calls[0].nnz,
                    "widths": [c.width for c in calls], "parallelism": "1 GPU"},
         "gnnzf_per_s": round(gnnzf, 2),
@@ -433,6 +496,8 @@ def main():
                      "launch_ms": round(dom_ms, 4), "bytes_per_launch": dom.bytes},
         "kernels": kernels,
         "stream_measured": stream_ref,
+        **({"transpose_once_ms": round(build_workload.transpose_ms, 3)}
+           if getattr(build_workload, "transpose_ms", None) is not None else {}),
     }
     result["roofline"]["frac_of_measured_copy"] = round(achieved / stream_ref["copy_GB_s"], 4)
     if not args.no_study:

@@ -62,11 +62,13 @@ __global__ void k_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz
         else
             hi = mid;
     }
+    // clamped to the arrays' extents: a row_ptr whose last value is not nnz
+    // then gives wrong results instead of reads past the entry arrays
     coords[2 * c] = (int32_t)lo;
-    coords[2 * c + 1] = (int32_t)(d - lo);
+    coords[2 * c + 1] = (int32_t)min(d - lo, nnz);
     if (bounds) {
-        bounds[2 * c] = lo < n_rows ? row_ptr[lo] : (int32_t)nnz;
-        bounds[2 * c + 1] = lo < n_rows ? row_ptr[lo + 1] : (int32_t)nnz;
+        bounds[2 * c] = lo < n_rows ? (int32_t)min((int64_t)row_ptr[lo], nnz) : (int32_t)nnz;
+        bounds[2 * c + 1] = lo < n_rows ? (int32_t)min((int64_t)row_ptr[lo + 1], nnz) : (int32_t)nnz;
     }
 }
 

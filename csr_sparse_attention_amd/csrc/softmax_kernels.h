@@ -191,9 +191,11 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     // a later chunk if short
     const bool slotA = active && x0 < x1 && a_end - a_beg > D;
     const bool slotB = active && x1 < a.n_rows && b_end - b_beg > D && max(b_beg, y0) < y1;
-    const int lo = (active && x0 < x1 && !slotA) ? a_beg : y0;
-    const int hi = slotB ? y1 : max(b_beg, lo);
-    const int ne = active ? hi - lo : 0;
+    // (for a valid CSR lo > y0 - D and hi <= y1; the clamps keep an invalid
+    // row_ptr from reading past the arrays or the LDS)
+    const int lo = max((active && x0 < x1 && !slotA) ? a_beg : y0, max(0, y0 - D + 1));
+    const int hi = min(min(slotB ? y1 : max(b_beg, lo), y1), lo + 2 * D - 1);
+    const int ne = active ? max(0, hi - lo) : 0;
     const int nend = x1 - x0, nrow = nend + (slotB ? 1 : 0);
     int32_t* rp = sh.rp[wave];
     uint16_t* mark = reinterpret_cast<uint16_t*>(sh.l[wave]);
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     // mark the first staged entry of every non-empty row after row 0 with its index + 1
     for (int i = 1 + lane; i < nrow; i += CSR_WAVE) {
         const int b = rp[i];
-        if (b < rp[i + 1]) mark[b - lo] = (uint16_t)(i + 1);
+        if (b < rp[i + 1] && b >= lo && b < lo + ne) mark[b - lo] = (uint16_t)(i + 1);
     }
     __syncthreads();
     // rows of the run's entries and scores in log2 units
@@ -472,8 +474,8 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split_runs(SoftmaxArgs a)
         rb = a.carry_row[2 * c + 1];
         const int y0 = a.part[2 * c + 1], y1 = a.part[2 * c + 3];
         a0 = y0;
-        a1 = a.bounds[2 * c + 1];                // end of row x0
-        b0 = max(a.bounds[2 * c + 2], y0);       // start of row x1
+        a1 = min(a.bounds[2 * c + 1], y1);            // end of row x0
+        b0 = min(max(a.bounds[2 * c + 2], y0), y1);   // start of row x1
         b1 = y1;
     }
     float ma = 0.f, la = 1.f, mb = 0.f, lb = 1.f;

@@ -1,0 +1,36 @@
+"""Host-side checks of the benchmark's workload assembly (no GPU): every
+operand must have the size its call implies before anything is launched."""
+
+import importlib.util
+import os
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+_spec = importlib.util.spec_from_file_location("bench", os.path.join(os.path.dirname(__file__), "..", "bench.py"))
+bench = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(bench)
+
+
+def _call(op, args, n_rows, nnz, **kw):
+    return bench.Call("x", op, None, args, kw, n_rows, nnz, 1, None)
+
+
+def test_shapes_accepted():
+    rp, ci, v = torch.zeros(11, dtype=torch.int32), torch.zeros(40, dtype=torch.int32), torch.zeros(40)
+    bench.check_shapes([_call("row_softmax", (rp, v), 10, 40, out=torch.zeros(40)),
+                        _call("spmm", (rp, ci, v, torch.zeros(5, 3)), 10, 40),
+                        _call("gather", (ci, v, v), 10, 40)])
+
+
+def test_per_entry_array_of_the_wrong_length_is_caught():
+    # scores drawn per row instead of per entry
+    rp = torch.zeros(11, dtype=torch.int32)
+    with pytest.raises(AssertionError):
+        bench.check_shapes([_call("row_softmax", (rp, torch.zeros(10)), 10, 40)])
+    with pytest.raises(AssertionError):
+        bench.check_shapes([_call("row_softmax_backward", (rp, torch.zeros(40), torch.zeros(39)), 10, 40)])
+    with pytest.raises(AssertionError):
+        bench.check_shapes([_call("spmm", (rp, torch.zeros(40, dtype=torch.int32), torch.zeros(39),
+                                           torch.zeros(5, 3)), 10, 40)])
