@@ -316,6 +316,123 @@ def cold_times(calls, torch, reps=5, flush_gib=1):
     return out
 
 
+def vendor_compare(calls, torch, reps=5):
+    """The same SpMM and SDDMM calls timed with the vendor library (rocSPARSE's
+    generic API through ctypes; a measurement beside the library, never a
+    dispatch target): every CSR SpMM algorithm it offers for row-major dense
+    operands, the analysis / preprocess stage outside the timed region, median
+    of ``reps`` HIP-event timed compute calls.  Returns per call the vendor
+    times and the ratio vendor best / this library."""
+    import ctypes
+
+    try:
+        rs = ctypes.CDLL("librocsparse.so.1")
+    except OSError as e:  # pragma: no cover - library not installed
+        return {"error": str(e)}
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    OP_N, OP_T, I32, BASE0, F32, ROW = 111, 112, 2, 0, 151, 0
+    ALGS = {"default": 0, "csr_row_split": 4, "csr_nnz_split": 5, "csr_merge_path": 9}
+    h = P()
+    assert rs.rocsparse_create_handle(ctypes.byref(h)) == 0
+    stream = torch.cuda.current_stream()
+    rs.rocsparse_set_stream(h, P(stream.cuda_stream))
+    rs.rocsparse_create_csr_descr.argtypes = [ctypes.POINTER(P), I64, I64, I64, P, P, P, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int]
+    rs.rocsparse_create_dnmat_descr.argtypes = [ctypes.POINTER(P), I64, I64, I64, P, ctypes.c_int, ctypes.c_int]
+    rs.rocsparse_spmm.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.POINTER(ctypes.c_size_t), P]
+    for f in ("rocsparse_sddmm_buffer_size",):
+        getattr(rs, f).argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_size_t)]
+    for f in ("rocsparse_sddmm_preprocess", "rocsparse_sddmm"):
+        getattr(rs, f).argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P]
+    one, zero = ctypes.c_float(1.0), ctypes.c_float(0.0)
+
+    def timed(fn):
+        ts = []
+        fn()
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = fn()
+            b.record(stream)
+            b.synchronize()
+            if rc != 0:
+                return None, rc
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)), 0
+
+    out = {}
+    for c in calls:
+        if c.op not in ("spmm", "sddmm"):
+            continue
+        rp, ci = c.args[0], c.args[1]
+        n_rows, nnz = rp.numel() - 1, ci.numel()
+        res = {}
+        if c.op == "spmm":
+            vals, X = c.args[2], c.args[3]
+            Y = c.kwargs["out"]
+            v = vals if vals is not None else torch.ones(nnz, device=X.device)
+            A, B, C = P(), P(), P()
+            rs.rocsparse_create_csr_descr(ctypes.byref(A), n_rows, X.shape[0], nnz, P(rp.data_ptr()),
+                                          P(ci.data_ptr()), P(v.data_ptr()), I32, I32, BASE0, F32)
+            rs.rocsparse_create_dnmat_descr(ctypes.byref(B), X.shape[0], X.shape[1], X.stride(0), P(X.data_ptr()),
+                                            F32, ROW)
+            rs.rocsparse_create_dnmat_descr(ctypes.byref(C), n_rows, X.shape[1], Y.stride(0), P(Y.data_ptr()),
+                                            F32, ROW)
+            for name, alg in ALGS.items():
+                sz = ctypes.c_size_t(0)
+                rc = rs.rocsparse_spmm(h, OP_N, OP_N, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32, alg, 1,
+                                       ctypes.byref(sz), None)
+                if rc != 0:
+                    res[name] = f"status {rc}"
+                    continue
+                buf = torch.empty(max(1, sz.value), dtype=torch.uint8, device=X.device)
+                rc = rs.rocsparse_spmm(h, OP_N, OP_N, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32, alg, 2,
+                                       ctypes.byref(sz), P(buf.data_ptr()))
+                if rc != 0:
+                    res[name] = f"status {rc}"
+                    continue
+                ms, rc = timed(lambda: rs.rocsparse_spmm(h, OP_N, OP_N, ctypes.byref(one), A, B, ctypes.byref(zero),
+                                                         C, F32, alg, 3, ctypes.byref(sz), P(buf.data_ptr())))
+                res[name] = round(ms, 4) if ms is not None else f"status {rc}"
+                del buf
+            for d_ in (B, C):
+                rs.rocsparse_destroy_dnmat_descr(d_)
+            rs.rocsparse_destroy_spmat_descr(A)
+        else:
+            U, V = c.args[2], c.args[3]
+            o = c.kwargs["out"]
+            A, B, C = P(), P(), P()
+            rs.rocsparse_create_dnmat_descr(ctypes.byref(A), n_rows, U.shape[1], U.stride(0), P(U.data_ptr()), F32, ROW)
+            rs.rocsparse_create_dnmat_descr(ctypes.byref(B), V.shape[0], V.shape[1], V.stride(0), P(V.data_ptr()), F32,
+                                            ROW)
+            rs.rocsparse_create_csr_descr(ctypes.byref(C), n_rows, V.shape[0], nnz, P(rp.data_ptr()), P(ci.data_ptr()),
+                                          P(o.data_ptr()), I32, I32, BASE0, F32)
+            sz = ctypes.c_size_t(0)
+            rc = rs.rocsparse_sddmm_buffer_size(h, OP_N, OP_T, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32, 0,
+                                                ctypes.byref(sz))
+            if rc == 0:
+                buf = torch.empty(max(1, sz.value), dtype=torch.uint8, device=U.device)
+                rc = rs.rocsparse_sddmm_preprocess(h, OP_N, OP_T, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32,
+                                                   0, P(buf.data_ptr()))
+            if rc == 0:
+                ms, rc = timed(lambda: rs.rocsparse_sddmm(h, OP_N, OP_T, ctypes.byref(one), A, B, ctypes.byref(zero), C,
+                                                          F32, 0, P(buf.data_ptr())))
+                res["default"] = round(ms, 4) if ms is not None else f"status {rc}"
+            else:
+                res["default"] = f"status {rc}"
+            rs.rocsparse_destroy_dnmat_descr(A)
+            rs.rocsparse_destroy_dnmat_descr(B)
+            rs.rocsparse_destroy_spmat_descr(C)
+        best = min([t for t in res.values() if isinstance(t, float)], default=None)
+        mine = float(np.mean(c.times)) if c.times else None
+        out[c.name] = {"rocsparse_ms": res, "rocsparse_best_ms": best,
+                       "vendor_over_this": round(best / mine, 3) if best and mine else None}
+    rs.rocsparse_destroy_handle(h)
+    return out
+
+
 def cpu_baseline(calls, target_s=15.0):
     """Times the oracle (as it is) on a bounded sample of the step: the same
     contiguous block of leading rows for every call, sized so that the whole
@@ -370,6 +487,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of every call")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the SpMM / SDDMM calls with rocSPARSE (a measured comparison, not a dispatch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one device copy of 1 GiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -440,6 +559,7 @@ def main():
     wall = time.perf_counter() - t0
     for c in calls:
         per_call[c.name] = [a.elapsed_time(b) for a, b in cev[c.name]]
+        c.times = per_call[c.name]
     step_bytes = sum(c.bytes for c in calls)
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
@@ -504,6 +624,9 @@ def main():
         print("[bench] selector study: every candidate schedule of every call", file=sys.stderr, flush=True)
         result["selector"] = selector_study(calls, torch, csa)
         result["selector_worst_ratio"] = max(v["selected_over_best"] for v in result["selector"].values())
+    if args.vendor:
+        print("[bench] vendor comparison (rocSPARSE)", file=sys.stderr, flush=True)
+        result["vendor"] = vendor_compare(calls, torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(calls, args.cpu_seconds)
