@@ -81,22 +81,25 @@ def build_workload(name, torch, csa):
 
     calls = []
     t0 = time.time()
-    if name in ("c2", "c3", "c4"):
-        csr = configs.config_pattern(name)
+    if name in ("c2", "c3", "c4", "c3sweep"):
+        pat = "c3" if name == "c3sweep" else name
+        csr = configs.config_pattern(pat)
         rp, ci = d(csr.row_ptr), d(csr.col_idx)
-        vals = configs.config_dense(name, "vals", csr)
+        vals = configs.config_dense(pat, "vals", csr)
         vd = d(vals)
-        widths = {"c2": (32, 64, 128, 602), "c3": (100, 128), "c4": (4, 8, 16, 32)}[name]
+        # c3sweep: the c3 SpMM at growing widths, i.e. a growing gathered operand
+        widths = {"c2": (32, 64, 128, 602), "c3": (100, 128), "c4": (4, 8, 16, 32),
+                  "c3sweep": (128, 256, 384, 512)}[name]
         for F in widths:
-            X = configs.config_dense(name, "X", csr, F)
+            X = configs.config_dense(pat, "X", csr, F)
             Xd = d(X)
             Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device="cuda")
             calls.append(Call(f"spmm_F{F}", "spmm", csa.spmm, (rp, ci, vd, Xd), {"out": Y}, csr.n_rows, csr.nnz, F,
                               ("spmm", csr, vals, X)))
-        sd_widths = {"c2": (), "c3": (128,), "c4": (4, 8, 16, 32)}[name]
+        sd_widths = {"c2": (), "c3": (128,), "c4": (4, 8, 16, 32), "c3sweep": ()}[name]
         for K in sd_widths:
-            U = configs.config_dense(name, "U", csr, K)
-            V = configs.config_dense(name, "V", csr, K)
+            U = configs.config_dense(pat, "U", csr, K)
+            V = configs.config_dense(pat, "V", csr, K)
             out = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
             calls.append(Call(f"sddmm_K{K}", "sddmm", csa.sddmm, (rp, ci, d(U), d(V)), {"out": out}, csr.n_rows,
                               csr.nnz, K, ("sddmm", csr, U, V)))
@@ -482,7 +485,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2",
-                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3bwd")
+                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3bwd, c3sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -604,6 +607,8 @@ def main():
                                           "SDDMM K=64 -> row softmax -> SpMM F=64",
                                 "c3fused": "single-head fp32 attention on the log-normal graph: "
                                            "SDDMM K=64 -> fused softmax-SpMM F=64",
+                                "c3sweep": "CSR SpMM on the log-normal graph at F in {128,256,384,512}: "
+                                           "gathered operand of 1.25 to 5.0 GB",
                                 "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "
                                          "row softmax, SDDMM dP, softmax backward, gather P^T, SpMM dV on A^T"
                                 }[args.config],
