@@ -673,3 +673,43 @@ def test_attention_backward(graph, scale):
     P = oracle.attention(csr.row_ptr, csr.col_idx, sc, zero, scale, want_probs=True)[2]
     ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P, dO, csr.n_cols)
     assert_close(dV.cpu().numpy(), ref, mag, TOL_F32, "dV")
+
+
+def test_backward_edge_cases():
+    # no entries at all: nothing to write, shapes still right
+    rp = dev(np.zeros(6, np.int32))
+    ci = dev(np.zeros(0, np.int32))
+    empty = dev(np.zeros(0, np.float32))
+    assert csa.row_softmax_backward(rp, empty, empty).numel() == 0
+    t = csa.transpose(rp, ci, 0)
+    assert t.row_ptr.cpu().numpy().tolist() == [0] and t.col_idx.numel() == 0
+    assert csa.gather_values(t.perm, empty).numel() == 0
+    # a single entry per row: the softmax is 1, its gradient 0
+    csr = CSR(4, 3, np.arange(5, dtype=np.int32), np.array([2, 0, 1, 2], np.int32))
+    rp, ci = pattern_dev(csr)
+    p = dev(np.ones(4, np.float32))
+    g = dev(np.array([3.0, -1.0, 0.5, 7.0], np.float32))
+    assert np.array_equal(csa.row_softmax_backward(rp, p, g, scale=0.5).cpu().numpy(), np.zeros(4, np.float32))
+    # the gradient of an identity-pattern attention with respect to V is dOut itself (bit-exact: p = 1)
+    n = 300
+    csr = CSR(n, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32))
+    rp, ci = pattern_dev(csr)
+    rng = np.random.default_rng(640)
+    dO = rng.standard_normal((n, 8)).astype(np.float32)
+    dS, dV = csa.attention_backward(rp, ci, dev(rng.standard_normal(n).astype(np.float32)),
+                                    dev(rng.standard_normal((n, 8)).astype(np.float32)), dev(dO))
+    assert np.array_equal(dV.cpu().numpy(), dO)
+    assert np.array_equal(dS.cpu().numpy(), np.zeros(n, np.float32))
+
+
+def test_backward_deterministic():
+    csr = skew_graph(9, n_rows=1500, n_cols=8000, giant=6000)
+    rng = np.random.default_rng(650)
+    sc = dev(rng.standard_normal(csr.nnz).astype(np.float32))
+    V = dev(rng.standard_normal((csr.n_cols, 12)).astype(np.float32))
+    dO = dev(rng.standard_normal((csr.n_rows, 12)).astype(np.float32))
+    rp, ci = pattern_dev(csr)
+    a = [x.cpu().numpy() for x in csa.attention_backward(rp, ci, sc, V, dO, scale=0.3)]
+    b = [x.cpu().numpy() for x in csa.attention_backward(rp, ci, sc, V, dO, scale=0.3)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
