@@ -16,22 +16,35 @@ __global__ void k_iota(int32_t* v, int64_t n)
         v[i] = (int32_t)i;
 }
 
-// t_col_idx[k] = the row holding original entry perm[k]: the last row i with
-// row_ptr[i] <= perm[k]
-__global__ void k_rows_of(const int32_t* row_ptr, int64_t n_rows, const int32_t* perm, int32_t* rows, int64_t nnz)
+// last row i in [lo, hi] with row_ptr[i] <= e
+__device__ __forceinline__ int64_t row_search(const int32_t* row_ptr, int64_t lo, int64_t hi, int64_t e)
 {
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t e = perm[k];
-        int64_t lo = 0, hi = n_rows - 1;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) >> 1;
-            if (row_ptr[mid] <= e)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        rows[k] = (int32_t)lo;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (row_ptr[mid] <= e)
+            lo = mid;
+        else
+            hi = mid - 1;
     }
+    return lo;
+}
+
+// rows[e] = the row holding entry e (the COO row array).  A block covers 256
+// consecutive entries: two full searches find the rows of its first and last
+// entry, and every entry is then searched only between those two rows (one
+// or two steps for rows of tens of entries).
+__global__ __launch_bounds__(CSR_BLOCK) void k_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows,
+                                                        int64_t nnz)
+{
+    __shared__ int64_t span[2];
+    const int64_t e0 = (int64_t)blockIdx.x * CSR_BLOCK;
+    if (threadIdx.x < 2) {
+        const int64_t e = threadIdx.x == 0 ? e0 : min(e0 + CSR_BLOCK, nnz) - 1;
+        span[threadIdx.x] = row_search(row_ptr, 0, n_rows - 1, e);
+    }
+    __syncthreads();
+    const int64_t e = e0 + threadIdx.x;
+    if (e < nnz) rows[e] = (int32_t)row_search(row_ptr, span[0], span[1], e);
 }
 
 // t_row_ptr[c] = number of sorted column keys below c, for c in [0, n_cols]
@@ -48,6 +61,12 @@ __global__ void k_col_starts(const int32_t* keys, int64_t nnz, int32_t* t_row_pt
         }
         t_row_ptr[c] = (int32_t)lo;
     }
+}
+
+__global__ void k_gather_rows(const int32_t* perm, const int32_t* src, int32_t* dst, int64_t n)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
+        dst[k] = src[perm[k]];
 }
 
 __global__ void k_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n)
@@ -102,8 +121,15 @@ hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int6
     e = rocprim::radix_sort_pairs(temp, temp_bytes, col_idx, keys, (const int32_t*)iota, t_perm, (unsigned)nnz, 0,
                                   key_bits(n_cols), s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_rows_of, dim3(grid_of(nnz)), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, (const int32_t*)t_perm,
-                       t_col_idx, nnz);
+    // the sort no longer needs the entry indices: their buffer takes the COO
+    // rows, and each transposed entry's row is gathered through the permutation
+    int32_t* rows = iota;
+    const int64_t blocks = (nnz + CSR_BLOCK - 1) / CSR_BLOCK;
+    hipLaunchKernelGGL(k_coo_rows, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gather_rows, dim3(grid_of(nnz)), dim3(CSR_BLOCK), 0, s, (const int32_t*)t_perm,
+                       (const int32_t*)rows, t_col_idx, nnz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_col_starts, dim3(grid_of(n_cols + 1)), dim3(CSR_BLOCK), 0, s, (const int32_t*)keys, nnz,
