@@ -65,9 +65,72 @@ class Call:
         self.oracle_fn = oracle_fn
         self.schedule = None
         self.times = []
+        self.fmt = None  # column-part segment format of the call, when its rule proposes one
 
-    def run(self):
-        return self.fn(*self.args, schedule=self.schedule, **self.kwargs)
+    def run(self, schedule=None):
+        s = schedule if schedule is not None else self.schedule
+        if self.fmt is not None:
+            return self.fmt["run"](s)
+        return self.fn(*self.args, schedule=s, **self.kwargs)
+
+    def select(self, csa, mode="auto"):
+        if self.fmt is not None:
+            return self.fmt["select"](mode)
+        sel_args = (self.args[0], None) + tuple(self.args[1:]) if self.op.startswith("row_softmax") else self.args
+        kw = {"scale": self.kwargs["scale"]} if "scale" in self.kwargs else {}
+        return csa.select(self.op, *sel_args, mode=mode, **kw)
+
+
+def format_plan(csa, torch, c, P, cache):
+    """Builds (once per pattern and part count) the column-part segment format
+    of call c and the closures that run and select over it; SpMM edge values
+    are moved into the format's order once, here (they are constant across
+    steps).  Returns the plan dict with the one-time costs in ms."""
+    rp, ci = c.args[0], c.args[1]
+    dense = c.args[3] if c.op == "spmm" else c.args[3]
+    key = (rp.data_ptr(), ci.data_ptr(), P)
+    if key not in cache:
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        h = csa.hybrid_format(rp, ci, dense.shape[0], P)
+        torch.cuda.synchronize()
+        cache[key] = (h, (time.perf_counter() - t) * 1e3)
+    h, build_ms = cache[key]
+    out = c.kwargs.get("out")
+    values_ms = 0.0
+    if c.op == "spmm":
+        vals, X = c.args[2], c.args[3]
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        hv = None if vals is None else csa.hybrid_values(h, vals)
+        torch.cuda.synchronize()
+        values_ms = (time.perf_counter() - t) * 1e3
+        run = lambda s: csa.hybrid_spmm(h, hv, X, out=out, schedule=s)  # noqa: E731
+        select = lambda mode: csa.hybrid_select(h, "spmm", hv, X, mode=mode)  # noqa: E731
+        a, b = hv, X
+    else:
+        U, V = c.args[2], c.args[3]
+        run = lambda s: csa.hybrid_sddmm(h, U, V, out=out, schedule=s)  # noqa: E731
+        select = lambda mode: csa.hybrid_select(h, "sddmm", U, V, mode=mode, out=out)  # noqa: E731
+        a, b = U, V
+    return {"h": h, "parts": P, "run": run, "select": select, "operands": (a, b), "build_ms": build_ms,
+            "values_ms": values_ms}
+
+
+def apply_formats(calls, csa, torch):
+    """Per SpMM / SDDMM call, asks the library's rule for the column parts of
+    the column-part segment format (csr_hybrid_parts: 1 = plain CSR) and plans
+    the call over the format when it proposes one."""
+    cache = {}
+    for c in calls:
+        if c.op not in ("spmm", "sddmm"):
+            continue
+        p, _ = csa.make_problem(c.op, *c.args, out=c.kwargs.get("out"))
+        counts, sums, mx = csa.degree_histogram(c.args[0])
+        P = csa.hybrid_parts(p, counts + sums + [mx])
+        if P > 1:
+            c.fmt = format_plan(csa, torch, c, P, cache)
+    return cache
 
 
 def build_workload(name, torch, csa):
@@ -247,19 +310,22 @@ def committed_traffic(config, call, schedule):
     return None
 
 
-def selector_study(calls, torch, csa, rounds=5, per_round=3):
-    """Times every candidate schedule of each call (the fixed mappings of the
-    selector's search space) and the selected one under one protocol: the
-    distinct schedules are run in interleaved rounds (so clock and thermal
-    drift bias none of them), `per_round` HIP-event timed runs each, and the
-    median over all rounds is kept.  The selected schedule is one of the
-    candidates, so its time is that candidate's time."""
+def selector_study(calls, torch, csa, formats, rounds=5, per_round=3):
+    """Times every candidate of each call under one protocol and compares the
+    selected one with the best: the candidate schedules of the plain CSR
+    problem, for a call planned over the column-part segment format also the
+    candidate schedules of its segment problem, and for SpMM / SDDMM the
+    format at other part counts (half and twice the rule's choice, or 4 and
+    16 parts when the rule chose the plain path), each with its own selected
+    schedule.  The distinct candidates run in interleaved rounds (so clock and
+    thermal drift bias none of them), `per_round` HIP-event timed runs each,
+    and the median over all rounds is kept."""
     stream = torch.cuda.current_stream()
 
-    def timed(call, sched):
+    def timed(run):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        call.fn(*call.args, schedule=sched, **call.kwargs)
+        run()
         b.record(stream)
         b.synchronize()
         return a.elapsed_time(b)
@@ -272,26 +338,42 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
         args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
         p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale)
         counts, sums, mx = csa.degree_histogram(c.args[0])
-        cands = csa.candidates(p, counts + sums + [mx])
-        keys = [bytes(s) for s in cands]
-        if bytes(c.schedule) not in keys:
-            cands.append(c.schedule)
-            keys.append(bytes(c.schedule))
+        cands = [({"format_parts": 1, **s.as_dict()}, lambda s=s: c.fn(*c.args, schedule=s, **c.kwargs))
+                 for s in csa.candidates(p, counts + sums + [mx])]
+        if c.fmt is not None:
+            h = c.fmt["h"]
+            hp = csa.hybrid_problem(h, c.op, *c.fmt["operands"])
+            sc, ss, smx = csa.degree_histogram(h.seg_ptr)
+            cands += [({"format_parts": c.fmt["parts"], **s.as_dict()}, lambda s=s: c.fmt["run"](s))
+                      for s in csa.candidates(hp, sc + ss + [smx])]
+        selected = {"format_parts": c.fmt["parts"] if c.fmt is not None else 1, **c.schedule.as_dict()}
+        n_cand = len(cands)
+        if selected not in [lab for lab, _ in cands]:
+            cands.append((selected, lambda: c.run()))
+        if c.op in ("spmm", "sddmm"):
+            P0 = c.fmt["parts"] if c.fmt is not None else 1
+            for P in ([P0 // 2, P0 * 2] if P0 > 1 else [4, 16]):
+                if 2 <= P <= 32:
+                    plan = format_plan(csa, torch, c, P, formats)
+                    s_alt, _ = plan["select"]("auto")
+                    cands.append(({"format_parts": P, **s_alt.as_dict()}, lambda plan=plan, s=s_alt: plan["run"](s)))
+                    n_cand += 1
+        labels = [lab for lab, _ in cands]
         times = [[] for _ in cands]
-        for s in cands:
-            timed(c, s)
+        for _, run in cands:
+            timed(run)
         for _ in range(rounds):
-            for i, s in enumerate(cands):
+            for i, (_, run) in enumerate(cands):
                 for _ in range(per_round):
-                    times[i].append(timed(c, s))
+                    times[i].append(timed(run))
         med = [float(np.median(t)) for t in times]
-        n_cand = len(keys) if bytes(c.schedule) in keys[:-1] or len(cands) == len(keys) else len(keys) - 1
-        sel = med[keys.index(bytes(c.schedule))]
+        sel = med[labels.index(selected)]
         best = int(np.argmin(med))
         out[c.name] = {"selected_ms": round(sel, 4), "best_fixed_ms": round(med[best], 4),
-                       "best_fixed": cands[best].as_dict(), "n_candidates": n_cand,
+                       "selected": selected, "best_fixed": labels[best], "n_candidates": n_cand,
                        "selected_over_best": round(sel / med[best], 4),
-                       "candidate_ms": [round(t, 4) for t in med]}
+                       "candidate_ms": [round(t, 4) for t in med],
+                       "candidate_format_parts": [lab["format_parts"] for lab in labels]}
     return out
 
 
@@ -490,6 +572,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of every call")
+    ap.add_argument("--no-format", action="store_true",
+                    help="run every call on the plain CSR pattern (no column-part segment format)")
     ap.add_argument("--vendor", action="store_true",
                     help="also time the SpMM / SDDMM calls with rocSPARSE (a measured comparison, not a dispatch)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -517,6 +601,11 @@ def main():
     calls, gen_s = build_workload(args.config, torch, csa)
     check_shapes(calls)
     print(f"[bench] workload {args.config}: {len(calls)} calls, generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    formats = {} if args.no_format else apply_formats(calls, csa, torch)
+    for c in calls:
+        if c.fmt is not None:
+            print(f"[bench] {c.name}: column-part segment format, {c.fmt['parts']} parts, {c.fmt['h'].n_seg} "
+                  f"segments (built in {c.fmt['build_ms']:.1f} ms)", file=sys.stderr, flush=True)
 
     # selection (histogram, signature, cost model, probes) once per call
     sel = {}
@@ -525,19 +614,21 @@ def main():
         t = time.perf_counter()
         if c.op == "gather":  # no schedule
             continue
-        sel_args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
-        kw = {"scale": c.kwargs["scale"]} if "scale" in c.kwargs else {}
-        s, sig = csa.select(c.op, *sel_args, **kw)
+        s, sig = c.select(csa)
         torch.cuda.synchronize()
         first = time.perf_counter() - t
         t = time.perf_counter()
-        s2, sig2 = csa.select(c.op, *sel_args, mode="replay", **kw)
+        s2, sig2 = c.select(csa, mode="replay")
         torch.cuda.synchronize()
         replay = time.perf_counter() - t
         assert bytes(s) == bytes(s2) and sig == sig2
         c.schedule = s
         sel[c.name] = {"schedule": s.as_dict(), "signature": f"{sig:016x}", "select_ms": round(first * 1e3, 3),
                        "replay_select_ms": round(replay * 1e3, 3)}
+        if c.fmt is not None:
+            sel[c.name]["format"] = {"parts": c.fmt["parts"], "segments": c.fmt["h"].n_seg,
+                                     "build_ms": round(c.fmt["build_ms"], 3),
+                                     "values_to_format_order_ms": round(c.fmt["values_ms"], 3)}
         print(f"[bench] {c.name}: {s} select {first * 1e3:.1f} ms", file=sys.stderr, flush=True)
 
     dom = max(calls, key=lambda c: c.bytes)
@@ -627,7 +718,7 @@ def main():
     result["roofline"]["frac_of_measured_copy"] = round(achieved / stream_ref["copy_GB_s"], 4)
     if not args.no_study:
         print("[bench] selector study: every candidate schedule of every call", file=sys.stderr, flush=True)
-        result["selector"] = selector_study(calls, torch, csa)
+        result["selector"] = selector_study(calls, torch, csa, formats)
         result["selector_worst_ratio"] = max(v["selected_over_best"] for v in result["selector"].values())
     if args.vendor:
         print("[bench] vendor comparison (rocSPARSE)", file=sys.stderr, flush=True)

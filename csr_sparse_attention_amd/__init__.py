@@ -15,6 +15,7 @@ import torch  # noqa: F401
 from ._ffi import (  # noqa: F401,E402
     OP_SOFTMAX_BWD,
     CsrError,
+    CsrHybrid,
     CsrProblem,
     CsrSchedule,
     EXPORTS,
@@ -31,6 +32,7 @@ load_library()
 
 from .ops import (  # noqa: E402,F401
     Context,
+    Hybrid,
     Transposed,
     attention,
     attention_backward,
@@ -40,6 +42,13 @@ from .ops import (  # noqa: E402,F401
     default_schedule,
     degree_histogram,
     gather_values,
+    hybrid_format,
+    hybrid_parts,
+    hybrid_problem,
+    hybrid_sddmm,
+    hybrid_select,
+    hybrid_spmm,
+    hybrid_values,
     make_problem,
     merge_path_partition,
     mha_attention,

@@ -34,6 +34,8 @@ EXPORTS = (
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
+    "csr_hybrid_parts", "csr_hybrid_capacity", "csr_hybrid_build_workspace_size", "csr_hybrid_build", "csr_hybrid_workspace_size",
+    "csr_hybrid_spmm", "csr_hybrid_sddmm", "csr_hybrid_select",
 )
 
 
@@ -98,6 +100,28 @@ class CsrProblem(ctypes.Structure):
 assert ctypes.sizeof(CsrSchedule) == 64
 
 
+class CsrHybrid(ctypes.Structure):
+    """csr_hybrid_t: a column-part segment format (device arrays owned by the caller)."""
+    _fields_ = [
+        ("n_rows", ctypes.c_int64),
+        ("n_cols", ctypes.c_int64),
+        ("nnz", ctypes.c_int64),
+        ("parts", ctypes.c_int32),
+        ("part_cols", ctypes.c_int32),
+        ("seg_cap", ctypes.c_int64),
+        ("n_seg", ctypes.c_int64),
+        ("perm", ctypes.c_void_p),
+        ("col_idx", ctypes.c_void_p),
+        ("seg_ptr", ctypes.c_void_p),
+        ("seg_row", ctypes.c_void_p),
+        ("row_seg_ptr", ctypes.c_void_p),
+        ("row_seg", ctypes.c_void_p),
+    ]
+
+
+assert ctypes.sizeof(CsrHybrid) == 96
+
+
 class CsrError(RuntimeError):
     def __init__(self, code: int, where: str, message: str = ""):
         self.code = code
@@ -120,7 +144,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, U32, F, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
                                ctypes.c_float, ctypes.c_size_t)
-    SP, PP = ctypes.POINTER(CsrSchedule), ctypes.POINTER(CsrProblem)
+    SP, PP, HP = ctypes.POINTER(CsrSchedule), ctypes.POINTER(CsrProblem), ctypes.POINTER(CsrHybrid)
     sig = {
         "csr_context_create": [ctypes.POINTER(P), ctypes.c_int, ctypes.c_char_p, U32],
         "csr_context_destroy": [P],
@@ -146,6 +170,14 @@ def load() -> ctypes.CDLL:
         "csr_degree_histogram": [P, I64, P, ctypes.POINTER(I64), P, SZ, P],
         "csr_merge_path_partition": [P, I64, I64, P, I32, P, P],
         "csr_signature": [P, PP, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_uint64)],
+        "csr_hybrid_parts": [P, PP, ctypes.POINTER(I64), ctypes.POINTER(I32)],
+        "csr_hybrid_capacity": [I64, I64, I32, ctypes.POINTER(I64)],
+        "csr_hybrid_build_workspace_size": [P, I64, I64, I32, ctypes.POINTER(SZ)],
+        "csr_hybrid_build": [P, P, P, HP, P, SZ, P],
+        "csr_hybrid_workspace_size": [P, HP, I32, I64, SP, ctypes.POINTER(SZ)],
+        "csr_hybrid_spmm": [P, HP, P, P, I64, I64, P, I64, SP, P, SZ, P],
+        "csr_hybrid_sddmm": [P, HP, P, I64, P, I64, I64, P, SP, P, SZ, P],
+        "csr_hybrid_select": [P, HP, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
     }
     for name, argtypes in sig.items():
         fn = getattr(lib, name)

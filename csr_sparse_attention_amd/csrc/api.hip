@@ -141,7 +141,14 @@ int env_int(const char* name, int dflt)
 // Execution of one schedule
 // ---------------------------------------------------------------------------
 
-int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st)
+// Index maps of an SDDMM over the column-part segment format (see csrk::Fp32Args)
+struct RowMaps {
+    const int32_t* u_row;
+    const int32_t* out_idx;
+};
+
+int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st,
+                 const RowMaps* maps = nullptr)
 {
     char* ws = static_cast<char*>(p.workspace);
     if (ctx->flags & CSR_CTX_VALIDATE) {
@@ -221,6 +228,10 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
     a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
     if (p.op == CSR_OP_SDDMM) {
+        if (maps) {
+            a.u_row = maps->u_row;
+            a.out_idx = maps->out_idx;
+        }
         a.U = static_cast<const float*>(p.a);
         a.ldu = p.ld_a;
         a.X = static_cast<const float*>(p.b);
@@ -274,14 +285,15 @@ int histogram(csr_context_t ctx, const csr_problem_t& p, hipStream_t st, int64_t
 }
 
 // One timed run of schedule s on p (milliseconds), or a negative value if it failed.
-double timed_run(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st)
+double timed_run(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st,
+                 const RowMaps* maps)
 {
     if (env_flag("CSRSA_FAIL_PROBE")) return -1.0;
     if (!ctx->ev0) {
         if (hipEventCreate(&ctx->ev0) != hipSuccess || hipEventCreate(&ctx->ev1) != hipSuccess) return -1.0;
     }
     if (hipEventRecord(ctx->ev0, st) != hipSuccess) return -1.0;
-    if (run_schedule(ctx, p, s, st) != CSR_OK) return -1.0;
+    if (run_schedule(ctx, p, s, st, maps) != CSR_OK) return -1.0;
     if (hipEventRecord(ctx->ev1, st) != hipSuccess) return -1.0;
     if (hipEventSynchronize(ctx->ev1) != hipSuccess) return -1.0;
     float ms = 0.f;
@@ -295,14 +307,14 @@ double timed_run(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
 // in interleaved rounds so that slow drifts (clocks, temperature) bias none
 // of them; the number of runs per round adapts to the kernel's duration.
 std::vector<double> probe_all(csr_context_t ctx, const csr_problem_t& p, const std::vector<csr_schedule_t>& cand,
-                              const std::vector<size_t>& which, hipStream_t st)
+                              const std::vector<size_t>& which, hipStream_t st, const RowMaps* maps)
 {
     std::vector<double> med(cand.size(), -1.0);
     std::vector<std::vector<double>> t(cand.size());
     std::vector<bool> failed(cand.size(), false);
     double warm = 0.0, last = -1.0;
     for (int k = 0; k < 20 && warm < 20.0; ++k) {
-        last = timed_run(ctx, p, cand[which[0]], st);
+        last = timed_run(ctx, p, cand[which[0]], st, maps);
         if (last < 0) break;
         warm += last;
     }
@@ -311,13 +323,13 @@ std::vector<double> probe_all(csr_context_t ctx, const csr_problem_t& p, const s
                           : (last > 0 ? std::max(1, std::min(3, (int)(10.0 / last))) : 1);
     const int rounds = env_int("CSRSA_PROBE_REPS", 0) > 0 ? reps : 3;
     for (size_t i : which) {  // one untimed run each (code loading, caches)
-        if (timed_run(ctx, p, cand[i], st) < 0) failed[i] = true;
+        if (timed_run(ctx, p, cand[i], st, maps) < 0) failed[i] = true;
     }
     for (int r = 0; r < rounds; ++r) {
         for (size_t i : which) {
             if (failed[i]) continue;
             for (int k = 0; k < per_round; ++k) {
-                const double ms = timed_run(ctx, p, cand[i], st);
+                const double ms = timed_run(ctx, p, cand[i], st, maps);
                 if (ms < 0) {
                     failed[i] = true;
                     break;
@@ -334,7 +346,8 @@ std::vector<double> probe_all(csr_context_t ctx, const csr_problem_t& p, const s
     return med;
 }
 
-int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_schedule_t* out, uint64_t* sig_out)
+int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_schedule_t* out, uint64_t* sig_out,
+                  const RowMaps* maps = nullptr)
 {
     std::string why;
     const bool need_ptrs = (mode == CSR_SELECT_AUTO || mode == CSR_SELECT_FORCE_PROBE);
@@ -380,7 +393,7 @@ int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_
     std::vector<size_t> probe_set;
     for (size_t k = 0; k < order.size() && (int)probe_set.size() < max_probe; ++k) probe_set.push_back(order[k].second);
     std::sort(probe_set.begin(), probe_set.end());  // fixed candidate order for tie-breaking
-    const std::vector<double> med = probe_all(ctx, p, cand, probe_set, st);
+    const std::vector<double> med = probe_all(ctx, p, cand, probe_set, st, maps);
     double best = -1.0;
     size_t best_i = 0;
     for (size_t i : probe_set) {
@@ -732,6 +745,286 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
     return CSR_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Column-part segment format
+// ---------------------------------------------------------------------------
+
+static bool valid_parts(int32_t parts)
+{
+    return parts == 1 || parts == 2 || parts == 4 || parts == 8 || parts == 16 || parts == 32;
+}
+
+int csr_hybrid_capacity(int64_t n_rows, int64_t nnz, int32_t parts, int64_t* seg_cap)
+{
+    if (!seg_cap) return CSR_ERR_NULL;
+    const int64_t lim = (int64_t)1 << 31;
+    if (n_rows < 0 || nnz < 0 || n_rows >= lim - 1 || nnz >= lim || !valid_parts(parts)) return CSR_ERR_SHAPE;
+    *seg_cap = std::min(nnz, n_rows * (int64_t)parts);
+    return CSR_OK;
+}
+
+int csr_hybrid_build_workspace_size(csr_context_t ctx, int64_t n_rows, int64_t nnz, int32_t parts, size_t* bytes)
+{
+    if (!ctx || !bytes) return CSR_ERR_NULL;
+    int64_t cap = 0;
+    if (csr_hybrid_capacity(n_rows, nnz, parts, &cap) != CSR_OK) return set_err(ctx, CSR_ERR_SHAPE, "bad sizes or parts");
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    hipError_t e = csrk::hybrid_build_workspace(n_rows, nnz, parts, bytes);
+    if (e != hipSuccess) return hip_err(ctx, e, "hybrid build workspace");
+    return CSR_OK;
+}
+
+// Checks a format description: sizes, parts, capacity and arrays, and for a
+// built format the segment count and part width it records.
+static int check_hybrid(csr_context_t ctx, const csr_hybrid_t* h, bool built)
+{
+    if (!h) return CSR_ERR_NULL;
+    int rc = transpose_args(h->n_rows, h->n_cols, h->nnz);
+    if (rc != CSR_OK) return set_err(ctx, rc, "bad format sizes");
+    if (!valid_parts(h->parts)) return set_err(ctx, CSR_ERR_SHAPE, "parts must be 1, 2, 4, 8, 16 or 32");
+    int64_t cap = 0;
+    (void)csr_hybrid_capacity(h->n_rows, h->nnz, h->parts, &cap);
+    if (h->seg_cap < cap) return set_err(ctx, CSR_ERR_WORKSPACE, "segment capacity below min(nnz, n_rows * parts)");
+    if (!h->seg_ptr || !h->row_seg_ptr) return set_err(ctx, CSR_ERR_NULL, "seg_ptr / row_seg_ptr is NULL");
+    if (h->nnz > 0 && (!h->perm || !h->col_idx || !h->seg_row || !h->row_seg))
+        return set_err(ctx, CSR_ERR_NULL, "a format array is NULL");
+    if (built) {
+        const int64_t pc = h->n_cols > 0 ? (h->n_cols + h->parts - 1) / h->parts : 1;
+        if (h->part_cols != pc || h->n_seg < 0 || h->n_seg > cap || (h->nnz > 0) != (h->n_seg > 0))
+            return set_err(ctx, CSR_ERR_SHAPE, "the format is not built (part_cols / n_seg)");
+    }
+    return CSR_OK;
+}
+
+int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* col_idx, csr_hybrid_t* h,
+                     void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx || !row_ptr || !h) return CSR_ERR_NULL;
+    int rc = check_hybrid(ctx, h, false);
+    if (rc != CSR_OK) return rc;
+    if (!workspace || (h->nnz > 0 && !col_idx)) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        DeviceGuard g(ctx->device);
+        size_t need = 0;
+        CSR_HIP(ctx, csrk::hybrid_build_workspace(h->n_rows, h->nnz, h->parts, &need));
+        if (ws_bytes < need || (uintptr_t)workspace % csrh::kAlign)
+            return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small (or not 256-byte aligned) for the build");
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        const int32_t part_cols = h->n_cols > 0 ? (int32_t)((h->n_cols + h->parts - 1) / h->parts) : 1;
+        if ((ctx->flags & CSR_CTX_VALIDATE) && h->nnz > 0) {
+            int64_t* bad = reinterpret_cast<int64_t*>(workspace);
+            CSR_HIP(ctx, csrk::launch_validate(row_ptr, col_idx, h->n_rows, h->n_cols, h->nnz, bad, st));
+            CSR_HIP(ctx, hipMemcpyAsync(ctx->pinned, bad, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+            CSR_HIP(ctx, hipStreamSynchronize(st));
+            if (ctx->pinned[0] != 0) return set_err(ctx, CSR_ERR_INVALID_CSR, "row_ptr / col_idx fail CSR validation");
+        }
+        int64_t n_seg = 0;
+        if (h->nnz > 0) {
+            int32_t* count = reinterpret_cast<int32_t*>(ctx->pinned);
+            CSR_HIP(ctx, csrk::launch_hybrid_build_sort(row_ptr, col_idx, h->n_rows, h->nnz, h->parts, part_cols,
+                                                        h->perm, h->col_idx, workspace, ws_bytes, count, st));
+            CSR_HIP(ctx, hipStreamSynchronize(st));
+            n_seg = count[0];
+            if (n_seg < 1 || n_seg > h->seg_cap) return set_err(ctx, CSR_ERR_INTERNAL, "segment count out of range");
+        }
+        CSR_HIP(ctx, csrk::launch_hybrid_build_segments(h->n_rows, h->nnz, h->parts, n_seg, h->seg_ptr, h->seg_row,
+                                                        h->row_seg_ptr, h->row_seg, workspace, st));
+        h->n_seg = n_seg;
+        h->part_cols = part_cols;
+        return CSR_OK;
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+// The product over the format as a plain problem on the segment pattern
+static csr_problem_t hybrid_problem(const csr_hybrid_t* h, int32_t op, int64_t width)
+{
+    csr_problem_t p = blank_problem();
+    p.op = op;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = h->n_seg;
+    p.n_cols = h->n_cols;
+    p.nnz = h->nnz;
+    p.width = width;
+    p.ld_a = p.ld_b = p.ld_out = width;
+    p.row_ptr = h->seg_ptr;
+    p.col_idx = h->col_idx;
+    return p;
+}
+
+// workspace of the segment product (schedule sched, or any the selector picks)
+static int hybrid_inner_bytes(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t* sched, size_t* bytes)
+{
+    std::string why;
+    int rc = csrh::check_problem(p, false, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    size_t need = auto_workspace(p);
+    if (sched) {
+        rc = csrh::check_schedule(p, *sched, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+        need = std::max(need, csrh::workspace_bytes(p, *sched));
+    }
+    *bytes = (need + csrh::kAlign - 1) / csrh::kAlign * csrh::kAlign;
+    return CSR_OK;
+}
+
+int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width,
+                              const csr_schedule_t* sched, size_t* bytes)
+{
+    if (!bytes) return CSR_ERR_NULL;
+    int rc = check_hybrid(ctx, h, true);
+    if (rc != CSR_OK) return rc;
+    if (op != CSR_OP_SPMM && op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "the format serves SpMM and SDDMM");
+    csr_problem_t p = hybrid_problem(h, op, width);
+    size_t inner = 0;
+    rc = hybrid_inner_bytes(ctx, p, sched, &inner);
+    if (rc != CSR_OK) return rc;
+    *bytes = inner + (op == CSR_OP_SPMM ? (size_t)h->n_seg * width * 4 : 0);
+    return CSR_OK;
+}
+
+// The segment product of a call over the format: the plain problem on the
+// segment pattern with the caller's operands, its workspace (SpMM: followed
+// by the segments' partial rows) and, for SDDMM, the index maps.
+struct HybridCall {
+    csr_problem_t p;
+    RowMaps maps;
+    float* part_rows;  // SpMM only
+};
+
+static int hybrid_call(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width, const void* a,
+                       int64_t lda, const void* b, int64_t ldb, const csr_schedule_t* sched, void* workspace,
+                       size_t ws_bytes, void* stream, float* sddmm_out, HybridCall* c)
+{
+    int rc = check_hybrid(ctx, h, true);
+    if (rc != CSR_OK) return rc;
+    if (op != CSR_OP_SPMM && op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "the format serves SpMM and SDDMM");
+    c->p = hybrid_problem(h, op, width);
+    c->p.a = a;
+    c->p.b = b;
+    c->p.ld_b = ldb;
+    c->maps = RowMaps{nullptr, nullptr};
+    c->part_rows = nullptr;
+    if (op == CSR_OP_SDDMM) {
+        c->p.ld_a = lda;
+        c->p.out = sddmm_out;
+        c->maps = RowMaps{h->seg_row, h->perm};
+    }
+    size_t inner = 0;
+    rc = hybrid_inner_bytes(ctx, c->p, sched, &inner);
+    if (rc != CSR_OK) return rc;
+    const size_t need = inner + (op == CSR_OP_SPMM ? (size_t)h->n_seg * width * 4 : 0);
+    if (!workspace || (uintptr_t)workspace % csrh::kAlign)
+        return set_err(ctx, CSR_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+    if (ws_bytes < need) return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need));
+    if (op == CSR_OP_SPMM) {
+        c->part_rows = reinterpret_cast<float*>(static_cast<char*>(workspace) + inner);
+        c->p.out = c->part_rows;
+        c->p.ld_out = width;
+    }
+    c->p.workspace = workspace;
+    c->p.workspace_bytes = op == CSR_OP_SPMM ? inner : ws_bytes;
+    c->p.stream = stream;
+    std::string why;
+    rc = csrh::check_problem(c->p, true, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    return CSR_OK;
+}
+
+// Runs a prepared call (ctx locked, device current): the segment product
+// with sched or the selected schedule, then (SpMM) the sum of the partial rows.
+static int hybrid_run(csr_context_t ctx, const csr_hybrid_t* h, const HybridCall& c, const csr_schedule_t* sched,
+                      float* Y, int64_t ldy)
+{
+    hipStream_t st = static_cast<hipStream_t>(c.p.stream);
+    const RowMaps* maps = c.p.op == CSR_OP_SDDMM ? &c.maps : nullptr;
+    if (h->n_seg > 0) {
+        csr_schedule_t s;
+        if (sched) {
+            s = *sched;
+        } else {
+            int rc = select_locked(ctx, c.p, CSR_SELECT_AUTO, &s, nullptr, maps);
+            if (rc != CSR_OK) return rc;
+        }
+        int rc = run_schedule(ctx, c.p, s, st, maps);
+        if (rc != CSR_OK) return rc;
+    }
+    if (c.p.op == CSR_OP_SPMM)
+        CSR_HIP(ctx, csrk::launch_hybrid_reduce(Y, ldy, c.part_rows, (int32_t)c.p.width, h->row_seg_ptr, h->row_seg,
+                                                h->n_rows, st));
+    return CSR_OK;
+}
+
+int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals, const float* X, int64_t F,
+                    int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
+                    size_t ws_bytes, void* stream)
+{
+    if (!ctx || !X || !Y) return CSR_ERR_NULL;
+    if (F < 1 || ldy < F) return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        HybridCall c;
+        int rc = hybrid_call(ctx, h, CSR_OP_SPMM, F, vals, 0, X, ldx, sched, workspace, ws_bytes, stream, nullptr, &c);
+        if (rc != CSR_OK) return rc;
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        DeviceGuard g(ctx->device);
+        return hybrid_run(ctx, h, c, sched, Y, ldy);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const float* U, int64_t ldu, const float* V,
+                     int64_t ldv, int64_t K, float* out, const csr_schedule_t* sched, void* workspace,
+                     size_t ws_bytes, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        HybridCall c;
+        int rc = hybrid_call(ctx, h, CSR_OP_SDDMM, K, U, ldu, V, ldv, sched, workspace, ws_bytes, stream, out, &c);
+        if (rc != CSR_OK) return rc;
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        DeviceGuard g(ctx->device);
+        return hybrid_run(ctx, h, c, sched, nullptr, 0);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_problem_t* call, uint32_t mode,
+                      csr_schedule_t* out, uint64_t* signature)
+{
+    if (!ctx || !call || !out) return CSR_ERR_NULL;
+    if (mode > CSR_SELECT_ESTIMATE) return set_err(ctx, CSR_ERR_SHAPE, "unknown selection mode");
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        HybridCall c;
+        int rc = hybrid_call(ctx, h, call->op, call->width, call->a, call->ld_a, call->b, call->ld_b, nullptr,
+                             call->workspace, call->workspace_bytes, call->stream, static_cast<float*>(call->out), &c);
+        if (rc != CSR_OK) return rc;
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        DeviceGuard g(ctx->device);
+        if (h->n_seg == 0) {  // nothing to run: the default schedule
+            *out = csrh::default_schedule(c.p);
+            if (signature) *signature = 0;
+            return CSR_OK;
+        }
+        return select_locked(ctx, c.p, mode, out, signature, c.p.op == CSR_OP_SDDMM ? &c.maps : nullptr);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
 int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_schedule_t* out, uint64_t* signature)
 {
     if (!ctx || !p || !out) return CSR_ERR_NULL;
@@ -753,6 +1046,16 @@ int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule
     int rc = csrh::check_problem(*p, false, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);
     *out = csrh::default_schedule(*p);
+    return CSR_OK;
+}
+
+int csr_hybrid_parts(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, int32_t* parts)
+{
+    if (!p || !parts) return CSR_ERR_NULL;
+    std::string why;
+    int rc = csrh::check_problem(*p, false, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    *parts = csrh::hybrid_parts(*p, histogram);
     return CSR_OK;
 }
 

@@ -25,6 +25,11 @@ struct Fp32Args {
     int32_t* carry_row;   // [2 n_chunks]: row of slot A / slot B, -1 if empty
     float* carry_ml;      // [2 n_chunks][2]: attention piece (max, sum of exp)
     float* carry_val;     // [2 n_chunks][F]
+    // SDDMM on the column-part segment format: U row of each pattern row
+    // (its segment's row) and output slot of each entry (its original
+    // position); null = the row / entry itself
+    const int32_t* u_row;
+    const int32_t* out_idx;
 };
 
 struct MhaArgs {

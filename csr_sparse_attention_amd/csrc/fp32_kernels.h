@@ -165,7 +165,7 @@ __device__ __forceinline__ void store_row_div(float* dst, const float (&acc)[NV]
 template <int VEC, int NV, int U>
 __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int32_t* col, int kb, int ke,
                                             int step, const float* X, int64_t ldx, const Lanes<VEC, NV>& L,
-                                            int F, float* out)
+                                            int F, float* out, const int32_t* out_idx)
 {
     for (int k = kb; k < ke; k += step * U) {
         float xv[U][NV][VEC];
@@ -203,11 +203,14 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 int e = k + uu * step;
-                if (e < ke) out[e] = d[uu];
+                if (e < ke) out[out_idx ? out_idx[e] : e] = d[uu];
             }
         }
     }
 }
+
+// U row read for pattern row r: its own row, or the row a segment belongs to
+__device__ __forceinline__ int64_t u_row_of(const Fp32Args& a, int64_t r) { return a.u_row ? a.u_row[r] : r; }
 
 template <int VEC, int NV>
 __device__ __forceinline__ void load_row(float (&u)[NV][VEC], const float* src, const Lanes<VEC, NV>& L, int F)
@@ -236,8 +239,8 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
 
     if constexpr (OP == Op::Sddmm) {
         float u[NV][VEC];
-        load_row<VEC, NV>(u, a.U + row * a.ldu, L, a.F);
-        sddmm_edges<VEC, NV, U>(u, a.col_idx, b, e, 1, a.X, a.ldx, L, a.F, a.Y);
+        load_row<VEC, NV>(u, a.U + u_row_of(a, row) * a.ldu, L, a.F);
+        sddmm_edges<VEC, NV, U>(u, a.col_idx, b, e, 1, a.X, a.ldx, L, a.F, a.Y, a.out_idx);
     } else {
         float acc[NV][VEC];
         zero(acc);
@@ -335,16 +338,16 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
             const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
             if (se - sb < long_row || se <= sb) continue;
             float u[NV][VEC];
-            load_row<VEC, NV>(u, a.U + ((int64_t)x0 + i) * a.ldu, L, a.F);
-            sddmm_edges<VEC, NV, U>(u, col, sb + L.g, se, G, a.X, a.ldx, L, a.F, a.Y);
+            load_row<VEC, NV>(u, a.U + u_row_of(a, (int64_t)x0 + i) * a.ldu, L, a.F);
+            sddmm_edges<VEC, NV, U>(u, col, sb + L.g, se, G, a.X, a.ldx, L, a.F, a.Y, a.out_idx);
         }
         // pass 2: short segments, one group each
         for (int i = L.g; i < nrow; i += G) {
             const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
             if (se - sb >= long_row || se <= sb) continue;
             float u[NV][VEC];
-            load_row<VEC, NV>(u, a.U + ((int64_t)x0 + i) * a.ldu, L, a.F);
-            sddmm_edges<VEC, NV, U>(u, col, sb, se, 1, a.X, a.ldx, L, a.F, a.Y);
+            load_row<VEC, NV>(u, a.U + u_row_of(a, (int64_t)x0 + i) * a.ldu, L, a.F);
+            sddmm_edges<VEC, NV, U>(u, col, sb, se, 1, a.X, a.ldx, L, a.F, a.Y, a.out_idx);
         }
     } else {
         for (int i = 0; i < nrow; ++i) {
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
             for (int u = 0; u < U; ++u) {
                 const int e = b + u * CSR_WAVE + lane;
                 if (e < y1) {
-                    load_row(uv[u], a.U + ((int64_t)x0 + row_of(e)) * a.ldu);
+                    load_row(uv[u], a.U + u_row_of(a, (int64_t)x0 + row_of(e)) * a.ldu);
                     load_row(xv[u], a.X + (int64_t)col[e] * a.ldx);
                 }
             }
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
                     for (int j = 0; j < NV; ++j)
 #pragma unroll
                         for (int t = 0; t < VEC; ++t) d = fmaf(uv[u][j][t], xv[u][j][t], d);
-                    a.Y[e] = d;
+                    a.Y[a.out_idx ? a.out_idx[e] : e] = d;
                 }
             }
         }

@@ -401,6 +401,32 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
     return t;
 }
 
+// Rule of the column-part segment format, from measurements on MI355X (two
+// graphs, widths 4 to 128): the best part count puts about 4 MiB of the
+// gathered matrix in each part, the L2 of one XCD, so P is the power of two
+// nearest to (gathered bytes / 4 MiB).  The format pays when that gives at
+// least 4 parts and at most 32 (beyond 32 x 4 MiB a part no longer fits the
+// L2 and the segments' partial rows cost more than the gathers save), for
+// SpMM at any width and for SDDMM with rows of at most 16 floats (at wider
+// rows the per-entry output scatter cancels the gain), and when non-empty
+// rows hold at least 8 entries on average (shorter rows make about one
+// segment per entry: a guard, not measured).
+int hybrid_parts(const csr_problem_t& p, const int64_t* hist)
+{
+    if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return 1;
+    if (p.op == CSR_OP_SDDMM && p.width > 16) return 1;
+    const double gathered = (double)p.n_cols * p.width * 4.0;
+    const double slices = gathered / (4.0 * (1 << 20));
+    if (slices < 2.83 || slices > 45.3) return 1;  // nearest power of two below 4 or above 32
+    int P = 1;
+    while (P < 32 && (double)P * 1.41421356 < slices) P *= 2;
+    if (hist) {
+        const int64_t nonempty = p.n_rows - hist[0];
+        if (nonempty > 0 && p.nnz < 8 * nonempty) return 1;
+    }
+    return P;
+}
+
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev)
 {
     uint64_t h = 0xcbf29ce484222325ull;

@@ -64,6 +64,10 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
 // FNV-1a 64 signature of (problem shape, alignment class, histogram, device).
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev);
 
+// Column parts of the column-part segment format expected to be fastest for
+// problem p (1: the plain CSR path); see hybrid_parts in host.cpp.
+int hybrid_parts(const csr_problem_t& p, const int64_t* hist);
+
 // Cache log line format.
 std::string format_cache_line(uint64_t sig, const csr_schedule_t& s, double probe_us);
 bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s, double* probe_us);

@@ -137,6 +137,14 @@ hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int6
     return hipGetLastError();
 }
 
+hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows, int64_t nnz, hipStream_t s)
+{
+    if (nnz == 0) return hipSuccess;
+    const int64_t blocks = (nnz + CSR_BLOCK - 1) / CSR_BLOCK;
+    hipLaunchKernelGGL(k_coo_rows, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
+    return hipGetLastError();
+}
+
 hipError_t launch_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n, hipStream_t s)
 {
     if (n == 0) return hipSuccess;

@@ -16,7 +16,7 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _ffi
-from ._ffi import CsrError, CsrProblem, CsrSchedule
+from ._ffi import CsrError, CsrHybrid, CsrProblem, CsrSchedule
 
 _lock = threading.Lock()
 _contexts: dict = {}
@@ -445,6 +445,169 @@ def attention_backward(row_ptr, col_idx, edge_scores, node_value, d_out, *, scal
     dS = row_softmax_backward(row_ptr, P, dP, scale=scale, out=dP, ctx=ctx)
     dV = spmm(At.row_ptr, At.col_idx, gather_values(At.perm, P, ctx=ctx), d_out, ctx=ctx)
     return dS, dV
+
+
+# ---------------------------------------------------------------------------
+# column-part segment format
+# ---------------------------------------------------------------------------
+
+class Hybrid:
+    """A column-part segment format of a CSR pattern (see hybrid_format): the
+    device arrays and the csr_hybrid_t that describes them.  seg_ptr, seg_row
+    and row_seg are views of their first n_seg (+1) entries."""
+
+    def __init__(self, desc: CsrHybrid, arrays: dict):
+        self.desc = desc
+        self._arrays = arrays  # keeps the device memory alive
+        n = desc.n_seg
+        self.n_rows, self.n_cols, self.nnz = desc.n_rows, desc.n_cols, desc.nnz
+        self.parts, self.part_cols, self.n_seg = desc.parts, desc.part_cols, n
+        self.perm, self.col_idx = arrays["perm"], arrays["col_idx"]
+        self.seg_ptr = arrays["seg_ptr"][:n + 1]
+        self.seg_row = arrays["seg_row"][:n]
+        self.row_seg_ptr = arrays["row_seg_ptr"]
+        self.row_seg = arrays["row_seg"][:n]
+
+    def __repr__(self):
+        return (f"Hybrid(n_rows={self.n_rows}, n_cols={self.n_cols}, nnz={self.nnz}, parts={self.parts}, "
+                f"part_cols={self.part_cols}, n_seg={self.n_seg})")
+
+
+def hybrid_parts(problem: CsrProblem, histogram=None) -> int:
+    """Column parts for which the column-part segment format is expected to
+    beat the plain CSR path on this problem (1: use the plain path)."""
+    h = None if histogram is None else (ctypes.c_int64 * 67)(*[int(v) for v in histogram])
+    out = ctypes.c_int32()
+    _check(_lib().csr_hybrid_parts(None, ctypes.byref(problem), h, ctypes.byref(out)), "csr_hybrid_parts")
+    return out.value
+
+
+def hybrid_format(row_ptr, col_idx, n_cols: int, parts: int, *, ctx: Optional[Context] = None) -> Hybrid:
+    """Builds the column-part segment format of (row_ptr, col_idx) with
+    ``parts`` column parts (1, 2, 4, 8, 16 or 32)."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    device = row_ptr.device
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    cap = ctypes.c_int64()
+    _check(lib.csr_hybrid_capacity(n_rows, nnz, parts, ctypes.byref(cap)), "csr_hybrid_capacity")
+    nbytes = ctypes.c_size_t()
+    _check(lib.csr_hybrid_build_workspace_size(ctx.handle, n_rows, nnz, parts, ctypes.byref(nbytes)),
+           "csr_hybrid_build_workspace_size", ctx)
+    ws = _workspace(device, nbytes.value)
+
+    def i32(n):
+        return torch.empty(max(n, 1), dtype=torch.int32, device=device)
+
+    arrays = {"perm": i32(nnz)[:nnz], "col_idx": i32(nnz)[:nnz], "seg_ptr": i32(cap.value + 1),
+              "seg_row": i32(cap.value), "row_seg_ptr": i32(n_rows + 1), "row_seg": i32(cap.value)}
+    h = CsrHybrid()
+    h.n_rows, h.n_cols, h.nnz, h.parts, h.seg_cap = n_rows, n_cols, nnz, parts, cap.value
+    for k, t in arrays.items():
+        setattr(h, k, t.data_ptr())
+    _check(lib.csr_hybrid_build(ctx.handle, row_ptr.data_ptr(), col_idx.data_ptr(), ctypes.byref(h), ws.data_ptr(),
+                                nbytes.value, _stream(device)), "csr_hybrid_build", ctx)
+    return Hybrid(h, arrays)
+
+
+def hybrid_values(h: Hybrid, vals, *, out=None, ctx: Optional[Context] = None) -> torch.Tensor:
+    """Per-entry values moved into the format's entry order (vals[perm])."""
+    return gather_values(h.perm, vals, out=out, ctx=ctx)
+
+
+def hybrid_problem(h: Hybrid, op: str, *operands) -> CsrProblem:
+    """The plain problem of the segment product ('spmm': vals, X; 'sddmm': U, V),
+    for candidates() / default_schedule(): its schedules are the ones that
+    hybrid_spmm / hybrid_sddmm accept."""
+    if op == "spmm":
+        vals, X = operands
+        p = _problem(_ffi.OP_SPMM, h.seg_ptr, h.col_idx, vals, X, None, None, n_cols=X.shape[0], width=X.shape[1],
+                     ld_b=_dense(X, "X", torch.float32), ld_out=X.shape[1])
+        p.out = 256  # stands for the partial rows, which sit 256-byte aligned in the workspace
+        return p
+    if op == "sddmm":
+        U, V = operands
+        return _sddmm_problem(h.seg_ptr, h.col_idx, U, V, None)
+    raise ValueError(op)
+
+
+def _hybrid_run(h, op, width, schedule, ctx, device, call):
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    nbytes = ctypes.c_size_t()
+    _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), op, width, _sched_arg(schedule),
+                                         ctypes.byref(nbytes)), "csr_hybrid_workspace_size", ctx)
+    ws = _workspace(device, nbytes.value)
+    _check(call(ctx, ws, nbytes.value, _stream(device)), "csr hybrid call", ctx)
+
+
+def hybrid_select(h: Hybrid, op: str, *operands, mode: str = "auto", out=None, ctx: Optional[Context] = None):
+    """Selects the segment product's schedule for a call over the format
+    ('spmm': format-order vals or None, X; 'sddmm': U, V); returns
+    (schedule, signature).  Probes run on the given operands (SDDMM: they
+    write ``out``)."""
+    a, b = operands
+    device = b.device
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    call = CsrProblem()
+    call.op = _ffi.OP_SPMM if op == "spmm" else _ffi.OP_SDDMM if op == "sddmm" else -1
+    if call.op < 0:
+        raise ValueError(op)
+    call.width = b.shape[1]
+    call.b, call.ld_b = b.data_ptr(), _dense(b, "X" if op == "spmm" else "V", torch.float32)
+    if op == "spmm":
+        call.a = _ptr(a)
+    else:
+        call.a, call.ld_a = a.data_ptr(), _dense(a, "U", torch.float32)
+        out = out if out is not None else torch.empty(h.nnz, dtype=torch.float32, device=device)
+        call.out = out.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), call.op, call.width, None,
+                                         ctypes.byref(nbytes)), "csr_hybrid_workspace_size", ctx)
+    ws = _workspace(device, nbytes.value)
+    call.workspace, call.workspace_bytes, call.stream = ws.data_ptr(), nbytes.value, _stream(device)
+    s, sig = CsrSchedule(), ctypes.c_uint64()
+    _check(lib.csr_hybrid_select(ctx.handle, ctypes.byref(h.desc), ctypes.byref(call), _ffi.SELECT_MODES[mode],
+                                 ctypes.byref(s), ctypes.byref(sig)), "csr_hybrid_select", ctx)
+    return s, sig.value
+
+
+def hybrid_spmm(h: Hybrid, vals, X, *, out=None, schedule: Optional[CsrSchedule] = None,
+                ctx: Optional[Context] = None) -> torch.Tensor:
+    """Y = A X over the format; ``vals`` in the format's entry order
+    (hybrid_values) or None for all ones."""
+    ldx = _dense(X, "X", torch.float32)
+    if out is None:
+        out = torch.empty((h.n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
+    ldy = _dense(out, "out", torch.float32)
+    if vals is not None:
+        _flat_f32(vals, "vals", h.nnz)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), _ptr(vals), X.data_ptr(), X.shape[1], ldx,
+                                      out.data_ptr(), ldy, _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _hybrid_run(h, _ffi.OP_SPMM, X.shape[1], schedule, ctx, X.device, call)
+    return out
+
+
+def hybrid_sddmm(h: Hybrid, U, V, *, out=None, schedule: Optional[CsrSchedule] = None,
+                 ctx: Optional[Context] = None) -> torch.Tensor:
+    """out[e] = <U[row(e)], V[col(e)]> over the format, in the original entry order."""
+    ldu = _dense(U, "U", torch.float32)
+    ldv = _dense(V, "V", torch.float32)
+    if U.shape[1] != V.shape[1]:
+        raise ValueError("U and V must have the same width")
+    if out is None:
+        out = torch.empty(h.nnz, dtype=torch.float32, device=U.device)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_hybrid_sddmm(ctx.handle, ctypes.byref(h.desc), U.data_ptr(), ldu, V.data_ptr(), ldv,
+                                       U.shape[1], out.data_ptr(), _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _hybrid_run(h, _ffi.OP_SDDMM, U.shape[1], schedule, ctx, U.device, call)
+    return out
 
 
 def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0) -> CsrProblem:

@@ -316,6 +316,102 @@ int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
 int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const float* src, float* dst, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Column-part segment format (a composed, "hybrid" format)
+ *
+ * The SparseTIR page (abstract) holds that no single sparse format gets full
+ * hardware efficiency on every input and that formats should be composed.
+ * This format composes a partition of the columns with a compaction of the
+ * rows: the columns are cut into P equal parts (column c lies in part
+ * c / part_cols, part_cols = ceil(n_cols / P)); a segment is the run of one
+ * row's entries whose columns lie in one part (the entries keep their
+ * original order); the segments are ordered by (part, row) and only non-empty
+ * segments are stored.  The segments form a plain CSR pattern (seg_ptr over
+ * the reordered entries, n_seg rows), so every mapping of the plain products
+ * runs on it; blocks reach the parts in order, so at any time the gathered
+ * rows of the dense operand come from about one 1/P slice of it, a slice that
+ * the caches hold.  A product over the format equals the plain product up to
+ * the order of the additions (a row's segments are summed in part order).
+ * ------------------------------------------------------------------------- */
+typedef struct csr_hybrid_s {
+    int64_t n_rows, n_cols, nnz; /* the pattern's shape (set by the caller) */
+    int32_t parts;               /* P in {1, 2, 4, 8, 16, 32} (set by the caller) */
+    int32_t part_cols;           /* ceil(n_cols / P) (written by csr_hybrid_build) */
+    int64_t seg_cap;             /* capacity of the segment arrays, >= csr_hybrid_capacity (set by the caller) */
+    int64_t n_seg;               /* number of segments (written by csr_hybrid_build) */
+    int32_t* perm;               /* [nnz] original entry index of each format entry */
+    int32_t* col_idx;            /* [nnz] column of each format entry */
+    int32_t* seg_ptr;            /* [seg_cap + 1] first format entry of each segment; seg_ptr[n_seg] = nnz */
+    int32_t* seg_row;            /* [seg_cap] row of each segment */
+    int32_t* row_seg_ptr;        /* [n_rows + 1] each row's slots in row_seg */
+    int32_t* row_seg;            /* [seg_cap] each row's segments, in part order */
+} csr_hybrid_t;
+
+/* The column parts for which the format is expected to beat the plain CSR
+ * path on problem p (op CSR_OP_SPMM or CSR_OP_SDDMM; shape fields only) with
+ * degree histogram (int64 [67], or NULL), or 1 when the plain path is
+ * expected to be faster.  A measured rule: each part should hold about 4 MiB
+ * of the gathered matrix (one XCD's L2); the format is proposed when that
+ * gives 4 to 32 parts, for SpMM, and for SDDMM rows of at most 16 floats,
+ * with at least 8 entries per non-empty row on average.  Host-only. */
+int csr_hybrid_parts(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, int32_t* parts);
+
+/* Upper bound of the segment count, min(nnz, n_rows * parts): the capacity
+ * the segment arrays need.  Host-only; CSR_ERR_SHAPE for bad sizes or
+ * parts. */
+int csr_hybrid_capacity(int64_t n_rows, int64_t nnz, int32_t parts, int64_t* seg_cap);
+
+/* Device workspace (bytes) that csr_hybrid_build needs for these sizes. */
+int csr_hybrid_build_workspace_size(csr_context_t ctx, int64_t n_rows, int64_t nnz, int32_t parts, size_t* bytes);
+
+/* Builds the format of the CSR pattern (row_ptr, col_idx) into the
+ * caller-allocated device arrays of *h (sizes and parts set by the caller;
+ * part_cols and n_seg are written).  Deterministic (stable sorts, no
+ * order-dependent atomics).  Synchronous: it reads the segment count back.
+ * col_idx must lie in [0, n_cols) (checked only with CSR_CTX_VALIDATE:
+ * CSR_ERR_INVALID_CSR).  CSR_ERR_WORKSPACE when ws_bytes or h->seg_cap is too
+ * small. */
+int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* col_idx, csr_hybrid_t* h,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Device workspace (bytes) of csr_hybrid_spmm (op CSR_OP_SPMM: includes the
+ * segments' partial rows, n_seg * width floats) or csr_hybrid_sddmm (op
+ * CSR_OP_SDDMM) at this width, for schedule sched (NULL: any the selector may
+ * pick).  h must be built. */
+int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width,
+                              const csr_schedule_t* sched, size_t* bytes);
+
+/* Y = A X over a built format: each segment's product into its partial row
+ * (a CSR SpMM of the n_seg-row segment pattern, any mapping), then
+ * Y[r] = the sum of row r's partial rows in part order (+0 for a row without
+ * entries).  vals: [nnz] edge values in FORMAT order (csr_gather_values with
+ * h->perm moves them there), or NULL for all ones.  X, F, ldx, Y, ldy as for
+ * csr_spmm.  sched: a schedule of op CSR_OP_SPMM for the segment pattern
+ * (NULL: selected and cached as for csr_spmm, keyed by the segment pattern's
+ * shape and degree histogram). */
+int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals, const float* X, int64_t F,
+                    int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+/* out[e] = dot(U[row(e)], V[col(e)]) over a built format, written in the
+ * ORIGINAL entry order (the kernels read U through seg_row and write through
+ * perm).  U, ldu, V, ldv, K, out as for csr_sddmm; sched: a schedule of op
+ * CSR_OP_SDDMM for the segment pattern (NULL: selected). */
+int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const float* U, int64_t ldu, const float* V,
+                     int64_t ldv, int64_t K, float* out, const csr_schedule_t* sched, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/* Selects (and caches) the schedule of the segment product of a call over a
+ * built format, as csr_select does for a plain call.  call describes the
+ * call's operands only: op (CSR_OP_SPMM or CSR_OP_SDDMM), width, a / ld_a
+ * (SpMM: the format-order values or NULL; SDDMM: U), b / ld_b (X or V), out
+ * (SDDMM: the [nnz] output, written by the probes; SpMM: unused, the probes
+ * write the partial rows into the workspace), workspace (of
+ * csr_hybrid_workspace_size bytes), workspace_bytes and stream; its pattern
+ * fields are ignored.  Modes and the signature as for csr_select. */
+int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_problem_t* call, uint32_t mode,
+                      csr_schedule_t* out, uint64_t* signature);
+
+/* ---------------------------------------------------------------------------
  * Schedule selection and cache (AutoSAGE page, Abstract: input-aware choice
  * refined by on-device micro-probes, guarded fallback, persistent cache for
  * deterministic replay).

@@ -22,6 +22,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from .structure import (  # noqa: F401
+    hybrid_format,
+    hybrid_format_loops,
     transpose,
     degree_histogram,
     merge_path_partition,

@@ -16,6 +16,13 @@
 * Transpose: the CSR pattern of A^T, i.e. the entries regrouped by column,
   each column listing its rows in increasing order (a stable sort by column).
 
+* Column-part segment format: the composition of a column partition and a
+  row compaction (the SparseTIR page, abstract: formats compose, and no one
+  format serves every input).  Columns are cut into P equal parts, part of
+  column c = c // ceil(n_cols / P); segment (p, r) is the list of row r's
+  entries (original order) whose columns lie in part p; the non-empty
+  segments are listed by part, then row; each row lists its segments by part.
+
 * FNV-1a 64: the published Fowler-Noll-Vo hash (offset basis
   0xcbf29ce484222325, prime 0x100000001b3; per byte: xor, then multiply).
 """
@@ -104,3 +111,56 @@ def transpose(row_ptr, col_idx, n_cols):
     t_rp = np.zeros(n_cols + 1, dtype=np.int64)
     np.cumsum(counts, out=t_rp[1:])
     return t_rp.astype(np.int32), rows[perm].astype(np.int32), perm.astype(np.int32)
+
+
+def hybrid_format_loops(row_ptr, col_idx, n_cols, parts):
+    """The column-part segment format by its definition, with plain loops
+    (tiny inputs): for each part p, for each row r, the entries of r whose
+    column lies in p, in their original order, form segment (p, r) when there
+    are any.  Returns a dict of int64 arrays: part_cols, perm, col_idx,
+    seg_ptr, seg_row, row_seg_ptr, row_seg."""
+    rp = [int(v) for v in row_ptr]
+    ci = [int(v) for v in col_idx]
+    n_rows = len(rp) - 1
+    part_cols = -(-n_cols // parts) if n_cols > 0 else 1
+    perm, seg_ptr, seg_row, seg_part = [], [], [], []
+    for p in range(parts):
+        for r in range(n_rows):
+            mine = [e for e in range(rp[r], rp[r + 1]) if ci[e] // part_cols == p]
+            if mine:
+                seg_ptr.append(len(perm))
+                seg_row.append(r)
+                seg_part.append(p)
+                perm += mine
+    seg_ptr.append(len(perm))
+    row_seg_ptr, row_seg = [0], []
+    for r in range(n_rows):
+        row_seg += [s for s in range(len(seg_row)) if seg_row[s] == r]  # ascending s = ascending part
+        row_seg_ptr.append(len(row_seg))
+    a = lambda v: np.asarray(v, dtype=np.int64)  # noqa: E731
+    return {"part_cols": part_cols, "perm": a(perm), "col_idx": a([ci[e] for e in perm]), "seg_ptr": a(seg_ptr),
+            "seg_row": a(seg_row), "seg_part": a(seg_part), "row_seg_ptr": a(row_seg_ptr), "row_seg": a(row_seg)}
+
+
+def hybrid_format(row_ptr, col_idx, n_cols, parts):
+    """The same format for larger inputs: the entries ordered by the key
+    (part, row) with a stable sort (which keeps each segment's entries in
+    their original order), a segment wherever the key changes, and each row's
+    segments found by a stable sort of the segments by row."""
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    n_rows = len(rp) - 1
+    part_cols = -(-n_cols // parts) if n_cols > 0 else 1
+    rows = np.repeat(np.arange(n_rows, dtype=np.int64), np.diff(rp))
+    key = (ci // part_cols) * n_rows + rows
+    perm = np.argsort(key, kind="stable")
+    k = key[perm]
+    starts = np.flatnonzero(np.r_[True, k[1:] != k[:-1]]) if len(k) else np.zeros(0, dtype=np.int64)
+    seg_row = k[starts] % max(n_rows, 1)
+    row_seg = np.argsort(seg_row, kind="stable")
+    row_seg_ptr = np.zeros(n_rows + 1, dtype=np.int64)
+    np.cumsum(np.bincount(seg_row, minlength=n_rows)[:n_rows], out=row_seg_ptr[1:])
+    return {"part_cols": part_cols, "perm": perm.astype(np.int64), "col_idx": ci[perm],
+            "seg_ptr": np.r_[starts, len(k)].astype(np.int64), "seg_row": seg_row.astype(np.int64),
+            "seg_part": (k[starts] // max(n_rows, 1)).astype(np.int64), "row_seg_ptr": row_seg_ptr,
+            "row_seg": row_seg.astype(np.int64)}

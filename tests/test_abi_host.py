@@ -236,3 +236,37 @@ def test_host_only_context_refuses_operations():
     assert lib.csr_spmm(ctx.handle, 1, 1, 0, 0x1000, None, None, 0x1000, 4, 4, 0x1000, 4, None, 0x1000, 4096,
                         None) == -11
     ctx.close()
+
+
+def test_hybrid_parts_rule():
+    # about 4 MiB of the gathered matrix per part, 4 to 32 parts
+    def parts(op, n_cols, width, n_rows=100_000, nnz=5_000_000, hist=None):
+        return csa.hybrid_parts(problem(op, n_rows=n_rows, n_cols=n_cols, nnz=nnz, width=width), hist)
+
+    S, D = _ffi.OP_SPMM, _ffi.OP_SDDMM
+    assert [parts(S, 232_965, F) for F in (32, 64, 128, 602)] == [8, 16, 32, 1]
+    assert [parts(S, 1_000_000, F) for F in (4, 8, 16, 32)] == [4, 8, 16, 32]
+    assert [parts(D, 1_000_000, K) for K in (4, 8, 16, 32)] == [4, 8, 16, 1]
+    assert parts(S, 2_449_029, 100) == 1  # slices far beyond an L2
+    assert parts(S, 100_000, 4) == 1      # 1.5 MiB: fits without the format
+    assert parts(_ffi.OP_ATTENTION, 232_965, 32) == 1
+    # the average non-empty row must hold at least 8 entries
+    hist = np.zeros(67, dtype=np.int64)
+    hist[0] = 60_000  # empty rows
+    assert parts(S, 232_965, 32, nnz=40_000 * 8, hist=hist) == 8
+    assert parts(S, 232_965, 32, nnz=40_000 * 8 - 1, hist=hist) == 1
+
+
+def test_hybrid_capacity_and_host_only_context():
+    lib = csa.load_library()
+    n = ctypes.c_int64()
+    assert lib.csr_hybrid_capacity(10, 100, 4, ctypes.byref(n)) == 0 and n.value == 40
+    assert lib.csr_hybrid_capacity(1000, 100, 32, ctypes.byref(n)) == 0 and n.value == 100
+    assert lib.csr_hybrid_capacity(0, 0, 1, ctypes.byref(n)) == 0 and n.value == 0
+    for bad in ((10, 100, 3), (10, 100, 64), (10, 100, 0), (-1, 100, 4), (10, 2**31, 4)):
+        assert lib.csr_hybrid_capacity(*bad, ctypes.byref(n)) == -2
+    assert lib.csr_hybrid_capacity(10, 100, 4, None) == -1
+    ctx = csa.Context(-1, None)
+    b = ctypes.c_size_t()
+    assert lib.csr_hybrid_build_workspace_size(ctx.handle, 10, 100, 4, ctypes.byref(b)) == -11
+    ctx.close()

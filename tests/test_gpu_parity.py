@@ -713,3 +713,157 @@ def test_backward_deterministic():
     b = [x.cpu().numpy() for x in csa.attention_backward(rp, ci, sc, V, dO, scale=0.3)]
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# column-part segment format
+# ---------------------------------------------------------------------------
+
+def _format_graph(name):
+    if name == "skew":
+        return skew_graph(1)
+    if name == "dup":
+        return dup_graph(3)
+    if name == "short":
+        return short_rows_graph(5)
+    if name == "edges":
+        return chunk_edge_graph(6)
+    if name == "empty":
+        return CSR(50, 40, np.zeros(51, np.int32), np.zeros(0, np.int32))
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges", "empty"])
+@pytest.mark.parametrize("P", [1, 4, 32])
+def test_hybrid_format_bit_exact(graph, P):
+    csr = _format_graph(graph)
+    rp, ci = pattern_dev(csr)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+    want = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, P)
+    assert h.part_cols == want["part_cols"] and h.n_seg == len(want["seg_row"])
+    for k in ("perm", "col_idx", "seg_ptr", "seg_row", "row_seg_ptr", "row_seg"):
+        assert np.array_equal(getattr(h, k).cpu().numpy(), want[k]), k
+    h2 = csa.hybrid_format(rp, ci, csr.n_cols, P)  # rebuilt: the same arrays
+    for k in ("perm", "seg_ptr", "row_seg"):
+        assert torch.equal(getattr(h, k), getattr(h2, k))
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("F", [1, 4, 32, 100])
+def test_hybrid_spmm_every_schedule(graph, F):
+    csr = _format_graph(graph)
+    rng = np.random.default_rng(1100 + F)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    Xd = dev(X)
+    for P in (2, 8, 32):
+        h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+        hv = csa.hybrid_values(h, dev(vals))
+        p = csa.hybrid_problem(h, "spmm", hv, Xd)
+        for s in schedules(p, thorough=(P == 8 and graph == "skew")):
+            Y = csa.hybrid_spmm(h, hv, Xd, schedule=s)
+            assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-" + sched_id(s))
+        Y = csa.hybrid_spmm(h, hv, Xd)  # selected
+        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-auto")
+    ones, omag = oracle.spmm(csr.row_ptr, csr.col_idx, None, X, threads=oracle.default_threads())
+    Y = csa.hybrid_spmm(h, None, Xd)
+    assert_close(Y.cpu().numpy(), ones, omag, TOL_F32, "unit values")
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("K", [1, 4, 32, 128])
+def test_hybrid_sddmm_every_schedule(graph, K):
+    csr = _format_graph(graph)
+    rng = np.random.default_rng(1200 + K)
+    U = rng.standard_normal((csr.n_rows, K)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, K)).astype(np.float32)
+    ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    Ud, Vd = dev(U), dev(V)
+    for P in (2, 8, 32):
+        h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+        p = csa.hybrid_problem(h, "sddmm", Ud, Vd)
+        for s in schedules(p, thorough=(P == 8 and graph == "skew")):
+            out = csa.hybrid_sddmm(h, Ud, Vd, schedule=s)
+            assert_close(out.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-" + sched_id(s))
+        out = csa.hybrid_sddmm(h, Ud, Vd)
+        assert_close(out.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-auto")
+
+
+def test_hybrid_edge_cases():
+    # no entries: Y is +0 everywhere, SDDMM writes nothing
+    csr = _format_graph("empty")
+    rp, ci = pattern_dev(csr)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, 8)
+    assert h.n_seg == 0 and h.row_seg_ptr.cpu().numpy().tolist() == [0] * 51
+    Y = csa.hybrid_spmm(h, None, dev(np.ones((40, 6), np.float32))).cpu().numpy()
+    assert np.all(Y == 0) and not np.signbit(Y).any()
+    out = csa.hybrid_sddmm(h, dev(np.ones((50, 6), np.float32)), dev(np.ones((40, 6), np.float32)))
+    assert out.numel() == 0
+    # fewer columns than parts, strided operands, empty rows stay +0
+    rng = np.random.default_rng(41)
+    csr = graphs.random_small_graph(2000, 3, 0.5, rng, empty_frac=0.3, allow_dup=True)
+    rp, ci = pattern_dev(csr)
+    h = csa.hybrid_format(rp, ci, 3, 32)
+    assert h.part_cols == 1
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((3, 20)).astype(np.float32)
+    Xs = torch.zeros((3, 24), device="cuda")
+    Xs[:, :20] = dev(X)
+    Ys = torch.full((2000, 28), 7.0, device="cuda")
+    csa.hybrid_spmm(h, csa.hybrid_values(h, dev(vals)), Xs[:, :20], out=Ys[:, :20])
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X)
+    Y = Ys.cpu().numpy()
+    assert_close(Y[:, :20], ref, mag, TOL_F32, "strided")
+    assert np.all(Y[:, 20:] == 7.0)  # the padding columns are not written
+    empty = np.diff(csr.row_ptr) == 0
+    assert np.all(Y[empty, :20] == 0) and not np.signbit(Y[empty, :20]).any()
+
+
+def test_hybrid_deterministic_and_errors():
+    csr = skew_graph(4, n_rows=2000, n_cols=40_000, giant=20_000)
+    rng = np.random.default_rng(9)
+    rp, ci = pattern_dev(csr)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, 16)
+    hv = csa.hybrid_values(h, dev(rng.standard_normal(csr.nnz).astype(np.float32)))
+    X = dev(rng.standard_normal((csr.n_cols, 16)).astype(np.float32))
+    U = dev(rng.standard_normal((csr.n_rows, 16)).astype(np.float32))
+    assert torch.equal(csa.hybrid_spmm(h, hv, X), csa.hybrid_spmm(h, hv, X))
+    assert torch.equal(csa.hybrid_sddmm(h, U, X), csa.hybrid_sddmm(h, U, X))
+    # selection: replayed from the cache, and the schedule the call itself uses
+    ctx = csa.Context(0, None)
+    for op, a, b in (("spmm", hv, X), ("sddmm", U, X)):
+        s1, sig1 = csa.hybrid_select(h, op, a, b, ctx=ctx)
+        s2, sig2 = csa.hybrid_select(h, op, a, b, mode="replay", ctx=ctx)
+        assert bytes(s1) == bytes(s2) and sig1 == sig2 and sig1 != 0
+        run = csa.hybrid_spmm if op == "spmm" else csa.hybrid_sddmm
+        assert torch.equal(run(h, a, b, schedule=s1, ctx=ctx), run(h, a, b, ctx=ctx))
+    assert ctx.cache_info()["entries"] == 2
+    ctx.close()
+    lib = csa.load_library()
+    ctx = csa.default_context(0)
+    st = torch.cuda.current_stream().cuda_stream
+    n = ctypes.c_int64()
+    assert lib.csr_hybrid_capacity(10, 100, 3, ctypes.byref(n)) == -2
+    assert lib.csr_hybrid_capacity(10, 100, 64, ctypes.byref(n)) == -2
+    assert lib.csr_hybrid_capacity(10, 100, 4, ctypes.byref(n)) == 0 and n.value == 40
+    # segment capacity below the bound
+    d = _ffi.CsrHybrid.from_buffer_copy(bytes(h.desc))
+    d.seg_cap = h.desc.seg_cap - 1
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    assert lib.csr_hybrid_build(ctx.handle, rp.data_ptr(), ci.data_ptr(), ctypes.byref(d), ws.data_ptr(),
+                                ws.numel(), st) == -5
+    # a description that was never built
+    d = _ffi.CsrHybrid.from_buffer_copy(bytes(h.desc))
+    d.n_seg = -1
+    Y = torch.empty((csr.n_rows, 16), device="cuda")
+    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(d), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(), 16,
+                               None, ws.data_ptr(), ws.numel(), st) == -2
+    # workspace too small, ldy below the width
+    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(),
+                               16, None, ws.data_ptr(), 4096, st) == -5
+    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(),
+                               8, None, ws.data_ptr(), ws.numel(), st) == -2
+    torch.cuda.synchronize()

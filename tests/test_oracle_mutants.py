@@ -129,3 +129,61 @@ def test_pins_catch_mutant(tmp_path, name, edits):
                 caught.append(pin)
     assert caught, f"no pin catches the mutant '{name}'"
 
+
+
+# Mistakes planted in a copy of the Python structure oracle (both of its
+# constructions of the column-part segment format where the mistake is a
+# misreading of the definition rather than a slip in one of them).
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "structure.py")
+PY_MUTANTS = [
+    ("format reverses equal keys (unstable order)", [
+        ('perm = np.argsort(key, kind="stable")', 'perm = np.argsort(-key, kind="stable")[::-1]')]),
+    ("format parts columns by proportional scaling", [
+        ("key = (ci // part_cols) * n_rows + rows", "key = (ci * parts // max(n_cols, 1)) * n_rows + rows"),
+        ("if ci[e] // part_cols == p]", "if ci[e] * parts // n_cols == p]")]),
+    ("format orders segments by row first", [
+        ("key = (ci // part_cols) * n_rows + rows", "key = rows * parts + (ci // part_cols)"),
+        ("    for p in range(parts):\n        for r in range(n_rows):",
+         "    for r in range(n_rows):\n        for p in range(parts):")]),
+    ("format lists a row's segments last part first", [
+        ('row_seg = np.argsort(seg_row, kind="stable")',
+         'row_seg = np.lexsort((-np.arange(len(seg_row)), seg_row))'),
+        ("if seg_row[s] == r]  # ascending", "if seg_row[s] == r][::-1]  # ascending")]),
+    ("format drops the last segment's end", [
+        ('"seg_ptr": np.r_[starts, len(k)]', '"seg_ptr": np.r_[starts, len(k) - 1]'),
+        ("    seg_ptr.append(len(perm))\n    row_seg_ptr", "    seg_ptr.append(len(perm) - 1)\n    row_seg_ptr")]),
+]
+
+
+def structure_pins():
+    out = [("hand example", pins.test_hybrid_format_hand_example)]
+    out += [(f"bruteforce[{s}]", lambda s=s: pins.test_hybrid_format_bruteforce(s)) for s in range(8)]
+    out += [(f"invariants[{s}]", lambda s=s: pins.test_hybrid_format_invariants(s)) for s in range(4)]
+    out += [(f"identity[{s}]", lambda s=s: pins.test_hybrid_product_identity(oracle, s)) for s in range(4)]
+    return out
+
+
+def test_unmutated_structure_passes_every_pin():
+    for name, fn in structure_pins():
+        fn()
+
+
+@pytest.mark.parametrize("name,edits", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_structure_mutant(monkeypatch, name, edits):
+    import types
+
+    src = open(PY_SRC).read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation site not found: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("structure_mutant")
+    exec(compile(src, "structure_mutant.py", "exec"), mod.__dict__)
+    for fn in ("hybrid_format", "hybrid_format_loops"):
+        monkeypatch.setattr(oracle, fn, getattr(mod, fn))
+    caught = []
+    for pin, fn in structure_pins():
+        try:
+            fn()
+        except Exception:
+            caught.append(pin)
+    assert caught, f"no pin catches the mutant '{name}'"

@@ -532,3 +532,100 @@ def test_transpose_definition(seed):
     order = np.lexsort((np.arange(csr.nnz), csr.col_idx, csr.row_of_edge()))
     assert np.array_equal(rp2, csr.row_ptr) and np.array_equal(ci2, csr.col_idx[order])
     assert np.array_equal(perm[perm2], order)
+
+
+# ---------------------------------------------------------------------------
+# column-part segment format
+# ---------------------------------------------------------------------------
+
+def test_hybrid_format_hand_example():
+    """Worked by hand from the definition: 10 columns in 4 parts of 3 columns
+    (0-2, 3-5, 6-8, 9); row 0 lists unsorted columns, row 1 is empty."""
+    row_ptr = [0, 5, 5, 7, 10]
+    col_idx = [5, 0, 9, 3, 1,  # row 0: parts 1 0 3 1 0
+               7, 8,           # row 2: parts 2 2
+               2, 6, 4]        # row 3: parts 0 2 1
+    want = {
+        "part_cols": 3,
+        # segments (part, row): (0,0) = e1 e4; (0,3) = e7; (1,0) = e0 e3; (1,3) = e9;
+        # (2,2) = e5 e6; (2,3) = e8; (3,0) = e2
+        "perm": [1, 4, 7, 0, 3, 9, 5, 6, 8, 2],
+        "col_idx": [0, 1, 2, 5, 3, 4, 7, 8, 6, 9],
+        "seg_ptr": [0, 2, 3, 5, 6, 8, 9, 10],
+        "seg_row": [0, 3, 0, 3, 2, 3, 0],
+        "seg_part": [0, 0, 1, 1, 2, 2, 3],
+        "row_seg_ptr": [0, 3, 3, 4, 7],
+        "row_seg": [0, 2, 6, 4, 1, 3, 5],
+    }
+    for build in (oracle.hybrid_format_loops, oracle.hybrid_format):
+        got = build(row_ptr, col_idx, 10, 4)
+        for k, v in want.items():
+            assert np.array_equal(np.asarray(got[k]), np.asarray(v)), (build.__name__, k)
+    # one part: the segments are the non-empty rows, in order
+    one = oracle.hybrid_format(row_ptr, col_idx, 10, 1)
+    assert one["perm"].tolist() == list(range(10)) and one["seg_row"].tolist() == [0, 2, 3]
+    assert one["seg_ptr"].tolist() == [0, 5, 7, 10] and one["row_seg_ptr"].tolist() == [0, 1, 1, 2, 3]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_hybrid_format_bruteforce(seed):
+    """The stable-sort construction equals the loop construction on small
+    patterns: unsorted and duplicate columns, empty rows, fewer columns than
+    parts, no entries."""
+    rng = np.random.default_rng(760 + seed)
+    n_cols = [1, 3, 7, 20, 33, 64, 5, 40][seed]
+    csr = random_small_graph(25, n_cols, 0.0 if seed == 6 else 0.3, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
+    for P in (1, 2, 4, 8, 16, 32):
+        a = oracle.hybrid_format_loops(csr.row_ptr, csr.col_idx, n_cols, P)
+        b = oracle.hybrid_format(csr.row_ptr, csr.col_idx, n_cols, P)
+        for k in a:
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), (P, k)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hybrid_format_invariants(seed):
+    rng = np.random.default_rng(770 + seed)
+    csr = random_small_graph(300, 500, 0.05, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
+    rows = csr.row_of_edge()
+    for P in (2, 8, 32):
+        h = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, P)
+        perm, sp, sr, spart = h["perm"], h["seg_ptr"], h["seg_row"], h["seg_part"]
+        assert h["part_cols"] == -(-500 // P)
+        assert sorted(perm.tolist()) == list(range(csr.nnz))  # a permutation of the entries
+        assert np.array_equal(h["col_idx"], csr.col_idx[perm])
+        assert sp[0] == 0 and sp[-1] == csr.nnz and np.all(np.diff(sp) > 0)  # no empty segment
+        for s in range(len(sr)):
+            seg = perm[sp[s]:sp[s + 1]]
+            assert np.all(rows[seg] == sr[s]) and np.all(csr.col_idx[seg] // h["part_cols"] == spart[s])
+            assert np.all(np.diff(seg) > 0)  # original order inside a segment
+        key = spart * csr.n_rows + sr
+        assert np.all(np.diff(key) > 0)  # ordered by (part, row), each pair once
+        # every row's entries are its segments, by part
+        for r in range(csr.n_rows):
+            mine = h["row_seg"][h["row_seg_ptr"][r]:h["row_seg_ptr"][r + 1]]
+            assert np.all(sr[mine] == r) and np.all(np.diff(spart[mine]) > 0)
+            got = np.concatenate([perm[sp[s]:sp[s + 1]] for s in mine]) if len(mine) else np.zeros(0, int)
+            e = np.arange(csr.row_ptr[r], csr.row_ptr[r + 1])
+            assert np.array_equal(got, e[np.argsort(csr.col_idx[e] // h["part_cols"], kind="stable")])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hybrid_product_identity(oracle_lib, seed):
+    """The product summed segment by segment (each row's segments in part
+    order) is the dense product: the format only re-associates the sum."""
+    rng = np.random.default_rng(780 + seed)
+    csr = random_small_graph(40, 60, 0.2, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32).astype(np.float64)  # the oracle reads fp32 values
+    X = rng.standard_normal((60, 5)).astype(np.float32)
+    h = oracle.hybrid_format(csr.row_ptr, csr.col_idx, 60, 4)
+    ref, mag = oracle_lib.spmm(csr.row_ptr, csr.col_idx, vals, X)
+    part_rows = np.zeros((len(h["seg_row"]), 5))
+    for s in range(len(h["seg_row"])):
+        for k in range(h["seg_ptr"][s], h["seg_ptr"][s + 1]):
+            part_rows[s] += vals[h["perm"][k]] * X[h["col_idx"][k]].astype(np.float64)
+    Y = np.zeros((csr.n_rows, 5))
+    for r in range(csr.n_rows):
+        for s in h["row_seg"][h["row_seg_ptr"][r]:h["row_seg_ptr"][r + 1]]:
+            Y[r] += part_rows[s]
+    assert rel_err(Y, ref, mag) < 1e-12
+    assert rel_err(Y, dense_of(csr, vals) @ X.astype(np.float64), mag) < 1e-12
