@@ -144,6 +144,83 @@ def test_c4_sddmm_full(K):
 
 
 # ---------------------------------------------------------------------------
+# column-part segment format, in the launch configuration the benchmark times:
+# the part count of the library's rule and the selected segment schedule
+# ---------------------------------------------------------------------------
+
+def planned_format(op, name, rp, ci, a, b):
+    csr = pattern(name)
+    p, _ = csa.make_problem(op, rp, ci, a, b)
+    counts, sums, mx = csa.degree_histogram(rp)
+    P = csa.hybrid_parts(p, counts + sums + [mx])
+    assert P > 1, (name, op, b.shape)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+    if op == "spmm":
+        a = None if a is None else csa.hybrid_values(h, a)
+    s, _ = csa.hybrid_select(h, op, a, b)
+    return h, a, s
+
+
+@pytest.mark.parametrize("F", [32, 64, 128])
+def test_c2_spmm_format(F):
+    csr = pattern("c2")
+    rp, ci = pattern_dev("c2")
+    vals = configs.config_dense("c2", "vals", csr)
+    X = configs.config_dense("c2", "X", csr, F)
+    vd, Xd = dev(vals), dev(X)
+    h, hv, s = planned_format("spmm", "c2", rp, ci, vd, Xd)
+    assert h.parts == {32: 8, 64: 16, 128: 32}[F]
+    # the format at full size: a permutation, segments in (part, row) order
+    assert torch.equal(torch.sort(h.perm.long())[0], torch.arange(csr.nnz, device="cuda"))
+    assert bool((h.seg_ptr[1:] > h.seg_ptr[:-1]).all()) and int(h.seg_ptr[-1]) == csr.nnz
+    assert int(h.row_seg_ptr[-1]) == h.n_seg
+    Y = csa.hybrid_spmm(h, hv, Xd, schedule=s)
+    rows = sample_rows(csr, seed=F)
+    Ys = Y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref, mag = oracle_rows(lambda r: oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, r, r + 1), rows)
+    print(f"c2 format F={F}: P={h.parts} {s} max err {assert_close(Ys, ref, mag, TOL_F32, 'c2 format'):.2e}")
+    ones = torch.ones((csr.n_cols, F), device="cuda")
+    Y1 = csa.hybrid_spmm(h, hv, ones, schedule=s)
+    live = torch.from_numpy(csr.degrees() > 0).cuda()
+    assert torch.max(torch.abs(Y1[live] - 1.0)).item() < 1e-5
+    assert bool((Y1[~live] == 0).all())
+
+
+def test_c4_format_bit_exact():
+    csr = pattern("c4")
+    rp, ci = pattern_dev("c4")
+    h = csa.hybrid_format(rp, ci, csr.n_cols, 8)
+    want = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, 8)
+    assert h.n_seg == len(want["seg_row"])
+    for k in ("perm", "col_idx", "seg_ptr", "seg_row", "row_seg_ptr", "row_seg"):
+        assert np.array_equal(getattr(h, k).cpu().numpy(), want[k]), k
+
+
+@pytest.mark.parametrize("F", [4, 8, 16, 32])
+def test_c4_spmm_format_full(F):
+    csr = pattern("c4")
+    rp, ci = pattern_dev("c4")
+    vals = configs.config_dense("c4", "vals", csr)
+    X = configs.config_dense("c4", "X", csr, F)
+    h, hv, s = planned_format("spmm", "c4", rp, ci, dev(vals), dev(X))
+    Y = csa.hybrid_spmm(h, hv, dev(X), schedule=s).cpu().numpy()
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=16)
+    print(f"c4 format spmm F={F}: P={h.parts} {s} max err {assert_close(Y, ref, mag, TOL_F32, 'c4 format'):.2e}")
+
+
+@pytest.mark.parametrize("K", [4, 8, 16])
+def test_c4_sddmm_format_full(K):
+    csr = pattern("c4")
+    rp, ci = pattern_dev("c4")
+    U = configs.config_dense("c4", "U", csr, K)
+    V = configs.config_dense("c4", "V", csr, K)
+    h, Ud, s = planned_format("sddmm", "c4", rp, ci, dev(U), dev(V))
+    out = csa.hybrid_sddmm(h, Ud, dev(V), schedule=s).cpu().numpy()
+    ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, threads=16)
+    print(f"c4 format sddmm K={K}: P={h.parts} {s} max err {assert_close(out, ref, mag, TOL_F32, 'c4 fmt'):.2e}")
+
+
+# ---------------------------------------------------------------------------
 # c5: 8-head bf16 attention on the c3 graph and on the window pattern
 # ---------------------------------------------------------------------------
 
