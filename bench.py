@@ -298,8 +298,11 @@ def committed_traffic(config, call, schedule):
     if isinstance(recs, dict):
         recs = [recs]
     sd = schedule.as_dict()
+    parts = call.fmt["parts"] if call.fmt is not None else 1
     for rec in recs:
         if rec.get("call") != call.name or any(sd.get(k) != v for k, v in rec["schedule"].items()):
+            continue
+        if rec.get("format_parts", 1) != parts:  # counters of the plain pattern, or of a format
             continue
         h = hashlib.sha256()
         for src in rec["sources"]:
