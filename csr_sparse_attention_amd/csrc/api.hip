@@ -751,7 +751,7 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
 
 static bool valid_parts(int32_t parts)
 {
-    return parts == 1 || parts == 2 || parts == 4 || parts == 8 || parts == 16 || parts == 32;
+    return parts >= 1 && parts <= 256 && (parts & (parts - 1)) == 0;
 }
 
 int csr_hybrid_capacity(int64_t n_rows, int64_t nnz, int32_t parts, int64_t* seg_cap)
@@ -783,7 +783,7 @@ static int check_hybrid(csr_context_t ctx, const csr_hybrid_t* h, bool built)
     if (!h) return CSR_ERR_NULL;
     int rc = transpose_args(h->n_rows, h->n_cols, h->nnz);
     if (rc != CSR_OK) return set_err(ctx, rc, "bad format sizes");
-    if (!valid_parts(h->parts)) return set_err(ctx, CSR_ERR_SHAPE, "parts must be 1, 2, 4, 8, 16 or 32");
+    if (!valid_parts(h->parts)) return set_err(ctx, CSR_ERR_SHAPE, "parts must be a power of two from 1 to 256");
     int64_t cap = 0;
     (void)csr_hybrid_capacity(h->n_rows, h->nnz, h->parts, &cap);
     if (h->seg_cap < cap) return set_err(ctx, CSR_ERR_WORKSPACE, "segment capacity below min(nnz, n_rows * parts)");

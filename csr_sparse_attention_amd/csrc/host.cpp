@@ -401,30 +401,84 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
     return t;
 }
 
-// Rule of the column-part segment format, from measurements on MI355X (two
-// graphs, widths 4 to 128): the best part count puts about 4 MiB of the
-// gathered matrix in each part, the L2 of one XCD, so P is the power of two
-// nearest to (gathered bytes / 4 MiB).  The format pays when that gives at
-// least 4 parts and at most 32 (beyond 32 x 4 MiB a part no longer fits the
-// L2 and the segments' partial rows cost more than the gathers save), for
-// SpMM at any width and for SDDMM with rows of at most 16 floats (at wider
-// rows the per-entry output scatter cancels the gain), and when non-empty
-// rows hold at least 8 entries on average (shorter rows make about one
-// segment per entry: a guard, not measured).
+// Expected number of non-empty segments with P column parts: a row of
+// degree d whose columns are spread uniformly meets P (1 - (1 - 1/P)^d)
+// parts; summed over the degree histogram at each bucket's mean degree
+// (without a histogram: every row at the mean degree).
+static double expected_segments(const csr_problem_t& p, const int64_t* hist, int P)
+{
+    const double q = 1.0 - 1.0 / P;
+    if (!hist) {
+        const double d = p.n_rows > 0 ? (double)p.nnz / p.n_rows : 0.0;
+        return p.n_rows * P * (1.0 - std::pow(q, d));
+    }
+    double s = 0.0;
+    for (int b = 1; b < 33; ++b) {
+        if (hist[b] <= 0) continue;
+        const double d = (double)hist[33 + b] / hist[b];
+        s += hist[b] * P * (1.0 - std::pow(q, d));
+    }
+    return s;
+}
+
+// Time (ms) per GB of gathered rows when they come from a slice of s bytes
+// of the dense operand, measured on MI355X (c2 SpMM, F = 32 to 602, over the
+// format at 4 to 256 parts): 0.070 while a slice fits one XCD's L2 (4 MiB),
+// rising with log2 of the slice through 0.0855 (8 MiB), 0.109 (16 MiB) and
+// 0.125 (32 MiB) to the rate of gathers spread over the whole operand,
+// 0.137, at 64 MiB and beyond.
+static double gather_ms_per_gb(double s)
+{
+    static const double pts[5][2] = {{4, 0.070}, {8, 0.0855}, {16, 0.1087}, {32, 0.125}, {64, 0.137}};
+    const double mib = s / (1 << 20);
+    if (mib <= pts[0][0]) return pts[0][1];
+    for (int i = 0; i < 4; ++i) {
+        if (mib <= pts[i + 1][0]) {
+            const double x = std::log2(mib / pts[i][0]);  // 0 .. 1 between two points
+            return pts[i][1] + (pts[i + 1][1] - pts[i][1]) * x;
+        }
+    }
+    return pts[4][1];
+}
+
+// Column parts of the column-part segment format (1: the plain CSR path).
+// SpMM: a cost model, time(P) = gathered GB x gather_ms_per_gb(slice of
+// n_cols x width x 4 / P bytes) + the segments' partial rows (written and
+// read: expected segments x width x 8 bytes) at 0.35 ms per GB, both
+// measured; a gather moves at least one 64-byte sector.  Parts from 4 to 256
+// with slices of at least 2 MiB are considered, and the best is used when it
+// is estimated at least 5 % faster than the plain path.  SDDMM (no partial
+// rows; rows of at most 16 floats, where the per-entry output scatter does
+// not cancel the gain): the power of two nearest to (gathered bytes / 4 MiB),
+// from 4 to 256, when the expected segments stay under an eighth of the
+// entries.
 int hybrid_parts(const csr_problem_t& p, const int64_t* hist)
 {
     if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return 1;
-    if (p.op == CSR_OP_SDDMM && p.width > 16) return 1;
-    const double gathered = (double)p.n_cols * p.width * 4.0;
-    const double slices = gathered / (4.0 * (1 << 20));
-    if (slices < 2.83 || slices > 45.3) return 1;  // nearest power of two below 4 or above 32
-    int P = 1;
-    while (P < 32 && (double)P * 1.41421356 < slices) P *= 2;
-    if (hist) {
-        const int64_t nonempty = p.n_rows - hist[0];
-        if (nonempty > 0 && p.nnz < 8 * nonempty) return 1;
+    if (p.nnz <= 0 || p.n_cols <= 0 || p.n_rows <= 0) return 1;
+    const double mib = 1 << 20;
+    const double row = p.width * 4.0;
+    const double X = p.n_cols * row;
+    if (p.op == CSR_OP_SDDMM) {
+        if (p.width > 16) return 1;
+        const double slices = X / (4.0 * mib);
+        if (slices < 2.83) return 1;  // nearest power of two below 4
+        int P = 4;
+        while (P < 256 && (double)P * 1.41421356 < slices) P *= 2;
+        return 2.0 * expected_segments(p, hist, P) <= 0.25 * p.nnz ? P : 1;
     }
-    return P;
+    const double G = p.nnz * std::max(row, 64.0) / 1e9;
+    const double plain = G * gather_ms_per_gb(X);
+    double best = plain;
+    int best_p = 1;
+    for (int P = 4; P <= 256 && X / P >= 2.0 * mib; P *= 2) {
+        const double t = G * gather_ms_per_gb(X / P) + 0.35 * expected_segments(p, hist, P) * p.width * 8.0 / 1e9;
+        if (t < best) {
+            best = t;
+            best_p = P;
+        }
+    }
+    return best < 0.95 * plain ? best_p : 1;
 }
 
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev)

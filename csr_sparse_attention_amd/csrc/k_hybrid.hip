@@ -5,11 +5,11 @@
 // log2(P) bits), which groups them by (part, row) with each group in its
 // original order, since the CSR entries are already in row order.  A
 // segment starts wherever (part, row) changes; segment indices come from an
-// inclusive scan of those start flags.  Each row's non-empty parts are
-// recorded as a bit mask (an atomic OR: the resulting mask does not depend
-// on the order of the ORs), its segment count is the mask's population count,
-// and a segment's slot in its row's list is the number of lower parts set
-// in the mask.  Every step is deterministic.
+// inclusive scan of those start flags.  Each row's segment count (integer
+// atomic adds: the counts do not depend on their order) gives the row's
+// slots by an exclusive scan, and a stable radix sort of the segments by row
+// lists each row's segments in increasing index, i.e. part, order.  Every
+// step is deterministic.
 #include <algorithm>
 
 #include <rocprim/device/device_radix_sort.hpp>
@@ -30,11 +30,12 @@ unsigned grid_for_n(int64_t n)
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int part_bits(int32_t parts)
+// bits of a sort key below n (at least 1)
+int key_bits(int64_t n)
 {
-    int b = 0;
-    while ((1 << b) < parts) ++b;
-    return b < 1 ? 1 : b;
+    int b = 1;
+    while (b < 31 && ((int64_t)1 << b) < n) ++b;
+    return b;
 }
 
 #define CSR_GRID_STRIDE(i, n) \
@@ -82,9 +83,9 @@ __global__ void k_seg_flags(const int32_t* fpart, const int32_t* frow, int64_t n
     flags[k] = (k == 0 || fpart[k] != fpart[k - 1] || frow[k] != frow[k - 1]) ? 1 : 0;
 }
 
-// segment starts and rows; each row's mask of non-empty parts
-__global__ void k_seg_fill(const int32_t* flags, const int32_t* sid, const int32_t* fpart, const int32_t* frow,
-                           int64_t nnz, int32_t* seg_ptr, int32_t* seg_row, uint32_t* mask)
+// segment starts and rows; each row's segment count (cnt zeroed before)
+__global__ void k_seg_fill(const int32_t* flags, const int32_t* sid, const int32_t* frow, int64_t nnz,
+                           int32_t* seg_ptr, int32_t* seg_row, int32_t* cnt)
 {
     CSR_GRID_STRIDE(k, nnz)
     {
@@ -92,28 +93,9 @@ __global__ void k_seg_fill(const int32_t* flags, const int32_t* sid, const int32
             const int32_t s = sid[k] - 1;
             seg_ptr[s] = (int32_t)k;
             seg_row[s] = frow[k];
-            atomicOr(&mask[frow[k]], 1u << fpart[k]);
+            atomicAdd(&cnt[frow[k]], 1);
         }
         if (k == nnz - 1) seg_ptr[sid[k]] = (int32_t)nnz;
-    }
-}
-
-// segments per row (cnt has n_rows + 1 slots, the last one 0 for the scan)
-__global__ void k_mask_count(const uint32_t* mask, int64_t n_rows, int32_t* cnt)
-{
-    CSR_GRID_STRIDE(r, n_rows + 1) cnt[r] = (r < n_rows) ? __popc(mask[r]) : 0;
-}
-
-// each segment into its row's list: slot = segments of the row in lower parts
-__global__ void k_seg_place(const int32_t* seg_ptr, const int32_t* seg_row, const int32_t* fpart,
-                            const uint32_t* mask, const int32_t* row_seg_ptr, int64_t n_seg, int32_t* row_seg)
-{
-    CSR_GRID_STRIDE(s, n_seg)
-    {
-        const int32_t r = seg_row[s];
-        const int32_t p = fpart[seg_ptr[s]];
-        const uint32_t below = mask[r] & ((1u << p) - 1u);
-        row_seg[row_seg_ptr[r] + __popc(below)] = (int32_t)s;
     }
 }
 
@@ -131,19 +113,23 @@ __global__ void k_hyb_reduce(float* Y, int64_t ldy, const float* part_rows, int3
     }
 }
 
-// Workspace regions: A (parts, then start flags), B (entry indices, then
-// format rows), C (sorted parts), D (COO rows, then segment ids), masks,
-// counts, and the sort / scan temporary storage.
+// Workspace regions: A (parts, then start flags, then segment indices), B
+// (entry indices, then format rows, then sorted segment rows), C (sorted
+// parts), D (COO rows, then segment ids), per-row counts, and the sorts' /
+// scans' temporary storage.
 struct HybLayout {
-    size_t a, b, c, d, mask, cnt, temp, temp_bytes, total;
+    size_t a, b, c, d, cnt, temp, temp_bytes, total;
 };
 
 static hipError_t hyb_layout(int64_t n_rows, int64_t nnz, int32_t parts, HybLayout* L)
 {
-    size_t sort_t = 0, iscan_t = 0, escan_t = 0;
+    size_t sort_t = 0, row_sort_t = 0, iscan_t = 0, escan_t = 0;
     const unsigned n = (unsigned)(nnz > 0 ? nnz : 1);
     hipError_t e = rocprim::radix_sort_pairs(nullptr, sort_t, (const int32_t*)nullptr, (int32_t*)nullptr,
-                                             (const int32_t*)nullptr, (int32_t*)nullptr, n, 0, part_bits(parts));
+                                             (const int32_t*)nullptr, (int32_t*)nullptr, n, 0, key_bits(parts));
+    if (e != hipSuccess) return e;
+    e = rocprim::radix_sort_pairs(nullptr, row_sort_t, (const int32_t*)nullptr, (int32_t*)nullptr,
+                                  (const int32_t*)nullptr, (int32_t*)nullptr, n, 0, key_bits(n_rows));
     if (e != hipSuccess) return e;
     e = rocprim::inclusive_scan(nullptr, iscan_t, (const int32_t*)nullptr, (int32_t*)nullptr, (size_t)n,
                                 rocprim::plus<int32_t>());
@@ -156,10 +142,9 @@ static hipError_t hyb_layout(int64_t n_rows, int64_t nnz, int32_t parts, HybLayo
     L->b = L->a + ent;
     L->c = L->b + ent;
     L->d = L->c + ent;
-    L->mask = L->d + ent;
-    L->cnt = L->mask + rows;
+    L->cnt = L->d + ent;
     L->temp = L->cnt + rows;
-    L->temp_bytes = up256(std::max(sort_t, std::max(iscan_t, escan_t)));
+    L->temp_bytes = up256(std::max(std::max(sort_t, row_sort_t), std::max(iscan_t, escan_t)));
     L->total = L->temp + L->temp_bytes;
     return hipSuccess;
 }
@@ -198,7 +183,7 @@ hipError_t launch_hybrid_build_sort(const int32_t* row_ptr, const int32_t* col_i
     hipLaunchKernelGGL(k_iota_i32, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, B, nnz);
     CSR_TRY(hipGetLastError());
     CSR_TRY(rocprim::radix_sort_pairs(temp, temp_bytes, (const int32_t*)A, C, (const int32_t*)B, perm, (unsigned)nnz,
-                                      0, part_bits(parts), s));
+                                      0, key_bits(parts), s));
     CSR_TRY(launch_coo_rows(row_ptr, n_rows, D, nnz, s));
     hipLaunchKernelGGL(k_hyb_gather, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, (const int32_t*)perm, col_idx,
                        (const int32_t*)D, nnz, fcol, B);
@@ -220,35 +205,32 @@ hipError_t launch_hybrid_build_segments(int64_t n_rows, int64_t nnz, int32_t par
     HybLayout L;
     CSR_TRY(hyb_layout(n_rows, nnz, parts, &L));
     char* w = static_cast<char*>(ws);
-    const int32_t* A = reinterpret_cast<const int32_t*>(w + L.a);  // start flags
-    const int32_t* B = reinterpret_cast<const int32_t*>(w + L.b);  // format rows
-    const int32_t* C = reinterpret_cast<const int32_t*>(w + L.c);  // sorted parts
+    int32_t* A = reinterpret_cast<int32_t*>(w + L.a);  // start flags, then segment indices
+    int32_t* B = reinterpret_cast<int32_t*>(w + L.b);  // format rows, then sorted segment rows
     const int32_t* D = reinterpret_cast<const int32_t*>(w + L.d);  // segment ids (1-based)
-    uint32_t* mask = reinterpret_cast<uint32_t*>(w + L.mask);
     int32_t* cnt = reinterpret_cast<int32_t*>(w + L.cnt);
     void* temp = w + L.temp;
     size_t temp_bytes = L.temp_bytes;
-    hipLaunchKernelGGL(k_fill_i32, dim3(grid_for_n(n_rows)), dim3(CSR_BLOCK), 0, s, reinterpret_cast<int32_t*>(mask),
-                       n_rows, 0);
+    hipLaunchKernelGGL(k_fill_i32, dim3(grid_for_n(n_rows + 1)), dim3(CSR_BLOCK), 0, s, cnt, n_rows + 1, 0);
     CSR_TRY(hipGetLastError());
     if (nnz == 0) {
         hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(CSR_BLOCK), 0, s, seg_ptr, (int64_t)1, 0);
         CSR_TRY(hipGetLastError());
     } else {
-        hipLaunchKernelGGL(k_seg_fill, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, A, D, C, B, nnz, seg_ptr,
-                           seg_row, mask);
+        hipLaunchKernelGGL(k_seg_fill, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, (const int32_t*)A, D,
+                           (const int32_t*)B, nnz, seg_ptr, seg_row, cnt);
         CSR_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL(k_mask_count, dim3(grid_for_n(n_rows + 1)), dim3(CSR_BLOCK), 0, s, (const uint32_t*)mask,
-                       n_rows, cnt);
-    CSR_TRY(hipGetLastError());
     CSR_TRY(rocprim::exclusive_scan(temp, temp_bytes, (const int32_t*)cnt, row_seg_ptr, (int32_t)0,
                                     (size_t)(n_rows + 1), rocprim::plus<int32_t>(), s));
     if (n_seg > 0) {
-        hipLaunchKernelGGL(k_seg_place, dim3(grid_for_n(n_seg)), dim3(CSR_BLOCK), 0, s, (const int32_t*)seg_ptr,
-                           (const int32_t*)seg_row, C, (const uint32_t*)mask, (const int32_t*)row_seg_ptr, n_seg,
-                           row_seg);
+        // each row's segments in part order: a stable sort of the segment
+        // indices by row (segments are already in (part, row) order)
+        hipLaunchKernelGGL(k_iota_i32, dim3(grid_for_n(n_seg)), dim3(CSR_BLOCK), 0, s, A, n_seg);
         CSR_TRY(hipGetLastError());
+        temp_bytes = L.temp_bytes;
+        CSR_TRY(rocprim::radix_sort_pairs(temp, temp_bytes, (const int32_t*)seg_row, B, (const int32_t*)A, row_seg,
+                                          (unsigned)n_seg, 0, key_bits(n_rows), s));
     }
     (void)parts;
     return hipSuccess;

@@ -484,7 +484,7 @@ def hybrid_parts(problem: CsrProblem, histogram=None) -> int:
 
 def hybrid_format(row_ptr, col_idx, n_cols: int, parts: int, *, ctx: Optional[Context] = None) -> Hybrid:
     """Builds the column-part segment format of (row_ptr, col_idx) with
-    ``parts`` column parts (1, 2, 4, 8, 16 or 32)."""
+    ``parts`` column parts (a power of two from 1 to 256)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)

@@ -334,7 +334,7 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
  * ------------------------------------------------------------------------- */
 typedef struct csr_hybrid_s {
     int64_t n_rows, n_cols, nnz; /* the pattern's shape (set by the caller) */
-    int32_t parts;               /* P in {1, 2, 4, 8, 16, 32} (set by the caller) */
+    int32_t parts;               /* P: a power of two from 1 to 256 (set by the caller) */
     int32_t part_cols;           /* ceil(n_cols / P) (written by csr_hybrid_build) */
     int64_t seg_cap;             /* capacity of the segment arrays, >= csr_hybrid_capacity (set by the caller) */
     int64_t n_seg;               /* number of segments (written by csr_hybrid_build) */

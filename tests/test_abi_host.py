@@ -238,23 +238,43 @@ def test_host_only_context_refuses_operations():
     ctx.close()
 
 
+def _hist_of_degrees(deg):
+    counts, sums, mx = oracle.degree_histogram(np.concatenate([[0], np.cumsum(deg)]))
+    return np.concatenate([counts, sums, [mx]]).astype(np.int64)
+
+
 def test_hybrid_parts_rule():
-    # about 4 MiB of the gathered matrix per part, 4 to 32 parts
-    def parts(op, n_cols, width, n_rows=100_000, nnz=5_000_000, hist=None):
-        return csa.hybrid_parts(problem(op, n_rows=n_rows, n_cols=n_cols, nnz=nnz, width=width), hist)
+    # measured cost model: gathers from a slice (cheapest at <= 4 MiB per part)
+    # against the segments' partial rows, with the segment count expected from
+    # the degree histogram; the plain path unless 5 % faster
+    from synth import configs, graphs
+
+    def parts(op, deg, n_cols, width, hist=True):
+        p = problem(op, n_rows=len(deg), n_cols=n_cols, nnz=int(np.sum(deg)), width=width)
+        return csa.hybrid_parts(p, _hist_of_degrees(deg) if hist else None)
 
     S, D = _ffi.OP_SPMM, _ffi.OP_SDDMM
-    assert [parts(S, 232_965, F) for F in (32, 64, 128, 602)] == [8, 16, 32, 1]
-    assert [parts(S, 1_000_000, F) for F in (4, 8, 16, 32)] == [4, 8, 16, 32]
-    assert [parts(D, 1_000_000, K) for K in (4, 8, 16, 32)] == [4, 8, 16, 1]
-    assert parts(S, 2_449_029, 100) == 1  # slices far beyond an L2
-    assert parts(S, 100_000, 4) == 1      # 1.5 MiB: fits without the format
-    assert parts(_ffi.OP_ATTENTION, 232_965, 32) == 1
-    # the average non-empty row must hold at least 8 entries
-    hist = np.zeros(67, dtype=np.int64)
-    hist[0] = 60_000  # empty rows
-    assert parts(S, 232_965, 32, nnz=40_000 * 8, hist=hist) == 8
-    assert parts(S, 232_965, 32, nnz=40_000 * 8 - 1, hist=hist) == 1
+    # the power-law graph's degrees (~490 entries per row on average): up to 64 parts at F = 602
+    pl = graphs.powerlaw_degrees(configs.C2_N, configs.C2_GAMMA, configs.C2_KMAX)
+    assert [parts(S, pl, configs.C2_N, F) for F in (32, 64, 128, 602)] == [8, 16, 32, 64]
+    assert [parts(D, pl, configs.C2_N, K) for K in (8, 16, 32)] == [1, 4, 1]  # K = 8: 7.5 MB, fits as it is
+    # log-normal degrees (~50 per row) and a 1 GB operand: the partial rows
+    # would cost more than the gathers save
+    ln = graphs.lognormal_degrees(configs.C3_N, configs.C3_MU, configs.C3_SIGMA)
+    assert [parts(S, ln, configs.C3_N, F) for F in (64, 100, 128)] == [1, 1, 1]
+    # the skew workload's lengths: 30 % empty rows
+    sk = np.zeros(configs.C4_N, dtype=np.int64)
+    sk[:configs.C4_N - configs.C4_EMPTY] = graphs.rank_size_lengths(configs.C4_N - configs.C4_EMPTY, configs.C4_CAP,
+                                                                    configs.C4_NNZ)
+    assert [parts(S, sk, configs.C4_N, F) for F in (4, 8, 16, 32)] == [4, 8, 16, 32]
+    assert [parts(D, sk, configs.C4_N, K) for K in (4, 8, 16, 32)] == [4, 8, 16, 1]
+    # small operand (fits without the format), short rows, other ops
+    assert parts(S, np.full(100_000, 50), 100_000, 4) == 1
+    assert parts(S, np.full(1_000_000, 3), 1_000_000, 32) == 1
+    assert csa.hybrid_parts(problem(_ffi.OP_ATTENTION, n_rows=232_965, n_cols=232_965, nnz=114_600_002, width=32),
+                            None) == 1
+    # without a histogram every row counts at the mean degree (here: long rows, many segments)
+    assert parts(S, pl, configs.C2_N, 128, hist=False) == 16
 
 
 def test_hybrid_capacity_and_host_only_context():
@@ -262,8 +282,9 @@ def test_hybrid_capacity_and_host_only_context():
     n = ctypes.c_int64()
     assert lib.csr_hybrid_capacity(10, 100, 4, ctypes.byref(n)) == 0 and n.value == 40
     assert lib.csr_hybrid_capacity(1000, 100, 32, ctypes.byref(n)) == 0 and n.value == 100
+    assert lib.csr_hybrid_capacity(10, 10_000, 256, ctypes.byref(n)) == 0 and n.value == 2560
     assert lib.csr_hybrid_capacity(0, 0, 1, ctypes.byref(n)) == 0 and n.value == 0
-    for bad in ((10, 100, 3), (10, 100, 64), (10, 100, 0), (-1, 100, 4), (10, 2**31, 4)):
+    for bad in ((10, 100, 3), (10, 100, 512), (10, 100, 0), (10, 100, 96), (-1, 100, 4), (10, 2**31, 4)):
         assert lib.csr_hybrid_capacity(*bad, ctypes.byref(n)) == -2
     assert lib.csr_hybrid_capacity(10, 100, 4, None) == -1
     ctx = csa.Context(-1, None)

@@ -734,7 +734,7 @@ def _format_graph(name):
 
 
 @pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges", "empty"])
-@pytest.mark.parametrize("P", [1, 4, 32])
+@pytest.mark.parametrize("P", [1, 4, 32, 256])
 def test_hybrid_format_bit_exact(graph, P):
     csr = _format_graph(graph)
     rp, ci = pattern_dev(csr)
@@ -758,7 +758,7 @@ def test_hybrid_spmm_every_schedule(graph, F):
     ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=oracle.default_threads())
     rp, ci = pattern_dev(csr)
     Xd = dev(X)
-    for P in (2, 8, 32):
+    for P in (2, 8, 32, 128):
         h = csa.hybrid_format(rp, ci, csr.n_cols, P)
         hv = csa.hybrid_values(h, dev(vals))
         p = csa.hybrid_problem(h, "spmm", hv, Xd)
@@ -847,7 +847,7 @@ def test_hybrid_deterministic_and_errors():
     st = torch.cuda.current_stream().cuda_stream
     n = ctypes.c_int64()
     assert lib.csr_hybrid_capacity(10, 100, 3, ctypes.byref(n)) == -2
-    assert lib.csr_hybrid_capacity(10, 100, 64, ctypes.byref(n)) == -2
+    assert lib.csr_hybrid_capacity(10, 100, 512, ctypes.byref(n)) == -2
     assert lib.csr_hybrid_capacity(10, 100, 4, ctypes.byref(n)) == 0 and n.value == 40
     # segment capacity below the bound
     d = _ffi.CsrHybrid.from_buffer_copy(bytes(h.desc))

@@ -575,7 +575,7 @@ def test_hybrid_format_bruteforce(seed):
     rng = np.random.default_rng(760 + seed)
     n_cols = [1, 3, 7, 20, 33, 64, 5, 40][seed]
     csr = random_small_graph(25, n_cols, 0.0 if seed == 6 else 0.3, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
-    for P in (1, 2, 4, 8, 16, 32):
+    for P in (1, 2, 4, 8, 16, 32, 64, 256):
         a = oracle.hybrid_format_loops(csr.row_ptr, csr.col_idx, n_cols, P)
         b = oracle.hybrid_format(csr.row_ptr, csr.col_idx, n_cols, P)
         for k in a:
