@@ -955,9 +955,17 @@ static int hybrid_run(csr_context_t ctx, const csr_hybrid_t* h, const HybridCall
         int rc = run_schedule(ctx, c.p, s, st, maps);
         if (rc != CSR_OK) return rc;
     }
-    if (c.p.op == CSR_OP_SPMM)
-        CSR_HIP(ctx, csrk::launch_hybrid_reduce(Y, ldy, c.part_rows, (int32_t)c.p.width, h->row_seg_ptr, h->row_seg,
+    if (c.p.op == CSR_OP_SPMM) {
+        // lane layout of the sum: the widest access that F, ldy and Y allow
+        // (the partial rows are 256-byte aligned with leading dimension F)
+        const int64_t F = c.p.width;
+        int vec = 4, W = 0, nv = 0;
+        while (vec > 1 && (F % vec || ldy % vec || (uintptr_t)Y % (4 * vec) || !csrh::natural_layout(F, vec, &W, &nv)))
+            vec /= 2;
+        if (vec == 1 && !csrh::natural_layout(F, 1, &W, &nv)) return set_err(ctx, CSR_ERR_SHAPE, "width too large");
+        CSR_HIP(ctx, csrk::launch_hybrid_reduce(vec, nv, W, Y, ldy, c.part_rows, (int32_t)F, h->row_seg_ptr, h->row_seg,
                                                 h->n_rows, st));
+    }
     return CSR_OK;
 }
 

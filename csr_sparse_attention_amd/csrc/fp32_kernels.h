@@ -648,4 +648,46 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_fixup(Fp32Args a)
     }
 }
 
+// Column-part segment format: Y[r] = the sum of row r's segment partial rows
+// in segment (= part) order, +0 for a row without segments.  One lane group
+// per row, laid out as in the row-group mapping (16-byte lane accesses),
+// with 4 partial rows in flight per group; the sum's order is fixed.
+template <int VEC, int NV>
+__global__ __launch_bounds__(CSR_BLOCK) void k_hyb_reduce_rows(float* Y, int64_t ldy, const float* part, int32_t F,
+                                                               int32_t W, const int32_t* row_seg_ptr,
+                                                               const int32_t* row_seg, int64_t n_rows)
+{
+    constexpr int UR = 4;
+    Lanes<VEC, NV> L(W);
+    const int64_t row = ((int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x) / W;
+    if (row >= n_rows) return;  // groups are whole: no group is split by this test
+    const int b = row_seg_ptr[row], e = row_seg_ptr[row + 1];
+    float acc[NV][VEC];
+    zero(acc);
+    for (int k = b; k < e; k += UR) {
+        float x[UR][NV][VEC];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int sg = (k + u < e) ? row_seg[k + u] : -1;
+            const float* src = part + (int64_t)(sg < 0 ? 0 : sg) * F;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (sg >= 0 && L.valid(j, F)) {
+                    vload<VEC>(x[u][j], src + L.off(j));
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) x[u][j][v] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[j][v] += x[u][j][v];
+    }
+    store_row<VEC, NV>(Y + row * ldy, acc, L, F, 1.f);
+}
+
 } // namespace csrk

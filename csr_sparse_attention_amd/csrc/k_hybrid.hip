@@ -1,5 +1,6 @@
-// Column-part segment format: construction, and the sum of a row's segment
-// partial rows after a product over the format.
+// Column-part segment format: construction (the products over it run the
+// plain kernels on the segment pattern; the sum of the partial rows is in
+// fp32_kernels.h).
 //
 // The entries are stably sorted by their column part (a radix sort on
 // log2(P) bits), which groups them by (part, row) with each group in its
@@ -96,20 +97,6 @@ __global__ void k_seg_fill(const int32_t* flags, const int32_t* sid, const int32
             atomicAdd(&cnt[frow[k]], 1);
         }
         if (k == nnz - 1) seg_ptr[sid[k]] = (int32_t)nnz;
-    }
-}
-
-// Y[r][f] = sum over row r's segments (part order) of part_rows[seg][f]; +0 without segments
-__global__ void k_hyb_reduce(float* Y, int64_t ldy, const float* part_rows, int32_t F, const int32_t* row_seg_ptr,
-                             const int32_t* row_seg, int64_t n_rows)
-{
-    CSR_GRID_STRIDE(t, n_rows * F)
-    {
-        const int64_t r = t / F, f = t - r * F;
-        const int32_t b = row_seg_ptr[r], e = row_seg_ptr[r + 1];
-        float acc = 0.f;
-        for (int32_t k = b; k < e; ++k) acc += part_rows[(int64_t)row_seg[k] * F + f];
-        Y[r * ldy + f] = acc;
     }
 }
 
@@ -234,15 +221,6 @@ hipError_t launch_hybrid_build_segments(int64_t n_rows, int64_t nnz, int32_t par
     }
     (void)parts;
     return hipSuccess;
-}
-
-hipError_t launch_hybrid_reduce(float* Y, int64_t ldy, const float* part_rows, int32_t F, const int32_t* row_seg_ptr,
-                                const int32_t* row_seg, int64_t n_rows, hipStream_t s)
-{
-    if (n_rows == 0 || F == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_hyb_reduce, dim3(grid_for_n(n_rows * F)), dim3(CSR_BLOCK), 0, s, Y, ldy, part_rows, F,
-                       row_seg_ptr, row_seg, n_rows);
-    return hipGetLastError();
 }
 
 }  // namespace csrk

@@ -55,7 +55,8 @@ hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows
 
 // column-part segment format (k_hybrid.hip): construction in two steps (the
 // sort, which reads the segment count back into pinned host memory, then the
-// segment arrays), and the sum of each row's segment partial rows
+// segment arrays); and (k_spmm.hip) the sum of each row's segment partial rows
+// with the lane layout (vec, nv, W)
 hipError_t hybrid_build_workspace(int64_t n_rows, int64_t nnz, int32_t parts, size_t* bytes);
 hipError_t launch_hybrid_build_sort(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t nnz,
                                     int32_t parts, int32_t part_cols, int32_t* perm, int32_t* fcol, void* ws,
@@ -63,8 +64,8 @@ hipError_t launch_hybrid_build_sort(const int32_t* row_ptr, const int32_t* col_i
 hipError_t launch_hybrid_build_segments(int64_t n_rows, int64_t nnz, int32_t parts, int64_t n_seg, int32_t* seg_ptr,
                                         int32_t* seg_row, int32_t* row_seg_ptr, int32_t* row_seg, void* ws,
                                         hipStream_t s);
-hipError_t launch_hybrid_reduce(float* Y, int64_t ldy, const float* part_rows, int32_t F, const int32_t* row_seg_ptr,
-                                const int32_t* row_seg, int64_t n_rows, hipStream_t s);
+hipError_t launch_hybrid_reduce(int vec, int nv, int W, float* Y, int64_t ldy, const float* part, int32_t F,
+                                const int32_t* row_seg_ptr, const int32_t* row_seg, int64_t n_rows, hipStream_t s);
 
 // Structure kernels.
 hipError_t launch_fill_i64(int64_t* p, int64_t n, int64_t value, hipStream_t s);
