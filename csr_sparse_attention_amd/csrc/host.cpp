@@ -422,29 +422,30 @@ static double expected_segments(const csr_problem_t& p, const int64_t* hist, int
 }
 
 // Time (ms) per GB of gathered rows when they come from a slice of s bytes
-// of the dense operand, measured on MI355X (c2 SpMM, F = 32 to 602, over the
-// format at 4 to 256 parts): 0.070 while a slice fits one XCD's L2 (4 MiB),
-// rising with log2 of the slice through 0.0855 (8 MiB), 0.109 (16 MiB) and
-// 0.125 (32 MiB) to the rate of gathers spread over the whole operand,
-// 0.137, at 64 MiB and beyond.
+// of the dense operand, measured on MI355X (the power-law graph's SpMM at
+// F = 602 over the format at 4 to 256 parts, less the partial rows' share):
+// 0.070 while a slice fits one XCD's L2 (4 MiB), rising with log2 of the
+// slice through 0.089 (8 MiB), 0.111 (16 MiB), 0.124 (32 MiB) and 0.131
+// (64 MiB) to the rate of gathers spread over an operand far beyond the
+// caches, 0.137, from 256 MiB on.
 static double gather_ms_per_gb(double s)
 {
-    static const double pts[5][2] = {{4, 0.070}, {8, 0.0855}, {16, 0.1087}, {32, 0.125}, {64, 0.137}};
+    static const double pts[6][2] = {{4, 0.070}, {8, 0.0894}, {16, 0.1113}, {32, 0.1235}, {64, 0.1313}, {256, 0.137}};
     const double mib = s / (1 << 20);
     if (mib <= pts[0][0]) return pts[0][1];
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 5; ++i) {
         if (mib <= pts[i + 1][0]) {
-            const double x = std::log2(mib / pts[i][0]);  // 0 .. 1 between two points
+            const double x = std::log2(mib / pts[i][0]) / std::log2(pts[i + 1][0] / pts[i][0]);  // 0 .. 1
             return pts[i][1] + (pts[i + 1][1] - pts[i][1]) * x;
         }
     }
-    return pts[4][1];
+    return pts[5][1];
 }
 
 // Column parts of the column-part segment format (1: the plain CSR path).
 // SpMM: a cost model, time(P) = gathered GB x gather_ms_per_gb(slice of
 // n_cols x width x 4 / P bytes) + the segments' partial rows (written and
-// read: expected segments x width x 8 bytes) at 0.35 ms per GB, both
+// read: expected segments x width x 8 bytes) at 0.118 ms per GB, both
 // measured; a gather moves at least one 64-byte sector.  Parts from 4 to 256
 // with slices of at least 2 MiB are considered, and the best is used when it
 // is estimated at least 5 % faster than the plain path.  SDDMM (no partial
@@ -472,7 +473,7 @@ int hybrid_parts(const csr_problem_t& p, const int64_t* hist)
     double best = plain;
     int best_p = 1;
     for (int P = 4; P <= 256 && X / P >= 2.0 * mib; P *= 2) {
-        const double t = G * gather_ms_per_gb(X / P) + 0.35 * expected_segments(p, hist, P) * p.width * 8.0 / 1e9;
+        const double t = G * gather_ms_per_gb(X / P) + 0.118 * expected_segments(p, hist, P) * p.width * 8.0 / 1e9;
         if (t < best) {
             best = t;
             best_p = P;

@@ -254,9 +254,9 @@ def test_hybrid_parts_rule():
         return csa.hybrid_parts(p, _hist_of_degrees(deg) if hist else None)
 
     S, D = _ffi.OP_SPMM, _ffi.OP_SDDMM
-    # the power-law graph's degrees (~490 entries per row on average): up to 64 parts at F = 602
+    # the power-law graph's degrees (~490 entries per row on average): up to 128 parts at F = 602
     pl = graphs.powerlaw_degrees(configs.C2_N, configs.C2_GAMMA, configs.C2_KMAX)
-    assert [parts(S, pl, configs.C2_N, F) for F in (32, 64, 128, 602)] == [8, 16, 32, 64]
+    assert [parts(S, pl, configs.C2_N, F) for F in (32, 64, 128, 602)] == [8, 16, 32, 128]
     assert [parts(D, pl, configs.C2_N, K) for K in (8, 16, 32)] == [1, 4, 1]  # K = 8: 7.5 MB, fits as it is
     # log-normal degrees (~50 per row) and a 1 GB operand: the partial rows
     # would cost more than the gathers save
@@ -274,7 +274,7 @@ def test_hybrid_parts_rule():
     assert csa.hybrid_parts(problem(_ffi.OP_ATTENTION, n_rows=232_965, n_cols=232_965, nnz=114_600_002, width=32),
                             None) == 1
     # without a histogram every row counts at the mean degree (here: long rows, many segments)
-    assert parts(S, pl, configs.C2_N, 128, hist=False) == 16
+    assert parts(S, pl, configs.C2_N, 602, hist=False) == 64  # 128 with the histogram
 
 
 def test_hybrid_capacity_and_host_only_context():

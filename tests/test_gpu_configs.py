@@ -169,7 +169,7 @@ def test_c2_spmm_format(F):
     X = configs.config_dense("c2", "X", csr, F)
     vd, Xd = dev(vals), dev(X)
     h, hv, s = planned_format("spmm", "c2", rp, ci, vd, Xd)
-    assert h.parts == {32: 8, 64: 16, 128: 32, 602: 64}[F]
+    assert h.parts == {32: 8, 64: 16, 128: 32, 602: 128}[F]
     # the format at full size: a permutation, segments in (part, row) order
     assert torch.equal(torch.sort(h.perm.long())[0], torch.arange(csr.nnz, device="cuda"))
     assert bool((h.seg_ptr[1:] > h.seg_ptr[:-1]).all()) and int(h.seg_ptr[-1]) == csr.nnz
