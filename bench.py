@@ -719,6 +719,11 @@ def main():
            if getattr(build_workload, "transpose_ms", None) is not None else {}),
     }
     result["roofline"]["frac_of_measured_copy"] = round(achieved / stream_ref["copy_GB_s"], 4)
+    if result["roofline"]["traffic"]:
+        # the physical rate: counted L2-to-memory bytes per launch over the launch time
+        rate = result["roofline"]["traffic"] / (dom_ms * 1e-3) / 1e9
+        result["roofline"]["traffic_GB_s"] = round(rate, 1)
+        result["roofline"]["traffic_frac"] = round(rate / HBM_PEAK_GBS, 4)
     if not args.no_study:
         print("[bench] selector study: every candidate schedule of every call", file=sys.stderr, flush=True)
         result["selector"] = selector_study(calls, torch, csa, formats)
