@@ -145,6 +145,7 @@ int env_int(const char* name, int dflt)
 struct RowMaps {
     const int32_t* u_row;
     const int32_t* out_idx;
+    int32_t stream_y;  // SpMM: output rows stored non-temporally (the format's partial rows)
 };
 
 int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t& s, hipStream_t st,
@@ -227,6 +228,7 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
     a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
     a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
+    a.stream_y = maps ? maps->stream_y : 0;
     if (p.op == CSR_OP_SDDMM) {
         if (maps) {
             a.u_row = maps->u_row;
@@ -909,12 +911,12 @@ static int hybrid_call(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int
     c->p.a = a;
     c->p.b = b;
     c->p.ld_b = ldb;
-    c->maps = RowMaps{nullptr, nullptr};
+    c->maps = RowMaps{nullptr, nullptr, 1};  // SpMM: the partial rows are read only by the sum
     c->part_rows = nullptr;
     if (op == CSR_OP_SDDMM) {
         c->p.ld_a = lda;
         c->p.out = sddmm_out;
-        c->maps = RowMaps{h->seg_row, h->perm};
+        c->maps = RowMaps{h->seg_row, h->perm, 0};
     }
     size_t inner = 0;
     rc = hybrid_inner_bytes(ctx, c->p, sched, &inner);
@@ -943,7 +945,7 @@ static int hybrid_run(csr_context_t ctx, const csr_hybrid_t* h, const HybridCall
                       float* Y, int64_t ldy)
 {
     hipStream_t st = static_cast<hipStream_t>(c.p.stream);
-    const RowMaps* maps = c.p.op == CSR_OP_SDDMM ? &c.maps : nullptr;
+    const RowMaps* maps = &c.maps;
     if (h->n_seg > 0) {
         csr_schedule_t s;
         if (sched) {
@@ -1027,7 +1029,7 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
             if (signature) *signature = 0;
             return CSR_OK;
         }
-        return select_locked(ctx, c.p, mode, out, signature, c.p.op == CSR_OP_SDDMM ? &c.maps : nullptr);
+        return select_locked(ctx, c.p, mode, out, signature, &c.maps);
     } catch (...) {
         return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
     }

@@ -30,6 +30,7 @@ struct Fp32Args {
     // position); null = the row / entry itself
     const int32_t* u_row;
     const int32_t* out_idx;
+    int32_t stream_y;  // SpMM output rows by non-temporal stores (partial rows of the format)
 };
 
 struct MhaArgs {

@@ -49,6 +49,24 @@ __device__ __forceinline__ void vstore(float* p, const float (&s)[VEC])
     *reinterpret_cast<T*>(p) = v;
 }
 
+// Streamed store (an output row written once and not read again by the
+// kernel): non-temporal, so that it does not push the gathered feature rows
+// out of the caches.
+template <int VEC>
+__device__ __forceinline__ void vstore_stream(float* p, const float (&s)[VEC])
+{
+    typedef float T __attribute__((ext_vector_type(VEC == 1 ? 1 : VEC)));
+    if constexpr (VEC == 1) {
+        __builtin_nontemporal_store(s[0], p);
+    } else if constexpr (VEC == 2) {
+        T v = {s[0], s[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+    } else {
+        T v = {s[0], s[1], s[2], s[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+    }
+}
+
 // Streamed (read-once) loads of the CSR arrays: non-temporal so that they do
 // not push the gathered feature rows out of the caches.
 __device__ __forceinline__ int ld_stream(const int32_t* p) { return __builtin_nontemporal_load(p); }

@@ -130,9 +130,11 @@ __device__ __forceinline__ void seg_softmax_stats(const float* ev, int kb, int k
     }
 }
 
+// stream: non-temporal stores, for rows that are read again only after the
+// kernel (the column-part segment format's partial rows)
 template <int VEC, int NV>
 __device__ __forceinline__ void store_row(float* dst, const float (&acc)[NV][VEC], const Lanes<VEC, NV>& L,
-                                          int F, float mul)
+                                          int F, float mul, bool stream = false)
 {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -140,7 +142,10 @@ __device__ __forceinline__ void store_row(float* dst, const float (&acc)[NV][VEC
             float o[VEC];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) o[v] = acc[j][v] * mul;
-            vstore<VEC>(dst + L.off(j), o);
+            if (stream)
+                vstore_stream<VEC>(dst + L.off(j), o);
+            else
+                vstore<VEC>(dst + L.off(j), o);
         }
     }
 }
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
         if (OP == Op::Attention && e > b)
             store_row_div<VEC, NV>(dst, acc, L, a.F, l);
         else
-            store_row<VEC, NV>(dst, acc, L, a.F, 1.f);  // empty rows: acc == 0
+            store_row<VEC, NV>(dst, acc, L, a.F, 1.f, a.stream_y);  // empty rows: acc == 0
     }
 }
 
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
             if (OP == Op::Attention && re > rs)
                 store_row_div<VEC, NV>(dst, acc, L, a.F, l);
             else
-                store_row<VEC, NV>(dst, acc, L, a.F, 1.f);
+                store_row<VEC, NV>(dst, acc, L, a.F, 1.f, a.stream_y);
         } else {
             const int64_t slot = 2 * chunk + ((i == nend) ? 1 : 0);
             store_row<VEC, NV>(a.carry_val + slot * a.F, acc, L, a.F, 1.f);
@@ -477,14 +482,19 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
     } else {
         // a row's result, written by one lane: final row, or a piece of a split row
         auto emit = [&](int i, const float (&v)[NV][VEC]) {
-            float* dst;
-            if (i < nend && rp[i] >= y0)
-                dst = a.Y + ((int64_t)x0 + i) * a.ldy;
-            else
-                dst = a.carry_val + (2 * chunk + ((i == nend) ? 1 : 0)) * F;
+            const bool to_y = i < nend && rp[i] >= y0;
+            float* dst = to_y ? a.Y + ((int64_t)x0 + i) * a.ldy
+                              : a.carry_val + (2 * chunk + ((i == nend) ? 1 : 0)) * F;
+            const bool stream = a.stream_y && to_y;
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
-                if (j * VEC < F) vstore<VEC>(dst + j * VEC, v[j]);
+            for (int j = 0; j < NV; ++j) {
+                if (j * VEC < F) {
+                    if (stream)
+                        vstore_stream<VEC>(dst + j * VEC, v[j]);
+                    else
+                        vstore<VEC>(dst + j * VEC, v[j]);
+                }
+            }
         };
         // rows without entries in this chunk: zero rows (or zero pieces)
         for (int i = lane; i < nrow; i += CSR_WAVE) {
@@ -629,7 +639,7 @@ __device__ __forceinline__ void fixup_one(const Fp32Args& a, int64_t c, int r)
     if constexpr (OP == Op::Attention)
         store_row_div<VEC, NV>(dst, acc, L, a.F, lsum);
     else
-        store_row<VEC, NV>(dst, acc, L, a.F, 1.f);
+        store_row<VEC, NV>(dst, acc, L, a.F, 1.f, a.stream_y);
 }
 
 template <Op OP, int VEC, int NV>
