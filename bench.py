@@ -81,18 +81,18 @@ class Call:
         return csa.select(self.op, *sel_args, mode=mode, **kw)
 
 
-def format_plan(csa, torch, c, P, cache):
+def format_plan(csa, torch, c, P, cache, whole_below=0):
     """Builds (once per pattern and part count) the column-part segment format
     of call c and the closures that run and select over it; SpMM edge values
     are moved into the format's order once, here (they are constant across
     steps).  Returns the plan dict with the one-time costs in ms."""
     rp, ci = c.args[0], c.args[1]
     dense = c.args[3] if c.op == "spmm" else c.args[3]
-    key = (rp.data_ptr(), ci.data_ptr(), P)
+    key = (rp.data_ptr(), ci.data_ptr(), P, whole_below)
     if key not in cache:
         torch.cuda.synchronize()
         t = time.perf_counter()
-        h = csa.hybrid_format(rp, ci, dense.shape[0], P)
+        h = csa.hybrid_format(rp, ci, dense.shape[0], P, whole_below=whole_below)
         torch.cuda.synchronize()
         cache[key] = (h, (time.perf_counter() - t) * 1e3)
     h, build_ms = cache[key]
@@ -113,23 +113,24 @@ def format_plan(csa, torch, c, P, cache):
         run = lambda s: csa.hybrid_sddmm(h, U, V, out=out, schedule=s)  # noqa: E731
         select = lambda mode: csa.hybrid_select(h, "sddmm", U, V, mode=mode, out=out)  # noqa: E731
         a, b = U, V
-    return {"h": h, "parts": P, "run": run, "select": select, "operands": (a, b), "build_ms": build_ms,
-            "values_ms": values_ms}
+    return {"h": h, "parts": P, "whole_below": whole_below, "run": run, "select": select, "operands": (a, b),
+            "build_ms": build_ms, "values_ms": values_ms}
 
 
 def apply_formats(calls, csa, torch):
-    """Per SpMM / SDDMM call, asks the library's rule for the column parts of
-    the column-part segment format (csr_hybrid_parts: 1 = plain CSR) and plans
-    the call over the format when it proposes one."""
+    """Per SpMM / SDDMM call, asks the library's cost model for the plan of
+    the column-part segment format (csr_hybrid_plan: parts, 1 = plain CSR,
+    and the whole-row threshold) and plans the call over the format when it
+    proposes one."""
     cache = {}
     for c in calls:
         if c.op not in ("spmm", "sddmm"):
             continue
         p, _ = csa.make_problem(c.op, *c.args, out=c.kwargs.get("out"))
         counts, sums, mx = csa.degree_histogram(c.args[0])
-        P = csa.hybrid_parts(p, counts + sums + [mx])
+        P, T = csa.hybrid_plan(p, counts + sums + [mx])
         if P > 1:
-            c.fmt = format_plan(csa, torch, c, P, cache)
+            c.fmt = format_plan(csa, torch, c, P, cache, T)
     return cache
 
 
@@ -299,10 +300,11 @@ def committed_traffic(config, call, schedule):
         recs = [recs]
     sd = schedule.as_dict()
     parts = call.fmt["parts"] if call.fmt is not None else 1
+    whole = call.fmt["whole_below"] if call.fmt is not None else 0
     for rec in recs:
         if rec.get("call") != call.name or any(sd.get(k) != v for k, v in rec["schedule"].items()):
             continue
-        if rec.get("format_parts", 1) != parts:  # counters of the plain pattern, or of a format
+        if rec.get("format_parts", 1) != parts or rec.get("whole_below", 0) != whole:  # another pattern or format
             continue
         h = hashlib.sha256()
         for src in rec["sources"]:
@@ -347,19 +349,24 @@ def selector_study(calls, torch, csa, formats, rounds=5, per_round=3):
             h = c.fmt["h"]
             hp = csa.hybrid_problem(h, c.op, *c.fmt["operands"])
             sc, ss, smx = csa.degree_histogram(h.seg_ptr)
-            cands += [({"format_parts": c.fmt["parts"], **s.as_dict()}, lambda s=s: c.fmt["run"](s))
-                      for s in csa.candidates(hp, sc + ss + [smx])]
-        selected = {"format_parts": c.fmt["parts"] if c.fmt is not None else 1, **c.schedule.as_dict()}
+            cands += [({"format_parts": c.fmt["parts"], "whole_below": c.fmt["whole_below"], **s.as_dict()},
+                       lambda s=s: c.fmt["run"](s)) for s in csa.candidates(hp, sc + ss + [smx])]
+            selected = {"format_parts": c.fmt["parts"], "whole_below": c.fmt["whole_below"], **c.schedule.as_dict()}
+        else:
+            selected = {"format_parts": 1, **c.schedule.as_dict()}
         n_cand = len(cands)
         if selected not in [lab for lab, _ in cands]:
             cands.append((selected, lambda: c.run()))
         if c.op in ("spmm", "sddmm"):
             P0 = c.fmt["parts"] if c.fmt is not None else 1
-            for P in ([P0 // 2, P0 * 2] if P0 > 1 else [4, 16]):
-                if 2 <= P <= 32:
-                    plan = format_plan(csa, torch, c, P, formats)
+            T0 = c.fmt["whole_below"] if c.fmt is not None else 0
+            alts = [(P0 // 2, T0), (P0 * 2, T0)] + ([(P0, 0)] if T0 > 0 else []) if P0 > 1 else [(4, 0), (16, 0)]
+            for P, T in alts:
+                if 2 <= P <= 256:
+                    plan = format_plan(csa, torch, c, P, formats, T)
                     s_alt, _ = plan["select"]("auto")
-                    cands.append(({"format_parts": P, **s_alt.as_dict()}, lambda plan=plan, s=s_alt: plan["run"](s)))
+                    cands.append(({"format_parts": P, "whole_below": T, **s_alt.as_dict()},
+                                  lambda plan=plan, s=s_alt: plan["run"](s)))
                     n_cand += 1
         labels = [lab for lab, _ in cands]
         times = [[] for _ in cands]
@@ -607,8 +614,9 @@ def main():
     formats = {} if args.no_format else apply_formats(calls, csa, torch)
     for c in calls:
         if c.fmt is not None:
-            print(f"[bench] {c.name}: column-part segment format, {c.fmt['parts']} parts, {c.fmt['h'].n_seg} "
-                  f"segments (built in {c.fmt['build_ms']:.1f} ms)", file=sys.stderr, flush=True)
+            print(f"[bench] {c.name}: column-part segment format, {c.fmt['parts']} parts, rows under "
+                  f"{c.fmt['whole_below']} entries whole, {c.fmt['h'].n_seg} segments (built in "
+                  f"{c.fmt['build_ms']:.1f} ms)", file=sys.stderr, flush=True)
 
     # selection (histogram, signature, cost model, probes) once per call
     sel = {}
@@ -629,7 +637,8 @@ def main():
         sel[c.name] = {"schedule": s.as_dict(), "signature": f"{sig:016x}", "select_ms": round(first * 1e3, 3),
                        "replay_select_ms": round(replay * 1e3, 3)}
         if c.fmt is not None:
-            sel[c.name]["format"] = {"parts": c.fmt["parts"], "segments": c.fmt["h"].n_seg,
+            sel[c.name]["format"] = {"parts": c.fmt["parts"], "whole_below": c.fmt["whole_below"],
+                                     "segments": c.fmt["h"].n_seg,
                                      "build_ms": round(c.fmt["build_ms"], 3),
                                      "values_to_format_order_ms": round(c.fmt["values_ms"], 3)}
         print(f"[bench] {c.name}: {s} select {first * 1e3:.1f} ms", file=sys.stderr, flush=True)

@@ -44,6 +44,7 @@ from .ops import (  # noqa: E402,F401
     gather_values,
     hybrid_format,
     hybrid_parts,
+    hybrid_plan,
     hybrid_problem,
     hybrid_sddmm,
     hybrid_select,

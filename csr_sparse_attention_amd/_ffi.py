@@ -34,7 +34,7 @@ EXPORTS = (
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
-    "csr_hybrid_parts", "csr_hybrid_capacity", "csr_hybrid_build_workspace_size", "csr_hybrid_build", "csr_hybrid_workspace_size",
+    "csr_hybrid_plan", "csr_hybrid_parts", "csr_hybrid_capacity", "csr_hybrid_build_workspace_size", "csr_hybrid_build", "csr_hybrid_workspace_size",
     "csr_hybrid_spmm", "csr_hybrid_sddmm", "csr_hybrid_select",
 )
 
@@ -108,6 +108,8 @@ class CsrHybrid(ctypes.Structure):
         ("nnz", ctypes.c_int64),
         ("parts", ctypes.c_int32),
         ("part_cols", ctypes.c_int32),
+        ("whole_below", ctypes.c_int32),
+        ("reserved_", ctypes.c_int32),
         ("seg_cap", ctypes.c_int64),
         ("n_seg", ctypes.c_int64),
         ("perm", ctypes.c_void_p),
@@ -119,7 +121,7 @@ class CsrHybrid(ctypes.Structure):
     ]
 
 
-assert ctypes.sizeof(CsrHybrid) == 96
+assert ctypes.sizeof(CsrHybrid) == 104
 
 
 class CsrError(RuntimeError):
@@ -170,6 +172,7 @@ def load() -> ctypes.CDLL:
         "csr_degree_histogram": [P, I64, P, ctypes.POINTER(I64), P, SZ, P],
         "csr_merge_path_partition": [P, I64, I64, P, I32, P, P],
         "csr_signature": [P, PP, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_uint64)],
+        "csr_hybrid_plan": [P, PP, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32)],
         "csr_hybrid_parts": [P, PP, ctypes.POINTER(I64), ctypes.POINTER(I32)],
         "csr_hybrid_capacity": [I64, I64, I32, ctypes.POINTER(I64)],
         "csr_hybrid_build_workspace_size": [P, I64, I64, I32, ctypes.POINTER(SZ)],

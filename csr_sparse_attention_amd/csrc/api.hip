@@ -786,6 +786,7 @@ static int check_hybrid(csr_context_t ctx, const csr_hybrid_t* h, bool built)
     int rc = transpose_args(h->n_rows, h->n_cols, h->nnz);
     if (rc != CSR_OK) return set_err(ctx, rc, "bad format sizes");
     if (!valid_parts(h->parts)) return set_err(ctx, CSR_ERR_SHAPE, "parts must be a power of two from 1 to 256");
+    if (h->whole_below < 0 || h->reserved_ != 0) return set_err(ctx, CSR_ERR_SHAPE, "whole_below < 0 or reserved != 0");
     int64_t cap = 0;
     (void)csr_hybrid_capacity(h->n_rows, h->nnz, h->parts, &cap);
     if (h->seg_cap < cap) return set_err(ctx, CSR_ERR_WORKSPACE, "segment capacity below min(nnz, n_rows * parts)");
@@ -829,7 +830,8 @@ int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* c
         if (h->nnz > 0) {
             int32_t* count = reinterpret_cast<int32_t*>(ctx->pinned);
             CSR_HIP(ctx, csrk::launch_hybrid_build_sort(row_ptr, col_idx, h->n_rows, h->nnz, h->parts, part_cols,
-                                                        h->perm, h->col_idx, workspace, ws_bytes, count, st));
+                                                        h->whole_below, h->perm, h->col_idx, workspace, ws_bytes,
+                                                        count, st));
             CSR_HIP(ctx, hipStreamSynchronize(st));
             n_seg = count[0];
             if (n_seg < 1 || n_seg > h->seg_cap) return set_err(ctx, CSR_ERR_INTERNAL, "segment count out of range");
@@ -1061,11 +1063,20 @@ int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule
 
 int csr_hybrid_parts(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, int32_t* parts)
 {
+    return csr_hybrid_plan(ctx, p, histogram, parts, nullptr);
+}
+
+int csr_hybrid_plan(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, int32_t* parts,
+                    int32_t* whole_below)
+{
     if (!p || !parts) return CSR_ERR_NULL;
     std::string why;
     int rc = csrh::check_problem(*p, false, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);
-    *parts = csrh::hybrid_parts(*p, histogram);
+    int P = 1, T = 0;
+    csrh::hybrid_plan(*p, histogram, &P, &T);
+    *parts = P;
+    if (whole_below) *whole_below = T;
     return CSR_OK;
 }
 

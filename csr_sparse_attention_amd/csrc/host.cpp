@@ -442,44 +442,85 @@ static double gather_ms_per_gb(double s)
     return pts[5][1];
 }
 
-// Column parts of the column-part segment format (1: the plain CSR path).
-// SpMM: a cost model, time(P) = gathered GB x gather_ms_per_gb(slice of
-// n_cols x width x 4 / P bytes) + the segments' partial rows (written and
-// read: expected segments x width x 8 bytes) at 0.118 ms per GB, both
-// measured; a gather moves at least one 64-byte sector.  Parts from 4 to 256
-// with slices of at least 2 MiB are considered, and the best is used when it
-// is estimated at least 5 % faster than the plain path.  SDDMM (no partial
-// rows; rows of at most 16 floats, where the per-entry output scatter does
-// not cancel the gain): the power of two nearest to (gathered bytes / 4 MiB),
-// from 4 to 256, when the expected segments stay under an eighth of the
-// entries.
-int hybrid_parts(const csr_problem_t& p, const int64_t* hist)
+// Plan of the column-part segment format (parts 1: the plain CSR path).
+// SpMM: a cost model, time(P, T) = gathered GB of the split rows x
+// gather_ms_per_gb(slice of n_cols x width x 4 / P bytes) + gathered GB of
+// the rows kept whole (fewer than T entries) x gather_ms_per_gb(the whole
+// operand) + the partial rows (written and read: width x 8 bytes per
+// segment; a whole row is one segment) at 0.118 ms per GB, all measured; a
+// gather moves at least one 64-byte sector; the split rows' segments are
+// expected from the degree histogram.  P from 4 to 256 with slices of at
+// least 2 MiB and T a power of two (or 0) are scored, and the best is used
+// when it is estimated at least 5 % faster than the plain path.  SDDMM (no
+// partial rows; rows of at most 16 floats, where the per-entry output
+// scatter does not cancel the gain): the power of two nearest to (gathered
+// bytes / 4 MiB), from 4 to 256, when the expected segments stay under an
+// eighth of the entries, every row split.
+void hybrid_plan(const csr_problem_t& p, const int64_t* hist, int* parts, int* whole_below)
 {
-    if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return 1;
-    if (p.nnz <= 0 || p.n_cols <= 0 || p.n_rows <= 0) return 1;
+    *parts = 1;
+    *whole_below = 0;
+    if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return;
+    if (p.nnz <= 0 || p.n_cols <= 0 || p.n_rows <= 0) return;
     const double mib = 1 << 20;
     const double row = p.width * 4.0;
     const double X = p.n_cols * row;
     if (p.op == CSR_OP_SDDMM) {
-        if (p.width > 16) return 1;
+        if (p.width > 16) return;
         const double slices = X / (4.0 * mib);
-        if (slices < 2.83) return 1;  // nearest power of two below 4
+        if (slices < 2.83) return;  // nearest power of two below 4
         int P = 4;
         while (P < 256 && (double)P * 1.41421356 < slices) P *= 2;
-        return 2.0 * expected_segments(p, hist, P) <= 0.25 * p.nnz ? P : 1;
+        if (2.0 * expected_segments(p, hist, P) <= 0.25 * p.nnz) *parts = P;
+        return;
     }
-    const double G = p.nnz * std::max(row, 64.0) / 1e9;
-    const double plain = G * gather_ms_per_gb(X);
+    const double gather_bytes = std::max(row, 64.0) / 1e9;  // GB per gathered row
+    const double part_bytes = p.width * 8.0 / 1e9;          // GB per partial row, written and read
+    const double plain = p.nnz * gather_bytes * gather_ms_per_gb(X);
     double best = plain;
-    int best_p = 1;
+    // whole-row thresholds T = 2^k: buckets 1 .. k of the histogram (degrees below 2^k) stay whole
+    const int kmax = hist ? 12 : 0;
     for (int P = 4; P <= 256 && X / P >= 2.0 * mib; P *= 2) {
-        const double t = G * gather_ms_per_gb(X / P) + 0.118 * expected_segments(p, hist, P) * p.width * 8.0 / 1e9;
-        if (t < best) {
-            best = t;
-            best_p = P;
+        const double q = 1.0 - 1.0 / P;
+        for (int k = 0; k <= kmax; ++k) {
+            double split_nnz = (double)p.nnz, split_seg = 0.0, whole_rows = 0.0, whole_nnz = 0.0;
+            if (hist) {
+                split_nnz = 0.0;
+                for (int b = 1; b < 33; ++b) {
+                    if (hist[b] <= 0) continue;
+                    if (b <= k) {
+                        whole_rows += hist[b];
+                        whole_nnz += hist[33 + b];
+                    } else {
+                        const double d = (double)hist[33 + b] / hist[b];
+                        split_nnz += hist[33 + b];
+                        split_seg += hist[b] * P * (1.0 - std::pow(q, d));
+                    }
+                }
+            } else {
+                split_seg = expected_segments(p, nullptr, P);
+            }
+            const double t = split_nnz * gather_bytes * gather_ms_per_gb(X / P) +
+                             whole_nnz * gather_bytes * gather_ms_per_gb(X) +
+                             0.118 * (split_seg + whole_rows) * part_bytes;
+            if (t < best) {
+                best = t;
+                *parts = P;
+                *whole_below = k > 0 ? (1 << k) : 0;
+            }
         }
     }
-    return best < 0.95 * plain ? best_p : 1;
+    if (!(best < 0.95 * plain)) {
+        *parts = 1;
+        *whole_below = 0;
+    }
+}
+
+int hybrid_parts(const csr_problem_t& p, const int64_t* hist)
+{
+    int P = 1, T = 0;
+    hybrid_plan(p, hist, &P, &T);
+    return P;
 }
 
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev)

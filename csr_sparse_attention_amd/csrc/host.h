@@ -64,8 +64,10 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
 // FNV-1a 64 signature of (problem shape, alignment class, histogram, device).
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev);
 
-// Column parts of the column-part segment format expected to be fastest for
-// problem p (1: the plain CSR path); see hybrid_parts in host.cpp.
+// Column parts and whole-row threshold of the column-part segment format
+// expected to be fastest for problem p (parts 1: the plain CSR path); see
+// hybrid_plan in host.cpp.
+void hybrid_plan(const csr_problem_t& p, const int64_t* hist, int* parts, int* whole_below);
 int hybrid_parts(const csr_problem_t& p, const int64_t* hist);
 
 // Cache log line format.

@@ -3,8 +3,9 @@
 // fp32_kernels.h).
 //
 // The entries are stably sorted by their column part (a radix sort on
-// log2(P) bits), which groups them by (part, row) with each group in its
-// original order, since the CSR entries are already in row order.  A
+// log2(P) + 1 bits; the entries of rows kept whole take part P), which
+// groups them by (part, row) with each group in its original order, since
+// the CSR entries are already in row order.  A
 // segment starts wherever (part, row) changes; segment indices come from an
 // inclusive scan of those start flags.  Each row's segment count (integer
 // atomic adds: the counts do not depend on their order) gives the row's
@@ -44,14 +45,21 @@ int key_bits(int64_t n)
 
 }  // namespace
 
-// part of every entry (clamped into [0, P): a column out of range cannot
-// send the construction out of bounds)
-__global__ void k_entry_parts(const int32_t* col, int64_t nnz, int32_t part_cols, int32_t parts, int32_t* out)
+// part of every entry: its column's part (clamped into [0, P): a column out
+// of range cannot send the construction out of bounds), or P for an entry of
+// a row with fewer than whole_below entries (kept whole, after all parts)
+__global__ void k_entry_parts(const int32_t* col, const int32_t* row_ptr, const int32_t* coo_row, int64_t nnz,
+                              int32_t part_cols, int32_t parts, int32_t whole_below, int32_t* out)
 {
     CSR_GRID_STRIDE(e, nnz)
     {
-        const int32_t p = col[e] / part_cols;
-        out[e] = p < 0 ? 0 : (p >= parts ? parts - 1 : p);
+        const int32_t r = coo_row[e];
+        if (row_ptr[r + 1] - row_ptr[r] < whole_below) {
+            out[e] = parts;
+        } else {
+            const int32_t p = col[e] / part_cols;
+            out[e] = p < 0 ? 0 : (p >= parts ? parts - 1 : p);
+        }
     }
 }
 
@@ -113,7 +121,7 @@ static hipError_t hyb_layout(int64_t n_rows, int64_t nnz, int32_t parts, HybLayo
     size_t sort_t = 0, row_sort_t = 0, iscan_t = 0, escan_t = 0;
     const unsigned n = (unsigned)(nnz > 0 ? nnz : 1);
     hipError_t e = rocprim::radix_sort_pairs(nullptr, sort_t, (const int32_t*)nullptr, (int32_t*)nullptr,
-                                             (const int32_t*)nullptr, (int32_t*)nullptr, n, 0, key_bits(parts));
+                                             (const int32_t*)nullptr, (int32_t*)nullptr, n, 0, key_bits(parts + 1));
     if (e != hipSuccess) return e;
     e = rocprim::radix_sort_pairs(nullptr, row_sort_t, (const int32_t*)nullptr, (int32_t*)nullptr,
                                   (const int32_t*)nullptr, (int32_t*)nullptr, n, 0, key_bits(n_rows));
@@ -151,8 +159,8 @@ hipError_t hybrid_build_workspace(int64_t n_rows, int64_t nnz, int32_t parts, si
     } while (0)
 
 hipError_t launch_hybrid_build_sort(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t nnz,
-                                    int32_t parts, int32_t part_cols, int32_t* perm, int32_t* fcol, void* ws,
-                                    size_t ws_bytes, int32_t* seg_count_host, hipStream_t s)
+                                    int32_t parts, int32_t part_cols, int32_t whole_below, int32_t* perm,
+                                    int32_t* fcol, void* ws, size_t ws_bytes, int32_t* seg_count_host, hipStream_t s)
 {
     HybLayout L;
     CSR_TRY(hyb_layout(n_rows, nnz, parts, &L));
@@ -164,14 +172,14 @@ hipError_t launch_hybrid_build_sort(const int32_t* row_ptr, const int32_t* col_i
     int32_t* D = reinterpret_cast<int32_t*>(w + L.d);
     void* temp = w + L.temp;
     size_t temp_bytes = L.temp_bytes;
-    hipLaunchKernelGGL(k_entry_parts, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, col_idx, nnz, part_cols, parts,
-                       A);
+    CSR_TRY(launch_coo_rows(row_ptr, n_rows, D, nnz, s));
+    hipLaunchKernelGGL(k_entry_parts, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, col_idx, row_ptr,
+                       (const int32_t*)D, nnz, part_cols, parts, whole_below, A);
     CSR_TRY(hipGetLastError());
     hipLaunchKernelGGL(k_iota_i32, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, B, nnz);
     CSR_TRY(hipGetLastError());
     CSR_TRY(rocprim::radix_sort_pairs(temp, temp_bytes, (const int32_t*)A, C, (const int32_t*)B, perm, (unsigned)nnz,
-                                      0, key_bits(parts), s));
-    CSR_TRY(launch_coo_rows(row_ptr, n_rows, D, nnz, s));
+                                      0, key_bits(parts + 1), s));
     hipLaunchKernelGGL(k_hyb_gather, dim3(grid_for_n(nnz)), dim3(CSR_BLOCK), 0, s, (const int32_t*)perm, col_idx,
                        (const int32_t*)D, nnz, fcol, B);
     CSR_TRY(hipGetLastError());

@@ -59,8 +59,8 @@ hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows
 // with the lane layout (vec, nv, W)
 hipError_t hybrid_build_workspace(int64_t n_rows, int64_t nnz, int32_t parts, size_t* bytes);
 hipError_t launch_hybrid_build_sort(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t nnz,
-                                    int32_t parts, int32_t part_cols, int32_t* perm, int32_t* fcol, void* ws,
-                                    size_t ws_bytes, int32_t* seg_count_host, hipStream_t s);
+                                    int32_t parts, int32_t part_cols, int32_t whole_below, int32_t* perm,
+                                    int32_t* fcol, void* ws, size_t ws_bytes, int32_t* seg_count_host, hipStream_t s);
 hipError_t launch_hybrid_build_segments(int64_t n_rows, int64_t nnz, int32_t parts, int64_t n_seg, int32_t* seg_ptr,
                                         int32_t* seg_row, int32_t* row_seg_ptr, int32_t* row_seg, void* ws,
                                         hipStream_t s);

@@ -462,6 +462,7 @@ class Hybrid:
         n = desc.n_seg
         self.n_rows, self.n_cols, self.nnz = desc.n_rows, desc.n_cols, desc.nnz
         self.parts, self.part_cols, self.n_seg = desc.parts, desc.part_cols, n
+        self.whole_below = desc.whole_below
         self.perm, self.col_idx = arrays["perm"], arrays["col_idx"]
         self.seg_ptr = arrays["seg_ptr"][:n + 1]
         self.seg_row = arrays["seg_row"][:n]
@@ -470,21 +471,29 @@ class Hybrid:
 
     def __repr__(self):
         return (f"Hybrid(n_rows={self.n_rows}, n_cols={self.n_cols}, nnz={self.nnz}, parts={self.parts}, "
-                f"part_cols={self.part_cols}, n_seg={self.n_seg})")
+                f"part_cols={self.part_cols}, whole_below={self.whole_below}, n_seg={self.n_seg})")
+
+
+def hybrid_plan(problem: CsrProblem, histogram=None):
+    """(parts, whole_below) of the column-part segment format expected to be
+    fastest for this problem (parts 1: use the plain CSR path)."""
+    h = None if histogram is None else (ctypes.c_int64 * 67)(*[int(v) for v in histogram])
+    parts, whole = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib().csr_hybrid_plan(None, ctypes.byref(problem), h, ctypes.byref(parts), ctypes.byref(whole)),
+           "csr_hybrid_plan")
+    return parts.value, whole.value
 
 
 def hybrid_parts(problem: CsrProblem, histogram=None) -> int:
-    """Column parts for which the column-part segment format is expected to
-    beat the plain CSR path on this problem (1: use the plain path)."""
-    h = None if histogram is None else (ctypes.c_int64 * 67)(*[int(v) for v in histogram])
-    out = ctypes.c_int32()
-    _check(_lib().csr_hybrid_parts(None, ctypes.byref(problem), h, ctypes.byref(out)), "csr_hybrid_parts")
-    return out.value
+    """The parts of hybrid_plan."""
+    return hybrid_plan(problem, histogram)[0]
 
 
-def hybrid_format(row_ptr, col_idx, n_cols: int, parts: int, *, ctx: Optional[Context] = None) -> Hybrid:
+def hybrid_format(row_ptr, col_idx, n_cols: int, parts: int, *, whole_below: int = 0,
+                  ctx: Optional[Context] = None) -> Hybrid:
     """Builds the column-part segment format of (row_ptr, col_idx) with
-    ``parts`` column parts (a power of two from 1 to 256)."""
+    ``parts`` column parts (a power of two from 1 to 256); rows with fewer
+    than ``whole_below`` entries stay whole (one segment after all parts)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)
@@ -503,6 +512,7 @@ def hybrid_format(row_ptr, col_idx, n_cols: int, parts: int, *, ctx: Optional[Co
               "seg_row": i32(cap.value), "row_seg_ptr": i32(n_rows + 1), "row_seg": i32(cap.value)}
     h = CsrHybrid()
     h.n_rows, h.n_cols, h.nnz, h.parts, h.seg_cap = n_rows, n_cols, nnz, parts, cap.value
+    h.whole_below = whole_below
     for k, t in arrays.items():
         setattr(h, k, t.data_ptr())
     _check(lib.csr_hybrid_build(ctx.handle, row_ptr.data_ptr(), col_idx.data_ptr(), ctypes.byref(h), ws.data_ptr(),

@@ -325,7 +325,10 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
  * c / part_cols, part_cols = ceil(n_cols / P)); a segment is the run of one
  * row's entries whose columns lie in one part (the entries keep their
  * original order); the segments are ordered by (part, row) and only non-empty
- * segments are stored.  The segments form a plain CSR pattern (seg_ptr over
+ * segments are stored.  A row with fewer than whole_below entries is not
+ * split: its entries form one segment in an extra part P, after all the
+ * column parts (a short row would otherwise make about one segment per
+ * entry).  The segments form a plain CSR pattern (seg_ptr over
  * the reordered entries, n_seg rows), so every mapping of the plain products
  * runs on it; blocks reach the parts in order, so at any time the gathered
  * rows of the dense operand come from about one 1/P slice of it, a slice that
@@ -336,6 +339,10 @@ typedef struct csr_hybrid_s {
     int64_t n_rows, n_cols, nnz; /* the pattern's shape (set by the caller) */
     int32_t parts;               /* P: a power of two from 1 to 256 (set by the caller) */
     int32_t part_cols;           /* ceil(n_cols / P) (written by csr_hybrid_build) */
+    int32_t whole_below;         /* rows with fewer entries are kept whole: one segment in
+                                    part P, after all column parts; 0 = split every row
+                                    (set by the caller) */
+    int32_t reserved_;           /* must be 0 */
     int64_t seg_cap;             /* capacity of the segment arrays, >= csr_hybrid_capacity (set by the caller) */
     int64_t n_seg;               /* number of segments (written by csr_hybrid_build) */
     int32_t* perm;               /* [nnz] original entry index of each format entry */
@@ -346,13 +353,21 @@ typedef struct csr_hybrid_s {
     int32_t* row_seg;            /* [seg_cap] each row's segments, in part order */
 } csr_hybrid_t;
 
-/* The column parts for which the format is expected to beat the plain CSR
- * path on problem p (op CSR_OP_SPMM or CSR_OP_SDDMM; shape fields only) with
- * degree histogram (int64 [67], or NULL), or 1 when the plain path is
- * expected to be faster.  A measured rule: each part should hold about 4 MiB
- * of the gathered matrix (one XCD's L2); the format is proposed when that
- * gives 4 to 32 parts, for SpMM, and for SDDMM rows of at most 16 floats,
- * with at least 8 entries per non-empty row on average.  Host-only. */
+/* The format's plan for problem p (op CSR_OP_SPMM or CSR_OP_SDDMM; shape
+ * fields only) with degree histogram (int64 [67], or NULL): the column parts
+ * (1 when the plain CSR path is expected to be faster) and the whole-row
+ * threshold (whole_below may be NULL).  A cost model measured on MI355X:
+ * the gathers of the split rows cost least while one part holds about 4 MiB
+ * of the gathered matrix (one XCD's L2), the rows kept whole gather from all
+ * of it, and every segment's partial row is written and read once; the
+ * segment count is expected from the histogram.  Parts 4 ... 256 and
+ * power-of-two thresholds are scored; the format is proposed when it is
+ * estimated at least 5 % faster.  SDDMM: rows of at most 16 floats, about
+ * 4 MiB per part, every row split.  Host-only. */
+int csr_hybrid_plan(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, int32_t* parts,
+                    int32_t* whole_below);
+
+/* The parts of csr_hybrid_plan.  Host-only. */
 int csr_hybrid_parts(csr_context_t ctx, const csr_problem_t* p, const int64_t* histogram, int32_t* parts);
 
 /* Upper bound of the segment count, min(nnz, n_rows * parts): the capacity

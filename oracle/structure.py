@@ -22,6 +22,8 @@
   column c = c // ceil(n_cols / P); segment (p, r) is the list of row r's
   entries (original order) whose columns lie in part p; the non-empty
   segments are listed by part, then row; each row lists its segments by part.
+  A row with fewer than whole_below entries stays whole: one segment in an
+  extra part P, after all the column parts.
 
 * FNV-1a 64: the published Fowler-Noll-Vo hash (offset basis
   0xcbf29ce484222325, prime 0x100000001b3; per byte: xor, then multiply).
@@ -113,20 +115,26 @@ def transpose(row_ptr, col_idx, n_cols):
     return t_rp.astype(np.int32), rows[perm].astype(np.int32), perm.astype(np.int32)
 
 
-def hybrid_format_loops(row_ptr, col_idx, n_cols, parts):
+def hybrid_format_loops(row_ptr, col_idx, n_cols, parts, whole_below=0):
     """The column-part segment format by its definition, with plain loops
     (tiny inputs): for each part p, for each row r, the entries of r whose
     column lies in p, in their original order, form segment (p, r) when there
-    are any.  Returns a dict of int64 arrays: part_cols, perm, col_idx,
-    seg_ptr, seg_row, row_seg_ptr, row_seg."""
+    are any; a row with fewer than whole_below entries is not split but forms
+    one segment in part P = parts, after all column parts.  Returns a dict of
+    int64 arrays: part_cols, perm, col_idx, seg_ptr, seg_row, seg_part,
+    row_seg_ptr, row_seg."""
     rp = [int(v) for v in row_ptr]
     ci = [int(v) for v in col_idx]
     n_rows = len(rp) - 1
     part_cols = -(-n_cols // parts) if n_cols > 0 else 1
+
+    def part_of(r, e):
+        return parts if rp[r + 1] - rp[r] < whole_below else ci[e] // part_cols
+
     perm, seg_ptr, seg_row, seg_part = [], [], [], []
-    for p in range(parts):
+    for p in range(parts + 1):
         for r in range(n_rows):
-            mine = [e for e in range(rp[r], rp[r + 1]) if ci[e] // part_cols == p]
+            mine = [e for e in range(rp[r], rp[r + 1]) if part_of(r, e) == p]
             if mine:
                 seg_ptr.append(len(perm))
                 seg_row.append(r)
@@ -142,7 +150,7 @@ def hybrid_format_loops(row_ptr, col_idx, n_cols, parts):
             "seg_row": a(seg_row), "seg_part": a(seg_part), "row_seg_ptr": a(row_seg_ptr), "row_seg": a(row_seg)}
 
 
-def hybrid_format(row_ptr, col_idx, n_cols, parts):
+def hybrid_format(row_ptr, col_idx, n_cols, parts, whole_below=0):
     """The same format for larger inputs: the entries ordered by the key
     (part, row) with a stable sort (which keeps each segment's entries in
     their original order), a segment wherever the key changes, and each row's
@@ -151,8 +159,10 @@ def hybrid_format(row_ptr, col_idx, n_cols, parts):
     ci = np.asarray(col_idx, dtype=np.int64)
     n_rows = len(rp) - 1
     part_cols = -(-n_cols // parts) if n_cols > 0 else 1
-    rows = np.repeat(np.arange(n_rows, dtype=np.int64), np.diff(rp))
-    key = (ci // part_cols) * n_rows + rows
+    deg = np.diff(rp)
+    rows = np.repeat(np.arange(n_rows, dtype=np.int64), deg)
+    part = np.where(deg[rows] < whole_below, parts, ci // part_cols)
+    key = part * n_rows + rows
     perm = np.argsort(key, kind="stable")
     k = key[perm]
     starts = np.flatnonzero(np.r_[True, k[1:] != k[:-1]]) if len(k) else np.zeros(0, dtype=np.int64)

@@ -273,6 +273,15 @@ def test_hybrid_parts_rule():
     assert parts(S, np.full(1_000_000, 3), 1_000_000, 32) == 1
     assert csa.hybrid_parts(problem(_ffi.OP_ATTENTION, n_rows=232_965, n_cols=232_965, nnz=114_600_002, width=32),
                             None) == 1
+    # the plan's whole-row threshold: the power-law graph's short rows stay whole
+    def plan(op, deg, n_cols, width):
+        p = problem(op, n_rows=len(deg), n_cols=n_cols, nnz=int(np.sum(deg)), width=width)
+        return csa.hybrid_plan(p, _hist_of_degrees(deg))
+
+    assert [plan(S, pl, configs.C2_N, F) for F in (32, 128, 602)] == [(8, 32), (32, 128), (128, 512)]
+    assert [plan(S, sk, configs.C4_N, F) for F in (4, 32)] == [(4, 0), (32, 0)]
+    assert plan(D, sk, configs.C4_N, 8) == (8, 0)  # SDDMM splits every row
+    assert plan(S, ln, configs.C3_N, 100) == (1, 0)
     # without a histogram every row counts at the mean degree (here: long rows, many segments)
     assert parts(S, pl, configs.C2_N, 602, hist=False) == 64  # 128 with the histogram
 

@@ -152,9 +152,9 @@ def planned_format(op, name, rp, ci, a, b):
     csr = pattern(name)
     p, _ = csa.make_problem(op, rp, ci, a, b)
     counts, sums, mx = csa.degree_histogram(rp)
-    P = csa.hybrid_parts(p, counts + sums + [mx])
+    P, T = csa.hybrid_plan(p, counts + sums + [mx])
     assert P > 1, (name, op, b.shape)
-    h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, P, whole_below=T)
     if op == "spmm":
         a = None if a is None else csa.hybrid_values(h, a)
     s, _ = csa.hybrid_select(h, op, a, b)
@@ -169,7 +169,7 @@ def test_c2_spmm_format(F):
     X = configs.config_dense("c2", "X", csr, F)
     vd, Xd = dev(vals), dev(X)
     h, hv, s = planned_format("spmm", "c2", rp, ci, vd, Xd)
-    assert h.parts == {32: 8, 64: 16, 128: 32, 602: 128}[F]
+    assert (h.parts, h.whole_below) == {32: (8, 32), 64: (16, 64), 128: (32, 128), 602: (128, 512)}[F]
     # the format at full size: a permutation, segments in (part, row) order
     assert torch.equal(torch.sort(h.perm.long())[0], torch.arange(csr.nnz, device="cuda"))
     assert bool((h.seg_ptr[1:] > h.seg_ptr[:-1]).all()) and int(h.seg_ptr[-1]) == csr.nnz
@@ -189,8 +189,8 @@ def test_c2_spmm_format(F):
 def test_c4_format_bit_exact():
     csr = pattern("c4")
     rp, ci = pattern_dev("c4")
-    h = csa.hybrid_format(rp, ci, csr.n_cols, 8)
-    want = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, 8)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, 8, whole_below=16)
+    want = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, 8, whole_below=16)
     assert h.n_seg == len(want["seg_row"])
     for k in ("perm", "col_idx", "seg_ptr", "seg_row", "row_seg_ptr", "row_seg"):
         assert np.array_equal(getattr(h, k).cpu().numpy(), want[k]), k

@@ -734,16 +734,16 @@ def _format_graph(name):
 
 
 @pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges", "empty"])
-@pytest.mark.parametrize("P", [1, 4, 32, 256])
-def test_hybrid_format_bit_exact(graph, P):
+@pytest.mark.parametrize("P,T", [(1, 0), (4, 0), (32, 0), (256, 0), (8, 4), (32, 300)])
+def test_hybrid_format_bit_exact(graph, P, T):
     csr = _format_graph(graph)
     rp, ci = pattern_dev(csr)
-    h = csa.hybrid_format(rp, ci, csr.n_cols, P)
-    want = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, P)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, P, whole_below=T)
+    want = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, P, whole_below=T)
     assert h.part_cols == want["part_cols"] and h.n_seg == len(want["seg_row"])
     for k in ("perm", "col_idx", "seg_ptr", "seg_row", "row_seg_ptr", "row_seg"):
         assert np.array_equal(getattr(h, k).cpu().numpy(), want[k]), k
-    h2 = csa.hybrid_format(rp, ci, csr.n_cols, P)  # rebuilt: the same arrays
+    h2 = csa.hybrid_format(rp, ci, csr.n_cols, P, whole_below=T)  # rebuilt: the same arrays
     for k in ("perm", "seg_ptr", "row_seg"):
         assert torch.equal(getattr(h, k), getattr(h2, k))
 
@@ -758,15 +758,15 @@ def test_hybrid_spmm_every_schedule(graph, F):
     ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=oracle.default_threads())
     rp, ci = pattern_dev(csr)
     Xd = dev(X)
-    for P in (2, 8, 32, 128):
-        h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+    for P, T in ((2, 0), (8, 0), (32, 0), (128, 0), (8, 40), (32, 300)):
+        h = csa.hybrid_format(rp, ci, csr.n_cols, P, whole_below=T)
         hv = csa.hybrid_values(h, dev(vals))
         p = csa.hybrid_problem(h, "spmm", hv, Xd)
-        for s in schedules(p, thorough=(P == 8 and graph == "skew")):
+        for s in schedules(p, thorough=(P == 8 and T == 0 and graph == "skew")):
             Y = csa.hybrid_spmm(h, hv, Xd, schedule=s)
-            assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-" + sched_id(s))
+            assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-T{T}-" + sched_id(s))
         Y = csa.hybrid_spmm(h, hv, Xd)  # selected
-        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-auto")
+        assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, f"P{P}-T{T}-auto")
     ones, omag = oracle.spmm(csr.row_ptr, csr.col_idx, None, X, threads=oracle.default_threads())
     Y = csa.hybrid_spmm(h, None, Xd)
     assert_close(Y.cpu().numpy(), ones, omag, TOL_F32, "unit values")
@@ -782,8 +782,8 @@ def test_hybrid_sddmm_every_schedule(graph, K):
     ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, threads=oracle.default_threads())
     rp, ci = pattern_dev(csr)
     Ud, Vd = dev(U), dev(V)
-    for P in (2, 8, 32):
-        h = csa.hybrid_format(rp, ci, csr.n_cols, P)
+    for P, T in ((2, 0), (8, 0), (32, 0), (32, 300)):
+        h = csa.hybrid_format(rp, ci, csr.n_cols, P, whole_below=T)
         p = csa.hybrid_problem(h, "sddmm", Ud, Vd)
         for s in schedules(p, thorough=(P == 8 and graph == "skew")):
             out = csa.hybrid_sddmm(h, Ud, Vd, schedule=s)
@@ -856,6 +856,10 @@ def test_hybrid_deterministic_and_errors():
     assert lib.csr_hybrid_build(ctx.handle, rp.data_ptr(), ci.data_ptr(), ctypes.byref(d), ws.data_ptr(),
                                 ws.numel(), st) == -5
     # a description that was never built
+    d = _ffi.CsrHybrid.from_buffer_copy(bytes(h.desc))
+    d.whole_below = -1
+    assert lib.csr_hybrid_build(ctx.handle, rp.data_ptr(), ci.data_ptr(), ctypes.byref(d), ws.data_ptr(),
+                                ws.numel(), st) == -2
     d = _ffi.CsrHybrid.from_buffer_copy(bytes(h.desc))
     d.n_seg = -1
     Y = torch.empty((csr.n_rows, 16), device="cuda")

@@ -139,12 +139,24 @@ PY_MUTANTS = [
     ("format reverses equal keys (unstable order)", [
         ('perm = np.argsort(key, kind="stable")', 'perm = np.argsort(-key, kind="stable")[::-1]')]),
     ("format parts columns by proportional scaling", [
-        ("key = (ci // part_cols) * n_rows + rows", "key = (ci * parts // max(n_cols, 1)) * n_rows + rows"),
-        ("if ci[e] // part_cols == p]", "if ci[e] * parts // n_cols == p]")]),
+        ("part = np.where(deg[rows] < whole_below, parts, ci // part_cols)",
+         "part = np.where(deg[rows] < whole_below, parts, ci * parts // max(n_cols, 1))"),
+        ("return parts if rp[r + 1] - rp[r] < whole_below else ci[e] // part_cols",
+         "return parts if rp[r + 1] - rp[r] < whole_below else ci[e] * parts // n_cols")]),
+    ("format keeps rows of exactly whole_below entries whole", [
+        ("part = np.where(deg[rows] < whole_below, parts, ci // part_cols)",
+         "part = np.where(deg[rows] <= whole_below, parts, ci // part_cols)"),
+        ("return parts if rp[r + 1] - rp[r] < whole_below else ci[e] // part_cols",
+         "return parts if rp[r + 1] - rp[r] <= whole_below else ci[e] // part_cols")]),
+    ("format puts whole rows before the column parts", [
+        ("part = np.where(deg[rows] < whole_below, parts, ci // part_cols)",
+         "part = np.where(deg[rows] < whole_below, 0, ci // part_cols + 1)"),
+        ("return parts if rp[r + 1] - rp[r] < whole_below else ci[e] // part_cols",
+         "return 0 if rp[r + 1] - rp[r] < whole_below else ci[e] // part_cols + 1")]),
     ("format orders segments by row first", [
-        ("key = (ci // part_cols) * n_rows + rows", "key = rows * parts + (ci // part_cols)"),
-        ("    for p in range(parts):\n        for r in range(n_rows):",
-         "    for r in range(n_rows):\n        for p in range(parts):")]),
+        ("key = part * n_rows + rows", "key = rows * (parts + 1) + part"),
+        ("    for p in range(parts + 1):\n        for r in range(n_rows):",
+         "    for r in range(n_rows):\n        for p in range(parts + 1):")]),
     ("format lists a row's segments last part first", [
         ('row_seg = np.argsort(seg_row, kind="stable")',
          'row_seg = np.lexsort((-np.arange(len(seg_row)), seg_row))'),

@@ -561,6 +561,20 @@ def test_hybrid_format_hand_example():
         got = build(row_ptr, col_idx, 10, 4)
         for k, v in want.items():
             assert np.array_equal(np.asarray(got[k]), np.asarray(v)), (build.__name__, k)
+    # rows with fewer than 3 entries kept whole (row 2): one segment in part 4, after all column parts
+    want_whole = {
+        "perm": [1, 4, 7, 0, 3, 9, 8, 2, 5, 6],
+        "col_idx": [0, 1, 2, 5, 3, 4, 6, 9, 7, 8],
+        "seg_ptr": [0, 2, 3, 5, 6, 7, 8, 10],
+        "seg_row": [0, 3, 0, 3, 3, 0, 2],
+        "seg_part": [0, 0, 1, 1, 2, 3, 4],
+        "row_seg_ptr": [0, 3, 3, 4, 7],
+        "row_seg": [0, 2, 5, 6, 1, 3, 4],
+    }
+    for build in (oracle.hybrid_format_loops, oracle.hybrid_format):
+        got = build(row_ptr, col_idx, 10, 4, whole_below=3)
+        for k, v in want_whole.items():
+            assert np.array_equal(np.asarray(got[k]), np.asarray(v)), (build.__name__, "whole", k)
     # one part: the segments are the non-empty rows, in order
     one = oracle.hybrid_format(row_ptr, col_idx, 10, 1)
     assert one["perm"].tolist() == list(range(10)) and one["seg_row"].tolist() == [0, 2, 3]
@@ -576,10 +590,11 @@ def test_hybrid_format_bruteforce(seed):
     n_cols = [1, 3, 7, 20, 33, 64, 5, 40][seed]
     csr = random_small_graph(25, n_cols, 0.0 if seed == 6 else 0.3, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
     for P in (1, 2, 4, 8, 16, 32, 64, 256):
-        a = oracle.hybrid_format_loops(csr.row_ptr, csr.col_idx, n_cols, P)
-        b = oracle.hybrid_format(csr.row_ptr, csr.col_idx, n_cols, P)
-        for k in a:
-            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), (P, k)
+        for T in (0, 4, 1000):
+            a = oracle.hybrid_format_loops(csr.row_ptr, csr.col_idx, n_cols, P, whole_below=T)
+            b = oracle.hybrid_format(csr.row_ptr, csr.col_idx, n_cols, P, whole_below=T)
+            for k in a:
+                assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), (P, T, k)
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -587,17 +602,22 @@ def test_hybrid_format_invariants(seed):
     rng = np.random.default_rng(770 + seed)
     csr = random_small_graph(300, 500, 0.05, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
     rows = csr.row_of_edge()
-    for P in (2, 8, 32):
-        h = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, P)
+    deg = np.diff(csr.row_ptr)
+    for P, T in ((2, 0), (8, 0), (32, 0), (8, 25), (32, 30)):
+        h = oracle.hybrid_format(csr.row_ptr, csr.col_idx, csr.n_cols, P, whole_below=T)
         perm, sp, sr, spart = h["perm"], h["seg_ptr"], h["seg_row"], h["seg_part"]
         assert h["part_cols"] == -(-500 // P)
         assert sorted(perm.tolist()) == list(range(csr.nnz))  # a permutation of the entries
         assert np.array_equal(h["col_idx"], csr.col_idx[perm])
         assert sp[0] == 0 and sp[-1] == csr.nnz and np.all(np.diff(sp) > 0)  # no empty segment
+        whole = deg < T
         for s in range(len(sr)):
             seg = perm[sp[s]:sp[s + 1]]
-            assert np.all(rows[seg] == sr[s]) and np.all(csr.col_idx[seg] // h["part_cols"] == spart[s])
-            assert np.all(np.diff(seg) > 0)  # original order inside a segment
+            assert np.all(rows[seg] == sr[s]) and np.all(np.diff(seg) > 0)  # one row, original order
+            if whole[sr[s]]:  # a row kept whole: all its entries, in part P
+                assert spart[s] == P and len(seg) == deg[sr[s]]
+            else:
+                assert np.all(csr.col_idx[seg] // h["part_cols"] == spart[s])
         key = spart * csr.n_rows + sr
         assert np.all(np.diff(key) > 0)  # ordered by (part, row), each pair once
         # every row's entries are its segments, by part
@@ -606,7 +626,8 @@ def test_hybrid_format_invariants(seed):
             assert np.all(sr[mine] == r) and np.all(np.diff(spart[mine]) > 0)
             got = np.concatenate([perm[sp[s]:sp[s + 1]] for s in mine]) if len(mine) else np.zeros(0, int)
             e = np.arange(csr.row_ptr[r], csr.row_ptr[r + 1])
-            assert np.array_equal(got, e[np.argsort(csr.col_idx[e] // h["part_cols"], kind="stable")])
+            want = e if whole[r] else e[np.argsort(csr.col_idx[e] // h["part_cols"], kind="stable")]
+            assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -617,7 +638,7 @@ def test_hybrid_product_identity(oracle_lib, seed):
     csr = random_small_graph(40, 60, 0.2, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
     vals = rng.standard_normal(csr.nnz).astype(np.float32).astype(np.float64)  # the oracle reads fp32 values
     X = rng.standard_normal((60, 5)).astype(np.float32)
-    h = oracle.hybrid_format(csr.row_ptr, csr.col_idx, 60, 4)
+    h = oracle.hybrid_format(csr.row_ptr, csr.col_idx, 60, 4, whole_below=(0, 6, 12, 100)[seed])
     ref, mag = oracle_lib.spmm(csr.row_ptr, csr.col_idx, vals, X)
     part_rows = np.zeros((len(h["seg_row"]), 5))
     for s in range(len(h["seg_row"])):
