@@ -36,8 +36,10 @@
  *    sized with csr_workspace_size().  The auto-select path also uses a small
  *    pinned host buffer owned by the context.
  *  - stream is a hipStream_t (NULL = the null stream).  Work is enqueued
- *    asynchronously.  Only the auto-select path (sched == NULL) and the
- *    calls marked "synchronous" wait on the stream.
+ *    asynchronously.  Only the auto-select path (sched == NULL), validation
+ *    (CSR_CTX_VALIDATE) and the calls marked "synchronous" wait on the
+ *    stream; otherwise a call only enqueues kernels (no memset, no
+ *    allocation), so it may be captured into a HIP graph.
  *  - Every call returns a csr_status (0 = CSR_OK).  No C++ exception or abort
  *    crosses the ABI.  On error nothing has been written to the outputs
  *    unless stated; csr_last_error() gives a message.

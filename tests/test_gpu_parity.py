@@ -871,3 +871,58 @@ def test_hybrid_deterministic_and_errors():
     assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(),
                                8, None, ws.data_ptr(), ws.numel(), st) == -2
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture of launch-bound calls
+# ---------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager():
+    """With explicit schedules (and no validation) the calls only enqueue
+    kernels: captured into a graph, every replay, with eager work and
+    synchronisations between the replays, equals the eager result bit for bit."""
+    c = __import__("synth").configs.make_config("c1")
+    csr = c["csr"]
+    rp, ci = pattern_dev(csr)
+    S, V = dev(c["scores"]), dev(c["V"])
+    rng = np.random.default_rng(3)
+    X = dev(rng.standard_normal((csr.n_cols, 32)).astype(np.float32))
+    outs = {"att": torch.empty((csr.n_rows, V.shape[1]), device="cuda"),
+            "spmm": torch.empty((csr.n_rows, 32), device="cuda"),
+            "sddmm": torch.empty(csr.nnz, device="cuda"),
+            "fmt": torch.empty((csr.n_rows, 32), device="cuda")}
+    sa, _ = csa.select("attention", rp, ci, S, V, out=outs["att"])
+    ss, _ = csa.select("spmm", rp, ci, S, X, out=outs["spmm"])
+    sd, _ = csa.select("sddmm", rp, ci, X, X, out=outs["sddmm"])
+    h = csa.hybrid_format(rp, ci, csr.n_cols, 4, whole_below=8)
+    hv = csa.hybrid_values(h, S)
+    sh, _ = csa.hybrid_select(h, "spmm", hv, X)
+
+    def step():
+        csa.attention(rp, ci, S, V, out=outs["att"], schedule=sa)
+        csa.spmm(rp, ci, S, X, out=outs["spmm"], schedule=ss)
+        csa.sddmm(rp, ci, X, X, out=outs["sddmm"], schedule=sd)
+        csa.hybrid_spmm(h, hv, X, out=outs["fmt"], schedule=sh)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on a side stream, as graph capture requires
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        for v in outs.values():
+            v.fill_(float("nan"))
+        # eager work between the replays (other inputs, other outputs)
+        csa.spmm(rp, ci, None, X * (r + 2))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], eager[k]), (r, k)
+    ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, c["scores"], c["V"])
+    assert_close(outs["att"].cpu().numpy(), ref, mag, TOL_F32, "graph attention")
