@@ -203,7 +203,9 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
     if (!nv_ok(s.passes)) return fail("unsupported pass count");
     const int64_t per_pass = (int64_t)s.group_lanes * s.vec;
     if (per_pass * s.passes < p.width) return fail("layout does not cover the feature width");
-    if (s.passes > 1 && per_pass * (s.passes - 1) >= p.width) return fail("layout has an empty pass");
+    // canonical: the fewest supported passes that cover the width (a pass
+    // count between supported ones may leave a trailing pass all masked)
+    if (nv_up((p.width + per_pass - 1) / per_pass) != s.passes) return fail("layout has an avoidable empty pass");
     return CSR_OK;
 }
 

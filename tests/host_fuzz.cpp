@@ -1,0 +1,193 @@
+// Randomised check of the library's host logic (problem and schedule checks,
+// lane layouts, workspace layout, candidates, cost model, format plan,
+// signature, cache log format), built with g++ and the address and
+// undefined-behaviour sanitizers by tests/test_host_fuzz.py.  No GPU.
+//
+// Invariants checked on every accepted problem: the default schedule and
+// every candidate pass the schedule check; workspace sizes are aligned and
+// at least the head; estimates are finite and non-negative; the signature is
+// a pure function of its inputs; the plan proposes 1 part or a power of two
+// from 4 to 256 with a power-of-two (or zero) whole-row threshold; a cache
+// line parses back to the schedule it was written from.  Malformed cache
+// lines and arbitrary problem / schedule fields must be rejected without a
+// crash.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../csr_sparse_attention_amd/csrc/host.h"
+
+static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
+static uint64_t next()  // splitmix64
+{
+    uint64_t z = (rng_state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+static int64_t pick(const int64_t* v, int n) { return v[next() % n]; }
+
+static int failures = 0;
+#define CHECK(cond, ...)                                   \
+    do {                                                   \
+        if (!(cond)) {                                     \
+            if (failures < 20) std::fprintf(stderr, __VA_ARGS__); \
+            ++failures;                                    \
+        }                                                  \
+    } while (0)
+
+static csr_problem_t random_problem()
+{
+    static const int64_t sizes[] = {-1, 0, 1, 2, 7, 64, 1000, 232965, 2449029, 1000000, (int64_t)1 << 31};
+    static const int64_t widths[] = {-3, 0, 1, 2, 3, 4, 5, 8, 16, 32, 64, 100, 128, 512, 602, 1024, 4096, 4097};
+    csr_problem_t p;
+    std::memset(&p, 0, sizeof p);
+    p.op = (int32_t)(next() % 8);  // includes invalid ops 0 and 7
+    p.dtype = (int32_t)(next() % 3);
+    p.n_rows = pick(sizes, 11);
+    p.n_cols = pick(sizes, 11);
+    p.nnz = (next() % 4 == 0) ? pick(sizes, 11) : (int64_t)(next() % 200000000);
+    p.width = pick(widths, 18);
+    static const int32_t hd[][2] = {{8, 64}, {1, 512}, {2, 8}, {4, 32}, {3, 16}, {8, 48}, {0, 0}, {16, 64}};
+    const int h = (int)(next() % 8);
+    p.heads = hd[h][0];
+    p.head_dim = hd[h][1];
+    if (p.op == CSR_OP_MHA && next() % 2) p.width = (int64_t)p.heads * p.head_dim;
+    const int64_t lds[] = {p.width, p.width + 1, p.width + 4, p.width - 1, 0};
+    p.ld_a = pick(lds, 5);
+    p.ld_b = pick(lds, 5);
+    p.ld_out = pick(lds, 5);
+    auto ptr = [&]() -> void* {
+        static const uintptr_t bases[] = {0, 0x1000, 0x1004, 0x1008, 0x100000, 0x100010};
+        return reinterpret_cast<void*>(bases[next() % 6]);
+    };
+    p.row_ptr = static_cast<const int32_t*>(ptr());
+    p.col_idx = static_cast<const int32_t*>(ptr());
+    p.a = ptr();
+    p.b = ptr();
+    p.c = ptr();
+    p.out = ptr();
+    const float scales[] = {1.f, 0.125f, -2.f, 0.f, INFINITY, NAN};
+    p.scale = scales[next() % 6];
+    if (next() % 2) {
+        // mostly well-formed: the op's dtype, positive sizes, natural strides
+        // and aligned operands, with any width
+        p.op = 1 + (int32_t)(next() % 6);
+        p.dtype = p.op == CSR_OP_MHA ? CSR_DTYPE_BF16 : CSR_DTYPE_F32;
+        p.n_rows = 1 + (int64_t)(next() % 3000000);
+        p.n_cols = 1 + (int64_t)(next() % 3000000);
+        p.nnz = (int64_t)(next() % 120000000);
+        if (p.op == CSR_OP_MHA) {
+            static const int32_t dims[] = {8, 16, 32, 64, 128, 256, 512};
+            p.heads = 1 + (int32_t)(next() % 16);
+            p.head_dim = dims[next() % 7];
+            p.width = (int64_t)p.heads * p.head_dim;
+        } else {
+            p.width = 1 + (int64_t)(next() % 4096);
+        }
+        p.ld_a = p.ld_b = p.ld_out = p.width + (int64_t)(next() % 3);
+        static const uintptr_t good[] = {0x100000, 0x100004, 0x100008, 0x100010};
+        p.row_ptr = reinterpret_cast<const int32_t*>(good[next() % 4]);
+        p.col_idx = reinterpret_cast<const int32_t*>(good[next() % 4]);
+        p.a = reinterpret_cast<const void*>(good[next() % 4]);
+        p.b = reinterpret_cast<const void*>(good[next() % 4]);
+        p.c = reinterpret_cast<const void*>(good[next() % 4]);
+        p.out = reinterpret_cast<void*>(good[next() % 4]);
+        p.scale = 0.125f;
+    }
+    return p;
+}
+
+static void random_hist(int64_t* h, const csr_problem_t& p)
+{
+    std::memset(h, 0, sizeof(int64_t) * csrh::kHistInts);
+    if (p.n_rows <= 0) return;
+    int64_t rows_left = p.n_rows, nnz_left = p.nnz > 0 ? p.nnz : 0;
+    for (int b = 0; b < 33 && rows_left > 0; ++b) {
+        const int64_t c = (b == 32) ? rows_left : (int64_t)(next() % (uint64_t)(rows_left + 1));
+        h[b] = c;
+        rows_left -= c;
+        if (b > 0 && c > 0) {
+            const int64_t lo = (int64_t)1 << (b - 1);
+            const int64_t s = std::min(nnz_left, c * lo);
+            h[33 + b] = s;
+            nnz_left -= s;
+            h[66] = std::max(h[66], lo);
+        }
+    }
+}
+
+int main(int argc, char** argv)
+{
+    const int iters = argc > 1 ? std::atoi(argv[1]) : 100000;
+    csrh::DeviceInfo dev;
+    dev.cu_count = 256;
+    dev.arch = 950;
+    int accepted = 0, planned = 0, parsed = 0;
+    for (int it = 0; it < iters; ++it) {
+        csr_problem_t p = random_problem();
+        std::string why;
+        const bool need_ptrs = next() % 2;
+        const int rc = csrh::check_problem(p, need_ptrs, &why);
+        int64_t hist[csrh::kHistInts];
+        random_hist(hist, p);
+        if (rc == CSR_OK) {
+            ++accepted;
+            const csr_schedule_t d = csrh::default_schedule(p);
+            CHECK(csrh::check_schedule(p, d, &why) == CSR_OK, "default schedule rejected (op %d F %lld): %s\n",
+                  p.op, (long long)p.width, why.c_str());
+            const size_t wb = csrh::workspace_bytes(p, d);
+            CHECK(wb >= csrh::kHeadBytes && wb % csrh::kAlign == 0, "bad workspace size %zu\n", wb);
+            const auto cands = csrh::candidates(p, (next() % 2) ? hist : nullptr);
+            CHECK(!cands.empty() && std::memcmp(&cands[0], &d, sizeof d) == 0, "first candidate is not the default\n");
+            for (const auto& c : cands) {
+                CHECK(csrh::check_schedule(p, c, &why) == CSR_OK, "candidate rejected (op %d map %d): %s\n", p.op,
+                      c.mapping, why.c_str());
+                const double e = csrh::estimate(p, c, hist, dev);
+                CHECK(std::isfinite(e) && e >= 0.0, "estimate %g\n", e);
+                const size_t w = csrh::workspace_bytes(p, c);
+                CHECK(w >= csrh::kHeadBytes && w % csrh::kAlign == 0, "bad candidate workspace %zu\n", w);
+            }
+            const uint64_t s1 = csrh::signature(p, hist, dev), s2 = csrh::signature(p, hist, dev);
+            CHECK(s1 == s2, "signature not deterministic\n");
+            int P = -1, T = -1;
+            csrh::hybrid_plan(p, (next() % 2) ? hist : nullptr, &P, &T);
+            const bool p_ok = P == 1 || (P >= 4 && P <= 256 && (P & (P - 1)) == 0);
+            const bool t_ok = T == 0 || (T > 0 && (T & (T - 1)) == 0);
+            CHECK(p_ok && t_ok && (P > 1 || T == 0), "plan P %d T %d\n", P, T);
+            if (P > 1) ++planned;
+            // the cache line round trip
+            const double us = (double)(next() % 100000) / 7.0;
+            const std::string line = csrh::format_cache_line(s1, d, us);
+            uint64_t sig = 0;
+            csr_schedule_t back;
+            double us2 = 0;
+            CHECK(csrh::parse_cache_line(line, &sig, &back, &us2) && sig == s1 && std::memcmp(&back, &d, sizeof d) == 0,
+                  "cache line round trip: %s\n", line.c_str());
+            // truncated and corrupted lines are rejected or parse to a valid schedule, never crash
+            std::string bad = line.substr(0, next() % (line.size() + 1));
+            if (!bad.empty() && next() % 2) bad[next() % bad.size()] = (char)(32 + next() % 95);
+            if (csrh::parse_cache_line(bad, &sig, &back, &us2)) ++parsed;
+        }
+        // arbitrary schedule fields: checked without a crash
+        csr_schedule_t s;
+        std::memset(&s, 0, sizeof s);
+        s.version = (int32_t)(next() % 3);
+        s.op = (int32_t)(next() % 8);
+        s.mapping = (int32_t)(next() % 5);
+        s.vec = (int32_t)(next() % 10);
+        s.group_lanes = (int32_t)(1 << (next() % 8)) - (int32_t)(next() % 2);
+        s.passes = (int32_t)(next() % 20);
+        s.chunk_items = (int32_t)((next() % 2) ? 256 << (next() % 4) : next() % 5000);
+        s.long_row = (int32_t)(next() % 300) - 10;
+        s.flags = (int32_t)(next() % 8 == 0);
+        if (rc == CSR_OK && csrh::check_schedule(p, s, &why) == CSR_OK) {
+            const size_t w = csrh::workspace_bytes(p, s);
+            CHECK(w >= csrh::kHeadBytes && w % csrh::kAlign == 0, "bad workspace for an accepted schedule\n");
+        }
+    }
+    std::printf("iterations %d accepted problems %d planned formats %d corrupted lines parsed %d failures %d\n", iters,
+                accepted, planned, parsed, failures);
+    return failures ? 1 : 0;
+}

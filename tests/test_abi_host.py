@@ -63,6 +63,33 @@ def test_default_layout(F, vec, W, nv):
     assert s.mapping == _ffi.MAP_MERGEPATH and s.version == _ffi.SCHEDULE_VERSION
 
 
+@pytest.mark.parametrize("ptr", [0x1000, 0x1004, 0x1008])
+@pytest.mark.parametrize("op", [_ffi.OP_SPMM, _ffi.OP_SDDMM, _ffi.OP_ATTENTION])
+def test_default_schedule_is_valid_at_every_width(op, ptr):
+    # the default is also what a caller may pass back explicitly; widths whose
+    # lane count falls between supported pass counts (e.g. 601 one float at a
+    # time: 10 passes of 64 lanes, rounded up to 12) must still be accepted
+    # (a width no layout covers, e.g. an odd width above 1024, has no default)
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+    covered = 0
+    for F in range(1, 4097):
+        p = problem(op, width=F, ptr=ptr)
+        s = csa.CsrSchedule()
+        rc = lib.csr_default_schedule(None, ctypes.byref(p), ctypes.byref(s))
+        if rc == -2:  # CSR_ERR_SHAPE
+            assert F > 1024
+            continue
+        assert rc == 0
+        covered += 1
+        assert lib.csr_workspace_size(None, ctypes.byref(p), ctypes.byref(s), ctypes.byref(n)) == 0, (F, s.vec,
+                                                                                                      s.passes)
+    # vec 1 covers widths up to 1024, vec 2 even widths up to 2048, vec 4 multiples of 4 up to 4096
+    max_vec = {0x1000: 4, 0x1008: 2, 0x1004: 1}[ptr]
+    assert covered == sum(1 for F in range(1, 4097) if any(F % v == 0 and F <= 1024 * v for v in (1, 2, 4)
+                                                                if v <= max_vec))
+
+
 def test_alignment_limits_vector_width():
     s = csa.default_schedule(problem(_ffi.OP_SPMM, width=64, ld=66))
     assert s.vec == 2
