@@ -56,7 +56,9 @@ def schedules(problem, thorough=True):
     base = csa.default_schedule(problem)
     layouts = [(base.group_lanes, base.passes)]
     W2, nv2 = base.group_lanes // 2, base.passes * 2
-    if W2 >= 1 and nv2 in (2, 4, 6, 8, 12, 16) and W2 * base.vec * (nv2 - 1) < problem.width:
+    # the halved layout when its pass count is the fewest supported that covers the width
+    need = -(-problem.width // max(1, W2 * base.vec))
+    if W2 >= 1 and nv2 in (2, 4, 6, 8, 12, 16) and min(v for v in (1, 2, 3, 4, 5, 6, 8, 12, 16, 99) if v >= need) == nv2:
         layouts.append((W2, nv2))
     out = []
     for W, nv in layouts:
@@ -114,7 +116,8 @@ def test_spmm_every_schedule(skew, F):
     assert_close(Y.cpu().numpy(), ref, mag, TOL_F32, "auto")
 
 
-@pytest.mark.parametrize("F", [2, 3, 5, 7, 8, 16, 17, 100, 128, 256, 300, 1024])
+# 601 and 777 floats one at a time: 12 and 16 passes of 64 lanes, the last 2 and 3 all masked
+@pytest.mark.parametrize("F", [2, 3, 5, 7, 8, 16, 17, 100, 128, 256, 300, 601, 777, 1024])
 def test_spmm_widths(F):
     csr = skew_graph(2, n_rows=1500, n_cols=20_000, giant=9000)
     rng = np.random.default_rng(100 + F)
@@ -162,7 +165,7 @@ def test_spmm_duplicates_unsorted():
 # attention (scores given)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("F", [1, 4, 32, 64, 100])
+@pytest.mark.parametrize("F", [1, 4, 32, 64, 100, 601])
 def test_attention_every_schedule(skew, F):
     csr = skew
     rng = np.random.default_rng(200 + F)
@@ -240,7 +243,7 @@ def test_p4_size_attention():
 # SDDMM
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("K", [1, 4, 32, 64, 128, 602])
+@pytest.mark.parametrize("K", [1, 4, 32, 64, 128, 601, 602])
 def test_sddmm_every_schedule(K):
     csr = skew_graph(7, n_rows=2000, n_cols=30_000, giant=25_000)
     rng = np.random.default_rng(300 + K)
