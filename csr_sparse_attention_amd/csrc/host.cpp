@@ -36,7 +36,7 @@ int nv_up(int64_t nv)
     return -1;
 }
 
-int unroll_for(int vec, int nv) { return (vec * nv <= 2) ? 8 : (vec * nv <= 8) ? 4 : (vec * nv <= 16) ? 2 : 1; }
+int unroll_for(int vec, int nv) { return (vec * nv <= 2) ? 8 : (vec * nv <= 16) ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 

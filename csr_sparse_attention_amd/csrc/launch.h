@@ -27,7 +27,7 @@ inline bool chunk_supported(int d) { return d == 256 || d == 512 || d == 1024; }
 // Entries in flight per lane group, from the registers one entry needs.
 constexpr int unroll_for(int vec, int nv)
 {
-    return (vec * nv <= 2) ? 8 : (vec * nv <= 8) ? 4 : (vec * nv <= 16) ? 2 : 1;
+    return (vec * nv <= 2) ? 8 : (vec * nv <= 16) ? 4 : 2;
 }
 
 // Returns hipSuccess or the launch error.  mapping: 1 row-group, 2 merge path
