@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 #include "../../include/csrsa.h"
 
 #define CSR_WAVE 64
@@ -121,6 +123,67 @@ __device__ __forceinline__ float exp_neg(float x)
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, CSR_WAVE); }
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves on the DPP path (VALU, no LDS traffic).  GFX9 controls:
+// row_shr:n = 0x110 + n, wave_shl:1 = 0x130, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143.  A lane whose source lies outside its row (or the
+// wave), or whose row is masked off, keeps `old`.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int v)
+{
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf,
+                                                      false));
+}
+
+// Lane l + 1's value (lane 63: `old`).
+__device__ __forceinline__ int next_lane_i(int old, int v) { return dpp_i<0x130, 0xf>(old, v); }
+
+__device__ __forceinline__ int lane63_i(int v) { return __builtin_amdgcn_readlane(v, CSR_WAVE - 1); }
+__device__ __forceinline__ float lane63_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), CSR_WAVE - 1));
+}
+
+// One step of a segmented sum: add the source lane's partial sum when it
+// carries the same run id.
+template <int CTRL, int ROW_MASK, int A, int B>
+__device__ __forceinline__ void seg_sum_step(int id, float (&v)[A][B])
+{
+    const bool join = dpp_i<CTRL, ROW_MASK>(INT_MIN, id) == id;
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float o = dpp_f<CTRL, ROW_MASK>(0.f, v[a][b]);
+            if (join) v[a][b] += o;
+        }
+}
+
+// Inclusive segmented sum over the wave: runs are lanes with equal ids, and
+// ids never decrease from one lane to the next among the lanes that may
+// join (any other lane carries an id no lane shares), so two lanes with one
+// id enclose a single run.  Within each row of 16 lanes the partial sums
+// shift by 1, 2, 4 and 8 lanes (Hillis-Steele); then lane 15 of rows 0 and 2
+// feeds rows 1 and 3, and lane 31 feeds rows 2 and 3, which completes every
+// run across rows: each lane ends with the sum over its run up to itself.
+template <int A, int B>
+__device__ __forceinline__ void seg_sum_wave(int id, float (&v)[A][B])
+{
+    seg_sum_step<0x111, 0xf>(id, v);
+    seg_sum_step<0x112, 0xf>(id, v);
+    seg_sum_step<0x114, 0xf>(id, v);
+    seg_sum_step<0x118, 0xf>(id, v);
+    seg_sum_step<0x142, 0xa>(id, v);
+    seg_sum_step<0x143, 0xc>(id, v);
+}
 
 // Sum over the lanes l, l ^ from, l ^ 2 from, ... (from a power of two < 64):
 // afterwards every lane holds the sum over its coset.

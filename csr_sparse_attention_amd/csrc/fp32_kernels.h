@@ -532,38 +532,29 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
                 for (int j = 0; j < NV; ++j)
 #pragma unroll
                     for (int t = 0; t < VEC; ++t) v[j][t] = w[u] * xv[u][j][t];
-                // inclusive segmented scan across lanes
-#pragma unroll
-                for (int off = 1; off < CSR_WAVE; off <<= 1) {
-                    const int io = __shfl_up(i, off, CSR_WAVE);
-                    const bool join = lane >= off && io == i;
-#pragma unroll
-                    for (int j = 0; j < NV; ++j)
-#pragma unroll
-                        for (int t = 0; t < VEC; ++t) {
-                            const float o = __shfl_up(v[j][t], off, CSR_WAVE);
-                            if (join) v[j][t] += o;
-                        }
-                }
+                // inclusive segmented scan across lanes (row ids never
+                // decrease over the lanes holding entries; lanes past the end
+                // carry ids no other lane has)
+                seg_sum_wave(i, v);
                 if (i == carry_row) {
 #pragma unroll
                     for (int j = 0; j < NV; ++j)
 #pragma unroll
                         for (int t = 0; t < VEC; ++t) v[j][t] += carry[j][t];
                 }
-                const int inext = __shfl_down(i, 1, CSR_WAVE);
+                const int inext = next_lane_i(INT_MIN, i);
                 const bool ok = e < y1;
                 const bool tail = ok && (lane == CSR_WAVE - 1 || inext != i);
                 const bool row_last = ok && (e == min(rp[i + 1], y1) - 1);
                 if (tail && row_last) emit(i, v);
                 // the run of the last lane continues into the next batch unless its row ended
-                const int last_i = __shfl(i, CSR_WAVE - 1, CSR_WAVE);
-                const bool last_done = __shfl((int)row_last, CSR_WAVE - 1, CSR_WAVE) != 0;
+                const int last_i = lane63_i(i);
+                const bool last_done = lane63_i((int)row_last) != 0;
                 carry_row = last_done ? -1 : last_i;
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
 #pragma unroll
-                    for (int t = 0; t < VEC; ++t) carry[j][t] = __shfl(v[j][t], CSR_WAVE - 1, CSR_WAVE);
+                    for (int t = 0; t < VEC; ++t) carry[j][t] = lane63_f(v[j][t]);
             }
         }
     }
