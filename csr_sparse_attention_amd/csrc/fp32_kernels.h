@@ -103,6 +103,50 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
     }
 }
 
+// SpMM with one row per wave (W = 64): the row's columns and values are
+// read 64 at a time, one entry per lane, and each gather takes its column
+// and weight from that lane (readlane), so the gathers of a batch of U
+// entries wait on one coalesced load per 64 entries instead of on their own
+// column loads.  b and e must be wave-uniform.
+template <int VEC, int NV, int U>
+__device__ __forceinline__ void gather_acc_wave(float (&acc)[NV][VEC], const int32_t* col, const float* ev, int b,
+                                                int e, const float* X, int64_t ldx, const Lanes<VEC, NV>& L, int F)
+{
+    const int lane = lane_id();
+    for (int base = b; base < e; base += CSR_WAVE) {
+        const int n = min(CSR_WAVE, e - base);
+        const int cl = lane < n ? col[base + lane] : 0;
+        const float wl = lane < n ? (ev ? ev[base + lane] : 1.f) : 0.f;
+        for (int i = 0; i < n; i += U) {
+            float xv[U][NV][VEC];
+            float w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = i + u < n;
+                const int k = ok ? i + u : 0;
+                const int c = __builtin_amdgcn_readlane(cl, k);
+                w[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 0.f;
+                const float* xr = X + (int64_t)c * ldx;
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    if (ok && L.valid(j, F)) {
+                        vload<VEC>(xv[u][j], xr + L.off(j));
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) xv[u][j][v] = 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[j][v] = fmaf(w[u], xv[u][j][v], acc[j][v]);
+        }
+    }
+}
+
 // Softmax statistics (max, sum of exp) of scale * ev[e] over e = kb + t, kb + t + n, ...
 // for this lane's t, merged over the n lanes (an aligned power-of-two set).
 __device__ __forceinline__ void seg_softmax_stats(const float* ev, int kb, int ke, int t, int n,
@@ -253,7 +297,11 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
         if constexpr (OP == Op::Attention) {
             seg_softmax_stats(a.ev, b, e, L.lg, a.W, a.scale, m, l);
         }
-        gather_acc<OP, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, a.X, a.ldx, L, a.F, a.scale, m);
+        if (OP == Op::Spmm && a.W == CSR_WAVE)
+            gather_acc_wave<VEC, NV, U>(acc, a.col_idx, a.ev, __builtin_amdgcn_readfirstlane(b),
+                                        __builtin_amdgcn_readfirstlane(e), a.X, a.ldx, L, a.F);
+        else
+            gather_acc<OP, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, a.X, a.ldx, L, a.F, a.scale, m);
         float* dst = a.Y + row * a.ldy;
         if (OP == Op::Attention && e > b)
             store_row_div<VEC, NV>(dst, acc, L, a.F, l);
