@@ -34,3 +34,25 @@ def test_per_entry_array_of_the_wrong_length_is_caught():
     with pytest.raises(AssertionError):
         bench.check_shapes([_call("spmm", (rp, torch.zeros(40, dtype=torch.int32), torch.zeros(39),
                                            torch.zeros(5, 3)), 10, 40)])
+
+
+def test_committed_traffic_records_are_self_consistent():
+    # each record's per-launch bytes follow from its counter medians and the
+    # copy-calibrated factors, and names sources that exist and a summary file
+    import json
+
+    root = os.path.join(os.path.dirname(__file__), "..")
+    with open(os.path.join(root, "profiles", "traffic.json")) as f:
+        recs = json.load(f)
+    assert recs.get("c2"), "the default workload has a record"
+    for config, lst in recs.items():
+        for r in (lst if isinstance(lst, list) else [lst]):
+            fk = r["fetch_kib"] if isinstance(r["fetch_kib"], list) else [r["fetch_kib"]]
+            wk = r["write_kib"] if isinstance(r["write_kib"], list) else [r["write_kib"]]
+            want = sum(f * r["fetch_factor"] * 1024 + w * r["write_factor"] * 1024 for f, w in zip(fk, wk))
+            assert abs(r["traffic_bytes"] - want) <= 1, (config, r["call"])
+            assert 1.9 < r["fetch_factor"] < 2.1 and 0.95 < r["write_factor"] < 1.05
+            assert set(r["schedule"]) <= {"mapping", "vec", "group_lanes", "passes", "chunk_items", "long_row"}
+            for src in r["sources"]:
+                assert os.path.exists(os.path.join(root, src)), src
+            assert os.path.exists(os.path.join(root, r["profile"]))
