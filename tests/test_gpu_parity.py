@@ -751,8 +751,9 @@ def test_hybrid_format_bit_exact(graph, P, T):
         assert torch.equal(getattr(h, k), getattr(h2, k))
 
 
+# F = 300: one segment per wave in the row-group mapping (64 lanes, 2 passes of 4)
 @pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
-@pytest.mark.parametrize("F", [1, 4, 32, 100])
+@pytest.mark.parametrize("F", [1, 4, 32, 100, 300])
 def test_hybrid_spmm_every_schedule(graph, F):
     csr = _format_graph(graph)
     rng = np.random.default_rng(1100 + F)
