@@ -57,6 +57,17 @@ struct DeviceGuard {
     }
 };
 
+// The context's lock for the whole of a call that may record an error (none
+// for a NULL context): the checks, the error message and the work of one call
+// are serialised with the other calls on the context.
+struct CtxLock {
+    std::unique_lock<std::mutex> lk;
+    explicit CtxLock(csr_context_t ctx)
+    {
+        if (ctx) lk = std::unique_lock<std::mutex>(ctx->mu);
+    }
+};
+
 int set_err(csr_context_t ctx, int code, const std::string& msg)
 {
     if (ctx) ctx->last_error = msg;
@@ -692,9 +703,9 @@ static int transpose_args(int64_t n_rows, int64_t n_cols, int64_t nnz)
 int csr_transpose_workspace_size(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, size_t* bytes)
 {
     if (!ctx || !bytes) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
     const int rc = transpose_args(n_rows, n_cols, nnz);
     if (rc != CSR_OK) return set_err(ctx, rc, "bad sizes");
-    std::lock_guard<std::mutex> lk(ctx->mu);
     if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
     DeviceGuard g(ctx->device);
     hipError_t e = csrk::transpose_workspace(n_cols, nnz, bytes);
@@ -708,10 +719,10 @@ int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
 {
     if (!ctx || !row_ptr || !t_row_ptr) return CSR_ERR_NULL;
     if (nnz > 0 && (!col_idx || !t_col_idx || !t_perm || !workspace)) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
     const int rc = transpose_args(n_rows, n_cols, nnz);
     if (rc != CSR_OK) return set_err(ctx, rc, "bad sizes");
     try {
-        std::lock_guard<std::mutex> lk(ctx->mu);
         ctx->last_error.clear();
         if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
         DeviceGuard g(ctx->device);
@@ -737,10 +748,10 @@ int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
 int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const float* src, float* dst, void* stream)
 {
     if (!ctx) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
     if (n < 0 || n >= ((int64_t)1 << 31)) return set_err(ctx, CSR_ERR_SHAPE, "bad size");
     if (n > 0 && (!perm || !src || !dst)) return CSR_ERR_NULL;
     if (n > 0 && src == dst) return set_err(ctx, CSR_ERR_SHAPE, "src and dst must not alias");
-    std::lock_guard<std::mutex> lk(ctx->mu);
     if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
     DeviceGuard g(ctx->device);
     CSR_HIP(ctx, csrk::launch_gather_values(perm, src, dst, n, static_cast<hipStream_t>(stream)));
@@ -768,9 +779,9 @@ int csr_hybrid_capacity(int64_t n_rows, int64_t nnz, int32_t parts, int64_t* seg
 int csr_hybrid_build_workspace_size(csr_context_t ctx, int64_t n_rows, int64_t nnz, int32_t parts, size_t* bytes)
 {
     if (!ctx || !bytes) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
     int64_t cap = 0;
     if (csr_hybrid_capacity(n_rows, nnz, parts, &cap) != CSR_OK) return set_err(ctx, CSR_ERR_SHAPE, "bad sizes or parts");
-    std::lock_guard<std::mutex> lk(ctx->mu);
     if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
     DeviceGuard g(ctx->device);
     hipError_t e = csrk::hybrid_build_workspace(n_rows, nnz, parts, bytes);
@@ -805,12 +816,12 @@ int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* c
                      void* workspace, size_t ws_bytes, void* stream)
 {
     if (!ctx || !row_ptr || !h) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->last_error.clear();
     int rc = check_hybrid(ctx, h, false);
     if (rc != CSR_OK) return rc;
     if (!workspace || (h->nnz > 0 && !col_idx)) return CSR_ERR_NULL;
     try {
-        std::lock_guard<std::mutex> lk(ctx->mu);
-        ctx->last_error.clear();
         if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
         DeviceGuard g(ctx->device);
         size_t need = 0;
@@ -882,6 +893,7 @@ int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t 
                               const csr_schedule_t* sched, size_t* bytes)
 {
     if (!bytes) return CSR_ERR_NULL;
+    CtxLock lk(ctx);
     int rc = check_hybrid(ctx, h, true);
     if (rc != CSR_OK) return rc;
     if (op != CSR_OP_SPMM && op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "the format serves SpMM and SDDMM");
@@ -978,10 +990,10 @@ int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals,
                     size_t ws_bytes, void* stream)
 {
     if (!ctx || !X || !Y) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->last_error.clear();
     if (F < 1 || ldy < F) return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
     try {
-        std::lock_guard<std::mutex> lk(ctx->mu);
-        ctx->last_error.clear();
         HybridCall c;
         int rc = hybrid_call(ctx, h, CSR_OP_SPMM, F, vals, 0, X, ldx, sched, workspace, ws_bytes, stream, nullptr, &c);
         if (rc != CSR_OK) return rc;
@@ -1016,10 +1028,10 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
                       csr_schedule_t* out, uint64_t* signature)
 {
     if (!ctx || !call || !out) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->last_error.clear();
     if (mode > CSR_SELECT_ESTIMATE) return set_err(ctx, CSR_ERR_SHAPE, "unknown selection mode");
     try {
-        std::lock_guard<std::mutex> lk(ctx->mu);
-        ctx->last_error.clear();
         HybridCall c;
         int rc = hybrid_call(ctx, h, call->op, call->width, call->a, call->ld_a, call->b, call->ld_b, nullptr,
                              call->workspace, call->workspace_bytes, call->stream, static_cast<float*>(call->out), &c);
@@ -1040,10 +1052,10 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
 int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_schedule_t* out, uint64_t* signature)
 {
     if (!ctx || !p || !out) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->last_error.clear();
     if (mode > CSR_SELECT_ESTIMATE) return set_err(ctx, CSR_ERR_SHAPE, "unknown selection mode");
     try {
-        std::lock_guard<std::mutex> lk(ctx->mu);
-        ctx->last_error.clear();
         DeviceGuard g(ctx->device);
         return select_locked(ctx, *p, mode, out, signature);
     } catch (...) {
@@ -1054,6 +1066,7 @@ int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_sch
 int csr_default_schedule(csr_context_t ctx, const csr_problem_t* p, csr_schedule_t* out)
 {
     if (!p || !out) return CSR_ERR_NULL;
+    CtxLock lk(ctx);
     std::string why;
     int rc = csrh::check_problem(*p, false, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);
@@ -1070,6 +1083,7 @@ int csr_hybrid_plan(csr_context_t ctx, const csr_problem_t* p, const int64_t* hi
                     int32_t* whole_below)
 {
     if (!p || !parts) return CSR_ERR_NULL;
+    CtxLock lk(ctx);
     std::string why;
     int rc = csrh::check_problem(*p, false, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);
@@ -1084,6 +1098,7 @@ int csr_candidates(csr_context_t ctx, const csr_problem_t* p, const int64_t* his
                    int32_t max, int32_t* n)
 {
     if (!p || !n || (max > 0 && !out)) return CSR_ERR_NULL;
+    CtxLock lk(ctx);
     std::string why;
     int rc = csrh::check_problem(*p, false, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);
@@ -1096,6 +1111,7 @@ int csr_candidates(csr_context_t ctx, const csr_problem_t* p, const int64_t* his
 int csr_workspace_size(csr_context_t ctx, const csr_problem_t* p, const csr_schedule_t* sched, size_t* bytes)
 {
     if (!p || !bytes) return CSR_ERR_NULL;
+    CtxLock lk(ctx);
     std::string why;
     int rc = csrh::check_problem(*p, false, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);

@@ -43,7 +43,10 @@
  *  - Every call returns a csr_status (0 = CSR_OK).  No C++ exception or abort
  *    crosses the ABI.  On error nothing has been written to the outputs
  *    unless stated; csr_last_error() gives a message.
- *  - Calls on one context are serialised by an internal mutex.
+ *  - Calls on one context are serialised by an internal mutex, argument
+ *    checks and error messages included, so a context may be shared by
+ *    threads; csr_last_error() then gives the message of the last failed
+ *    call from any thread, valid until the next call on the context.
  */
 #ifndef CSRSA_H
 #define CSRSA_H

@@ -327,3 +327,43 @@ def test_hybrid_capacity_and_host_only_context():
     b = ctypes.c_size_t()
     assert lib.csr_hybrid_build_workspace_size(ctx.handle, 10, 100, 4, ctypes.byref(b)) == -11
     ctx.close()
+
+
+def test_context_shared_by_threads():
+    # calls on one context from several threads (ctypes drops the GIL during
+    # the call): failing and succeeding host-side calls interleave, each
+    # returns its own status, and the context stays usable
+    import threading
+
+    lib = csa.load_library()
+    ctx = csa.Context(-1, None)
+    good = problem(_ffi.OP_SPMM, width=602)
+    bad = problem(_ffi.OP_SPMM, width=0)
+    errors = []
+
+    def work(seed):
+        n = ctypes.c_size_t()
+        s = csa.CsrSchedule()
+        P, T = ctypes.c_int32(), ctypes.c_int32()
+        for i in range(2000):
+            if (i + seed) % 2:
+                rc = lib.csr_workspace_size(ctx.handle, ctypes.byref(bad), None, ctypes.byref(n))
+                if rc != -2:
+                    errors.append(("bad", rc))
+            else:
+                if lib.csr_default_schedule(ctx.handle, ctypes.byref(good), ctypes.byref(s)) != 0:
+                    errors.append(("default", i))
+                if lib.csr_hybrid_plan(ctx.handle, ctypes.byref(good), None, ctypes.byref(P), ctypes.byref(T)) != 0:
+                    errors.append(("plan", i))
+                if lib.csr_hybrid_build_workspace_size(ctx.handle, 10, 100, 4, ctypes.byref(n)) != -11:
+                    errors.append(("host-only", i))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
+    msg = lib.csr_last_error(ctx.handle).decode()
+    assert msg  # the message of one of the failed calls
+    ctx.close()
