@@ -992,7 +992,7 @@ int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals,
     if (!ctx || !X || !Y) return CSR_ERR_NULL;
     std::lock_guard<std::mutex> lk(ctx->mu);
     ctx->last_error.clear();
-    if (F < 1 || ldy < F) return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
+    if (F < 1 || ldy < F || ldy >= ((int64_t)1 << 30)) return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
     try {
         HybridCall c;
         int rc = hybrid_call(ctx, h, CSR_OP_SPMM, F, vals, 0, X, ldx, sched, workspace, ws_bytes, stream, nullptr, &c);

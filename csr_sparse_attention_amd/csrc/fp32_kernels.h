@@ -67,31 +67,61 @@ __device__ __forceinline__ float edge_weight(const float* ev, int e, float scale
     }
 }
 
+// Row addresses: leading dimensions are below 2^30 elements, so a row's byte
+// offset is one 32 x 32 -> 64-bit multiply-add of the column index.
+__device__ __forceinline__ const char* row_at(const char* base, int32_t row, uint32_t row_bytes)
+{
+    return base + (uint64_t)(uint32_t)row * row_bytes;
+}
+
 // acc += sum over entries e = kb, kb + step, ... < ke of w_e * X[col[e], lane features].
 // col / ev are indexed directly by e (they may point into LDS or global memory).
+// Batches of U entries run without per-entry tests; only the last, partial
+// batch is masked.  Lanes past the width read the row's first features (in
+// bounds) and accumulate values that are never stored.
 template <Op OP, int VEC, int NV, int U>
 __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t* col, const float* ev,
                                            int kb, int ke, int step, const float* X, int64_t ldx,
                                            const Lanes<VEC, NV>& L, int F, float scale, float m)
 {
-    for (int k = kb; k < ke; k += step * U) {
+    uint32_t off[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) off[j] = L.valid(j, F) ? (uint32_t)L.off(j) * 4u : 0u;
+    const uint32_t row_bytes = (uint32_t)ldx * 4u;
+    const char* xb = reinterpret_cast<const char*>(X);
+    int k = kb;
+    for (; k + (U - 1) * step < ke; k += step * U) {
         float xv[U][NV][VEC];
         float w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int e = k + u * step;
-            bool ok = e < ke;
-            int c = ok ? col[e] : 0;
+            const int e = k + u * step;
+            w[u] = edge_weight<OP>(ev, e, scale, m);
+            const char* xr = row_at(xb, col[e], row_bytes);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) vload<VEC>(xv[u][j], reinterpret_cast<const float*>(xr + off[j]));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[j][v] = fmaf(w[u], xv[u][j][v], acc[j][v]);
+    }
+    if (k < ke) {
+        float xv[U][NV][VEC];
+        float w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = k + u * step;
+            const bool ok = e < ke;
             w[u] = ok ? edge_weight<OP>(ev, e, scale, m) : 0.f;
-            const float* xr = X + (int64_t)c * ldx;
+            if (ok) {
+                const char* xr = row_at(xb, col[e], row_bytes);
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                if (ok && L.valid(j, F)) {
-                    vload<VEC>(xv[u][j], xr + L.off(j));
-                } else {
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) xv[u][j][v] = 0.f;
-                }
+                for (int j = 0; j < NV; ++j) vload<VEC>(xv[u][j], reinterpret_cast<const float*>(xr + off[j]));
+            } else {
+                zero(xv[u]);
             }
         }
 #pragma unroll

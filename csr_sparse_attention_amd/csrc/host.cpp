@@ -125,10 +125,14 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
             return fail(CSR_ERR_SHAPE, "feature width not supported");
         if (!natural_layout(p.width, max_vec_f32(p), &W, &nv))
             return fail(CSR_ERR_SHAPE, "feature width too large for the operands' alignment");
+        // leading dimensions below 2^30 elements: row strides in bytes fit 32 bits
+        const int64_t ld_lim = (int64_t)1 << 30;
         if (p.op == CSR_OP_SDDMM) {
             if (p.ld_a < p.width || p.ld_b < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < K");
+            if (p.ld_a >= ld_lim || p.ld_b >= ld_lim) return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
         } else {
             if (p.ld_b < p.width || p.ld_out < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < F");
+            if (p.ld_b >= ld_lim || p.ld_out >= ld_lim) return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
         }
         if (!aligned(p.a, 4) || !aligned(p.b, 4) || !aligned(p.out, 4))
             return fail(CSR_ERR_ALIGN, "fp32 operands must be 4-byte aligned");

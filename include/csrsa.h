@@ -27,8 +27,8 @@
  *    (duplicates add in SpMM and are separate terms of a row's softmax).
  *    The library never writes row_ptr or col_idx (they pass through bit-exact).
  *  - Dense matrices are row-major with a leading dimension (elements between
- *    consecutive rows) >= their width.  Index arithmetic is 64-bit, so a
- *    dense operand may exceed 2^31 elements; nnz must be < 2^31.
+ *    consecutive rows) >= their width and < 2^30.  Index arithmetic is
+ *    64-bit, so a dense operand may exceed 2^31 elements; nnz must be < 2^31.
  *  - Outputs are fully overwritten (including zero rows for rows without
  *    entries); no pre-zeroing is needed.  Inputs are never modified.
  *  - The caller owns all memory.  The library allocates no device memory on

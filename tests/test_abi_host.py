@@ -367,3 +367,16 @@ def test_context_shared_by_threads():
     msg = lib.csr_last_error(ctx.handle).decode()
     assert msg  # the message of one of the failed calls
     ctx.close()
+
+
+@pytest.mark.parametrize("op", [_ffi.OP_SPMM, _ffi.OP_SDDMM, _ffi.OP_ATTENTION])
+def test_leading_dimension_bound(op):
+    # row strides in bytes fit 32 bits: leading dimensions below 2^30 elements
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+    ok = problem(op, width=64, ld=(1 << 30) - 64)
+    assert lib.csr_workspace_size(None, ctypes.byref(ok), None, ctypes.byref(n)) == 0
+    for field in (("ld_a", "ld_b") if op == _ffi.OP_SDDMM else ("ld_b", "ld_out")):
+        bad = problem(op, width=64)
+        setattr(bad, field, 1 << 30)
+        assert lib.csr_workspace_size(None, ctypes.byref(bad), None, ctypes.byref(n)) == -2, field
