@@ -23,6 +23,7 @@ from ._ffi import (  # noqa: F401,E402
     MAP_MERGEPATH,
     MAP_ROWGROUP,
     MAP_SEGSCAN,
+    SCHED_WIDE,
     CTX_NO_PROBE,
     CTX_VALIDATE,
     load as load_library,

@@ -22,6 +22,7 @@ CSR_ERR_NO_CACHE_ENTRY = -8
 OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX, OP_SOFTMAX_BWD = 1, 2, 3, 4, 5, 6
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAP_ROWGROUP, MAP_MERGEPATH, MAP_SEGSCAN = 1, 2, 3
+SCHED_WIDE = 1  # schedule flag: 16-byte lanes over 4-byte aligned rows (SpMM, row-group)
 CTX_VALIDATE, CTX_NO_PROBE = 1, 2
 SELECT_MODES = {"auto": 0, "replay": 1, "probe": 2, "estimate": 3}
 SCHEDULE_VERSION = 1

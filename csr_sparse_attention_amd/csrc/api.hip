@@ -258,7 +258,9 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     a.ldx = p.ld_b;
     a.Y = static_cast<float*>(p.out);
     a.ldy = p.ld_out;
-    if (p.op == CSR_OP_SPMM) {
+    if (p.op == CSR_OP_SPMM && (s.flags & CSR_SCHED_WIDE)) {
+        CSR_HIP(ctx, csrk::launch_spmm_wide(s.passes, a, st));
+    } else if (p.op == CSR_OP_SPMM) {
         CSR_HIP(ctx, csrk::launch_spmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
         if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_spmm_fixup(s.vec, s.passes, a, st));
     } else {

@@ -340,6 +340,86 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
     }
 }
 
+// 4 floats at a 4-byte aligned address: one 16-byte access (the hardware
+// takes dword-aligned multi-dword loads and stores).
+typedef float float4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Row-group SpMM with wide lanes: one row per wave, 4 floats per lane in each
+// of NV passes of 64 lanes, over rows that are only 4-byte aligned or whose
+// width is not a multiple of 4.  Lane l of pass j covers features
+// off = (j * 64 + l) * 4 ..; the lane whose 4 floats would pass the width F
+// reads the 4 ending at F instead (shift = off - (F - 4)) and writes the top
+// F - off of its sums, so every access stays inside its row; lanes past the
+// width read the row's first 4 floats and write nothing.  Columns and values
+// are read 64 at a time, one per lane, and each gather takes its column from
+// that lane (readlane).
+template <int NV, int U>
+__global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup_wide(Fp32Args a)
+{
+    const int lane = lane_id();
+    const int64_t row = ((int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x) / CSR_WAVE;
+    if (row >= a.n_rows) return;  // whole waves: no wave is split by this test
+    const int b = __builtin_amdgcn_readfirstlane(a.row_ptr[row]);
+    const int e = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]);
+    const int F = a.F;
+    uint32_t lo[NV];  // byte offset of the lane's 4 floats in a row
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int off = (j * CSR_WAVE + lane) * 4;
+        lo[j] = (uint32_t)(off + 4 <= F ? off : (off < F ? F - 4 : 0)) * 4u;
+    }
+    const uint32_t row_bytes = (uint32_t)a.ldx * 4u;
+    const char* xb = reinterpret_cast<const char*>(a.X);
+    float4_a4 acc[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[j] = float4_a4{0.f, 0.f, 0.f, 0.f};
+    for (int base = b; base < e; base += CSR_WAVE) {
+        const int n = min(CSR_WAVE, e - base);
+        const int cl = lane < n ? a.col_idx[base + lane] : 0;
+        const float wl = lane < n ? (a.ev ? a.ev[base + lane] : 1.f) : 0.f;
+        for (int i = 0; i < n; i += U) {
+            float4_a4 xv[U][NV];
+            float w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = i + u < n;
+                const int k = ok ? i + u : 0;
+                const char* xr = row_at(xb, __builtin_amdgcn_readlane(cl, k), row_bytes);
+                w[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 0.f;
+#pragma unroll
+                for (int j = 0; j < NV; ++j) xv[u][j] = *reinterpret_cast<const float4_a4*>(xr + lo[j]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    acc[j].x = fmaf(w[u], xv[u][j].x, acc[j].x);
+                    acc[j].y = fmaf(w[u], xv[u][j].y, acc[j].y);
+                    acc[j].z = fmaf(w[u], xv[u][j].z, acc[j].z);
+                    acc[j].w = fmaf(w[u], xv[u][j].w, acc[j].w);
+                }
+        }
+    }
+    float* dst = a.Y + row * a.ldy;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int off = (j * CSR_WAVE + lane) * 4;
+        if (off + 4 <= F) {
+            float4_a4* d = reinterpret_cast<float4_a4*>(dst + off);
+            if (a.stream_y)
+                __builtin_nontemporal_store(acc[j], d);
+            else
+                *d = acc[j];
+        } else if (off < F) {  // the top F - off of the 4 floats ending at F
+            const int sh = off - (F - 4);
+            for (int t = 0; t < F - off; ++t) {
+                const int i = sh + t;
+                dst[off + t] = i == 1 ? acc[j].y : (i == 2 ? acc[j].z : acc[j].w);  // i >= 1 here
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Merge-path mapping
 // ---------------------------------------------------------------------------

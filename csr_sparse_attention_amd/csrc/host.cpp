@@ -174,9 +174,21 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
         if (s.group_lanes != 1 || s.passes > 4 || s.long_row != 0)
             return fail("segmented-scan schedules take group_lanes 1, passes <= 4, long_row 0");
     }
-    if (s.flags != 0) return fail("unknown schedule flags");
+    if (s.flags & ~CSR_SCHED_WIDE) return fail("unknown schedule flags");
     for (int r : s.reserved)
         if (r != 0) return fail("reserved schedule fields must be 0");
+    if (s.flags & CSR_SCHED_WIDE) {
+        // 4 floats per lane at any 4-byte alignment, 64 lanes per row, the
+        // last lane's vector ending at the width
+        if (p.op != CSR_OP_SPMM || s.mapping != CSR_MAP_ROWGROUP)
+            return fail("wide lanes serve SpMM with the row-group mapping");
+        if (p.width < 4) return fail("wide lanes need a width of at least 4");
+        if (s.vec != 4 || s.group_lanes != 64 || s.chunk_items != 0 || s.long_row != 0)
+            return fail("wide lanes take vec 4, 64 lanes per row, chunk_items = long_row = 0");
+        if (s.passes != nv_up((p.width + 255) / 256))
+            return fail("wide lanes take the fewest supported passes covering width / 256");
+        return CSR_OK;
+    }
     if (s.mapping != CSR_MAP_ROWGROUP) {
         if (s.chunk_items != 256 && s.chunk_items != 512 && s.chunk_items != 1024) return fail("chunk_items must be 256, 512 or 1024");
         if (s.long_row < 0) return fail("long_row must be >= 0");
@@ -341,6 +353,15 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
         s.chunk_items = 0;
         s.long_row = 0;
         add(s);
+        // wide lanes where the operands allow only narrower aligned accesses
+        if (p.op == CSR_OP_SPMM && p.width >= 64 && (max_vec_f32(p) < 4 || p.width % 4)) {
+            s.vec = 4;
+            s.group_lanes = 64;
+            s.passes = nv_up((p.width + 255) / 256);
+            s.flags = CSR_SCHED_WIDE;
+            add(s);
+            s.flags = 0;
+        }
     }
     if (p.op != CSR_OP_MHA) {
         // half the lanes per row, twice the passes: more rows in flight
@@ -390,9 +411,13 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
     const double esize = (p.op == CSR_OP_MHA) ? 2.0 : 4.0;
     const double gathers = (p.op == CSR_OP_MHA) ? 2.0 : 1.0;
     const double row_bytes = p.width * esize * gathers;
-    const double lanes_used = (p.op == CSR_OP_MHA) ? 1.0
+    // wide lanes: idle lanes read lines that their pass reads anyway, and
+    // 16-byte accesses gather about 0.82x the time of 8-byte ones (measured)
+    const bool wide = (s.flags & CSR_SCHED_WIDE) != 0;
+    const double lanes_used = (p.op == CSR_OP_MHA || wide) ? 1.0
         : (double)p.width / ((double)s.group_lanes * s.vec * s.passes);
-    const double bytes = p.nnz * (8.0 + row_bytes / (lanes_used > 0 ? lanes_used : 1.0)) + p.n_rows * p.width * 4.0;
+    const double bytes = p.nnz * (8.0 + (wide ? 0.82 : 1.0) * row_bytes / (lanes_used > 0 ? lanes_used : 1.0)) +
+                         p.n_rows * p.width * 4.0;
     double t = bytes / bw;
     const double max_deg = hist ? (double)hist[66] : 0.0;
     if (s.mapping == CSR_MAP_ROWGROUP) {

@@ -13,6 +13,26 @@ hipError_t launch_spmm_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s)
 {
     return dispatch_fixup<Op::Spmm>(vec, nv, a, s);
 }
+
+template <int NV>
+static hipError_t run_wide(const Fp32Args& a, hipStream_t s)
+{
+    constexpr int U = unroll_for(4, NV);
+    const int64_t blocks = (a.n_rows * CSR_WAVE + CSR_BLOCK - 1) / CSR_BLOCK;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_rowgroup_wide<NV, U>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_spmm_wide(int nv, const Fp32Args& a, hipStream_t s)
+{
+    if (a.F < 4 || (int64_t)nv * CSR_WAVE * 4 < a.F) return hipErrorInvalidValue;
+#define CSR_CASE(V, N) \
+    if (nv == N) return run_wide<N>(a, s);
+    CSR_NV_CASES(CSR_CASE, 4)
+#undef CSR_CASE
+    return hipErrorInvalidValue;
+}
 template <int VEC, int NV>
 static hipError_t run_hyb_reduce(int W, float* Y, int64_t ldy, const float* part, int32_t F,
                                  const int32_t* row_seg_ptr, const int32_t* row_seg, int64_t n_rows, hipStream_t s)

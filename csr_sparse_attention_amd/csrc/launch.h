@@ -34,6 +34,8 @@ constexpr int unroll_for(int vec, int nv)
 // (main pass; the fix-up is launched separately).
 hipError_t launch_spmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_spmm_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
+// row-group SpMM with wide lanes (one row per wave, 4 floats per lane, nv passes)
+hipError_t launch_spmm_wide(int nv, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
 hipError_t launch_sddmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);

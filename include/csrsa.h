@@ -106,6 +106,17 @@ enum csr_mapping {
                               (group_lanes 1, long_row 0, chunk_items 256, 512, 1024) */
 };
 
+/* Schedule flags. */
+enum csr_schedule_flags {
+    /* 16-byte lane accesses over rows that are only 4-byte aligned or whose
+     * width is not a multiple of 4: vec 4, 64 lanes per row, passes = the
+     * fewest supported counts covering width / 256; the lane whose 4 floats
+     * would pass the width reads the 4 ending at it (so every access stays
+     * inside its row, the last row of X included) and uses the top ones.
+     * SpMM with the row-group mapping only, width >= 4. */
+    CSR_SCHED_WIDE = 1
+};
+
 /* Context flags. */
 enum csr_ctx_flags {
     CSR_CTX_VALIDATE = 1u,   /* check row_ptr / col_idx on every call (one extra pass) */
@@ -136,7 +147,7 @@ typedef struct csr_schedule_s {
     int32_t passes;      /* feature passes per lane (width = W * vec * passes, rounded) */
     int32_t chunk_items; /* merge-path: rows + entries per wavefront chunk (256, 512, 1024) */
     int32_t long_row;    /* merge-path: a row segment this long is shared by the whole wave */
-    int32_t flags;       /* reserved, 0 */
+    int32_t flags;       /* enum csr_schedule_flags (0 = none) */
     int32_t reserved[7]; /* 0 */
 } csr_schedule_t;
 

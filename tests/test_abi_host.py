@@ -380,3 +380,44 @@ def test_leading_dimension_bound(op):
         bad = problem(op, width=64)
         setattr(bad, field, 1 << 30)
         assert lib.csr_workspace_size(None, ctypes.byref(bad), None, ctypes.byref(n)) == -2, field
+
+
+def test_wide_lane_schedules():
+    # 16-byte lanes over rows that are only 4-byte aligned: SpMM row groups of
+    # 64 lanes, passes = the fewest supported counts covering width / 256
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+
+    def wide(F, passes=None, **kw):
+        p = problem(kw.pop("op", _ffi.OP_SPMM), width=F)
+        s = csa.CsrSchedule.from_buffer_copy(bytes(csa.default_schedule(p)))
+        s.mapping, s.vec, s.group_lanes, s.chunk_items, s.long_row = _ffi.MAP_ROWGROUP, 4, 64, 0, 0
+        s.passes = passes if passes is not None else min(v for v in (1, 2, 3, 4, 5, 6, 8, 12, 16)
+                                                         if v * 256 >= F)
+        s.flags = _ffi.SCHED_WIDE
+        for k, v in kw.items():
+            setattr(s, k, v)
+        return lib.csr_workspace_size(None, ctypes.byref(p), ctypes.byref(s), ctypes.byref(n))
+
+    for F in (4, 5, 602, 777, 1023, 2600, 4096):
+        assert wide(F) == 0, F
+    assert wide(3) == -7                       # narrower than one vector
+    assert wide(602, passes=4) == -7           # not the fewest passes
+    assert wide(2600, passes=11) == -7         # unsupported pass count
+    assert wide(602, group_lanes=32) == -7
+    assert wide(602, vec=2) == -7
+    assert wide(602, mapping=_ffi.MAP_MERGEPATH, chunk_items=256) == -7
+    assert wide(602, flags=3) == -7            # unknown flag bit
+    assert wide(602, op=_ffi.OP_ATTENTION) == -7
+    # offered where the operands allow only narrower aligned accesses
+    hist = (ctypes.c_int64 * 67)()
+    hist[66] = 100
+    for F, ld, expect in ((602, 602, True), (600, 600, False), (600, 602, True), (32, 34, False)):
+        p = problem(_ffi.OP_SPMM, width=F, ld=ld)
+        out = (csa.CsrSchedule * 32)()
+        cnt = ctypes.c_int32()
+        assert lib.csr_candidates(None, ctypes.byref(p), hist, out, 32, ctypes.byref(cnt)) == 0
+        got = [out[i] for i in range(cnt.value) if out[i].flags == _ffi.SCHED_WIDE]
+        assert bool(got) == expect, (F, ld)
+        for s in got:
+            assert (s.vec, s.group_lanes, s.mapping) == (4, 64, _ffi.MAP_ROWGROUP)

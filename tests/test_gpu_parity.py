@@ -75,6 +75,14 @@ def schedules(problem, thorough=True):
                 s.group_lanes, s.passes = W, nv
                 s.mapping, s.chunk_items, s.long_row = csa.MAP_MERGEPATH, D, lr
                 out.append(s)
+    # SpMM row groups with wide lanes (4 floats per lane at any 4-byte alignment)
+    if problem.op == _ffi.OP_SPMM and problem.width >= 4:
+        s = csa.CsrSchedule.from_buffer_copy(bytes(base))
+        s.mapping, s.vec, s.group_lanes, s.chunk_items, s.long_row = csa.MAP_ROWGROUP, 4, 64, 0, 0
+        need = -(-problem.width // 256)
+        s.passes = min(v for v in (1, 2, 3, 4, 5, 6, 8, 12, 16) if v >= need)
+        s.flags = csa.SCHED_WIDE
+        out.append(s)
     # entry-parallel segmented scan for small widths (SpMM, SDDMM)
     if problem.op in (_ffi.OP_SPMM, _ffi.OP_SDDMM) and problem.width <= 4 * base.vec:
         for D in ((256, 512, 1024) if thorough else (512,)):
@@ -86,7 +94,7 @@ def schedules(problem, thorough=True):
 
 
 def sched_id(s):
-    return f"m{s.mapping}-w{s.group_lanes}-nv{s.passes}-v{s.vec}-d{s.chunk_items}-lr{s.long_row}"
+    return f"m{s.mapping}-w{s.group_lanes}-nv{s.passes}-v{s.vec}-d{s.chunk_items}-lr{s.long_row}-f{s.flags}"
 
 
 # ---------------------------------------------------------------------------
