@@ -52,7 +52,7 @@ def test_committed_traffic_records_are_self_consistent():
             want = sum(f * r["fetch_factor"] * 1024 + w * r["write_factor"] * 1024 for f, w in zip(fk, wk))
             assert abs(r["traffic_bytes"] - want) <= 1, (config, r["call"])
             assert 1.9 < r["fetch_factor"] < 2.1 and 0.95 < r["write_factor"] < 1.05
-            assert set(r["schedule"]) <= {"mapping", "vec", "group_lanes", "passes", "chunk_items", "long_row"}
+            assert set(r["schedule"]) <= {"mapping", "vec", "group_lanes", "passes", "chunk_items", "long_row", "flags"}
             for src in r["sources"]:
                 assert os.path.exists(os.path.join(root, src)), src
             assert os.path.exists(os.path.join(root, r["profile"]))
