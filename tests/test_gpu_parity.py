@@ -938,3 +938,40 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(outs[k], eager[k]), (r, k)
     ref, mag, _ = oracle.attention(csr.row_ptr, csr.col_idx, c["scores"], c["V"])
     assert_close(outs["att"].cpu().numpy(), ref, mag, TOL_F32, "graph attention")
+
+
+@pytest.mark.parametrize("F", [4, 5, 6, 7, 255, 257, 602, 1021, 2600, 4096])
+def test_wide_lanes_misaligned_operands(F):
+    # 4 floats per lane over rows that are only 4-byte aligned: X and Y are
+    # column views at an odd offset of wider buffers (odd leading dimensions),
+    # every remainder of F mod 4 and the 1, 2, 4, 12 and 16 pass layouts
+    # (a width above 1024 needs 16-byte aligned rows to be a valid problem:
+    # there the views start 4 floats in)
+    o = 1 if F <= 1024 else 4
+    csr = skew_graph(11, n_rows=700, n_cols=3000, giant=2500)
+    rng = np.random.default_rng(1200 + F)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    Xb = rng.standard_normal((csr.n_cols, F + 2 * o)).astype(np.float32)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, Xb[:, o:F + o], threads=oracle.default_threads())
+    rp, ci = pattern_dev(csr)
+    Xd = dev(Xb)[:, o:F + o]
+    Yd = torch.full((csr.n_rows, F + 4 * o), float("nan"), device="cuda")
+    Y = Yd[:, 3 * o:F + 3 * o]
+    p, _ = csa.make_problem("spmm", rp, ci, dev(vals), Xd, out=Y)
+    s = csa.CsrSchedule.from_buffer_copy(bytes(csa.default_schedule(p)))
+    s.mapping, s.vec, s.group_lanes, s.chunk_items, s.long_row = csa.MAP_ROWGROUP, 4, 64, 0, 0
+    s.passes = min(v for v in (1, 2, 3, 4, 5, 6, 8, 12, 16) if v * 256 >= F)
+    s.flags = csa.SCHED_WIDE
+    csa.spmm(rp, ci, dev(vals), Xd, out=Y, schedule=s)
+    torch.cuda.synchronize()
+    got = Yd.cpu().numpy()
+    assert_close(got[:, 3 * o:F + 3 * o], ref, mag, TOL_F32, f"wide F{F}")
+    assert np.isnan(got[:, :3 * o]).all() and np.isnan(got[:, F + 3 * o:]).all()  # nothing written outside Y
+    ones, omag = oracle.spmm(csr.row_ptr, csr.col_idx, None, Xb[:, o:F + o], threads=oracle.default_threads())
+    csa.spmm(rp, ci, None, Xd, out=Y, schedule=s)
+    assert_close(Y.cpu().numpy(), ones, omag, TOL_F32, f"wide F{F} unit values")
+    # over the format (partial rows with leading dimension F, then the sum)
+    h = csa.hybrid_format(rp, ci, csr.n_cols, 8, whole_below=16)
+    hv = csa.hybrid_values(h, dev(vals))
+    Yh = csa.hybrid_spmm(h, hv, Xd, schedule=s)
+    assert_close(Yh.cpu().numpy(), ref, mag, TOL_F32, f"wide F{F} over the format")
