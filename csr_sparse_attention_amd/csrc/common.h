@@ -143,6 +143,43 @@ __device__ __forceinline__ float dpp_f(float old, float v)
                                                       false));
 }
 
+// Every lane of an aligned group of W lanes (W a power of two <= 64) gets
+// the group's sum of v[k].  After the steps for distances 1 and 2 (quad
+// permutes [1,0,3,2] and [2,3,0,1]) each quad holds its sum in all lanes, so
+// the next steps may pair a lane with any lane of the other half of its
+// group: the half-row mirror (lane i of 8 with 7 - i) and the row mirror
+// (i of 16 with 15 - i), still on the DPP path; distance 16 is a swizzle
+// inside each 32 lanes, distance 32 a permute.  W is uniform over the wave.
+template <int N>
+__device__ __forceinline__ void group_sum_lanes(float (&v)[N], int W)
+{
+    if (W > 1) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += dpp_f<0xB1, 0xf>(0.f, v[k]);
+    }
+    if (W > 2) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += dpp_f<0x4E, 0xf>(0.f, v[k]);
+    }
+    if (W > 4) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += dpp_f<0x141, 0xf>(0.f, v[k]);
+    }
+    if (W > 8) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += dpp_f<0x140, 0xf>(0.f, v[k]);
+    }
+    if (W > 16) {
+        // bit mode: and 0x1f, or 0, xor 0x10
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[k]), 0x401F));
+    }
+    if (W > 32) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += shfl_xor(v[k], 32);
+    }
+}
+
 // Lane l + 1's value (lane 63: `old`).
 __device__ __forceinline__ int next_lane_i(int old, int v) { return dpp_i<0x130, 0xf>(old, v); }
 

@@ -274,10 +274,7 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
                 for (int v = 0; v < VEC; ++v) s = fmaf(u[j][v], xv[uu][j][v], s);
             d[uu] = s;
         }
-        for (int s = 1; s < L.W; s <<= 1) {
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu) d[uu] += shfl_xor(d[uu], s);
-        }
+        group_sum_lanes(d, L.W);
         if (L.lg == 0) {
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
