@@ -374,17 +374,28 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup_wide(Fp32Args a)
         const int n = min(CSR_WAVE, e - base);
         const int cl = lane < n ? a.col_idx[base + lane] : 0;
         const float wl = lane < n ? (a.ev ? a.ev[base + lane] : 1.f) : 0.f;
-        for (int i = 0; i < n; i += U) {
+        // U entries per batch, every load issued before the first multiply-add
+        auto batch = [&](int i, bool tail) {
             float4_a4 xv[U][NV];
             float w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool ok = i + u < n;
-                const int k = ok ? i + u : 0;
+                const int k = (i + u < n) ? i + u : 0;
                 const char* xr = row_at(xb, __builtin_amdgcn_readlane(cl, k), row_bytes);
-                w[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 0.f;
+                w[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
 #pragma unroll
                 for (int j = 0; j < NV; ++j) xv[u][j] = *reinterpret_cast<const float4_a4*>(xr + lo[j]);
+            }
+            if (tail) {
+                // padded entries (the same for the whole wave) add exact zeros:
+                // weighting their row by 0 would turn an infinite feature into NaN
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (i + u >= n) {
+                        w[u] = 0.f;
+#pragma unroll
+                        for (int j = 0; j < NV; ++j) xv[u][j] = float4_a4{0.f, 0.f, 0.f, 0.f};
+                    }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -395,7 +406,10 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup_wide(Fp32Args a)
                     acc[j].z = fmaf(w[u], xv[u][j].z, acc[j].z);
                     acc[j].w = fmaf(w[u], xv[u][j].w, acc[j].w);
                 }
-        }
+        };
+        int i = 0;
+        for (; i + U <= n; i += U) batch(i, false);
+        if (i < n) batch(i, true);
     }
     float* dst = a.Y + row * a.ldy;
 #pragma unroll

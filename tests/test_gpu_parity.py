@@ -975,3 +975,36 @@ def test_wide_lanes_misaligned_operands(F):
     hv = csa.hybrid_values(h, dev(vals))
     Yh = csa.hybrid_spmm(h, hv, Xd, schedule=s)
     assert_close(Yh.cpu().numpy(), ref, mag, TOL_F32, f"wide F{F} over the format")
+
+
+@pytest.mark.parametrize("F", [4, 602])
+def test_infinite_features_propagate_without_nan(F):
+    # X row 7 holds +inf in feature 0: every row with an entry in column 7
+    # (positive weights) gets +inf there and stays finite elsewhere; rows of
+    # 1-3 entries leave padded slots in the last batch of every mapping, which
+    # must add nothing (0 * inf would be NaN)
+    rng = np.random.default_rng(77 + F)
+    n_rows, n_cols = 300, 50
+    deg = rng.integers(0, 9, n_rows)
+    cols = [np.sort(rng.choice(n_cols, d, replace=False)) for d in deg]
+    for r in range(0, n_rows, 5):  # many rows start with column 7
+        if deg[r] > 0:
+            cols[r][0] = 7
+            cols[r] = np.sort(cols[r])
+    row_ptr = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    col_idx = np.concatenate(cols).astype(np.int32)
+    vals = rng.uniform(0.5, 1.5, col_idx.size).astype(np.float32)
+    X = rng.standard_normal((n_cols, F)).astype(np.float32)
+    X[7, 0] = np.inf
+    csr = CSR(n_rows, n_cols, row_ptr, col_idx)
+    ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=1)
+    rp, ci = pattern_dev(csr)
+    p, _ = csa.make_problem("spmm", rp, ci, dev(vals), dev(X))
+    has7 = np.array([7 in c for c in cols])
+    assert has7.sum() > 20
+    for s in schedules(p):
+        Y = csa.spmm(rp, ci, dev(vals), dev(X), schedule=s).cpu().numpy()
+        assert not np.isnan(Y).any(), sched_id(s)
+        assert np.isposinf(Y[has7, 0]).all() and np.isfinite(Y[~has7]).all(), sched_id(s)
+        fin = np.isfinite(ref)
+        assert_close(np.where(fin, Y, 0), np.where(fin, ref, 0), np.where(fin, mag, 1), TOL_F32, sched_id(s))
