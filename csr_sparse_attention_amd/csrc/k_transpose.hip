@@ -16,35 +16,34 @@ __global__ void k_iota(int32_t* v, int64_t n)
         v[i] = (int32_t)i;
 }
 
-// last row i in [lo, hi] with row_ptr[i] <= e
-__device__ __forceinline__ int64_t row_search(const int32_t* row_ptr, int64_t lo, int64_t hi, int64_t e)
-{
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (row_ptr[mid] <= e)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
-// rows[e] = the row holding entry e (the COO row array).  A block covers 256
-// consecutive entries: two full searches find the rows of its first and last
-// entry, and every entry is then searched only between those two rows (one
-// or two steps for rows of tens of entries).
+// rows[e] = the row holding entry e (the COO row array), written row by row:
+// a wave takes 64 consecutive rows and fills each row's entries with its
+// lanes, so consecutive rows' stores are adjacent and coalesced.  Row i's
+// range is [row_ptr[i], row_ptr[i + 1]) clamped to [0, nnz], with the first
+// row starting at 0 and the last ending at nnz: any entry x then lies in the
+// range of the last row whose start is <= x, so for every row_ptr each entry
+// receives a row in [0, n_rows) and no store leaves the array (a valid CSR
+// gives exactly its rows).
 __global__ __launch_bounds__(CSR_BLOCK) void k_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows,
                                                         int64_t nnz)
 {
-    __shared__ int64_t span[2];
-    const int64_t e0 = (int64_t)blockIdx.x * CSR_BLOCK;
-    if (threadIdx.x < 2) {
-        const int64_t e = threadIdx.x == 0 ? e0 : min(e0 + CSR_BLOCK, nnz) - 1;
-        span[threadIdx.x] = row_search(row_ptr, 0, n_rows - 1, e);
+    const int lane = lane_id();
+    const int64_t r0 = (int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x - lane;
+    if (r0 >= n_rows) return;
+    auto bound = [&](int64_t i) -> int32_t {
+        if (i == 0) return 0;
+        if (i == n_rows) return (int32_t)nnz;
+        const int32_t v = row_ptr[i];
+        return v < 0 ? 0 : (v > nnz ? (int32_t)nnz : v);
+    };
+    const int64_t r = r0 + lane;
+    const int32_t b = r < n_rows ? bound(r) : 0;
+    const int32_t e = r < n_rows ? bound(r + 1) : 0;
+    const int nr = (int)min((int64_t)CSR_WAVE, n_rows - r0);
+    for (int j = 0; j < nr; ++j) {
+        const int32_t bj = __builtin_amdgcn_readlane(b, j), ej = __builtin_amdgcn_readlane(e, j);
+        for (int32_t k = bj + lane; k < ej; k += CSR_WAVE) rows[k] = (int32_t)(r0 + j);
     }
-    __syncthreads();
-    const int64_t e = e0 + threadIdx.x;
-    if (e < nnz) rows[e] = (int32_t)row_search(row_ptr, span[0], span[1], e);
 }
 
 // t_row_ptr[c] = number of sorted column keys below c, for c in [0, n_cols]
@@ -63,17 +62,18 @@ __global__ void k_col_starts(const int32_t* keys, int64_t nnz, int32_t* t_row_pt
     }
 }
 
-__global__ void k_gather_rows(const int32_t* perm, const int32_t* src, int32_t* dst, int64_t n)
+// dst[k] = src[perm[k]], one entry per thread over a grid that covers all of
+// them: the waves in flight then cover one contiguous window of k (about
+// 1.8x faster on a power-law transpose than a grid-stride loop, whose
+// resident waves spread over the whole array)
+template <typename T>
+__global__ __launch_bounds__(CSR_BLOCK) void k_gather(const int32_t* perm, const T* src, T* dst, int64_t n)
 {
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
-        dst[k] = src[perm[k]];
+    const int64_t k = (int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x;
+    if (k < n) dst[k] = src[perm[k]];
 }
 
-__global__ void k_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n)
-{
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
-        dst[k] = src[perm[k]];
-}
+static unsigned full_grid(int64_t n) { return (unsigned)((n + CSR_BLOCK - 1) / CSR_BLOCK); }
 
 static unsigned grid_of(int64_t n)
 {
@@ -124,11 +124,9 @@ hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int6
     // the sort no longer needs the entry indices: their buffer takes the COO
     // rows, and each transposed entry's row is gathered through the permutation
     int32_t* rows = iota;
-    const int64_t blocks = (nnz + CSR_BLOCK - 1) / CSR_BLOCK;
-    hipLaunchKernelGGL(k_coo_rows, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
-    e = hipGetLastError();
+    e = launch_coo_rows(row_ptr, n_rows, rows, nnz, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gather_rows, dim3(grid_of(nnz)), dim3(CSR_BLOCK), 0, s, (const int32_t*)t_perm,
+    hipLaunchKernelGGL(k_gather<int32_t>, dim3(full_grid(nnz)), dim3(CSR_BLOCK), 0, s, (const int32_t*)t_perm,
                        (const int32_t*)rows, t_col_idx, nnz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -139,16 +137,15 @@ hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int6
 
 hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows, int64_t nnz, hipStream_t s)
 {
-    if (nnz == 0) return hipSuccess;
-    const int64_t blocks = (nnz + CSR_BLOCK - 1) / CSR_BLOCK;
-    hipLaunchKernelGGL(k_coo_rows, dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
+    if (nnz == 0 || n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_coo_rows, dim3(full_grid(n_rows)), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
     return hipGetLastError();
 }
 
 hipError_t launch_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gather_values, dim3(grid_of(n)), dim3(CSR_BLOCK), 0, s, perm, src, dst, n);
+    hipLaunchKernelGGL(k_gather<float>, dim3(full_grid(n)), dim3(CSR_BLOCK), 0, s, perm, src, dst, n);
     return hipGetLastError();
 }
 

@@ -599,6 +599,26 @@ def test_transpose_bit_exact(graph):
         assert np.array_equal(got, vals[want[2]])
 
 
+@pytest.mark.gpu
+def test_transpose_rows_in_range_for_unvalidated_row_ptr():
+    # A row_ptr that is not monotone (and not checked: no validation flag)
+    # still gives every transposed entry a row index inside [0, n_rows) and a
+    # permutation of the entries, so later products never index out of range.
+    n_rows, nnz = 6, 40
+    rp = np.array([0, 25, 3, 31, 12, 50, 40], np.int32)  # 50 > nnz is clamped
+    ci = np.random.default_rng(77).integers(0, 9, nnz).astype(np.int32)
+    t = csa.transpose(dev(rp), dev(ci), 9)
+    rows = t.col_idx.cpu().numpy()
+    assert rows.min() >= 0 and rows.max() < n_rows
+    assert np.array_equal(np.sort(t.perm.cpu().numpy()), np.arange(nnz))
+    # each entry lies in the clamped range of the row it was given (ranges of
+    # such a row_ptr overlap, so which of the covering rows is not fixed)
+    bounds = np.clip(rp, 0, nnz)
+    bounds[0], bounds[-1] = 0, nnz
+    entry = t.perm.cpu().numpy()
+    assert np.all((bounds[rows] <= entry) & (entry < bounds[rows + 1]))
+
+
 def _probs_and_grad(csr, seed, scale):
     rng = np.random.default_rng(seed)
     sc = (3 * rng.standard_normal(csr.nnz)).astype(np.float32)
