@@ -17,7 +17,8 @@ static hipError_t run_softmax(const SoftmaxArgs& a, hipStream_t s)
         hipLaunchKernelGGL((k_softmax_main<D>), dim3((unsigned)blocks), dim3(CSR_BLOCK), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t fblocks = (a.n_chunks + CSR_WAVE * CSR_WAVES_PER_BLOCK - 1) / (CSR_WAVE * CSR_WAVES_PER_BLOCK);
+    const int64_t fblocks =
+        (a.n_chunks + SM_FIX_CHUNKS * CSR_WAVES_PER_BLOCK - 1) / (SM_FIX_CHUNKS * CSR_WAVES_PER_BLOCK);
     hipLaunchKernelGGL((k_softmax_fixup<BWD>), dim3((unsigned)fblocks), dim3(CSR_BLOCK), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

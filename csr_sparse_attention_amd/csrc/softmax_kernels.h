@@ -400,14 +400,27 @@ __device__ __forceinline__ void softmax_fixup_one(const SoftmaxArgs& a, int64_t 
     }
 }
 
+// The fix-up and the long-row pass give each wave SM_FIX_CHUNKS consecutive
+// chunks (one lane reads each chunk's slots) and handle the chunks with work
+// one after the other.  Each such chunk costs a few dependent loads, so the
+// window is kept short: more waves share the work and their loads overlap
+// (with 64 chunks a wave, a few thousand waves each walked dozens of chunks).
+constexpr int SM_FIX_CHUNKS = 16;
+
+__device__ __forceinline__ int64_t sm_fix_window()
+{
+    return ((int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x / CSR_WAVE)) *
+           SM_FIX_CHUNKS;
+}
+
 template <bool BWD>
 __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_fixup(SoftmaxArgs a)
 {
-    const int64_t base = fixup_window(a.n_chunks);
-    if (base < 0) return;
+    const int64_t base = sm_fix_window();
+    if (base >= a.n_chunks) return;
     const int lane = lane_id();
     const int64_t mine = base + lane;
-    const int rl = (mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
+    const int rl = (lane < SM_FIX_CHUNKS && mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
     uint64_t todo = __ballot(rl >= 0);
     while (todo) {
         const int j = __builtin_ctzll(todo);
@@ -453,7 +466,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split(SoftmaxArgs a)
 }
 
 // Probabilities of the long rows' entries after the entry-run kernel: a wave
-// per window of 64 chunks.  Lane j reads chunk base + j's slot rows, bounds
+// per window of SM_FIX_CHUNKS chunks.  Lane j reads chunk base + j's slot rows, bounds
 // (from the row-bound records, no row_ptr reads) and the slot rows' merged
 // statistics in two rounds of independent loads; a ballot then lists the
 // window's segments and the whole wave writes each one, lanes over
@@ -463,13 +476,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split(SoftmaxArgs a)
 template <bool BWD>
 __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_split_runs(SoftmaxArgs a)
 {
-    const int64_t base = ((int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK +
-                          __builtin_amdgcn_readfirstlane(threadIdx.x / CSR_WAVE)) * CSR_WAVE;
+    const int64_t base = sm_fix_window();
     if (base >= a.n_chunks) return;
     const int lane = lane_id();
     const int64_t c = base + lane;
     int ra = -1, rb = -1, a0 = 0, a1 = 0, b0 = 0, b1 = 0;
-    if (c < a.n_chunks) {
+    if (lane < SM_FIX_CHUNKS && c < a.n_chunks) {
         ra = a.carry_row[2 * c];
         rb = a.carry_row[2 * c + 1];
         const int y0 = a.part[2 * c + 1], y1 = a.part[2 * c + 3];
