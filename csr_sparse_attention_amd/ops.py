@@ -380,7 +380,10 @@ class Transposed(NamedTuple):
 
 def transpose(row_ptr, col_idx, n_cols: int, *, ctx: Optional[Context] = None) -> Transposed:
     """CSR of A^T for the pattern (row_ptr, col_idx) with n_cols columns; the
-    entries of each column keep their row order (deterministic)."""
+    entries of each column keep their row order (deterministic).  row_ptr is
+    checked only on a validating context; without the check, and with col_idx
+    in range, a row_ptr that is not monotone still yields rows in
+    [0, n_rows) and a permutation of the entries (which rows is unspecified)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)
