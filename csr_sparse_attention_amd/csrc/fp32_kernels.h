@@ -802,14 +802,19 @@ __device__ __forceinline__ void fixup_one(const Fp32Args& a, int64_t c, int r)
         store_row<VEC, NV>(dst, acc, L, a.F, 1.f, a.stream_y);
 }
 
+// chunks per fix-up wave: each chunk with a split row costs the wave a few
+// dependent loads, so a short window lets more waves share that work
+constexpr int FP32_FIX_CHUNKS = 16;
+
 template <Op OP, int VEC, int NV>
 __global__ __launch_bounds__(CSR_BLOCK) void k_fixup(Fp32Args a)
 {
-    const int64_t base = fixup_window(a.n_chunks);
-    if (base < 0) return;
+    const int64_t base = ((int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x / CSR_WAVE)) * FP32_FIX_CHUNKS;
+    if (base >= a.n_chunks) return;
     const int lane = lane_id();
     const int64_t mine = base + lane;
-    const int rl = (mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
+    const int rl = (lane < FP32_FIX_CHUNKS && mine < a.n_chunks) ? a.carry_row[2 * mine] : -1;
     uint64_t todo = __ballot(rl >= 0);
     while (todo) {
         const int j = __builtin_ctzll(todo);
