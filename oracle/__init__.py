@@ -55,10 +55,11 @@ def _declare(lib):
     lib.oracle_sddmm.argtypes = [P, P, P, I, P, I, I, I, I, P, P]
     lib.oracle_attention.argtypes = [P, P, P, P, I, I, D, I, I, P, P, P]
     lib.oracle_mha.argtypes = [P, P, P, P, P, I, I, D, I, I, P, P, P]
+    lib.oracle_attention_qk.argtypes = [P, P, P, P, P, I, I, D, I, I, P, P, P]
     lib.oracle_softmax_backward.argtypes = [P, P, P, D, I, I, P, P]
     lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, D, I, I, P, P]
     lib.oracle_spmm_transpose.argtypes = [P, P, P, P, I, I, I, P, P]
-    for f in (lib.oracle_spmm, lib.oracle_sddmm, lib.oracle_attention, lib.oracle_mha,
+    for f in (lib.oracle_spmm, lib.oracle_sddmm, lib.oracle_attention, lib.oracle_mha, lib.oracle_attention_qk,
               lib.oracle_softmax_backward, lib.oracle_attention_backward, lib.oracle_spmm_transpose):
         f.restype = None
     return lib
@@ -216,6 +217,38 @@ def mha(row_ptr, col_idx, Q, K, V, scale, r0=0, r1=None, threads=1, want_probs=F
     return out, mag, probs
 
 
+
+
+def attention_qk(row_ptr, col_idx, Q, K, V, scale, r0=0, r1=None, threads=1, want_probs=False):
+    """Attention from fp32 queries and keys: Q [n_rows, H, D] (or [n_rows, D]
+    for one head), K, V [n_cols, H, D]; per head, softmax over the row's
+    entries of scale * <Q_i, K_j>, then the weighted sum of V rows.
+    Returns (out [rows, H, D], mag, probs [entries, H] or None)."""
+    lib = _load()
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    Qc, Kc, Vc = _c(Q, np.float32), _c(K, np.float32), _c(V, np.float32)
+    if Qc.ndim == 2:
+        Qc, Kc, Vc = Qc[:, None, :], Kc[:, None, :], Vc[:, None, :]
+    H, D = Qc.shape[1], Qc.shape[2]
+    assert Kc.shape[1:] == (H, D) and Vc.shape[1:] == (H, D)
+    r1 = len(rp) - 1 if r1 is None else r1
+    base = int(rp[r0])
+    out, mag = np.zeros((r1 - r0, H, D)), np.zeros((r1 - r0, H, D))
+    probs = np.zeros((int(rp[r1]) - base, H)) if want_probs else None
+
+    def fn(a, b):
+        lib.oracle_attention_qk(_ptr(rp), _ptr(ci), _ptr(Qc), _ptr(Kc), _ptr(Vc), H, D, float(scale), a, b,
+                                out[a - r0:].ctypes.data, mag[a - r0:].ctypes.data,
+                                None if probs is None else probs[int(rp[a]) - base:].ctypes.data)
+
+    _run(_ranges(rp, r0, r1, threads), fn)
+    return out, mag, probs
+
+
+def bf16_to_f32(bits):
+    """bfloat16 bit patterns (uint16) widened exactly to float32 (the 16 bits
+    become the high half of the float's 32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
 def softmax_backward(row_ptr, probs, grad, scale=1.0, r0=0, r1=None, threads=1):

@@ -23,7 +23,8 @@
  *    exponentials), then the weighted sum with p_e = exp(t_e - m) / l.
  *  - Multi-head attention: the same per head h, with the score of edge e
  *    t_e = scale * sum_d Q[i, h, d] * K[col_e, h, d] from bfloat16 inputs read
- *    exactly.
+ *    exactly, or from fp32 inputs (the scores computed from queries and keys
+ *    rather than given).
  *
  *  - Backward (the gradients of the three products; prior art's GNN training,
  *    SparseTIR page, Abstract): the softmax backward over a row's entries,
@@ -183,6 +184,62 @@ void oracle_mha(const int32_t *row_ptr, const int32_t *col_idx,
                 for (int64_t d = 0; d < D; ++d) {
                     y[h * D + d] += p * bf16_to_double(v[d]);
                     if (g) g[h * D + d] += p * fabs(bf16_to_double(v[d]));
+                }
+            }
+        }
+    }
+}
+
+/* fp32 queries and keys (SDDMM -> row-softmax -> SpMM from Q, K, V): the same
+ * as oracle_mha with float inputs.  Q: [n_rows, H, D], K, V: [n_cols, H, D],
+ * node stride H * D.  Per head h of row i: t_e = scale * sum_d Q[i, h, d] *
+ * K[col_e, h, d]; the row maximum, then the sum of exponentials, then
+ * out[i, h, :] = sum_e p_e V[col_e, h, :].  out, mag: [r1 - r0, H, D]; probs
+ * (may be NULL): [entry - row_ptr[r0]][H]. */
+void oracle_attention_qk(const int32_t *row_ptr, const int32_t *col_idx,
+                         const float *Q, const float *K, const float *V,
+                         int64_t H, int64_t D, double scale, int64_t r0, int64_t r1,
+                         double *out, double *mag, double *probs)
+{
+    int64_t base = row_ptr[r0];
+    int64_t HD = H * D;
+    for (int64_t i = r0; i < r1; ++i) {
+        double *y = out + (i - r0) * HD;
+        double *g = mag ? mag + (i - r0) * HD : 0;
+        for (int64_t f = 0; f < HD; ++f) {
+            y[f] = 0.0;
+            if (g) g[f] = 0.0;
+        }
+        int64_t b = row_ptr[i], end = row_ptr[i + 1];
+        if (end == b) continue;
+
+        for (int64_t h = 0; h < H; ++h) {
+            const float *q = Q + i * HD + h * D;
+            double m = -INFINITY;
+            for (int64_t e = b; e < end; ++e) {
+                const float *kq = K + (int64_t)col_idx[e] * HD + h * D;
+                double t = 0.0;
+                for (int64_t d = 0; d < D; ++d) t += (double)q[d] * (double)kq[d];
+                t *= scale;
+                if (t > m) m = t;
+            }
+            double l = 0.0;
+            for (int64_t e = b; e < end; ++e) {
+                const float *kq = K + (int64_t)col_idx[e] * HD + h * D;
+                double t = 0.0;
+                for (int64_t d = 0; d < D; ++d) t += (double)q[d] * (double)kq[d];
+                l += exp(scale * t - m);
+            }
+            for (int64_t e = b; e < end; ++e) {
+                const float *kq = K + (int64_t)col_idx[e] * HD + h * D;
+                const float *vq = V + (int64_t)col_idx[e] * HD + h * D;
+                double t = 0.0;
+                for (int64_t d = 0; d < D; ++d) t += (double)q[d] * (double)kq[d];
+                double p = exp(scale * t - m) / l;
+                if (probs) probs[(e - base) * H + h] = p;
+                for (int64_t d = 0; d < D; ++d) {
+                    y[h * D + d] += p * (double)vq[d];
+                    if (g) g[h * D + d] += p * fabs((double)vq[d]);
                 }
             }
         }

@@ -51,6 +51,19 @@ MUTANTS = [
                                             None)]),
     ("multi-head values of head 0", [("const uint16_t *v = V + (int64_t)col_idx[e] * HD + h * D;",
                                       "const uint16_t *v = V + (int64_t)col_idx[e] * HD;", None)]),
+    ("fp32 q-k scores use head 0's keys", [(
+        "const float *kq = K + (int64_t)col_idx[e] * HD + h * D;\n                const float *vq",
+        "const float *kq = K + (int64_t)col_idx[e] * HD;\n                const float *vq", None)]),
+    ("fp32 q-k weights from the first neighbour's key", [(
+        "const float *kq = K + (int64_t)col_idx[e] * HD + h * D;\n                const float *vq",
+        "const float *kq = K + (int64_t)col_idx[b] * HD + h * D;\n                const float *vq", None)]),
+    ("fp32 q-k weights drop the scale", [("double p = exp(scale * t - m) / l;\n                if (probs) probs[(e - base) * H + h] = p;\n                for (int64_t d = 0; d < D; ++d) {\n                    y[h * D + d] += p * (double)vq[d];",
+                                          "double p = exp(t - m) / l;\n                if (probs) probs[(e - base) * H + h] = p;\n                for (int64_t d = 0; d < D; ++d) {\n                    y[h * D + d] += p * (double)vq[d];", None)]),
+    ("fp32 q-k values of head 0", [("const float *vq = V + (int64_t)col_idx[e] * HD + h * D;",
+                                    "const float *vq = V + (int64_t)col_idx[e] * HD;", None)]),
+    ("fp32 q-k drops the last feature of the dot product", [(
+        "for (int64_t d = 0; d < D; ++d) t += (double)q[d] * (double)kq[d];",
+        "for (int64_t d = 0; d < D - 1; ++d) t += (double)q[d] * (double)kq[d];", None)]),
     ("bfloat16 widened with the wrong shift", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;",
                                                 None)]),
     ("softmax backward drops the row sum", [("out[e - base] = scale * p * ((double)grad[e] - S);",

@@ -157,6 +157,60 @@ def test_mha_dense_bruteforce(oracle_lib, seed):
         assert np.allclose(p[:, h], refp, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_qk_dense_bruteforce(oracle_lib, seed):
+    """fp32 queries and keys: per head, dense scores Q_h K_h^T sampled on the
+    pattern, then the masked dense softmax attention (duplicates included:
+    each stored entry is its own term)."""
+    rng = np.random.default_rng(340 + seed)
+    n, m = int(rng.integers(1, 40)), int(rng.integers(1, 45))
+    H, D = int(rng.integers(1, 4)), int(rng.integers(1, 20))
+    csr = random_small_graph(n, m, rng.random() * 0.5, rng, empty_frac=0.2, allow_dup=seed % 2 == 1)
+    Q = rng.standard_normal((n, H, D)).astype(np.float32)
+    K = rng.standard_normal((m, H, D)).astype(np.float32)
+    V = rng.standard_normal((m, H, D)).astype(np.float32)
+    scale = [1.0, 0.125, 0.7][seed % 3]
+    out, mag, p = oracle.attention_qk(csr.row_ptr, csr.col_idx, Q, K, V, scale, want_probs=True)
+    for h in range(H):
+        S = Q[:, h, :].astype(np.float64) @ K[:, h, :].astype(np.float64).T
+        ref, refp = dense_attention(csr, S[csr.row_of_edge(), csr.col_idx], V[:, h, :], scale)
+        assert np.allclose(out[:, h, :], ref, rtol=0, atol=1e-12)
+        assert np.allclose(p[:, h], refp, rtol=0, atol=1e-13)
+        refmag, _ = dense_attention(csr, S[csr.row_of_edge(), csr.col_idx], np.abs(V[:, h, :]), scale)
+        assert np.allclose(mag[:, h, :], refmag, rtol=0, atol=1e-12)
+    # one head given as 2-D arrays is the same call with H = 1
+    o1, _, _ = oracle.attention_qk(csr.row_ptr, csr.col_idx, Q[:, 0], K[:, 0], V[:, 0], scale)
+    assert np.array_equal(o1[:, 0], out[:, 0])
+
+
+def test_attention_qk_identity_and_uniform(oracle_lib):
+    """Identity pattern: every row attends only to itself, out = V exactly;
+    keys all equal: uniform weights, out = the mean of the neighbours' V."""
+    rng = np.random.default_rng(7)
+    n, D = 17, 6
+    Q = rng.standard_normal((n, 1, D)).astype(np.float32)
+    V = rng.standard_normal((n, 1, D)).astype(np.float32)
+    eye = CSR(n, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32))
+    out, _, _ = oracle.attention_qk(eye.row_ptr, eye.col_idx, Q, Q, V, 0.3)
+    assert np.array_equal(out, V.astype(np.float64))
+    csr = random_small_graph(n, n, 0.4, rng, empty_frac=0.2)
+    K = np.tile(rng.standard_normal((1, 1, D)).astype(np.float32), (n, 1, 1))
+    out, _, _ = oracle.attention_qk(csr.row_ptr, csr.col_idx, Q, K, V, 1.0)
+    for i in range(n):
+        cols = csr.col_idx[csr.row_ptr[i]:csr.row_ptr[i + 1]]
+        want = V[cols, 0].astype(np.float64).mean(axis=0) if len(cols) else np.zeros(D)
+        assert np.allclose(out[i, 0], want, rtol=0, atol=1e-14)
+
+
+def test_bf16_widening_known_patterns():
+    """bfloat16 is the high half of an IEEE float32: known bit patterns."""
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x3FC0, 0x4049], np.uint16)
+    want = np.array([1.0, -2.0, np.inf, -np.inf, 0.0, -0.0, 2.0 ** -133, 1.5, 3.140625], np.float32)
+    got = oracle.bf16_to_f32(bits)
+    assert got.dtype == np.float32 and np.array_equal(got, want)
+    assert np.signbit(got[5]) and not np.signbit(got[4])
+
+
 def test_exhaustive_3x3_patterns(oracle_lib):
     """Every one of the 512 patterns of a 3 x 3 matrix."""
     rng = np.random.default_rng(7)
