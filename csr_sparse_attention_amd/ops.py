@@ -21,6 +21,7 @@ from ._ffi import CsrError, CsrHybrid, CsrProblem, CsrSchedule
 _lock = threading.Lock()
 _contexts: dict = {}
 _workspaces: dict = {}
+_graph_held: list = []  # workspaces a captured graph refers to: never freed
 
 
 def _lib():
@@ -96,14 +97,32 @@ def default_context(device: Optional[int] = None) -> Context:
         return ctx
 
 
-def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A cached device buffer of at least nbytes (256-byte aligned)."""
-    key = device.index
+def _workspace(device: torch.device, nbytes: int, given: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A device buffer of at least nbytes, 256-byte aligned: ``given`` (a
+    caller-owned uint8 tensor) when passed, else a buffer cached per (device,
+    current stream).  Calls on different streams thus never share scratch
+    memory.  A cached buffer is allocated on the stream that uses it, so
+    replacing it by a larger one is stream-ordered; a buffer that was handed
+    out while the stream was being captured into a graph is kept alive for
+    the life of the process, since the graph's replays still write to it."""
+    if given is not None:
+        if given.dtype != torch.uint8 or not given.is_contiguous() or given.device != device:
+            raise ValueError("workspace must be a contiguous uint8 tensor on the operands' device")
+        off = (-given.data_ptr()) % 256
+        if given.numel() < nbytes + off:
+            raise ValueError(f"workspace too small: {given.numel()} bytes, need {nbytes + off}")
+        return given[off:]
+    stream = torch.cuda.current_stream(device)
+    key = (device.index, stream.cuda_stream)
+    capturing = torch.cuda.is_current_stream_capturing()
     with _lock:
         ws = _workspaces.get(key)
         if ws is None or ws.numel() < nbytes + 256:
-            ws = torch.empty(max(nbytes + 256, 1 << 20), dtype=torch.uint8, device=device)
+            grow = 0 if ws is None else 2 * ws.numel()
+            ws = torch.empty(max(nbytes + 256, 1 << 20, grow), dtype=torch.uint8, device=device)
             _workspaces[key] = ws
+        if capturing and all(t is not ws for t in _graph_held):
+            _graph_held.append(ws)
     off = (-ws.data_ptr()) % 256
     return ws[off:]
 
@@ -131,7 +150,56 @@ def _pattern(row_ptr: torch.Tensor, col_idx: torch.Tensor):
             raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
         if not t.is_cuda:
             raise ValueError(f"{name} must be on the GPU")
+    if row_ptr.numel() < 1:
+        raise ValueError("row_ptr must hold n_rows + 1 >= 1 offsets")
+    if col_idx.device != row_ptr.device:
+        raise ValueError("row_ptr and col_idx must be on the same device")
     return row_ptr.numel() - 1, col_idx.numel()
+
+
+# Host-side checks that run before any launch: every row-indexed operand and
+# every output has the shape, dtype and element count its call implies, so no
+# kernel is handed a buffer shorter than what it reads or writes.
+
+def _on(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the pattern on {device}")
+
+
+def _rows(t, name, n_rows, width=None, dtype=torch.float32):
+    """A row-major 2-D operand of exactly n_rows rows (and width columns)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[0] != n_rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows, the call needs {n_rows}")
+    if width is not None and t.shape[1] != width:
+        raise ValueError(f"{name} has {t.shape[1]} columns, the call needs {width}")
+
+
+def _entries(t, name, n):
+    """A contiguous fp32 array of exactly n per-entry values."""
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} values "
+                         f"(got {t.dtype}, {t.numel()} values)")
+
+
+def _out_rows(out, n_rows, width, device):
+    if out is None:
+        return torch.empty((n_rows, width), dtype=torch.float32, device=device)
+    _on(device, out=out)
+    _rows(out, "out", n_rows, width)
+    return out
+
+
+def _out_entries(out, n, device):
+    if out is None:
+        return torch.empty(n, dtype=torch.float32, device=device)
+    _on(device, out=out)
+    _entries(out, "out", n)
+    return out
 
 
 def _sched_arg(schedule: Optional[CsrSchedule]):
@@ -206,13 +274,13 @@ def _softmax_problem(row_ptr, scores, out, scale):
     return p
 
 
-def _run(problem: CsrProblem, device, schedule, ctx, call):
+def _run(problem: CsrProblem, device, schedule, ctx, call, workspace=None):
     ctx = ctx or default_context(device.index)
     lib = _lib()
     nbytes = ctypes.c_size_t()
     _check(lib.csr_workspace_size(ctx.handle, ctypes.byref(problem), _sched_arg(schedule), ctypes.byref(nbytes)),
            "csr_workspace_size", ctx)
-    ws = _workspace(device, nbytes.value)
+    ws = _workspace(device, nbytes.value, workspace)
     rc = call(ctx, ws, nbytes.value, _stream(device))
     _check(rc, "csr call", ctx)
 
@@ -222,52 +290,59 @@ def _run(problem: CsrProblem, device, schedule, ctx, call):
 # ---------------------------------------------------------------------------
 
 def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule] = None,
-         ctx: Optional[Context] = None) -> torch.Tensor:
+         ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = A X for the CSR matrix A (row_ptr, col_idx, vals; vals=None means 1)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
-    if out is None:
-        out = torch.empty((n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
-    if vals is not None and (vals.dtype != torch.float32 or vals.numel() != nnz or not vals.is_contiguous()):
-        raise ValueError("vals must be a contiguous fp32 tensor with one value per entry")
+    _on(row_ptr.device, vals=vals, X=X)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [n_cols, F]")
+    if vals is not None:
+        _entries(vals, "vals", nnz)
+    out = _out_rows(out, n_rows, X.shape[1], X.device)
     p = _spmm_problem(row_ptr, col_idx, vals, X, out)
 
     def call(ctx, ws, nb, st):
         return _lib().csr_spmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
                                p.width, p.ld_b, p.out, p.ld_out, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _run(p, X.device, schedule, ctx, call)
+    _run(p, X.device, schedule, ctx, call, workspace)
     return out
 
 
 def sddmm(row_ptr, col_idx, U, V, *, out=None, schedule: Optional[CsrSchedule] = None,
-          ctx: Optional[Context] = None) -> torch.Tensor:
+          ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[e] = <U[row(e)], V[col_idx[e]]> for every stored entry e."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
-    if out is None:
-        out = torch.empty(nnz, dtype=torch.float32, device=U.device)
-    if out.dtype != torch.float32 or out.numel() != nnz or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp32 tensor with one value per entry")
+    _on(row_ptr.device, U=U, V=V)
+    _rows(U, "U", n_rows)
+    if V.dim() != 2:
+        raise ValueError("V must be 2-D [n_cols, K]")
+    out = _out_entries(out, nnz, U.device)
     p = _sddmm_problem(row_ptr, col_idx, U, V, out)
 
     def call(ctx, ws, nb, st):
         return _lib().csr_sddmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.ld_a,
                                 p.b, p.ld_b, p.width, p.out, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _run(p, U.device, schedule, ctx, call)
+    _run(p, U.device, schedule, ctx, call, workspace)
     return out
 
 
 def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, out=None,
-              schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None) -> torch.Tensor:
+              schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Fused CSR attention with given scores: per row, softmax over the row's
     entries of scale * edge_scores, then the weighted sum of node_value rows
     (zero for rows without entries).  Arguments in the order row_ptr,
     col_idx, edge_scores, node_value."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
-    if edge_scores.dtype != torch.float32 or edge_scores.numel() != nnz or not edge_scores.is_contiguous():
-        raise ValueError("edge_scores must be a contiguous fp32 tensor with one score per entry")
-    if out is None:
-        out = torch.empty((n_rows, node_value.shape[1]), dtype=torch.float32, device=node_value.device)
+    _on(row_ptr.device, edge_scores=edge_scores, node_value=node_value)
+    _entries(edge_scores, "edge_scores", nnz)
+    if node_value.dim() != 2:
+        raise ValueError("node_value must be 2-D [n_cols, F]")
+    out = _out_rows(out, n_rows, node_value.shape[1], node_value.device)
     p = _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale)
 
     def call(ctx, ws, nb, st):
@@ -275,21 +350,28 @@ def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, 
                                     p.width, p.ld_b, ctypes.c_float(scale), p.out, p.ld_out,
                                     _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _run(p, node_value.device, schedule, ctx, call)
+    _run(p, node_value.device, schedule, ctx, call, workspace)
     return out
 
 
 def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, out=None,
-                  schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None) -> torch.Tensor:
+                  schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Multi-head fused CSR attention: bf16 Q [n_rows, H, D], K, V [n_cols, H, D];
     per head, softmax over the row's entries of scale * <Q_i, K_j>, times V.
     Returns fp32 [n_rows, H, D].  scale defaults to 1/sqrt(D)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
+    _on(row_ptr.device, Q=Q, K=K, V=V)
+    if Q.dim() != 3 or Q.shape[0] != n_rows:
+        raise ValueError(f"Q must be [n_rows={n_rows}, heads, head_dim], got {tuple(Q.shape)}")
     H, D = Q.shape[1], Q.shape[2]
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     if out is None:
         out = torch.empty((n_rows, H, D), dtype=torch.float32, device=Q.device)
+    _on(row_ptr.device, out=out)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (n_rows, H, D):
+        raise ValueError(f"out must be a contiguous fp32 tensor [{n_rows}, {H}, {D}]")
     p = _mha_problem(row_ptr, col_idx, Q, K, V, out, scale)
 
     def call(ctx, ws, nb, st):
@@ -297,26 +379,27 @@ def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, o
                                         p.c, H, D, ctypes.c_float(scale), p.out, _sched_arg(schedule),
                                         ws.data_ptr(), nb, st)
 
-    _run(p, Q.device, schedule, ctx, call)
+    _run(p, Q.device, schedule, ctx, call, workspace)
     return out
 
 
 def row_softmax(row_ptr, scores, *, scale: float = 1.0, out=None, schedule: Optional[CsrSchedule] = None,
-                ctx: Optional[Context] = None) -> torch.Tensor:
+                ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-row softmax over the stored entries: out[e] = exp(scale * s_e - m_i) /
     sum over row i of exp(scale * s - m_i).  ``out`` may be ``scores`` (in place)."""
     _pattern(row_ptr, row_ptr)
+    _on(row_ptr.device, scores=scores)
     if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
         raise ValueError("scores must be a contiguous 1-D fp32 tensor")
-    if out is None:
-        out = torch.empty_like(scores)
+    out = _out_entries(out, scores.numel(), scores.device)
     p = _softmax_problem(row_ptr, scores, out, scale)
 
     def call(ctx, ws, nb, st):
         return _lib().csr_row_softmax(ctx.handle, p.n_rows, p.nnz, p.row_ptr, p.a, ctypes.c_float(scale), p.out,
                                       _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _run(p, scores.device, schedule, ctx, call)
+    _run(p, scores.device, schedule, ctx, call, workspace)
     return out
 
 
@@ -350,15 +433,16 @@ def _flat_f32(t, name, n):
 
 
 def row_softmax_backward(row_ptr, probs, grad, *, scale: float = 1.0, out=None,
-                         schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None) -> torch.Tensor:
+                         schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Gradient of the row softmax: out[e] = scale * p_e * (g_e - sum over the
     row of p g), for p = row_softmax(s, scale) and g = dL/dp.  ``out`` may be
     ``probs`` or ``grad`` (in place)."""
     _pattern(row_ptr, row_ptr)
+    _on(row_ptr.device, probs=probs, grad=grad)
     _flat_f32(probs, "probs", probs.numel())
     _flat_f32(grad, "grad", probs.numel())
-    if out is None:
-        out = torch.empty_like(probs)
+    out = _out_entries(out, probs.numel(), probs.device)
     p = _softmax_bwd_problem(row_ptr, probs, grad, out, scale)
 
     def call(ctx, ws, nb, st):
@@ -366,7 +450,7 @@ def row_softmax_backward(row_ptr, probs, grad, *, scale: float = 1.0, out=None,
                                                ctypes.c_float(scale), p.out, _sched_arg(schedule), ws.data_ptr(),
                                                nb, st)
 
-    _run(p, probs.device, schedule, ctx, call)
+    _run(p, probs.device, schedule, ctx, call, workspace)
     return out
 
 
@@ -405,10 +489,9 @@ def gather_values(perm, src, *, out=None, ctx: Optional[Context] = None) -> torc
     """out[k] = src[perm[k]] (per-entry values into a transposed pattern's order)."""
     if perm.dtype != torch.int32 or perm.dim() != 1 or not perm.is_contiguous() or not perm.is_cuda:
         raise ValueError("perm must be a contiguous 1-D int32 GPU tensor")
-    if src.dtype != torch.float32 or not src.is_contiguous():
-        raise ValueError("src must be a contiguous fp32 tensor")
-    if out is None:
-        out = torch.empty(perm.numel(), dtype=torch.float32, device=perm.device)
+    _on(perm.device, src=src)
+    _entries(src, "src", perm.numel())
+    out = _out_entries(out, perm.numel(), perm.device)
     ctx = ctx or default_context(perm.device.index)
     _check(_lib().csr_gather_values(ctx.handle, perm.numel(), perm.data_ptr(), src.data_ptr(), out.data_ptr(),
                                     _stream(perm.device)), "csr_gather_values", ctx)
@@ -544,13 +627,13 @@ def hybrid_problem(h: Hybrid, op: str, *operands) -> CsrProblem:
     raise ValueError(op)
 
 
-def _hybrid_run(h, op, width, schedule, ctx, device, call):
+def _hybrid_run(h, op, width, schedule, ctx, device, call, workspace=None):
     ctx = ctx or default_context(device.index)
     lib = _lib()
     nbytes = ctypes.c_size_t()
     _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), op, width, _sched_arg(schedule),
                                          ctypes.byref(nbytes)), "csr_hybrid_workspace_size", ctx)
-    ws = _workspace(device, nbytes.value)
+    ws = _workspace(device, nbytes.value, workspace)
     _check(call(ctx, ws, nbytes.value, _stream(device)), "csr hybrid call", ctx)
 
 
@@ -587,12 +670,14 @@ def hybrid_select(h: Hybrid, op: str, *operands, mode: str = "auto", out=None, c
 
 
 def hybrid_spmm(h: Hybrid, vals, X, *, out=None, schedule: Optional[CsrSchedule] = None,
-                ctx: Optional[Context] = None) -> torch.Tensor:
+                ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = A X over the format; ``vals`` in the format's entry order
     (hybrid_values) or None for all ones."""
+    _on(h.perm.device, vals=vals, X=X)
+    _rows(X, "X", h.n_cols)
     ldx = _dense(X, "X", torch.float32)
-    if out is None:
-        out = torch.empty((h.n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
+    out = _out_rows(out, h.n_rows, X.shape[1], X.device)
     ldy = _dense(out, "out", torch.float32)
     if vals is not None:
         _flat_f32(vals, "vals", h.nnz)
@@ -601,25 +686,26 @@ def hybrid_spmm(h: Hybrid, vals, X, *, out=None, schedule: Optional[CsrSchedule]
         return _lib().csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), _ptr(vals), X.data_ptr(), X.shape[1], ldx,
                                       out.data_ptr(), ldy, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _hybrid_run(h, _ffi.OP_SPMM, X.shape[1], schedule, ctx, X.device, call)
+    _hybrid_run(h, _ffi.OP_SPMM, X.shape[1], schedule, ctx, X.device, call, workspace)
     return out
 
 
 def hybrid_sddmm(h: Hybrid, U, V, *, out=None, schedule: Optional[CsrSchedule] = None,
-                 ctx: Optional[Context] = None) -> torch.Tensor:
+                 ctx: Optional[Context] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[e] = <U[row(e)], V[col(e)]> over the format, in the original entry order."""
+    _on(h.perm.device, U=U, V=V)
+    _rows(U, "U", h.n_rows)
+    _rows(V, "V", h.n_cols, U.shape[1])
     ldu = _dense(U, "U", torch.float32)
     ldv = _dense(V, "V", torch.float32)
-    if U.shape[1] != V.shape[1]:
-        raise ValueError("U and V must have the same width")
-    if out is None:
-        out = torch.empty(h.nnz, dtype=torch.float32, device=U.device)
+    out = _out_entries(out, h.nnz, U.device)
 
     def call(ctx, ws, nb, st):
         return _lib().csr_hybrid_sddmm(ctx.handle, ctypes.byref(h.desc), U.data_ptr(), ldu, V.data_ptr(), ldv,
                                        U.shape[1], out.data_ptr(), _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _hybrid_run(h, _ffi.OP_SDDMM, U.shape[1], schedule, ctx, U.device, call)
+    _hybrid_run(h, _ffi.OP_SDDMM, U.shape[1], schedule, ctx, U.device, call, workspace)
     return out
 
 
