@@ -45,3 +45,27 @@ def assert_close(gpu, ref, mag, tol=TOL_F32, what=""):
     e = max_err(gpu, ref, mag)
     assert e <= tol, f"{what}: max error {e:.3e} > {tol:.0e}"
     return e
+
+
+def compare_all_rows(got, oracle_block, row_ptr, width, tol, what, per_entry=False,
+                     work_per_block=3e9, elems_per_block=4e7):
+    """Compares a full GPU output with the oracle over every row: the rows
+    are cut into blocks of about work_per_block multiply-adds (entries times
+    width) and at most elems_per_block output elements, oracle_block(r0, r1)
+    returns (ref, mag) of rows [r0, r1) (per-entry arrays for per_entry), and
+    each block is checked before the next is computed, so host memory stays
+    bounded.  Returns the largest error."""
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    n = len(rp) - 1
+    w = max(1, int(width))
+    worst = 0.0
+    r0 = 0
+    while r0 < n:
+        r1 = int(np.searchsorted(rp, rp[r0] + max(1, int(work_per_block / w)), side="right")) - 1
+        r1 = min(max(r1, r0 + 1), n, r0 + max(1, int(elems_per_block / w)))
+        ref, mag = oracle_block(r0, r1)
+        g = got[rp[r0]:rp[r1]] if per_entry else got[r0:r1]
+        worst = max(worst, max_err(g, ref, mag))
+        r0 = r1
+    assert worst <= tol, f"{what}: max error {worst:.3e} > {tol:.0e}"
+    return worst
