@@ -153,8 +153,8 @@ def load() -> ctypes.CDLL:
         "csr_context_destroy": [P],
         "csr_status_string": [ctypes.c_int],
         "csr_last_error": [P],
-        "csr_spmm": [P, I64, I64, I64, P, P, P, P, I64, I64, P, I64, SP, P, SZ, P],
-        "csr_sddmm": [P, I64, I64, I64, P, P, P, I64, P, I64, I64, P, SP, P, SZ, P],
+        "csr_spmm": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
+        "csr_sddmm": [P, I64, I64, I64, P, P, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
         "csr_attention": [P, I64, I64, I64, P, P, P, P, I64, I64, F, P, I64, SP, P, SZ, P],
         "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, SP, P, SZ, P],
         "csr_row_softmax": [P, I64, I64, P, P, F, P, SP, P, SZ, P],
@@ -178,9 +178,9 @@ def load() -> ctypes.CDLL:
         "csr_hybrid_capacity": [I64, I64, I32, ctypes.POINTER(I64)],
         "csr_hybrid_build_workspace_size": [P, I64, I64, I32, ctypes.POINTER(SZ)],
         "csr_hybrid_build": [P, P, P, HP, P, SZ, P],
-        "csr_hybrid_workspace_size": [P, HP, I32, I64, SP, ctypes.POINTER(SZ)],
-        "csr_hybrid_spmm": [P, HP, P, P, I64, I64, P, I64, SP, P, SZ, P],
-        "csr_hybrid_sddmm": [P, HP, P, I64, P, I64, I64, P, SP, P, SZ, P],
+        "csr_hybrid_workspace_size": [P, HP, I32, I64, I32, SP, ctypes.POINTER(SZ)],
+        "csr_hybrid_spmm": [P, HP, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
+        "csr_hybrid_sddmm": [P, HP, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
         "csr_hybrid_select": [P, HP, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
     }
     for name, argtypes in sig.items():

@@ -240,32 +240,48 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
     a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
     a.stream_y = maps ? maps->stream_y : 0;
+    const bool bf = p.dtype == CSR_DTYPE_BF16;
     if (p.op == CSR_OP_SDDMM) {
         if (maps) {
             a.u_row = maps->u_row;
             a.out_idx = maps->out_idx;
         }
-        a.U = static_cast<const float*>(p.a);
+        a.U = p.a;
         a.ldu = p.ld_a;
-        a.X = static_cast<const float*>(p.b);
+        a.X = p.b;
         a.ldx = p.ld_b;
         a.Y = static_cast<float*>(p.out);
-        CSR_HIP(ctx, csrk::launch_sddmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        CSR_HIP(ctx, bf ? csrk::launch_sddmm_bf16(s.mapping, s.vec, s.passes, s.chunk_items, a, st)
+                        : csrk::launch_sddmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
         return CSR_OK;
     }
     a.ev = static_cast<const float*>(p.a);
-    a.X = static_cast<const float*>(p.b);
+    a.X = p.b;
     a.ldx = p.ld_b;
     a.Y = static_cast<float*>(p.out);
     a.ldy = p.ld_out;
+    // the fix-up reads fp32 pieces and writes fp32 rows: over bf16 operands it
+    // takes the widest fp32 lane layout the width and the output allow
+    csrk::Fp32Args fa = a;
+    int fvec = s.vec, fnv = s.passes;
+    if (bf && s.mapping != CSR_MAP_ROWGROUP) {
+        fvec = 4;
+        while (fvec > 1 && (p.width % fvec || p.ld_out % fvec || (uintptr_t)p.out % (4 * fvec))) fvec /= 2;
+        int W = 0;
+        if (!csrh::natural_layout(p.width, fvec, &W, &fnv))
+            return set_err(ctx, CSR_ERR_SHAPE, "no fp32 layout for the fix-up of this width");
+        fa.W = W;
+    }
     if (p.op == CSR_OP_SPMM && (s.flags & CSR_SCHED_WIDE)) {
         CSR_HIP(ctx, csrk::launch_spmm_wide(s.passes, a, st));
     } else if (p.op == CSR_OP_SPMM) {
-        CSR_HIP(ctx, csrk::launch_spmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
-        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_spmm_fixup(s.vec, s.passes, a, st));
+        CSR_HIP(ctx, bf ? csrk::launch_spmm_bf16(s.mapping, s.vec, s.passes, s.chunk_items, a, st)
+                        : csrk::launch_spmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_spmm_fixup(fvec, fnv, fa, st));
     } else {
-        CSR_HIP(ctx, csrk::launch_attention(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
-        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_attention_fixup(s.vec, s.passes, a, st));
+        CSR_HIP(ctx, bf ? csrk::launch_attention_bf16(s.mapping, s.vec, s.passes, s.chunk_items, a, st)
+                        : csrk::launch_attention(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_attention_fixup(fvec, fnv, fa, st));
     }
     return CSR_OK;
 }
@@ -550,12 +566,12 @@ int csr_context_destroy(csr_context_t ctx)
 }
 
 int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
-             const int32_t* col_idx, const float* vals, const float* X, int64_t F, int64_t ldx, float* Y,
-             int64_t ldy, const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
+             const int32_t* col_idx, const float* vals, const void* X, int32_t x_dtype, int64_t F, int64_t ldx,
+             float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
 {
     csr_problem_t p = blank_problem();
     p.op = CSR_OP_SPMM;
-    p.dtype = CSR_DTYPE_F32;
+    p.dtype = x_dtype;
     p.n_rows = n_rows;
     p.n_cols = n_cols;
     p.nnz = nnz;
@@ -574,12 +590,12 @@ int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, con
 }
 
 int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
-              const int32_t* col_idx, const float* U, int64_t ldu, const float* V, int64_t ldv, int64_t K,
-              float* out, const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
+              const int32_t* col_idx, const void* U, int64_t ldu, const void* V, int64_t ldv, int32_t dtype,
+              int64_t K, float* out, const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
 {
     csr_problem_t p = blank_problem();
     p.op = CSR_OP_SDDMM;
-    p.dtype = CSR_DTYPE_F32;
+    p.dtype = dtype;
     p.n_rows = n_rows;
     p.n_cols = n_cols;
     p.nnz = nnz;
@@ -860,11 +876,11 @@ int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* c
 }
 
 // The product over the format as a plain problem on the segment pattern
-static csr_problem_t hybrid_problem(const csr_hybrid_t* h, int32_t op, int64_t width)
+static csr_problem_t hybrid_problem(const csr_hybrid_t* h, int32_t op, int64_t width, int32_t dtype)
 {
     csr_problem_t p = blank_problem();
     p.op = op;
-    p.dtype = CSR_DTYPE_F32;
+    p.dtype = dtype;
     p.n_rows = h->n_seg;
     p.n_cols = h->n_cols;
     p.nnz = h->nnz;
@@ -891,7 +907,7 @@ static int hybrid_inner_bytes(csr_context_t ctx, const csr_problem_t& p, const c
     return CSR_OK;
 }
 
-int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width,
+int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width, int32_t dtype,
                               const csr_schedule_t* sched, size_t* bytes)
 {
     if (!bytes) return CSR_ERR_NULL;
@@ -899,7 +915,7 @@ int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t 
     int rc = check_hybrid(ctx, h, true);
     if (rc != CSR_OK) return rc;
     if (op != CSR_OP_SPMM && op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "the format serves SpMM and SDDMM");
-    csr_problem_t p = hybrid_problem(h, op, width);
+    csr_problem_t p = hybrid_problem(h, op, width, dtype);
     size_t inner = 0;
     rc = hybrid_inner_bytes(ctx, p, sched, &inner);
     if (rc != CSR_OK) return rc;
@@ -916,14 +932,14 @@ struct HybridCall {
     float* part_rows;  // SpMM only
 };
 
-static int hybrid_call(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width, const void* a,
-                       int64_t lda, const void* b, int64_t ldb, const csr_schedule_t* sched, void* workspace,
-                       size_t ws_bytes, void* stream, float* sddmm_out, HybridCall* c)
+static int hybrid_call(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width, int32_t dtype,
+                       const void* a, int64_t lda, const void* b, int64_t ldb, const csr_schedule_t* sched,
+                       void* workspace, size_t ws_bytes, void* stream, float* sddmm_out, HybridCall* c)
 {
     int rc = check_hybrid(ctx, h, true);
     if (rc != CSR_OK) return rc;
     if (op != CSR_OP_SPMM && op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "the format serves SpMM and SDDMM");
-    c->p = hybrid_problem(h, op, width);
+    c->p = hybrid_problem(h, op, width, dtype);
     c->p.a = a;
     c->p.b = b;
     c->p.ld_b = ldb;
@@ -987,8 +1003,8 @@ static int hybrid_run(csr_context_t ctx, const csr_hybrid_t* h, const HybridCall
     return CSR_OK;
 }
 
-int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals, const float* X, int64_t F,
-                    int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
+int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals, const void* X, int32_t x_dtype,
+                    int64_t F, int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
                     size_t ws_bytes, void* stream)
 {
     if (!ctx || !X || !Y) return CSR_ERR_NULL;
@@ -997,7 +1013,8 @@ int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals,
     if (F < 1 || ldy < F || ldy >= ((int64_t)1 << 30)) return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
     try {
         HybridCall c;
-        int rc = hybrid_call(ctx, h, CSR_OP_SPMM, F, vals, 0, X, ldx, sched, workspace, ws_bytes, stream, nullptr, &c);
+        int rc = hybrid_call(ctx, h, CSR_OP_SPMM, F, x_dtype, vals, 0, X, ldx, sched, workspace, ws_bytes, stream,
+                             nullptr, &c);
         if (rc != CSR_OK) return rc;
         if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
         DeviceGuard g(ctx->device);
@@ -1007,8 +1024,8 @@ int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals,
     }
 }
 
-int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const float* U, int64_t ldu, const float* V,
-                     int64_t ldv, int64_t K, float* out, const csr_schedule_t* sched, void* workspace,
+int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const void* U, int64_t ldu, const void* V,
+                     int64_t ldv, int32_t dtype, int64_t K, float* out, const csr_schedule_t* sched, void* workspace,
                      size_t ws_bytes, void* stream)
 {
     if (!ctx) return CSR_ERR_NULL;
@@ -1016,7 +1033,8 @@ int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const float* U, i
         std::lock_guard<std::mutex> lk(ctx->mu);
         ctx->last_error.clear();
         HybridCall c;
-        int rc = hybrid_call(ctx, h, CSR_OP_SDDMM, K, U, ldu, V, ldv, sched, workspace, ws_bytes, stream, out, &c);
+        int rc = hybrid_call(ctx, h, CSR_OP_SDDMM, K, dtype, U, ldu, V, ldv, sched, workspace, ws_bytes, stream, out,
+                             &c);
         if (rc != CSR_OK) return rc;
         if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
         DeviceGuard g(ctx->device);
@@ -1035,8 +1053,9 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
     if (mode > CSR_SELECT_ESTIMATE) return set_err(ctx, CSR_ERR_SHAPE, "unknown selection mode");
     try {
         HybridCall c;
-        int rc = hybrid_call(ctx, h, call->op, call->width, call->a, call->ld_a, call->b, call->ld_b, nullptr,
-                             call->workspace, call->workspace_bytes, call->stream, static_cast<float*>(call->out), &c);
+        int rc = hybrid_call(ctx, h, call->op, call->width, call->dtype, call->a, call->ld_a, call->b, call->ld_b,
+                             nullptr, call->workspace, call->workspace_bytes, call->stream,
+                             static_cast<float*>(call->out), &c);
         if (rc != CSR_OK) return rc;
         if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
         DeviceGuard g(ctx->device);

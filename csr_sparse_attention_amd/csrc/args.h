@@ -10,9 +10,9 @@ struct Fp32Args {
     const int32_t* col_idx;
     int64_t n_rows;
     const float* ev;   // per-entry input: SpMM values (may be null = 1) or attention scores
-    const float* U;    // SDDMM row operand
+    const void* U;     // SDDMM row operand (fp32 or bf16, as the gathered operand)
     int64_t ldu;
-    const float* X;    // gathered operand: SpMM X, attention node_value, SDDMM V
+    const void* X;     // gathered operand: SpMM X, attention node_value, SDDMM V (fp32 or bf16)
     int64_t ldx;
     float* Y;          // output rows (SpMM, attention) or per-entry output (SDDMM)
     int64_t ldy;

@@ -39,16 +39,59 @@ __device__ __forceinline__ void vload(float (&d)[VEC], const float* p)
 template <int VEC>
 __device__ __forceinline__ void vstore(float* p, const float (&s)[VEC])
 {
-    typedef typename vtype<VEC>::t T;
-    T v;
-    if constexpr (VEC == 1) {
-        v = s[0];
-    } else if constexpr (VEC == 2) {
-        v.x = s[0]; v.y = s[1];
+    if constexpr (VEC == 8) {
+        // two 16-byte stores (the lane layout of bf16 operands read 8 at a time)
+        reinterpret_cast<float4*>(p)[0] = make_float4(s[0], s[1], s[2], s[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(s[4], s[5], s[6], s[7]);
+        return;
     } else {
-        v.x = s[0]; v.y = s[1]; v.z = s[2]; v.w = s[3];
+        typedef typename vtype<VEC>::t T;
+        T v;
+        if constexpr (VEC == 1) {
+            v = s[0];
+        } else if constexpr (VEC == 2) {
+            v.x = s[0]; v.y = s[1];
+        } else {
+            v.x = s[0]; v.y = s[1]; v.z = s[2]; v.w = s[3];
+        }
+        *reinterpret_cast<T*>(p) = v;
     }
-    *reinterpret_cast<T*>(p) = v;
+}
+
+// bfloat16 operands: raw 16-bit patterns in memory, widened exactly to fp32
+// in registers (the 16 bits become the float's high half).  bf16_t is a tag
+// type; the kernels read it VEC elements at a time (VEC = 2, 4, 8: one 4-,
+// 8- or 16-byte load per lane).
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ void widen2(float& lo, float& hi, uint32_t w)
+{
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+}
+
+// VEC consecutive elements of type T at p, as fp32
+template <typename T, int VEC>
+__device__ __forceinline__ void vload_t(float (&d)[VEC], const T* p)
+{
+    if constexpr (sizeof(T) == 4) {
+        vload<VEC>(d, reinterpret_cast<const float*>(p));
+    } else if constexpr (VEC == 2) {
+        widen2(d[0], d[1], *reinterpret_cast<const uint32_t*>(p));
+    } else if constexpr (VEC == 4) {
+        const uint2 r = *reinterpret_cast<const uint2*>(p);
+        widen2(d[0], d[1], r.x);
+        widen2(d[2], d[3], r.y);
+    } else {
+        static_assert(VEC == 8, "bf16 operands are read 2, 4 or 8 at a time");
+        const uint4 r = *reinterpret_cast<const uint4*>(p);
+        widen2(d[0], d[1], r.x);
+        widen2(d[2], d[3], r.y);
+        widen2(d[4], d[5], r.z);
+        widen2(d[6], d[7], r.w);
+    }
 }
 
 // Streamed store (an output row written once and not read again by the
@@ -57,8 +100,12 @@ __device__ __forceinline__ void vstore(float* p, const float (&s)[VEC])
 template <int VEC>
 __device__ __forceinline__ void vstore_stream(float* p, const float (&s)[VEC])
 {
-    typedef float T __attribute__((ext_vector_type(VEC == 1 ? 1 : VEC)));
-    if constexpr (VEC == 1) {
+    typedef float T __attribute__((ext_vector_type(VEC == 1 ? 1 : (VEC == 8 ? 4 : VEC))));
+    if constexpr (VEC == 8) {
+        T v0 = {s[0], s[1], s[2], s[3]}, v1 = {s[4], s[5], s[6], s[7]};
+        __builtin_nontemporal_store(v0, reinterpret_cast<T*>(p));
+        __builtin_nontemporal_store(v1, reinterpret_cast<T*>(p + 4));
+    } else if constexpr (VEC == 1) {
         __builtin_nontemporal_store(s[0], p);
     } else if constexpr (VEC == 2) {
         T v = {s[0], s[1]};

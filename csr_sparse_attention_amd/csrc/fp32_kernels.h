@@ -79,15 +79,16 @@ __device__ __forceinline__ const char* row_at(const char* base, int32_t row, uin
 // Batches of U entries run without per-entry tests; only the last, partial
 // batch is masked.  Lanes past the width read the row's first features (in
 // bounds) and accumulate values that are never stored.
-template <Op OP, int VEC, int NV, int U>
+template <Op OP, typename T, int VEC, int NV, int U>
 __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t* col, const float* ev,
-                                           int kb, int ke, int step, const float* X, int64_t ldx,
+                                           int kb, int ke, int step, const T* X, int64_t ldx,
                                            const Lanes<VEC, NV>& L, int F, float scale, float m)
 {
+    constexpr uint32_t ES = sizeof(T);
     uint32_t off[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) off[j] = L.valid(j, F) ? (uint32_t)L.off(j) * 4u : 0u;
-    const uint32_t row_bytes = (uint32_t)ldx * 4u;
+    for (int j = 0; j < NV; ++j) off[j] = L.valid(j, F) ? (uint32_t)L.off(j) * ES : 0u;
+    const uint32_t row_bytes = (uint32_t)ldx * ES;
     const char* xb = reinterpret_cast<const char*>(X);
     int k = kb;
     for (; k + (U - 1) * step < ke; k += step * U) {
@@ -99,7 +100,7 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
             w[u] = edge_weight<OP>(ev, e, scale, m);
             const char* xr = row_at(xb, col[e], row_bytes);
 #pragma unroll
-            for (int j = 0; j < NV; ++j) vload<VEC>(xv[u][j], reinterpret_cast<const float*>(xr + off[j]));
+            for (int j = 0; j < NV; ++j) vload_t<T, VEC>(xv[u][j], reinterpret_cast<const T*>(xr + off[j]));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -119,7 +120,7 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
             if (ok) {
                 const char* xr = row_at(xb, col[e], row_bytes);
 #pragma unroll
-                for (int j = 0; j < NV; ++j) vload<VEC>(xv[u][j], reinterpret_cast<const float*>(xr + off[j]));
+                for (int j = 0; j < NV; ++j) vload_t<T, VEC>(xv[u][j], reinterpret_cast<const T*>(xr + off[j]));
             } else {
                 zero(xv[u]);
             }
@@ -138,9 +139,9 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
 // and weight from that lane (readlane), so the gathers of a batch of U
 // entries wait on one coalesced load per 64 entries instead of on their own
 // column loads.  b and e must be wave-uniform.
-template <int VEC, int NV, int U>
+template <typename T, int VEC, int NV, int U>
 __device__ __forceinline__ void gather_acc_wave(float (&acc)[NV][VEC], const int32_t* col, const float* ev, int b,
-                                                int e, const float* X, int64_t ldx, const Lanes<VEC, NV>& L, int F)
+                                                int e, const T* X, int64_t ldx, const Lanes<VEC, NV>& L, int F)
 {
     const int lane = lane_id();
     for (int base = b; base < e; base += CSR_WAVE) {
@@ -156,11 +157,11 @@ __device__ __forceinline__ void gather_acc_wave(float (&acc)[NV][VEC], const int
                 const int k = ok ? i + u : 0;
                 const int c = __builtin_amdgcn_readlane(cl, k);
                 w[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 0.f;
-                const float* xr = X + (int64_t)c * ldx;
+                const T* xr = X + (int64_t)c * ldx;
 #pragma unroll
                 for (int j = 0; j < NV; ++j) {
                     if (ok && L.valid(j, F)) {
-                        vload<VEC>(xv[u][j], xr + L.off(j));
+                        vload_t<T, VEC>(xv[u][j], xr + L.off(j));
                     } else {
 #pragma unroll
                         for (int v = 0; v < VEC; ++v) xv[u][j][v] = 0.f;
@@ -241,9 +242,9 @@ __device__ __forceinline__ void store_row_div(float* dst, const float (&acc)[NV]
 
 // SDDMM: out[e] = <u, X[col[e]]> for e = kb, kb + step, ... < ke; the W lanes
 // of the group reduce the partial dot products and lane 0 of the group writes.
-template <int VEC, int NV, int U>
+template <typename T, int VEC, int NV, int U>
 __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int32_t* col, int kb, int ke,
-                                            int step, const float* X, int64_t ldx, const Lanes<VEC, NV>& L,
+                                            int step, const T* X, int64_t ldx, const Lanes<VEC, NV>& L,
                                             int F, float* out, const int32_t* out_idx)
 {
     for (int k = kb; k < ke; k += step * U) {
@@ -253,11 +254,11 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
             int e = k + uu * step;
             bool ok = e < ke;
             int c = ok ? col[e] : 0;
-            const float* xr = X + (int64_t)c * ldx;
+            const T* xr = X + (int64_t)c * ldx;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 if (ok && L.valid(j, F)) {
-                    vload<VEC>(xv[uu][j], xr + L.off(j));
+                    vload_t<T, VEC>(xv[uu][j], xr + L.off(j));
                 } else {
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) xv[uu][j][v] = 0.f;
@@ -288,13 +289,13 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
 // U row read for pattern row r: its own row, or the row a segment belongs to
 __device__ __forceinline__ int64_t u_row_of(const Fp32Args& a, int64_t r) { return a.u_row ? a.u_row[r] : r; }
 
-template <int VEC, int NV>
-__device__ __forceinline__ void load_row(float (&u)[NV][VEC], const float* src, const Lanes<VEC, NV>& L, int F)
+template <typename T, int VEC, int NV>
+__device__ __forceinline__ void load_row(float (&u)[NV][VEC], const T* src, const Lanes<VEC, NV>& L, int F)
 {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         if (L.valid(j, F)) {
-            vload<VEC>(u[j], src + L.off(j));
+            vload_t<T, VEC>(u[j], src + L.off(j));
         } else {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) u[j][v] = 0.f;
@@ -305,9 +306,10 @@ __device__ __forceinline__ void load_row(float (&u)[NV][VEC], const float* src, 
 // ---------------------------------------------------------------------------
 // Row-group mapping
 // ---------------------------------------------------------------------------
-template <Op OP, int VEC, int NV, int U>
+template <Op OP, typename T, int VEC, int NV, int U>
 __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
 {
+    const T* X = static_cast<const T*>(a.X);
     Lanes<VEC, NV> L(a.W);
     int64_t row = ((int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x) / a.W;
     if (row >= a.n_rows) return;  // groups are whole: no group is split by this test
@@ -315,8 +317,8 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
 
     if constexpr (OP == Op::Sddmm) {
         float u[NV][VEC];
-        load_row<VEC, NV>(u, a.U + u_row_of(a, row) * a.ldu, L, a.F);
-        sddmm_edges<VEC, NV, U>(u, a.col_idx, b, e, 1, a.X, a.ldx, L, a.F, a.Y, a.out_idx);
+        load_row<T, VEC, NV>(u, static_cast<const T*>(a.U) + u_row_of(a, row) * a.ldu, L, a.F);
+        sddmm_edges<T, VEC, NV, U>(u, a.col_idx, b, e, 1, X, a.ldx, L, a.F, a.Y, a.out_idx);
     } else {
         float acc[NV][VEC];
         zero(acc);
@@ -325,10 +327,10 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
             seg_softmax_stats(a.ev, b, e, L.lg, a.W, a.scale, m, l);
         }
         if (OP == Op::Spmm && a.W == CSR_WAVE)
-            gather_acc_wave<VEC, NV, U>(acc, a.col_idx, a.ev, __builtin_amdgcn_readfirstlane(b),
-                                        __builtin_amdgcn_readfirstlane(e), a.X, a.ldx, L, a.F);
+            gather_acc_wave<T, VEC, NV, U>(acc, a.col_idx, a.ev, __builtin_amdgcn_readfirstlane(b),
+                                           __builtin_amdgcn_readfirstlane(e), X, a.ldx, L, a.F);
         else
-            gather_acc<OP, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, a.X, a.ldx, L, a.F, a.scale, m);
+            gather_acc<OP, T, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, X, a.ldx, L, a.F, a.scale, m);
         float* dst = a.Y + row * a.ldy;
         if (OP == Op::Attention && e > b)
             store_row_div<VEC, NV>(dst, acc, L, a.F, l);
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup_wide(Fp32Args a)
         lo[j] = (uint32_t)(off + 4 <= F ? off : (off < F ? F - 4 : 0)) * 4u;
     }
     const uint32_t row_bytes = (uint32_t)a.ldx * 4u;
-    const char* xb = reinterpret_cast<const char*>(a.X);
+    const char* xb = static_cast<const char*>(a.X);
     float4_a4 acc[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) acc[j] = float4_a4{0.f, 0.f, 0.f, 0.f};
@@ -441,10 +443,12 @@ struct MpShared {
     float ev[CSR_WAVES_PER_BLOCK][D];
 };
 
-template <Op OP, int VEC, int NV, int U, int D>
+template <Op OP, typename T, int VEC, int NV, int U, int D>
 __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
 {
     __shared__ MpShared<D> sh;
+    const T* X = static_cast<const T*>(a.X);
+    const T* Urow = static_cast<const T*>(a.U);
     const int wave = threadIdx.x / CSR_WAVE;
     const int lane = lane_id();
     const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
@@ -512,16 +516,16 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
             const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
             if (se - sb < long_row || se <= sb) continue;
             float u[NV][VEC];
-            load_row<VEC, NV>(u, a.U + u_row_of(a, (int64_t)x0 + i) * a.ldu, L, a.F);
-            sddmm_edges<VEC, NV, U>(u, col, sb + L.g, se, G, a.X, a.ldx, L, a.F, a.Y, a.out_idx);
+            load_row<T, VEC, NV>(u, Urow + u_row_of(a, (int64_t)x0 + i) * a.ldu, L, a.F);
+            sddmm_edges<T, VEC, NV, U>(u, col, sb + L.g, se, G, X, a.ldx, L, a.F, a.Y, a.out_idx);
         }
         // pass 2: short segments, one group each
         for (int i = L.g; i < nrow; i += G) {
             const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
             if (se - sb >= long_row || se <= sb) continue;
             float u[NV][VEC];
-            load_row<VEC, NV>(u, a.U + u_row_of(a, (int64_t)x0 + i) * a.ldu, L, a.F);
-            sddmm_edges<VEC, NV, U>(u, col, sb, se, 1, a.X, a.ldx, L, a.F, a.Y, a.out_idx);
+            load_row<T, VEC, NV>(u, Urow + u_row_of(a, (int64_t)x0 + i) * a.ldu, L, a.F);
+            sddmm_edges<T, VEC, NV, U>(u, col, sb, se, 1, X, a.ldx, L, a.F, a.Y, a.out_idx);
         }
     } else {
         for (int i = 0; i < nrow; ++i) {
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
             zero(acc);
             float m = 0.f, l = 1.f;
             if constexpr (OP == Op::Attention) seg_softmax_stats(ev, sb, se, lane, CSR_WAVE, a.scale, m, l);
-            gather_acc<OP, VEC, NV, U>(acc, col, ev, sb + L.g, se, G, a.X, a.ldx, L, a.F, a.scale, m);
+            gather_acc<OP, T, VEC, NV, U>(acc, col, ev, sb + L.g, se, G, X, a.ldx, L, a.F, a.scale, m);
             if (G > 1) {
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
                 zero(acc);
                 float m = 0.f, l = 1.f;
                 if constexpr (OP == Op::Attention) seg_softmax_stats(ev, sb, se, L.lg, a.W, a.scale, m, l);
-                gather_acc<OP, VEC, NV, U>(acc, col, ev, sb, se, 1, a.X, a.ldx, L, a.F, a.scale, m);
+                gather_acc<OP, T, VEC, NV, U>(acc, col, ev, sb, se, 1, X, a.ldx, L, a.F, a.scale, m);
                 emit(i, acc, m, l, false);
             }
         }
@@ -566,10 +570,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
 // across the lanes (segments = runs of lanes holding the same row) and a
 // carry between batches; the last lane of a row's run writes the row.  SDDMM
 // needs no reduction across entries: each lane forms its entry's dot product.
-template <Op OP, int VEC, int NV, int U, int D>
+template <Op OP, typename T, int VEC, int NV, int U, int D>
 __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
 {
     __shared__ MpShared<D> sh;
+    const T* X = static_cast<const T*>(a.X);
+    const T* Urow = static_cast<const T*>(a.U);
     const int wave = threadIdx.x / CSR_WAVE;
     const int lane = lane_id();
     const int64_t chunk = (int64_t)blockIdx.x * CSR_WAVES_PER_BLOCK + wave;
@@ -612,11 +618,11 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
         }
         return lo;
     };
-    auto load_row = [&](float (&v)[NV][VEC], const float* src) {
+    auto load_row = [&](float (&v)[NV][VEC], const T* src) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             if (j * VEC < F) {
-                vload<VEC>(v[j], src + j * VEC);
+                vload_t<T, VEC>(v[j], src + j * VEC);
             } else {
 #pragma unroll
                 for (int t = 0; t < VEC; ++t) v[j][t] = 0.f;
@@ -631,8 +637,8 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
             for (int u = 0; u < U; ++u) {
                 const int e = b + u * CSR_WAVE + lane;
                 if (e < y1) {
-                    load_row(uv[u], a.U + u_row_of(a, (int64_t)x0 + row_of(e)) * a.ldu);
-                    load_row(xv[u], a.X + (int64_t)col[e] * a.ldx);
+                    load_row(uv[u], Urow + u_row_of(a, (int64_t)x0 + row_of(e)) * a.ldu);
+                    load_row(xv[u], X + (int64_t)col[e] * a.ldx);
                 }
             }
 #pragma unroll
@@ -687,7 +693,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
                 w[u] = ok ? ev[e] : 0.f;
                 ri[u] = ok ? row_of(e) : -1 - lane;  // a lane past the end forms no segment
                 if (ok) {
-                    load_row(xv[u], a.X + (int64_t)col[e] * a.ldx);
+                    load_row(xv[u], X + (int64_t)col[e] * a.ldx);
                 } else {
                     zero(xv[u]);
                 }

@@ -42,6 +42,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// ops of the lane-group kernels (fp32 accumulation; fp32 or bf16 operands)
 bool is_fp32_op(int op) { return op == CSR_OP_SPMM || op == CSR_OP_SDDMM || op == CSR_OP_ATTENTION; }
 
 void fnv(uint64_t& h, int64_t v)
@@ -70,6 +71,33 @@ int max_vec_f32(const csr_problem_t& p)
     return 1;
 }
 
+// bf16 operands are read 8, 4 or 2 values (16, 8 or 4 bytes) per lane
+// access; the fp32 output rows of SpMM and attention are written with the
+// same lane layout (8 floats as two 16-byte stores).  0: no such access fits
+// (an odd width or leading dimension, or operands not 4-byte aligned).
+int max_vec_bf16(const csr_problem_t& p)
+{
+    for (int v : {8, 4, 2}) {
+        if (p.width % v) continue;
+        const size_t in = 2u * v, outv = (v > 4 ? 4 : v), out = 4u * outv;
+        bool ok = true;
+        if (p.op == CSR_OP_SPMM || p.op == CSR_OP_ATTENTION) {
+            ok = (p.ld_b % v == 0) && (p.ld_out % outv == 0) && aligned(p.b, in) && aligned(p.out, out);
+        } else if (p.op == CSR_OP_SDDMM) {
+            ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && aligned(p.a, in) && aligned(p.b, in);
+        }
+        if (ok) return v;
+    }
+    return 0;
+}
+
+int max_vec(const csr_problem_t& p) { return p.dtype == CSR_DTYPE_BF16 ? max_vec_bf16(p) : max_vec_f32(p); }
+
+bool vec_ok(const csr_problem_t& p, int v)
+{
+    return p.dtype == CSR_DTYPE_BF16 ? (v == 2 || v == 4 || v == 8) : (v == 1 || v == 2 || v == 4);
+}
+
 bool natural_layout(int64_t width, int vec, int* W, int* nv)
 {
     if (width <= 0 || vec <= 0 || width % vec) return false;
@@ -93,7 +121,8 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         return code;
     };
     if (p.op < CSR_OP_SPMM || p.op > CSR_OP_SOFTMAX_BWD) return fail(CSR_ERR_SHAPE, "unknown op");
-    if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "this op takes fp32 operands");
+    if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32 && p.dtype != CSR_DTYPE_BF16)
+        return fail(CSR_ERR_DTYPE, "this op takes fp32 or bf16 operands");
     if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
     if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         const int64_t lim = (int64_t)1 << 31;
@@ -120,10 +149,15 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
     if (is_fp32_op(p.op)) {
         if (p.width < 1 || p.width > 4096) return fail(CSR_ERR_SHAPE, "feature width must be in [1, 4096]");
         int W, nv;
-        if (!natural_layout(p.width, 1, &W, &nv) && !natural_layout(p.width, 2, &W, &nv) &&
-            !natural_layout(p.width, 4, &W, &nv))
+        if (p.dtype == CSR_DTYPE_BF16) {
+            if (p.width % 2) return fail(CSR_ERR_SHAPE, "bf16 operands need an even width");
+            if (max_vec_bf16(p) == 0)
+                return fail(CSR_ERR_ALIGN, "bf16 operands need even leading dimensions and 4-byte aligned rows");
+        } else if (!natural_layout(p.width, 1, &W, &nv) && !natural_layout(p.width, 2, &W, &nv) &&
+                   !natural_layout(p.width, 4, &W, &nv)) {
             return fail(CSR_ERR_SHAPE, "feature width not supported");
-        if (!natural_layout(p.width, max_vec_f32(p), &W, &nv))
+        }
+        if (!natural_layout(p.width, max_vec(p), &W, &nv))
             return fail(CSR_ERR_SHAPE, "feature width too large for the operands' alignment");
         // leading dimensions below 2^30 elements: row strides in bytes fit 32 bits
         const int64_t ld_lim = (int64_t)1 << 30;
@@ -180,8 +214,8 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
     if (s.flags & CSR_SCHED_WIDE) {
         // 4 floats per lane at any 4-byte alignment, 64 lanes per row, the
         // last lane's vector ending at the width
-        if (p.op != CSR_OP_SPMM || s.mapping != CSR_MAP_ROWGROUP)
-            return fail("wide lanes serve SpMM with the row-group mapping");
+        if (p.op != CSR_OP_SPMM || s.mapping != CSR_MAP_ROWGROUP || p.dtype != CSR_DTYPE_F32)
+            return fail("wide lanes serve fp32 SpMM with the row-group mapping");
         if (p.width < 4) return fail("wide lanes need a width of at least 4");
         if (s.vec != 4 || s.group_lanes != 64 || s.chunk_items != 0 || s.long_row != 0)
             return fail("wide lanes take vec 4, 64 lanes per row, chunk_items = long_row = 0");
@@ -213,8 +247,8 @@ int check_schedule(const csr_problem_t& p, const csr_schedule_t& s, std::string*
         if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
         return CSR_OK;
     }
-    if (s.vec != 1 && s.vec != 2 && s.vec != 4) return fail("vec must be 1, 2 or 4");
-    if (s.vec > max_vec_f32(p) || p.width % s.vec) return fail("vec not allowed by the operands' width or alignment");
+    if (!vec_ok(p, s.vec)) return fail(p.dtype == CSR_DTYPE_BF16 ? "bf16 vec must be 2, 4 or 8" : "vec must be 1, 2 or 4");
+    if (s.vec > max_vec(p) || p.width % s.vec) return fail("vec not allowed by the operands' width or alignment");
     if (!pow2(s.group_lanes) || s.group_lanes > 64) return fail("group_lanes must be a power of two <= 64");
     if (!nv_ok(s.passes)) return fail("unsupported pass count");
     const int64_t per_pass = (int64_t)s.group_lanes * s.vec;
@@ -298,7 +332,7 @@ csr_schedule_t default_schedule(const csr_problem_t& p)
         s.long_row = 0;
         return s;
     }
-    s.vec = max_vec_f32(p);
+    s.vec = max_vec(p);
     int W = 1, nv = 1;
     natural_layout(p.width, s.vec, &W, &nv);
     s.group_lanes = W;
@@ -354,7 +388,7 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
         s.long_row = 0;
         add(s);
         // wide lanes where the operands allow only narrower aligned accesses
-        if (p.op == CSR_OP_SPMM && p.width >= 64 && (max_vec_f32(p) < 4 || p.width % 4)) {
+        if (p.op == CSR_OP_SPMM && p.dtype == CSR_DTYPE_F32 && p.width >= 64 && (max_vec_f32(p) < 4 || p.width % 4)) {
             s.vec = 4;
             s.group_lanes = 64;
             s.passes = nv_up((p.width + 255) / 256);
@@ -408,7 +442,7 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
         const double cus = dev.cu_count > 0 ? dev.cu_count : 256.0;
         return p.nnz * 8.0 / bw + 3 * launch + nc * per_chunk / (cus * 8.0);
     }
-    const double esize = (p.op == CSR_OP_MHA) ? 2.0 : 4.0;
+    const double esize = (p.op == CSR_OP_MHA || p.dtype == CSR_DTYPE_BF16) ? 2.0 : 4.0;
     const double gathers = (p.op == CSR_OP_MHA) ? 2.0 : 1.0;
     const double row_bytes = p.width * esize * gathers;
     // wide lanes: idle lanes read lines that their pass reads anyway, and
@@ -494,7 +528,7 @@ void hybrid_plan(const csr_problem_t& p, const int64_t* hist, int* parts, int* w
     if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return;
     if (p.nnz <= 0 || p.n_cols <= 0 || p.n_rows <= 0) return;
     const double mib = 1 << 20;
-    const double row = p.width * 4.0;
+    const double row = p.width * (p.dtype == CSR_DTYPE_BF16 ? 2.0 : 4.0);
     const double X = p.n_cols * row;
     if (p.op == CSR_OP_SDDMM) {
         if (p.width > 16) return;
@@ -567,7 +601,7 @@ uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo
     fnv(h, p.width);
     fnv(h, p.op == CSR_OP_MHA ? p.heads : 0);
     fnv(h, p.op == CSR_OP_MHA ? p.head_dim : 0);
-    fnv(h, p.op == CSR_OP_MHA ? 8 : max_vec_f32(p));
+    fnv(h, p.op == CSR_OP_MHA ? 8 : (is_fp32_op(p.op) ? max_vec(p) : max_vec_f32(p)));
     fnv(h, dev.cu_count);
     fnv(h, dev.arch);
     for (int i = 0; i < kHistInts; ++i) fnv(h, hist ? hist[i] : 0);

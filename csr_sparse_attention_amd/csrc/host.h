@@ -24,6 +24,10 @@ struct DeviceInfo {
 
 // Largest fp32 vector width (1, 2, 4) that the operands' alignment allows.
 int max_vec_f32(const csr_problem_t& p);
+// Largest bf16 vector width (2, 4, 8; 0 if none) that the operands allow.
+int max_vec_bf16(const csr_problem_t& p);
+// The widest lane access for p's element type.
+int max_vec(const csr_problem_t& p);
 
 // Checks the shape, dtype and pointer fields of p for its op.  need_ptrs:
 // operand pointers must be non-null.  Returns CSR_OK or an error code and a

@@ -7,7 +7,7 @@
 namespace csrk {
 hipError_t launch_attention(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s)
 {
-    return dispatch_main<Op::Attention>(mapping, vec, nv, chunk, a, s);
+    return dispatch_main<Op::Attention, float>(mapping, vec, nv, chunk, a, s);
 }
 hipError_t launch_attention_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s)
 {

@@ -7,6 +7,6 @@
 namespace csrk {
 hipError_t launch_sddmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s)
 {
-    return dispatch_main<Op::Sddmm>(mapping, vec, nv, chunk, a, s);
+    return dispatch_main<Op::Sddmm, float>(mapping, vec, nv, chunk, a, s);
 }
 } // namespace csrk

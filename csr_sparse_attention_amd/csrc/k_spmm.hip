@@ -7,7 +7,7 @@
 namespace csrk {
 hipError_t launch_spmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s)
 {
-    return dispatch_main<Op::Spmm>(mapping, vec, nv, chunk, a, s);
+    return dispatch_main<Op::Spmm, float>(mapping, vec, nv, chunk, a, s);
 }
 hipError_t launch_spmm_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s)
 {

@@ -39,6 +39,11 @@ hipError_t launch_spmm_wide(int nv, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
 hipError_t launch_sddmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+// the same main kernels over bf16 gathered (and SDDMM row) operands, vec = 2, 4, 8
+// bf16 values per lane; the fix-ups read fp32 pieces and are shared
+hipError_t launch_spmm_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_sddmm_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_attention_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_mha(int mapping, int lph, int chunk, const MhaArgs& a, hipStream_t s);
 hipError_t launch_mha_fixup(int lph, const MhaArgs& a, hipStream_t s);
 

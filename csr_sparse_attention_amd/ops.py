@@ -135,9 +135,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+_DTYPES = {torch.float32: _ffi.DTYPE_F32, torch.bfloat16: _ffi.DTYPE_BF16}
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    """The csr_dtype of a dense operand (fp32 or bf16)."""
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
 def _dense(t: torch.Tensor, name: str, dtype) -> int:
-    """Leading dimension of a row-major 2-D operand (inner stride 1)."""
-    if t.dtype != dtype:
+    """Leading dimension of a row-major 2-D operand (inner stride 1); dtype
+    is one torch dtype or a tuple of accepted ones."""
+    if t.dtype != dtype and not (isinstance(dtype, tuple) and t.dtype in dtype):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit inner stride")
@@ -168,8 +179,9 @@ def _on(device, **tensors):
 
 
 def _rows(t, name, n_rows, width=None, dtype=torch.float32):
-    """A row-major 2-D operand of exactly n_rows rows (and width columns)."""
-    if t.dtype != dtype:
+    """A row-major 2-D operand of exactly n_rows rows (and width columns);
+    dtype is one torch dtype or a tuple of accepted ones."""
+    if t.dtype != dtype and not (isinstance(dtype, tuple) and t.dtype in dtype):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
@@ -211,10 +223,12 @@ def _sched_arg(schedule: Optional[CsrSchedule]):
 # ---------------------------------------------------------------------------
 
 def _problem(op: int, row_ptr, col_idx, a, b, c, out, *, n_cols, width, ld_a=0, ld_b=0, ld_out=0,
-             heads=0, head_dim=0, scale=1.0) -> CsrProblem:
+             heads=0, head_dim=0, scale=1.0, dtype=None) -> CsrProblem:
     p = CsrProblem()
     p.op = op
-    p.dtype = _ffi.DTYPE_BF16 if op == _ffi.OP_MHA else _ffi.DTYPE_F32
+    if dtype is None:
+        dtype = _ffi.DTYPE_BF16 if op == _ffi.OP_MHA else _ffi.DTYPE_F32
+    p.dtype = dtype
     p.n_rows = row_ptr.numel() - 1
     p.n_cols = n_cols
     p.nnz = col_idx.numel()
@@ -228,19 +242,21 @@ def _problem(op: int, row_ptr, col_idx, a, b, c, out, *, n_cols, width, ld_a=0, 
 
 
 def _spmm_problem(row_ptr, col_idx, vals, X, out):
-    ldx = _dense(X, "X", torch.float32)
+    ldx = _dense(X, "X", (torch.float32, torch.bfloat16))
     ldy = _dense(out, "out", torch.float32)
     return _problem(_ffi.OP_SPMM, row_ptr, col_idx, vals, X, None, out, n_cols=X.shape[0],
-                    width=X.shape[1], ld_b=ldx, ld_out=ldy)
+                    width=X.shape[1], ld_b=ldx, ld_out=ldy, dtype=_dtype_code(X, "X"))
 
 
 def _sddmm_problem(row_ptr, col_idx, U, V, out):
-    ldu = _dense(U, "U", torch.float32)
-    ldv = _dense(V, "V", torch.float32)
+    ldu = _dense(U, "U", (torch.float32, torch.bfloat16))
+    ldv = _dense(V, "V", (torch.float32, torch.bfloat16))
     if U.shape[1] != V.shape[1]:
         raise ValueError("U and V must have the same width")
+    if U.dtype != V.dtype:
+        raise TypeError(f"U and V must have one dtype, got {U.dtype} and {V.dtype}")
     return _problem(_ffi.OP_SDDMM, row_ptr, col_idx, U, V, None, out, n_cols=V.shape[0],
-                    width=U.shape[1], ld_a=ldu, ld_b=ldv)
+                    width=U.shape[1], ld_a=ldu, ld_b=ldv, dtype=_dtype_code(U, "U"))
 
 
 def _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale):
@@ -292,7 +308,8 @@ def _run(problem: CsrProblem, device, schedule, ctx, call, workspace=None):
 def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule] = None,
          ctx: Optional[Context] = None,
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = A X for the CSR matrix A (row_ptr, col_idx, vals; vals=None means 1)."""
+    """Y = A X for the CSR matrix A (row_ptr, col_idx, vals; vals=None means 1).
+    X is float32 or bfloat16 (fp32 accumulation); Y is float32."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     _on(row_ptr.device, vals=vals, X=X)
     if X.dim() != 2:
@@ -303,7 +320,7 @@ def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule]
     p = _spmm_problem(row_ptr, col_idx, vals, X, out)
 
     def call(ctx, ws, nb, st):
-        return _lib().csr_spmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
+        return _lib().csr_spmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b, p.dtype,
                                p.width, p.ld_b, p.out, p.ld_out, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
     _run(p, X.device, schedule, ctx, call, workspace)
@@ -313,10 +330,11 @@ def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule]
 def sddmm(row_ptr, col_idx, U, V, *, out=None, schedule: Optional[CsrSchedule] = None,
           ctx: Optional[Context] = None,
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out[e] = <U[row(e)], V[col_idx[e]]> for every stored entry e."""
+    """out[e] = <U[row(e)], V[col_idx[e]]> for every stored entry e (U and V
+    both float32 or both bfloat16; fp32 accumulation and output)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     _on(row_ptr.device, U=U, V=V)
-    _rows(U, "U", n_rows)
+    _rows(U, "U", n_rows, dtype=(torch.float32, torch.bfloat16))
     if V.dim() != 2:
         raise ValueError("V must be 2-D [n_cols, K]")
     out = _out_entries(out, nnz, U.device)
@@ -324,7 +342,7 @@ def sddmm(row_ptr, col_idx, U, V, *, out=None, schedule: Optional[CsrSchedule] =
 
     def call(ctx, ws, nb, st):
         return _lib().csr_sddmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.ld_a,
-                                p.b, p.ld_b, p.width, p.out, _sched_arg(schedule), ws.data_ptr(), nb, st)
+                                p.b, p.ld_b, p.dtype, p.width, p.out, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
     _run(p, U.device, schedule, ctx, call, workspace)
     return out
@@ -618,7 +636,7 @@ def hybrid_problem(h: Hybrid, op: str, *operands) -> CsrProblem:
     if op == "spmm":
         vals, X = operands
         p = _problem(_ffi.OP_SPMM, h.seg_ptr, h.col_idx, vals, X, None, None, n_cols=X.shape[0], width=X.shape[1],
-                     ld_b=_dense(X, "X", torch.float32), ld_out=X.shape[1])
+                     ld_b=_dense(X, "X", (torch.float32, torch.bfloat16)), ld_out=X.shape[1], dtype=_dtype_code(X, "X"))
         p.out = 256  # stands for the partial rows, which sit 256-byte aligned in the workspace
         return p
     if op == "sddmm":
@@ -627,11 +645,11 @@ def hybrid_problem(h: Hybrid, op: str, *operands) -> CsrProblem:
     raise ValueError(op)
 
 
-def _hybrid_run(h, op, width, schedule, ctx, device, call, workspace=None):
+def _hybrid_run(h, op, width, dtype, schedule, ctx, device, call, workspace=None):
     ctx = ctx or default_context(device.index)
     lib = _lib()
     nbytes = ctypes.c_size_t()
-    _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), op, width, _sched_arg(schedule),
+    _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), op, width, dtype, _sched_arg(schedule),
                                          ctypes.byref(nbytes)), "csr_hybrid_workspace_size", ctx)
     ws = _workspace(device, nbytes.value, workspace)
     _check(call(ctx, ws, nbytes.value, _stream(device)), "csr hybrid call", ctx)
@@ -651,15 +669,18 @@ def hybrid_select(h: Hybrid, op: str, *operands, mode: str = "auto", out=None, c
     if call.op < 0:
         raise ValueError(op)
     call.width = b.shape[1]
-    call.b, call.ld_b = b.data_ptr(), _dense(b, "X" if op == "spmm" else "V", torch.float32)
+    call.b, call.ld_b = b.data_ptr(), _dense(b, "X" if op == "spmm" else "V", (torch.float32, torch.bfloat16))
+    call.dtype = _dtype_code(b, "X" if op == "spmm" else "V")
     if op == "spmm":
         call.a = _ptr(a)
     else:
-        call.a, call.ld_a = a.data_ptr(), _dense(a, "U", torch.float32)
+        call.a, call.ld_a = a.data_ptr(), _dense(a, "U", (torch.float32, torch.bfloat16))
+        if a.dtype != b.dtype:
+            raise TypeError("U and V must have one dtype")
         out = out if out is not None else torch.empty(h.nnz, dtype=torch.float32, device=device)
         call.out = out.data_ptr()
     nbytes = ctypes.c_size_t()
-    _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), call.op, call.width, None,
+    _check(lib.csr_hybrid_workspace_size(ctx.handle, ctypes.byref(h.desc), call.op, call.width, call.dtype, None,
                                          ctypes.byref(nbytes)), "csr_hybrid_workspace_size", ctx)
     ws = _workspace(device, nbytes.value)
     call.workspace, call.workspace_bytes, call.stream = ws.data_ptr(), nbytes.value, _stream(device)
@@ -675,18 +696,19 @@ def hybrid_spmm(h: Hybrid, vals, X, *, out=None, schedule: Optional[CsrSchedule]
     """Y = A X over the format; ``vals`` in the format's entry order
     (hybrid_values) or None for all ones."""
     _on(h.perm.device, vals=vals, X=X)
-    _rows(X, "X", h.n_cols)
-    ldx = _dense(X, "X", torch.float32)
+    _rows(X, "X", h.n_cols, dtype=(torch.float32, torch.bfloat16))
+    ldx = _dense(X, "X", (torch.float32, torch.bfloat16))
+    xd = _dtype_code(X, "X")
     out = _out_rows(out, h.n_rows, X.shape[1], X.device)
     ldy = _dense(out, "out", torch.float32)
     if vals is not None:
         _flat_f32(vals, "vals", h.nnz)
 
     def call(ctx, ws, nb, st):
-        return _lib().csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), _ptr(vals), X.data_ptr(), X.shape[1], ldx,
-                                      out.data_ptr(), ldy, _sched_arg(schedule), ws.data_ptr(), nb, st)
+        return _lib().csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), _ptr(vals), X.data_ptr(), xd, X.shape[1],
+                                      ldx, out.data_ptr(), ldy, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _hybrid_run(h, _ffi.OP_SPMM, X.shape[1], schedule, ctx, X.device, call, workspace)
+    _hybrid_run(h, _ffi.OP_SPMM, X.shape[1], xd, schedule, ctx, X.device, call, workspace)
     return out
 
 
@@ -695,17 +717,18 @@ def hybrid_sddmm(h: Hybrid, U, V, *, out=None, schedule: Optional[CsrSchedule] =
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[e] = <U[row(e)], V[col(e)]> over the format, in the original entry order."""
     _on(h.perm.device, U=U, V=V)
-    _rows(U, "U", h.n_rows)
-    _rows(V, "V", h.n_cols, U.shape[1])
-    ldu = _dense(U, "U", torch.float32)
-    ldv = _dense(V, "V", torch.float32)
+    _rows(U, "U", h.n_rows, dtype=(torch.float32, torch.bfloat16))
+    _rows(V, "V", h.n_cols, U.shape[1], dtype=U.dtype)
+    ldu = _dense(U, "U", (torch.float32, torch.bfloat16))
+    ldv = _dense(V, "V", (torch.float32, torch.bfloat16))
+    dt = _dtype_code(U, "U")
     out = _out_entries(out, h.nnz, U.device)
 
     def call(ctx, ws, nb, st):
-        return _lib().csr_hybrid_sddmm(ctx.handle, ctypes.byref(h.desc), U.data_ptr(), ldu, V.data_ptr(), ldv,
+        return _lib().csr_hybrid_sddmm(ctx.handle, ctypes.byref(h.desc), U.data_ptr(), ldu, V.data_ptr(), ldv, dt,
                                        U.shape[1], out.data_ptr(), _sched_arg(schedule), ws.data_ptr(), nb, st)
 
-    _hybrid_run(h, _ffi.OP_SDDMM, U.shape[1], schedule, ctx, U.device, call, workspace)
+    _hybrid_run(h, _ffi.OP_SDDMM, U.shape[1], dt, schedule, ctx, U.device, call, workspace)
     return out
 
 

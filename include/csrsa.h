@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define CSRSA_ABI_VERSION 1
+#define CSRSA_ABI_VERSION 2
 #define CSR_SCHEDULE_VERSION 1
 
 typedef struct csr_context_s* csr_context_t;
@@ -88,6 +88,11 @@ enum csr_op {
     CSR_OP_SOFTMAX_BWD = 6  /* ds_e = scale * p_e * (g_e - sum over the row of p g) */
 };
 
+/* Element types of the dense operands.  bf16 operands are raw bfloat16 bit
+ * patterns (uint16), widened exactly to fp32 on load; every op accumulates
+ * and writes fp32.  bf16 operands of the lane-group ops (SpMM, SDDMM,
+ * attention) need an even width, even leading dimensions and 4-byte aligned
+ * rows (lane accesses of 2, 4 or 8 values). */
 enum csr_dtype { CSR_DTYPE_F32 = 0, CSR_DTYPE_BF16 = 1 };
 
 /* Row mappings (the "mapping" half of a schedule). */
@@ -142,7 +147,7 @@ typedef struct csr_schedule_s {
     int32_t version;     /* CSR_SCHEDULE_VERSION */
     int32_t op;          /* enum csr_op */
     int32_t mapping;     /* enum csr_mapping */
-    int32_t vec;         /* elements per lane access: 1, 2, 4 (fp32), 8 (bf16) */
+    int32_t vec;         /* elements per lane access: 1, 2, 4 (fp32 operands); 2, 4, 8 (bf16) */
     int32_t group_lanes; /* W: lanes per row group, power of two in [1, 64] */
     int32_t passes;      /* feature passes per lane (width = W * vec * passes, rounded) */
     int32_t chunk_items; /* merge-path: rows + entries per wavefront chunk (256, 512, 1024) */
@@ -155,10 +160,10 @@ typedef struct csr_schedule_s {
  * A problem description: the same fields as the operation calls, used by
  * csr_select() and csr_workspace_size().  Unused pointers may be NULL for
  * csr_workspace_size().
- *   op = CSR_OP_SPMM:      a = vals (fp32 [nnz], NULL = all ones), b = X, width = F,
+ *   op = CSR_OP_SPMM:      a = vals (fp32 [nnz], NULL = all ones), b = X (dtype), width = F,
  *                          ld_b = ldx, out = Y, ld_out = ldy
- *   op = CSR_OP_SDDMM:     a = U [n_rows, K], ld_a = ldu, b = V [n_cols, K], ld_b = ldv,
- *                          width = K, out = fp32 [nnz]
+ *   op = CSR_OP_SDDMM:     a = U [n_rows, K], ld_a = ldu, b = V [n_cols, K], ld_b = ldv
+ *                          (both of dtype), width = K, out = fp32 [nnz]
  *   op = CSR_OP_ATTENTION: a = edge_scores fp32 [nnz], b = node_value [n_cols, F],
  *                          ld_b, width = F, out [n_rows, F], ld_out, scale
  *   op = CSR_OP_MHA:       a = Q, b = K, c = V (bf16 [n, heads, head_dim]), heads,
@@ -223,20 +228,25 @@ const char* csr_last_error(csr_context_t ctx);
 
 /* SpMM (AutoSAGE page, Abstract: CSR SpMM):
  *   Y[i, f] = sum over stored entries e of row i of vals[e] * X[col_idx[e], f]
- * vals: fp32 [nnz] or NULL (all ones).  X: fp32 [n_cols, ldx], F <= ldx.
- * Y: fp32 [n_rows, ldy], F <= ldy.  1 <= F <= 4096. */
+ * vals: fp32 [nnz] or NULL (all ones).  X: [n_cols, ldx] of x_dtype
+ * (CSR_DTYPE_F32, or CSR_DTYPE_BF16 bit patterns), F <= ldx.  Y: fp32
+ * [n_rows, ldy], F <= ldy.  1 <= F <= 4096.  Accumulation is fp32 for both
+ * dtypes.  CSR_ERR_DTYPE for another dtype; bf16 X with an odd width:
+ * CSR_ERR_SHAPE; with odd ldx or rows not 4-byte aligned: CSR_ERR_ALIGN. */
 int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
              const int32_t* row_ptr, const int32_t* col_idx, const float* vals,
-             const float* X, int64_t F, int64_t ldx, float* Y, int64_t ldy,
+             const void* X, int32_t x_dtype, int64_t F, int64_t ldx, float* Y, int64_t ldy,
              const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
 
 /* SDDMM (AutoSAGE page, Abstract: CSR SDDMM):
  *   out[e] = sum over k < K of U[i, k] * V[col_idx[e], k] for every stored
  *   entry e of row i, in CSR order.
- * U: fp32 [n_rows, ldu], V: fp32 [n_cols, ldv], out: fp32 [nnz].  1 <= K <= 4096. */
+ * U: [n_rows, ldu], V: [n_cols, ldv], both of dtype (CSR_DTYPE_F32 or
+ * CSR_DTYPE_BF16); out: fp32 [nnz], fp32 accumulation.  1 <= K <= 4096.
+ * bf16 rules and errors as for csr_spmm. */
 int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
               const int32_t* row_ptr, const int32_t* col_idx,
-              const float* U, int64_t ldu, const float* V, int64_t ldv, int64_t K,
+              const void* U, int64_t ldu, const void* V, int64_t ldv, int32_t dtype, int64_t K,
               float* out, const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
               void* stream);
 
@@ -406,34 +416,34 @@ int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* c
 
 /* Device workspace (bytes) of csr_hybrid_spmm (op CSR_OP_SPMM: includes the
  * segments' partial rows, n_seg * width floats) or csr_hybrid_sddmm (op
- * CSR_OP_SDDMM) at this width, for schedule sched (NULL: any the selector may
- * pick).  h must be built. */
-int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width,
+ * CSR_OP_SDDMM) at this width and dtype, for schedule sched (NULL: any the
+ * selector may pick).  h must be built. */
+int csr_hybrid_workspace_size(csr_context_t ctx, const csr_hybrid_t* h, int32_t op, int64_t width, int32_t dtype,
                               const csr_schedule_t* sched, size_t* bytes);
 
 /* Y = A X over a built format: each segment's product into its partial row
  * (a CSR SpMM of the n_seg-row segment pattern, any mapping), then
  * Y[r] = the sum of row r's partial rows in part order (+0 for a row without
  * entries).  vals: [nnz] edge values in FORMAT order (csr_gather_values with
- * h->perm moves them there), or NULL for all ones.  X, F, ldx, Y, ldy as for
- * csr_spmm.  sched: a schedule of op CSR_OP_SPMM for the segment pattern
- * (NULL: selected and cached as for csr_spmm, keyed by the segment pattern's
- * shape and degree histogram). */
-int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals, const float* X, int64_t F,
-                    int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
+ * h->perm moves them there), or NULL for all ones.  X, x_dtype, F, ldx, Y,
+ * ldy as for csr_spmm.  sched: a schedule of op CSR_OP_SPMM for the segment
+ * pattern (NULL: selected and cached as for csr_spmm, keyed by the segment
+ * pattern's shape and degree histogram). */
+int csr_hybrid_spmm(csr_context_t ctx, const csr_hybrid_t* h, const float* vals, const void* X, int32_t x_dtype,
+                    int64_t F, int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
                     size_t ws_bytes, void* stream);
 
 /* out[e] = dot(U[row(e)], V[col(e)]) over a built format, written in the
  * ORIGINAL entry order (the kernels read U through seg_row and write through
- * perm).  U, ldu, V, ldv, K, out as for csr_sddmm; sched: a schedule of op
- * CSR_OP_SDDMM for the segment pattern (NULL: selected). */
-int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const float* U, int64_t ldu, const float* V,
-                     int64_t ldv, int64_t K, float* out, const csr_schedule_t* sched, void* workspace,
+ * perm).  U, ldu, V, ldv, dtype, K, out as for csr_sddmm; sched: a schedule
+ * of op CSR_OP_SDDMM for the segment pattern (NULL: selected). */
+int csr_hybrid_sddmm(csr_context_t ctx, const csr_hybrid_t* h, const void* U, int64_t ldu, const void* V,
+                     int64_t ldv, int32_t dtype, int64_t K, float* out, const csr_schedule_t* sched, void* workspace,
                      size_t ws_bytes, void* stream);
 
 /* Selects (and caches) the schedule of the segment product of a call over a
  * built format, as csr_select does for a plain call.  call describes the
- * call's operands only: op (CSR_OP_SPMM or CSR_OP_SDDMM), width, a / ld_a
+ * call's operands only: op (CSR_OP_SPMM or CSR_OP_SDDMM), dtype, width, a / ld_a
  * (SpMM: the format-order values or NULL; SDDMM: U), b / ld_b (X or V), out
  * (SDDMM: the [nnz] output, written by the probes; SpMM: unused, the probes
  * write the partial rows into the workspace), workspace (of

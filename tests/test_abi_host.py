@@ -111,6 +111,22 @@ def test_problem_errors():
     assert rc(problem(_ffi.OP_SPMM, nnz=-1)) == -2
     assert rc(problem(_ffi.OP_SPMM, nnz=2**31)) == -2
     p = problem(_ffi.OP_SPMM)
+    p.dtype = 7  # no such element type
+    assert rc(p) == -3
+    for op in (_ffi.OP_SPMM, _ffi.OP_SDDMM, _ffi.OP_ATTENTION):
+        p = problem(op)
+        p.dtype = _ffi.DTYPE_BF16
+        assert rc(p) == 0                        # bf16 operands, fp32 accumulation
+        p = problem(op, width=63, ld=64)
+        p.dtype = _ffi.DTYPE_BF16
+        assert rc(p) == -2                       # bf16 needs an even width
+        p = problem(op, width=64, ld=65)
+        p.dtype = _ffi.DTYPE_BF16
+        assert rc(p) == -4                       # and even leading dimensions
+        p = problem(op, ptr=0x1002)
+        p.dtype = _ffi.DTYPE_BF16
+        assert rc(p) == -4                       # and 4-byte aligned rows
+    p = problem(_ffi.OP_ROW_SOFTMAX, width=1)
     p.dtype = _ffi.DTYPE_BF16
     assert rc(p) == -3
     assert rc(problem(_ffi.OP_MHA, width=512, heads=8, head_dim=64)) == 0
@@ -120,6 +136,24 @@ def test_problem_errors():
     p = problem(_ffi.OP_ATTENTION)
     p.scale = float("inf")
     assert rc(p) == -2
+
+
+@pytest.mark.parametrize("F,ld,ptr,vec,W,nv", [
+    (128, 128, 0x1000, 8, 16, 1), (602, 602, 0x1000, 2, 64, 5), (100, 100, 0x1000, 4, 32, 1),
+    (512, 512, 0x1000, 8, 64, 1), (4096, 4096, 0x1000, 8, 64, 8), (2, 2, 0x1000, 2, 1, 1),
+    (64, 64, 0x1008, 4, 16, 1), (64, 64, 0x1004, 2, 32, 1), (6, 6, 0x1000, 2, 4, 1),
+])
+def test_default_layout_bf16(F, ld, ptr, vec, W, nv):
+    """bf16 operands: the widest of 8, 4, 2 values per lane that the width,
+    the leading dimensions and the alignment allow (fp32 outputs written with
+    the same layout need 4 * min(vec, 4)-byte alignment)."""
+    p = problem(_ffi.OP_SPMM, width=F, ld=ld, ptr=ptr)
+    p.dtype = _ffi.DTYPE_BF16
+    p.out = 0x1000
+    s = csa.default_schedule(p)
+    assert (s.vec, s.group_lanes, s.passes) == (vec, W, nv)
+    # wide lanes are an fp32 schedule
+    assert all(not (c.flags & _ffi.SCHED_WIDE) for c in csa.candidates(p, [0] * 66 + [100]))
 
 
 def test_workspace_layout_sizes():
@@ -260,7 +294,7 @@ def test_cache_missing_and_unwritable(tmp_path):
 def test_host_only_context_refuses_operations():
     lib = csa.load_library()
     ctx = csa.Context(-1, None)
-    assert lib.csr_spmm(ctx.handle, 1, 1, 0, 0x1000, None, None, 0x1000, 4, 4, 0x1000, 4, None, 0x1000, 4096,
+    assert lib.csr_spmm(ctx.handle, 1, 1, 0, 0x1000, None, None, 0x1000, 0, 4, 4, 0x1000, 4, None, 0x1000, 4096,
                         None) == -11
     ctx.close()
 

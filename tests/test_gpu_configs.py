@@ -166,6 +166,36 @@ def test_c3_sddmm_full():
     print(f"c3 sddmm: {s} max err {e:.2e} over all {csr.nnz} entries")
 
 
+@pytest.mark.timeout(900)
+def test_c3_bf16_full():
+    """bf16 features on the c3 graph (SpMM F = 128, SDDMM K = 128), fp32
+    accumulation: every output element against the oracle reading the same
+    bf16 values exactly."""
+    from synth import to_bf16_bits
+
+    csr = pattern("c3")
+    rp, ci = pattern_dev("c3")
+    vals = configs.config_dense("c3", "vals", csr)
+    Xb = to_bf16_bits(configs.config_dense("c3", "X", csr, 128))
+    Xf = oracle.bf16_to_f32(Xb)
+    vd, Xd = dev(vals), bf16_dev(Xb)
+    s = selected("spmm", rp, ci, vd, Xd)
+    Y = csa.spmm(rp, ci, vd, Xd, schedule=s).cpu().numpy()
+    e1 = compare_all_rows(Y, lambda r0, r1: oracle.spmm(csr.row_ptr, csr.col_idx, vals, Xf, r0, r1, threads=THREADS),
+                          csr.row_ptr, 128, TOL_BF16, "c3 bf16 spmm")
+    del Y
+    Ub = to_bf16_bits(configs.config_dense("c3", "U", csr, 128))
+    Vb = to_bf16_bits(configs.config_dense("c3", "V", csr, 128))
+    Uf, Vf = oracle.bf16_to_f32(Ub), oracle.bf16_to_f32(Vb)
+    Ud, Vd = bf16_dev(Ub), bf16_dev(Vb)
+    sd = selected("sddmm", rp, ci, Ud, Vd)
+    out = csa.sddmm(rp, ci, Ud, Vd, schedule=sd).cpu().numpy()
+    e2 = compare_all_rows(out, lambda r0, r1: oracle.sddmm(csr.row_ptr, csr.col_idx, Uf, Vf, r0, r1, threads=THREADS),
+                          csr.row_ptr, 128, TOL_BF16, "c3 bf16 sddmm", per_entry=True)
+    assert max(e1, e2) <= TOL_F32  # exact bf16 inputs: only fp32 accumulation error remains
+    print(f"c3 bf16: spmm {s} max err {e1:.2e}; sddmm {sd} max err {e2:.2e} (all rows / entries)")
+
+
 # ---------------------------------------------------------------------------
 # single-head fp32 attention on the c3 graph, every output element: scores
 # given (the fused softmax-aggregation), and from queries and keys as the

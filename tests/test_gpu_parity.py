@@ -76,7 +76,7 @@ def schedules(problem, thorough=True):
                 s.mapping, s.chunk_items, s.long_row = csa.MAP_MERGEPATH, D, lr
                 out.append(s)
     # SpMM row groups with wide lanes (4 floats per lane at any 4-byte alignment)
-    if problem.op == _ffi.OP_SPMM and problem.width >= 4:
+    if problem.op == _ffi.OP_SPMM and problem.width >= 4 and problem.dtype == _ffi.DTYPE_F32:
         s = csa.CsrSchedule.from_buffer_copy(bytes(base))
         s.mapping, s.vec, s.group_lanes, s.chunk_items, s.long_row = csa.MAP_ROWGROUP, 4, 64, 0, 0
         need = -(-problem.width // 256)
@@ -451,10 +451,10 @@ def test_error_codes(skew):
 
     def call(**kw):
         a = dict(rp=rp.data_ptr(), ci=ci.data_ptr(), X=X.data_ptr(), F=16, ldx=16, Y=Y.data_ptr(), ldy=16,
-                 ws=ws.data_ptr(), wsb=ws.numel(), n=n, m=m, nnz=nnz, sched=None)
+                 ws=ws.data_ptr(), wsb=ws.numel(), n=n, m=m, nnz=nnz, sched=None, dt=0)
         a.update(kw)
-        return lib.csr_spmm(ctx.handle, a["n"], a["m"], a["nnz"], a["rp"], a["ci"], None, a["X"], a["F"], a["ldx"],
-                            a["Y"], a["ldy"], a["sched"], a["ws"], a["wsb"], st)
+        return lib.csr_spmm(ctx.handle, a["n"], a["m"], a["nnz"], a["rp"], a["ci"], None, a["X"], a["dt"], a["F"],
+                            a["ldx"], a["Y"], a["ldy"], a["sched"], a["ws"], a["wsb"], st)
 
     assert call() == 0
     assert call(rp=None) == -1
@@ -465,6 +465,10 @@ def test_error_codes(skew):
     assert call(X=X.data_ptr() + 2) == -4
     assert call(wsb=16) == -5
     assert call(ws=ws.data_ptr() + 64) == -4
+    assert call(dt=7) == -3                                   # unknown dtype
+    assert call(dt=1, F=15, ldx=16) == -2                     # bf16 with an odd width
+    assert call(dt=1, F=16, ldx=15) == -4                     # bf16 with an odd leading dimension
+    assert call(dt=1, X=X.data_ptr() + 2) == -4               # bf16 rows not 4-byte aligned
     p, _ = csa.make_problem("spmm", rp, ci, None, X, out=Y)
     s = csa.default_schedule(p)
     s.op = _ffi.OP_ATTENTION
@@ -895,12 +899,12 @@ def test_hybrid_deterministic_and_errors():
     d = _ffi.CsrHybrid.from_buffer_copy(bytes(h.desc))
     d.n_seg = -1
     Y = torch.empty((csr.n_rows, 16), device="cuda")
-    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(d), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(), 16,
+    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(d), hv.data_ptr(), X.data_ptr(), 0, 16, 16, Y.data_ptr(), 16,
                                None, ws.data_ptr(), ws.numel(), st) == -2
     # workspace too small, ldy below the width
-    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(),
+    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 0, 16, 16, Y.data_ptr(),
                                16, None, ws.data_ptr(), 4096, st) == -5
-    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 16, 16, Y.data_ptr(),
+    assert lib.csr_hybrid_spmm(ctx.handle, ctypes.byref(h.desc), hv.data_ptr(), X.data_ptr(), 0, 16, 16, Y.data_ptr(),
                                8, None, ws.data_ptr(), ws.numel(), st) == -2
     torch.cuda.synchronize()
 
