@@ -62,6 +62,7 @@ from .ops import (  # noqa: E402,F401
     signature,
     spmm,
     spmm_backward,
+    spmm_noalloc,
     transpose,
     workspace_size,
 )

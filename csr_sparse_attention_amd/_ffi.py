@@ -26,11 +26,12 @@ SCHED_WIDE = 1  # schedule flag: 16-byte lanes over 4-byte aligned rows (SpMM, r
 CTX_VALIDATE, CTX_NO_PROBE = 1, 2
 SELECT_MODES = {"auto": 0, "replay": 1, "probe": 2, "estimate": 3}
 SCHEDULE_VERSION = 1
+NOALLOC_SCRATCH_BYTES = 32 << 20  # CSR_NOALLOC_SCRATCH_BYTES
 
 # Every symbol the header declares.
 EXPORTS = (
     "csr_context_create", "csr_context_destroy", "csr_status_string", "csr_last_error",
-    "csr_spmm", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
+    "csr_spmm", "csr_spmm_noalloc", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
     "csr_row_softmax_backward", "csr_transpose_workspace_size", "csr_transpose", "csr_gather_values",
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
@@ -154,6 +155,7 @@ def load() -> ctypes.CDLL:
         "csr_status_string": [ctypes.c_int],
         "csr_last_error": [P],
         "csr_spmm": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
+        "csr_spmm_noalloc": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P],
         "csr_sddmm": [P, I64, I64, I64, P, P, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
         "csr_attention": [P, I64, I64, I64, P, P, P, P, I64, I64, F, P, I64, SP, P, SZ, P],
         "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, SP, P, SZ, P],

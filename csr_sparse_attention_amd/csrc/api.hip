@@ -37,9 +37,38 @@ struct csr_context_s {
     int64_t* pinned = nullptr;  // 4 KiB pinned host buffer
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     std::string last_error;
+    void* scratch = nullptr;        // this device's copy of the allocation-free scratch array
+    hipError_t scratch_err = hipSuccess;
 };
 
+// Scratch memory of the allocation-free entry point (csr_spmm_noalloc): a
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never uses the name itself (on the host it is only a stand-in,
+// not a device address): the address of each device's copy comes from
+// hipGetSymbolAddress, once per device, and is what kernels receive.
+static __device__ __align__(256) unsigned char scratch[CSR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Address of each device's copy of `scratch`, looked up once per device with
+// that device current.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[256] = {};
+
+hipError_t scratch_address(int device, void** out)
+{
+    if (device < 0 || device >= 256) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));  // the current device is `device`
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
 struct DeviceGuard {
     int prev = -1;
@@ -537,6 +566,9 @@ int csr_context_create(csr_context_t* out, int device, const char* cache_path, u
                 delete ctx;
                 return CSR_ERR_HIP;
             }
+            // with the device current: its copy of the allocation-free scratch
+            // array (a failure only disables csr_spmm_noalloc)
+            ctx->scratch_err = scratch_address(device, &ctx->scratch);
         } else {
             ctx->pinned = static_cast<int64_t*>(std::calloc(512, sizeof(int64_t)));
         }
@@ -587,6 +619,53 @@ int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, con
     p.workspace_bytes = ws_bytes;
     p.stream = stream;
     return op_call(ctx, p, sched);
+}
+
+int csr_spmm_noalloc(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                     const int32_t* col_idx, const float* vals, const void* X, int32_t x_dtype, int64_t F,
+                     int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        if (!sched) return set_err(ctx, CSR_ERR_NULL, "an explicit schedule is required (select one beforehand)");
+        if (ctx->scratch_err != hipSuccess || !ctx->scratch)
+            return hip_err(ctx, ctx->scratch_err != hipSuccess ? ctx->scratch_err : hipErrorInvalidSymbol,
+                           "scratch array address");
+        csr_problem_t p = blank_problem();
+        p.op = CSR_OP_SPMM;
+        p.dtype = x_dtype;
+        p.n_rows = n_rows;
+        p.n_cols = n_cols;
+        p.nnz = nnz;
+        p.width = F;
+        p.ld_b = ldx;
+        p.ld_out = ldy;
+        p.row_ptr = row_ptr;
+        p.col_idx = col_idx;
+        p.a = vals;
+        p.b = X;
+        p.out = Y;
+        p.stream = stream;
+        std::string why;
+        int rc = csrh::check_problem(p, true, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+        rc = csrh::check_schedule(p, *sched, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+        const size_t need = csrh::workspace_bytes(p, *sched);
+        if (need > (size_t)CSR_NOALLOC_SCRATCH_BYTES)
+            return set_err(ctx, CSR_ERR_WORKSPACE, "the problem needs " + std::to_string(need) +
+                                                       " bytes of scratch, more than the array's " +
+                                                       std::to_string((size_t)CSR_NOALLOC_SCRATCH_BYTES));
+        p.workspace = ctx->scratch;
+        p.workspace_bytes = CSR_NOALLOC_SCRATCH_BYTES;
+        DeviceGuard g(ctx->device);
+        return run_schedule(ctx, p, *sched, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
 }
 
 int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,

@@ -327,6 +327,30 @@ def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule]
     return out
 
 
+def spmm_noalloc(row_ptr, col_idx, vals, X, *, schedule: CsrSchedule, out=None,
+                 ctx: Optional[Context] = None) -> torch.Tensor:
+    """spmm without a workspace (csr_spmm_noalloc): the kernels' scratch lives
+    in a fixed device array inside the library (CSR_NOALLOC_SCRATCH_BYTES per
+    GPU), so the call allocates nothing but ``out`` when it is not given.  A
+    schedule is required.  Calls overlapping on one GPU share the array and
+    must be ordered by the caller."""
+    if schedule is None:
+        raise ValueError("spmm_noalloc needs an explicit schedule (select() one beforehand)")
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    _on(row_ptr.device, vals=vals, X=X)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [n_cols, F]")
+    if vals is not None:
+        _entries(vals, "vals", nnz)
+    out = _out_rows(out, n_rows, X.shape[1], X.device)
+    p = _spmm_problem(row_ptr, col_idx, vals, X, out)
+    ctx = ctx or default_context(X.device.index)
+    _check(_lib().csr_spmm_noalloc(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b, p.dtype,
+                                   p.width, p.ld_b, p.out, p.ld_out, ctypes.byref(schedule), _stream(X.device)),
+           "csr_spmm_noalloc", ctx)
+    return out
+
+
 def sddmm(row_ptr, col_idx, U, V, *, out=None, schedule: Optional[CsrSchedule] = None,
           ctx: Optional[Context] = None,
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:

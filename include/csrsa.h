@@ -238,6 +238,29 @@ int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
              const void* X, int32_t x_dtype, int64_t F, int64_t ldx, float* Y, int64_t ldy,
              const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
 
+/* Scratch capacity (bytes per GPU) of csr_spmm_noalloc. */
+#define CSR_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* csr_spmm for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, result and errors as csr_spmm with an explicit schedule, but
+ * without a workspace: the kernels' scratch (merge-path coordinates and
+ * split-row pieces) lives in a device array of CSR_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends.  Nothing
+ * is allocated and nothing synchronised (unless the context validates).
+ * sched must not be NULL (select it once beforehand: CSR_ERR_NULL);
+ * problems whose schedule needs more scratch than the array holds
+ * (csr_workspace_size > CSR_NOALLOC_SCRATCH_BYTES) are refused with
+ * CSR_ERR_WORKSPACE before anything is enqueued; CSR_ERR_HIP if the array's
+ * address could not be obtained for the context's device.  Every call on a
+ * GPU uses that GPU's one array, whatever the context or stream: calls whose
+ * kernels overlap in time on one GPU race and must be ordered by the caller
+ * (one stream, or events).  No scratch content has to start at zero. */
+int csr_spmm_noalloc(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                     const int32_t* row_ptr, const int32_t* col_idx, const float* vals,
+                     const void* X, int32_t x_dtype, int64_t F, int64_t ldx, float* Y, int64_t ldy,
+                     const csr_schedule_t* sched, void* stream);
+
 /* SDDMM (AutoSAGE page, Abstract: CSR SDDMM):
  *   out[e] = sum over k < K of U[i, k] * V[col_idx[e], k] for every stored
  *   entry e of row i, in CSR order.
