@@ -40,13 +40,17 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s and GNNZ*F/s per kernel; % of MI355X HBM roofline"
 
 
-def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64):
+def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64, esize=4):
     """Algorithmic bytes of one call (index arrays, values, one gathered row
-    per stored entry, dense row operands, output)."""
+    per stored entry, dense row operands, output); esize = bytes per element
+    of the dense operands (4 fp32, 2 bf16; outputs are fp32)."""
     if op == "spmm":
-        return 4 * (n_rows + 1) + nnz * 8 + nnz * width * 4 + n_rows * width * 4
+        return 4 * (n_rows + 1) + nnz * 8 + nnz * width * esize + n_rows * width * 4
     if op == "sddmm":
-        return 4 * (n_rows + 1) + nnz * 8 + n_rows * width * 4 + nnz * width * 4
+        return 4 * (n_rows + 1) + nnz * 8 + n_rows * width * esize + nnz * width * esize
+    if op == "attention_qk":
+        # Q row per row, K and V rows per stored entry, output row per row
+        return 4 * (n_rows + 1) + nnz * 4 + n_rows * width * esize + 2 * nnz * width * esize + n_rows * width * 4
     if op == "attention":
         return 4 * (n_rows + 1) + nnz * 8 + nnz * width * 4 + n_rows * width * 4
     if op == "row_softmax":
@@ -91,10 +95,10 @@ def compulsory_bytes(c, torch):
 class Call:
     """One library call of the step with its operands and replayed schedule."""
 
-    def __init__(self, name, op, fn, args, kwargs, n_rows, nnz, width, oracle_fn):
+    def __init__(self, name, op, fn, args, kwargs, n_rows, nnz, width, oracle_fn, esize=4):
         self.name, self.op, self.fn, self.args, self.kwargs = name, op, fn, args, kwargs
-        self.n_rows, self.nnz, self.width = n_rows, nnz, width
-        self.bytes = b_alg(op, n_rows, nnz, width)
+        self.n_rows, self.nnz, self.width, self.esize = n_rows, nnz, width, esize
+        self.bytes = b_alg(op, n_rows, nnz, width, esize=esize)
         self.oracle_fn = oracle_fn
         self.schedule = None
         self.times = []
@@ -200,6 +204,33 @@ def build_workload(name, torch, csa):
             out = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
             calls.append(Call(f"sddmm_K{K}", "sddmm", csa.sddmm, (rp, ci, d(U), d(V)), {"out": out}, csr.n_rows,
                               csr.nnz, K, ("sddmm", csr, U, V)))
+    elif name == "c3qk":
+        # single-head fp32 attention on the c3 graph from Q, K, V of width 64
+        # in one pass (scores formed in registers, never written)
+        csr = configs.config_pattern("c3")
+        rp, ci = d(csr.row_ptr), d(csr.col_idx)
+        Q = configs.config_dense("c3", "U", csr, 64)
+        K = configs.config_dense("c3", "V", csr, 64)
+        V = configs.config_dense("c3", "X", csr, 64)
+        Y = torch.empty((csr.n_rows, 64), dtype=torch.float32, device="cuda")
+        calls.append(Call("attention_qk_F64", "attention_qk", csa.attention_qk, (rp, ci, d(Q), d(K), d(V)),
+                          {"out": Y, "scale": 0.125}, csr.n_rows, csr.nnz, 64, ("attention_qk", csr, Q, K, V)))
+    elif name == "c3bf16":
+        # bf16 features on the c3 graph: SpMM F = 128 and SDDMM K = 128, fp32 accumulation
+        from synth import to_bf16_bits
+
+        csr = configs.config_pattern("c3")
+        rp, ci = d(csr.row_ptr), d(csr.col_idx)
+        vals = configs.config_dense("c3", "vals", csr)
+        Xb = to_bf16_bits(configs.config_dense("c3", "X", csr, 128))
+        Y = torch.empty((csr.n_rows, 128), dtype=torch.float32, device="cuda")
+        calls.append(Call("spmm_bf16_F128", "spmm", csa.spmm, (rp, ci, d(vals), b16(Xb)), {"out": Y}, csr.n_rows,
+                          csr.nnz, 128, ("spmm", csr, vals, Xb), esize=2))
+        Ub = to_bf16_bits(configs.config_dense("c3", "U", csr, 128))
+        Vb = to_bf16_bits(configs.config_dense("c3", "V", csr, 128))
+        out = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+        calls.append(Call("sddmm_bf16_K128", "sddmm", csa.sddmm, (rp, ci, b16(Ub), b16(Vb)), {"out": out},
+                          csr.n_rows, csr.nnz, 128, ("sddmm", csr, Ub, Vb), esize=2))
     elif name in ("c3pipe", "c3fused"):
         # single-head fp32 attention on the c3 graph from Q, K, V of width 64:
         # SDDMM -> row softmax -> SpMM as three calls, or SDDMM -> fused
@@ -596,8 +627,12 @@ def cpu_baseline(calls, target_s=8.0, runs=3):
 
     def run(call, r1, th):
         kind, csr, *ops = call.oracle_fn
+        if call.esize == 2:  # bf16 bit patterns, read exactly by the oracle
+            ops = [o if o.dtype != np.uint16 else oracle.bf16_to_f32(o) for o in ops]
         t = time.perf_counter()
-        if kind == "spmm":
+        if kind == "attention_qk":
+            oracle.attention_qk(csr.row_ptr, csr.col_idx, ops[0], ops[1], ops[2], 0.125, 0, r1, th)
+        elif kind == "spmm":
             oracle.spmm(csr.row_ptr, csr.col_idx, ops[0], ops[1], 0, r1, th)
         elif kind == "sddmm":
             oracle.sddmm(csr.row_ptr, csr.col_idx, ops[0], ops[1], 0, r1, th)
@@ -627,7 +662,7 @@ def cpu_baseline(calls, target_s=8.0, runs=3):
         t, b = 0.0, 0.0
         for c in calls:
             t += run(c, r1, threads)
-            b += b_alg(c.op, r1, int(rp[r1]), c.width)
+            b += b_alg(c.op, r1, int(rp[r1]), c.width, esize=c.esize)
         return t, b
 
     # calibrate on ~1% of the entries, then size the row block for target_s
@@ -653,7 +688,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2",
-                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3bwd, c3sweep")
+                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3qk, c3bf16, c3bwd, c3sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds per pass of the CPU oracle sample")
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -783,7 +818,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if calls[0].op == "mha" else "f32",
+        "dtype": "bf16" if calls[0].op == "mha" or calls[0].esize == 2 else "f32",
         "data": "synthetic",
         "config": {"workload": {"c2": "CSR SpMM, power-law graph 232,965 rows ~114.6M nnz, F in {32,64,128,602}",
                                 "c1": "fused CSR attention, 2,048 nodes Poisson(18), F=32",
@@ -796,6 +831,10 @@ def main():
                                           "SDDMM K=64 -> row softmax -> SpMM F=64",
                                 "c3fused": "single-head fp32 attention on the log-normal graph: "
                                            "SDDMM K=64 -> fused softmax-SpMM F=64",
+                                "c3qk": "single-head fp32 attention on the log-normal graph from Q, K, V of "
+                                        "width 64 in one pass (SDDMM -> softmax -> SpMM, scores in registers)",
+                                "c3bf16": "CSR SpMM F=128 + SDDMM K=128 over bf16 features, fp32 accumulation, "
+                                          "log-normal graph 2,449,029 rows ~123.7M nnz",
                                 "c3sweep": "CSR SpMM on the log-normal graph at F in {128,256,384,512}: "
                                            "gathered operand of 1.25 to 5.0 GB",
                                 "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "

@@ -16,6 +16,7 @@ from ._ffi import (  # noqa: F401,E402
     OP_SOFTMAX_BWD,
     CsrError,
     CsrHybrid,
+    CsrPlan,
     CsrProblem,
     CsrSchedule,
     EXPORTS,
@@ -38,6 +39,7 @@ from .ops import (  # noqa: E402,F401
     attention,
     attention_backward,
     attention_pipeline,
+    attention_qk,
     candidates,
     default_context,
     default_schedule,
@@ -54,6 +56,10 @@ from .ops import (  # noqa: E402,F401
     make_problem,
     merge_path_partition,
     mha_attention,
+    Plan,
+    plan,
+    plan_sddmm,
+    plan_spmm,
     row_softmax,
     row_softmax_backward,
     sddmm,

@@ -19,7 +19,7 @@ STATUS = {
 }
 CSR_ERR_NO_CACHE_ENTRY = -8
 
-OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX, OP_SOFTMAX_BWD = 1, 2, 3, 4, 5, 6
+OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX, OP_SOFTMAX_BWD, OP_ATTENTION_QK = 1, 2, 3, 4, 5, 6, 7
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAP_ROWGROUP, MAP_MERGEPATH, MAP_SEGSCAN = 1, 2, 3
 SCHED_WIDE = 1  # schedule flag: 16-byte lanes over 4-byte aligned rows (SpMM, row-group)
@@ -38,6 +38,7 @@ EXPORTS = (
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
     "csr_hybrid_plan", "csr_hybrid_parts", "csr_hybrid_capacity", "csr_hybrid_build_workspace_size", "csr_hybrid_build", "csr_hybrid_workspace_size",
     "csr_hybrid_spmm", "csr_hybrid_sddmm", "csr_hybrid_select",
+    "csr_plan_size", "csr_plan_create", "csr_plan_spmm", "csr_plan_sddmm",
 )
 
 
@@ -96,6 +97,9 @@ class CsrProblem(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("ld_c", ctypes.c_int64),
+        ("probs", ctypes.c_void_p),
+        ("probs_stride", ctypes.c_int64),
     ]
 
 
@@ -125,6 +129,35 @@ class CsrHybrid(ctypes.Structure):
 
 assert ctypes.sizeof(CsrHybrid) == 104
 
+PLAN_VERSION = 1
+
+
+class CsrPlan(ctypes.Structure):
+    """csr_plan_t: a CSR matrix prepared for one SpMM or SDDMM (layout and schedule)."""
+    _fields_ = [
+        ("version", ctypes.c_int32),
+        ("op", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("parts", ctypes.c_int32),
+        ("whole_below", ctypes.c_int32),
+        ("reserved_", ctypes.c_int32),
+        ("n_rows", ctypes.c_int64),
+        ("n_cols", ctypes.c_int64),
+        ("nnz", ctypes.c_int64),
+        ("width", ctypes.c_int64),
+        ("signature", ctypes.c_uint64),
+        ("sched", CsrSchedule),
+        ("fmt", CsrHybrid),
+        ("row_ptr", ctypes.c_void_p),
+        ("col_idx", ctypes.c_void_p),
+        ("vals", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("probe_ms", ctypes.c_double),
+    ]
+
+
+assert ctypes.sizeof(CsrPlan) == 272
+
 
 class CsrError(RuntimeError):
     def __init__(self, code: int, where: str, message: str = ""):
@@ -149,6 +182,7 @@ def load() -> ctypes.CDLL:
     P, I64, I32, U32, F, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
                                ctypes.c_float, ctypes.c_size_t)
     SP, PP, HP = ctypes.POINTER(CsrSchedule), ctypes.POINTER(CsrProblem), ctypes.POINTER(CsrHybrid)
+    PLP = ctypes.POINTER(CsrPlan)
     sig = {
         "csr_context_create": [ctypes.POINTER(P), ctypes.c_int, ctypes.c_char_p, U32],
         "csr_context_destroy": [P],
@@ -157,8 +191,8 @@ def load() -> ctypes.CDLL:
         "csr_spmm": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
         "csr_spmm_noalloc": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P],
         "csr_sddmm": [P, I64, I64, I64, P, P, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
-        "csr_attention": [P, I64, I64, I64, P, P, P, P, I64, I64, F, P, I64, SP, P, SZ, P],
-        "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, SP, P, SZ, P],
+        "csr_attention": [P, I64, I64, I64, P, P, P, P, P, P, I32, I32, I64, I64, F, P, I64, P, SP, P, SZ, P],
+        "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, P, SP, P, SZ, P],
         "csr_row_softmax": [P, I64, I64, P, P, F, P, SP, P, SZ, P],
         "csr_row_softmax_backward": [P, I64, I64, P, P, P, F, P, SP, P, SZ, P],
         "csr_transpose_workspace_size": [P, I64, I64, I64, ctypes.POINTER(SZ)],
@@ -184,6 +218,10 @@ def load() -> ctypes.CDLL:
         "csr_hybrid_spmm": [P, HP, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
         "csr_hybrid_sddmm": [P, HP, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
         "csr_hybrid_select": [P, HP, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
+        "csr_plan_size": [P, PP, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+        "csr_plan_create": [P, PP, U32, P, SZ, PLP],
+        "csr_plan_spmm": [P, PLP, P, P, I64, P, I64, P, SZ, P],
+        "csr_plan_sddmm": [P, PLP, P, I64, P, I64, P, P, SZ, P],
     }
     for name, argtypes in sig.items():
         fn = getattr(lib, name)

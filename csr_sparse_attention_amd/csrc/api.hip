@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <functional>
 #include <map>
 #include <mutex>
 #include <string>
@@ -25,6 +26,12 @@ struct CacheEntry {
     bool persisted;
 };
 
+struct PlanEntry {
+    csrh::PlanChoice choice;
+    double probe_us;
+    bool persisted;
+};
+
 struct csr_context_s {
     std::mutex mu;
     int device = -1;  // -1: host-only context (cache and host logic only)
@@ -32,6 +39,7 @@ struct csr_context_s {
     uint32_t flags = 0;
     std::string cache_path;
     std::map<uint64_t, CacheEntry> cache;
+    std::map<uint64_t, PlanEntry> plans;  // planned products: layout and schedule chosen together
     int64_t skipped_lines = 0;
     int64_t io_errors = 0;
     int64_t* pinned = nullptr;  // 4 KiB pinned host buffer
@@ -140,12 +148,15 @@ void load_cache(csr_context_t ctx)
         if (line.empty() || line[0] == '#') continue;
         uint64_t sig;
         csr_schedule_t s;
+        csrh::PlanChoice c;
         double us;
-        if (!csrh::parse_cache_line(line, &sig, &s, &us)) {
+        if (csrh::parse_cache_line(line, &sig, &s, &us)) {
+            ctx->cache[sig] = CacheEntry{s, us, true};  // a later line for a signature replaces an earlier one
+        } else if (csrh::parse_plan_line(line, &sig, &c, &us)) {
+            ctx->plans[sig] = PlanEntry{c, us, true};
+        } else {
             ++ctx->skipped_lines;
-            continue;
         }
-        ctx->cache[sig] = CacheEntry{s, us, true};  // a later line for a signature replaces an earlier one
     }
 }
 
@@ -158,6 +169,21 @@ int store_entry(csr_context_t ctx, uint64_t sig, const csr_schedule_t& s, double
     }
     if (append_line(ctx->cache_path, csrh::format_cache_line(sig, s, us))) {
         ctx->cache[sig].persisted = true;
+        return CSR_OK;
+    }
+    ++ctx->io_errors;
+    return set_err(ctx, CSR_ERR_CACHE_IO, "cannot append to the cache log " + ctx->cache_path);
+}
+
+int store_plan(csr_context_t ctx, uint64_t sig, const csrh::PlanChoice& c, double us)
+{
+    ctx->plans[sig] = PlanEntry{c, us, false};
+    if (ctx->cache_path.empty()) {
+        ctx->plans[sig].persisted = true;
+        return CSR_OK;
+    }
+    if (append_line(ctx->cache_path, csrh::format_plan_line(sig, c, us))) {
+        ctx->plans[sig].persisted = true;
         return CSR_OK;
     }
     ++ctx->io_errors;
@@ -249,6 +275,7 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         a.carry_row = reinterpret_cast<int32_t*>(ws + L.carry_row);
         a.carry_ml = reinterpret_cast<float*>(ws + L.carry_ml);
         a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
+        a.probs = p.probs;
         const int lph = p.head_dim / 8;
         CSR_HIP(ctx, csrk::launch_mha(s.mapping, lph, s.chunk_items, a, st));
         if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_mha_fixup(lph, a, st));
@@ -270,6 +297,18 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     a.carry_val = reinterpret_cast<float*>(ws + L.carry_val);
     a.stream_y = maps ? maps->stream_y : 0;
     const bool bf = p.dtype == CSR_DTYPE_BF16;
+    if (p.op == CSR_OP_ATTENTION_QK) {
+        a.U = p.a;
+        a.ldu = p.ld_a;
+        a.X = p.b;
+        a.ldx = p.ld_b;
+        a.V = p.c;
+        a.ldv = p.ld_c;
+        a.Y = static_cast<float*>(p.out);
+        a.ldy = p.ld_out;
+        a.probs = p.probs;
+        a.probs_stride = p.probs_stride > 0 ? p.probs_stride : 1;
+    }
     if (p.op == CSR_OP_SDDMM) {
         if (maps) {
             a.u_row = maps->u_row;
@@ -284,11 +323,15 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
                         : csrk::launch_sddmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
         return CSR_OK;
     }
-    a.ev = static_cast<const float*>(p.a);
-    a.X = p.b;
-    a.ldx = p.ld_b;
-    a.Y = static_cast<float*>(p.out);
-    a.ldy = p.ld_out;
+    if (p.op != CSR_OP_ATTENTION_QK) {
+        a.ev = static_cast<const float*>(p.a);
+        a.X = p.b;
+        a.ldx = p.ld_b;
+        a.Y = static_cast<float*>(p.out);
+        a.ldy = p.ld_out;
+        a.probs = p.probs;
+        a.probs_stride = p.probs_stride > 0 ? p.probs_stride : 1;
+    }
     // the fix-up reads fp32 pieces and writes fp32 rows: over bf16 operands it
     // takes the widest fp32 lane layout the width and the output allow
     csrk::Fp32Args fa = a;
@@ -307,6 +350,10 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         CSR_HIP(ctx, bf ? csrk::launch_spmm_bf16(s.mapping, s.vec, s.passes, s.chunk_items, a, st)
                         : csrk::launch_spmm(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
         if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_spmm_fixup(fvec, fnv, fa, st));
+    } else if (p.op == CSR_OP_ATTENTION_QK) {
+        CSR_HIP(ctx, bf ? csrk::launch_attention_qk_bf16(s.mapping, s.vec, s.passes, s.chunk_items, a, st)
+                        : csrk::launch_attention_qk(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_attention_qk_fixup(fvec, fnv, fa, st));
     } else {
         CSR_HIP(ctx, bf ? csrk::launch_attention_bf16(s.mapping, s.vec, s.passes, s.chunk_items, a, st)
                         : csrk::launch_attention(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
@@ -366,6 +413,64 @@ double timed_run(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
 // first candidate (clocks ramp up from idle), then the candidates are timed
 // in interleaved rounds so that slow drifts (clocks, temperature) bias none
 // of them; the number of runs per round adapts to the kernel's duration.
+// One timed run of run() (milliseconds), or a negative value if it failed.
+double timed_fn(csr_context_t ctx, const std::function<int()>& run, hipStream_t st)
+{
+    if (env_flag("CSRSA_FAIL_PROBE")) return -1.0;
+    if (!ctx->ev0) {
+        if (hipEventCreate(&ctx->ev0) != hipSuccess || hipEventCreate(&ctx->ev1) != hipSuccess) return -1.0;
+    }
+    if (hipEventRecord(ctx->ev0, st) != hipSuccess) return -1.0;
+    if (run() != CSR_OK) return -1.0;
+    if (hipEventRecord(ctx->ev1, st) != hipSuccess) return -1.0;
+    if (hipEventSynchronize(ctx->ev1) != hipSuccess) return -1.0;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ctx->ev0, ctx->ev1) != hipSuccess) return -1.0;
+    return ms;
+}
+
+// Micro-probes of n alternatives run(0) .. run(n - 1), as probe_all does for
+// schedules: warm-up on the first, one untimed run each, then interleaved
+// timed rounds; the median per alternative, negative for one that failed.
+std::vector<double> probe_runs(csr_context_t ctx, size_t n, const std::function<int(size_t)>& run, hipStream_t st)
+{
+    std::vector<double> med(n, -1.0);
+    if (n == 0) return med;
+    std::vector<std::vector<double>> t(n);
+    std::vector<bool> failed(n, false);
+    double warm = 0.0, last = -1.0;
+    for (int k = 0; k < 20 && warm < 20.0; ++k) {
+        last = timed_fn(ctx, [&] { return run(0); }, st);
+        if (last < 0) break;
+        warm += last;
+    }
+    const int reps = std::max(1, env_int("CSRSA_PROBE_REPS", 0));
+    const int per_round = env_int("CSRSA_PROBE_REPS", 0) > 0 ? 1
+                          : (last > 0 ? std::max(1, std::min(3, (int)(10.0 / last))) : 1);
+    const int rounds = env_int("CSRSA_PROBE_REPS", 0) > 0 ? reps : 3;
+    for (size_t i = 0; i < n; ++i)
+        if (timed_fn(ctx, [&] { return run(i); }, st) < 0) failed[i] = true;
+    for (int r = 0; r < rounds; ++r) {
+        for (size_t i = 0; i < n; ++i) {
+            if (failed[i]) continue;
+            for (int k = 0; k < per_round; ++k) {
+                const double ms = timed_fn(ctx, [&] { return run(i); }, st);
+                if (ms < 0) {
+                    failed[i] = true;
+                    break;
+                }
+                t[i].push_back(ms);
+            }
+        }
+    }
+    for (size_t i = 0; i < n; ++i) {
+        if (failed[i] || t[i].empty()) continue;
+        std::sort(t[i].begin(), t[i].end());
+        med[i] = t[i][t[i].size() / 2];
+    }
+    return med;
+}
+
 std::vector<double> probe_all(csr_context_t ctx, const csr_problem_t& p, const std::vector<csr_schedule_t>& cand,
                               const std::vector<size_t>& which, hipStream_t st, const RowMaps* maps)
 {
@@ -692,36 +797,141 @@ int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, co
     return op_call(ctx, p, sched);
 }
 
+// The one-head problem of head h: column views of Q, K, V, out and probs.
+static csr_problem_t head_view(const csr_problem_t& p, int32_t h, int64_t head_dim, size_t esize)
+{
+    csr_problem_t q = p;
+    const int64_t off = (int64_t)h * head_dim;
+    q.a = static_cast<const char*>(p.a) + off * esize;
+    q.b = static_cast<const char*>(p.b) + off * esize;
+    q.c = static_cast<const char*>(p.c) + off * esize;
+    q.out = static_cast<float*>(p.out) + off;
+    q.probs = p.probs ? p.probs + h : nullptr;
+    return q;
+}
+
+// Runs the heads of an attention from queries and keys as one-head problems
+// (ctx locked, device current).  One schedule serves every head: given, or
+// selected on the head whose views allow the narrowest lane accesses (the
+// lowest head index among equals), and checked against every head before
+// anything is launched.
+static int attention_heads(csr_context_t ctx, const csr_problem_t& p, int32_t heads, int64_t head_dim, size_t esize,
+                           const csr_schedule_t* sched)
+{
+    std::string why;
+    int h_sel = 0, v_sel = 1 << 30;
+    for (int32_t h = 0; h < heads; ++h) {
+        const csr_problem_t q = head_view(p, h, head_dim, esize);
+        int rc = csrh::check_problem(q, true, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+        const int v = csrh::max_vec(q);
+        if (v < v_sel) {
+            v_sel = v;
+            h_sel = h;
+        }
+    }
+    const csr_problem_t qs = head_view(p, h_sel, head_dim, esize);
+    csr_schedule_t s;
+    if (sched) {
+        s = *sched;
+    } else {
+        int rc = select_locked(ctx, qs, CSR_SELECT_AUTO, &s, nullptr);
+        if (rc != CSR_OK) return rc;
+    }
+    for (int32_t h = 0; h < heads; ++h) {
+        int rc = csrh::check_schedule(head_view(p, h, head_dim, esize), s, &why);
+        if (rc != CSR_OK) return set_err(ctx, rc, why);
+    }
+    int rc = check_workspace(ctx, qs, csrh::workspace_bytes(qs, s));
+    if (rc != CSR_OK) return rc;
+    for (int32_t h = 0; h < heads; ++h) {
+        rc = run_schedule(ctx, head_view(p, h, head_dim, esize), s, static_cast<hipStream_t>(p.stream));
+        if (rc != CSR_OK) return rc;
+    }
+    return CSR_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p % 16) == 0; }
+
 int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
-                  const int32_t* col_idx, const float* edge_scores, const float* node_value, int64_t F, int64_t ldv,
-                  float scale, float* out, int64_t ldo, const csr_schedule_t* sched, void* workspace,
+                  const int32_t* col_idx, const float* edge_scores, const void* Q, const void* K,
+                  const void* node_value, int32_t dtype, int32_t heads, int64_t head_dim, int64_t ldv, float scale,
+                  float* out, int64_t ldo, float* probs_out, const csr_schedule_t* sched, void* workspace,
                   size_t ws_bytes, void* stream)
 {
     csr_problem_t p = blank_problem();
-    p.op = CSR_OP_ATTENTION;
-    p.dtype = CSR_DTYPE_F32;
+    p.dtype = dtype;
     p.n_rows = n_rows;
     p.n_cols = n_cols;
     p.nnz = nnz;
-    p.width = F;
-    p.ld_b = ldv;
-    p.ld_out = ldo;
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
-    p.a = edge_scores;
-    p.b = node_value;
-    p.out = out;
     p.scale = scale;
+    p.out = out;
+    p.probs = probs_out;
     p.workspace = workspace;
     p.workspace_bytes = ws_bytes;
     p.stream = stream;
-    return op_call(ctx, p, sched);
+    if (edge_scores || (!Q && !K)) {
+        // scores given (the trace page's operation): one head; edge_scores may
+        // be NULL only when there are no entries
+        if (heads != 1) {
+            if (!ctx) return CSR_ERR_NULL;
+            std::lock_guard<std::mutex> lk(ctx->mu);
+            return set_err(ctx, CSR_ERR_SHAPE, "given edge scores serve one head");
+        }
+        p.op = CSR_OP_ATTENTION;
+        p.width = head_dim;
+        p.ld_b = ldv;
+        p.ld_out = ldo;
+        p.a = edge_scores;
+        p.b = node_value;
+        p.probs_stride = 1;
+        return op_call(ctx, p, sched);
+    }
+    if (!ctx) return CSR_ERR_NULL;
+    const int64_t width = (int64_t)heads * head_dim;
+    const bool mha = dtype == CSR_DTYPE_BF16 && heads >= 1 && head_dim >= 8 && head_dim <= 512 &&
+                     (head_dim & (head_dim - 1)) == 0 && width <= 512 && ldv == width && ldo == width &&
+                     aligned16(Q) && aligned16(K) && aligned16(node_value) && aligned16(out);
+    if (mha) {
+        // the multi-head kernel: every head of a row in one wavefront
+        p.op = CSR_OP_MHA;
+        p.heads = heads;
+        p.head_dim = (int32_t)head_dim;
+        p.width = width;
+        p.a = Q;
+        p.b = K;
+        p.c = node_value;
+        return op_call(ctx, p, sched);
+    }
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+        if (heads < 1 || head_dim < 1) return set_err(ctx, CSR_ERR_SHAPE, "heads and head_dim must be >= 1");
+        if (!Q || !K || (nnz > 0 && !node_value)) return set_err(ctx, CSR_ERR_NULL, "Q, K or node_value is NULL");
+        if (ldv < width || ldo < width) return set_err(ctx, CSR_ERR_SHAPE, "ldv and ldo must be >= heads * head_dim");
+        p.op = CSR_OP_ATTENTION_QK;
+        p.width = head_dim;
+        p.ld_a = p.ld_b = width;
+        p.ld_c = ldv;
+        p.ld_out = ldo;
+        p.a = Q;
+        p.b = K;
+        p.c = node_value;
+        p.probs_stride = heads;
+        DeviceGuard g(ctx->device);
+        return attention_heads(ctx, p, heads, head_dim, dtype == CSR_DTYPE_BF16 ? 2 : 4, sched);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
 }
 
 int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
                       const int32_t* col_idx, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                      int32_t heads, int32_t head_dim, float scale, float* out, const csr_schedule_t* sched,
-                      void* workspace, size_t ws_bytes, void* stream)
+                      int32_t heads, int32_t head_dim, float scale, float* out, float* probs_out,
+                      const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
 {
     csr_problem_t p = blank_problem();
     p.op = CSR_OP_MHA;
@@ -738,6 +948,7 @@ int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t
     p.b = K;
     p.c = V;
     p.out = out;
+    p.probs = probs_out;
     p.scale = scale;
     p.workspace = workspace;
     p.workspace_bytes = ws_bytes;
@@ -897,15 +1108,47 @@ static int check_hybrid(csr_context_t ctx, const csr_hybrid_t* h, bool built)
     if (h->whole_below < 0 || h->reserved_ != 0) return set_err(ctx, CSR_ERR_SHAPE, "whole_below < 0 or reserved != 0");
     int64_t cap = 0;
     (void)csr_hybrid_capacity(h->n_rows, h->nnz, h->parts, &cap);
-    if (h->seg_cap < cap) return set_err(ctx, CSR_ERR_WORKSPACE, "segment capacity below min(nnz, n_rows * parts)");
+    // a build needs room for the worst case; a built format for its own segments
+    if (!built && h->seg_cap < cap)
+        return set_err(ctx, CSR_ERR_WORKSPACE, "segment capacity below min(nnz, n_rows * parts)");
     if (!h->seg_ptr || !h->row_seg_ptr) return set_err(ctx, CSR_ERR_NULL, "seg_ptr / row_seg_ptr is NULL");
     if (h->nnz > 0 && (!h->perm || !h->col_idx || !h->seg_row || !h->row_seg))
         return set_err(ctx, CSR_ERR_NULL, "a format array is NULL");
     if (built) {
         const int64_t pc = h->n_cols > 0 ? (h->n_cols + h->parts - 1) / h->parts : 1;
-        if (h->part_cols != pc || h->n_seg < 0 || h->n_seg > cap || (h->nnz > 0) != (h->n_seg > 0))
+        if (h->part_cols != pc || h->n_seg < 0 || h->n_seg > cap || h->n_seg > h->seg_cap ||
+            (h->nnz > 0) != (h->n_seg > 0))
             return set_err(ctx, CSR_ERR_SHAPE, "the format is not built (part_cols / n_seg)");
     }
+    return CSR_OK;
+}
+
+// Builds the format of (row_ptr, col_idx) into h's arrays (ctx locked, device
+// current).  h->seg_cap need only hold the segments this input has: the
+// count is read back after the sort and checked before any segment array is
+// written.  Synchronous.
+static int build_format(csr_context_t ctx, const int32_t* row_ptr, const int32_t* col_idx, csr_hybrid_t* h,
+                        void* workspace, size_t ws_bytes, hipStream_t st)
+{
+    size_t need = 0;
+    CSR_HIP(ctx, csrk::hybrid_build_workspace(h->n_rows, h->nnz, h->parts, &need));
+    if (ws_bytes < need || !workspace || (uintptr_t)workspace % csrh::kAlign)
+        return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small (or not 256-byte aligned) for the build");
+    const int32_t part_cols = h->n_cols > 0 ? (int32_t)((h->n_cols + h->parts - 1) / h->parts) : 1;
+    int64_t n_seg = 0;
+    if (h->nnz > 0) {
+        int32_t* count = reinterpret_cast<int32_t*>(ctx->pinned);
+        CSR_HIP(ctx, csrk::launch_hybrid_build_sort(row_ptr, col_idx, h->n_rows, h->nnz, h->parts, part_cols,
+                                                    h->whole_below, h->perm, h->col_idx, workspace, ws_bytes, count,
+                                                    st));
+        CSR_HIP(ctx, hipStreamSynchronize(st));
+        n_seg = count[0];
+        if (n_seg < 1 || n_seg > h->seg_cap) return set_err(ctx, CSR_ERR_INTERNAL, "segment count out of range");
+    }
+    CSR_HIP(ctx, csrk::launch_hybrid_build_segments(h->n_rows, h->nnz, h->parts, n_seg, h->seg_ptr, h->seg_row,
+                                                    h->row_seg_ptr, h->row_seg, workspace, st));
+    h->n_seg = n_seg;
+    h->part_cols = part_cols;
     return CSR_OK;
 }
 
@@ -926,7 +1169,6 @@ int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* c
         if (ws_bytes < need || (uintptr_t)workspace % csrh::kAlign)
             return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small (or not 256-byte aligned) for the build");
         hipStream_t st = static_cast<hipStream_t>(stream);
-        const int32_t part_cols = h->n_cols > 0 ? (int32_t)((h->n_cols + h->parts - 1) / h->parts) : 1;
         if ((ctx->flags & CSR_CTX_VALIDATE) && h->nnz > 0) {
             int64_t* bad = reinterpret_cast<int64_t*>(workspace);
             CSR_HIP(ctx, csrk::launch_validate(row_ptr, col_idx, h->n_rows, h->n_cols, h->nnz, bad, st));
@@ -934,21 +1176,7 @@ int csr_hybrid_build(csr_context_t ctx, const int32_t* row_ptr, const int32_t* c
             CSR_HIP(ctx, hipStreamSynchronize(st));
             if (ctx->pinned[0] != 0) return set_err(ctx, CSR_ERR_INVALID_CSR, "row_ptr / col_idx fail CSR validation");
         }
-        int64_t n_seg = 0;
-        if (h->nnz > 0) {
-            int32_t* count = reinterpret_cast<int32_t*>(ctx->pinned);
-            CSR_HIP(ctx, csrk::launch_hybrid_build_sort(row_ptr, col_idx, h->n_rows, h->nnz, h->parts, part_cols,
-                                                        h->whole_below, h->perm, h->col_idx, workspace, ws_bytes,
-                                                        count, st));
-            CSR_HIP(ctx, hipStreamSynchronize(st));
-            n_seg = count[0];
-            if (n_seg < 1 || n_seg > h->seg_cap) return set_err(ctx, CSR_ERR_INTERNAL, "segment count out of range");
-        }
-        CSR_HIP(ctx, csrk::launch_hybrid_build_segments(h->n_rows, h->nnz, h->parts, n_seg, h->seg_ptr, h->seg_row,
-                                                        h->row_seg_ptr, h->row_seg, workspace, st));
-        h->n_seg = n_seg;
-        h->part_cols = part_cols;
-        return CSR_OK;
+        return build_format(ctx, row_ptr, col_idx, h, workspace, ws_bytes, st);
     } catch (...) {
         return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
     }
@@ -1149,6 +1377,480 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
     }
 }
 
+// ---------------------------------------------------------------------------
+// Planned products
+// ---------------------------------------------------------------------------
+
+static size_t up256(size_t v) { return (v + csrh::kAlign - 1) / csrh::kAlign * csrh::kAlign; }
+
+// Plan memory of a format with room for cap segments: perm, col_idx, seg_ptr,
+// seg_row, row_seg_ptr, row_seg, then (SpMM) the values in format order.
+struct PlanLayout {
+    size_t perm, col, seg_ptr, seg_row, row_seg_ptr, row_seg, vals, total;
+};
+
+static PlanLayout plan_layout(const csr_problem_t& p, int64_t cap)
+{
+    PlanLayout L{};
+    L.perm = 0;
+    L.col = L.perm + up256((size_t)p.nnz * 4);
+    L.seg_ptr = L.col + up256((size_t)p.nnz * 4);
+    L.seg_row = L.seg_ptr + up256((size_t)(cap + 1) * 4);
+    L.row_seg_ptr = L.seg_row + up256((size_t)cap * 4);
+    L.row_seg = L.row_seg_ptr + up256((size_t)(p.n_rows + 1) * 4);
+    L.vals = L.row_seg + up256((size_t)cap * 4);
+    L.total = L.vals + (p.op == CSR_OP_SPMM ? up256((size_t)p.nnz * 4) : 0);
+    return L;
+}
+
+// The format description of (P, T) with its arrays in plan memory.
+static csr_hybrid_t plan_format(const csr_problem_t& p, int P, int T, int64_t cap, void* mem, float** vals)
+{
+    const PlanLayout L = plan_layout(p, cap);
+    char* m = static_cast<char*>(mem);
+    csr_hybrid_t h;
+    std::memset(&h, 0, sizeof h);
+    h.n_rows = p.n_rows;
+    h.n_cols = p.n_cols;
+    h.nnz = p.nnz;
+    h.parts = P;
+    h.whole_below = T;
+    h.seg_cap = cap;
+    h.perm = reinterpret_cast<int32_t*>(m + L.perm);
+    h.col_idx = reinterpret_cast<int32_t*>(m + L.col);
+    h.seg_ptr = reinterpret_cast<int32_t*>(m + L.seg_ptr);
+    h.seg_row = reinterpret_cast<int32_t*>(m + L.seg_row);
+    h.row_seg_ptr = reinterpret_cast<int32_t*>(m + L.row_seg_ptr);
+    h.row_seg = reinterpret_cast<int32_t*>(m + L.row_seg);
+    if (vals) *vals = p.op == CSR_OP_SPMM ? reinterpret_cast<float*>(m + L.vals) : nullptr;
+    return h;
+}
+
+// Plan memory and workspace for every layout a plan of p may probe.
+static void plan_sizes(const csr_problem_t& p, const int64_t* hist, size_t* plan_bytes, size_t* ws_bytes)
+{
+    size_t mem = csrh::kAlign, ws = up256(auto_workspace(p));
+    for (const auto& f : csrh::plan_formats(p, hist)) {
+        const int64_t cap = csrh::segment_bound(p, hist, f.first, f.second);
+        mem = std::max(mem, plan_layout(p, cap).total);
+        size_t build = 0;
+        (void)csrk::hybrid_build_workspace(p.n_rows, p.nnz, f.first, &build);
+        csr_problem_t q = p;  // the product on at most cap segments
+        q.n_rows = cap;
+        q.row_ptr = nullptr;
+        q.ld_out = p.width;
+        if (p.op == CSR_OP_SPMM) q.out = reinterpret_cast<void*>(csrh::kAlign);  // partial rows, 256-byte aligned
+        const size_t inner = up256(auto_workspace(q)) + (p.op == CSR_OP_SPMM ? (size_t)cap * p.width * 4 : 0);
+        ws = std::max(ws, std::max(up256(build), inner));
+    }
+    *plan_bytes = mem;
+    *ws_bytes = ws;
+}
+
+static int check_plan_problem(csr_context_t ctx, const csr_problem_t& p, bool need_ptrs)
+{
+    if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "plans serve SpMM and SDDMM");
+    std::string why;
+    int rc = csrh::check_problem(p, need_ptrs, &why);
+    if (rc != CSR_OK) return set_err(ctx, rc, why);
+    if (!p.row_ptr) return set_err(ctx, CSR_ERR_NULL, "row_ptr is NULL");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    return CSR_OK;
+}
+
+int csr_plan_size(csr_context_t ctx, const csr_problem_t* p, size_t* plan_bytes, size_t* workspace_bytes)
+{
+    if (!ctx || !p || !plan_bytes || !workspace_bytes) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        int rc = check_plan_problem(ctx, *p, false);
+        if (rc != CSR_OK) return rc;
+        rc = check_workspace(ctx, *p, csrh::kHeadBytes);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        int64_t hist[csrh::kHistInts];
+        rc = histogram(ctx, *p, static_cast<hipStream_t>(p->stream), hist);
+        if (rc != CSR_OK) return rc;
+        plan_sizes(*p, hist, plan_bytes, workspace_bytes);
+        return CSR_OK;
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+namespace {
+
+// A plan under construction: the problem, its histogram and the format last
+// built into the plan memory.
+struct PlanBuild {
+    csr_context_t ctx;
+    const csr_problem_t& p;
+    const int64_t* hist;
+    void* mem;
+    hipStream_t st;
+    int built_P = 0, built_T = -1;
+    csr_hybrid_t h{};
+    float* hv = nullptr;  // SpMM: the plan's values in format order
+
+    PlanBuild(csr_context_t c, const csr_problem_t& pr, const int64_t* hi, void* m)
+        : ctx(c), p(pr), hist(hi), mem(m), st(static_cast<hipStream_t>(pr.stream))
+    {
+    }
+
+    // builds the format (P, T) into the plan memory (kept if already there)
+    // and moves the values into its order (ones when p has none)
+    int build(int P, int T)
+    {
+        if (P == built_P && T == built_T) return CSR_OK;
+        built_P = 0;
+        h = plan_format(p, P, T, csrh::segment_bound(p, hist, P, T), mem, &hv);
+        int rc = build_format(ctx, p.row_ptr, p.col_idx, &h, p.workspace, p.workspace_bytes, st);
+        if (rc != CSR_OK) return rc;
+        if (hv) {
+            if (p.a)
+                CSR_HIP(ctx, csrk::launch_gather_values(h.perm, static_cast<const float*>(p.a), hv, p.nnz, st));
+            else
+                CSR_HIP(ctx, csrk::launch_fill_f32(hv, p.nnz, 1.f, st));
+        }
+        built_P = P;
+        built_T = T;
+        return CSR_OK;
+    }
+
+    // the call over the built format with p's operands
+    int call(HybridCall* c, const csr_schedule_t* sched)
+    {
+        const void* a = p.op == CSR_OP_SPMM ? static_cast<const void*>(hv) : p.a;
+        return hybrid_call(ctx, &h, p.op, p.width, p.dtype, a, p.ld_a, p.b, p.ld_b, sched, p.workspace,
+                           p.workspace_bytes, p.stream, static_cast<float*>(p.out), c);
+    }
+
+    int run(const HybridCall& c, const csr_schedule_t& s)
+    {
+        return hybrid_run(ctx, &h, c, &s, static_cast<float*>(p.out), p.ld_out);
+    }
+};
+
+struct PlanOption {
+    int P, T;
+    csr_schedule_t s;
+    double ms;
+};
+
+// The cost model's choice: the format's plan (or the plain pattern), with the
+// estimated best schedule of the product.
+int estimate_plan(PlanBuild& b, csrh::PlanChoice* out)
+{
+    int P = 1, T = 0;
+    csrh::hybrid_plan(b.p, b.hist, &P, &T);
+    out->parts = 1;
+    out->whole_below = 0;
+    auto best_of = [&](const csr_problem_t& q, const int64_t* hq) {
+        const std::vector<csr_schedule_t> cand = csrh::candidates(q, hq);
+        size_t bi = 0;
+        double bt = 0;
+        for (size_t i = 0; i < cand.size(); ++i) {
+            const double t = csrh::estimate(q, cand[i], hq, b.ctx->dev);
+            if (i == 0 || t < bt) {
+                bt = t;
+                bi = i;
+            }
+        }
+        return cand[bi];
+    };
+    if (P > 1 && b.build(P, T) == CSR_OK) {
+        HybridCall c;
+        if (b.call(&c, nullptr) == CSR_OK) {
+            int64_t hs[csrh::kHistInts];
+            if (histogram(b.ctx, c.p, b.st, hs) == CSR_OK) {
+                out->parts = P;
+                out->whole_below = T;
+                out->sched = best_of(c.p, hs);
+                return CSR_OK;
+            }
+        }
+    }
+    b.ctx->last_error.clear();
+    out->sched = best_of(b.p, b.hist);
+    return CSR_OK;
+}
+
+// Micro-probes the plain pattern's best schedules and, for each candidate
+// format, its product's best schedules (the whole call: segment product and
+// the sum of the partial rows); returns the fastest option (within 1 %, the
+// earlier one: plain first, then the formats in order) and its median time.
+int probe_plan(PlanBuild& b, csrh::PlanChoice* out, double* ms)
+{
+    const int max_probe = std::max(1, env_int("CSRSA_PROBE_CANDIDATES", 6));
+    auto top = [&](const csr_problem_t& q, const int64_t* hq, int k) {
+        const std::vector<csr_schedule_t> cand = csrh::candidates(q, hq);
+        std::vector<std::pair<double, size_t>> order;
+        for (size_t i = 0; i < cand.size(); ++i) order.push_back({csrh::estimate(q, cand[i], hq, b.ctx->dev), i});
+        std::stable_sort(order.begin(), order.end(),
+                         [](const std::pair<double, size_t>& x, const std::pair<double, size_t>& y) { return x.first < y.first; });
+        std::vector<size_t> which;
+        for (size_t i = 0; i < order.size() && (int)which.size() < k; ++i) which.push_back(order[i].second);
+        std::sort(which.begin(), which.end());  // fixed candidate order for the ties
+        std::vector<csr_schedule_t> r;
+        for (size_t i : which) r.push_back(cand[i]);
+        return r;
+    };
+    std::vector<PlanOption> opts;
+    {
+        const std::vector<csr_schedule_t> cand = top(b.p, b.hist, max_probe);
+        const std::vector<double> t =
+            probe_runs(b.ctx, cand.size(), [&](size_t i) { return run_schedule(b.ctx, b.p, cand[i], b.st); }, b.st);
+        for (size_t i = 0; i < cand.size(); ++i) opts.push_back({1, 0, cand[i], t[i]});
+    }
+    for (const auto& f : csrh::plan_formats(b.p, b.hist)) {
+        if (b.build(f.first, f.second) != CSR_OK) continue;  // a format that cannot be built is not a candidate
+        HybridCall c;
+        if (b.call(&c, nullptr) != CSR_OK) continue;
+        int64_t hs[csrh::kHistInts];
+        if (histogram(b.ctx, c.p, b.st, hs) != CSR_OK) continue;
+        const std::vector<csr_schedule_t> cand = top(c.p, hs, std::max(1, max_probe / 2));
+        const std::vector<double> t = probe_runs(b.ctx, cand.size(), [&](size_t i) { return b.run(c, cand[i]); }, b.st);
+        for (size_t i = 0; i < cand.size(); ++i) opts.push_back({f.first, f.second, cand[i], t[i]});
+    }
+    b.ctx->last_error.clear();
+    (void)hipGetLastError();
+    double best = -1.0;
+    size_t bi = 0;
+    for (size_t i = 0; i < opts.size(); ++i) {
+        if (opts[i].ms < 0) continue;  // guardrail: a failing option is never chosen
+        if (best < 0 || opts[i].ms < best * 0.99) {
+            best = opts[i].ms;
+            bi = i;
+        }
+    }
+    if (best < 0) {  // every probe failed: the plain pattern, default schedule
+        out->parts = 1;
+        out->whole_below = 0;
+        out->sched = csrh::default_schedule(b.p);
+        *ms = 0.0;
+        return CSR_OK;
+    }
+    out->parts = opts[bi].P;
+    out->whole_below = opts[bi].T;
+    out->sched = opts[bi].s;
+    *ms = best;
+    return CSR_OK;
+}
+
+// Fills *plan for choice c (building its format when it has one).
+int materialize_plan(PlanBuild& b, const csrh::PlanChoice& c, uint64_t sig, double ms, csr_plan_t* plan)
+{
+    std::string why;
+    csr_plan_t r;
+    std::memset(&r, 0, sizeof r);
+    r.version = CSR_PLAN_VERSION;
+    r.op = b.p.op;
+    r.dtype = b.p.dtype;
+    r.parts = c.parts;
+    r.whole_below = c.whole_below;
+    r.n_rows = b.p.n_rows;
+    r.n_cols = b.p.n_cols;
+    r.nnz = b.p.nnz;
+    r.width = b.p.width;
+    r.signature = sig;
+    r.sched = c.sched;
+    r.row_ptr = b.p.row_ptr;
+    r.col_idx = b.p.col_idx;
+    r.probe_ms = ms;
+    if (c.parts == 1) {
+        int rc = csrh::check_schedule(b.p, c.sched, &why);
+        if (rc != CSR_OK) return set_err(b.ctx, rc, why);
+        r.vals = b.p.op == CSR_OP_SPMM ? const_cast<float*>(static_cast<const float*>(b.p.a)) : nullptr;
+        r.workspace_bytes = up256(csrh::workspace_bytes(b.p, c.sched));
+    } else {
+        int rc = b.build(c.parts, c.whole_below);
+        if (rc != CSR_OK) return rc;
+        HybridCall hc;
+        rc = b.call(&hc, &c.sched);
+        if (rc != CSR_OK) return rc;
+        r.fmt = b.h;
+        r.vals = b.hv;
+        size_t inner = 0;
+        rc = hybrid_inner_bytes(b.ctx, hc.p, &c.sched, &inner);
+        if (rc != CSR_OK) return rc;
+        r.workspace_bytes = inner + (b.p.op == CSR_OP_SPMM ? (size_t)b.h.n_seg * b.p.width * 4 : 0);
+    }
+    *plan = r;
+    return CSR_OK;
+}
+
+int check_plan(csr_context_t ctx, const csr_plan_t* plan, int op)
+{
+    if (!plan) return CSR_ERR_NULL;
+    if (plan->version != CSR_PLAN_VERSION || plan->op != op)
+        return set_err(ctx, CSR_ERR_SHAPE, "not a plan of this operation and library version");
+    if (plan->parts != 1 && plan->fmt.parts != plan->parts)
+        return set_err(ctx, CSR_ERR_SHAPE, "the plan's format does not match its parts");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    return CSR_OK;
+}
+
+}  // namespace
+
+int csr_plan_create(csr_context_t ctx, const csr_problem_t* pp, uint32_t mode, void* plan_mem, size_t plan_bytes,
+                    csr_plan_t* plan)
+{
+    if (!ctx || !pp || !plan) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        if (mode > CSR_SELECT_ESTIMATE) return set_err(ctx, CSR_ERR_SHAPE, "unknown selection mode");
+        const csr_problem_t& p = *pp;
+        int rc = check_plan_problem(ctx, p, true);
+        if (rc != CSR_OK) return rc;
+        rc = check_workspace(ctx, p, csrh::kHeadBytes);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        hipStream_t st = static_cast<hipStream_t>(p.stream);
+        int64_t hist[csrh::kHistInts];
+        rc = histogram(ctx, p, st, hist);
+        if (rc != CSR_OK) return rc;
+        size_t need_mem = 0, need_ws = 0;
+        plan_sizes(p, hist, &need_mem, &need_ws);
+        if (!plan_mem || plan_bytes < need_mem || (uintptr_t)plan_mem % csrh::kAlign)
+            return set_err(ctx, CSR_ERR_WORKSPACE, "plan memory NULL, unaligned or below " + std::to_string(need_mem) +
+                                                       " bytes");
+        rc = check_workspace(ctx, p, need_ws);
+        if (rc != CSR_OK) return rc;
+        const uint64_t sig = csrh::plan_signature(p, hist, ctx->dev);
+        PlanBuild b(ctx, p, hist, plan_mem);
+        csrh::PlanChoice c;
+        double ms = 0.0;
+        bool have = false;
+        if (mode == CSR_SELECT_AUTO || mode == CSR_SELECT_REPLAY_ONLY) {
+            auto it = ctx->plans.find(sig);
+            if (it != ctx->plans.end()) {
+                c = it->second.choice;
+                have = true;
+            } else if (mode == CSR_SELECT_REPLAY_ONLY) {
+                return set_err(ctx, CSR_ERR_NO_CACHE_ENTRY, "no cached plan for this input");
+            }
+        }
+        if (!have) {
+            if (mode == CSR_SELECT_ESTIMATE || (ctx->flags & CSR_CTX_NO_PROBE)) {
+                rc = estimate_plan(b, &c);
+                if (rc != CSR_OK) return rc;
+                if (mode != CSR_SELECT_ESTIMATE) (void)store_plan(ctx, sig, c, 0.0);
+            } else {
+                rc = probe_plan(b, &c, &ms);
+                if (rc != CSR_OK) return rc;
+                (void)store_plan(ctx, sig, c, ms * 1000.0);  // a log write failure keeps the entry in memory
+            }
+        }
+        rc = materialize_plan(b, c, sig, ms, plan);
+        if (rc == CSR_OK) ctx->last_error.clear();
+        return rc;
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_plan_spmm(csr_context_t ctx, const csr_plan_t* plan, const float* vals, const void* X, int64_t ldx, float* Y,
+                  int64_t ldy, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx || !plan || !X || !Y) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        int rc = check_plan(ctx, plan, CSR_OP_SPMM);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        std::string why;
+        if (plan->parts == 1) {
+            csr_problem_t p = blank_problem();
+            p.op = CSR_OP_SPMM;
+            p.dtype = plan->dtype;
+            p.n_rows = plan->n_rows;
+            p.n_cols = plan->n_cols;
+            p.nnz = plan->nnz;
+            p.width = plan->width;
+            p.ld_b = ldx;
+            p.ld_out = ldy;
+            p.row_ptr = plan->row_ptr;
+            p.col_idx = plan->col_idx;
+            p.a = vals ? vals : plan->vals;
+            p.b = X;
+            p.out = Y;
+            p.workspace = workspace;
+            p.workspace_bytes = ws_bytes;
+            p.stream = stream;
+            rc = csrh::check_problem(p, true, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            rc = csrh::check_schedule(p, plan->sched, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            rc = check_workspace(ctx, p, csrh::workspace_bytes(p, plan->sched));
+            if (rc != CSR_OK) return rc;
+            return run_schedule(ctx, p, plan->sched, st);
+        }
+        if (plan->width < 1 || ldy < plan->width || ldy >= ((int64_t)1 << 30))
+            return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
+        if (!plan->vals) return set_err(ctx, CSR_ERR_NULL, "the plan has no value array");
+        if (vals) CSR_HIP(ctx, csrk::launch_gather_values(plan->fmt.perm, vals, plan->vals, plan->nnz, st));
+        HybridCall c;
+        rc = hybrid_call(ctx, &plan->fmt, CSR_OP_SPMM, plan->width, plan->dtype, plan->vals, 0, X, ldx, &plan->sched,
+                         workspace, ws_bytes, stream, nullptr, &c);
+        if (rc != CSR_OK) return rc;
+        return hybrid_run(ctx, &plan->fmt, c, &plan->sched, Y, ldy);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_plan_sddmm(csr_context_t ctx, const csr_plan_t* plan, const void* U, int64_t ldu, const void* V, int64_t ldv,
+                   float* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx || !plan) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        int rc = check_plan(ctx, plan, CSR_OP_SDDMM);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        std::string why;
+        if (plan->parts == 1) {
+            csr_problem_t p = blank_problem();
+            p.op = CSR_OP_SDDMM;
+            p.dtype = plan->dtype;
+            p.n_rows = plan->n_rows;
+            p.n_cols = plan->n_cols;
+            p.nnz = plan->nnz;
+            p.width = plan->width;
+            p.ld_a = ldu;
+            p.ld_b = ldv;
+            p.row_ptr = plan->row_ptr;
+            p.col_idx = plan->col_idx;
+            p.a = U;
+            p.b = V;
+            p.out = out;
+            p.workspace = workspace;
+            p.workspace_bytes = ws_bytes;
+            p.stream = stream;
+            rc = csrh::check_problem(p, true, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            rc = csrh::check_schedule(p, plan->sched, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            rc = check_workspace(ctx, p, csrh::workspace_bytes(p, plan->sched));
+            if (rc != CSR_OK) return rc;
+            return run_schedule(ctx, p, plan->sched, st);
+        }
+        HybridCall c;
+        rc = hybrid_call(ctx, &plan->fmt, CSR_OP_SDDMM, plan->width, plan->dtype, U, ldu, V, ldv, &plan->sched,
+                         workspace, ws_bytes, stream, out, &c);
+        if (rc != CSR_OK) return rc;
+        return hybrid_run(ctx, &plan->fmt, c, &plan->sched, nullptr, 0);
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
 int csr_select(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, csr_schedule_t* out, uint64_t* signature)
 {
     if (!ctx || !p || !out) return CSR_ERR_NULL;
@@ -1238,6 +1940,13 @@ int csr_cache_flush(csr_context_t ctx)
         else
             rc = CSR_ERR_CACHE_IO;
     }
+    for (auto& kv : ctx->plans) {
+        if (kv.second.persisted) continue;
+        if (append_line(ctx->cache_path, csrh::format_plan_line(kv.first, kv.second.choice, kv.second.probe_us)))
+            kv.second.persisted = true;
+        else
+            rc = CSR_ERR_CACHE_IO;
+    }
     return rc;
 }
 
@@ -1245,7 +1954,7 @@ int csr_cache_info(csr_context_t ctx, int64_t* entries, int64_t* skipped_lines, 
 {
     if (!ctx) return CSR_ERR_NULL;
     std::lock_guard<std::mutex> lk(ctx->mu);
-    if (entries) *entries = (int64_t)ctx->cache.size();
+    if (entries) *entries = (int64_t)(ctx->cache.size() + ctx->plans.size());
     if (skipped_lines) *skipped_lines = ctx->skipped_lines;
     if (io_errors) *io_errors = ctx->io_errors;
     return CSR_OK;
@@ -1265,7 +1974,7 @@ int csr_cache_store(csr_context_t ctx, uint64_t signature, const csr_schedule_t*
 {
     if (!ctx || !sched) return CSR_ERR_NULL;
     std::lock_guard<std::mutex> lk(ctx->mu);
-    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_SOFTMAX_BWD)
+    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_ATTENTION_QK)
         return set_err(ctx, CSR_ERR_SCHEDULE, "not a schedule of this library version");
     return store_entry(ctx, signature, *sched, 0.0);
 }

@@ -31,6 +31,13 @@ struct Fp32Args {
     const int32_t* u_row;
     const int32_t* out_idx;
     int32_t stream_y;  // SpMM output rows by non-temporal stores (partial rows of the format)
+    // attention from queries and keys: U = Q (ldu), X = K (ldx), V = values (ldv)
+    const void* V;
+    int64_t ldv;
+    // attention: the probabilities of the entries (null = not wanted), entry e
+    // at probs[e * probs_stride]
+    float* probs;
+    int64_t probs_stride;
 };
 
 struct MhaArgs {
@@ -48,6 +55,7 @@ struct MhaArgs {
     int32_t* carry_row;  // [2 n_chunks]
     float* carry_ml;     // [2 n_chunks][H][2]
     float* carry_val;    // [2 n_chunks][H * Dh]
+    float* probs;        // [nnz][H] probabilities of the entries per head, or null
 };
 
 struct SoftmaxArgs {

@@ -30,7 +30,10 @@
 
 namespace csrk {
 
-enum class Op { Spmm, Attention, Sddmm };
+// AttnQK: attention from queries and keys, SDDMM -> row-softmax -> SpMM in one
+// pass (U = Q, X = K, V = values): each score is formed on the fly and folded
+// into an online softmax.
+enum class Op { Spmm, Attention, Sddmm, AttnQK };
 
 
 template <int VEC, int NV>
@@ -205,6 +208,120 @@ __device__ __forceinline__ void seg_softmax_stats(const float* ev, int kb, int k
     }
 }
 
+// Attention from queries and keys: walks entries e = kb, kb + step, ... < ke
+// of one row.  Per batch of U entries the group gathers the K and V rows,
+// forms each score t = scale * <q, K[col_e]> (partial products summed over
+// the group's W lanes), and folds the batch into the running maximum m, sum
+// of exponentials l and weighted sum acc, rescaling them only by the batch's
+// new maximum.  With probs, lane 0 of the group stores each entry's t; it is
+// turned into the probability once the row's statistics are final.
+template <typename T, int VEC, int NV, int U>
+__device__ __forceinline__ void qk_walk(const float (&q)[NV][VEC], const int32_t* col, int kb, int ke, int step,
+                                        const T* K, int64_t ldk, const T* Vv, int64_t ldv,
+                                        const Lanes<VEC, NV>& L, int F, float scale, float& m, float& l,
+                                        float (&acc)[NV][VEC], float* probs, int64_t pstride)
+{
+    for (int k = kb; k < ke; k += step * U) {
+        float kv[U][NV][VEC], vv[U][NV][VEC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = k + u * step;
+            const bool ok = e < ke;
+            const int c = ok ? col[e] : 0;
+            const T* kr = K + (int64_t)c * ldk;
+            const T* vr = Vv + (int64_t)c * ldv;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (ok && L.valid(j, F)) {
+                    vload_t<T, VEC>(kv[u][j], kr + L.off(j));
+                    vload_t<T, VEC>(vv[u][j], vr + L.off(j));
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) kv[u][j][v] = vv[u][j][v] = 0.f;
+                }
+            }
+        }
+        float t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float d = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) d = fmaf(q[j][v], kv[u][j][v], d);
+            t[u] = d;
+        }
+        group_sum_lanes(t, L.W);
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            t[u] = (k + u * step < ke) ? t[u] * scale : -INFINITY;
+            mn = fmaxf(mn, t[u]);
+        }
+        if (probs && L.lg == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = k + u * step;
+                if (e < ke) probs[(int64_t)e * pstride] = t[u];
+            }
+        }
+        const float corr = (l > 0.f) ? exp_neg(m - mn) : 0.f;
+        l *= corr;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[j][v] *= corr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = (k + u * step < ke) ? exp_neg(t[u] - mn) : 0.f;
+            l += w;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[j][v] = fmaf(w, vv[u][j][v], acc[j][v]);
+        }
+        m = mn;
+    }
+}
+
+// Merges the online-softmax states of a row whose entries the wave's groups
+// took in turn (each group of W lanes holds its own m, l, acc): every lane
+// ends with the row's maximum, sum and accumulated row.
+template <int VEC, int NV>
+__device__ __forceinline__ void qk_merge_groups(float& m, float& l, float (&acc)[NV][VEC], int W)
+{
+    float M = m;
+    for (int s = W; s < CSR_WAVE; s <<= 1) M = fmaxf(M, shfl_xor(M, s));
+    const float f = (l > 0.f) ? exp_neg(m - M) : 0.f;
+    l = xor_sum_from(l * f, W);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[j][v] = xor_sum_from(acc[j][v] * f, W);
+    m = M;
+}
+
+// The probabilities of entries e = kb + t0, kb + t0 + n, ... < ke of a row
+// whose scores t_e this wave stored in probs: exp(t_e - m) / l.  The fence
+// orders the wave's stores of the scores before the lanes read them back.
+__device__ __forceinline__ void probs_from_scores(float* probs, int64_t stride, int kb, int ke, int t0, int n,
+                                                  float m, float l)
+{
+    __threadfence_block();
+    for (int e = kb + t0; e < ke; e += n) {
+        float* p = probs + (int64_t)e * stride;
+        *p = exp_neg(*p - m) / l;
+    }
+}
+
+// The probabilities of the entries of a row with given scores (scale * ev)
+// and final statistics (m, l).
+__device__ __forceinline__ void probs_from_given(float* probs, int64_t stride, const float* ev, float scale, int kb,
+                                                 int ke, int t0, int n, float m, float l)
+{
+    for (int e = kb + t0; e < ke; e += n) probs[(int64_t)e * stride] = exp_neg(ev[e] * scale - m) / l;
+}
+
 // stream: non-temporal stores, for rows that are read again only after the
 // kernel (the column-part segment format's partial rows)
 template <int VEC, int NV>
@@ -319,12 +436,28 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
         float u[NV][VEC];
         load_row<T, VEC, NV>(u, static_cast<const T*>(a.U) + u_row_of(a, row) * a.ldu, L, a.F);
         sddmm_edges<T, VEC, NV, U>(u, a.col_idx, b, e, 1, X, a.ldx, L, a.F, a.Y, a.out_idx);
+    } else if constexpr (OP == Op::AttnQK) {
+        constexpr int UQ = U > 1 ? U / 2 : 1;  // K and V rows in flight: half the entries
+        float q[NV][VEC], acc[NV][VEC];
+        load_row<T, VEC, NV>(q, static_cast<const T*>(a.U) + row * a.ldu, L, a.F);
+        zero(acc);
+        float m = -INFINITY, l = 0.f;
+        qk_walk<T, VEC, NV, UQ>(q, a.col_idx, b, e, 1, X, a.ldx, static_cast<const T*>(a.V), a.ldv, L, a.F, a.scale,
+                                m, l, acc, a.probs, a.probs_stride);
+        float* dst = a.Y + row * a.ldy;
+        if (e > b) {
+            store_row_div<VEC, NV>(dst, acc, L, a.F, l);
+            if (a.probs) probs_from_scores(a.probs, a.probs_stride, b, e, L.lg, a.W, m, l);
+        } else {
+            store_row<VEC, NV>(dst, acc, L, a.F, 1.f);
+        }
     } else {
         float acc[NV][VEC];
         zero(acc);
         float m = 0.f, l = 1.f;
         if constexpr (OP == Op::Attention) {
             seg_softmax_stats(a.ev, b, e, L.lg, a.W, a.scale, m, l);
+            if (a.probs && e > b) probs_from_given(a.probs, a.probs_stride, a.ev, a.scale, b, e, L.lg, a.W, m, l);
         }
         if (OP == Op::Spmm && a.W == CSR_WAVE)
             gather_acc_wave<T, VEC, NV, U>(acc, a.col_idx, a.ev, __builtin_amdgcn_readfirstlane(b),
@@ -490,27 +623,72 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
     // x0 .. x1-1 end here and are final unless they began before y0 (slot A,
     // only possible for i == 0); row x1, when present, continues (slot B).
     const int nend = x1 - x0;
+    constexpr bool SOFT = OP == Op::Attention || OP == Op::AttnQK;
     auto emit = [&](int i, float (&acc)[NV][VEC], float m, float l, bool whole_wave) {
         const int rs = rp[i], re = rp[i + 1];
         const int64_t row = (int64_t)x0 + i;
+        const bool complete = i < nend && rs >= y0;
+        if constexpr (SOFT) {
+            // a row complete in this chunk: its probabilities, from every lane
+            // that holds the row's statistics (a split row gets them in the fix-up)
+            if (a.probs && complete && re > rs) {
+                const int t0 = whole_wave ? lane : L.lg, n = whole_wave ? CSR_WAVE : a.W;
+                if constexpr (OP == Op::Attention)
+                    probs_from_given(a.probs, a.probs_stride, ev, a.scale, rs, re, t0, n, m, l);
+                else
+                    probs_from_scores(a.probs, a.probs_stride, rs, re, t0, n, m, l);
+            }
+        }
         if (whole_wave && L.g != 0) return;
-        if (i < nend && rs >= y0) {
+        if (complete) {
             float* dst = a.Y + row * a.ldy;
-            if (OP == Op::Attention && re > rs)
+            if (SOFT && re > rs)
                 store_row_div<VEC, NV>(dst, acc, L, a.F, l);
             else
                 store_row<VEC, NV>(dst, acc, L, a.F, 1.f, a.stream_y);
         } else {
             const int64_t slot = 2 * chunk + ((i == nend) ? 1 : 0);
             store_row<VEC, NV>(a.carry_val + slot * a.F, acc, L, a.F, 1.f);
-            if (OP == Op::Attention && L.lg == 0) {
+            if (SOFT && L.lg == 0) {
                 a.carry_ml[2 * slot] = m;
                 a.carry_ml[2 * slot + 1] = l;
             }
         }
     };
 
-    if constexpr (OP == Op::Sddmm) {
+    if constexpr (OP == Op::AttnQK) {
+        constexpr int UQ = U > 1 ? U / 2 : 1;
+        const T* Q = static_cast<const T*>(a.U);
+        const T* Vv = static_cast<const T*>(a.V);
+        // pass 1: long segments, whole wave (the groups take interleaved
+        // entries, then their states are merged)
+        for (int i = 0; i < nrow; ++i) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb < long_row) continue;
+            float q[NV][VEC], acc[NV][VEC];
+            load_row<T, VEC, NV>(q, Q + ((int64_t)x0 + i) * a.ldu, L, a.F);
+            zero(acc);
+            float m = -INFINITY, l = 0.f;
+            qk_walk<T, VEC, NV, UQ>(q, col, sb + L.g, se, G, X, a.ldx, Vv, a.ldv, L, a.F, a.scale, m, l, acc,
+                                    a.probs, a.probs_stride);
+            if (G > 1) qk_merge_groups<VEC, NV>(m, l, acc, a.W);
+            emit(i, acc, m, l, true);
+        }
+        // pass 2: short segments, one group each
+        if (G > 1) {
+            for (int i = L.g; i < nrow; i += G) {
+                const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+                if (se - sb >= long_row) continue;
+                float q[NV][VEC], acc[NV][VEC];
+                load_row<T, VEC, NV>(q, Q + ((int64_t)x0 + i) * a.ldu, L, a.F);
+                zero(acc);
+                float m = -INFINITY, l = 0.f;
+                qk_walk<T, VEC, NV, UQ>(q, col, sb, se, 1, X, a.ldx, Vv, a.ldv, L, a.F, a.scale, m, l, acc, a.probs,
+                                        a.probs_stride);
+                emit(i, acc, m, l, false);
+            }
+        }
+    } else if constexpr (OP == Op::Sddmm) {
         // pass 1: long segments, whole wave
         for (int i = 0; i < nrow; ++i) {
             const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
@@ -761,8 +939,9 @@ __device__ __forceinline__ void fixup_one(const Fp32Args& a, int64_t c, int r)
     auto slot_of = [&](int64_t p) -> int64_t { return (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c; };
 
     Lanes<VEC, NV> L(a.W);
+    constexpr bool SOFT = OP == Op::Attention || OP == Op::AttnQK;
     float M = 0.f;
-    if constexpr (OP == Op::Attention) {
+    if constexpr (SOFT) {
         float mm = -INFINITY;
         for (int64_t p = lane; p < np; p += CSR_WAVE) {
             int64_t s = slot_of(p);
@@ -777,7 +956,7 @@ __device__ __forceinline__ void fixup_one(const Fp32Args& a, int64_t c, int r)
     for (int64_t p = L.g; p < np; p += L.G) {
         int64_t s = slot_of(p);
         float w = 1.f;
-        if constexpr (OP == Op::Attention) {
+        if constexpr (SOFT) {
             float lp = a.carry_ml[2 * s + 1];
             w = (lp > 0.f) ? exp_neg(a.carry_ml[2 * s] - M) : 0.f;
             lsum = fmaf(w, lp, lsum);
@@ -800,9 +979,22 @@ __device__ __forceinline__ void fixup_one(const Fp32Args& a, int64_t c, int r)
             for (int v = 0; v < VEC; ++v) acc[j][v] = xor_sum_from(acc[j][v], a.W);
         lsum = xor_sum_from(lsum, a.W);
     }
+    if constexpr (SOFT) {
+        // the split row's probabilities, now that its statistics are final
+        // (the scores t of attention from queries and keys were stored by the
+        // main kernel)
+        if (a.probs) {
+            const int rb = a.row_ptr[r], re = a.row_ptr[r + 1];
+            for (int e = rb + lane; e < re; e += CSR_WAVE) {
+                float* pp = a.probs + (int64_t)e * a.probs_stride;
+                const float t = (OP == Op::AttnQK) ? *pp : a.ev[e] * a.scale;
+                *pp = exp_neg(t - M) / lsum;
+            }
+        }
+    }
     if (L.g != 0) return;
     float* dst = a.Y + (int64_t)r * a.ldy;
-    if constexpr (OP == Op::Attention)
+    if constexpr (SOFT)
         store_row_div<VEC, NV>(dst, acc, L, a.F, lsum);
     else
         store_row<VEC, NV>(dst, acc, L, a.F, 1.f, a.stream_y);

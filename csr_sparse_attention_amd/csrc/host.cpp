@@ -3,6 +3,7 @@
 // model, input signature and the cache log format.
 #include "host.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -43,7 +44,12 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // ops of the lane-group kernels (fp32 accumulation; fp32 or bf16 operands)
-bool is_fp32_op(int op) { return op == CSR_OP_SPMM || op == CSR_OP_SDDMM || op == CSR_OP_ATTENTION; }
+bool is_fp32_op(int op)
+{
+    return op == CSR_OP_SPMM || op == CSR_OP_SDDMM || op == CSR_OP_ATTENTION || op == CSR_OP_ATTENTION_QK;
+}
+
+bool is_softmax_op(int op) { return op == CSR_OP_ATTENTION || op == CSR_OP_ATTENTION_QK || op == CSR_OP_MHA; }
 
 void fnv(uint64_t& h, int64_t v)
 {
@@ -65,6 +71,9 @@ int max_vec_f32(const csr_problem_t& p)
             ok = (p.ld_b % v == 0) && (p.ld_out % v == 0) && aligned(p.b, bytes) && aligned(p.out, bytes);
         } else if (p.op == CSR_OP_SDDMM) {
             ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && aligned(p.a, bytes) && aligned(p.b, bytes);
+        } else if (p.op == CSR_OP_ATTENTION_QK) {
+            ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && (p.ld_c % v == 0) && (p.ld_out % v == 0) &&
+                 aligned(p.a, bytes) && aligned(p.b, bytes) && aligned(p.c, bytes) && aligned(p.out, bytes);
         }
         if (ok) return v;
     }
@@ -85,6 +94,9 @@ int max_vec_bf16(const csr_problem_t& p)
             ok = (p.ld_b % v == 0) && (p.ld_out % outv == 0) && aligned(p.b, in) && aligned(p.out, out);
         } else if (p.op == CSR_OP_SDDMM) {
             ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && aligned(p.a, in) && aligned(p.b, in);
+        } else if (p.op == CSR_OP_ATTENTION_QK) {
+            ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && (p.ld_c % v == 0) && (p.ld_out % outv == 0) &&
+                 aligned(p.a, in) && aligned(p.b, in) && aligned(p.c, in) && aligned(p.out, out);
         }
         if (ok) return v;
     }
@@ -120,7 +132,7 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (why) *why = msg;
         return code;
     };
-    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_SOFTMAX_BWD) return fail(CSR_ERR_SHAPE, "unknown op");
+    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_ATTENTION_QK) return fail(CSR_ERR_SHAPE, "unknown op");
     if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32 && p.dtype != CSR_DTYPE_BF16)
         return fail(CSR_ERR_DTYPE, "this op takes fp32 or bf16 operands");
     if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
@@ -148,6 +160,8 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
     if (p.nnz > 0 && p.n_rows == 0) return fail(CSR_ERR_SHAPE, "entries but no rows");
     if (is_fp32_op(p.op)) {
         if (p.width < 1 || p.width > 4096) return fail(CSR_ERR_SHAPE, "feature width must be in [1, 4096]");
+        if (p.op == CSR_OP_ATTENTION_QK && p.width > 1024)
+            return fail(CSR_ERR_SHAPE, "attention from queries and keys: head_dim must be in [1, 1024]");
         int W, nv;
         if (p.dtype == CSR_DTYPE_BF16) {
             if (p.width % 2) return fail(CSR_ERR_SHAPE, "bf16 operands need an even width");
@@ -164,11 +178,16 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (p.op == CSR_OP_SDDMM) {
             if (p.ld_a < p.width || p.ld_b < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < K");
             if (p.ld_a >= ld_lim || p.ld_b >= ld_lim) return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
+        } else if (p.op == CSR_OP_ATTENTION_QK) {
+            if (p.ld_a < p.width || p.ld_b < p.width || p.ld_c < p.width || p.ld_out < p.width)
+                return fail(CSR_ERR_SHAPE, "leading dimension < head_dim");
+            if (p.ld_a >= ld_lim || p.ld_b >= ld_lim || p.ld_c >= ld_lim || p.ld_out >= ld_lim)
+                return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
         } else {
             if (p.ld_b < p.width || p.ld_out < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < F");
             if (p.ld_b >= ld_lim || p.ld_out >= ld_lim) return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
         }
-        if (!aligned(p.a, 4) || !aligned(p.b, 4) || !aligned(p.out, 4))
+        if (!aligned(p.a, 4) || !aligned(p.b, 4) || !aligned(p.c, 4) || !aligned(p.out, 4))
             return fail(CSR_ERR_ALIGN, "fp32 operands must be 4-byte aligned");
     } else {
         if (p.heads < 1) return fail(CSR_ERR_SHAPE, "heads must be >= 1");
@@ -178,14 +197,19 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (!aligned(p.a, 16) || !aligned(p.b, 16) || !aligned(p.c, 16) || !aligned(p.out, 16))
             return fail(CSR_ERR_ALIGN, "Q, K, V and out must be 16-byte aligned");
     }
-    if ((p.op == CSR_OP_ATTENTION || p.op == CSR_OP_MHA) && !std::isfinite(p.scale))
-        return fail(CSR_ERR_SHAPE, "scale must be finite");
+    if (is_softmax_op(p.op) && !std::isfinite(p.scale)) return fail(CSR_ERR_SHAPE, "scale must be finite");
+    if (p.probs) {
+        if (!is_softmax_op(p.op)) return fail(CSR_ERR_SHAPE, "probabilities are an output of the attention ops");
+        if (!aligned(p.probs, 4)) return fail(CSR_ERR_ALIGN, "probs must be 4-byte aligned");
+        if (p.probs_stride < 0 || (p.op == CSR_OP_MHA && p.probs_stride > 1))
+            return fail(CSR_ERR_SHAPE, "probs_stride must be >= 0 (multi-head: 0, the layout is [nnz, heads])");
+    }
     if (need_ptrs) {
         if (!p.row_ptr) return fail(CSR_ERR_NULL, "row_ptr is NULL");
         if (p.nnz > 0 && !p.col_idx) return fail(CSR_ERR_NULL, "col_idx is NULL");
         if (p.op != CSR_OP_SPMM && p.nnz > 0 && !p.a) return fail(CSR_ERR_NULL, "operand a is NULL");
         if (p.nnz > 0 && !p.b) return fail(CSR_ERR_NULL, "operand b is NULL");
-        if (p.op == CSR_OP_MHA && p.nnz > 0 && !p.c) return fail(CSR_ERR_NULL, "V is NULL");
+        if ((p.op == CSR_OP_MHA || p.op == CSR_OP_ATTENTION_QK) && p.nnz > 0 && !p.c) return fail(CSR_ERR_NULL, "V is NULL");
         if (p.op == CSR_OP_SDDMM ? (p.nnz > 0 && !p.out) : (p.n_rows > 0 && !p.out))
             return fail(CSR_ERR_NULL, "output is NULL");
     }
@@ -277,7 +301,7 @@ WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
     w.carry_row = w.coords + up((size_t)(nc + 1) * 2 * 4);
     w.carry_ml = w.carry_row + up((size_t)nc * 2 * 4);
     size_t ml = 0, val = 0;
-    if (p.op == CSR_OP_ATTENTION) {
+    if (p.op == CSR_OP_ATTENTION || p.op == CSR_OP_ATTENTION_QK) {
         ml = (size_t)nc * 2 * 2 * 4;
         val = (size_t)nc * 2 * p.width * 4;
     } else if (p.op == CSR_OP_SPMM) {
@@ -413,7 +437,7 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
             add(s);
         }
         // small widths: lanes over entries, segmented scan
-        if (p.op != CSR_OP_ATTENTION && p.width <= 4 * d.vec) {
+        if ((p.op == CSR_OP_SPMM || p.op == CSR_OP_SDDMM) && p.width <= 4 * d.vec) {
             for (int D : {512, 256}) {
                 s = d;
                 s.mapping = CSR_MAP_SEGSCAN;
@@ -443,7 +467,7 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
         return p.nnz * 8.0 / bw + 3 * launch + nc * per_chunk / (cus * 8.0);
     }
     const double esize = (p.op == CSR_OP_MHA || p.dtype == CSR_DTYPE_BF16) ? 2.0 : 4.0;
-    const double gathers = (p.op == CSR_OP_MHA) ? 2.0 : 1.0;
+    const double gathers = (p.op == CSR_OP_MHA || p.op == CSR_OP_ATTENTION_QK) ? 2.0 : 1.0;
     const double row_bytes = p.width * esize * gathers;
     // wide lanes: idle lanes read lines that their pass reads anyway, and
     // 16-byte accesses gather about 0.82x the time of 8-byte ones (measured)
@@ -608,6 +632,92 @@ uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo
     return h;
 }
 
+uint64_t plan_signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev)
+{
+    uint64_t h = signature(p, hist, dev);
+    fnv(h, 0x4e414c50);  // 'PLAN'
+    return h;
+}
+
+int64_t segment_bound(const csr_problem_t& p, const int64_t* hist, int P, int T)
+{
+    if (!hist) return std::min(p.nnz, p.n_rows * (int64_t)P);
+    int64_t n = 0;
+    for (int b = 1; b < 33; ++b) {
+        if (hist[b] <= 0) continue;
+        const int64_t lo = (int64_t)1 << (b - 1), hi = (int64_t)1 << b;  // degrees in [lo, hi)
+        if (hi <= T)
+            n += hist[b];  // every row of the bucket is kept whole
+        else
+            n += std::min(hist[33 + b], hist[b] * (int64_t)P);
+        (void)lo;
+    }
+    return std::max<int64_t>(0, std::min(n, p.nnz));
+}
+
+std::vector<std::pair<int, int>> plan_formats(const csr_problem_t& p, const int64_t* hist)
+{
+    std::vector<std::pair<int, int>> out;
+    if ((p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) || p.nnz <= 0 || p.n_rows <= 0 || p.n_cols <= 0) return out;
+    auto add = [&](int P, int T) {
+        if (P < 2 || P > 256) return;
+        for (const auto& f : out)
+            if (f.first == P && f.second == T) return;
+        out.push_back({P, T});
+    };
+    int P = 1, T = 0;
+    hybrid_plan(p, hist, &P, &T);
+    if (P > 1) {
+        add(P, T);
+        add(P / 2, T);
+        add(P * 2, T);
+        if (T > 0) add(P, 0);
+    } else {
+        const double X = (double)p.n_cols * p.width * (p.dtype == CSR_DTYPE_BF16 ? 2.0 : 4.0);
+        if (X / 4 >= 2.0 * (1 << 20)) add(4, 0);
+        if (X / 16 >= 2.0 * (1 << 20)) add(16, 0);
+    }
+    return out;
+}
+
+std::string format_plan_line(uint64_t sig, const PlanChoice& c, double probe_us)
+{
+    char buf[288];
+    const csr_schedule_t& s = c.sched;
+    std::snprintf(buf, sizeof buf,
+                  "csrsa-plan v%d %016llx parts=%d whole=%d op=%d map=%d vec=%d w=%d nv=%d chunk=%d long=%d "
+                  "flags=%d us=%.3f\n",
+                  CSR_SCHEDULE_VERSION, (unsigned long long)sig, c.parts, c.whole_below, s.op, s.mapping, s.vec,
+                  s.group_lanes, s.passes, s.chunk_items, s.long_row, s.flags, probe_us);
+    return buf;
+}
+
+bool parse_plan_line(const std::string& line, uint64_t* sig, PlanChoice* c, double* probe_us)
+{
+    int ver = 0, n = 0;
+    unsigned long long sg = 0;
+    PlanChoice t;
+    std::memset(&t.sched, 0, sizeof t.sched);
+    double us = 0;
+    csr_schedule_t& s = t.sched;
+    const int got = std::sscanf(line.c_str(),
+                                "csrsa-plan v%d %16llx parts=%d whole=%d op=%d map=%d vec=%d w=%d nv=%d chunk=%d "
+                                "long=%d flags=%d us=%lf%n",
+                                &ver, &sg, &t.parts, &t.whole_below, &s.op, &s.mapping, &s.vec, &s.group_lanes,
+                                &s.passes, &s.chunk_items, &s.long_row, &s.flags, &us, &n);
+    if (got != 13 || ver != CSR_SCHEDULE_VERSION) return false;
+    for (size_t i = (size_t)n; i < line.size(); ++i)
+        if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
+    if (s.op != CSR_OP_SPMM && s.op != CSR_OP_SDDMM) return false;
+    if (t.parts < 1 || t.parts > 256 || (t.parts & (t.parts - 1)) || t.whole_below < 0) return false;
+    if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH && s.mapping != CSR_MAP_SEGSCAN) return false;
+    s.version = CSR_SCHEDULE_VERSION;
+    *sig = sg;
+    *c = t;
+    if (probe_us) *probe_us = us;
+    return true;
+}
+
 std::string format_cache_line(uint64_t sig, const csr_schedule_t& s, double probe_us)
 {
     char buf[256];
@@ -632,7 +742,7 @@ bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s,
     if (got != 11 || ver != CSR_SCHEDULE_VERSION) return false;
     for (size_t i = (size_t)n; i < line.size(); ++i)
         if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
-    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_SOFTMAX_BWD) return false;
+    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_ATTENTION_QK) return false;
     if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH && t.mapping != CSR_MAP_SEGSCAN) return false;
     t.version = CSR_SCHEDULE_VERSION;
     *sig = sg;

@@ -78,4 +78,31 @@ int hybrid_parts(const csr_problem_t& p, const int64_t* hist);
 std::string format_cache_line(uint64_t sig, const csr_schedule_t& s, double probe_us);
 bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s, double* probe_us);
 
+// Planned products (a CSR matrix prepared for one SpMM / SDDMM): the joint
+// choice of layout (plain CSR, or the column-part segment format with its
+// parts and whole-row threshold) and of the product's schedule.
+struct PlanChoice {
+    int parts = 1;        // 1: the plain pattern
+    int whole_below = 0;
+    csr_schedule_t sched{};
+};
+
+// Signature of a planned problem: the plain signature's fields under a
+// marker of its own, so plans and plain schedules never share a key.
+uint64_t plan_signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev);
+
+// Upper bound of the segment count of the format with P parts and rows under
+// T entries kept whole, from the degree histogram: a whole row is one
+// segment, a split row of degree d at most min(d, P).
+int64_t segment_bound(const csr_problem_t& p, const int64_t* hist, int P, int T);
+
+// The formats a plan probes beside the plain pattern: the cost model's
+// choice, half and twice its parts, and its parts with every row split; with
+// the plain pattern chosen by the model, 4 and 16 parts when one part of the
+// gathered operand would still hold at least 2 MiB.  (parts, whole_below) pairs.
+std::vector<std::pair<int, int>> plan_formats(const csr_problem_t& p, const int64_t* hist);
+
+std::string format_plan_line(uint64_t sig, const PlanChoice& c, double probe_us);
+bool parse_plan_line(const std::string& line, uint64_t* sig, PlanChoice* c, double* probe_us);
+
 }  // namespace csrh

@@ -96,6 +96,19 @@ static unsigned grid_for(int64_t n, int64_t cap)
     return (unsigned)b;
 }
 
+__global__ void k_fill_f32(float* p, int64_t n, float value)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(n, 65536)), dim3(CSR_BLOCK), 0, s, p, n, value);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_i64(int64_t* p, int64_t n, int64_t value, hipStream_t s)
 {
     if (n <= 0) return hipSuccess;

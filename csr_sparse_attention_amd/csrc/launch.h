@@ -44,6 +44,10 @@ hipError_t launch_sddmm(int mapping, int vec, int nv, int chunk, const Fp32Args&
 hipError_t launch_spmm_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_sddmm_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+// attention from queries and keys in one pass (U = Q, X = K, V = values)
+hipError_t launch_attention_qk(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_attention_qk_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+hipError_t launch_attention_qk_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
 hipError_t launch_mha(int mapping, int lph, int chunk, const MhaArgs& a, hipStream_t s);
 hipError_t launch_mha_fixup(int lph, const MhaArgs& a, hipStream_t s);
 
@@ -76,6 +80,7 @@ hipError_t launch_hybrid_reduce(int vec, int nv, int W, float* Y, int64_t ldy, c
 
 // Structure kernels.
 hipError_t launch_fill_i64(int64_t* p, int64_t n, int64_t value, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_degree_hist(const int32_t* row_ptr, int64_t n_rows, int64_t* out, hipStream_t s);
 hipError_t launch_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz, int64_t items,
                              int64_t n_chunks, int32_t* coords, hipStream_t s, int32_t* bounds = nullptr);

@@ -75,8 +75,9 @@ __device__ __forceinline__ void mha_issue(const MhaArgs& a, const MhaLanes<LPH>&
 // Folds entries k .. k+U-1 (< ke), whose K and V rows are in kr / vr, into the
 // online softmax state (m, l, acc) of the row whose query is q.
 template <int LPH, int U>
-__device__ __forceinline__ void mha_fold(const MhaArgs& a, const float (&q)[8], int k, int ke, const uint4 (&kr)[U],
-                                         const uint4 (&vr)[U], float& m, float& l, float (&acc)[8])
+__device__ __forceinline__ void mha_fold(const MhaArgs& a, const MhaLanes<LPH>& L, const float (&q)[8], int k, int ke,
+                                         const uint4 (&kr)[U], const uint4 (&vr)[U], float& m, float& l,
+                                         float (&acc)[8])
 {
     float t[U];
 #pragma unroll
@@ -92,6 +93,12 @@ __device__ __forceinline__ void mha_fold(const MhaArgs& a, const float (&q)[8], 
     float mn = m;
 #pragma unroll
     for (int u = 0; u < U; ++u) mn = fmaxf(mn, t[u]);
+    if (a.probs && L.valid && (L.lane % LPH) == 0) {
+        // the scores, turned into probabilities once the row's statistics are final
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k + u < ke) a.probs[(int64_t)(k + u) * a.H + L.head] = t[u];
+    }
     const float corr = (l > 0.f) ? exp_neg(m - mn) : 0.f;
     l *= corr;
 #pragma unroll
@@ -117,7 +124,7 @@ __device__ __forceinline__ void mha_walk(const MhaArgs& a, const MhaLanes<LPH>& 
     for (int k = kb; k < ke; k += U) {
         uint4 kr[U], vr[U];
         mha_issue<LPH, U>(a, L, col, k, ke, kr, vr);
-        mha_fold<LPH, U>(a, q, k, ke, kr, vr, m, l, acc);
+        mha_fold<LPH, U>(a, L, q, k, ke, kr, vr, m, l, acc);
     }
 }
 
@@ -127,6 +134,27 @@ __device__ __forceinline__ void mha_load_q(float (&q)[8], const MhaArgs& a, cons
     uint4 r = L.valid ? *reinterpret_cast<const uint4*>(a.Q + row * ((int64_t)a.H * a.Dh) + L.off)
                       : make_uint4(0, 0, 0, 0);
     bf16x8_to_f32(q, r);
+}
+
+// The probabilities of entries [kb, ke) of a row, every head: exp(t - m_h) /
+// l_h from the scores t the wave stored; (m_h, l_h) are held by the lanes of
+// head h, so every lane of the wave takes part (the fence orders the stored
+// scores before they are read back).
+template <int LPH>
+__device__ __forceinline__ void mha_probs(const MhaArgs& a, int kb, int ke, float m, float l)
+{
+    __threadfence_block();
+    const int lane = lane_id();
+    const int64_t n = (int64_t)(ke - kb) * a.H;
+    const int64_t n_up = (n + CSR_WAVE - 1) / CSR_WAVE * CSR_WAVE;  // the same trip count in every lane
+    for (int64_t idx = lane; idx < n_up; idx += CSR_WAVE) {
+        const int h = (int)(idx % a.H);
+        const float mh = __shfl(m, h * LPH, CSR_WAVE), lh = __shfl(l, h * LPH, CSR_WAVE);
+        if (idx < n) {
+            float* p = a.probs + ((int64_t)kb + idx / a.H) * a.H + h;
+            *p = exp_neg(*p - mh) / lh;
+        }
+    }
 }
 
 __device__ __forceinline__ void store8(float* dst, const float (&v)[8], float den)
@@ -155,6 +183,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mha_rowgroup(MhaArgs a)
     float m = -INFINITY, l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int b = a.row_ptr[row], e = a.row_ptr[row + 1];
     mha_walk<LPH, U>(a, L, q, a.col_idx, b, e, m, l, acc);
+    if (a.probs && e > b) mha_probs<LPH>(a, b, e, m, l);
     if (!L.valid) return;
     float* dst = a.out + row * ((int64_t)a.H * a.Dh) + L.off;
     if (e > b)
@@ -212,8 +241,10 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mha_mergepath(MhaArgs a)
         mha_load_q<LPH>(q, a, L, row);
         float m = -INFINITY, l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         mha_walk<LPH, U>(a, L, q, col, sb, se, m, l, acc);
+        const bool complete = i < nend && rs >= y0;
+        if (a.probs && complete && re > rs) mha_probs<LPH>(a, rs, re, m, l);
         if (!L.valid) continue;
-        if (i < nend && rs >= y0) {
+        if (complete) {
             float* dst = a.out + row * ld + L.off;
             if (re > rs)
                 store8(dst, acc, l);
@@ -246,26 +277,31 @@ __device__ __forceinline__ void mha_fixup_one(const MhaArgs& a, int64_t c, int r
     }
     const int64_t np = c - k0 + 1;
     MhaLanes<LPH> L(a.H, a.Dh);
-    if (!L.valid) return;
     const int64_t ld = (int64_t)a.H * a.Dh;
     float M = -INFINITY;
-    for (int64_t p = 0; p < np; ++p) {
-        const int64_t s = (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c;
-        const float* ml = a.carry_ml + (s * a.H + L.head) * 2;
-        if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
-    }
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, lsum = 0.f;
-    for (int64_t p = 0; p < np; ++p) {
-        const int64_t s = (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c;
-        const float* ml = a.carry_ml + (s * a.H + L.head) * 2;
-        const float w = (ml[1] > 0.f) ? exp_neg(ml[0] - M) : 0.f;
-        lsum = fmaf(w, ml[1], lsum);
-        const float4* src = reinterpret_cast<const float4*>(a.carry_val + s * ld + L.off);
-        float4 v0 = src[0], v1 = src[1];
-        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (L.valid) {
+        for (int64_t p = 0; p < np; ++p) {
+            const int64_t s = (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c;
+            const float* ml = a.carry_ml + (s * a.H + L.head) * 2;
+            if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+        }
+        for (int64_t p = 0; p < np; ++p) {
+            const int64_t s = (p < np - 1) ? 2 * (k0 + p) + 1 : 2 * c;
+            const float* ml = a.carry_ml + (s * a.H + L.head) * 2;
+            const float w = (ml[1] > 0.f) ? exp_neg(ml[0] - M) : 0.f;
+            lsum = fmaf(w, ml[1], lsum);
+            const float4* src = reinterpret_cast<const float4*>(a.carry_val + s * ld + L.off);
+            float4 v0 = src[0], v1 = src[1];
+            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+        }
     }
+    // the split row's probabilities (every lane takes part: the heads'
+    // statistics are exchanged between lanes)
+    if (a.probs) mha_probs<LPH>(a, a.row_ptr[r], a.row_ptr[r + 1], M, lsum);
+    if (!L.valid) return;
     store8(a.out + (int64_t)r * ld + L.off, acc, lsum);
 }
 

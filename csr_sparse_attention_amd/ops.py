@@ -16,7 +16,7 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _ffi
-from ._ffi import CsrError, CsrHybrid, CsrProblem, CsrSchedule
+from ._ffi import CsrError, CsrHybrid, CsrPlan, CsrProblem, CsrSchedule
 
 _lock = threading.Lock()
 _contexts: dict = {}
@@ -259,12 +259,78 @@ def _sddmm_problem(row_ptr, col_idx, U, V, out):
                     width=U.shape[1], ld_a=ldu, ld_b=ldv, dtype=_dtype_code(U, "U"))
 
 
-def _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale):
-    ldv = _dense(node_value, "node_value", torch.float32)
+def _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale, probs=None):
+    ldv = _dense(node_value, "node_value", (torch.float32, torch.bfloat16))
     ldo = _dense(out, "out", torch.float32)
-    return _problem(_ffi.OP_ATTENTION, row_ptr, col_idx, edge_scores, node_value, None, out,
-                    n_cols=node_value.shape[0], width=node_value.shape[1], ld_b=ldv, ld_out=ldo,
-                    scale=scale)
+    p = _problem(_ffi.OP_ATTENTION, row_ptr, col_idx, edge_scores, node_value, None, out,
+                 n_cols=node_value.shape[0], width=node_value.shape[1], ld_b=ldv, ld_out=ldo,
+                 scale=scale, dtype=_dtype_code(node_value, "node_value"))
+    p.probs, p.probs_stride = _ptr(probs), 1
+    return p
+
+
+def _qk_views(row_ptr, col_idx, Q, K, V, out, probs):
+    """Heads H and head_dim D of an attention from queries and keys with
+    operands Q [n_rows, (H,) D], K and V [n_cols, (H,) D] (one dtype, fp32 or
+    bf16; Q and K rows contiguous), out fp32 [n_rows, (H,) D] and probs fp32
+    [nnz, (H)] or None; checks every shape and returns (H, D, ldv, ldo)."""
+    n_rows, nnz = row_ptr.numel() - 1, col_idx.numel()
+    if Q.dim() not in (2, 3) or K.dim() != Q.dim() or V.dim() != Q.dim():
+        raise ValueError("Q, K, V must all be [n, D] or all [n, heads, D]")
+    H, D = (1, Q.shape[1]) if Q.dim() == 2 else (Q.shape[1], Q.shape[2])
+    if Q.shape[0] != n_rows or K.shape[1:] != Q.shape[1:] or V.shape[1:] != Q.shape[1:] or K.shape[0] != V.shape[0]:
+        raise ValueError(f"Q must be [n_rows={n_rows}, ...] and K, V [n_cols, ...] with Q's head shape")
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _dtype_code(t, name)
+        if t.dtype != Q.dtype:
+            raise TypeError("Q, K and V must have one dtype")
+        if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != D):
+            raise ValueError(f"{name} must have contiguous heads")
+    for name, t in (("Q", Q), ("K", K)):
+        if t.shape[0] > 1 and t.stride(0) != H * D:
+            raise ValueError(f"{name} rows must be contiguous")
+    ldv = V.stride(0) if V.shape[0] > 1 else H * D
+    if out.dtype != torch.float32 or out.shape != Q.shape or out.stride(-1) != 1 or \
+            (out.dim() == 3 and out.stride(1) != D):
+        raise ValueError(f"out must be fp32 of Q's shape {tuple(Q.shape)}")
+    ldo = out.stride(0) if out.shape[0] > 1 else H * D
+    if probs is not None:
+        want = (nnz,) if Q.dim() == 2 else (nnz, H)
+        if probs.dtype != torch.float32 or not probs.is_contiguous() or tuple(probs.shape) != want:
+            raise ValueError(f"probs must be a contiguous fp32 tensor {want}")
+    return H, D, ldv, ldo
+
+
+def _qk_problem(row_ptr, col_idx, Q, K, V, out, probs, scale):
+    """The problem the library runs for an attention from queries and keys:
+    the multi-head kernel's (bf16, head_dim a power of two in [8, 512],
+    heads * head_dim <= 512, contiguous and 16-byte aligned operands), else
+    the one-head problem of the head whose column views allow the narrowest
+    lane accesses (its schedule serves every head)."""
+    H, D, ldv, ldo = _qk_views(row_ptr, col_idx, Q, K, V, out, probs)
+    dt = _dtype_code(Q, "Q")
+    aligned = all(t.data_ptr() % 16 == 0 for t in (Q, K, V, out))
+    if dt == _ffi.DTYPE_BF16 and 8 <= D <= 512 and D & (D - 1) == 0 and H * D <= 512 and ldv == H * D \
+            and ldo == H * D and aligned:
+        p = _problem(_ffi.OP_MHA, row_ptr, col_idx, Q, K, V, out, n_cols=K.shape[0], width=H * D, heads=H,
+                     head_dim=D, scale=scale, dtype=dt)
+        p.probs = _ptr(probs)
+        return p, H, D, ldv, ldo
+    es = Q.element_size()
+    best = None
+    for h in range(H):
+        p = _problem(_ffi.OP_ATTENTION_QK, row_ptr, col_idx, None, None, None, None, n_cols=K.shape[0], width=D,
+                     ld_a=H * D, ld_b=H * D, ld_out=ldo, scale=scale, dtype=dt)
+        p.a, p.b, p.c = Q.data_ptr() + h * D * es, K.data_ptr() + h * D * es, V.data_ptr() + h * D * es
+        p.ld_c = ldv
+        p.out = out.data_ptr() + h * D * 4
+        p.probs = None if probs is None else probs.data_ptr() + h * 4
+        p.probs_stride = H
+        s = CsrSchedule()
+        _check(_lib().csr_default_schedule(None, ctypes.byref(p), ctypes.byref(s)), "csr_default_schedule")
+        if best is None or s.vec < best[0]:
+            best = (s.vec, p)
+    return best[1], H, D, ldv, ldo
 
 
 def _mha_problem(row_ptr, col_idx, Q, K, V, out, scale):
@@ -372,36 +438,67 @@ def sddmm(row_ptr, col_idx, U, V, *, out=None, schedule: Optional[CsrSchedule] =
     return out
 
 
-def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, out=None,
+def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, out=None, probs=None,
               schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
-        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Fused CSR attention with given scores: per row, softmax over the row's
     entries of scale * edge_scores, then the weighted sum of node_value rows
-    (zero for rows without entries).  Arguments in the order row_ptr,
-    col_idx, edge_scores, node_value."""
+    (fp32 or bf16; zero for rows without entries).  Arguments in the order
+    row_ptr, col_idx, edge_scores, node_value.  ``probs`` (fp32 [nnz]), when
+    given, receives every entry's probability."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
-    _on(row_ptr.device, edge_scores=edge_scores, node_value=node_value)
+    _on(row_ptr.device, edge_scores=edge_scores, node_value=node_value, probs=probs)
     _entries(edge_scores, "edge_scores", nnz)
     if node_value.dim() != 2:
         raise ValueError("node_value must be 2-D [n_cols, F]")
+    if probs is not None:
+        _entries(probs, "probs", nnz)
     out = _out_rows(out, n_rows, node_value.shape[1], node_value.device)
-    p = _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale)
+    p = _attention_problem(row_ptr, col_idx, edge_scores, node_value, out, scale, probs)
 
     def call(ctx, ws, nb, st):
-        return _lib().csr_attention(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
-                                    p.width, p.ld_b, ctypes.c_float(scale), p.out, p.ld_out,
-                                    _sched_arg(schedule), ws.data_ptr(), nb, st)
+        return _lib().csr_attention(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, None, None,
+                                    p.b, p.dtype, 1, p.width, p.ld_b, ctypes.c_float(scale), p.out, p.ld_out,
+                                    _ptr(probs), _sched_arg(schedule), ws.data_ptr(), nb, st)
 
     _run(p, node_value.device, schedule, ctx, call, workspace)
     return out
 
 
-def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, out=None,
+def attention_qk(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, out=None, probs=None,
+                 schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """CSR attention from queries and keys in one pass (SDDMM -> row-softmax ->
+    SpMM with the scores formed on the fly): Q [n_rows, D] or [n_rows, H, D],
+    K and V [n_cols, (H,) D], all fp32 or all bf16; per head, softmax over the
+    row's entries of scale * <Q_i, K_j> (scale defaults to 1/sqrt(D)), then the
+    weighted sum of V rows (fp32 accumulation).  Returns fp32 of Q's shape.
+    ``probs`` (fp32 [nnz] or [nnz, H]) receives the probabilities."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    _on(row_ptr.device, Q=Q, K=K, V=V, out=out, probs=probs)
+    if scale is None:
+        scale = 1.0 / float(Q.shape[-1]) ** 0.5
+    if out is None:
+        out = torch.empty(tuple(Q.shape), dtype=torch.float32, device=Q.device)
+    p, H, D, ldv, ldo = _qk_problem(row_ptr, col_idx, Q, K, V, out, probs, scale)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_attention(ctx.handle, n_rows, K.shape[0], nnz, row_ptr.data_ptr(), col_idx.data_ptr(),
+                                    None, Q.data_ptr(), K.data_ptr(), V.data_ptr(), p.dtype, H, D, ldv,
+                                    ctypes.c_float(scale), out.data_ptr(), ldo, _ptr(probs), _sched_arg(schedule),
+                                    ws.data_ptr(), nb, st)
+
+    _run(p, Q.device, schedule, ctx, call, workspace)
+    return out
+
+
+def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, out=None, probs=None,
                   schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
-        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Multi-head fused CSR attention: bf16 Q [n_rows, H, D], K, V [n_cols, H, D];
     per head, softmax over the row's entries of scale * <Q_i, K_j>, times V.
-    Returns fp32 [n_rows, H, D].  scale defaults to 1/sqrt(D)."""
+    Returns fp32 [n_rows, H, D].  scale defaults to 1/sqrt(D).  ``probs``
+    (fp32 [nnz, H]) receives the probabilities."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     _on(row_ptr.device, Q=Q, K=K, V=V)
     if Q.dim() != 3 or Q.shape[0] != n_rows:
@@ -414,12 +511,17 @@ def mha_attention(row_ptr, col_idx, Q, K, V, *, scale: Optional[float] = None, o
     _on(row_ptr.device, out=out)
     if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (n_rows, H, D):
         raise ValueError(f"out must be a contiguous fp32 tensor [{n_rows}, {H}, {D}]")
+    if probs is not None:
+        _on(row_ptr.device, probs=probs)
+        if probs.dtype != torch.float32 or not probs.is_contiguous() or tuple(probs.shape) != (nnz, H):
+            raise ValueError(f"probs must be a contiguous fp32 tensor [{nnz}, {H}]")
     p = _mha_problem(row_ptr, col_idx, Q, K, V, out, scale)
+    p.probs = _ptr(probs)
 
     def call(ctx, ws, nb, st):
         return _lib().csr_mha_attention(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b,
-                                        p.c, H, D, ctypes.c_float(scale), p.out, _sched_arg(schedule),
-                                        ws.data_ptr(), nb, st)
+                                        p.c, H, D, ctypes.c_float(scale), p.out, _ptr(probs),
+                                        _sched_arg(schedule), ws.data_ptr(), nb, st)
 
     _run(p, Q.device, schedule, ctx, call, workspace)
     return out
@@ -445,12 +547,16 @@ def row_softmax(row_ptr, scores, *, scale: float = 1.0, out=None, schedule: Opti
     return out
 
 
-def attention_pipeline(row_ptr, col_idx, Q, K, V, *, scale: float = 1.0, fused: bool = True,
+def attention_pipeline(row_ptr, col_idx, Q, K, V, *, scale: float = 1.0, fused=True,
                        ctx: Optional[Context] = None) -> torch.Tensor:
     """Single-head fp32 CSR attention from Q [n_rows, d], K [n_cols, d],
     V [n_cols, F] as the composition of library calls SDDMM -> row-softmax ->
-    SpMM.  fused=True runs SDDMM then the fused softmax-aggregation
-    (``attention``); fused=False runs the three stages separately."""
+    SpMM.  fused="single" runs the one-pass kernel (``attention_qk``: the
+    scores never leave the registers; needs F == d); fused=True runs SDDMM
+    then the fused softmax-aggregation (``attention``); fused=False runs the
+    three stages separately."""
+    if fused == "single":
+        return attention_qk(row_ptr, col_idx, Q, K, V, scale=scale, ctx=ctx)
     scores = sddmm(row_ptr, col_idx, Q, K, ctx=ctx)
     if fused:
         return attention(row_ptr, col_idx, scores, V, scale=scale, ctx=ctx)
@@ -756,10 +862,134 @@ def hybrid_sddmm(h: Hybrid, U, V, *, out=None, schedule: Optional[CsrSchedule] =
     return out
 
 
+# ---------------------------------------------------------------------------
+# planned products: the library chooses layout (plain CSR or the column-part
+# segment format at some part count and whole-row threshold) and schedule
+# together, and caches the choice
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """A CSR matrix prepared for one SpMM or SDDMM (csr_plan_t): the chosen
+    layout and schedule, the plan memory that holds its arrays, and the
+    tensors it refers to (kept alive with it)."""
+
+    def __init__(self, desc: CsrPlan, mem, keep):
+        self.desc = desc
+        self._mem = mem
+        self._keep = keep
+
+    @property
+    def op(self):
+        return {_ffi.OP_SPMM: "spmm", _ffi.OP_SDDMM: "sddmm"}[self.desc.op]
+
+    @property
+    def parts(self):
+        return self.desc.parts
+
+    @property
+    def whole_below(self):
+        return self.desc.whole_below
+
+    @property
+    def schedule(self) -> CsrSchedule:
+        return CsrSchedule.from_buffer_copy(bytes(self.desc.sched))
+
+    @property
+    def signature(self) -> int:
+        return self.desc.signature
+
+    @property
+    def n_seg(self) -> int:
+        return self.desc.fmt.n_seg if self.desc.parts > 1 else 0
+
+    @property
+    def workspace_bytes(self) -> int:
+        return self.desc.workspace_bytes
+
+    def choice(self):
+        """(parts, whole_below, schedule as a dict): the plan's joint choice."""
+        return self.parts, self.whole_below, self.schedule.as_dict()
+
+    def __repr__(self):
+        return (f"Plan({self.op}, parts={self.parts}, whole_below={self.whole_below}, n_seg={self.n_seg}, "
+                f"{self.schedule}, probe_ms={self.desc.probe_ms:.3f})")
+
+
+def plan(op: str, row_ptr, col_idx, *operands, mode: str = "auto", out=None, ctx: Optional[Context] = None) -> Plan:
+    """Plans a product ('spmm': vals or None, X; 'sddmm': U, V): the library
+    chooses the layout and the schedule together by its cost model and
+    micro-probes on these operands (the probes write ``out``), or replays the
+    cached choice.  Synchronous."""
+    if op not in ("spmm", "sddmm"):
+        raise ValueError("plans serve 'spmm' and 'sddmm'")
+    p, out = make_problem(op, row_ptr, col_idx, *operands, out=out)
+    device = row_ptr.device
+    ctx = ctx or default_context(device.index)
+    lib = _lib()
+    head = _workspace(device, 1024)
+    p.workspace, p.workspace_bytes, p.stream = head.data_ptr(), 1024, _stream(device)
+    mem_bytes, ws_bytes = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.csr_plan_size(ctx.handle, ctypes.byref(p), ctypes.byref(mem_bytes), ctypes.byref(ws_bytes)),
+           "csr_plan_size", ctx)
+    mem = torch.empty(mem_bytes.value + 256, dtype=torch.uint8, device=device)
+    off = (-mem.data_ptr()) % 256
+    ws = _workspace(device, ws_bytes.value)
+    p.workspace, p.workspace_bytes = ws.data_ptr(), ws_bytes.value
+    desc = CsrPlan()
+    _check(lib.csr_plan_create(ctx.handle, ctypes.byref(p), _ffi.SELECT_MODES[mode], mem.data_ptr() + off,
+                               mem_bytes.value, ctypes.byref(desc)), "csr_plan_create", ctx)
+    keep = (row_ptr, col_idx) + tuple(t for t in operands if t is not None)
+    return Plan(desc, mem, keep)
+
+
+def plan_spmm(pl: Plan, X, *, vals=None, out=None, ctx: Optional[Context] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = A X with a plan of 'spmm'; ``vals`` (original entry order) replaces
+    the plan's values from this call on (over the format they are first
+    moved into the plan's copy)."""
+    if pl.desc.op != _ffi.OP_SPMM:
+        raise ValueError("not a plan of 'spmm'")
+    _rows(X, "X", pl.desc.n_cols, pl.desc.width, dtype=(torch.float32, torch.bfloat16))
+    ldx = _dense(X, "X", (torch.float32, torch.bfloat16))
+    if _dtype_code(X, "X") != pl.desc.dtype:
+        raise TypeError("X's dtype is not the plan's")
+    if vals is not None:
+        _entries(vals, "vals", pl.desc.nnz)
+        if pl.parts == 1:
+            pl._keep = pl._keep + (vals,)
+    out = _out_rows(out, pl.desc.n_rows, pl.desc.width, X.device)
+    ldy = _dense(out, "out", torch.float32)
+    ctx = ctx or default_context(X.device.index)
+    ws = _workspace(X.device, pl.desc.workspace_bytes, workspace)
+    _check(_lib().csr_plan_spmm(ctx.handle, ctypes.byref(pl.desc), _ptr(vals), X.data_ptr(), ldx, out.data_ptr(), ldy,
+                                ws.data_ptr(), pl.desc.workspace_bytes, _stream(X.device)), "csr_plan_spmm", ctx)
+    return out
+
+
+def plan_sddmm(pl: Plan, U, V, *, out=None, ctx: Optional[Context] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[e] = <U[row_e], V[col_e]> (original entry order) with a plan of 'sddmm'."""
+    if pl.desc.op != _ffi.OP_SDDMM:
+        raise ValueError("not a plan of 'sddmm'")
+    _rows(U, "U", pl.desc.n_rows, pl.desc.width, dtype=(torch.float32, torch.bfloat16))
+    _rows(V, "V", pl.desc.n_cols, pl.desc.width, dtype=U.dtype)
+    if _dtype_code(U, "U") != pl.desc.dtype:
+        raise TypeError("U's dtype is not the plan's")
+    ldu, ldv = _dense(U, "U", U.dtype), _dense(V, "V", V.dtype)
+    out = _out_entries(out, pl.desc.nnz, U.device)
+    ctx = ctx or default_context(U.device.index)
+    ws = _workspace(U.device, pl.desc.workspace_bytes, workspace)
+    _check(_lib().csr_plan_sddmm(ctx.handle, ctypes.byref(pl.desc), U.data_ptr(), ldu, V.data_ptr(), ldv,
+                                 out.data_ptr(), ws.data_ptr(), pl.desc.workspace_bytes, _stream(U.device)),
+           "csr_plan_sddmm", ctx)
+    return out
+
+
 def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0) -> CsrProblem:
     """The csr_problem_t of a call, for select() / workspace_size() /
     default_schedule(): op is 'spmm' (vals, X), 'sddmm' (U, V), 'attention'
-    (edge_scores, node_value) or 'mha' (Q, K, V)."""
+    (edge_scores, node_value), 'mha' (Q, K, V) or 'attention_qk' (Q, K, V:
+    the problem that csr_attention runs for them)."""
     _pattern(row_ptr, row_ptr if col_idx is None else col_idx)
     n_rows = row_ptr.numel() - 1
     if op == "spmm":
@@ -787,6 +1017,10 @@ def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 
         out = out if out is not None else torch.empty((n_rows,) + tuple(Q.shape[1:]), dtype=torch.float32,
                                                        device=Q.device)
         return _mha_problem(row_ptr, col_idx, Q, K, V, out, scale), out
+    if op == "attention_qk":
+        Q, K, V = operands
+        out = out if out is not None else torch.empty(tuple(Q.shape), dtype=torch.float32, device=Q.device)
+        return _qk_problem(row_ptr, col_idx, Q, K, V, out, None, scale)[0], out
     raise ValueError(op)
 
 

@@ -85,7 +85,8 @@ enum csr_op {
     CSR_OP_ATTENTION = 3, /* scores given: out = softmax_row(scale * S) V */
     CSR_OP_MHA = 4,       /* multi-head, scores = scale * <Q_i, K_j> per head */
     CSR_OP_ROW_SOFTMAX = 5, /* p_e = softmax over the row's entries of scale * s */
-    CSR_OP_SOFTMAX_BWD = 6  /* ds_e = scale * p_e * (g_e - sum over the row of p g) */
+    CSR_OP_SOFTMAX_BWD = 6, /* ds_e = scale * p_e * (g_e - sum over the row of p g) */
+    CSR_OP_ATTENTION_QK = 7 /* one head, scores = scale * <Q_i, K_j> formed in the same pass */
 };
 
 /* Element types of the dense operands.  bf16 operands are raw bfloat16 bit
@@ -171,6 +172,12 @@ typedef struct csr_schedule_s {
  *                          scale
  *   op = CSR_OP_ROW_SOFTMAX: a = scores fp32 [nnz], out = probabilities fp32 [nnz],
  *                          width = 1, scale (n_cols is not used)
+ *   op = CSR_OP_ATTENTION_QK: one head of an attention from queries and keys:
+ *                          a = Q [n_rows, ld_a], b = K [n_cols, ld_b], c = V [n_cols, ld_c]
+ *                          (all of dtype), width = head_dim (<= 1024), out fp32
+ *                          [n_rows, ld_out], scale
+ *   probs (attention ops, optional): the softmax probability of every entry,
+ *   at probs[e * probs_stride] (stride 0 means 1); multi-head: [nnz, heads].
  */
 typedef struct csr_problem_s {
     int32_t op;
@@ -190,6 +197,9 @@ typedef struct csr_problem_s {
     void* workspace;
     size_t workspace_bytes;
     void* stream;
+    int64_t ld_c;          /* CSR_OP_ATTENTION_QK: leading dimension of c */
+    float* probs;          /* attention ops: per-entry probabilities out, or NULL */
+    int64_t probs_stride;  /* floats between consecutive entries' probabilities (0: 1) */
 } csr_problem_t;
 
 /* ---------------------------------------------------------------------------
@@ -273,19 +283,35 @@ int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
               float* out, const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
               void* stream);
 
-/* Fused CSR attention with given edge scores (AutoSAGE page, Abstract: the
- * SDDMM -> row-softmax -> SpMM pipeline; POPCORNBENCH trace page, task
- * statement: argument order row_ptr, col_idx, edge_scores, node_value):
- *   for row i with entries E_i: t_e = scale * edge_scores[e],
- *   p_e = exp(t_e - max t) / sum over E_i of exp(t - max t),
- *   out[i, f] = sum over e in E_i of p_e * node_value[col_idx[e], f];
- *   out[i, :] = 0 when E_i is empty.
- * edge_scores: fp32 [nnz].  node_value: fp32 [n_cols, ldv].  out: fp32
- * [n_rows, ldo].  scale: finite (1.0 = no scaling).  1 <= F <= 4096. */
+/* Fused CSR attention (AutoSAGE page, Abstract: the SDDMM -> row-softmax ->
+ * SpMM pipeline; POPCORNBENCH trace page, task statement: argument order
+ * row_ptr, col_idx, edge_scores, node_value).  For each row i with entries
+ * E_i, head h, the scores t_e, p_e = exp(t_e - max t) / sum over E_i of
+ * exp(t - max t), out[i, h, :] = sum over e in E_i of p_e * V[col_idx[e], h, :];
+ * out[i, h, :] = 0 when E_i is empty.
+ *   edge_scores != NULL, or Q and K both NULL (scores given): heads must be
+ *     1, Q and K are not read, t_e = scale * edge_scores[e] (fp32 [nnz];
+ *     NULL only when nnz = 0).
+ *   edge_scores == NULL and Q, K given (scores from queries and keys, one
+ *     pass): t_e =
+ *     scale * sum over d of Q[i, h, d] * K[col_idx[e], h, d]; Q: [n_rows,
+ *     heads * head_dim] and K: [n_cols, heads * head_dim], rows contiguous.
+ *     bf16 with head_dim a power of two in [8, 512], heads * head_dim <= 512,
+ *     ldv = ldo = heads * head_dim and 16-byte aligned operands runs the
+ *     multi-head kernel (schedule op CSR_OP_MHA); otherwise each head runs
+ *     as one CSR_OP_ATTENTION_QK problem (head_dim <= 1024; schedule op
+ *     CSR_OP_ATTENTION_QK, shared by the heads).
+ * V = node_value: [n_cols, ldv] of dtype (CSR_DTYPE_F32, or CSR_DTYPE_BF16
+ * bit patterns; Q and K of the same dtype), ldv >= heads * head_dim.  out:
+ * fp32 [n_rows, ldo].  probs_out: NULL, or fp32 [nnz * heads], entry-major
+ * (p of entry e, head h at probs_out[e * heads + h]).  scale: finite (1.0 =
+ * no scaling).  Accumulation is fp32.  CSR_ERR_SHAPE for heads != 1 with
+ * given scores; other errors as for csr_spmm. */
 int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
                   const int32_t* row_ptr, const int32_t* col_idx, const float* edge_scores,
-                  const float* node_value, int64_t F, int64_t ldv, float scale,
-                  float* out, int64_t ldo, const csr_schedule_t* sched,
+                  const void* Q, const void* K, const void* node_value, int32_t dtype,
+                  int32_t heads, int64_t head_dim, int64_t ldv, float scale,
+                  float* out, int64_t ldo, float* probs_out, const csr_schedule_t* sched,
                   void* workspace, size_t ws_bytes, void* stream);
 
 /* Multi-head fused CSR attention, SDDMM -> row-softmax -> SpMM in one pass
@@ -297,11 +323,12 @@ int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
  * Q: bf16 [n_rows, heads, head_dim]; K, V: bf16 [n_cols, heads, head_dim]
  * (raw bfloat16 bit patterns, contiguous); out: fp32 [n_rows, heads, head_dim].
  * head_dim in {8, 16, 32, 64, 128, 256, 512}, heads * head_dim <= 512,
- * 16-byte aligned pointers. */
+ * 16-byte aligned pointers.  probs_out: NULL, or fp32 [nnz, heads] (the
+ * probability of every entry per head). */
 int csr_mha_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
                       const int32_t* row_ptr, const int32_t* col_idx,
                       const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                      int32_t heads, int32_t head_dim, float scale, float* out,
+                      int32_t heads, int32_t head_dim, float scale, float* out, float* probs_out,
                       const csr_schedule_t* sched, void* workspace, size_t ws_bytes,
                       void* stream);
 
@@ -476,6 +503,76 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
                       csr_schedule_t* out, uint64_t* signature);
 
 /* ---------------------------------------------------------------------------
+ * Planned products: one CSR matrix prepared for one SpMM or SDDMM (AutoSAGE
+ * page, Abstract: tiling and mapping chosen per input by an estimate refined
+ * with on-device micro-probes, kept in a persistent cache for deterministic
+ * replay; SparseTIR page, Abstract: composed formats searched over).  The
+ * library chooses the layout and the schedule together: the plain CSR
+ * pattern, or the column-part segment format above at several part counts
+ * and whole-row thresholds, each with the schedules of its product; the
+ * joint choice is cached under the input's signature (a log line of its
+ * own) and replayed on later plans of the same input.  The plan's arrays
+ * (the format, the values in format order) live in caller memory sized by
+ * csr_plan_size.
+ * ------------------------------------------------------------------------- */
+#define CSR_PLAN_VERSION 1
+
+typedef struct csr_plan_s {
+    int32_t version;          /* CSR_PLAN_VERSION */
+    int32_t op;               /* CSR_OP_SPMM or CSR_OP_SDDMM */
+    int32_t dtype;            /* element type of the dense operands */
+    int32_t parts;            /* 1: the plain pattern; otherwise the format's column parts */
+    int32_t whole_below;      /* the format's whole-row threshold */
+    int32_t reserved_;
+    int64_t n_rows, n_cols, nnz, width;
+    uint64_t signature;       /* the cache key of the choice */
+    csr_schedule_t sched;     /* the product's schedule (on the segment pattern when parts > 1) */
+    csr_hybrid_t fmt;         /* the format (parts > 1), its arrays in the plan memory */
+    const int32_t* row_ptr;   /* the plain pattern: the caller's arrays, which must stay valid */
+    const int32_t* col_idx;
+    float* vals;              /* SpMM: the values the product reads (the caller's array on the
+                                 plain pattern, the plan's format-order copy otherwise; NULL: 1) */
+    size_t workspace_bytes;   /* workspace of csr_plan_spmm / csr_plan_sddmm */
+    double probe_ms;          /* probed time of the choice (0 when replayed or estimated) */
+} csr_plan_t;
+
+/* Sizes for planning problem p (op CSR_OP_SPMM or CSR_OP_SDDMM; shape,
+ * dtype, leading dimensions, operand pointers for their alignment, row_ptr,
+ * and a workspace of at least 1 KiB for the degree histogram): plan memory
+ * and workspace that csr_plan_create needs for every layout it may probe
+ * (the segment counts bounded from the degree histogram).  The workspace
+ * also serves the planned calls.  Synchronous (reads the histogram). */
+int csr_plan_size(csr_context_t ctx, const csr_problem_t* p, size_t* plan_bytes, size_t* workspace_bytes);
+
+/* Plans problem p (every operand set, as for csr_select; SpMM: a = the
+ * values in original order or NULL for ones, b = X; SDDMM: a = U, b = V;
+ * out written by the probes) into *plan, with plan_mem (plan_bytes of
+ * device memory, 256-byte aligned) holding the plan's arrays and
+ * p->workspace of csr_plan_size's workspace bytes.  mode as for csr_select:
+ * AUTO replays a cached choice or probes and caches one, REPLAY_ONLY
+ * (CSR_ERR_NO_CACHE_ENTRY on a miss), FORCE_PROBE, ESTIMATE (the cost model
+ * alone, nothing stored).  A layout whose every probe fails is never
+ * chosen; if all fail, the plain pattern with its default schedule.  The
+ * plan keeps pointers to row_ptr, col_idx and (plain SpMM) the values:
+ * they must outlive it.  Synchronous. */
+int csr_plan_create(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, void* plan_mem, size_t plan_bytes,
+                    csr_plan_t* plan);
+
+/* Y = A X with a plan of op CSR_OP_SPMM: X [n_cols, ldx] of the plan's dtype,
+ * Y fp32 [n_rows, ldy], with the alignment and leading-dimension class the
+ * plan was made for (CSR_ERR_SCHEDULE otherwise).  vals: NULL uses the
+ * plan's values; otherwise new values in original order (over the format
+ * they are first moved into the plan's copy, in stream order).  No
+ * synchronisation; a workspace of plan->workspace_bytes. */
+int csr_plan_spmm(csr_context_t ctx, const csr_plan_t* plan, const float* vals, const void* X, int64_t ldx,
+                  float* Y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
+
+/* out[e] = <U[row_e], V[col_e]> (original entry order) with a plan of op
+ * CSR_OP_SDDMM; operands as for csr_sddmm, of the plan's dtype. */
+int csr_plan_sddmm(csr_context_t ctx, const csr_plan_t* plan, const void* U, int64_t ldu, const void* V, int64_t ldv,
+                   float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Schedule selection and cache (AutoSAGE page, Abstract: input-aware choice
  * refined by on-device micro-probes, guarded fallback, persistent cache for
  * deterministic replay).
@@ -512,7 +609,8 @@ int csr_workspace_size(csr_context_t ctx, const csr_problem_t* p, const csr_sche
  * whose earlier append failed).  CSR_ERR_CACHE_IO if an append fails again. */
 int csr_cache_flush(csr_context_t ctx);
 
-/* Cache statistics (host-only; any pointer may be NULL): number of entries,
+/* Cache statistics (host-only; any pointer may be NULL): number of entries
+ * (schedules and plans),
  * log lines skipped at load (malformed, truncated or of another schema
  * version), failed log appends. */
 int csr_cache_info(csr_context_t ctx, int64_t* entries, int64_t* skipped_lines, int64_t* io_errors);

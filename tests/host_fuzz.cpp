@@ -43,7 +43,7 @@ static csr_problem_t random_problem()
     static const int64_t widths[] = {-3, 0, 1, 2, 3, 4, 5, 8, 16, 32, 64, 100, 128, 512, 602, 1024, 4096, 4097};
     csr_problem_t p;
     std::memset(&p, 0, sizeof p);
-    p.op = (int32_t)(next() % 8);  // includes invalid ops 0 and 7
+    p.op = (int32_t)(next() % 9);  // includes invalid ops 0 and 8
     p.dtype = (int32_t)(next() % 3);
     p.n_rows = pick(sizes, 11);
     p.n_cols = pick(sizes, 11);
@@ -58,6 +58,7 @@ static csr_problem_t random_problem()
     p.ld_a = pick(lds, 5);
     p.ld_b = pick(lds, 5);
     p.ld_out = pick(lds, 5);
+    p.ld_c = pick(lds, 5);
     auto ptr = [&]() -> void* {
         static const uintptr_t bases[] = {0, 0x1000, 0x1004, 0x1008, 0x100000, 0x100010};
         return reinterpret_cast<void*>(bases[next() % 6]);
@@ -68,13 +69,17 @@ static csr_problem_t random_problem()
     p.b = ptr();
     p.c = ptr();
     p.out = ptr();
+    p.probs = (next() % 3 == 0) ? static_cast<float*>(ptr()) : nullptr;
+    p.probs_stride = (int64_t)(next() % 4) - 1;
     const float scales[] = {1.f, 0.125f, -2.f, 0.f, INFINITY, NAN};
     p.scale = scales[next() % 6];
     if (next() % 2) {
         // mostly well-formed: the op's dtype, positive sizes, natural strides
         // and aligned operands, with any width
-        p.op = 1 + (int32_t)(next() % 6);
-        p.dtype = p.op == CSR_OP_MHA ? CSR_DTYPE_BF16 : CSR_DTYPE_F32;
+        p.op = 1 + (int32_t)(next() % 7);
+        const bool lane_group = p.op == CSR_OP_SPMM || p.op == CSR_OP_SDDMM || p.op == CSR_OP_ATTENTION ||
+                                p.op == CSR_OP_ATTENTION_QK;
+        p.dtype = (p.op == CSR_OP_MHA || (lane_group && next() % 3 == 0)) ? CSR_DTYPE_BF16 : CSR_DTYPE_F32;
         p.n_rows = 1 + (int64_t)(next() % 3000000);
         p.n_cols = 1 + (int64_t)(next() % 3000000);
         p.nnz = (int64_t)(next() % 120000000);
@@ -84,9 +89,10 @@ static csr_problem_t random_problem()
             p.head_dim = dims[next() % 7];
             p.width = (int64_t)p.heads * p.head_dim;
         } else {
-            p.width = 1 + (int64_t)(next() % 4096);
+            p.width = 1 + (int64_t)(next() % (p.op == CSR_OP_ATTENTION_QK ? 1024 : 4096));
+            if (p.dtype == CSR_DTYPE_BF16) p.width += p.width % 2;
         }
-        p.ld_a = p.ld_b = p.ld_out = p.width + (int64_t)(next() % 3);
+        p.ld_a = p.ld_b = p.ld_c = p.ld_out = p.width + (int64_t)(next() % 3);
         static const uintptr_t good[] = {0x100000, 0x100004, 0x100008, 0x100010};
         p.row_ptr = reinterpret_cast<const int32_t*>(good[next() % 4]);
         p.col_idx = reinterpret_cast<const int32_t*>(good[next() % 4]);
@@ -94,6 +100,9 @@ static csr_problem_t random_problem()
         p.b = reinterpret_cast<const void*>(good[next() % 4]);
         p.c = reinterpret_cast<const void*>(good[next() % 4]);
         p.out = reinterpret_cast<void*>(good[next() % 4]);
+        p.probs = (p.op == CSR_OP_ATTENTION || p.op == CSR_OP_ATTENTION_QK) && next() % 2
+                      ? reinterpret_cast<float*>(good[next() % 4]) : nullptr;
+        p.probs_stride = 1;
         p.scale = 0.125f;
     }
     return p;

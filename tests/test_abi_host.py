@@ -156,6 +156,49 @@ def test_default_layout_bf16(F, ld, ptr, vec, W, nv):
     assert all(not (c.flags & _ffi.SCHED_WIDE) for c in csa.candidates(p, [0] * 66 + [100]))
 
 
+def test_attention_qk_and_probs_rules():
+    """One head of an attention from queries and keys (a = Q, b = K, c = V):
+    widths up to 1024, every leading dimension at least the width, the
+    widest access all of Q, K, V and out allow; probabilities only on the
+    attention ops, 4-byte aligned."""
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+
+    def qk(width=64, ld=64, ld_c=None, ptr=0x1000, dtype=_ffi.DTYPE_F32):
+        p = problem(_ffi.OP_ATTENTION_QK, width=width, ld=ld, ptr=ptr)
+        p.ld_c = ld if ld_c is None else ld_c
+        p.dtype = dtype
+        return p
+
+    def rc(p):
+        return lib.csr_workspace_size(None, ctypes.byref(p), None, ctypes.byref(n))
+
+    assert rc(qk()) == 0
+    assert rc(qk(width=1024, ld=1024)) == 0
+    assert rc(qk(width=1025, ld=1025)) == -2
+    assert rc(qk(ld_c=32)) == -2                 # V's leading dimension below the width
+    assert rc(qk(dtype=_ffi.DTYPE_BF16)) == 0
+    assert rc(qk(width=63, ld=64, dtype=_ffi.DTYPE_BF16)) == -2
+    p = qk()
+    p.c = 0x1002
+    assert rc(p) == -4                           # V misaligned
+    p = qk(ld=66, ld_c=64)
+    assert csa.default_schedule(p).vec == 2      # Q and K rows only 8-byte aligned
+    s = csa.default_schedule(qk())
+    assert (s.vec, s.group_lanes, s.passes) == (4, 16, 1)
+    assert all(c.mapping != _ffi.MAP_SEGSCAN and not c.flags for c in csa.candidates(qk(), [0] * 66 + [100]))
+    for op, ok in ((_ffi.OP_ATTENTION, 0), (_ffi.OP_ATTENTION_QK, 0), (_ffi.OP_SPMM, -2), (_ffi.OP_SDDMM, -2)):
+        p = qk() if op == _ffi.OP_ATTENTION_QK else problem(op)
+        p.probs = 0x2000
+        assert rc(p) == ok, op
+    p = problem(_ffi.OP_ATTENTION)
+    p.probs = 0x2002
+    assert rc(p) == -4
+    p = problem(_ffi.OP_MHA, width=512, heads=8, head_dim=64)
+    p.probs, p.probs_stride = 0x2000, 8
+    assert rc(p) == -2                           # the multi-head layout is fixed: [nnz, heads]
+
+
 def test_workspace_layout_sizes():
     # merge path: 1 KiB head, coords, slot rows, (max, sum) pieces, value pieces
     def up(v):

@@ -227,14 +227,29 @@ def test_c3_attention_scores_full():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("fused", ["single", True, False])
 def test_c3_attention_chain_full(fused):
+    """The same attention from Q, K, V (width 64, scale 1/8) three ways: in one
+    pass (scores formed in registers, probabilities written too), as SDDMM then
+    the fused softmax-aggregation, and as SDDMM, row softmax and SpMM."""
     csr, Q, K, V = _c3_qkv()
     rp, ci = pattern_dev("c3")
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
-    ss = selected("sddmm", rp, ci, Qd, Kd)
-    S = csa.sddmm(rp, ci, Qd, Kd, schedule=ss)
-    if fused:
+    probs = None
+    if fused == "single":
+        sq = selected("attention_qk", rp, ci, Qd, Kd, Vd, scale=0.125)
+        P = torch.empty(csr.nnz, device="cuda")
+        out = csa.attention_qk(rp, ci, Qd, Kd, Vd, scale=0.125, probs=P, schedule=sq)
+        probs = P.cpu().numpy()
+        del P
+        label = f"one pass {sq}"
+        S = None
+    else:
+        ss = selected("sddmm", rp, ci, Qd, Kd)
+        S = csa.sddmm(rp, ci, Qd, Kd, schedule=ss)
+    if fused == "single":
+        pass
+    elif fused:
         sa = selected("attention", rp, ci, S, Vd, scale=0.125)
         out = csa.attention(rp, ci, S, Vd, scale=0.125, schedule=sa)
         label = f"sddmm {ss}, attention {sa}"
@@ -246,13 +261,20 @@ def test_c3_attention_chain_full(fused):
         out = csa.spmm(rp, ci, P, Vd, schedule=sm)
         label = f"sddmm {ss}, softmax {sp}, spmm {sm}"
     out = out.cpu().numpy()
+    worst_p = [0.0]
 
     def block(r0, r1):
-        ref, mag, _ = oracle.attention_qk(csr.row_ptr, csr.col_idx, Q, K, V, 0.125, r0, r1, threads=THREADS)
+        ref, mag, pr = oracle.attention_qk(csr.row_ptr, csr.col_idx, Q, K, V, 0.125, r0, r1, threads=THREADS,
+                                           want_probs=probs is not None)
+        if probs is not None:
+            got = probs[csr.row_ptr[r0]:csr.row_ptr[r1]].astype(np.float64)
+            worst_p[0] = max(worst_p[0], float(np.max(np.abs(got - pr[:, 0]) / pr[:, 0])))
         return ref[:, 0], mag[:, 0]
 
     e = compare_all_rows(out, block, csr.row_ptr, 64, TOL_F32, f"c3 chain fused={fused}")
-    print(f"c3 chain fused={fused}: {label} max err {e:.2e} over all {csr.n_rows} rows")
+    assert worst_p[0] <= 1e-5, f"probabilities: {worst_p[0]:.2e}"
+    print(f"c3 chain fused={fused}: {label} max err {e:.2e}"
+          + (f", probabilities {worst_p[0]:.2e}" if probs is not None else "") + f" over all {csr.n_rows} rows")
 
 
 # ---------------------------------------------------------------------------
