@@ -1440,7 +1440,8 @@ static void plan_sizes(const csr_problem_t& p, const int64_t* hist, size_t* plan
         q.row_ptr = nullptr;
         q.ld_out = p.width;
         if (p.op == CSR_OP_SPMM) q.out = reinterpret_cast<void*>(csrh::kAlign);  // partial rows, 256-byte aligned
-        const size_t inner = up256(auto_workspace(q)) + (p.op == CSR_OP_SPMM ? (size_t)cap * p.width * 4 : 0);
+        const size_t inner = up256(auto_workspace(q)) +
+                             (p.op == CSR_OP_SPMM ? up256((size_t)cap * p.width * 4) + up256((size_t)p.nnz * 4) : 0);
         ws = std::max(ws, std::max(up256(build), inner));
     }
     *plan_bytes = mem;
@@ -1674,7 +1675,11 @@ int materialize_plan(PlanBuild& b, const csrh::PlanChoice& c, uint64_t sig, doub
         size_t inner = 0;
         rc = hybrid_inner_bytes(b.ctx, hc.p, &c.sched, &inner);
         if (rc != CSR_OK) return rc;
-        r.workspace_bytes = inner + (b.p.op == CSR_OP_SPMM ? (size_t)b.h.n_seg * b.p.width * 4 : 0);
+        // SpMM: the partial rows, then room for the values of a call that
+        // passes its own (moved into format order there, for that call only)
+        r.workspace_bytes = inner + (b.p.op == CSR_OP_SPMM ? up256((size_t)b.h.n_seg * b.p.width * 4) +
+                                                                  up256((size_t)b.p.nnz * 4)
+                                                            : 0);
     }
     *plan = r;
     return CSR_OK;
@@ -1792,10 +1797,19 @@ int csr_plan_spmm(csr_context_t ctx, const csr_plan_t* plan, const float* vals, 
         if (plan->width < 1 || ldy < plan->width || ldy >= ((int64_t)1 << 30))
             return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");
         if (!plan->vals) return set_err(ctx, CSR_ERR_NULL, "the plan has no value array");
-        if (vals) CSR_HIP(ctx, csrk::launch_gather_values(plan->fmt.perm, vals, plan->vals, plan->nnz, st));
+        if (!workspace || ws_bytes < plan->workspace_bytes || (uintptr_t)workspace % csrh::kAlign)
+            return set_err(ctx, CSR_ERR_WORKSPACE, "workspace NULL, unaligned or below the plan's workspace_bytes");
+        // this call's own values go into format order at the end of the workspace
+        const float* fv = plan->vals;
+        if (vals) {
+            float* tmp = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->workspace_bytes -
+                                                  up256((size_t)plan->nnz * 4));
+            CSR_HIP(ctx, csrk::launch_gather_values(plan->fmt.perm, vals, tmp, plan->nnz, st));
+            fv = tmp;
+        }
         HybridCall c;
-        rc = hybrid_call(ctx, &plan->fmt, CSR_OP_SPMM, plan->width, plan->dtype, plan->vals, 0, X, ldx, &plan->sched,
-                         workspace, ws_bytes, stream, nullptr, &c);
+        rc = hybrid_call(ctx, &plan->fmt, CSR_OP_SPMM, plan->width, plan->dtype, fv, 0, X, ldx, &plan->sched,
+                         workspace, plan->workspace_bytes - up256((size_t)plan->nnz * 4), stream, nullptr, &c);
         if (rc != CSR_OK) return rc;
         return hybrid_run(ctx, &plan->fmt, c, &plan->sched, Y, ldy);
     } catch (...) {

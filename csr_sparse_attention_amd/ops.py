@@ -944,9 +944,8 @@ def plan(op: str, row_ptr, col_idx, *operands, mode: str = "auto", out=None, ctx
 
 def plan_spmm(pl: Plan, X, *, vals=None, out=None, ctx: Optional[Context] = None,
               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = A X with a plan of 'spmm'; ``vals`` (original entry order) replaces
-    the plan's values from this call on (over the format they are first
-    moved into the plan's copy)."""
+    """Y = A X with a plan of 'spmm'; ``vals`` (original entry order), when
+    given, are this call's values instead of the plan's (for this call only)."""
     if pl.desc.op != _ffi.OP_SPMM:
         raise ValueError("not a plan of 'spmm'")
     _rows(X, "X", pl.desc.n_cols, pl.desc.width, dtype=(torch.float32, torch.bfloat16))
@@ -955,8 +954,6 @@ def plan_spmm(pl: Plan, X, *, vals=None, out=None, ctx: Optional[Context] = None
         raise TypeError("X's dtype is not the plan's")
     if vals is not None:
         _entries(vals, "vals", pl.desc.nnz)
-        if pl.parts == 1:
-            pl._keep = pl._keep + (vals,)
     out = _out_rows(out, pl.desc.n_rows, pl.desc.width, X.device)
     ldy = _dense(out, "out", torch.float32)
     ctx = ctx or default_context(X.device.index)

@@ -561,9 +561,10 @@ int csr_plan_create(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, vo
 /* Y = A X with a plan of op CSR_OP_SPMM: X [n_cols, ldx] of the plan's dtype,
  * Y fp32 [n_rows, ldy], with the alignment and leading-dimension class the
  * plan was made for (CSR_ERR_SCHEDULE otherwise).  vals: NULL uses the
- * plan's values; otherwise new values in original order (over the format
- * they are first moved into the plan's copy, in stream order).  No
- * synchronisation; a workspace of plan->workspace_bytes. */
+ * plan's values (those it was created with); otherwise this call's values
+ * in original order, for this call only (over the format they are moved
+ * into format order inside the workspace first).  No synchronisation; a
+ * workspace of plan->workspace_bytes. */
 int csr_plan_spmm(csr_context_t ctx, const csr_plan_t* plan, const float* vals, const void* X, int64_t ldx,
                   float* Y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
 

@@ -11,9 +11,11 @@
 // line parses back to the schedule it was written from.  Malformed cache
 // lines and arbitrary problem / schedule fields must be rejected without a
 // crash.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 #include <string>
 
 #include "../csr_sparse_attention_amd/csrc/host.h"
@@ -196,7 +198,61 @@ int main(int argc, char** argv)
             CHECK(w >= csrh::kHeadBytes && w % csrh::kAlign == 0, "bad workspace for an accepted schedule\n");
         }
     }
-    std::printf("iterations %d accepted problems %d planned formats %d corrupted lines parsed %d failures %d\n", iters,
-                accepted, planned, parsed, failures);
+    // the plan memory bound on the format's segment count: a random pattern,
+    // its degree histogram, the segments the construction makes (one per
+    // nonempty row kept whole, else one per distinct (row, column part)),
+    // never above segment_bound
+    int64_t seg_checks = 0;
+    for (int it = 0; it < iters / 50; ++it) {
+        const int64_t n_rows = 1 + (int64_t)(next() % 300), n_cols = 1 + (int64_t)(next() % 5000);
+        std::vector<int64_t> deg(n_rows);
+        int64_t nnz = 0;
+        for (auto& d : deg) {
+            const int kind = (int)(next() % 4);
+            d = kind == 0 ? 0 : (kind == 1 ? (int64_t)(next() % 8) : (int64_t)(next() % (uint64_t)(n_cols + 1)));
+            nnz += d;
+        }
+        int64_t h[csrh::kHistInts] = {0};
+        for (int64_t d : deg) {
+            int b = 0;
+            while (b < 32 && ((int64_t)1 << b) <= d) ++b;  // d in [2^(b-1), 2^b)
+            h[b] += 1;
+            h[33 + b] += d;
+            h[66] = std::max(h[66], d);
+        }
+        csr_problem_t p;
+        std::memset(&p, 0, sizeof p);
+        p.op = CSR_OP_SPMM;
+        p.n_rows = n_rows;
+        p.n_cols = n_cols;
+        p.nnz = nnz;
+        p.width = 1;
+        const int P = 2 << (next() % 8);
+        const int T = (next() % 3 == 0) ? 0 : 1 << (next() % 12);
+        const int64_t part_cols = (n_cols + P - 1) / P;
+        int64_t segs = 0;
+        std::vector<char> seen(P);
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (deg[r] == 0) continue;
+            if (deg[r] < T) {
+                ++segs;
+                continue;
+            }
+            std::fill(seen.begin(), seen.end(), 0);
+            for (int64_t k = 0; k < deg[r]; ++k) {
+                const int64_t part = std::min<int64_t>((int64_t)(next() % (uint64_t)n_cols) / part_cols, P - 1);
+                if (!seen[part]) {
+                    seen[part] = 1;
+                    ++segs;
+                }
+            }
+        }
+        const int64_t bound = csrh::segment_bound(p, h, P, T), loose = csrh::segment_bound(p, nullptr, P, T);
+        CHECK(segs <= bound && bound <= loose, "segments %lld above the bound %lld (loose %lld) P %d T %d\n",
+              (long long)segs, (long long)bound, (long long)loose, P, T);
+        ++seg_checks;
+    }
+    std::printf("iterations %d accepted problems %d planned formats %d corrupted lines parsed %d segment bounds %lld "
+                "failures %d\n", iters, accepted, planned, parsed, (long long)seg_checks, failures);
     return failures ? 1 : 0;
 }
