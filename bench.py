@@ -76,24 +76,27 @@ def compulsory_bytes(c, torch):
     written and read once, the format's column indices and values, the
     segment and row-segment offsets, and the output.  SDDMM over the format:
     V once, each segment's U row, the indices and the permuted output."""
-    if c.fmt is None or c.op not in ("spmm", "sddmm"):
+    pl = c.plan
+    if pl is None or pl.parts == 1:
         return c.bytes
-    h = c.fmt["h"]
     rp = c.args[0]
     deg = (rp[1:] - rp[:-1]).long()
-    T = c.fmt["whole_below"]
+    T = pl.whole_below
     F = c.width
     n_cols = c.args[3].shape[0]
-    seg_idx = 4 * (h.n_seg + 1) + 4 * h.n_seg + 4 * (c.n_rows + 1)
+    n_seg = pl.n_seg
+    seg_idx = 4 * (n_seg + 1) + 4 * n_seg + 4 * (c.n_rows + 1)
     if c.op == "spmm":
         whole_nnz = int(deg[deg < T].sum().item()) if T > 0 else 0
-        return (n_cols * F * 4 + whole_nnz * F * 4 + 2 * h.n_seg * F * 4 + 8 * c.nnz + seg_idx
+        return (n_cols * F * 4 + whole_nnz * F * 4 + 2 * n_seg * F * 4 + 8 * c.nnz + seg_idx
                 + c.n_rows * F * 4)
-    return n_cols * F * 4 + h.n_seg * F * 4 + 12 * c.nnz + seg_idx
+    return n_cols * F * 4 + n_seg * F * 4 + 12 * c.nnz + seg_idx
 
 
 class Call:
-    """One library call of the step with its operands and replayed schedule."""
+    """One library call of the step with its operands.  SpMM and SDDMM run
+    through a plan (the library's joint choice of layout and schedule);
+    the other calls replay their selected schedule."""
 
     def __init__(self, name, op, fn, args, kwargs, n_rows, nnz, width, oracle_fn, esize=4):
         self.name, self.op, self.fn, self.args, self.kwargs = name, op, fn, args, kwargs
@@ -102,46 +105,73 @@ class Call:
         self.oracle_fn = oracle_fn
         self.schedule = None
         self.times = []
-        self.fmt = None  # column-part segment format of the call, when its rule proposes one
+        self.plan = None  # csa.Plan of an SpMM / SDDMM call
+        self.csa = None
 
     def run(self, schedule=None):
+        """The call as the step makes it (through its plan, when it has one),
+        or with ``schedule`` on the plain CSR pattern."""
+        if schedule is None and self.plan is not None:
+            out = self.kwargs.get("out")
+            if self.op == "spmm":
+                return self.csa.plan_spmm(self.plan, self.args[3], out=out)
+            return self.csa.plan_sddmm(self.plan, self.args[2], self.args[3], out=out)
         s = schedule if schedule is not None else self.schedule
-        if self.fmt is not None:
-            return self.fmt["run"](s)
         return self.fn(*self.args, schedule=s, **self.kwargs)
 
     def select(self, csa, mode="auto"):
-        if self.fmt is not None:
-            return self.fmt["select"](mode)
         sel_args = (self.args[0], None) + tuple(self.args[1:]) if self.op.startswith("row_softmax") else self.args
         kw = {"scale": self.kwargs["scale"]} if "scale" in self.kwargs else {}
         return csa.select(self.op, *sel_args, mode=mode, **kw)
 
+    def label(self):
+        """The call's layout and schedule as one dict."""
+        if self.plan is not None:
+            return {"format_parts": self.plan.parts, "whole_below": self.plan.whole_below,
+                    **self.plan.schedule.as_dict()}
+        return {"format_parts": 1, **self.schedule.as_dict()}
 
-def format_plan(csa, torch, c, P, cache, whole_below=0):
-    """Builds (once per pattern and part count) the column-part segment format
-    of call c and the closures that run and select over it; SpMM edge values
-    are moved into the format's order once, here (they are constant across
-    steps).  Returns the plan dict with the one-time costs in ms."""
+
+def make_plan(c, csa, torch):
+    """Plans call c through the library (csr_plan_create, mode auto): the
+    first creation runs the histogram, the cost model and the micro-probes
+    over the plain pattern and the format's candidate part counts and caches
+    the choice; a second creation replays it (histogram, cache lookup and
+    the chosen format's construction).  The replayed plan is kept.  Returns
+    the one-time costs in ms."""
+    operands = c.args[2:4]
+    out = c.kwargs.get("out")
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    first = csa.plan(c.op, c.args[0], c.args[1], *operands, out=out)
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t) * 1e3
+    probe_ms = first.desc.probe_ms
+    del first
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    c.plan = csa.plan(c.op, c.args[0], c.args[1], *operands, out=out, mode="replay")
+    torch.cuda.synchronize()
+    c.csa = csa
+    return {"plan_create_ms": round(first_ms, 3), "plan_probe_ms": round(probe_ms, 3),
+            "plan_replay_ms": round((time.perf_counter() - t) * 1e3, 3), "signature": f"{c.plan.signature:016x}"}
+
+
+def format_candidate(csa, torch, c, P, cache, whole_below=0):
+    """The column-part segment format of call c at P parts and whole-row
+    threshold whole_below, built once per pattern (SpMM values moved into the
+    format's order), with closures that run and select over it: the
+    candidates a plan weighs, rebuilt here so the study can time each."""
     rp, ci = c.args[0], c.args[1]
-    dense = c.args[3] if c.op == "spmm" else c.args[3]
+    dense = c.args[3]
     key = (rp.data_ptr(), ci.data_ptr(), P, whole_below)
     if key not in cache:
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        h = csa.hybrid_format(rp, ci, dense.shape[0], P, whole_below=whole_below)
-        torch.cuda.synchronize()
-        cache[key] = (h, (time.perf_counter() - t) * 1e3)
-    h, build_ms = cache[key]
+        cache[key] = csa.hybrid_format(rp, ci, dense.shape[0], P, whole_below=whole_below)
+    h = cache[key]
     out = c.kwargs.get("out")
-    values_ms = 0.0
     if c.op == "spmm":
         vals, X = c.args[2], c.args[3]
-        torch.cuda.synchronize()
-        t = time.perf_counter()
         hv = None if vals is None else csa.hybrid_values(h, vals)
-        torch.cuda.synchronize()
-        values_ms = (time.perf_counter() - t) * 1e3
         run = lambda s: csa.hybrid_spmm(h, hv, X, out=out, schedule=s)  # noqa: E731
         select = lambda mode: csa.hybrid_select(h, "spmm", hv, X, mode=mode)  # noqa: E731
         a, b = hv, X
@@ -150,25 +180,7 @@ def format_plan(csa, torch, c, P, cache, whole_below=0):
         run = lambda s: csa.hybrid_sddmm(h, U, V, out=out, schedule=s)  # noqa: E731
         select = lambda mode: csa.hybrid_select(h, "sddmm", U, V, mode=mode, out=out)  # noqa: E731
         a, b = U, V
-    return {"h": h, "parts": P, "whole_below": whole_below, "run": run, "select": select, "operands": (a, b),
-            "build_ms": build_ms, "values_ms": values_ms}
-
-
-def apply_formats(calls, csa, torch):
-    """Per SpMM / SDDMM call, asks the library's cost model for the plan of
-    the column-part segment format (csr_hybrid_plan: parts, 1 = plain CSR,
-    and the whole-row threshold) and plans the call over the format when it
-    proposes one."""
-    cache = {}
-    for c in calls:
-        if c.op not in ("spmm", "sddmm"):
-            continue
-        p, _ = csa.make_problem(c.op, *c.args, out=c.kwargs.get("out"))
-        counts, sums, mx = csa.degree_histogram(c.args[0])
-        P, T = csa.hybrid_plan(p, counts + sums + [mx])
-        if P > 1:
-            c.fmt = format_plan(csa, torch, c, P, cache, T)
-    return cache
+    return {"h": h, "parts": P, "whole_below": whole_below, "run": run, "select": select, "operands": (a, b)}
 
 
 def build_workload(name, torch, csa):
@@ -357,7 +369,7 @@ def stream_bandwidth(torch, gib=4):
     return res
 
 
-def committed_traffic(config, call, schedule):
+def committed_traffic(config, call):
     """HBM traffic per launch of the dominant kernel from the committed counter
     summary (profiles/traffic.json), or None when the kernel's sources or the
     selected schedule differ from those the counters were taken with."""
@@ -370,9 +382,8 @@ def committed_traffic(config, call, schedule):
         recs = json.load(f).get(config) or []
     if isinstance(recs, dict):
         recs = [recs]
-    sd = schedule.as_dict()
-    parts = call.fmt["parts"] if call.fmt is not None else 1
-    whole = call.fmt["whole_below"] if call.fmt is not None else 0
+    sd = call.label()
+    parts, whole = sd.pop("format_parts"), sd.pop("whole_below", 0)
     for rec in recs:
         if rec.get("call") != call.name or any(sd.get(k) != v for k, v in rec["schedule"].items()):
             continue
@@ -387,17 +398,21 @@ def committed_traffic(config, call, schedule):
     return None
 
 
-def selector_study(calls, torch, csa, formats, rounds=5, per_round=3):
+def selector_study(calls, torch, csa, rounds=5, per_round=3):
     """Times every candidate of each call under one protocol and compares the
-    selected one with the best: the candidate schedules of the plain CSR
-    problem, for a call planned over the column-part segment format also the
-    candidate schedules of its segment problem, and for SpMM / SDDMM the
-    format at other part counts (half and twice the rule's choice, or 4 and
-    16 parts when the rule chose the plain path), each with its own selected
-    schedule.  The distinct candidates run in interleaved rounds (so clock and
-    thermal drift bias none of them), `per_round` HIP-event timed runs each,
-    and the median over all rounds is kept."""
+    library's pick with the best: every candidate schedule of the plain CSR
+    problem; for SpMM / SDDMM also the format at each part count a plan
+    weighs (the cost model's part count and threshold, half and twice that
+    count, the same count with no whole rows; or 4 and 16 parts when the
+    model keeps the plain pattern), each with its own selected schedule, and
+    every candidate schedule of the format the plan chose.  The library's
+    pick is the call as the step makes it (through its plan for SpMM /
+    SDDMM, the selected schedule otherwise).  The distinct candidates run in
+    interleaved rounds (so clock and thermal drift bias none of them),
+    `per_round` HIP-event timed runs each, and the median over all rounds is
+    kept."""
     stream = torch.cuda.current_stream()
+    formats = {}
 
     def timed(run):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -415,31 +430,32 @@ def selector_study(calls, torch, csa, formats, rounds=5, per_round=3):
         args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
         p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale)
         counts, sums, mx = csa.degree_histogram(c.args[0])
+        hist = counts + sums + [mx]
         cands = [({"format_parts": 1, **s.as_dict()}, lambda s=s: c.fn(*c.args, schedule=s, **c.kwargs))
-                 for s in csa.candidates(p, counts + sums + [mx])]
-        if c.fmt is not None:
-            h = c.fmt["h"]
-            hp = csa.hybrid_problem(h, c.op, *c.fmt["operands"])
-            sc, ss, smx = csa.degree_histogram(h.seg_ptr)
-            cands += [({"format_parts": c.fmt["parts"], "whole_below": c.fmt["whole_below"], **s.as_dict()},
-                       lambda s=s: c.fmt["run"](s)) for s in csa.candidates(hp, sc + ss + [smx])]
-            selected = {"format_parts": c.fmt["parts"], "whole_below": c.fmt["whole_below"], **c.schedule.as_dict()}
-        else:
-            selected = {"format_parts": 1, **c.schedule.as_dict()}
-        n_cand = len(cands)
-        if selected not in [lab for lab, _ in cands]:
-            cands.append((selected, lambda: c.run()))
+                 for s in csa.candidates(p, hist)]
         if c.op in ("spmm", "sddmm"):
-            P0 = c.fmt["parts"] if c.fmt is not None else 1
-            T0 = c.fmt["whole_below"] if c.fmt is not None else 0
-            alts = [(P0 // 2, T0), (P0 * 2, T0)] + ([(P0, 0)] if T0 > 0 else []) if P0 > 1 else [(4, 0), (16, 0)]
-            for P, T in alts:
-                if 2 <= P <= 256:
-                    plan = format_plan(csa, torch, c, P, formats, T)
-                    s_alt, _ = plan["select"]("auto")
+            P0, T0 = csa.hybrid_plan(p, hist)
+            fmts = ([(P0, T0), (P0 // 2, T0), (P0 * 2, T0)] + ([(P0, 0)] if T0 > 0 else [])) if P0 > 1 \
+                else [(4, 0), (16, 0)]
+            chosen = (c.plan.parts, c.plan.whole_below) if c.plan is not None and c.plan.parts > 1 else None
+            for P, T in fmts:
+                if not 2 <= P <= 256:
+                    continue
+                f = format_candidate(csa, torch, c, P, formats, T)
+                if (P, T) == chosen:
+                    hp = csa.hybrid_problem(f["h"], c.op, *f["operands"])
+                    sc, ss, smx = csa.degree_histogram(f["h"].seg_ptr)
+                    cands += [({"format_parts": P, "whole_below": T, **s.as_dict()},
+                               lambda f=f, s=s: f["run"](s)) for s in csa.candidates(hp, sc + ss + [smx])]
+                else:
+                    s_alt, _ = f["select"]("auto")
                     cands.append(({"format_parts": P, "whole_below": T, **s_alt.as_dict()},
-                                  lambda plan=plan, s=s_alt: plan["run"](s)))
-                    n_cand += 1
+                                  lambda f=f, s=s_alt: f["run"](s)))
+        n_cand = len(cands)
+        selected = c.label()
+        # the pick, run as the step runs it (its own entry when a fixed
+        # candidate has the same layout and schedule: the two are one kernel)
+        cands = [(lab, run) for lab, run in cands if lab != selected] + [(selected, lambda: c.run())]
         labels = [lab for lab, _ in cands]
         times = [[] for _ in cands]
         for _, run in cands:
@@ -449,11 +465,12 @@ def selector_study(calls, torch, csa, formats, rounds=5, per_round=3):
                 for _ in range(per_round):
                     times[i].append(timed(run))
         med = [float(np.median(t)) for t in times]
-        sel = med[labels.index(selected)]
+        sel = med[-1]
         best = int(np.argmin(med))
         out[c.name] = {"selected_ms": round(sel, 4), "best_fixed_ms": round(med[best], 4),
                        "selected": selected, "best_fixed": labels[best], "n_candidates": n_cand,
                        "selected_over_best": round(sel / med[best], 4),
+                       "picked_by": "csr_plan_create (auto)" if c.plan is not None else "csr_select (auto)",
                        "candidate_ms": [round(t, 4) for t in med],
                        "candidate_format_parts": [lab["format_parts"] for lab in labels]}
     return out
@@ -694,7 +711,8 @@ def main():
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of every call")
     ap.add_argument("--no-format", action="store_true",
-                    help="run every call on the plain CSR pattern (no column-part segment format)")
+                    help="run SpMM / SDDMM with the selector on the plain CSR pattern instead of through a plan "
+                         "(no column-part segment format)")
     ap.add_argument("--vendor", action="store_true",
                     help="also time the SpMM / SDDMM calls with rocSPARSE (a measured comparison, not a dispatch)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -722,20 +740,23 @@ def main():
     calls, gen_s = build_workload(args.config, torch, csa)
     check_shapes(calls)
     print(f"[bench] workload {args.config}: {len(calls)} calls, generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
-    formats = {} if args.no_format else apply_formats(calls, csa, torch)
-    for c in calls:
-        if c.fmt is not None:
-            print(f"[bench] {c.name}: column-part segment format, {c.fmt['parts']} parts, rows under "
-                  f"{c.fmt['whole_below']} entries whole, {c.fmt['h'].n_seg} segments (built in "
-                  f"{c.fmt['build_ms']:.1f} ms)", file=sys.stderr, flush=True)
-
-    # selection (histogram, signature, cost model, probes) once per call
+    # SpMM / SDDMM: one plan per call (layout and schedule chosen together
+    # by the library); the other calls: the selector (histogram, signature,
+    # cost model, probes) once per call
     sel = {}
     for c in calls:
-        torch.cuda.synchronize()
-        t = time.perf_counter()
         if c.op == "gather":  # no schedule
             continue
+        if c.op in ("spmm", "sddmm") and not args.no_format:
+            info = make_plan(c, csa, torch)
+            pl = c.plan
+            sel[c.name] = {"plan": {"parts": pl.parts, "whole_below": pl.whole_below, "segments": pl.n_seg,
+                                    **info}, "schedule": pl.schedule.as_dict()}
+            print(f"[bench] {c.name}: {pl} created in {info['plan_create_ms']:.1f} ms, replayed in "
+                  f"{info['plan_replay_ms']:.1f} ms", file=sys.stderr, flush=True)
+            continue
+        torch.cuda.synchronize()
+        t = time.perf_counter()
         s, sig = c.select(csa)
         torch.cuda.synchronize()
         first = time.perf_counter() - t
@@ -747,11 +768,6 @@ def main():
         c.schedule = s
         sel[c.name] = {"schedule": s.as_dict(), "signature": f"{sig:016x}", "select_ms": round(first * 1e3, 3),
                        "replay_select_ms": round(replay * 1e3, 3)}
-        if c.fmt is not None:
-            sel[c.name]["format"] = {"parts": c.fmt["parts"], "whole_below": c.fmt["whole_below"],
-                                     "segments": c.fmt["h"].n_seg,
-                                     "build_ms": round(c.fmt["build_ms"], 3),
-                                     "values_to_format_order_ms": round(c.fmt["values_ms"], 3)}
         print(f"[bench] {c.name}: {s} select {first * 1e3:.1f} ms", file=sys.stderr, flush=True)
 
     dom = max(calls, key=lambda c: c.bytes)
@@ -798,7 +814,7 @@ def main():
     dom_ms = float(np.mean(per_call[dom.name]))
     gather_rate = dom.bytes / (dom_ms * 1e-3) / 1e9
     model = compulsory_bytes(dom, torch)
-    traffic = committed_traffic(args.config, dom, dom.schedule)
+    traffic = committed_traffic(args.config, dom)
     # HBM rate of the dominant call: counted bytes (FETCH_SIZE + WRITE_SIZE of
     # its kernels, scaled by the counters' reading of a copy of known size)
     # over the live HIP-event time; the compulsory-traffic model stands in
@@ -861,7 +877,7 @@ def main():
     result["roofline"]["frac_of_measured_copy"] = round(achieved / stream_ref["copy_GB_s"], 4)
     if not args.no_study:
         print("[bench] selector study: every candidate schedule of every call", file=sys.stderr, flush=True)
-        result["selector"] = selector_study(calls, torch, csa, formats)
+        result["selector"] = selector_study(calls, torch, csa)
         result["selector_worst_ratio"] = max(v["selected_over_best"] for v in result["selector"].values())
     if args.vendor:
         print("[bench] vendor comparison (rocSPARSE)", file=sys.stderr, flush=True)

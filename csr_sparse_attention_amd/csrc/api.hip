@@ -555,9 +555,9 @@ int select_locked(csr_context_t ctx, const csr_problem_t& p, uint32_t mode, csr_
         return CSR_OK;
     }
     const int max_probe = std::max(1, env_int("CSRSA_PROBE_CANDIDATES", 6));
-    std::vector<size_t> probe_set;
-    for (size_t k = 0; k < order.size() && (int)probe_set.size() < max_probe; ++k) probe_set.push_back(order[k].second);
-    std::sort(probe_set.begin(), probe_set.end());  // fixed candidate order for tie-breaking
+    std::vector<double> est(cand.size());
+    for (const auto& o : order) est[o.second] = o.first;
+    const std::vector<size_t> probe_set = csrh::probe_subset(cand, est, max_probe);  // ascending: ties go low
     const std::vector<double> med = probe_all(ctx, p, cand, probe_set, st, maps);
     double best = -1.0;
     size_t best_i = 0;
@@ -1586,17 +1586,14 @@ int probe_plan(PlanBuild& b, csrh::PlanChoice* out, double* ms)
     const int max_probe = std::max(1, env_int("CSRSA_PROBE_CANDIDATES", 6));
     auto top = [&](const csr_problem_t& q, const int64_t* hq, int k) {
         const std::vector<csr_schedule_t> cand = csrh::candidates(q, hq);
-        std::vector<std::pair<double, size_t>> order;
-        for (size_t i = 0; i < cand.size(); ++i) order.push_back({csrh::estimate(q, cand[i], hq, b.ctx->dev), i});
-        std::stable_sort(order.begin(), order.end(),
-                         [](const std::pair<double, size_t>& x, const std::pair<double, size_t>& y) { return x.first < y.first; });
-        std::vector<size_t> which;
-        for (size_t i = 0; i < order.size() && (int)which.size() < k; ++i) which.push_back(order[i].second);
-        std::sort(which.begin(), which.end());  // fixed candidate order for the ties
+        std::vector<double> est(cand.size());
+        for (size_t i = 0; i < cand.size(); ++i) est[i] = csrh::estimate(q, cand[i], hq, b.ctx->dev);
         std::vector<csr_schedule_t> r;
-        for (size_t i : which) r.push_back(cand[i]);
+        for (size_t i : csrh::probe_subset(cand, est, k)) r.push_back(cand[i]);
         return r;
     };
+    // first round: the plain pattern's best few schedules and, per format,
+    // its best few (one of each mapping first)
     std::vector<PlanOption> opts;
     {
         const std::vector<csr_schedule_t> cand = top(b.p, b.hist, max_probe);
@@ -1604,18 +1601,66 @@ int probe_plan(PlanBuild& b, csrh::PlanChoice* out, double* ms)
             probe_runs(b.ctx, cand.size(), [&](size_t i) { return run_schedule(b.ctx, b.p, cand[i], b.st); }, b.st);
         for (size_t i = 0; i < cand.size(); ++i) opts.push_back({1, 0, cand[i], t[i]});
     }
+    const int per_format = std::max(1, (max_probe + 1) / 2);
     for (const auto& f : csrh::plan_formats(b.p, b.hist)) {
         if (b.build(f.first, f.second) != CSR_OK) continue;  // a format that cannot be built is not a candidate
         HybridCall c;
         if (b.call(&c, nullptr) != CSR_OK) continue;
         int64_t hs[csrh::kHistInts];
         if (histogram(b.ctx, c.p, b.st, hs) != CSR_OK) continue;
-        const std::vector<csr_schedule_t> cand = top(c.p, hs, std::max(1, max_probe / 2));
+        const std::vector<csr_schedule_t> cand = top(c.p, hs, per_format);
         const std::vector<double> t = probe_runs(b.ctx, cand.size(), [&](size_t i) { return b.run(c, cand[i]); }, b.st);
         for (size_t i = 0; i < cand.size(); ++i) opts.push_back({f.first, f.second, cand[i], t[i]});
     }
+    // second round: the winning format's wider set of schedules, timed
+    // together (those of the first round again among them, so that the
+    // comparison is within one batch)
+    {
+        int wi = -1;
+        for (size_t i = 0; i < opts.size(); ++i)
+            if (opts[i].ms >= 0 && (wi < 0 || opts[i].ms < opts[wi].ms * 0.99)) wi = (int)i;
+        if (wi >= 0 && opts[wi].P > 1 && max_probe > per_format) {
+            const int P = opts[wi].P, T = opts[wi].T;
+            HybridCall c;
+            int64_t hs[csrh::kHistInts];
+            if (b.build(P, T) == CSR_OK && b.call(&c, nullptr) == CSR_OK && histogram(b.ctx, c.p, b.st, hs) == CSR_OK) {
+                const std::vector<csr_schedule_t> cand = top(c.p, hs, max_probe);
+                const std::vector<double> t =
+                    probe_runs(b.ctx, cand.size(), [&](size_t i) { return b.run(c, cand[i]); }, b.st);
+                // the other layouts' times came from another batch: scale
+                // them by the winner's ratio between the two batches
+                double ratio = 1.0;
+                for (size_t i = 0; i < cand.size(); ++i)
+                    if (t[i] > 0 && std::memcmp(&cand[i], &opts[wi].s, sizeof(csr_schedule_t)) == 0)
+                        ratio = t[i] / opts[wi].ms;
+                // the winning format's options replace its first-round ones,
+                // in the same place (plain first, then the formats in order:
+                // the order that decides ties)
+                std::vector<PlanOption> merged;
+                bool placed = false;
+                for (const auto& o : opts) {
+                    if (o.P == P && o.T == T) {
+                        if (!placed)
+                            for (size_t i = 0; i < cand.size(); ++i) merged.push_back({P, T, cand[i], t[i]});
+                        placed = true;
+                        continue;
+                    }
+                    merged.push_back(o);
+                    if (merged.back().ms >= 0) merged.back().ms *= ratio;
+                }
+                opts.swap(merged);
+            }
+        }
+    }
     b.ctx->last_error.clear();
     (void)hipGetLastError();
+    if (env_flag("CSRSA_PLAN_TRACE")) {  // every probed option on stderr, one line each
+        for (const auto& o : opts)
+            std::fprintf(stderr, "csrsa plan probe op=%d F=%lld parts=%d whole=%d map=%d vec=%d w=%d nv=%d chunk=%d "
+                                 "long=%d flags=%d ms=%.4f\n",
+                         b.p.op, (long long)b.p.width, o.P, o.T, o.s.mapping, o.s.vec, o.s.group_lanes, o.s.passes,
+                         o.s.chunk_items, o.s.long_row, o.s.flags, o.ms);
+    }
     double best = -1.0;
     size_t bi = 0;
     for (size_t i = 0; i < opts.size(); ++i) {

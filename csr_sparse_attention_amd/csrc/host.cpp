@@ -612,6 +612,33 @@ int hybrid_parts(const csr_problem_t& p, const int64_t* hist)
     return P;
 }
 
+std::vector<size_t> probe_subset(const std::vector<csr_schedule_t>& cand, const std::vector<double>& est, int k)
+{
+    std::vector<size_t> order(cand.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return est[x] < est[y]; });
+    std::vector<size_t> pick;
+    std::vector<char> taken(cand.size(), 0);
+    for (size_t i : order) {  // the best of each mapping
+        if ((int)pick.size() >= k) break;
+        bool seen = false;
+        for (size_t j : pick) seen = seen || (cand[j].mapping == cand[i].mapping && cand[j].flags == cand[i].flags);
+        if (!seen) {
+            pick.push_back(i);
+            taken[i] = 1;
+        }
+    }
+    for (size_t i : order) {  // then by estimate
+        if ((int)pick.size() >= k) break;
+        if (!taken[i]) {
+            pick.push_back(i);
+            taken[i] = 1;
+        }
+    }
+    std::sort(pick.begin(), pick.end());
+    return pick;
+}
+
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev)
 {
     uint64_t h = 0xcbf29ce484222325ull;

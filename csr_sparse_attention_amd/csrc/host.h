@@ -65,6 +65,12 @@ std::vector<csr_schedule_t> candidates(const csr_problem_t& p, const int64_t* hi
 // on problem p with degree histogram hist.
 double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* hist, const DeviceInfo& dev);
 
+// The candidates to micro-probe, at most k of them: the best-estimated
+// candidate of each mapping first (the cost model ranks schedules of one
+// mapping more reliably than it ranks mappings against each other), then the
+// rest in estimate order.  Returned as indices into cand, ascending.
+std::vector<size_t> probe_subset(const std::vector<csr_schedule_t>& cand, const std::vector<double>& est, int k);
+
 // FNV-1a 64 signature of (problem shape, alignment class, histogram, device).
 uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo& dev);
 

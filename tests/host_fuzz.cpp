@@ -160,6 +160,31 @@ int main(int argc, char** argv)
                 const size_t w = csrh::workspace_bytes(p, c);
                 CHECK(w >= csrh::kHeadBytes && w % csrh::kAlign == 0, "bad candidate workspace %zu\n", w);
             }
+            {  // the probe subset: at most k distinct candidates, ascending, the best estimate among them,
+               // and one of each mapping when k allows
+                std::vector<double> est;
+                for (const auto& c : cands) est.push_back(csrh::estimate(p, c, hist, dev));
+                const int k = 1 + (int)(next() % 8);
+                const std::vector<size_t> sub = csrh::probe_subset(cands, est, k);
+                size_t best = 0;
+                for (size_t i = 1; i < est.size(); ++i)
+                    if (est[i] < est[best]) best = i;
+                bool ok = (int)sub.size() == std::min<int>(k, (int)cands.size()), has_best = false;
+                for (size_t i = 0; i < sub.size(); ++i) {
+                    ok = ok && sub[i] < cands.size() && (i == 0 || sub[i] > sub[i - 1]);
+                    has_best = has_best || est[sub[i]] == est[best];
+                }
+                std::vector<std::pair<int, int>> kinds, got;
+                for (const auto& c : cands)
+                    if (std::find(kinds.begin(), kinds.end(), std::make_pair(c.mapping, c.flags)) == kinds.end())
+                        kinds.push_back({c.mapping, c.flags});
+                for (size_t i : sub)
+                    if (std::find(got.begin(), got.end(), std::make_pair(cands[i].mapping, cands[i].flags)) == got.end())
+                        got.push_back({cands[i].mapping, cands[i].flags});
+                const bool diverse = (int)got.size() >= std::min<int>(k, (int)kinds.size());
+                CHECK(ok && has_best && diverse, "probe subset k %d of %zu: size %zu best %d diverse %d\n", k,
+                      cands.size(), sub.size(), (int)has_best, (int)diverse);
+            }
             const uint64_t s1 = csrh::signature(p, hist, dev), s2 = csrh::signature(p, hist, dev);
             CHECK(s1 == s2, "signature not deterministic\n");
             int P = -1, T = -1;
