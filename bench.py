@@ -107,6 +107,9 @@ class Call:
         self.times = []
         self.plan = None  # csa.Plan of an SpMM / SDDMM call
         self.csa = None
+        # SpMM values that the step itself produces (probabilities): passed
+        # to every planned call, not taken from the plan's copy
+        self.step_values = False
 
     def run(self, schedule=None):
         """The call as the step makes it (through its plan, when it has one),
@@ -114,14 +117,15 @@ class Call:
         if schedule is None and self.plan is not None:
             out = self.kwargs.get("out")
             if self.op == "spmm":
-                return self.csa.plan_spmm(self.plan, self.args[3], out=out)
+                vals = self.args[2] if self.step_values else None
+                return self.csa.plan_spmm(self.plan, self.args[3], vals=vals, out=out)
             return self.csa.plan_sddmm(self.plan, self.args[2], self.args[3], out=out)
         s = schedule if schedule is not None else self.schedule
         return self.fn(*self.args, schedule=s, **self.kwargs)
 
     def select(self, csa, mode="auto"):
         sel_args = (self.args[0], None) + tuple(self.args[1:]) if self.op.startswith("row_softmax") else self.args
-        kw = {"scale": self.kwargs["scale"]} if "scale" in self.kwargs else {}
+        kw = {k: self.kwargs[k] for k in ("scale", "val_idx") if k in self.kwargs}
         return csa.select(self.op, *sel_args, mode=mode, **kw)
 
     def label(self):
@@ -263,10 +267,11 @@ def build_workload(name, torch, csa):
                               csr.n_rows, csr.nnz, 1, None))
             calls.append(Call("spmm_F64", "spmm", csa.spmm, (rp, ci, P, Vd), {"out": Y}, csr.n_rows, csr.nnz, 64,
                               None))
+            calls[-1].step_values = True
         else:
             calls.append(Call("attention_F64", "attention", csa.attention, (rp, ci, S, Vd),
                               {"out": Y, "scale": 0.125}, csr.n_rows, csr.nnz, 64, None))
-    elif name == "c3bwd":
+    elif name in ("c3bwd", "c3bwd_gather"):
         # backward of the single-head fp32 attention on the c3 graph (scores
         # given, F = 64): P = row softmax, dP = SDDMM(dOut, V), d scores =
         # softmax backward (in place), P^T order by gather, dV = SpMM on A^T.
@@ -299,10 +304,16 @@ def build_workload(name, torch, csa):
                           None))
         calls.append(Call("softmax_bwd", "row_softmax_backward", csa.row_softmax_backward, (rp, P, dP),
                           {"out": dP, "scale": 0.125}, csr.n_rows, csr.nnz, 1, None))
-        calls.append(Call("gather_Pt", "gather", lambda perm, src, out, schedule=None: csa.gather_values(
-            perm, src, out=out), (At.perm, P, Pt), {}, csr.n_rows, csr.nnz, 1, None))
-        calls.append(Call("spmm_dV", "spmm", csa.spmm, (At.row_ptr, At.col_idx, Pt, dO), {"out": dV}, csr.n_cols,
-                          csr.nnz, 64, None))
+        if name == "c3bwd_gather":
+            calls.append(Call("gather_Pt", "gather", lambda perm, src, out, schedule=None: csa.gather_values(
+                perm, src, out=out), (At.perm, P, Pt), {}, csr.n_rows, csr.nnz, 1, None))
+            calls.append(Call("spmm_dV", "spmm", csa.spmm, (At.row_ptr, At.col_idx, Pt, dO), {"out": dV},
+                              csr.n_cols, csr.nnz, 64, None))
+        else:
+            # P read through the transposed pattern's perm inside the SpMM
+            calls.append(Call("spmm_dV", "spmm", csa.spmm, (At.row_ptr, At.col_idx, P, dO),
+                              {"out": dV, "val_idx": At.perm}, csr.n_cols, csr.nnz, 64, None))
+            calls[-1].bytes += 4 * csr.nnz  # the value index
     elif name in ("c1", "p4"):
         c = configs.make_config(name)
         csr = c["csr"]
@@ -428,12 +439,12 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
             continue
         scale = c.kwargs.get("scale", 1.0)
         args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
-        p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale)
+        p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale, val_idx=c.kwargs.get("val_idx"))
         counts, sums, mx = csa.degree_histogram(c.args[0])
         hist = counts + sums + [mx]
         cands = [({"format_parts": 1, **s.as_dict()}, lambda s=s: c.fn(*c.args, schedule=s, **c.kwargs))
                  for s in csa.candidates(p, hist)]
-        if c.op in ("spmm", "sddmm"):
+        if c.op in ("spmm", "sddmm") and "val_idx" not in c.kwargs:
             P0, T0 = csa.hybrid_plan(p, hist)
             fmts = ([(P0, T0), (P0 // 2, T0), (P0 * 2, T0)] + ([(P0, 0)] if T0 > 0 else [])) if P0 > 1 \
                 else [(4, 0), (16, 0)]
@@ -705,7 +716,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2",
-                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3qk, c3bf16, c3bwd, c3sweep")
+                    help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3qk, c3bf16, c3bwd, "
+                         "c3bwd_gather, c3sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds per pass of the CPU oracle sample")
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -747,7 +759,7 @@ def main():
     for c in calls:
         if c.op == "gather":  # no schedule
             continue
-        if c.op in ("spmm", "sddmm") and not args.no_format:
+        if c.op in ("spmm", "sddmm") and not args.no_format and "val_idx" not in c.kwargs:
             info = make_plan(c, csa, torch)
             pl = c.plan
             sel[c.name] = {"plan": {"parts": pl.parts, "whole_below": pl.whole_below, "segments": pl.n_seg,
@@ -854,7 +866,11 @@ def main():
                                 "c3sweep": "CSR SpMM on the log-normal graph at F in {128,256,384,512}: "
                                            "gathered operand of 1.25 to 5.0 GB",
                                 "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "
-                                         "row softmax, SDDMM dP, softmax backward, gather P^T, SpMM dV on A^T"
+                                         "row softmax, SDDMM dP, softmax backward, SpMM dV on A^T reading P "
+                                         "through the transposed pattern's perm",
+                                "c3bwd_gather": "backward of single-head fp32 attention on the log-normal graph, "
+                                                "F=64: row softmax, SDDMM dP, softmax backward, gather P^T, "
+                                                "SpMM dV on A^T"
                                 }[args.config],
                    "name": args.config, "n_rows": calls[0].n_rows, "nnz": calls[0].nnz,
                    "widths": [c.width for c in calls], "parallelism": "1 GPU"},

@@ -68,6 +68,7 @@ from .ops import (  # noqa: E402,F401
     signature,
     spmm,
     spmm_backward,
+    spmm_transposed,
     spmm_noalloc,
     transpose,
     workspace_size,

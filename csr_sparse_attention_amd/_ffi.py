@@ -31,7 +31,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # CSR_NOALLOC_SCRATCH_BYTES
 # Every symbol the header declares.
 EXPORTS = (
     "csr_context_create", "csr_context_destroy", "csr_status_string", "csr_last_error",
-    "csr_spmm", "csr_spmm_noalloc", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
+    "csr_spmm", "csr_spmm_perm", "csr_spmm_noalloc", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
     "csr_row_softmax_backward", "csr_transpose_workspace_size", "csr_transpose", "csr_gather_values",
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
@@ -100,6 +100,7 @@ class CsrProblem(ctypes.Structure):
         ("ld_c", ctypes.c_int64),
         ("probs", ctypes.c_void_p),
         ("probs_stride", ctypes.c_int64),
+        ("a_idx", ctypes.c_void_p),
     ]
 
 
@@ -190,6 +191,7 @@ def load() -> ctypes.CDLL:
         "csr_last_error": [P],
         "csr_spmm": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
         "csr_spmm_noalloc": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P],
+        "csr_spmm_perm": [P, I64, I64, I64, P, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
         "csr_sddmm": [P, I64, I64, I64, P, P, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
         "csr_attention": [P, I64, I64, I64, P, P, P, P, P, P, I32, I32, I64, I64, F, P, I64, P, SP, P, SZ, P],
         "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, P, SP, P, SZ, P],

@@ -221,9 +221,12 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     if (ctx->flags & CSR_CTX_VALIDATE) {
         int64_t* bad = reinterpret_cast<int64_t*>(ws);
         CSR_HIP(ctx, csrk::launch_validate(p.row_ptr, p.col_idx, p.n_rows, p.n_cols, p.nnz, bad, st));
+        if (p.op == CSR_OP_SPMM && p.a_idx) CSR_HIP(ctx, csrk::launch_validate_index(p.a_idx, p.nnz, p.nnz, bad, st));
         CSR_HIP(ctx, hipMemcpyAsync(ctx->pinned, bad, sizeof(int64_t), hipMemcpyDeviceToHost, st));
         CSR_HIP(ctx, hipStreamSynchronize(st));
-        if (ctx->pinned[0] != 0) return set_err(ctx, CSR_ERR_INVALID_CSR, "row_ptr / col_idx fail CSR validation");
+        if (ctx->pinned[0] != 0)
+            return set_err(ctx, CSR_ERR_INVALID_CSR, p.a_idx ? "row_ptr / col_idx / val_idx fail CSR validation"
+                                                             : "row_ptr / col_idx fail CSR validation");
     }
     if (p.n_rows == 0) return CSR_OK;
     if (p.op == CSR_OP_SDDMM && p.nnz == 0) return CSR_OK;
@@ -325,6 +328,7 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     }
     if (p.op != CSR_OP_ATTENTION_QK) {
         a.ev = static_cast<const float*>(p.a);
+        if (p.op == CSR_OP_SPMM) a.ev_idx = p.a_idx;
         a.X = p.b;
         a.ldx = p.ld_b;
         a.Y = static_cast<float*>(p.out);
@@ -718,6 +722,37 @@ int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, con
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
     p.a = vals;
+    p.b = X;
+    p.out = Y;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
+int csr_spmm_perm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                  const int32_t* col_idx, const float* vals, const int32_t* val_idx, const void* X, int32_t x_dtype,
+                  int64_t F, int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* workspace,
+                  size_t ws_bytes, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    if (nnz > 0 && (!vals || !val_idx)) {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        return set_err(ctx, CSR_ERR_NULL, "vals and val_idx must not be NULL");
+    }
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_SPMM;
+    p.dtype = x_dtype;
+    p.n_rows = n_rows;
+    p.n_cols = n_cols;
+    p.nnz = nnz;
+    p.width = F;
+    p.ld_b = ldx;
+    p.ld_out = ldy;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.a = vals;
+    p.a_idx = val_idx;
     p.b = X;
     p.out = Y;
     p.workspace = workspace;
@@ -1451,6 +1486,7 @@ static void plan_sizes(const csr_problem_t& p, const int64_t* hist, size_t* plan
 static int check_plan_problem(csr_context_t ctx, const csr_problem_t& p, bool need_ptrs)
 {
     if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SDDMM) return set_err(ctx, CSR_ERR_SHAPE, "plans serve SpMM and SDDMM");
+    if (p.a_idx) return set_err(ctx, CSR_ERR_SHAPE, "plans take the values in entry order (no value index)");
     std::string why;
     int rc = csrh::check_problem(p, need_ptrs, &why);
     if (rc != CSR_OK) return set_err(ctx, rc, why);

@@ -38,6 +38,8 @@ struct Fp32Args {
     // at probs[e * probs_stride]
     float* probs;
     int64_t probs_stride;
+    // SpMM: entry e's value is ev[ev_idx[e]] (null: ev[e])
+    const int32_t* ev_idx;
 };
 
 struct MhaArgs {

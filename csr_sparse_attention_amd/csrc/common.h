@@ -124,12 +124,15 @@ __device__ __forceinline__ float ld_stream(const float* p) { return __builtin_no
 // Stages a merge-path chunk in LDS with the 64 lanes of a wave: row_ptr
 // entries rp_src[0 .. nr) (nr <= NR * 64) and, for the chunk's entries,
 // col_src[0 .. ne) and optionally val_src[0 .. ne) (ne <= NE * 64; a null
-// val_src with FILL set stores 1.0).  Every global load is issued before the
-// first LDS store, so the loads of one wave overlap instead of each waiting
-// for the previous one.  The per-entry arrays are read once: non-temporal.
+// val_src with FILL set stores 1.0), or val_src[val_idx[i]] for i < ne when
+// val_idx is given (values kept in another entry order).  Every global load
+// is issued before the first LDS store, so the loads of one wave overlap
+// instead of each waiting for the previous one.  The per-entry arrays are
+// read once: non-temporal.
 template <int NR, int NE, bool VALS, typename V>
 __device__ __forceinline__ void stage_chunk(int32_t* rp_dst, const int32_t* rp_src, int nr, int32_t* col_dst,
-                                            const int32_t* col_src, V* val_dst, const V* val_src, int ne)
+                                            const int32_t* col_src, V* val_dst, const V* val_src, int ne,
+                                            const int32_t* val_idx = nullptr)
 {
     const int lane = __lane_id();
     int32_t r[NR], c[NE];
@@ -139,12 +142,29 @@ __device__ __forceinline__ void stage_chunk(int32_t* rp_dst, const int32_t* rp_s
         const int i = lane + k * 64;
         if (i < nr) r[k] = rp_src[i];
     }
+    if (VALS && val_src && val_idx) {
+        int32_t ix[NE];
 #pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        const int i = lane + k * 64;
-        if (i < ne) {
-            if (col_src) c[k] = __builtin_nontemporal_load(col_src + i);
-            if constexpr (VALS) v[k] = val_src ? __builtin_nontemporal_load(val_src + i) : V(1);
+        for (int k = 0; k < NE; ++k) {
+            const int i = lane + k * 64;
+            if (i < ne) {
+                if (col_src) c[k] = __builtin_nontemporal_load(col_src + i);
+                ix[k] = __builtin_nontemporal_load(val_idx + i);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int i = lane + k * 64;
+            if (i < ne) v[k] = val_src[ix[k]];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int i = lane + k * 64;
+            if (i < ne) {
+                if (col_src) c[k] = __builtin_nontemporal_load(col_src + i);
+                if constexpr (VALS) v[k] = val_src ? __builtin_nontemporal_load(val_src + i) : V(1);
+            }
         }
     }
 #pragma unroll

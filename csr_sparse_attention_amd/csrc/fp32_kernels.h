@@ -61,10 +61,11 @@ __device__ __forceinline__ void zero(float (&a)[NV][VEC])
 
 // Edge weight: SpMM value (1 if absent) or unnormalised softmax weight.
 template <Op OP>
-__device__ __forceinline__ float edge_weight(const float* ev, int e, float scale, float m)
+__device__ __forceinline__ float edge_weight(const float* ev, int e, float scale, float m,
+                                             const int32_t* ev_idx = nullptr)
 {
     if constexpr (OP == Op::Spmm) {
-        return ev ? ev[e] : 1.f;
+        return ev ? ev[ev_idx ? ev_idx[e] : e] : 1.f;
     } else {
         return exp_neg(ev[e] * scale - m);
     }
@@ -85,7 +86,8 @@ __device__ __forceinline__ const char* row_at(const char* base, int32_t row, uin
 template <Op OP, typename T, int VEC, int NV, int U>
 __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t* col, const float* ev,
                                            int kb, int ke, int step, const T* X, int64_t ldx,
-                                           const Lanes<VEC, NV>& L, int F, float scale, float m)
+                                           const Lanes<VEC, NV>& L, int F, float scale, float m,
+                                           const int32_t* ev_idx = nullptr)
 {
     constexpr uint32_t ES = sizeof(T);
     uint32_t off[NV];
@@ -100,7 +102,7 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = k + u * step;
-            w[u] = edge_weight<OP>(ev, e, scale, m);
+            w[u] = edge_weight<OP>(ev, e, scale, m, ev_idx);
             const char* xr = row_at(xb, col[e], row_bytes);
 #pragma unroll
             for (int j = 0; j < NV; ++j) vload_t<T, VEC>(xv[u][j], reinterpret_cast<const T*>(xr + off[j]));
@@ -119,7 +121,7 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
         for (int u = 0; u < U; ++u) {
             const int e = k + u * step;
             const bool ok = e < ke;
-            w[u] = ok ? edge_weight<OP>(ev, e, scale, m) : 0.f;
+            w[u] = ok ? edge_weight<OP>(ev, e, scale, m, ev_idx) : 0.f;
             if (ok) {
                 const char* xr = row_at(xb, col[e], row_bytes);
 #pragma unroll
@@ -144,13 +146,14 @@ __device__ __forceinline__ void gather_acc(float (&acc)[NV][VEC], const int32_t*
 // column loads.  b and e must be wave-uniform.
 template <typename T, int VEC, int NV, int U>
 __device__ __forceinline__ void gather_acc_wave(float (&acc)[NV][VEC], const int32_t* col, const float* ev, int b,
-                                                int e, const T* X, int64_t ldx, const Lanes<VEC, NV>& L, int F)
+                                                int e, const T* X, int64_t ldx, const Lanes<VEC, NV>& L, int F,
+                                                const int32_t* ev_idx)
 {
     const int lane = lane_id();
     for (int base = b; base < e; base += CSR_WAVE) {
         const int n = min(CSR_WAVE, e - base);
         const int cl = lane < n ? col[base + lane] : 0;
-        const float wl = lane < n ? (ev ? ev[base + lane] : 1.f) : 0.f;
+        const float wl = lane < n ? (ev ? ev[ev_idx ? ev_idx[base + lane] : base + lane] : 1.f) : 0.f;
         for (int i = 0; i < n; i += U) {
             float xv[U][NV][VEC];
             float w[U];
@@ -461,9 +464,10 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
         }
         if (OP == Op::Spmm && a.W == CSR_WAVE)
             gather_acc_wave<T, VEC, NV, U>(acc, a.col_idx, a.ev, __builtin_amdgcn_readfirstlane(b),
-                                           __builtin_amdgcn_readfirstlane(e), X, a.ldx, L, a.F);
+                                           __builtin_amdgcn_readfirstlane(e), X, a.ldx, L, a.F, a.ev_idx);
         else
-            gather_acc<OP, T, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, X, a.ldx, L, a.F, a.scale, m);
+            gather_acc<OP, T, VEC, NV, U>(acc, a.col_idx, a.ev, b, e, 1, X, a.ldx, L, a.F, a.scale, m,
+                                          OP == Op::Spmm ? a.ev_idx : nullptr);
         float* dst = a.Y + row * a.ldy;
         if (OP == Op::Attention && e > b)
             store_row_div<VEC, NV>(dst, acc, L, a.F, l);
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup_wide(Fp32Args a)
     for (int base = b; base < e; base += CSR_WAVE) {
         const int n = min(CSR_WAVE, e - base);
         const int cl = lane < n ? a.col_idx[base + lane] : 0;
-        const float wl = lane < n ? (a.ev ? a.ev[base + lane] : 1.f) : 0.f;
+        const float wl = lane < n ? (a.ev ? a.ev[a.ev_idx ? a.ev_idx[base + lane] : base + lane] : 1.f) : 0.f;
         // U entries per batch, every load issued before the first multiply-add
         auto batch = [&](int i, bool tail) {
             float4_a4 xv[U][NV];
@@ -599,7 +603,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
         const int nr = (x1 < a.n_rows ? x1 : (int)a.n_rows - 1) - x0 + 2;
         stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, D / CSR_WAVE, OP != Op::Sddmm, float>(
             sh.rp[wave], a.row_ptr + x0, nr, sh.col[wave], a.col_idx + y0, sh.ev[wave],
-            a.ev ? a.ev + y0 : nullptr, y1 - y0);
+            a.ev ? (a.ev_idx ? a.ev : a.ev + y0) : nullptr, y1 - y0, a.ev_idx ? a.ev_idx + y0 : nullptr);
     }
     __syncthreads();
     if (!active) return;
@@ -767,7 +771,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_segscan(Fp32Args a)
         const int nr = (x1 < a.n_rows ? x1 : (int)a.n_rows - 1) - x0 + 2;
         stage_chunk<(D + 2 + CSR_WAVE - 1) / CSR_WAVE, D / CSR_WAVE, OP != Op::Sddmm, float>(
             sh.rp[wave], a.row_ptr + x0, nr, sh.col[wave], a.col_idx + y0, sh.ev[wave],
-            a.ev ? a.ev + y0 : nullptr, y1 - y0);
+            a.ev ? (a.ev_idx ? a.ev : a.ev + y0) : nullptr, y1 - y0, a.ev_idx ? a.ev_idx + y0 : nullptr);
     }
     __syncthreads();
     if (!active) return;

@@ -133,6 +133,11 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         return code;
     };
     if (p.op < CSR_OP_SPMM || p.op > CSR_OP_ATTENTION_QK) return fail(CSR_ERR_SHAPE, "unknown op");
+    if (p.a_idx) {
+        if (p.op != CSR_OP_SPMM) return fail(CSR_ERR_SHAPE, "a value index serves SpMM");
+        if (!aligned(p.a_idx, 4)) return fail(CSR_ERR_ALIGN, "the value index must be 4-byte aligned");
+        if (need_ptrs && p.nnz > 0 && !p.a) return fail(CSR_ERR_NULL, "a value index needs the values");
+    }
     if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32 && p.dtype != CSR_DTYPE_BF16)
         return fail(CSR_ERR_DTYPE, "this op takes fp32 or bf16 operands");
     if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
@@ -656,6 +661,7 @@ uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo
     fnv(h, dev.cu_count);
     fnv(h, dev.arch);
     for (int i = 0; i < kHistInts; ++i) fnv(h, hist ? hist[i] : 0);
+    if (p.a_idx) fnv(h, 0x58444956);  // 'VIDX': values read through an index
     return h;
 }
 

@@ -88,6 +88,18 @@ __global__ void k_validate(const int32_t* row_ptr, const int32_t* col_idx, int64
     if (local) atomicAdd(reinterpret_cast<unsigned long long*>(bad), local);
 }
 
+// Adds to *bad the number of idx[i], i < n, outside [0, bound).
+__global__ void k_validate_index(const int32_t* idx, int64_t n, int64_t bound, int64_t* bad)
+{
+    unsigned long long local = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int v = idx[i];
+        local += (v < 0) || ((int64_t)v >= bound);
+    }
+    if (local) atomicAdd(reinterpret_cast<unsigned long long*>(bad), local);
+}
+
 static unsigned grid_for(int64_t n, int64_t cap)
 {
     int64_t b = (n + CSR_BLOCK - 1) / CSR_BLOCK;
@@ -139,6 +151,13 @@ hipError_t launch_validate(const int32_t* row_ptr, const int32_t* col_idx, int64
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_validate, dim3(grid_for(n_rows > nnz ? n_rows : nnz, 4096)), dim3(CSR_BLOCK), 0, s, row_ptr,
                        col_idx, n_rows, n_cols, nnz, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_validate_index(const int32_t* idx, int64_t n, int64_t bound, int64_t* bad, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_validate_index, dim3(grid_for(n, 4096)), dim3(CSR_BLOCK), 0, s, idx, n, bound, bad);
     return hipGetLastError();
 }
 

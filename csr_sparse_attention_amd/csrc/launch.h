@@ -86,5 +86,7 @@ hipError_t launch_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz
                              int64_t n_chunks, int32_t* coords, hipStream_t s, int32_t* bounds = nullptr);
 hipError_t launch_validate(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows,
                            int64_t n_cols, int64_t nnz, int64_t* bad, hipStream_t s);
+// Adds the count of idx[0 .. n) outside [0, bound) to *bad (not zeroed here).
+hipError_t launch_validate_index(const int32_t* idx, int64_t n, int64_t bound, int64_t* bad, hipStream_t s);
 
 } // namespace csrk

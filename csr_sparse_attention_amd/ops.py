@@ -371,21 +371,36 @@ def _run(problem: CsrProblem, device, schedule, ctx, call, workspace=None):
 # public calls
 # ---------------------------------------------------------------------------
 
-def spmm(row_ptr, col_idx, vals, X, *, out=None, schedule: Optional[CsrSchedule] = None,
+def spmm(row_ptr, col_idx, vals, X, *, val_idx=None, out=None, schedule: Optional[CsrSchedule] = None,
          ctx: Optional[Context] = None,
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = A X for the CSR matrix A (row_ptr, col_idx, vals; vals=None means 1).
-    X is float32 or bfloat16 (fp32 accumulation); Y is float32."""
+    X is float32 or bfloat16 (fp32 accumulation); Y is float32.  With
+    ``val_idx`` (int32 [nnz], indices in [0, nnz)) entry e's value is
+    vals[val_idx[e]] (csr_spmm_perm): with a transposed pattern and its perm,
+    A^T X over values kept in A's order."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
-    _on(row_ptr.device, vals=vals, X=X)
+    _on(row_ptr.device, vals=vals, X=X, val_idx=val_idx)
     if X.dim() != 2:
         raise ValueError("X must be 2-D [n_cols, F]")
     if vals is not None:
         _entries(vals, "vals", nnz)
+    if val_idx is not None:
+        if vals is None:
+            raise ValueError("val_idx needs vals")
+        if val_idx.dtype != torch.int32 or val_idx.dim() != 1 or not val_idx.is_contiguous() \
+                or val_idx.numel() != nnz:
+            raise ValueError(f"val_idx must be a contiguous 1-D int32 tensor of {nnz} entries")
     out = _out_rows(out, n_rows, X.shape[1], X.device)
     p = _spmm_problem(row_ptr, col_idx, vals, X, out)
+    if val_idx is not None:
+        p.a_idx = val_idx.data_ptr()
 
     def call(ctx, ws, nb, st):
+        if val_idx is not None:
+            return _lib().csr_spmm_perm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.a_idx,
+                                        p.b, p.dtype, p.width, p.ld_b, p.out, p.ld_out, _sched_arg(schedule),
+                                        ws.data_ptr(), nb, st)
         return _lib().csr_spmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.b, p.dtype,
                                p.width, p.ld_b, p.out, p.ld_out, _sched_arg(schedule), ws.data_ptr(), nb, st)
 
@@ -646,38 +661,52 @@ def gather_values(perm, src, *, out=None, ctx: Optional[Context] = None) -> torc
     return out
 
 
+def spmm_transposed(At: Transposed, vals, X, *, fused: bool = True, out=None, ctx: Optional[Context] = None,
+                    schedule: Optional[CsrSchedule] = None) -> torch.Tensor:
+    """A^T X for the transposed pattern At of A, with vals in A's entry order
+    (None = 1): one SpMM reading each value through At.perm (fused), or a
+    csr_gather_values pass into At's order followed by the SpMM."""
+    if vals is None:
+        return spmm(At.row_ptr, At.col_idx, None, X, out=out, schedule=schedule, ctx=ctx)
+    if fused:
+        return spmm(At.row_ptr, At.col_idx, vals, X, val_idx=At.perm, out=out, schedule=schedule, ctx=ctx)
+    return spmm(At.row_ptr, At.col_idx, gather_values(At.perm, vals, ctx=ctx), X, out=out, schedule=schedule,
+                ctx=ctx)
+
+
 def spmm_backward(row_ptr, col_idx, vals, X, dY, *, transposed: Optional[Transposed] = None,
-                  ctx: Optional[Context] = None):
+                  fused: bool = True, ctx: Optional[Context] = None):
     """Gradients of Y = A X: (d vals, dX) with d vals_e = <dY[row_e], X[col_e]>
     (SDDMM; None when vals is None) and dX = A^T dY (SpMM on the transposed
-    pattern).  ``transposed`` (from transpose()) is reused when given."""
+    pattern, values read through its perm unless ``fused`` is False).
+    ``transposed`` (from transpose()) is reused when given."""
     At = transposed or transpose(row_ptr, col_idx, X.shape[0], ctx=ctx)
-    vt = None if vals is None else gather_values(At.perm, vals, ctx=ctx)
-    dX = spmm(At.row_ptr, At.col_idx, vt, dY, ctx=ctx)
+    dX = spmm_transposed(At, vals, dY, fused=fused, ctx=ctx)
     dvals = None if vals is None else sddmm(row_ptr, col_idx, dY, X, ctx=ctx)
     return dvals, dX
 
 
 def sddmm_backward(row_ptr, col_idx, U, V, dout, *, transposed: Optional[Transposed] = None,
-                   ctx: Optional[Context] = None):
+                   fused: bool = True, ctx: Optional[Context] = None):
     """Gradients of out_e = <U[row_e], V[col_e]>: dU = A_g V and dV = A_g^T U,
     A_g the pattern carrying dout."""
     At = transposed or transpose(row_ptr, col_idx, V.shape[0], ctx=ctx)
     dU = spmm(row_ptr, col_idx, dout, V, ctx=ctx)
-    dV = spmm(At.row_ptr, At.col_idx, gather_values(At.perm, dout, ctx=ctx), U, ctx=ctx)
+    dV = spmm_transposed(At, dout, U, fused=fused, ctx=ctx)
     return dU, dV
 
 
 def attention_backward(row_ptr, col_idx, edge_scores, node_value, d_out, *, scale: float = 1.0, probs=None,
-                       transposed: Optional[Transposed] = None, ctx: Optional[Context] = None):
+                       transposed: Optional[Transposed] = None, fused: bool = True, ctx: Optional[Context] = None):
     """Gradients of out = softmax_row(scale * S) V (scores given): returns
     (d edge_scores, d node_value).  P is recomputed by row_softmax unless given;
-    dP = SDDMM(d_out, V); d scores = row_softmax_backward(P, dP); dV = P^T d_out."""
+    dP = SDDMM(d_out, V); d scores = row_softmax_backward(P, dP); dV = P^T d_out
+    (P read through the transposed pattern's perm unless ``fused`` is False)."""
     At = transposed or transpose(row_ptr, col_idx, node_value.shape[0], ctx=ctx)
     P = probs if probs is not None else row_softmax(row_ptr, edge_scores, scale=scale, ctx=ctx)
+    dV = spmm_transposed(At, P, d_out, fused=fused, ctx=ctx)
     dP = sddmm(row_ptr, col_idx, d_out, node_value, ctx=ctx)
     dS = row_softmax_backward(row_ptr, P, dP, scale=scale, out=dP, ctx=ctx)
-    dV = spmm(At.row_ptr, At.col_idx, gather_values(At.perm, P, ctx=ctx), d_out, ctx=ctx)
     return dS, dV
 
 
@@ -982,17 +1011,23 @@ def plan_sddmm(pl: Plan, U, V, *, out=None, ctx: Optional[Context] = None,
     return out
 
 
-def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0) -> CsrProblem:
+def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0, val_idx=None) -> CsrProblem:
     """The csr_problem_t of a call, for select() / workspace_size() /
-    default_schedule(): op is 'spmm' (vals, X), 'sddmm' (U, V), 'attention'
-    (edge_scores, node_value), 'mha' (Q, K, V) or 'attention_qk' (Q, K, V:
-    the problem that csr_attention runs for them)."""
+    default_schedule(): op is 'spmm' (vals, X; val_idx: the value index of
+    csr_spmm_perm), 'sddmm' (U, V), 'attention' (edge_scores, node_value),
+    'mha' (Q, K, V) or 'attention_qk' (Q, K, V: the problem that
+    csr_attention runs for them)."""
     _pattern(row_ptr, row_ptr if col_idx is None else col_idx)
     n_rows = row_ptr.numel() - 1
+    if val_idx is not None and op != "spmm":
+        raise ValueError("val_idx serves 'spmm'")
     if op == "spmm":
         vals, X = operands
         out = out if out is not None else torch.empty((n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
-        return _spmm_problem(row_ptr, col_idx, vals, X, out), out
+        p = _spmm_problem(row_ptr, col_idx, vals, X, out)
+        if val_idx is not None:
+            p.a_idx = val_idx.data_ptr()
+        return p, out
     if op == "sddmm":
         U, V = operands
         out = out if out is not None else torch.empty(col_idx.numel(), dtype=torch.float32, device=U.device)
@@ -1022,11 +1057,11 @@ def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 
 
 
 def select(op: str, row_ptr, col_idx, *operands, mode: str = "auto", scale: float = 1.0, out=None,
-           ctx: Optional[Context] = None):
+           val_idx=None, ctx: Optional[Context] = None):
     """Runs the selector for a call; returns (schedule, signature).  With
     mode 'auto' or 'probe' the candidates run on the given operands and write
     ``out``."""
-    p, out = make_problem(op, row_ptr, col_idx, *operands, out=out, scale=scale)
+    p, out = make_problem(op, row_ptr, col_idx, *operands, out=out, scale=scale, val_idx=val_idx)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)
     lib = _lib()

@@ -200,6 +200,7 @@ typedef struct csr_problem_s {
     int64_t ld_c;          /* CSR_OP_ATTENTION_QK: leading dimension of c */
     float* probs;          /* attention ops: per-entry probabilities out, or NULL */
     int64_t probs_stride;  /* floats between consecutive entries' probabilities (0: 1) */
+    const int32_t* a_idx;  /* CSR_OP_SPMM: entry e's value is a[a_idx[e]] (NULL: a[e]) */
 } csr_problem_t;
 
 /* ---------------------------------------------------------------------------
@@ -247,6 +248,20 @@ int csr_spmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
              const int32_t* row_ptr, const int32_t* col_idx, const float* vals,
              const void* X, int32_t x_dtype, int64_t F, int64_t ldx, float* Y, int64_t ldy,
              const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
+
+/* SpMM with the values read through an index (SparseTIR page, Abstract:
+ * sparse operators of GNN training; the backward's dX = A^T dY):
+ *   Y[i, f] = sum over stored entries e of row i of vals[val_idx[e]] * X[col_idx[e], f]
+ * With the pattern and t_perm of csr_transpose this is the SpMM of A^T whose
+ * values stay in A's order: no csr_gather_values pass, no copy of the values
+ * in the transposed order.  vals: fp32, not NULL; val_idx: int32 [nnz], every
+ * index in [0, nnz) (checked only with CSR_CTX_VALIDATE: CSR_ERR_INVALID_CSR;
+ * an index out of range otherwise reads outside vals).  Other arguments,
+ * rules and errors as for csr_spmm. */
+int csr_spmm_perm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                  const int32_t* row_ptr, const int32_t* col_idx, const float* vals, const int32_t* val_idx,
+                  const void* X, int32_t x_dtype, int64_t F, int64_t ldx, float* Y, int64_t ldy,
+                  const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
 
 /* Scratch capacity (bytes per GPU) of csr_spmm_noalloc. */
 #define CSR_NOALLOC_SCRATCH_BYTES (32u << 20)

@@ -107,6 +107,7 @@ static csr_problem_t random_problem()
         p.probs_stride = 1;
         p.scale = 0.125f;
     }
+    p.a_idx = (next() % 4 == 0) ? static_cast<const int32_t*>(ptr()) : nullptr;
     return p;
 }
 
@@ -145,6 +146,8 @@ int main(int argc, char** argv)
         random_hist(hist, p);
         if (rc == CSR_OK) {
             ++accepted;
+            CHECK(!p.a_idx || (p.op == CSR_OP_SPMM && ((uintptr_t)p.a_idx % 4) == 0 && (!need_ptrs || p.nnz == 0 || p.a)),
+                  "value index accepted for op %d\n", p.op);
             const csr_schedule_t d = csrh::default_schedule(p);
             CHECK(csrh::check_schedule(p, d, &why) == CSR_OK, "default schedule rejected (op %d F %lld): %s\n",
                   p.op, (long long)p.width, why.c_str());
@@ -217,7 +220,7 @@ int main(int argc, char** argv)
         s.passes = (int32_t)(next() % 20);
         s.chunk_items = (int32_t)((next() % 2) ? 256 << (next() % 4) : next() % 5000);
         s.long_row = (int32_t)(next() % 300) - 10;
-        s.flags = (int32_t)(next() % 8 == 0);
+        s.flags = (int32_t)(next() % 8 == 0 ? 1 + next() % 3 : 0);
         if (rc == CSR_OK && csrh::check_schedule(p, s, &why) == CSR_OK) {
             const size_t w = csrh::workspace_bytes(p, s);
             CHECK(w >= csrh::kHeadBytes && w % csrh::kAlign == 0, "bad workspace for an accepted schedule\n");

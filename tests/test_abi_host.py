@@ -498,3 +498,22 @@ def test_wide_lane_schedules():
         assert bool(got) == expect, (F, ld)
         for s in got:
             assert (s.vec, s.group_lanes, s.mapping) == (4, 64, _ffi.MAP_ROWGROUP)
+
+
+def test_value_index_rules():
+    """A value index (entry e's value is a[a_idx[e]]) serves SpMM only, must
+    be 4-byte aligned and changes the input's signature."""
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+    for op, code in ((_ffi.OP_SPMM, 0), (_ffi.OP_SDDMM, -2), (_ffi.OP_ATTENTION, -2)):
+        p = problem(op, width=32)
+        p.a_idx = 0x2000
+        assert lib.csr_workspace_size(None, ctypes.byref(p), None, ctypes.byref(n)) == code, op
+    p = problem(_ffi.OP_SPMM, width=32)
+    p.a_idx = 0x2002
+    assert lib.csr_workspace_size(None, ctypes.byref(p), None, ctypes.byref(n)) == -4
+    hist = [0] * 66 + [10]
+    plain = problem(_ffi.OP_SPMM, width=32)
+    idx = problem(_ffi.OP_SPMM, width=32)
+    idx.a_idx = 0x2000
+    assert csa.signature(plain, hist) != csa.signature(idx, hist)

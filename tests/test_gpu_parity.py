@@ -674,6 +674,73 @@ def test_spmm_backward(graph):
     assert_close(dX1.cpu().numpy(), ref, mag, TOL_F32, "dX, unit values")
 
 
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("F,dt", [(3, "f32"), (24, "f32"), (130, "f32"), (64, "bf16")])
+def test_spmm_perm_every_schedule(graph, F, dt):
+    """A^T X with A's values read through the transposed pattern's perm
+    (csr_spmm_perm) under every schedule: against the oracle's transpose
+    product, and bit for bit equal to the same schedule over the values
+    gathered into the transposed order."""
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(615)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    Xf = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    if dt == "bf16":
+        Xb = to_bf16_bits(Xf)
+        Xd, Xref, tol = bf16_dev(Xb), oracle.bf16_to_f32(Xb), TOL_BF16
+    else:
+        Xd, Xref, tol = dev(Xf), Xf, TOL_F32
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    vd = dev(vals)
+    vt = csa.gather_values(t.perm, vd)
+    ref, mag = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, vals.astype(np.float64), Xref, csr.n_cols)
+    prob, _ = csa.make_problem("spmm", t.row_ptr, t.col_idx, vt, Xd)
+    for s in schedules(prob):
+        got = csa.spmm(t.row_ptr, t.col_idx, vd, Xd, val_idx=t.perm, schedule=s)
+        e = assert_close(got.cpu().numpy(), ref, mag, tol, sched_id(s))
+        assert e <= TOL_F32, sched_id(s)
+        want = csa.spmm(t.row_ptr, t.col_idx, vt, Xd, schedule=s)
+        assert torch.equal(got, want), sched_id(s)
+    got = csa.spmm_transposed(t, vd, Xd)  # automatic selection
+    assert_close(got.cpu().numpy(), ref, mag, tol, "auto")
+
+
+def test_spmm_perm_errors_and_validation():
+    csr = skew_graph(3, n_rows=600, n_cols=4000, giant=3000)
+    rng = np.random.default_rng(616)
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    vd = dev(rng.standard_normal(csr.nnz).astype(np.float32))
+    X = dev(rng.standard_normal((csr.n_rows, 16)).astype(np.float32))
+    with pytest.raises(ValueError):
+        csa.spmm(t.row_ptr, t.col_idx, None, X, val_idx=t.perm)
+    with pytest.raises(ValueError):
+        csa.spmm(t.row_ptr, t.col_idx, vd, X, val_idx=t.perm[1:])
+    lib = csa.load_library()
+    ctx = csa.Context(0, None)
+    Y = torch.empty((csr.n_cols, 16), device="cuda")
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib.csr_spmm_perm(ctx.handle, csr.n_cols, csr.n_rows, csr.nnz, t.row_ptr.data_ptr(), t.col_idx.data_ptr(),
+                           vd.data_ptr(), None, X.data_ptr(), 0, 16, 16, Y.data_ptr(), 16, None, ws.data_ptr(),
+                           ws.numel(), st)
+    assert rc == -1  # CSR_ERR_NULL
+    ctx.close()
+    # an index out of range is caught on a validating context, before any product runs
+    vctx = csa.Context(0, None, csa.CTX_VALIDATE)
+    for badv in (csr.nnz, -1):
+        bad = t.perm.clone()
+        bad[csr.nnz // 2] = badv
+        with pytest.raises(csa.CsrError) as ei:
+            csa.spmm(t.row_ptr, t.col_idx, vd, X, val_idx=bad, ctx=vctx)
+        assert "CSR_ERR_INVALID_CSR" in str(ei.value)
+    ref = csa.spmm_transposed(t, vd, X, fused=False)
+    got = csa.spmm_transposed(t, vd, X, ctx=vctx)
+    assert torch.allclose(got, ref, rtol=1e-5, atol=1e-5)
+    vctx.close()
+
+
 def test_sddmm_backward():
     csr = skew_graph(7, n_rows=1200, n_cols=9000, giant=5000)
     rng = np.random.default_rng(620)
