@@ -416,7 +416,9 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
     weighs (the cost model's part count and threshold, half and twice that
     count, the same count with no whole rows; or 4 and 16 parts when the
     model keeps the plain pattern), each with its own selected schedule, and
-    every candidate schedule of the format the plan chose.  The library's
+    every candidate schedule of the format the plan chose; for SpMM the
+    degree classes at short thresholds 8 and 32 with the selector's schedule
+    for their long rows.  The library's
     pick is the call as the step makes it (through its plan for SpMM /
     SDDMM, the selected schedule otherwise).  The distinct candidates run in
     interleaved rounds (so clock and thermal drift bias none of them),
@@ -462,6 +464,16 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
                     s_alt, _ = f["select"]("auto")
                     cands.append(({"format_parts": P, "whole_below": T, **s_alt.as_dict()},
                                   lambda f=f, s=s_alt: f["run"](s)))
+        if c.op == "spmm" and "val_idx" not in c.kwargs:
+            # the degree classes at both short thresholds, the long rows on the selector's schedule
+            for E in (8, 32):
+                try:
+                    pc = csa.plan("spmm", c.args[0], c.args[1], c.args[2], c.args[3], layout=(0, E),
+                                  out=c.kwargs.get("out"))
+                except csa.CsrError:
+                    continue
+                cands.append(({"format_parts": 0, "whole_below": E, **pc.schedule.as_dict()},
+                              lambda pc=pc: csa.plan_spmm(pc, c.args[3], out=c.kwargs.get("out"))))
         n_cand = len(cands)
         selected = c.label()
         # the pick, run as the step runs it (its own entry when a fixed

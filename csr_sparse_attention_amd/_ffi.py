@@ -38,7 +38,7 @@ EXPORTS = (
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
     "csr_hybrid_plan", "csr_hybrid_parts", "csr_hybrid_capacity", "csr_hybrid_build_workspace_size", "csr_hybrid_build", "csr_hybrid_workspace_size",
     "csr_hybrid_spmm", "csr_hybrid_sddmm", "csr_hybrid_select",
-    "csr_plan_size", "csr_plan_create", "csr_plan_spmm", "csr_plan_sddmm",
+    "csr_plan_size", "csr_plan_create", "csr_plan_layout_size", "csr_plan_build", "csr_plan_spmm", "csr_plan_sddmm",
 )
 
 
@@ -133,6 +133,27 @@ assert ctypes.sizeof(CsrHybrid) == 104
 PLAN_VERSION = 1
 
 
+class CsrBucket(ctypes.Structure):
+    """csr_bucket_t: degree classes (short rows packed slot-major by class, the
+    other rows as a CSR of their own), arrays in the plan memory."""
+    _fields_ = [
+        ("short_below", ctypes.c_int32),
+        ("n_classes", ctypes.c_int32),
+        ("n_short", ctypes.c_int64),
+        ("n_slots", ctypes.c_int64),
+        ("nnz_long", ctypes.c_int64),
+        ("class_rows", ctypes.c_int64 * 6),
+        ("rows", ctypes.c_void_p),
+        ("slot_col", ctypes.c_void_p),
+        ("slot_pos", ctypes.c_void_p),
+        ("slot_val", ctypes.c_void_p),
+        ("long_row_ptr", ctypes.c_void_p),
+        ("long_col", ctypes.c_void_p),
+        ("long_pos", ctypes.c_void_p),
+        ("long_val", ctypes.c_void_p),
+    ]
+
+
 class CsrPlan(ctypes.Structure):
     """csr_plan_t: a CSR matrix prepared for one SpMM or SDDMM (layout and schedule)."""
     _fields_ = [
@@ -149,6 +170,7 @@ class CsrPlan(ctypes.Structure):
         ("signature", ctypes.c_uint64),
         ("sched", CsrSchedule),
         ("fmt", CsrHybrid),
+        ("bkt", CsrBucket),
         ("row_ptr", ctypes.c_void_p),
         ("col_idx", ctypes.c_void_p),
         ("vals", ctypes.c_void_p),
@@ -157,7 +179,8 @@ class CsrPlan(ctypes.Structure):
     ]
 
 
-assert ctypes.sizeof(CsrPlan) == 272
+assert ctypes.sizeof(CsrBucket) == 144
+assert ctypes.sizeof(CsrPlan) == 416
 
 
 class CsrError(RuntimeError):
@@ -222,6 +245,8 @@ def load() -> ctypes.CDLL:
         "csr_hybrid_select": [P, HP, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
         "csr_plan_size": [P, PP, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "csr_plan_create": [P, PP, U32, P, SZ, PLP],
+        "csr_plan_layout_size": [P, PP, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+        "csr_plan_build": [P, PP, I32, I32, SP, P, SZ, PLP],
         "csr_plan_spmm": [P, PLP, P, P, I64, P, I64, P, SZ, P],
         "csr_plan_sddmm": [P, PLP, P, I64, P, I64, P, P, SZ, P],
     }

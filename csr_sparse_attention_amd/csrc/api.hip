@@ -1461,15 +1461,88 @@ static csr_hybrid_t plan_format(const csr_problem_t& p, int P, int T, int64_t ca
     return h;
 }
 
-// Plan memory and workspace for every layout a plan of p may probe.
-static void plan_sizes(const csr_problem_t& p, const int64_t* hist, size_t* plan_bytes, size_t* ws_bytes)
+// The long rows' CSR of degree classes bk as a problem with p's operands.
+static csr_problem_t bucket_long_problem(const csr_problem_t& p, const csr_bucket_t& bk, const float* long_val)
+{
+    csr_problem_t q = p;
+    q.nnz = bk.nnz_long;
+    q.row_ptr = bk.long_row_ptr;
+    q.col_idx = bk.long_col;
+    q.a = long_val;
+    q.a_idx = nullptr;
+    return q;
+}
+
+// The packed rows' SpMM for p (X = p.b, Y = p.out), in the natural lane
+// layout of the width at the widest access the operands allow.
+static int bucket_launch(csr_context_t ctx, const csr_problem_t& p, const csr_bucket_t& bk, const float* slot_val,
+                         hipStream_t st)
+{
+    if (bk.n_short == 0) return CSR_OK;
+    const int vec = csrh::max_vec(p);
+    int W = 0, nv = 0;
+    if (vec < 1 || !csrh::natural_layout(p.width, vec, &W, &nv))
+        return set_err(ctx, CSR_ERR_SHAPE, "no lane layout for the packed rows at this width");
+    constexpr int64_t kBlock = 256;  // threads per workgroup of the kernels
+    csrk::BucketArgs a{};
+    a.rows = bk.rows;
+    a.slot_col = bk.slot_col;
+    a.slot_val = slot_val;
+    a.n_classes = bk.n_classes;
+    a.F = (int32_t)p.width;
+    a.W = W;
+    int64_t blocks = 0, base = 0, row0 = 0;
+    for (int c = 0; c < bk.n_classes; ++c) {
+        a.cls_rows[c] = bk.class_rows[c];
+        a.cls_base[c] = base;
+        a.cls_row0[c] = row0;
+        a.cls_block0[c] = blocks;
+        base += bk.class_rows[c] * ((2 << c) - 1);
+        row0 += bk.class_rows[c];
+        blocks += (bk.class_rows[c] * W + kBlock - 1) / kBlock;
+    }
+    a.cls_block0[bk.n_classes] = blocks;
+    if (base != bk.n_slots || row0 != bk.n_short) return set_err(ctx, CSR_ERR_SHAPE, "inconsistent degree classes");
+    a.X = p.b;
+    a.ldx = p.ld_b;
+    a.Y = static_cast<float*>(p.out);
+    a.ldy = p.ld_out;
+    CSR_HIP(ctx, csrk::launch_bucket_spmm(p.dtype == CSR_DTYPE_BF16, vec, nv, a, st));
+    return CSR_OK;
+}
+
+// The whole product over degree classes: the long rows' CSR with schedule s
+// (it writes every row of Y, the packed ones as zeros), then the packed rows.
+static int bucket_run(csr_context_t ctx, const csr_problem_t& p, const csr_bucket_t& bk, const csr_schedule_t& s,
+                      const float* slot_val, const float* long_val, hipStream_t st)
+{
+    int rc = run_schedule(ctx, bucket_long_problem(p, bk, long_val), s, st);
+    if (rc != CSR_OK) return rc;
+    return bucket_launch(ctx, p, bk, slot_val, st);
+}
+
+// Plan memory and workspace of one layout of p (parts 1 plain, 0 degree
+// classes of short threshold T, else the format (parts, T)).
+static void layout_sizes(const csr_problem_t& p, const int64_t* hist, int P, int T, size_t* plan_bytes,
+                         size_t* ws_bytes)
 {
     size_t mem = csrh::kAlign, ws = up256(auto_workspace(p));
-    for (const auto& f : csrh::plan_formats(p, hist)) {
-        const int64_t cap = csrh::segment_bound(p, hist, f.first, f.second);
+    if (P == 0) {
+        const csrh::BucketShape sh = csrh::bucket_shape(p, hist, T);
+        mem = std::max(mem, csrh::bucket_layout(p, sh).total);
+        size_t build = 0;
+        (void)csrk::bucket_build_workspace(p.n_rows, p.nnz, &build);
+        csr_problem_t q = p;  // the long rows' product
+        q.nnz = sh.nnz_long;
+        q.row_ptr = nullptr;
+        const size_t inner = up256(auto_workspace(q)) + up256((size_t)sh.n_slots * 4) +
+                             up256((size_t)sh.nnz_long * 4);
+        ws = std::max(ws, std::max(up256(build), inner));
+    } else if (P > 1) {
+        const int64_t cap = csrh::segment_bound(p, hist, P, T);
         mem = std::max(mem, plan_layout(p, cap).total);
         size_t build = 0;
-        (void)csrk::hybrid_build_workspace(p.n_rows, p.nnz, f.first, &build);
+        (void)csrk::hybrid_build_workspace(p.n_rows, p.nnz, P, &build);
         csr_problem_t q = p;  // the product on at most cap segments
         q.n_rows = cap;
         q.row_ptr = nullptr;
@@ -1481,6 +1554,31 @@ static void plan_sizes(const csr_problem_t& p, const int64_t* hist, size_t* plan
     }
     *plan_bytes = mem;
     *ws_bytes = ws;
+}
+
+// Plan memory and workspace for every layout a plan of p may probe.
+static void plan_sizes(const csr_problem_t& p, const int64_t* hist, size_t* plan_bytes, size_t* ws_bytes)
+{
+    size_t mem = 0, ws = 0;
+    layout_sizes(p, hist, 1, 0, &mem, &ws);
+    auto take = [&](int P, int T) {
+        size_t m = 0, w = 0;
+        layout_sizes(p, hist, P, T, &m, &w);
+        mem = std::max(mem, m);
+        ws = std::max(ws, w);
+    };
+    for (int E : csrh::plan_buckets(p, hist)) take(0, E);
+    for (const auto& f : csrh::plan_formats(p, hist)) take(f.first, f.second);
+    *plan_bytes = mem;
+    *ws_bytes = ws;
+}
+
+// Whether (parts, whole_below) names a layout a plan of p can take.
+static bool layout_ok(const csr_problem_t& p, int P, int T)
+{
+    if (P == 1) return true;
+    if (P == 0) return p.op == CSR_OP_SPMM && T >= 2 && T <= (1 << CSR_BUCKET_MAX_CLASSES) && (T & (T - 1)) == 0;
+    return P >= 2 && P <= 256 && (P & (P - 1)) == 0 && T >= 0;
 }
 
 static int check_plan_problem(csr_context_t ctx, const csr_problem_t& p, bool need_ptrs)
@@ -1526,9 +1624,10 @@ struct PlanBuild {
     const int64_t* hist;
     void* mem;
     hipStream_t st;
-    int built_P = 0, built_T = -1;
+    int built_P = -1, built_T = -1;  // the layout in the plan memory: parts (0: degree classes), threshold
     csr_hybrid_t h{};
     float* hv = nullptr;  // SpMM: the plan's values in format order
+    csr_bucket_t bk{};    // degree classes, when built
 
     PlanBuild(csr_context_t c, const csr_problem_t& pr, const int64_t* hi, void* m)
         : ctx(c), p(pr), hist(hi), mem(m), st(static_cast<hipStream_t>(pr.stream))
@@ -1540,7 +1639,7 @@ struct PlanBuild {
     int build(int P, int T)
     {
         if (P == built_P && T == built_T) return CSR_OK;
-        built_P = 0;
+        built_P = -1;
         h = plan_format(p, P, T, csrh::segment_bound(p, hist, P, T), mem, &hv);
         int rc = build_format(ctx, p.row_ptr, p.col_idx, &h, p.workspace, p.workspace_bytes, st);
         if (rc != CSR_OK) return rc;
@@ -1554,6 +1653,46 @@ struct PlanBuild {
         built_T = T;
         return CSR_OK;
     }
+
+    // builds the degree classes of short threshold E into the plan memory
+    // (kept if already there), with the values in slot and long-row order
+    int build_bucket(int E)
+    {
+        if (built_P == 0 && built_T == E) return CSR_OK;
+        built_P = -1;
+        const csrh::BucketShape sh = csrh::bucket_shape(p, hist, E);
+        const csrh::BucketLayout L = csrh::bucket_layout(p, sh);
+        char* m = static_cast<char*>(mem);
+        std::memset(&bk, 0, sizeof bk);
+        bk.short_below = E;
+        bk.n_classes = sh.n_classes;
+        bk.n_short = sh.n_short;
+        bk.n_slots = sh.n_slots;
+        bk.nnz_long = sh.nnz_long;
+        for (int c = 0; c < CSR_BUCKET_MAX_CLASSES; ++c) bk.class_rows[c] = sh.class_rows[c];
+        bk.rows = reinterpret_cast<int32_t*>(m + L.rows);
+        bk.slot_col = reinterpret_cast<int32_t*>(m + L.slot_col);
+        bk.slot_pos = reinterpret_cast<int32_t*>(m + L.slot_pos);
+        bk.slot_val = reinterpret_cast<float*>(m + L.slot_val);
+        bk.long_row_ptr = reinterpret_cast<int32_t*>(m + L.long_row_ptr);
+        bk.long_col = reinterpret_cast<int32_t*>(m + L.long_col);
+        bk.long_pos = reinterpret_cast<int32_t*>(m + L.long_pos);
+        bk.long_val = reinterpret_cast<float*>(m + L.long_val);
+        CSR_HIP(ctx, csrk::launch_bucket_build(p.row_ptr, p.col_idx, p.n_rows, p.nnz, E, sh.n_classes, sh.class_rows,
+                                               sh.class_base, sh.class_row0, bk.rows, bk.slot_col, bk.slot_pos,
+                                               bk.long_row_ptr, bk.long_col, bk.long_pos, p.workspace,
+                                               p.workspace_bytes, st));
+        const float* v = static_cast<const float*>(p.a);  // NULL: ones
+        CSR_HIP(ctx, csrk::launch_gather_or_zero(bk.slot_pos, v, bk.slot_val, bk.n_slots, st));
+        CSR_HIP(ctx, csrk::launch_gather_or_zero(bk.long_pos, v, bk.long_val, bk.nnz_long, st));
+        built_P = 0;
+        built_T = E;
+        return CSR_OK;
+    }
+
+    // the built degree classes' long rows as a problem, and the whole product
+    csr_problem_t long_problem() const { return bucket_long_problem(p, bk, bk.long_val); }
+    int run_bucket(const csr_schedule_t& s) { return bucket_run(ctx, p, bk, s, bk.slot_val, bk.long_val, st); }
 
     // the call over the built format with p's operands
     int call(HybridCall* c, const csr_schedule_t* sched)
@@ -1648,6 +1787,16 @@ int probe_plan(PlanBuild& b, csrh::PlanChoice* out, double* ms)
         const std::vector<double> t = probe_runs(b.ctx, cand.size(), [&](size_t i) { return b.run(c, cand[i]); }, b.st);
         for (size_t i = 0; i < cand.size(); ++i) opts.push_back({f.first, f.second, cand[i], t[i]});
     }
+    // degree classes: the long rows' best few schedules, each timed with the packed rows
+    for (int E : csrh::plan_buckets(b.p, b.hist)) {
+        if (b.build_bucket(E) != CSR_OK) continue;
+        const csr_problem_t q = b.long_problem();
+        int64_t hs[csrh::kHistInts];
+        if (histogram(b.ctx, q, b.st, hs) != CSR_OK) continue;
+        const std::vector<csr_schedule_t> cand = top(q, hs, per_format);
+        const std::vector<double> t = probe_runs(b.ctx, cand.size(), [&](size_t i) { return b.run_bucket(cand[i]); }, b.st);
+        for (size_t i = 0; i < cand.size(); ++i) opts.push_back({0, E, cand[i], t[i]});
+    }
     // second round: the winning format's wider set of schedules, timed
     // together (those of the first round again among them, so that the
     // comparison is within one batch)
@@ -1655,14 +1804,18 @@ int probe_plan(PlanBuild& b, csrh::PlanChoice* out, double* ms)
         int wi = -1;
         for (size_t i = 0; i < opts.size(); ++i)
             if (opts[i].ms >= 0 && (wi < 0 || opts[i].ms < opts[wi].ms * 0.99)) wi = (int)i;
-        if (wi >= 0 && opts[wi].P > 1 && max_probe > per_format) {
+        if (wi >= 0 && opts[wi].P != 1 && max_probe > per_format) {
             const int P = opts[wi].P, T = opts[wi].T;
             HybridCall c;
             int64_t hs[csrh::kHistInts];
-            if (b.build(P, T) == CSR_OK && b.call(&c, nullptr) == CSR_OK && histogram(b.ctx, c.p, b.st, hs) == CSR_OK) {
-                const std::vector<csr_schedule_t> cand = top(c.p, hs, max_probe);
-                const std::vector<double> t =
-                    probe_runs(b.ctx, cand.size(), [&](size_t i) { return b.run(c, cand[i]); }, b.st);
+            const bool ok = P == 0 ? (b.build_bucket(T) == CSR_OK && histogram(b.ctx, b.long_problem(), b.st, hs) == CSR_OK)
+                                   : (b.build(P, T) == CSR_OK && b.call(&c, nullptr) == CSR_OK &&
+                                      histogram(b.ctx, c.p, b.st, hs) == CSR_OK);
+            if (ok) {
+                const std::vector<csr_schedule_t> cand = top(P == 0 ? b.long_problem() : c.p, hs, max_probe);
+                const std::vector<double> t = probe_runs(
+                    b.ctx, cand.size(), [&](size_t i) { return P == 0 ? b.run_bucket(cand[i]) : b.run(c, cand[i]); },
+                    b.st);
                 // the other layouts' times came from another batch: scale
                 // them by the winner's ratio between the two batches
                 double ratio = 1.0;
@@ -1745,6 +1898,18 @@ int materialize_plan(PlanBuild& b, const csrh::PlanChoice& c, uint64_t sig, doub
         if (rc != CSR_OK) return set_err(b.ctx, rc, why);
         r.vals = b.p.op == CSR_OP_SPMM ? const_cast<float*>(static_cast<const float*>(b.p.a)) : nullptr;
         r.workspace_bytes = up256(csrh::workspace_bytes(b.p, c.sched));
+    } else if (c.parts == 0) {
+        if (b.p.op != CSR_OP_SPMM) return set_err(b.ctx, CSR_ERR_SHAPE, "degree classes serve SpMM");
+        int rc = b.build_bucket(c.whole_below);
+        if (rc != CSR_OK) return rc;
+        const csr_problem_t q = b.long_problem();
+        rc = csrh::check_schedule(q, c.sched, &why);
+        if (rc != CSR_OK) return set_err(b.ctx, rc, why);
+        r.bkt = b.bk;
+        // the long rows' product, then room for the values of a call that
+        // passes its own (moved into slot and long-row order there)
+        r.workspace_bytes = up256(csrh::workspace_bytes(q, c.sched)) + up256((size_t)b.bk.n_slots * 4) +
+                            up256((size_t)b.bk.nnz_long * 4);
     } else {
         int rc = b.build(c.parts, c.whole_below);
         if (rc != CSR_OK) return rc;
@@ -1771,8 +1936,13 @@ int check_plan(csr_context_t ctx, const csr_plan_t* plan, int op)
     if (!plan) return CSR_ERR_NULL;
     if (plan->version != CSR_PLAN_VERSION || plan->op != op)
         return set_err(ctx, CSR_ERR_SHAPE, "not a plan of this operation and library version");
-    if (plan->parts != 1 && plan->fmt.parts != plan->parts)
+    if (plan->parts == 0) {
+        if (plan->op != CSR_OP_SPMM || plan->bkt.short_below != plan->whole_below || plan->bkt.n_classes < 1 ||
+            plan->bkt.n_classes > CSR_BUCKET_MAX_CLASSES)
+            return set_err(ctx, CSR_ERR_SHAPE, "the plan's degree classes do not match it");
+    } else if (plan->parts != 1 && plan->fmt.parts != plan->parts) {
         return set_err(ctx, CSR_ERR_SHAPE, "the plan's format does not match its parts");
+    }
     if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
     return CSR_OK;
 }
@@ -1837,6 +2007,80 @@ int csr_plan_create(csr_context_t ctx, const csr_problem_t* pp, uint32_t mode, v
     }
 }
 
+int csr_plan_layout_size(csr_context_t ctx, const csr_problem_t* p, int32_t parts, int32_t whole_below,
+                         size_t* plan_bytes, size_t* workspace_bytes)
+{
+    if (!ctx || !p || !plan_bytes || !workspace_bytes) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        int rc = check_plan_problem(ctx, *p, false);
+        if (rc != CSR_OK) return rc;
+        if (!layout_ok(*p, parts, whole_below)) return set_err(ctx, CSR_ERR_SHAPE, "no such layout for this problem");
+        rc = check_workspace(ctx, *p, csrh::kHeadBytes);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        int64_t hist[csrh::kHistInts];
+        rc = histogram(ctx, *p, static_cast<hipStream_t>(p->stream), hist);
+        if (rc != CSR_OK) return rc;
+        layout_sizes(*p, hist, parts, whole_below, plan_bytes, workspace_bytes);
+        return CSR_OK;
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
+int csr_plan_build(csr_context_t ctx, const csr_problem_t* pp, int32_t parts, int32_t whole_below,
+                   const csr_schedule_t* sched, void* plan_mem, size_t plan_bytes, csr_plan_t* plan)
+{
+    if (!ctx || !pp || !plan) return CSR_ERR_NULL;
+    try {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        ctx->last_error.clear();
+        const csr_problem_t& p = *pp;
+        int rc = check_plan_problem(ctx, p, true);
+        if (rc != CSR_OK) return rc;
+        if (!layout_ok(p, parts, whole_below)) return set_err(ctx, CSR_ERR_SHAPE, "no such layout for this problem");
+        rc = check_workspace(ctx, p, csrh::kHeadBytes);
+        if (rc != CSR_OK) return rc;
+        DeviceGuard g(ctx->device);
+        hipStream_t st = static_cast<hipStream_t>(p.stream);
+        int64_t hist[csrh::kHistInts];
+        rc = histogram(ctx, p, st, hist);
+        if (rc != CSR_OK) return rc;
+        size_t need_mem = 0, need_ws = 0;
+        layout_sizes(p, hist, parts, whole_below, &need_mem, &need_ws);
+        if (!plan_mem || plan_bytes < need_mem || (uintptr_t)plan_mem % csrh::kAlign)
+            return set_err(ctx, CSR_ERR_WORKSPACE, "plan memory NULL, unaligned or below " + std::to_string(need_mem) +
+                                                       " bytes");
+        rc = check_workspace(ctx, p, need_ws);
+        if (rc != CSR_OK) return rc;
+        PlanBuild b(ctx, p, hist, plan_mem);
+        csrh::PlanChoice c;
+        c.parts = parts;
+        c.whole_below = parts == 1 ? 0 : whole_below;
+        if (sched) {
+            c.sched = *sched;
+        } else if (parts == 1) {
+            rc = select_locked(ctx, p, CSR_SELECT_AUTO, &c.sched, nullptr, nullptr);
+        } else if (parts == 0) {
+            rc = b.build_bucket(whole_below);
+            if (rc == CSR_OK) rc = select_locked(ctx, b.long_problem(), CSR_SELECT_AUTO, &c.sched, nullptr, nullptr);
+        } else {
+            rc = b.build(parts, whole_below);
+            HybridCall hc;
+            if (rc == CSR_OK) rc = b.call(&hc, nullptr);
+            if (rc == CSR_OK) rc = select_locked(ctx, hc.p, CSR_SELECT_AUTO, &c.sched, nullptr, &hc.maps);
+        }
+        if (rc != CSR_OK) return rc;
+        rc = materialize_plan(b, c, csrh::plan_signature(p, hist, ctx->dev), 0.0, plan);
+        if (rc == CSR_OK) ctx->last_error.clear();
+        return rc;
+    } catch (...) {
+        return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+    }
+}
+
 int csr_plan_spmm(csr_context_t ctx, const csr_plan_t* plan, const float* vals, const void* X, int64_t ldx, float* Y,
                   int64_t ldy, void* workspace, size_t ws_bytes, void* stream)
 {
@@ -1874,6 +2118,51 @@ int csr_plan_spmm(csr_context_t ctx, const csr_plan_t* plan, const float* vals, 
             rc = check_workspace(ctx, p, csrh::workspace_bytes(p, plan->sched));
             if (rc != CSR_OK) return rc;
             return run_schedule(ctx, p, plan->sched, st);
+        }
+        if (plan->parts == 0) {
+            const csr_bucket_t& bk = plan->bkt;
+            csr_problem_t p = blank_problem();
+            p.op = CSR_OP_SPMM;
+            p.dtype = plan->dtype;
+            p.n_rows = plan->n_rows;
+            p.n_cols = plan->n_cols;
+            p.nnz = plan->nnz;
+            p.width = plan->width;
+            p.ld_b = ldx;
+            p.ld_out = ldy;
+            p.row_ptr = plan->row_ptr;
+            p.col_idx = plan->col_idx;
+            p.a = bk.long_val;
+            p.b = X;
+            p.out = Y;
+            p.workspace = workspace;
+            p.workspace_bytes = ws_bytes;
+            p.stream = stream;
+            rc = csrh::check_problem(p, true, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            const size_t tail = up256((size_t)bk.n_slots * 4) + up256((size_t)bk.nnz_long * 4);
+            if (!workspace || ws_bytes < plan->workspace_bytes || plan->workspace_bytes < tail ||
+                (uintptr_t)workspace % csrh::kAlign)
+                return set_err(ctx, CSR_ERR_WORKSPACE, "workspace NULL, unaligned or below the plan's workspace_bytes");
+            p.workspace_bytes = plan->workspace_bytes - tail;
+            const csr_problem_t q = bucket_long_problem(p, bk, bk.long_val);
+            rc = csrh::check_schedule(q, plan->sched, &why);
+            if (rc != CSR_OK) return set_err(ctx, rc, why);
+            rc = check_workspace(ctx, q, csrh::workspace_bytes(q, plan->sched));
+            if (rc != CSR_OK) return rc;
+            // this call's own values go into slot and long-row order at the end of the workspace
+            const float* sv = bk.slot_val;
+            const float* lv = bk.long_val;
+            if (vals) {
+                char* t = static_cast<char*>(workspace) + plan->workspace_bytes - tail;
+                float* s2 = reinterpret_cast<float*>(t);
+                float* l2 = reinterpret_cast<float*>(t + up256((size_t)bk.n_slots * 4));
+                CSR_HIP(ctx, csrk::launch_gather_or_zero(bk.slot_pos, vals, s2, bk.n_slots, st));
+                CSR_HIP(ctx, csrk::launch_gather_or_zero(bk.long_pos, vals, l2, bk.nnz_long, st));
+                sv = s2;
+                lv = l2;
+            }
+            return bucket_run(ctx, p, bk, plan->sched, sv, lv, st);
         }
         if (plan->width < 1 || ldy < plan->width || ldy >= ((int64_t)1 << 30))
             return set_err(ctx, CSR_ERR_SHAPE, "bad width or ldy");

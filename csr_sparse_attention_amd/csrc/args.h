@@ -42,6 +42,27 @@ struct Fp32Args {
     const int32_t* ev_idx;
 };
 
+// SpMM over the packed short rows of the degree classes (class c = 0 .. 5
+// holds rows of 2^c .. 2^(c+1) - 1 entries, 2^(c+1) - 1 slots each, slot j of
+// its row i at slot index base[c] + j * rows[c] + i)
+struct BucketArgs {
+    const int32_t* rows;      // packed rows, class by class
+    const int32_t* slot_col;  // -1: padding
+    const float* slot_val;
+    int32_t n_classes;
+    int32_t F;
+    int32_t W;                // lanes per row group
+    int32_t pad_;
+    int64_t cls_rows[6];
+    int64_t cls_base[6];
+    int64_t cls_row0[6];
+    int64_t cls_block0[7];    // first workgroup of each class; [n_classes] = the grid
+    const void* X;
+    int64_t ldx;
+    float* Y;
+    int64_t ldy;
+};
+
 struct MhaArgs {
     const int32_t* row_ptr;
     const int32_t* col_idx;

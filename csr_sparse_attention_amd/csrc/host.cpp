@@ -713,6 +713,57 @@ std::vector<std::pair<int, int>> plan_formats(const csr_problem_t& p, const int6
     return out;
 }
 
+BucketShape bucket_shape(const csr_problem_t& p, const int64_t* hist, int E)
+{
+    BucketShape b;
+    b.E = E;
+    int n = 0;
+    while ((1 << n) < E && n < CSR_BUCKET_MAX_CLASSES) ++n;
+    b.n_classes = n;
+    int64_t slots = 0, rows = 0;
+    for (int c = 1; c <= n; ++c) {
+        const int64_t cnt = hist ? hist[c] : 0;
+        b.class_rows[c - 1] = cnt;
+        b.class_base[c - 1] = slots;
+        b.class_row0[c - 1] = rows;
+        slots += cnt * (((int64_t)1 << c) - 1);
+        rows += cnt;
+        b.nnz_short += hist ? hist[33 + c] : 0;
+    }
+    b.n_short = rows;
+    b.n_slots = slots;
+    b.nnz_long = std::max<int64_t>(0, p.nnz - b.nnz_short);
+    return b;
+}
+
+BucketLayout bucket_layout(const csr_problem_t& p, const BucketShape& b)
+{
+    auto up = [](size_t v) { return (v + kAlign - 1) / kAlign * kAlign; };
+    BucketLayout L{};
+    L.rows = 0;
+    L.slot_col = L.rows + up((size_t)p.n_rows * 4);
+    L.slot_pos = L.slot_col + up((size_t)b.n_slots * 4);
+    L.slot_val = L.slot_pos + up((size_t)b.n_slots * 4);
+    L.long_row_ptr = L.slot_val + up((size_t)b.n_slots * 4);
+    L.long_col = L.long_row_ptr + up((size_t)(p.n_rows + 1) * 4);
+    L.long_pos = L.long_col + up((size_t)b.nnz_long * 4);
+    L.long_val = L.long_pos + up((size_t)b.nnz_long * 4);
+    L.total = L.long_val + up((size_t)b.nnz_long * 4);
+    return L;
+}
+
+std::vector<int> plan_buckets(const csr_problem_t& p, const int64_t* hist)
+{
+    std::vector<int> out;
+    if (p.op != CSR_OP_SPMM || !hist || p.n_rows <= 0 || p.nnz <= 0 || p.n_cols <= 0) return out;
+    for (int E : {8, 32}) {
+        const BucketShape b = bucket_shape(p, hist, E);
+        if (b.n_short * 4 >= p.n_rows && b.nnz_short * 10 >= p.nnz && b.n_slots - b.nnz_short <= b.nnz_short)
+            out.push_back(E);
+    }
+    return out;
+}
+
 std::string format_plan_line(uint64_t sig, const PlanChoice& c, double probe_us)
 {
     char buf[288];
@@ -742,7 +793,12 @@ bool parse_plan_line(const std::string& line, uint64_t* sig, PlanChoice* c, doub
     for (size_t i = (size_t)n; i < line.size(); ++i)
         if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
     if (s.op != CSR_OP_SPMM && s.op != CSR_OP_SDDMM) return false;
-    if (t.parts < 1 || t.parts > 256 || (t.parts & (t.parts - 1)) || t.whole_below < 0) return false;
+    if (t.parts == 0) {  // degree classes: whole_below is the short threshold (SpMM)
+        const int E = t.whole_below;
+        if (s.op != CSR_OP_SPMM || E < 2 || E > (1 << CSR_BUCKET_MAX_CLASSES) || (E & (E - 1))) return false;
+    } else if (t.parts < 1 || t.parts > 256 || (t.parts & (t.parts - 1)) || t.whole_below < 0) {
+        return false;
+    }
     if (s.mapping != CSR_MAP_ROWGROUP && s.mapping != CSR_MAP_MERGEPATH && s.mapping != CSR_MAP_SEGSCAN) return false;
     s.version = CSR_SCHEDULE_VERSION;
     *sig = sg;

@@ -85,11 +85,12 @@ std::string format_cache_line(uint64_t sig, const csr_schedule_t& s, double prob
 bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s, double* probe_us);
 
 // Planned products (a CSR matrix prepared for one SpMM / SDDMM): the joint
-// choice of layout (plain CSR, or the column-part segment format with its
-// parts and whole-row threshold) and of the product's schedule.
+// choice of layout (plain CSR, the column-part segment format with its
+// parts and whole-row threshold, or the degree classes with their short
+// threshold) and of the product's schedule.
 struct PlanChoice {
-    int parts = 1;        // 1: the plain pattern
-    int whole_below = 0;
+    int parts = 1;        // 1: the plain pattern; 0: degree classes
+    int whole_below = 0;  // the format's whole-row threshold, or the classes' short threshold
     csr_schedule_t sched{};
 };
 
@@ -107,6 +108,31 @@ int64_t segment_bound(const csr_problem_t& p, const int64_t* hist, int P, int T)
 // the plain pattern chosen by the model, 4 and 16 parts when one part of the
 // gathered operand would still hold at least 2 MiB.  (parts, whole_below) pairs.
 std::vector<std::pair<int, int>> plan_formats(const csr_problem_t& p, const int64_t* hist);
+
+// Degree classes with short threshold E (a power of two, 2 .. 64): the shape
+// from the degree histogram (class c = bucket c of the histogram, degrees
+// [2^(c-1), 2^c), padded to 2^c - 1 slots).
+struct BucketShape {
+    int E = 0, n_classes = 0;
+    int64_t class_rows[CSR_BUCKET_MAX_CLASSES] = {0};
+    int64_t class_base[CSR_BUCKET_MAX_CLASSES] = {0};  // first slot of each class
+    int64_t class_row0[CSR_BUCKET_MAX_CLASSES] = {0};  // first packed row of each class
+    int64_t n_short = 0, n_slots = 0, nnz_short = 0, nnz_long = 0;
+};
+BucketShape bucket_shape(const csr_problem_t& p, const int64_t* hist, int E);
+
+// Plan memory of the degree classes: rows, slot columns, slot entries, slot
+// values, the long rows' row_ptr, columns, entries and values (byte offsets).
+struct BucketLayout {
+    size_t rows, slot_col, slot_pos, slot_val, long_row_ptr, long_col, long_pos, long_val, total;
+};
+BucketLayout bucket_layout(const csr_problem_t& p, const BucketShape& b);
+
+// The short thresholds a plan of p weighs (SpMM only): 8 and 32 where at
+// least a quarter of the rows are nonempty and shorter, those rows hold at
+// least a tenth of the entries (the long rows' product dominates otherwise),
+// and padding stays under one slot per entry.
+std::vector<int> plan_buckets(const csr_problem_t& p, const int64_t* hist);
 
 std::string format_plan_line(uint64_t sig, const PlanChoice& c, double probe_us);
 bool parse_plan_line(const std::string& line, uint64_t* sig, PlanChoice* c, double* probe_us);

@@ -48,6 +48,20 @@ hipError_t launch_attention_bf16(int mapping, int vec, int nv, int chunk, const 
 hipError_t launch_attention_qk(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention_qk_bf16(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_attention_qk_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
+// degree classes: the SpMM of the packed short rows (T = float or bf16 by
+// dtype; vec, nv the lane layout of one row), and the construction
+hipError_t launch_bucket_spmm(int dtype_bf16, int vec, int nv, const BucketArgs& a, hipStream_t s);
+hipError_t bucket_build_workspace(int64_t n_rows, int64_t nnz, size_t* bytes);
+// rows: the packed rows (stable by class), slot_col / slot_pos, long_row_ptr,
+// long_col / long_pos of the rows with at least E entries or none;
+// cls_* as in BucketArgs.
+hipError_t launch_bucket_build(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t nnz, int E,
+                               int n_classes, const int64_t* cls_rows, const int64_t* cls_base,
+                               const int64_t* cls_row0, int32_t* rows, int32_t* slot_col, int32_t* slot_pos,
+                               int32_t* long_row_ptr, int32_t* long_col, int32_t* long_pos, void* ws,
+                               size_t ws_bytes, hipStream_t s);
+// dst[k] = pos[k] >= 0 ? (src ? src[pos[k]] : 1) : 0 for k < n
+hipError_t launch_gather_or_zero(const int32_t* pos, const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_mha(int mapping, int lph, int chunk, const MhaArgs& a, hipStream_t s);
 hipError_t launch_mha_fixup(int lph, const MhaArgs& a, hipStream_t s);
 

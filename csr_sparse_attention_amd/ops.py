@@ -899,8 +899,9 @@ def hybrid_sddmm(h: Hybrid, U, V, *, out=None, schedule: Optional[CsrSchedule] =
 
 class Plan:
     """A CSR matrix prepared for one SpMM or SDDMM (csr_plan_t): the chosen
-    layout and schedule, the plan memory that holds its arrays, and the
-    tensors it refers to (kept alive with it)."""
+    layout (the plain pattern, the column-part format, or the degree classes)
+    and schedule, the plan memory that holds its arrays, and the tensors it
+    refers to (kept alive with it)."""
 
     def __init__(self, desc: CsrPlan, mem, keep):
         self.desc = desc
@@ -928,6 +929,11 @@ class Plan:
         return self.desc.signature
 
     @property
+    def layout(self) -> str:
+        """'plain' (the caller's CSR), 'format' (column parts) or 'classes' (degree classes)."""
+        return {0: "classes", 1: "plain"}.get(self.desc.parts, "format")
+
+    @property
     def n_seg(self) -> int:
         return self.desc.fmt.n_seg if self.desc.parts > 1 else 0
 
@@ -940,17 +946,28 @@ class Plan:
         return self.parts, self.whole_below, self.schedule.as_dict()
 
     def __repr__(self):
-        return (f"Plan({self.op}, parts={self.parts}, whole_below={self.whole_below}, n_seg={self.n_seg}, "
-                f"{self.schedule}, probe_ms={self.desc.probe_ms:.3f})")
+        if self.desc.parts == 0:
+            b = self.desc.bkt
+            shape = f"short_below={b.short_below}, n_short={b.n_short}, n_slots={b.n_slots}, nnz_long={b.nnz_long}"
+        else:
+            shape = f"parts={self.parts}, whole_below={self.whole_below}, n_seg={self.n_seg}"
+        return f"Plan({self.op}, {self.layout}, {shape}, {self.schedule}, probe_ms={self.desc.probe_ms:.3f})"
 
 
-def plan(op: str, row_ptr, col_idx, *operands, mode: str = "auto", out=None, ctx: Optional[Context] = None) -> Plan:
+def plan(op: str, row_ptr, col_idx, *operands, mode: str = "auto", layout=None,
+         schedule: Optional[CsrSchedule] = None, out=None, ctx: Optional[Context] = None) -> Plan:
     """Plans a product ('spmm': vals or None, X; 'sddmm': U, V): the library
     chooses the layout and the schedule together by its cost model and
     micro-probes on these operands (the probes write ``out``), or replays the
-    cached choice.  Synchronous."""
+    cached choice.  With ``layout`` = (parts, whole_below) the plan takes that
+    layout (parts 1 the plain pattern, 2 .. 256 the column-part format, 0 the
+    degree classes with short threshold whole_below) and ``schedule`` for its
+    product, or the selector's schedule when none is given (csr_plan_build;
+    nothing cached).  Synchronous."""
     if op not in ("spmm", "sddmm"):
         raise ValueError("plans serve 'spmm' and 'sddmm'")
+    if schedule is not None and layout is None:
+        raise ValueError("a schedule is given with a layout")
     p, out = make_problem(op, row_ptr, col_idx, *operands, out=out)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)
@@ -958,15 +975,24 @@ def plan(op: str, row_ptr, col_idx, *operands, mode: str = "auto", out=None, ctx
     head = _workspace(device, 1024)
     p.workspace, p.workspace_bytes, p.stream = head.data_ptr(), 1024, _stream(device)
     mem_bytes, ws_bytes = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib.csr_plan_size(ctx.handle, ctypes.byref(p), ctypes.byref(mem_bytes), ctypes.byref(ws_bytes)),
-           "csr_plan_size", ctx)
+    if layout is None:
+        _check(lib.csr_plan_size(ctx.handle, ctypes.byref(p), ctypes.byref(mem_bytes), ctypes.byref(ws_bytes)),
+               "csr_plan_size", ctx)
+    else:
+        parts, whole = (int(v) for v in layout)
+        _check(lib.csr_plan_layout_size(ctx.handle, ctypes.byref(p), parts, whole, ctypes.byref(mem_bytes),
+                                        ctypes.byref(ws_bytes)), "csr_plan_layout_size", ctx)
     mem = torch.empty(mem_bytes.value + 256, dtype=torch.uint8, device=device)
     off = (-mem.data_ptr()) % 256
     ws = _workspace(device, ws_bytes.value)
     p.workspace, p.workspace_bytes = ws.data_ptr(), ws_bytes.value
     desc = CsrPlan()
-    _check(lib.csr_plan_create(ctx.handle, ctypes.byref(p), _ffi.SELECT_MODES[mode], mem.data_ptr() + off,
-                               mem_bytes.value, ctypes.byref(desc)), "csr_plan_create", ctx)
+    if layout is None:
+        _check(lib.csr_plan_create(ctx.handle, ctypes.byref(p), _ffi.SELECT_MODES[mode], mem.data_ptr() + off,
+                                   mem_bytes.value, ctypes.byref(desc)), "csr_plan_create", ctx)
+    else:
+        _check(lib.csr_plan_build(ctx.handle, ctypes.byref(p), parts, whole, _sched_arg(schedule),
+                                  mem.data_ptr() + off, mem_bytes.value, ctypes.byref(desc)), "csr_plan_build", ctx)
     keep = (row_ptr, col_idx) + tuple(t for t in operands if t is not None)
     return Plan(desc, mem, keep)
 

@@ -530,19 +530,50 @@ int csr_hybrid_select(csr_context_t ctx, const csr_hybrid_t* h, const csr_proble
  * (the format, the values in format order) live in caller memory sized by
  * csr_plan_size.
  * ------------------------------------------------------------------------- */
-#define CSR_PLAN_VERSION 1
+#define CSR_PLAN_VERSION 2
+
+/* Degree classes (SparseTIR page, Abstract: composable formats; rows
+ * bucketed by degree, the short ones packed ELL-style): the rows with 1 to
+ * short_below - 1 entries are grouped by class c = 1 .. n_classes (degrees
+ * [2^(c-1), 2^c)), each class padded to 2^c - 1 slots per row and stored
+ * slot-major (slot j of the class's row i at class_base + j * rows_in_class
+ * + i), so that a row per lane group reads its slots with the loads of the
+ * neighbouring rows; the other rows (empty or long) form a CSR of their own
+ * on the same row numbering, in which the packed rows are empty.  SpMM only.
+ * Built by csr_plan_create into the plan memory. */
+#define CSR_BUCKET_MAX_CLASSES 6
+
+typedef struct csr_bucket_s {
+    int32_t short_below;      /* 2, 4, ..., 64: rows with fewer entries (and at least one) are packed */
+    int32_t n_classes;        /* log2(short_below) */
+    int64_t n_short;          /* packed rows */
+    int64_t n_slots;          /* packed slots, entries and padding */
+    int64_t nnz_long;         /* entries of the other rows */
+    int64_t class_rows[CSR_BUCKET_MAX_CLASSES]; /* rows of classes 1 .. n_classes */
+    int32_t* rows;            /* [n_rows]: the packed rows, class by class, each class in row order */
+    int32_t* slot_col;        /* [n_slots] column of each slot, -1 for padding (after a row's entries) */
+    int32_t* slot_pos;        /* [n_slots] the entry behind each slot, -1 for padding */
+    float* slot_val;          /* [n_slots] its value (0 for padding) */
+    int32_t* long_row_ptr;    /* [n_rows + 1] the other rows' CSR */
+    int32_t* long_col;        /* [nnz_long] */
+    int32_t* long_pos;        /* [nnz_long] the entry behind each long entry */
+    float* long_val;          /* [nnz_long] */
+} csr_bucket_t;
 
 typedef struct csr_plan_s {
     int32_t version;          /* CSR_PLAN_VERSION */
     int32_t op;               /* CSR_OP_SPMM or CSR_OP_SDDMM */
     int32_t dtype;            /* element type of the dense operands */
-    int32_t parts;            /* 1: the plain pattern; otherwise the format's column parts */
-    int32_t whole_below;      /* the format's whole-row threshold */
+    int32_t parts;            /* 1: the plain pattern; 0: degree classes (bkt); otherwise the
+                                 column-part format's parts (fmt) */
+    int32_t whole_below;      /* the format's whole-row threshold; with parts 0, bkt.short_below */
     int32_t reserved_;
     int64_t n_rows, n_cols, nnz, width;
     uint64_t signature;       /* the cache key of the choice */
-    csr_schedule_t sched;     /* the product's schedule (on the segment pattern when parts > 1) */
+    csr_schedule_t sched;     /* the product's schedule (on the segment pattern when parts > 1, on
+                                 the long rows' CSR when parts is 0) */
     csr_hybrid_t fmt;         /* the format (parts > 1), its arrays in the plan memory */
+    csr_bucket_t bkt;         /* the degree classes (parts 0), their arrays in the plan memory */
     const int32_t* row_ptr;   /* the plain pattern: the caller's arrays, which must stay valid */
     const int32_t* col_idx;
     float* vals;              /* SpMM: the values the product reads (the caller's array on the
@@ -572,6 +603,25 @@ int csr_plan_size(csr_context_t ctx, const csr_problem_t* p, size_t* plan_bytes,
  * they must outlive it.  Synchronous. */
 int csr_plan_create(csr_context_t ctx, const csr_problem_t* p, uint32_t mode, void* plan_mem, size_t plan_bytes,
                     csr_plan_t* plan);
+
+/* Sizes for a plan of p in one given layout: parts 1 (the plain pattern),
+ * 2 .. 256 (the column-part format, a power of two, whole_below >= 0 its
+ * whole-row threshold) or 0 (SpMM: degree classes, whole_below the short
+ * threshold, a power of two from 2 to 64).  As csr_plan_size otherwise;
+ * CSR_ERR_SHAPE for a layout outside these rules. */
+int csr_plan_layout_size(csr_context_t ctx, const csr_problem_t* p, int32_t parts, int32_t whole_below,
+                         size_t* plan_bytes, size_t* workspace_bytes);
+
+/* Plans p in the given layout (rules of csr_plan_layout_size) with schedule
+ * sched for the product on that layout (the plain pattern, the segment
+ * pattern of the format, or the long rows of the degree classes), or with
+ * sched NULL the selector's choice for it (csr_select on that product, with
+ * its cache).  For replaying a known choice and for measuring layouts one
+ * by one; no plan choice is cached.  plan memory and workspace of
+ * csr_plan_layout_size.  CSR_ERR_SCHEDULE when sched does not fit the
+ * layout's product.  Synchronous. */
+int csr_plan_build(csr_context_t ctx, const csr_problem_t* p, int32_t parts, int32_t whole_below,
+                   const csr_schedule_t* sched, void* plan_mem, size_t plan_bytes, csr_plan_t* plan);
 
 /* Y = A X with a plan of op CSR_OP_SPMM: X [n_cols, ldx] of the plan's dtype,
  * Y fp32 [n_rows, ldy], with the alignment and leading-dimension class the

@@ -280,6 +280,90 @@ int main(int argc, char** argv)
               (long long)segs, (long long)bound, (long long)loose, P, T);
         ++seg_checks;
     }
+    // plan log lines (plain, format, degree classes) round trip; the degree
+    // classes' shape agrees with a row-by-row count of a random pattern
+    int64_t bucket_checks = 0;
+    for (int it = 0; it < iters / 50; ++it) {
+        csrh::PlanChoice c;
+        const int kind = (int)(next() % 3);
+        c.parts = kind == 0 ? 1 : (kind == 1 ? 2 << (next() % 7) : 0);
+        c.whole_below = kind == 2 ? 2 << (next() % 6) : (int)(next() % 3) * 64;
+        c.sched = csrh::default_schedule([] {
+            csr_problem_t q;
+            std::memset(&q, 0, sizeof q);
+            q.op = CSR_OP_SPMM;
+            q.width = 32;
+            q.ld_b = q.ld_out = 32;
+            q.b = q.out = reinterpret_cast<void*>(0x1000);
+            return q;
+        }());
+        const uint64_t sg = next();
+        const std::string line = csrh::format_plan_line(sg, c, 12.5);
+        uint64_t sg2 = 0;
+        csrh::PlanChoice c2;
+        double us = 0;
+        CHECK(csrh::parse_plan_line(line, &sg2, &c2, &us) && sg2 == sg && c2.parts == c.parts &&
+                  c2.whole_below == c.whole_below && std::memcmp(&c2.sched, &c.sched, sizeof c.sched) == 0,
+              "plan line round trip: %s", line.c_str());
+        // a degree-class line for SDDMM or with a threshold that is no power of two is refused
+        csrh::PlanChoice bad = c;
+        bad.parts = 0;
+        bad.whole_below = 3 + 2 * (int)(next() % 10);
+        CHECK(!csrh::parse_plan_line(csrh::format_plan_line(sg, bad, 1.0), &sg2, &c2, &us), "bad class line parsed\n");
+
+        const int64_t n_rows = 1 + (int64_t)(next() % 400);
+        std::vector<int64_t> deg(n_rows);
+        int64_t nnz = 0;
+        int64_t h[csrh::kHistInts] = {0};
+        for (auto& d : deg) {
+            d = (next() % 3 == 0) ? (int64_t)(next() % 200) : (int64_t)(next() % 9);
+            nnz += d;
+            int b = 0;
+            while (b < 32 && ((int64_t)1 << b) <= d) ++b;
+            h[b] += 1;
+            h[33 + b] += d;
+            h[66] = std::max(h[66], d);
+        }
+        csr_problem_t p;
+        std::memset(&p, 0, sizeof p);
+        p.op = CSR_OP_SPMM;
+        p.n_rows = n_rows;
+        p.n_cols = 1000;
+        p.nnz = nnz;
+        p.width = 4;
+        const int E = 2 << (next() % 6);
+        const csrh::BucketShape sh = csrh::bucket_shape(p, h, E);
+        int64_t n_short = 0, slots = 0, nnz_long = 0, per_class[CSR_BUCKET_MAX_CLASSES] = {0};
+        for (int64_t d : deg) {
+            if (d >= 1 && d < E) {
+                int c = 0;
+                while (((int64_t)2 << c) <= d) ++c;  // 2^c <= d < 2^(c+1)
+                ++per_class[c];
+                ++n_short;
+                slots += ((int64_t)2 << c) - 1;
+            } else {
+                nnz_long += d;
+            }
+        }
+        bool same = sh.n_short == n_short && sh.n_slots == slots && sh.nnz_long == nnz_long &&
+                    sh.nnz_short + sh.nnz_long == nnz && (1 << sh.n_classes) == E;
+        int64_t row0 = 0, base = 0;
+        for (int c = 0; c < sh.n_classes; ++c) {
+            same = same && sh.class_rows[c] == per_class[c] && sh.class_row0[c] == row0 && sh.class_base[c] == base;
+            row0 += per_class[c];
+            base += per_class[c] * (((int64_t)2 << c) - 1);
+        }
+        const csrh::BucketLayout L = csrh::bucket_layout(p, sh);
+        same = same && L.total >= (size_t)(n_rows * 4 + 3 * slots * 4 + (n_rows + 1) * 4 + 3 * nnz_long * 4) &&
+               L.slot_col % 256 == 0 && L.long_val % 256 == 0;
+        CHECK(same, "degree classes E %d: n_short %lld/%lld slots %lld/%lld nnz_long %lld/%lld\n", E,
+              (long long)sh.n_short, (long long)n_short, (long long)sh.n_slots, (long long)slots,
+              (long long)sh.nnz_long, (long long)nnz_long);
+        for (int e2 : csrh::plan_buckets(p, h))
+            CHECK(e2 == 8 || e2 == 32, "plan_buckets offered %d\n", e2);
+        ++bucket_checks;
+    }
+    std::printf("degree-class checks %lld\n", (long long)bucket_checks);
     std::printf("iterations %d accepted problems %d planned formats %d corrupted lines parsed %d segment bounds %lld "
                 "failures %d\n", iters, accepted, planned, parsed, (long long)seg_checks, failures);
     return failures ? 1 : 0;
