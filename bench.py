@@ -740,7 +740,9 @@ def main():
     ap.add_argument("--vendor", action="store_true",
                     help="also time the SpMM / SDDMM calls with rocSPARSE (a measured comparison, not a dispatch)")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run one device copy of 1 GiB (a known-size reference for HBM counters)")
+                    help="for counter runs: first run one device copy of 1 GiB (a known-size reference for HBM "
+                         "counters), and launch a short spin kernel before each call of the timed steps (outside "
+                         "its timed region) so that the dispatches can be told apart by call")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's hot path runs on a single MI355X "
@@ -809,6 +811,8 @@ def main():
     for k in range(args.steps):
         for c in calls:
             a, b = cev[c.name][k]
+            if args.calibrate_copy:
+                torch.cuda._sleep(1)  # a spin kernel before each call: counter runs split the dispatches by call
             a.record(stream)
             c.run()
             b.record(stream)
@@ -847,6 +851,11 @@ def main():
     achieved = hbm_bytes / (dom_ms * 1e-3) / 1e9
     for c in calls:
         kernels[c.name]["bytes_compulsory"] = compulsory_bytes(c, torch)
+        # counted HBM bytes of the call (committed counter record for these sources, layout and schedule)
+        t = committed_traffic(args.config, c) if c.op != "gather" else None
+        kernels[c.name]["traffic_bytes"] = t
+        kernels[c.name]["frac_hbm_counted"] = (round(t / (kernels[c.name]["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                               if t else None)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
