@@ -523,120 +523,146 @@ def cold_times(calls, torch, reps=5, flush_gib=1):
     return out
 
 
-def vendor_compare(calls, torch, reps=5):
-    """The same SpMM and SDDMM calls timed with the vendor library (rocSPARSE's
-    generic API through ctypes; a measurement beside the library, never a
-    dispatch target): every CSR SpMM algorithm it offers for row-major dense
-    operands, the analysis / preprocess stage outside the timed region, median
-    of ``reps`` HIP-event timed compute calls.  Returns per call the vendor
-    times and the ratio vendor best / this library."""
-    import ctypes
+class Rocsparse:
+    """rocSPARSE's generic CSR SpMM and SDDMM through ctypes: a measurement
+    beside this library, never a dispatch target.  Each call takes device
+    tensors and returns (median ms of ``reps`` HIP-event timed compute calls,
+    status); the analysis / preprocess stage runs outside the timed region."""
 
-    try:
-        rs = ctypes.CDLL("librocsparse.so.1")
-    except OSError as e:  # pragma: no cover - library not installed
-        return {"error": str(e)}
-    P, I64 = ctypes.c_void_p, ctypes.c_int64
-    OP_N, OP_T, I32, BASE0, F32, ROW = 111, 112, 2, 0, 151, 0
     ALGS = {"default": 0, "csr_row_split": 4, "csr_nnz_split": 5, "csr_merge_path": 9}
-    h = P()
-    assert rs.rocsparse_create_handle(ctypes.byref(h)) == 0
-    stream = torch.cuda.current_stream()
-    rs.rocsparse_set_stream(h, P(stream.cuda_stream))
-    rs.rocsparse_create_csr_descr.argtypes = [ctypes.POINTER(P), I64, I64, I64, P, P, P, ctypes.c_int, ctypes.c_int,
-                                              ctypes.c_int, ctypes.c_int]
-    rs.rocsparse_create_dnmat_descr.argtypes = [ctypes.POINTER(P), I64, I64, I64, P, ctypes.c_int, ctypes.c_int]
-    rs.rocsparse_spmm.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_int, ctypes.POINTER(ctypes.c_size_t), P]
-    for f in ("rocsparse_sddmm_buffer_size",):
-        getattr(rs, f).argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
-                                   ctypes.POINTER(ctypes.c_size_t)]
-    for f in ("rocsparse_sddmm_preprocess", "rocsparse_sddmm"):
-        getattr(rs, f).argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P]
-    one, zero = ctypes.c_float(1.0), ctypes.c_float(0.0)
 
-    def timed(fn):
+    def __init__(self, torch, reps=5):
+        import ctypes
+
+        self.ct, self.torch, self.reps = ctypes, torch, reps
+        self.rs = ctypes.CDLL("librocsparse.so.1")  # OSError when not installed
+        P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        rs = self.rs
+        self.h = P()
+        assert rs.rocsparse_create_handle(ctypes.byref(self.h)) == 0
+        self.stream = torch.cuda.current_stream()
+        rs.rocsparse_set_stream(self.h, P(self.stream.cuda_stream))
+        rs.rocsparse_create_csr_descr.argtypes = [ctypes.POINTER(P), I64, I64, I64, P, P, P, INT, INT, INT, INT]
+        rs.rocsparse_create_dnmat_descr.argtypes = [ctypes.POINTER(P), I64, I64, I64, P, INT, INT]
+        rs.rocsparse_spmm.argtypes = [P, INT, INT, P, P, P, P, P, INT, INT, INT, ctypes.POINTER(ctypes.c_size_t), P]
+        rs.rocsparse_sddmm_buffer_size.argtypes = [P, INT, INT, P, P, P, P, P, INT, INT,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        for f in ("rocsparse_sddmm_preprocess", "rocsparse_sddmm"):
+            getattr(rs, f).argtypes = [P, INT, INT, P, P, P, P, P, INT, INT, P]
+        self.one, self.zero = ctypes.c_float(1.0), ctypes.c_float(0.0)
+
+    def close(self):
+        self.rs.rocsparse_destroy_handle(self.h)
+
+    def _timed(self, fn):
         ts = []
-        fn()
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+        if fn() != 0:
+            return None, -1
+        for _ in range(self.reps):
+            a, b = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
             rc = fn()
-            b.record(stream)
+            b.record(self.stream)
             b.synchronize()
             if rc != 0:
                 return None, rc
             ts.append(a.elapsed_time(b))
         return float(np.median(ts)), 0
 
-    out = {}
-    for c in calls:
-        if c.op not in ("spmm", "sddmm"):
-            continue
-        rp, ci = c.args[0], c.args[1]
+    def spmm(self, rp, ci, vals, X, Y, alg):
+        """Y = A X (fp32, row-major X and Y) with rocSPARSE algorithm ``alg``."""
+        ct, rs, P = self.ct, self.rs, self.ct.c_void_p
         n_rows, nnz = rp.numel() - 1, ci.numel()
-        res = {}
-        if c.op == "spmm":
-            vals, X = c.args[2], c.args[3]
-            Y = c.kwargs["out"]
-            v = vals if vals is not None else torch.ones(nnz, device=X.device)
-            A, B, C = P(), P(), P()
-            rs.rocsparse_create_csr_descr(ctypes.byref(A), n_rows, X.shape[0], nnz, P(rp.data_ptr()),
-                                          P(ci.data_ptr()), P(v.data_ptr()), I32, I32, BASE0, F32)
-            rs.rocsparse_create_dnmat_descr(ctypes.byref(B), X.shape[0], X.shape[1], X.stride(0), P(X.data_ptr()),
-                                            F32, ROW)
-            rs.rocsparse_create_dnmat_descr(ctypes.byref(C), n_rows, X.shape[1], Y.stride(0), P(Y.data_ptr()),
-                                            F32, ROW)
-            for name, alg in ALGS.items():
-                sz = ctypes.c_size_t(0)
-                rc = rs.rocsparse_spmm(h, OP_N, OP_N, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32, alg, 1,
-                                       ctypes.byref(sz), None)
-                if rc != 0:
-                    res[name] = f"status {rc}"
-                    continue
-                buf = torch.empty(max(1, sz.value), dtype=torch.uint8, device=X.device)
-                rc = rs.rocsparse_spmm(h, OP_N, OP_N, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32, alg, 2,
-                                       ctypes.byref(sz), P(buf.data_ptr()))
-                if rc != 0:
-                    res[name] = f"status {rc}"
-                    continue
-                ms, rc = timed(lambda: rs.rocsparse_spmm(h, OP_N, OP_N, ctypes.byref(one), A, B, ctypes.byref(zero),
-                                                         C, F32, alg, 3, ctypes.byref(sz), P(buf.data_ptr())))
-                res[name] = round(ms, 4) if ms is not None else f"status {rc}"
-                del buf
-            for d_ in (B, C):
-                rs.rocsparse_destroy_dnmat_descr(d_)
+        v = vals if vals is not None else self.torch.ones(nnz, device=X.device)
+        A, B, C = P(), P(), P()
+        rs.rocsparse_create_csr_descr(ct.byref(A), n_rows, X.shape[0], nnz, P(rp.data_ptr()), P(ci.data_ptr()),
+                                      P(v.data_ptr()), 2, 2, 0, 151)
+        rs.rocsparse_create_dnmat_descr(ct.byref(B), X.shape[0], X.shape[1], X.stride(0), P(X.data_ptr()), 151, 0)
+        rs.rocsparse_create_dnmat_descr(ct.byref(C), n_rows, X.shape[1], Y.stride(0), P(Y.data_ptr()), 151, 0)
+        try:
+            sz = ct.c_size_t(0)
+            args = lambda stage, buf: (self.h, 111, 111, ct.byref(self.one), A, B, ct.byref(self.zero), C,  # noqa: E731
+                                       151, alg, stage, ct.byref(sz), buf)
+            rc = rs.rocsparse_spmm(*args(1, None))
+            if rc != 0:
+                return None, rc
+            buf = self.torch.empty(max(1, sz.value), dtype=self.torch.uint8, device=X.device)
+            rc = rs.rocsparse_spmm(*args(2, P(buf.data_ptr())))
+            if rc != 0:
+                return None, rc
+            return self._timed(lambda: rs.rocsparse_spmm(*args(3, P(buf.data_ptr()))))
+        finally:
+            rs.rocsparse_destroy_dnmat_descr(B)
+            rs.rocsparse_destroy_dnmat_descr(C)
             rs.rocsparse_destroy_spmat_descr(A)
-        else:
-            U, V = c.args[2], c.args[3]
-            o = c.kwargs["out"]
-            A, B, C = P(), P(), P()
-            rs.rocsparse_create_dnmat_descr(ctypes.byref(A), n_rows, U.shape[1], U.stride(0), P(U.data_ptr()), F32, ROW)
-            rs.rocsparse_create_dnmat_descr(ctypes.byref(B), V.shape[0], V.shape[1], V.stride(0), P(V.data_ptr()), F32,
-                                            ROW)
-            rs.rocsparse_create_csr_descr(ctypes.byref(C), n_rows, V.shape[0], nnz, P(rp.data_ptr()), P(ci.data_ptr()),
-                                          P(o.data_ptr()), I32, I32, BASE0, F32)
-            sz = ctypes.c_size_t(0)
-            rc = rs.rocsparse_sddmm_buffer_size(h, OP_N, OP_T, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32, 0,
-                                                ctypes.byref(sz))
-            if rc == 0:
-                buf = torch.empty(max(1, sz.value), dtype=torch.uint8, device=U.device)
-                rc = rs.rocsparse_sddmm_preprocess(h, OP_N, OP_T, ctypes.byref(one), A, B, ctypes.byref(zero), C, F32,
-                                                   0, P(buf.data_ptr()))
-            if rc == 0:
-                ms, rc = timed(lambda: rs.rocsparse_sddmm(h, OP_N, OP_T, ctypes.byref(one), A, B, ctypes.byref(zero), C,
-                                                          F32, 0, P(buf.data_ptr())))
-                res["default"] = round(ms, 4) if ms is not None else f"status {rc}"
-            else:
-                res["default"] = f"status {rc}"
+
+    def sddmm(self, rp, ci, U, V, out):
+        """out[e] = <U[row_e], V[col_e]> (fp32, row-major U and V) with rocSPARSE's default algorithm."""
+        ct, rs, P = self.ct, self.rs, self.ct.c_void_p
+        n_rows, nnz = rp.numel() - 1, ci.numel()
+        A, B, C = P(), P(), P()
+        rs.rocsparse_create_dnmat_descr(ct.byref(A), n_rows, U.shape[1], U.stride(0), P(U.data_ptr()), 151, 0)
+        rs.rocsparse_create_dnmat_descr(ct.byref(B), V.shape[0], V.shape[1], V.stride(0), P(V.data_ptr()), 151, 0)
+        rs.rocsparse_create_csr_descr(ct.byref(C), n_rows, V.shape[0], nnz, P(rp.data_ptr()), P(ci.data_ptr()),
+                                      P(out.data_ptr()), 2, 2, 0, 151)
+        try:
+            sz = ct.c_size_t(0)
+            head = (self.h, 111, 112, ct.byref(self.one), A, B, ct.byref(self.zero), C, 151, 0)
+            rc = rs.rocsparse_sddmm_buffer_size(*head, ct.byref(sz))
+            if rc != 0:
+                return None, rc
+            buf = self.torch.empty(max(1, sz.value), dtype=self.torch.uint8, device=U.device)
+            rc = rs.rocsparse_sddmm_preprocess(*head, P(buf.data_ptr()))
+            if rc != 0:
+                return None, rc
+            return self._timed(lambda: rs.rocsparse_sddmm(*head, P(buf.data_ptr())))
+        finally:
             rs.rocsparse_destroy_dnmat_descr(A)
             rs.rocsparse_destroy_dnmat_descr(B)
             rs.rocsparse_destroy_spmat_descr(C)
-        best = min([t for t in res.values() if isinstance(t, float)], default=None)
+
+
+def vendor_compare(calls, torch, reps=5):
+    """The step's fp32 SpMM and SDDMM calls timed with rocSPARSE (every CSR
+    SpMM algorithm it offers for row-major dense operands; its default
+    SDDMM), each output compared with this library's output of the same call
+    (max |difference| / max |this library's output|).  Returns per call the
+    vendor times, the ratio vendor best / this library, and the differences."""
+    try:
+        rs = Rocsparse(torch, reps)
+    except OSError as e:  # pragma: no cover - library not installed
+        return {"error": str(e)}
+    out = {}
+    for c in calls:
+        if c.op not in ("spmm", "sddmm") or c.esize != 4 or "val_idx" in c.kwargs:
+            continue
+        mine_out = c.kwargs["out"]
+        c.run()
+        ref = mine_out.clone()
+        scale = float(ref.abs().max()) or 1.0
+        vout = torch.empty_like(ref)
+        res, diff = {}, {}
+        if c.op == "spmm":
+            for name, alg in Rocsparse.ALGS.items():
+                vout.fill_(float("nan"))
+                ms, rc = rs.spmm(c.args[0], c.args[1], c.args[2], c.args[3], vout, alg)
+                res[name] = round(ms, 4) if ms is not None else f"status {rc}"
+                if ms is not None:
+                    diff[name] = float((vout - ref).abs().max()) / scale
+        else:
+            vout.zero_()  # rocSPARSE's SDDMM forms beta * C even for beta = 0
+            ms, rc = rs.sddmm(c.args[0], c.args[1], c.args[2], c.args[3], vout)
+            res["default"] = round(ms, 4) if ms is not None else f"status {rc}"
+            if ms is not None:
+                diff["default"] = float((vout - ref).abs().max()) / scale
+        ok = [n for n, t in res.items() if isinstance(t, float) and diff.get(n, 1.0) <= 1e-5]
+        best = min((res[n] for n in ok), default=None)
         mine = float(np.mean(c.times)) if c.times else None
-        out[c.name] = {"rocsparse_ms": res, "rocsparse_best_ms": best,
-                       "vendor_over_this": round(best / mine, 3) if best and mine else None}
-    rs.rocsparse_destroy_handle(h)
+        out[c.name] = {"rocsparse_ms": res, "rocsparse_best_ms": best, "this_ms": round(mine, 4) if mine else None,
+                       "vendor_over_this": round(best / mine, 3) if best and mine else None,
+                       "max_rel_diff_vs_this": {n: float(f"{d:.3g}") if np.isfinite(d) else None
+                                                for n, d in diff.items()}}
+    rs.close()
     return out
 
 

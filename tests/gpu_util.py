@@ -38,7 +38,10 @@ def max_err(gpu, ref, mag):
     nz = ~zero
     if not nz.any():
         return 0.0
-    return float(np.max(np.abs(g[nz] - r[nz]) / m[nz]))
+    e = np.abs(g[nz] - r[nz]) / m[nz]
+    # a NaN anywhere is an infinite error (np.max would return NaN, which
+    # Python's max() and comparisons with a tolerance would then pass over)
+    return float("inf") if np.isnan(e).any() else float(np.max(e))
 
 
 def assert_close(gpu, ref, mag, tol=TOL_F32, what=""):

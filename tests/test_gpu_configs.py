@@ -6,7 +6,9 @@ skew workloads, the single-head fp32 attention on the log-normal graph (scores
 given, and the SDDMM -> softmax -> SpMM chains from queries and keys) and the
 window attention; for the 8-head attention on the 123.7M-entry graph, a
 sample of rows that contains every row the selected partition splits, plus
-properties that hold at any size."""
+properties that hold at any size.  The SpMM and SDDMM calls also run through
+the library's plan (layout and schedule chosen together), the form bench.py
+times."""
 
 import functools
 import os
@@ -113,17 +115,22 @@ def test_c2_spmm_full(F):
     assert bool((h.seg_ptr[1:] > h.seg_ptr[:-1]).all()) and int(h.seg_ptr[-1]) == csr.nnz
     assert int(h.row_seg_ptr[-1]) == h.n_seg
     Yf = csa.hybrid_spmm(h, hv, Xd, schedule=sf).cpu().numpy()
-    worst = [0.0, 0.0]
+    # the library's plan, the call bench.py times
+    pl = csa.plan("spmm", rp, ci, vd, Xd)
+    Yp = csa.plan_spmm(pl, Xd).cpu().numpy()
+    worst = [0.0, 0.0, 0.0]
 
     def block(r0, r1):
         ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, r0, r1, threads=THREADS)
         worst[1] = max(worst[1], max_err(Yf[r0:r1], ref, mag))
+        worst[2] = max(worst[2], max_err(Yp[r0:r1], ref, mag))
         return ref, mag
 
     worst[0] = compare_all_rows(Y, block, csr.row_ptr, F, TOL_F32, f"c2 F={F}")
     assert worst[1] <= TOL_F32, f"c2 format F={F}: max error {worst[1]:.3e}"
-    print(f"c2 F={F}: plain {s} max err {worst[0]:.2e}; format P={h.parts} {sf} max err {worst[1]:.2e} "
-          f"over all {csr.n_rows} rows")
+    assert worst[2] <= TOL_F32, f"c2 plan F={F}: max error {worst[2]:.3e}"
+    print(f"c2 F={F}: plain {s} max err {worst[0]:.2e}; format P={h.parts} {sf} max err {worst[1]:.2e}; "
+          f"{pl} max err {worst[2]:.2e} over all {csr.n_rows} rows")
     # mean aggregation of a constant feature returns the constant on every non-empty row
     ones = torch.ones((csr.n_cols, F), device="cuda")
     Y1 = csa.hybrid_spmm(h, hv, ones, schedule=sf)
@@ -147,9 +154,18 @@ def test_c3_spmm_full(F):
     vd, Xd = dev(vals), dev(X)
     s = selected("spmm", rp, ci, vd, Xd)
     Y = csa.spmm(rp, ci, vd, Xd, schedule=s).cpu().numpy()
-    e = compare_all_rows(Y, lambda r0, r1: oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, r0, r1, threads=THREADS),
-                         csr.row_ptr, F, TOL_F32, f"c3 F={F}")
-    print(f"c3 F={F}: {s} max err {e:.2e} over all {csr.n_rows} rows")
+    pl = csa.plan("spmm", rp, ci, vd, Xd)
+    Yp = csa.plan_spmm(pl, Xd).cpu().numpy()
+    worst = [0.0]
+
+    def block(r0, r1):
+        ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, r0, r1, threads=THREADS)
+        worst[0] = max(worst[0], max_err(Yp[r0:r1], ref, mag))
+        return ref, mag
+
+    e = compare_all_rows(Y, block, csr.row_ptr, F, TOL_F32, f"c3 F={F}")
+    assert worst[0] <= TOL_F32, f"c3 plan F={F}: max error {worst[0]:.3e}"
+    print(f"c3 F={F}: {s} max err {e:.2e}; {pl} max err {worst[0]:.2e} over all {csr.n_rows} rows")
 
 
 @pytest.mark.timeout(900)
@@ -161,9 +177,19 @@ def test_c3_sddmm_full():
     Ud, Vd = dev(U), dev(V)
     s = selected("sddmm", rp, ci, Ud, Vd)
     out = csa.sddmm(rp, ci, Ud, Vd, schedule=s).cpu().numpy()
-    e = compare_all_rows(out, lambda r0, r1: oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, r0, r1, threads=THREADS),
-                         csr.row_ptr, 128, TOL_F32, "c3 sddmm", per_entry=True)
-    print(f"c3 sddmm: {s} max err {e:.2e} over all {csr.nnz} entries")
+    pl = csa.plan("sddmm", rp, ci, Ud, Vd)
+    outp = csa.plan_sddmm(pl, Ud, Vd).cpu().numpy()
+    worst = [0.0]
+    rp64 = csr.row_ptr.astype(np.int64)
+
+    def block(r0, r1):
+        ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, r0, r1, threads=THREADS)
+        worst[0] = max(worst[0], max_err(outp[rp64[r0]:rp64[r1]], ref, mag))
+        return ref, mag
+
+    e = compare_all_rows(out, block, csr.row_ptr, 128, TOL_F32, "c3 sddmm", per_entry=True)
+    assert worst[0] <= TOL_F32, f"c3 plan sddmm: max error {worst[0]:.3e}"
+    print(f"c3 sddmm: {s} max err {e:.2e}; {pl} max err {worst[0]:.2e} over all {csr.nnz} entries")
 
 
 @pytest.mark.timeout(900)
@@ -268,7 +294,10 @@ def test_c3_attention_chain_full(fused):
                                            want_probs=probs is not None)
         if probs is not None:
             got = probs[csr.row_ptr[r0]:csr.row_ptr[r1]].astype(np.float64)
-            worst_p[0] = max(worst_p[0], float(np.max(np.abs(got - pr[:, 0]) / pr[:, 0])))
+            live = pr[:, 0] > 0
+            assert np.all(got[~live] == 0)
+            d = np.abs(got[live] - pr[live, 0]) / pr[live, 0]
+            worst_p[0] = max(worst_p[0], float("inf") if np.isnan(d).any() else float(d.max(initial=0.0)))
         return ref[:, 0], mag[:, 0]
 
     e = compare_all_rows(out, block, csr.row_ptr, 64, TOL_F32, f"c3 chain fused={fused}")
@@ -292,6 +321,9 @@ def test_c4_spmm_full(F):
     Y = csa.spmm(rp, ci, vd, Xd, schedule=s).cpu().numpy()
     ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=THREADS)
     print(f"c4 spmm F={F}: {s} max err {assert_close(Y, ref, mag, TOL_F32, 'c4 spmm'):.2e}")
+    pl = csa.plan("spmm", rp, ci, vd, Xd)
+    Yp = csa.plan_spmm(pl, Xd).cpu().numpy()
+    print(f"c4 plan spmm F={F}: {pl} max err {assert_close(Yp, ref, mag, TOL_F32, 'c4 plan spmm'):.2e}")
 
 
 @pytest.mark.parametrize("K", [4, 8, 16, 32])
@@ -304,6 +336,10 @@ def test_c4_sddmm_full(K):
     out = csa.sddmm(rp, ci, dev(U), dev(V), schedule=s).cpu().numpy()
     ref, mag = oracle.sddmm(csr.row_ptr, csr.col_idx, U, V, threads=THREADS)
     print(f"c4 sddmm K={K}: {s} max err {assert_close(out, ref, mag, TOL_F32, 'c4 sddmm'):.2e}")
+    Ud, Vd = dev(U), dev(V)
+    pl = csa.plan("sddmm", rp, ci, Ud, Vd)
+    outp = csa.plan_sddmm(pl, Ud, Vd).cpu().numpy()
+    print(f"c4 plan sddmm K={K}: {pl} max err {assert_close(outp, ref, mag, TOL_F32, 'c4 plan sddmm'):.2e}")
 
 
 def test_c4_format_bit_exact():

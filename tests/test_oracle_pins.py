@@ -704,3 +704,17 @@ def test_hybrid_product_identity(oracle_lib, seed):
             Y[r] += part_rows[s]
     assert rel_err(Y, ref, mag) < 1e-12
     assert rel_err(Y, dense_of(csr, vals) @ X.astype(np.float64), mag) < 1e-12
+
+
+def test_gpu_error_measure_fails_on_nan():
+    # the parity tests' error measure: a NaN anywhere is an infinite error,
+    # so aggregating blocks with max() cannot pass over it
+    import gpu_util
+
+    ref = np.array([1.0, 2.0, 3.0])
+    mag = np.array([1.0, 2.0, 3.0])
+    assert gpu_util.max_err(np.array([1.0, np.nan, 3.0]), ref, mag) == float("inf")
+    assert max(0.0, gpu_util.max_err(np.array([np.nan, 2.0, 3.0]), ref, mag)) == float("inf")
+    with pytest.raises(AssertionError):
+        gpu_util.max_err(np.array([np.nan]), np.array([0.0]), np.array([0.0]))  # zero magnitude must be exactly 0
+    assert gpu_util.max_err(ref, ref, mag) == 0.0
