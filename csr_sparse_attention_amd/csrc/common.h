@@ -94,6 +94,42 @@ __device__ __forceinline__ void vload_t(float (&d)[VEC], const T* p)
     }
 }
 
+// VEC consecutive bf16 values at p, still packed: VEC / 2 words of two
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int VEC>
+__device__ __forceinline__ void vload_packed(uint32_t (&d)[VEC / 2], const bf16_t* p)
+{
+    if constexpr (VEC == 2) {
+        d[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (VEC == 4) {
+        const uint2 r = *reinterpret_cast<const uint2*>(p);
+        d[0] = r.x;
+        d[1] = r.y;
+    } else {
+        static_assert(VEC == 8, "bf16 operands are read 2, 4 or 8 at a time");
+        const uint4 r = *reinterpret_cast<const uint4*>(p);
+        d[0] = r.x;
+        d[1] = r.y;
+        d[2] = r.z;
+        d[3] = r.w;
+    }
+}
+
+// a0 b0 + a1 b1 + c over two packed bf16 pairs, in fp32 (v_dot2 on gfx950:
+// the bf16 products are exact in fp32 and the sum keeps fp32 accuracy)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// the bf16 pair of two fp32 values that are bf16 values widened (exact)
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi)
+{
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
 // Streamed store (an output row written once and not read again by the
 // kernel): non-temporal, so that it does not push the gathered feature rows
 // out of the caches.

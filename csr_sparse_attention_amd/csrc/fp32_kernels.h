@@ -224,8 +224,20 @@ __device__ __forceinline__ void qk_walk(const float (&q)[NV][VEC], const int32_t
                                         const Lanes<VEC, NV>& L, int F, float scale, float& m, float& l,
                                         float (&acc)[NV][VEC], float* probs, int64_t pstride)
 {
+    // bf16 keys stay packed for the score: the query's pairs are repacked
+    // once (exactly) and each key pair enters a two-term dot instruction
+    constexpr bool PACKED = sizeof(T) == 2;
+    constexpr int VP = PACKED ? VEC / 2 : 1;
+    uint32_t qp[NV][VP];
+    if constexpr (PACKED) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int v = 0; v < VP; ++v) qp[j][v] = pack_bf16_exact(q[j][2 * v], q[j][2 * v + 1]);
+    }
     for (int k = kb; k < ke; k += step * U) {
-        float kv[U][NV][VEC], vv[U][NV][VEC];
+        float kv[U][NV][PACKED ? 1 : VEC], vv[U][NV][VEC];
+        uint32_t kp[U][NV][VP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = k + u * step;
@@ -236,11 +248,21 @@ __device__ __forceinline__ void qk_walk(const float (&q)[NV][VEC], const int32_t
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 if (ok && L.valid(j, F)) {
-                    vload_t<T, VEC>(kv[u][j], kr + L.off(j));
+                    if constexpr (PACKED)
+                        vload_packed<VEC>(kp[u][j], reinterpret_cast<const bf16_t*>(kr + L.off(j)));
+                    else
+                        vload_t<T, VEC>(kv[u][j], kr + L.off(j));
                     vload_t<T, VEC>(vv[u][j], vr + L.off(j));
                 } else {
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) kv[u][j][v] = vv[u][j][v] = 0.f;
+                    for (int v = 0; v < VEC; ++v) vv[u][j][v] = 0.f;
+                    if constexpr (PACKED) {
+#pragma unroll
+                        for (int v = 0; v < VP; ++v) kp[u][j][v] = 0u;
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) kv[u][j][v] = 0.f;
+                    }
                 }
             }
         }
@@ -249,9 +271,15 @@ __device__ __forceinline__ void qk_walk(const float (&q)[NV][VEC], const int32_t
         for (int u = 0; u < U; ++u) {
             float d = 0.f;
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
+            for (int j = 0; j < NV; ++j) {
+                if constexpr (PACKED) {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) d = fmaf(q[j][v], kv[u][j][v], d);
+                    for (int v = 0; v < VP; ++v) d = dot2_bf16(qp[j][v], kp[u][j][v], d);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) d = fmaf(q[j][v], kv[u][j][v], d);
+                }
+            }
             t[u] = d;
         }
         group_sum_lanes(t, L.W);
@@ -367,8 +395,20 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
                                             int step, const T* X, int64_t ldx, const Lanes<VEC, NV>& L,
                                             int F, float* out, const int32_t* out_idx)
 {
+    // bf16 operands stay packed: the row's pairs are repacked once (exactly)
+    // and each gathered pair enters a two-term dot instruction
+    constexpr bool PACKED = sizeof(T) == 2;
+    constexpr int VP = PACKED ? VEC / 2 : 1;
+    uint32_t up[NV][VP];
+    if constexpr (PACKED) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int v = 0; v < VP; ++v) up[j][v] = pack_bf16_exact(u[j][2 * v], u[j][2 * v + 1]);
+    }
     for (int k = kb; k < ke; k += step * U) {
-        float xv[U][NV][VEC];
+        float xv[U][NV][PACKED ? 1 : VEC];
+        uint32_t xp[U][NV][VP];
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             int e = k + uu * step;
@@ -377,11 +417,20 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
             const T* xr = X + (int64_t)c * ldx;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                if (ok && L.valid(j, F)) {
-                    vload_t<T, VEC>(xv[uu][j], xr + L.off(j));
-                } else {
+                if constexpr (PACKED) {
+                    if (ok && L.valid(j, F)) {
+                        vload_packed<VEC>(xp[uu][j], reinterpret_cast<const bf16_t*>(xr + L.off(j)));
+                    } else {
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) xv[uu][j][v] = 0.f;
+                        for (int v = 0; v < VP; ++v) xp[uu][j][v] = 0u;
+                    }
+                } else {
+                    if (ok && L.valid(j, F)) {
+                        vload_t<T, VEC>(xv[uu][j], xr + L.off(j));
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) xv[uu][j][v] = 0.f;
+                    }
                 }
             }
         }
@@ -390,9 +439,15 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
         for (int uu = 0; uu < U; ++uu) {
             float s = 0.f;
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
+            for (int j = 0; j < NV; ++j) {
+                if constexpr (PACKED) {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) s = fmaf(u[j][v], xv[uu][j][v], s);
+                    for (int v = 0; v < VP; ++v) s = dot2_bf16(up[j][v], xp[uu][j][v], s);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) s = fmaf(u[j][v], xv[uu][j][v], s);
+                }
+            }
             d[uu] = s;
         }
         group_sum_lanes(d, L.W);

@@ -79,14 +79,19 @@ __device__ __forceinline__ void mha_fold(const MhaArgs& a, const MhaLanes<LPH>& 
                                          const uint4 (&kr)[U], const uint4 (&vr)[U], float& m, float& l,
                                          float (&acc)[8])
 {
+    // the score's 8 products of this lane: the query repacked (its values
+    // are bf16 widened, so exactly) and the key's bf16 pairs, two at a time
+    // through the two-term dot instruction
+    uint32_t qp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qp[i] = pack_bf16_exact(q[2 * i], q[2 * i + 1]);
     float t[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        float kf[8];
-        bf16x8_to_f32(kf, kr[u]);
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s = fmaf(q[i], kf[i], s);
+        float s = dot2_bf16(qp[0], kr[u].x, 0.f);
+        s = dot2_bf16(qp[1], kr[u].y, s);
+        s = dot2_bf16(qp[2], kr[u].z, s);
+        s = dot2_bf16(qp[3], kr[u].w, s);
         s = head_sum<LPH>(s) * a.scale;
         t[u] = (k + u < ke) ? s : -INFINITY;
     }
