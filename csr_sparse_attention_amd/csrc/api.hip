@@ -832,20 +832,25 @@ int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, co
     return op_call(ctx, p, sched);
 }
 
-// The one-head problem of head h: column views of Q, K, V, out and probs.
+// The one-head problem of head h: column views of Q, K, V, out and probs; for
+// given scores (CSR_OP_ATTENTION), head h's row of the head-major scores.
 static csr_problem_t head_view(const csr_problem_t& p, int32_t h, int64_t head_dim, size_t esize)
 {
     csr_problem_t q = p;
     const int64_t off = (int64_t)h * head_dim;
-    q.a = static_cast<const char*>(p.a) + off * esize;
-    q.b = static_cast<const char*>(p.b) + off * esize;
-    q.c = static_cast<const char*>(p.c) + off * esize;
+    if (p.op == CSR_OP_ATTENTION)
+        q.a = p.a ? static_cast<const float*>(p.a) + (int64_t)h * p.nnz : nullptr;
+    else
+        q.a = static_cast<const char*>(p.a) + off * esize;
+    q.b = p.b ? static_cast<const char*>(p.b) + off * esize : nullptr;
+    q.c = p.c ? static_cast<const char*>(p.c) + off * esize : nullptr;
     q.out = static_cast<float*>(p.out) + off;
     q.probs = p.probs ? p.probs + h : nullptr;
     return q;
 }
 
-// Runs the heads of an attention from queries and keys as one-head problems
+// Runs the heads of an attention (from queries and keys, or from given
+// scores) as one-head problems
 // (ctx locked, device current).  One schedule serves every head: given, or
 // selected on the head whose views allow the narrowest lane accesses (the
 // lowest head index among equals), and checked against every head before
@@ -908,21 +913,35 @@ int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
     p.workspace_bytes = ws_bytes;
     p.stream = stream;
     if (edge_scores || (!Q && !K)) {
-        // scores given (the trace page's operation): one head; edge_scores may
-        // be NULL only when there are no entries
-        if (heads != 1) {
-            if (!ctx) return CSR_ERR_NULL;
-            std::lock_guard<std::mutex> lk(ctx->mu);
-            return set_err(ctx, CSR_ERR_SHAPE, "given edge scores serve one head");
-        }
+        // scores given (the trace page's operation); edge_scores may be NULL
+        // only when there are no entries
         p.op = CSR_OP_ATTENTION;
         p.width = head_dim;
         p.ld_b = ldv;
         p.ld_out = ldo;
         p.a = edge_scores;
         p.b = node_value;
-        p.probs_stride = 1;
-        return op_call(ctx, p, sched);
+        if (heads == 1) {
+            p.probs_stride = 1;
+            return op_call(ctx, p, sched);
+        }
+        // several heads: head-major scores [heads, nnz], each head a one-head
+        // problem on column views of node_value and out
+        if (!ctx) return CSR_ERR_NULL;
+        try {
+            std::lock_guard<std::mutex> lk(ctx->mu);
+            ctx->last_error.clear();
+            if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+            if (heads < 1 || head_dim < 1) return set_err(ctx, CSR_ERR_SHAPE, "heads and head_dim must be >= 1");
+            const int64_t width = (int64_t)heads * head_dim;
+            if (ldv < width || ldo < width) return set_err(ctx, CSR_ERR_SHAPE, "ldv and ldo must be >= heads * head_dim");
+            if (nnz > 0 && (!edge_scores || !node_value)) return set_err(ctx, CSR_ERR_NULL, "edge_scores or node_value is NULL");
+            p.probs_stride = heads;
+            DeviceGuard g(ctx->device);
+            return attention_heads(ctx, p, heads, head_dim, dtype == CSR_DTYPE_BF16 ? 2 : 4, sched);
+        } catch (...) {
+            return set_err(ctx, CSR_ERR_INTERNAL, "internal error");
+        }
     }
     if (!ctx) return CSR_ERR_NULL;
     const int64_t width = (int64_t)heads * head_dim;

@@ -460,9 +460,14 @@ def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, 
     entries of scale * edge_scores, then the weighted sum of node_value rows
     (fp32 or bf16; zero for rows without entries).  Arguments in the order
     row_ptr, col_idx, edge_scores, node_value.  ``probs`` (fp32 [nnz]), when
-    given, receives every entry's probability."""
+    given, receives every entry's probability.  Several heads: edge_scores
+    [H, nnz] (head-major), node_value [n_cols, H, D] -> out [n_rows, H, D],
+    probs [nnz, H]."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
-    _on(row_ptr.device, edge_scores=edge_scores, node_value=node_value, probs=probs)
+    _on(row_ptr.device, edge_scores=edge_scores, node_value=node_value, probs=probs, out=out)
+    if edge_scores.dim() == 2:
+        return _attention_heads(row_ptr, col_idx, edge_scores, node_value, n_rows, nnz, scale, out, probs,
+                                schedule, ctx, workspace)
     _entries(edge_scores, "edge_scores", nnz)
     if node_value.dim() != 2:
         raise ValueError("node_value must be 2-D [n_cols, F]")
@@ -477,6 +482,38 @@ def attention(row_ptr, col_idx, edge_scores, node_value, *, scale: float = 1.0, 
                                     _ptr(probs), _sched_arg(schedule), ws.data_ptr(), nb, st)
 
     _run(p, node_value.device, schedule, ctx, call, workspace)
+    return out
+
+
+def _attention_heads(row_ptr, col_idx, scores, V, n_rows, nnz, scale, out, probs, schedule, ctx, workspace):
+    """attention() over several heads of given scores (csr_attention, heads > 1)."""
+    H = scores.shape[0]
+    if scores.dtype != torch.float32 or scores.shape[1] != nnz or not scores.is_contiguous():
+        raise ValueError(f"edge_scores must be contiguous float32 [heads, {nnz}]")
+    if V.dim() != 3 or V.shape[1] != H or V.stride(2) != 1 or V.stride(1) != V.shape[2]:
+        raise ValueError(f"node_value must be [n_cols, {H}, D] with contiguous heads")
+    D = V.shape[2]
+    V2 = V.view(V.shape[0], H * D) if V.shape[0] > 0 else V.reshape(0, H * D)
+    if out is None:
+        out = torch.empty((n_rows, H, D), dtype=torch.float32, device=V.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (n_rows, H, D) or out.stride(2) != 1 \
+            or out.stride(1) != D:
+        raise ValueError(f"out must be float32 [{n_rows}, {H}, {D}] with contiguous heads")
+    out2 = out.view(n_rows, H * D) if n_rows > 0 else out.reshape(0, H * D)
+    if probs is not None and (probs.dtype != torch.float32 or tuple(probs.shape) != (nnz, H)
+                              or not probs.is_contiguous()):
+        raise ValueError(f"probs must be contiguous float32 [{nnz}, {H}]")
+    # the problem of head 0 (every head shares its shape, strides and schedule)
+    p = _attention_problem(row_ptr, col_idx, scores, V2[:, :D], out2[:, :D], scale, None)
+    ldv, ldo = V2.stride(0) if V2.shape[0] > 1 else H * D, out2.stride(0) if n_rows > 1 else H * D
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_attention(ctx.handle, n_rows, V.shape[0], nnz, row_ptr.data_ptr(), col_idx.data_ptr(),
+                                    scores.data_ptr(), None, None, V.data_ptr(), p.dtype, H, D, ldv,
+                                    ctypes.c_float(scale), out.data_ptr(), ldo, _ptr(probs), _sched_arg(schedule),
+                                    ws.data_ptr(), nb, st)
+
+    _run(p, V.device, schedule, ctx, call, workspace)
     return out
 
 

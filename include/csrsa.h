@@ -304,9 +304,12 @@ int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
  * E_i, head h, the scores t_e, p_e = exp(t_e - max t) / sum over E_i of
  * exp(t - max t), out[i, h, :] = sum over e in E_i of p_e * V[col_idx[e], h, :];
  * out[i, h, :] = 0 when E_i is empty.
- *   edge_scores != NULL, or Q and K both NULL (scores given): heads must be
- *     1, Q and K are not read, t_e = scale * edge_scores[e] (fp32 [nnz];
- *     NULL only when nnz = 0).
+ *   edge_scores != NULL, or Q and K both NULL (scores given): Q and K are
+ *     not read, t_e = scale * edge_scores[h * nnz + e] (fp32 [heads, nnz],
+ *     head-major: each head's scores contiguous, in entry order; NULL only
+ *     when nnz = 0).  Several heads run as one-head problems on column
+ *     views of V and out (schedule op CSR_OP_ATTENTION, shared by the
+ *     heads).
  *   edge_scores == NULL and Q, K given (scores from queries and keys, one
  *     pass): t_e =
  *     scale * sum over d of Q[i, h, d] * K[col_idx[e], h, d]; Q: [n_rows,
@@ -320,8 +323,9 @@ int csr_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
  * bit patterns; Q and K of the same dtype), ldv >= heads * head_dim.  out:
  * fp32 [n_rows, ldo].  probs_out: NULL, or fp32 [nnz * heads], entry-major
  * (p of entry e, head h at probs_out[e * heads + h]).  scale: finite (1.0 =
- * no scaling).  Accumulation is fp32.  CSR_ERR_SHAPE for heads != 1 with
- * given scores; other errors as for csr_spmm. */
+ * no scaling).  Accumulation is fp32.  CSR_ERR_SHAPE for heads or head_dim
+ * below 1 or ldv / ldo below heads * head_dim; other errors as for
+ * csr_spmm. */
 int csr_attention(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
                   const int32_t* row_ptr, const int32_t* col_idx, const float* edge_scores,
                   const void* Q, const void* K, const void* node_value, int32_t dtype,

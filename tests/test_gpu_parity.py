@@ -1099,3 +1099,58 @@ def test_infinite_features_propagate_without_nan(F):
         assert np.isposinf(Y[has7, 0]).all() and np.isfinite(Y[~has7]).all(), sched_id(s)
         fin = np.isfinite(ref)
         assert_close(np.where(fin, Y, 0), np.where(fin, ref, 0), np.where(fin, mag, 1), TOL_F32, sched_id(s))
+
+
+# ---------------------------------------------------------------------------
+# several heads of given scores (head-major [H, nnz]): each head against the
+# oracle's one-head attention, probabilities [nnz, H]
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("H,D,dt", [(2, 16, "f32"), (3, 4, "f32"), (8, 64, "f32"), (4, 32, "bf16")])
+def test_attention_heads_given_scores(graph, H, D, dt):
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(700 + H * D)
+    scores = (2 * rng.standard_normal((H, csr.nnz))).astype(np.float32)
+    Vf = rng.standard_normal((csr.n_cols, H, D)).astype(np.float32)
+    if dt == "bf16":
+        Vb = to_bf16_bits(Vf)
+        Vd, Vref, tol = bf16_dev(Vb), oracle.bf16_to_f32(Vb), TOL_BF16
+    else:
+        Vd, Vref, tol = dev(Vf), Vf, TOL_F32
+    rp, ci = pattern_dev(csr)
+    sd = dev(scores)
+    scale = 0.37
+    refs = [oracle.attention(csr.row_ptr, csr.col_idx, scores[h], np.ascontiguousarray(Vref[:, h, :]), scale,
+                             want_probs=True, threads=oracle.default_threads()) for h in range(H)]
+    probs = torch.empty((csr.nnz, H), device="cuda")
+    out = csa.attention(rp, ci, sd, Vd, scale=scale, probs=probs)
+    assert tuple(out.shape) == (csr.n_rows, H, D)
+    got, gp = out.cpu().numpy(), probs.cpu().numpy()
+    for h, (ref, mag, pref) in enumerate(refs):
+        e = assert_close(got[:, h, :], ref, mag, tol, f"head {h}")
+        assert e <= TOL_F32, (h, e)
+        live = pref > 0
+        assert np.all(gp[~live, h] == 0)
+        assert float(np.max(np.abs(gp[live, h] - pref[live]) / pref[live], initial=0.0)) <= 1e-5, h
+    # the schedule the heads share, given explicitly: the same results bit for bit
+    p, _ = csa.make_problem("attention", rp, ci, sd[0], Vd.view(csr.n_cols, H * D)[:, :D], scale=scale)
+    for s in schedules(p, thorough=False):
+        o2 = csa.attention(rp, ci, sd, Vd, scale=scale, schedule=s).cpu().numpy()
+        for h, (ref, mag, _) in enumerate(refs):
+            assert_close(o2[:, h, :], ref, mag, tol, f"head {h} {sched_id(s)}")
+
+
+def test_attention_heads_given_scores_errors():
+    csr = dup_graph(3)
+    rp, ci = pattern_dev(csr)
+    sd = dev(np.zeros((2, csr.nnz), np.float32))
+    V = dev(np.zeros((csr.n_cols, 2, 8), np.float32))
+    with pytest.raises(ValueError):
+        csa.attention(rp, ci, sd[:, 1:], V)  # scores of the wrong length
+    with pytest.raises(ValueError):
+        csa.attention(rp, ci, sd, dev(np.zeros((csr.n_cols, 3, 8), np.float32)))  # head counts differ
+    with pytest.raises(ValueError):
+        csa.attention(rp, ci, sd, V, out=torch.empty((csr.n_rows, 2, 4), device="cuda"))
+    with pytest.raises(ValueError):
+        csa.attention(rp, ci, sd, V, probs=torch.empty((2, csr.nnz), device="cuda"))  # probs are [nnz, H]
