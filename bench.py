@@ -59,6 +59,9 @@ def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64, esize=4):
         return 4 * (n_rows + 1) + nnz * 12
     if op == "gather":
         return nnz * 12
+    if op == "spmm_sddmm":
+        # the SpMM's bytes, the U row per row and the per-entry output
+        return 4 * (n_rows + 1) + nnz * 8 + nnz * width * esize + 2 * n_rows * width * 4 + nnz * 4
     if op == "mha":
         hd = heads * head_dim
         return 4 * (n_rows + 1) + nnz * 4 + n_rows * hd * 2 + 2 * nnz * hd * 2 + n_rows * hd * 4
@@ -125,7 +128,7 @@ class Call:
 
     def select(self, csa, mode="auto"):
         sel_args = (self.args[0], None) + tuple(self.args[1:]) if self.op.startswith("row_softmax") else self.args
-        kw = {k: self.kwargs[k] for k in ("scale", "val_idx") if k in self.kwargs}
+        kw = {k: self.kwargs[k] for k in ("scale", "val_idx", "z_idx") if k in self.kwargs}
         return csa.select(self.op, *sel_args, mode=mode, **kw)
 
     def label(self):
@@ -271,26 +274,32 @@ def build_workload(name, torch, csa):
         else:
             calls.append(Call("attention_F64", "attention", csa.attention, (rp, ci, S, Vd),
                               {"out": Y, "scale": 0.125}, csr.n_rows, csr.nnz, 64, None))
-    elif name in ("c3bwd", "c3bwd_gather"):
+    elif name in ("c3bwd", "c3bwd_perm", "c3bwd_gather"):
         # backward of the single-head fp32 attention on the c3 graph (scores
-        # given, F = 64): P = row softmax, dP = SDDMM(dOut, V), d scores =
-        # softmax backward (in place), P^T order by gather, dV = SpMM on A^T.
-        # The transposed pattern is built once, outside the step.
+        # given, F = 64): P = row softmax; dV = P^T dOut and dP = dOut V^T;
+        # d scores = softmax backward.  c3bwd: dV and dP in one pass over A^T
+        # (csr_spmm_sddmm, P read through the transposed pattern's perm, dP
+        # written in A^T's order and gathered back through perm's inverse);
+        # c3bwd_perm: SDDMM dP on A, then the
+        # SpMM on A^T reading P through the perm; c3bwd_gather: P gathered
+        # into A^T's order first.  The transposed pattern is built once,
+        # outside the step.
         csr = configs.config_pattern("c3")
         rp, ci = d(csr.row_ptr), d(csr.col_idx)
         S = d(configs.config_dense("c3", "scores", csr) * 3.0)
         Vd = d(configs.config_dense("c3", "X", csr, 64))
         dO = d(configs.config_dense("c3", "V", csr, 64))
+        inverse = name == "c3bwd"  # the fused backward also reads perm's inverse
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        At = csa.transpose(rp, ci, csr.n_cols)
+        tt = time.perf_counter()
+        At = csa.transpose(rp, ci, csr.n_cols, inverse=inverse)
         torch.cuda.synchronize()
-        build_workload.transpose_first_ms = (time.perf_counter() - t0) * 1e3
+        build_workload.transpose_first_ms = (time.perf_counter() - tt) * 1e3
         # again with the buffers already in torch's pool: the build's own time
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         del At
         ev0.record()
-        At = csa.transpose(rp, ci, csr.n_cols)
+        At = csa.transpose(rp, ci, csr.n_cols, inverse=inverse)
         ev1.record()
         ev1.synchronize()
         build_workload.transpose_ms = ev0.elapsed_time(ev1)
@@ -300,6 +309,17 @@ def build_workload(name, torch, csa):
         dV = torch.empty((csr.n_cols, 64), dtype=torch.float32, device="cuda")
         calls.append(Call("row_softmax", "row_softmax", csa.row_softmax, (rp, S), {"out": P, "scale": 0.125},
                           csr.n_rows, csr.nnz, 1, None))
+        if name == "c3bwd":
+            # dP comes out in A^T's order (Pt's buffer) and is gathered back
+            # through perm's inverse; the softmax backward runs in place on it
+            calls.append(Call("spmm_sddmm_dV_dP", "spmm_sddmm", csa.spmm_sddmm, (At.row_ptr, At.col_idx, P, dO, Vd),
+                              {"out": dV, "z": Pt, "val_idx": At.perm}, csr.n_cols, csr.nnz, 64, None))
+            calls[-1].bytes += 4 * csr.nnz  # the value index
+            calls.append(Call("gather_dP", "gather", lambda perm, src, out, schedule=None: csa.gather_values(
+                perm, src, out=out), (At.inv, Pt, dP), {}, csr.n_rows, csr.nnz, 1, None))
+            calls.append(Call("softmax_bwd", "row_softmax_backward", csa.row_softmax_backward, (rp, P, dP),
+                              {"out": dP, "scale": 0.125}, csr.n_rows, csr.nnz, 1, None))
+            return calls, time.time() - t0
         calls.append(Call("sddmm_dP", "sddmm", csa.sddmm, (rp, ci, dO, Vd), {"out": dP}, csr.n_rows, csr.nnz, 64,
                           None))
         calls.append(Call("softmax_bwd", "row_softmax_backward", csa.row_softmax_backward, (rp, P, dP),
@@ -352,8 +372,13 @@ def check_shapes(calls):
             assert out is None or out.numel() == c.nnz, (c.name, "out")
         else:
             assert a[1].numel() == c.nnz, (c.name, "col_idx")
-            if c.op in ("spmm", "attention") and a[2] is not None:
+            if c.op in ("spmm", "attention", "spmm_sddmm") and a[2] is not None:
                 assert a[2].numel() == c.nnz, (c.name, "per-entry values")
+            for k in ("val_idx", "z_idx", "z"):
+                if k in c.kwargs:
+                    assert c.kwargs[k].numel() == c.nnz, (c.name, k)
+            if c.op == "spmm_sddmm":
+                assert a[4].shape[0] == c.n_rows and a[4].shape[1] == a[3].shape[1], (c.name, "U")
 
 
 def stream_bandwidth(torch, gib=4):
@@ -441,7 +466,8 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
             continue
         scale = c.kwargs.get("scale", 1.0)
         args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
-        p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale, val_idx=c.kwargs.get("val_idx"))
+        p, _ = csa.make_problem(c.op, *args, out=c.kwargs.get("out"), scale=scale, val_idx=c.kwargs.get("val_idx"),
+                                z_idx=c.kwargs.get("z_idx"))
         counts, sums, mx = csa.degree_histogram(c.args[0])
         hist = counts + sums + [mx]
         cands = [({"format_parts": 1, **s.as_dict()}, lambda s=s: c.fn(*c.args, schedule=s, **c.kwargs))
@@ -755,7 +781,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2",
                     help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3qk, c3bf16, c3bwd, "
-                         "c3bwd_gather, c3sweep")
+                         "c3bwd_perm, c3bwd_gather, c3sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds per pass of the CPU oracle sample")
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -913,8 +939,12 @@ def main():
                                 "c3sweep": "CSR SpMM on the log-normal graph at F in {128,256,384,512}: "
                                            "gathered operand of 1.25 to 5.0 GB",
                                 "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "
-                                         "row softmax, SDDMM dP, softmax backward, SpMM dV on A^T reading P "
-                                         "through the transposed pattern's perm",
+                                         "row softmax, dV = P^T dOut and dP = dOut V^T in one pass over A^T "
+                                         "(P read through the transposed pattern's perm, dP in A^T's order), "
+                                         "dP gathered back through the perm's inverse, softmax backward",
+                                "c3bwd_perm": "backward of single-head fp32 attention on the log-normal graph, "
+                                              "F=64: row softmax, SDDMM dP, softmax backward, SpMM dV on A^T "
+                                              "reading P through the transposed pattern's perm",
                                 "c3bwd_gather": "backward of single-head fp32 attention on the log-normal graph, "
                                                 "F=64: row softmax, SDDMM dP, softmax backward, gather P^T, "
                                                 "SpMM dV on A^T"

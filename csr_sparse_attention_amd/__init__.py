@@ -45,6 +45,7 @@ from .ops import (  # noqa: E402,F401
     default_schedule,
     degree_histogram,
     gather_values,
+    inverse_permutation,
     hybrid_format,
     hybrid_parts,
     hybrid_plan,
@@ -67,6 +68,7 @@ from .ops import (  # noqa: E402,F401
     select,
     signature,
     spmm,
+    spmm_sddmm,
     spmm_backward,
     spmm_transposed,
     spmm_noalloc,

@@ -19,7 +19,8 @@ STATUS = {
 }
 CSR_ERR_NO_CACHE_ENTRY = -8
 
-OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX, OP_SOFTMAX_BWD, OP_ATTENTION_QK = 1, 2, 3, 4, 5, 6, 7
+OP_SPMM, OP_SDDMM, OP_ATTENTION, OP_MHA, OP_ROW_SOFTMAX, OP_SOFTMAX_BWD, OP_ATTENTION_QK, OP_SPMM_SDDMM = \
+    1, 2, 3, 4, 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAP_ROWGROUP, MAP_MERGEPATH, MAP_SEGSCAN = 1, 2, 3
 SCHED_WIDE = 1  # schedule flag: 16-byte lanes over 4-byte aligned rows (SpMM, row-group)
@@ -31,8 +32,9 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # CSR_NOALLOC_SCRATCH_BYTES
 # Every symbol the header declares.
 EXPORTS = (
     "csr_context_create", "csr_context_destroy", "csr_status_string", "csr_last_error",
-    "csr_spmm", "csr_spmm_perm", "csr_spmm_noalloc", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
-    "csr_row_softmax_backward", "csr_transpose_workspace_size", "csr_transpose", "csr_gather_values",
+    "csr_spmm", "csr_spmm_perm", "csr_spmm_sddmm", "csr_spmm_noalloc", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
+    "csr_row_softmax_backward", "csr_transpose_workspace_size", "csr_transpose",
+    "csr_gather_values", "csr_inverse_permutation",
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
@@ -101,6 +103,8 @@ class CsrProblem(ctypes.Structure):
         ("probs", ctypes.c_void_p),
         ("probs_stride", ctypes.c_int64),
         ("a_idx", ctypes.c_void_p),
+        ("out2", ctypes.c_void_p),
+        ("out2_idx", ctypes.c_void_p),
     ]
 
 
@@ -215,6 +219,7 @@ def load() -> ctypes.CDLL:
         "csr_spmm": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
         "csr_spmm_noalloc": [P, I64, I64, I64, P, P, P, P, I32, I64, I64, P, I64, SP, P],
         "csr_spmm_perm": [P, I64, I64, I64, P, P, P, P, P, I32, I64, I64, P, I64, SP, P, SZ, P],
+        "csr_spmm_sddmm": [P, I64, I64, I64, P, P, P, P, P, I64, I64, P, I64, P, I64, P, P, SP, P, SZ, P],
         "csr_sddmm": [P, I64, I64, I64, P, P, P, I64, P, I64, I32, I64, P, SP, P, SZ, P],
         "csr_attention": [P, I64, I64, I64, P, P, P, P, P, P, I32, I32, I64, I64, F, P, I64, P, SP, P, SZ, P],
         "csr_mha_attention": [P, I64, I64, I64, P, P, P, P, P, I32, I32, F, P, P, SP, P, SZ, P],
@@ -223,6 +228,7 @@ def load() -> ctypes.CDLL:
         "csr_transpose_workspace_size": [P, I64, I64, I64, ctypes.POINTER(SZ)],
         "csr_transpose": [P, I64, I64, I64, P, P, P, P, P, P, SZ, P],
         "csr_gather_values": [P, I64, P, P, P, P],
+        "csr_inverse_permutation": [P, I64, P, P, P],
         "csr_select": [P, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
         "csr_default_schedule": [P, PP, SP],
         "csr_candidates": [P, PP, ctypes.POINTER(I64), SP, I32, ctypes.POINTER(I32)],

@@ -220,13 +220,18 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
     char* ws = static_cast<char*>(p.workspace);
     if (ctx->flags & CSR_CTX_VALIDATE) {
         int64_t* bad = reinterpret_cast<int64_t*>(ws);
-        CSR_HIP(ctx, csrk::launch_validate(p.row_ptr, p.col_idx, p.n_rows, p.n_cols, p.nnz, bad, st));
-        if (p.op == CSR_OP_SPMM && p.a_idx) CSR_HIP(ctx, csrk::launch_validate_index(p.a_idx, p.nnz, p.nnz, bad, st));
+        // the row softmax and its backward have no columns (col_idx is not read)
+        const bool rows_only = p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD;
+        CSR_HIP(ctx, csrk::launch_validate(p.row_ptr, rows_only ? nullptr : p.col_idx, p.n_rows, p.n_cols, p.nnz, bad,
+                                           st));
+        if (p.a_idx) CSR_HIP(ctx, csrk::launch_validate_index(p.a_idx, p.nnz, p.nnz, bad, st));
+        if (p.out2_idx) CSR_HIP(ctx, csrk::launch_validate_index(p.out2_idx, p.nnz, p.nnz, bad, st));
         CSR_HIP(ctx, hipMemcpyAsync(ctx->pinned, bad, sizeof(int64_t), hipMemcpyDeviceToHost, st));
         CSR_HIP(ctx, hipStreamSynchronize(st));
         if (ctx->pinned[0] != 0)
-            return set_err(ctx, CSR_ERR_INVALID_CSR, p.a_idx ? "row_ptr / col_idx / val_idx fail CSR validation"
-                                                             : "row_ptr / col_idx fail CSR validation");
+            return set_err(ctx, CSR_ERR_INVALID_CSR, (p.a_idx || p.out2_idx)
+                                                         ? "row_ptr / col_idx / the entry indexes fail CSR validation"
+                                                         : "row_ptr / col_idx fail CSR validation");
     }
     if (p.n_rows == 0) return CSR_OK;
     if (p.op == CSR_OP_SDDMM && p.nnz == 0) return CSR_OK;
@@ -311,6 +316,22 @@ int run_schedule(csr_context_t ctx, const csr_problem_t& p, const csr_schedule_t
         a.ldy = p.ld_out;
         a.probs = p.probs;
         a.probs_stride = p.probs_stride > 0 ? p.probs_stride : 1;
+    }
+    if (p.op == CSR_OP_SPMM_SDDMM) {
+        a.ev = static_cast<const float*>(p.a);
+        a.ev_idx = p.a_idx;
+        a.X = p.b;
+        a.ldx = p.ld_b;
+        a.U = p.c;
+        a.ldu = p.ld_c;
+        a.Y = static_cast<float*>(p.out);
+        a.ldy = p.ld_out;
+        a.Z = p.out2;
+        a.out_idx = p.out2_idx;
+        CSR_HIP(ctx, csrk::launch_dual(s.mapping, s.vec, s.passes, s.chunk_items, a, st));
+        // split rows: the SpMM's fix-up (the same carry layout)
+        if (s.mapping != CSR_MAP_ROWGROUP) CSR_HIP(ctx, csrk::launch_spmm_fixup(s.vec, s.passes, a, st));
+        return CSR_OK;
     }
     if (p.op == CSR_OP_SDDMM) {
         if (maps) {
@@ -761,6 +782,41 @@ int csr_spmm_perm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
     return op_call(ctx, p, sched);
 }
 
+int csr_spmm_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
+                   const int32_t* col_idx, const float* vals, const int32_t* val_idx, const float* X, int64_t F,
+                   int64_t ldx, const float* U, int64_t ldu, float* Y, int64_t ldy, float* z, const int32_t* z_idx,
+                   const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    if (nnz > 0 && val_idx && !vals) {
+        std::lock_guard<std::mutex> lk(ctx->mu);
+        return set_err(ctx, CSR_ERR_NULL, "val_idx needs vals");
+    }
+    csr_problem_t p = blank_problem();
+    p.op = CSR_OP_SPMM_SDDMM;
+    p.dtype = CSR_DTYPE_F32;
+    p.n_rows = n_rows;
+    p.n_cols = n_cols;
+    p.nnz = nnz;
+    p.width = F;
+    p.ld_b = ldx;
+    p.ld_c = ldu;
+    p.ld_out = ldy;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.a = vals;
+    p.a_idx = val_idx;
+    p.b = X;
+    p.c = U;
+    p.out = Y;
+    p.out2 = z;
+    p.out2_idx = z_idx;
+    p.workspace = workspace;
+    p.workspace_bytes = ws_bytes;
+    p.stream = stream;
+    return op_call(ctx, p, sched);
+}
+
 int csr_spmm_noalloc(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t* row_ptr,
                      const int32_t* col_idx, const float* vals, const void* X, int32_t x_dtype, int64_t F,
                      int64_t ldx, float* Y, int64_t ldy, const csr_schedule_t* sched, void* stream)
@@ -1117,6 +1173,19 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
     if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
     DeviceGuard g(ctx->device);
     CSR_HIP(ctx, csrk::launch_gather_values(perm, src, dst, n, static_cast<hipStream_t>(stream)));
+    return CSR_OK;
+}
+
+int csr_inverse_permutation(csr_context_t ctx, int64_t n, const int32_t* perm, int32_t* inv, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (n < 0 || n >= ((int64_t)1 << 31)) return set_err(ctx, CSR_ERR_SHAPE, "bad size");
+    if (n > 0 && (!perm || !inv)) return CSR_ERR_NULL;
+    if (n > 0 && (const void*)perm == (const void*)inv) return set_err(ctx, CSR_ERR_SHAPE, "perm and inv must not alias");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    CSR_HIP(ctx, csrk::launch_invert(perm, inv, n, static_cast<hipStream_t>(stream)));
     return CSR_OK;
 }
 
@@ -2377,7 +2446,7 @@ int csr_cache_store(csr_context_t ctx, uint64_t signature, const csr_schedule_t*
 {
     if (!ctx || !sched) return CSR_ERR_NULL;
     std::lock_guard<std::mutex> lk(ctx->mu);
-    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_ATTENTION_QK)
+    if (sched->version != CSR_SCHEDULE_VERSION || sched->op < CSR_OP_SPMM || sched->op > CSR_OP_SPMM_SDDMM)
         return set_err(ctx, CSR_ERR_SCHEDULE, "not a schedule of this library version");
     return store_entry(ctx, signature, *sched, 0.0);
 }

@@ -40,6 +40,10 @@ struct Fp32Args {
     int64_t probs_stride;
     // SpMM: entry e's value is ev[ev_idx[e]] (null: ev[e])
     const int32_t* ev_idx;
+    // SpMM + SDDMM on one pattern (Op::Dual): U the row operand (ldu), Y the
+    // SpMM's rows, Z the SDDMM's per-entry output, written at Z[out_idx[e]]
+    // (null: Z[e])
+    float* Z;
 };
 
 // SpMM over the packed short rows of the degree classes (class c = 0 .. 5

@@ -32,8 +32,10 @@ namespace csrk {
 
 // AttnQK: attention from queries and keys, SDDMM -> row-softmax -> SpMM in one
 // pass (U = Q, X = K, V = values): each score is formed on the fly and folded
-// into an online softmax.
-enum class Op { Spmm, Attention, Sddmm, AttnQK };
+// into an online softmax.  Dual: an SpMM and an SDDMM on one pattern that
+// share the gathered operand X (Y = A X and z_e = <U[row_e], X[col_e]>), each
+// gathered row read once for both.
+enum class Op { Spmm, Attention, Sddmm, AttnQK, Dual };
 
 
 template <int VEC, int NV>
@@ -461,6 +463,78 @@ __device__ __forceinline__ void sddmm_edges(const float (&u)[NV][VEC], const int
     }
 }
 
+// The SpMM and the SDDMM of Op::Dual over entries e = kb, kb + step, ... < ke
+// of one row: acc += w_e * X[col_e] (w_e = ev[ev_idx[e]], ev[e], or 1 without
+// values) and z_e = <u, X[col_e]>, both from one load of each gathered row.
+// The W lanes of the group reduce the partial dot products and lane 0 of the
+// group writes z_e at Z[z_idx[e]] (or Z[e]).  Lanes past the width read the
+// row's first features (in bounds) and zero them: their u is zero and an
+// infinite feature must not turn the dot product into NaN.
+template <typename T, int VEC, int NV, int U>
+__device__ __forceinline__ void dual_walk(float (&acc)[NV][VEC], const float (&u)[NV][VEC], const int32_t* col,
+                                          const float* ev, const int32_t* ev_idx, int kb, int ke, int step,
+                                          const T* X, int64_t ldx, const Lanes<VEC, NV>& L, int F, float* Z,
+                                          const int32_t* z_idx)
+{
+    constexpr uint32_t ES = sizeof(T);
+    uint32_t off[NV];
+    bool on[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        on[j] = L.valid(j, F);
+        off[j] = on[j] ? (uint32_t)L.off(j) * ES : 0u;
+    }
+    const uint32_t row_bytes = (uint32_t)ldx * ES;
+    const char* xb = reinterpret_cast<const char*>(X);
+    for (int k = kb; k < ke; k += step * U) {
+        float xv[U][NV][VEC];
+        float w[U];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            const int e = k + uu * step;
+            const bool ok = e < ke;
+            w[uu] = ok ? (ev ? ev[ev_idx ? ev_idx[e] : e] : 1.f) : 0.f;
+            if (ok) {
+                const char* xr = row_at(xb, col[e], row_bytes);
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    vload_t<T, VEC>(xv[uu][j], reinterpret_cast<const T*>(xr + off[j]));
+                    if (!on[j]) {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) xv[uu][j][v] = 0.f;
+                    }
+                }
+            } else {
+                zero(xv[uu]);
+            }
+        }
+        float d[U];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            float sdot = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) sdot = fmaf(u[j][v], xv[uu][j][v], sdot);
+            d[uu] = sdot;
+        }
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[j][v] = fmaf(w[uu], xv[uu][j][v], acc[j][v]);
+        group_sum_lanes(d, L.W);
+        if (L.lg == 0) {
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                const int e = k + uu * step;
+                if (e < ke) Z[z_idx ? z_idx[e] : e] = d[uu];
+            }
+        }
+    }
+}
+
 // U row read for pattern row r: its own row, or the row a segment belongs to
 __device__ __forceinline__ int64_t u_row_of(const Fp32Args& a, int64_t r) { return a.u_row ? a.u_row[r] : r; }
 
@@ -494,6 +568,12 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup(Fp32Args a)
         float u[NV][VEC];
         load_row<T, VEC, NV>(u, static_cast<const T*>(a.U) + u_row_of(a, row) * a.ldu, L, a.F);
         sddmm_edges<T, VEC, NV, U>(u, a.col_idx, b, e, 1, X, a.ldx, L, a.F, a.Y, a.out_idx);
+    } else if constexpr (OP == Op::Dual) {
+        float u[NV][VEC], acc[NV][VEC];
+        load_row<T, VEC, NV>(u, static_cast<const T*>(a.U) + row * a.ldu, L, a.F);
+        zero(acc);
+        dual_walk<T, VEC, NV, U>(acc, u, a.col_idx, a.ev, a.ev_idx, b, e, 1, X, a.ldx, L, a.F, a.Z, a.out_idx);
+        store_row<VEC, NV>(a.Y + row * a.ldy, acc, L, a.F, 1.f);
     } else if constexpr (OP == Op::AttnQK) {
         constexpr int UQ = U > 1 ? U / 2 : 1;  // K and V rows in flight: half the entries
         float q[NV][VEC], acc[NV][VEC];
@@ -745,6 +825,36 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_mergepath(Fp32Args a)
                 qk_walk<T, VEC, NV, UQ>(q, col, sb, se, 1, X, a.ldx, Vv, a.ldv, L, a.F, a.scale, m, l, acc, a.probs,
                                         a.probs_stride);
                 emit(i, acc, m, l, false);
+            }
+        }
+    } else if constexpr (OP == Op::Dual) {
+        // pass 1: long segments, whole wave (the groups take interleaved
+        // entries, then their sums are reduced); the values are in LDS
+        for (int i = 0; i < nrow; ++i) {
+            const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+            if (se - sb < long_row) continue;
+            float u[NV][VEC], acc[NV][VEC];
+            load_row<T, VEC, NV>(u, Urow + ((int64_t)x0 + i) * a.ldu, L, a.F);
+            zero(acc);
+            dual_walk<T, VEC, NV, U>(acc, u, col, ev, nullptr, sb + L.g, se, G, X, a.ldx, L, a.F, a.Z, a.out_idx);
+            if (G > 1) {
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[j][v] = xor_sum_from(acc[j][v], a.W);
+            }
+            emit(i, acc, 0.f, 1.f, true);
+        }
+        // pass 2: short segments, one group each
+        if (G > 1) {
+            for (int i = L.g; i < nrow; i += G) {
+                const int sb = max(rp[i], y0), se = min(rp[i + 1], y1);
+                if (se - sb >= long_row) continue;
+                float u[NV][VEC], acc[NV][VEC];
+                load_row<T, VEC, NV>(u, Urow + ((int64_t)x0 + i) * a.ldu, L, a.F);
+                zero(acc);
+                dual_walk<T, VEC, NV, U>(acc, u, col, ev, nullptr, sb, se, 1, X, a.ldx, L, a.F, a.Z, a.out_idx);
+                emit(i, acc, 0.f, 1.f, false);
             }
         }
     } else if constexpr (OP == Op::Sddmm) {

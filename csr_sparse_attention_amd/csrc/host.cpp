@@ -46,7 +46,8 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // ops of the lane-group kernels (fp32 accumulation; fp32 or bf16 operands)
 bool is_fp32_op(int op)
 {
-    return op == CSR_OP_SPMM || op == CSR_OP_SDDMM || op == CSR_OP_ATTENTION || op == CSR_OP_ATTENTION_QK;
+    return op == CSR_OP_SPMM || op == CSR_OP_SDDMM || op == CSR_OP_ATTENTION || op == CSR_OP_ATTENTION_QK ||
+           op == CSR_OP_SPMM_SDDMM;
 }
 
 bool is_softmax_op(int op) { return op == CSR_OP_ATTENTION || op == CSR_OP_ATTENTION_QK || op == CSR_OP_MHA; }
@@ -74,6 +75,9 @@ int max_vec_f32(const csr_problem_t& p)
         } else if (p.op == CSR_OP_ATTENTION_QK) {
             ok = (p.ld_a % v == 0) && (p.ld_b % v == 0) && (p.ld_c % v == 0) && (p.ld_out % v == 0) &&
                  aligned(p.a, bytes) && aligned(p.b, bytes) && aligned(p.c, bytes) && aligned(p.out, bytes);
+        } else if (p.op == CSR_OP_SPMM_SDDMM) {
+            ok = (p.ld_b % v == 0) && (p.ld_c % v == 0) && (p.ld_out % v == 0) && aligned(p.b, bytes) &&
+                 aligned(p.c, bytes) && aligned(p.out, bytes);
         }
         if (ok) return v;
     }
@@ -132,14 +136,20 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (why) *why = msg;
         return code;
     };
-    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_ATTENTION_QK) return fail(CSR_ERR_SHAPE, "unknown op");
+    if (p.op < CSR_OP_SPMM || p.op > CSR_OP_SPMM_SDDMM) return fail(CSR_ERR_SHAPE, "unknown op");
     if (p.a_idx) {
-        if (p.op != CSR_OP_SPMM) return fail(CSR_ERR_SHAPE, "a value index serves SpMM");
+        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SPMM_SDDMM) return fail(CSR_ERR_SHAPE, "a value index serves SpMM");
         if (!aligned(p.a_idx, 4)) return fail(CSR_ERR_ALIGN, "the value index must be 4-byte aligned");
         if (need_ptrs && p.nnz > 0 && !p.a) return fail(CSR_ERR_NULL, "a value index needs the values");
     }
+    if (p.out2 || p.out2_idx) {
+        if (p.op != CSR_OP_SPMM_SDDMM) return fail(CSR_ERR_SHAPE, "a second output serves the SpMM + SDDMM op");
+        if (!aligned(p.out2, 4) || !aligned(p.out2_idx, 4))
+            return fail(CSR_ERR_ALIGN, "the per-entry output and its index must be 4-byte aligned");
+    }
     if (is_fp32_op(p.op) && p.dtype != CSR_DTYPE_F32 && p.dtype != CSR_DTYPE_BF16)
         return fail(CSR_ERR_DTYPE, "this op takes fp32 or bf16 operands");
+    if (p.op == CSR_OP_SPMM_SDDMM && p.dtype != CSR_DTYPE_F32) return fail(CSR_ERR_DTYPE, "SpMM + SDDMM takes fp32 operands");
     if (p.op == CSR_OP_MHA && p.dtype != CSR_DTYPE_BF16) return fail(CSR_ERR_DTYPE, "multi-head attention takes bf16 Q/K/V");
     if (p.op == CSR_OP_ROW_SOFTMAX || p.op == CSR_OP_SOFTMAX_BWD) {
         const int64_t lim = (int64_t)1 << 31;
@@ -183,6 +193,10 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
         if (p.op == CSR_OP_SDDMM) {
             if (p.ld_a < p.width || p.ld_b < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < K");
             if (p.ld_a >= ld_lim || p.ld_b >= ld_lim) return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
+        } else if (p.op == CSR_OP_SPMM_SDDMM) {
+            if (p.ld_b < p.width || p.ld_c < p.width || p.ld_out < p.width) return fail(CSR_ERR_SHAPE, "leading dimension < F");
+            if (p.ld_b >= ld_lim || p.ld_c >= ld_lim || p.ld_out >= ld_lim)
+                return fail(CSR_ERR_SHAPE, "leading dimension >= 2^30");
         } else if (p.op == CSR_OP_ATTENTION_QK) {
             if (p.ld_a < p.width || p.ld_b < p.width || p.ld_c < p.width || p.ld_out < p.width)
                 return fail(CSR_ERR_SHAPE, "leading dimension < head_dim");
@@ -212,9 +226,12 @@ int check_problem(const csr_problem_t& p, bool need_ptrs, std::string* why)
     if (need_ptrs) {
         if (!p.row_ptr) return fail(CSR_ERR_NULL, "row_ptr is NULL");
         if (p.nnz > 0 && !p.col_idx) return fail(CSR_ERR_NULL, "col_idx is NULL");
-        if (p.op != CSR_OP_SPMM && p.nnz > 0 && !p.a) return fail(CSR_ERR_NULL, "operand a is NULL");
+        if (p.op != CSR_OP_SPMM && p.op != CSR_OP_SPMM_SDDMM && p.nnz > 0 && !p.a)
+            return fail(CSR_ERR_NULL, "operand a is NULL");
         if (p.nnz > 0 && !p.b) return fail(CSR_ERR_NULL, "operand b is NULL");
         if ((p.op == CSR_OP_MHA || p.op == CSR_OP_ATTENTION_QK) && p.nnz > 0 && !p.c) return fail(CSR_ERR_NULL, "V is NULL");
+        if (p.op == CSR_OP_SPMM_SDDMM && p.nnz > 0 && (!p.c || !p.out2))
+            return fail(CSR_ERR_NULL, "U or the per-entry output is NULL");
         if (p.op == CSR_OP_SDDMM ? (p.nnz > 0 && !p.out) : (p.n_rows > 0 && !p.out))
             return fail(CSR_ERR_NULL, "output is NULL");
     }
@@ -309,7 +326,7 @@ WsLayout ws_layout(const csr_problem_t& p, const csr_schedule_t& s)
     if (p.op == CSR_OP_ATTENTION || p.op == CSR_OP_ATTENTION_QK) {
         ml = (size_t)nc * 2 * 2 * 4;
         val = (size_t)nc * 2 * p.width * 4;
-    } else if (p.op == CSR_OP_SPMM) {
+    } else if (p.op == CSR_OP_SPMM || p.op == CSR_OP_SPMM_SDDMM) {
         val = (size_t)nc * 2 * p.width * 4;
     } else if (p.op == CSR_OP_MHA) {
         ml = (size_t)nc * 2 * p.heads * 2 * 4;
@@ -479,8 +496,9 @@ double estimate(const csr_problem_t& p, const csr_schedule_t& s, const int64_t* 
     const bool wide = (s.flags & CSR_SCHED_WIDE) != 0;
     const double lanes_used = (p.op == CSR_OP_MHA || wide) ? 1.0
         : (double)p.width / ((double)s.group_lanes * s.vec * s.passes);
-    const double bytes = p.nnz * (8.0 + (wide ? 0.82 : 1.0) * row_bytes / (lanes_used > 0 ? lanes_used : 1.0)) +
-                         p.n_rows * p.width * 4.0;
+    double bytes = p.nnz * (8.0 + (wide ? 0.82 : 1.0) * row_bytes / (lanes_used > 0 ? lanes_used : 1.0)) +
+                   p.n_rows * p.width * 4.0;
+    if (p.op == CSR_OP_SPMM_SDDMM) bytes += p.nnz * 4.0 + p.n_rows * p.width * 4.0;  // z written, U read
     double t = bytes / bw;
     const double max_deg = hist ? (double)hist[66] : 0.0;
     if (s.mapping == CSR_MAP_ROWGROUP) {
@@ -662,6 +680,7 @@ uint64_t signature(const csr_problem_t& p, const int64_t* hist, const DeviceInfo
     fnv(h, dev.arch);
     for (int i = 0; i < kHistInts; ++i) fnv(h, hist ? hist[i] : 0);
     if (p.a_idx) fnv(h, 0x58444956);  // 'VIDX': values read through an index
+    if (p.out2_idx) fnv(h, 0x5844495a);  // 'ZIDX': the per-entry output written through an index
     return h;
 }
 
@@ -831,7 +850,7 @@ bool parse_cache_line(const std::string& line, uint64_t* sig, csr_schedule_t* s,
     if (got != 11 || ver != CSR_SCHEDULE_VERSION) return false;
     for (size_t i = (size_t)n; i < line.size(); ++i)
         if (line[i] != '\n' && line[i] != '\r' && line[i] != ' ') return false;
-    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_ATTENTION_QK) return false;
+    if (t.op < CSR_OP_SPMM || t.op > CSR_OP_SPMM_SDDMM) return false;
     if (t.mapping != CSR_MAP_ROWGROUP && t.mapping != CSR_MAP_MERGEPATH && t.mapping != CSR_MAP_SEGSCAN) return false;
     t.version = CSR_SCHEDULE_VERSION;
     *sig = sg;

@@ -73,6 +73,8 @@ __global__ void k_merge_path(const int32_t* row_ptr, int64_t n_rows, int64_t nnz
 }
 
 // Counts violations of the CSR invariants into *bad (zeroed beforehand).
+// col_idx may be null (the row softmax and its backward read no columns):
+// then only row_ptr is checked.
 __global__ void k_validate(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_cols,
                            int64_t nnz, int64_t* bad)
 {
@@ -81,9 +83,11 @@ __global__ void k_validate(const int32_t* row_ptr, const int32_t* col_idx, int64
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t == 0) local += (row_ptr[0] != 0) + ((int64_t)row_ptr[n_rows] != nnz);
     for (int64_t i = t; i < n_rows; i += stride) local += row_ptr[i + 1] < row_ptr[i];
-    for (int64_t e = t; e < nnz; e += stride) {
-        const int c = col_idx[e];
-        local += (c < 0) || ((int64_t)c >= n_cols);
+    if (col_idx) {
+        for (int64_t e = t; e < nnz; e += stride) {
+            const int c = col_idx[e];
+            local += (c < 0) || ((int64_t)c >= n_cols);
+        }
     }
     if (local) atomicAdd(reinterpret_cast<unsigned long long*>(bad), local);
 }

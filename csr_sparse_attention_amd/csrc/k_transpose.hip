@@ -73,6 +73,16 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_gather(const int32_t* perm, const
     if (k < n) dst[k] = src[perm[k]];
 }
 
+// inv[perm[k]] = k; indices outside [0, n) are skipped
+__global__ __launch_bounds__(CSR_BLOCK) void k_invert(const int32_t* perm, int32_t* inv, int64_t n)
+{
+    const int64_t k = (int64_t)blockIdx.x * CSR_BLOCK + threadIdx.x;
+    if (k < n) {
+        const int32_t p = perm[k];
+        if (p >= 0 && (int64_t)p < n) inv[p] = (int32_t)k;
+    }
+}
+
 static unsigned full_grid(int64_t n) { return (unsigned)((n + CSR_BLOCK - 1) / CSR_BLOCK); }
 
 static unsigned grid_of(int64_t n)
@@ -139,6 +149,13 @@ hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows
 {
     if (nnz == 0 || n_rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_coo_rows, dim3(full_grid(n_rows)), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
+    return hipGetLastError();
+}
+
+hipError_t launch_invert(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_invert, dim3(full_grid(n)), dim3(CSR_BLOCK), 0, s, perm, inv, n);
     return hipGetLastError();
 }
 

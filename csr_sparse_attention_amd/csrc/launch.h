@@ -33,6 +33,9 @@ constexpr int unroll_for(int vec, int nv)
 // Returns hipSuccess or the launch error.  mapping: 1 row-group, 2 merge path
 // (main pass; the fix-up is launched separately).
 hipError_t launch_spmm(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
+// SpMM + SDDMM on one pattern sharing the gathered rows (fp32; row-group and
+// merge-path mappings; split rows then go through launch_spmm_fixup)
+hipError_t launch_dual(int mapping, int vec, int nv, int chunk, const Fp32Args& a, hipStream_t s);
 hipError_t launch_spmm_fixup(int vec, int nv, const Fp32Args& a, hipStream_t s);
 // row-group SpMM with wide lanes (one row per wave, 4 floats per lane, nv passes)
 hipError_t launch_spmm_wide(int nv, const Fp32Args& a, hipStream_t s);
@@ -75,6 +78,7 @@ hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int6
                             int64_t nnz, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm, void* ws,
                             size_t ws_bytes, hipStream_t s);
 hipError_t launch_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n, hipStream_t s);
+hipError_t launch_invert(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s);
 // the COO row array: rows[e] = the row holding entry e
 hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows, int64_t nnz, hipStream_t s);
 

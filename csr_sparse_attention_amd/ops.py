@@ -408,6 +408,59 @@ def spmm(row_ptr, col_idx, vals, X, *, val_idx=None, out=None, schedule: Optiona
     return out
 
 
+def _index_arg(t, name, nnz):
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.numel() != nnz:
+        raise ValueError(f"{name} must be a contiguous 1-D int32 tensor of {nnz} entries")
+
+
+def _spmm_sddmm_problem(row_ptr, col_idx, vals, X, U, out, z, val_idx, z_idx):
+    ldx = _dense(X, "X", torch.float32)
+    ldu = _dense(U, "U", torch.float32)
+    ldy = _dense(out, "out", torch.float32)
+    p = _problem(_ffi.OP_SPMM_SDDMM, row_ptr, col_idx, vals, X, U, out, n_cols=X.shape[0], width=X.shape[1],
+                 ld_b=ldx, ld_out=ldy)
+    p.ld_c = ldu
+    p.a_idx, p.out2, p.out2_idx = _ptr(val_idx), _ptr(z), _ptr(z_idx)
+    return p
+
+
+def spmm_sddmm(row_ptr, col_idx, vals, X, U, *, val_idx=None, z_idx=None, out=None, z=None,
+               schedule: Optional[CsrSchedule] = None, ctx: Optional[Context] = None,
+               workspace: Optional[torch.Tensor] = None):
+    """Y = A X and z_e = <U[row_e], X[col_e]> from one read of each gathered
+    row of X (csr_spmm_sddmm; fp32).  vals=None means 1; with ``val_idx``
+    entry e's value is vals[val_idx[e]]; with ``z_idx`` (distinct indices in
+    [0, nnz)) z_e is written at z[z_idx[e]].  X [n_cols, F], U [n_rows, F];
+    returns (Y [n_rows, F], z [nnz])."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    _on(row_ptr.device, vals=vals, X=X, U=U, val_idx=val_idx, z_idx=z_idx, out=out, z=z)
+    if X.dim() != 2 or U.dim() != 2:
+        raise ValueError("X and U must be 2-D")
+    if U.shape[0] != n_rows or U.shape[1] != X.shape[1]:
+        raise ValueError(f"U must be [n_rows={n_rows}, F={X.shape[1]}]")
+    if vals is not None:
+        _entries(vals, "vals", nnz)
+    if val_idx is not None:
+        if vals is None:
+            raise ValueError("val_idx needs vals")
+        _index_arg(val_idx, "val_idx", nnz)
+    if z_idx is not None:
+        _index_arg(z_idx, "z_idx", nnz)
+    out = _out_rows(out, n_rows, X.shape[1], X.device)
+    if z is None:
+        z = torch.empty(nnz, dtype=torch.float32, device=X.device)
+    _entries(z, "z", nnz)
+    p = _spmm_sddmm_problem(row_ptr, col_idx, vals, X, U, out, z, val_idx, z_idx)
+
+    def call(ctx, ws, nb, st):
+        return _lib().csr_spmm_sddmm(ctx.handle, p.n_rows, p.n_cols, p.nnz, p.row_ptr, p.col_idx, p.a, p.a_idx,
+                                     p.b, p.width, p.ld_b, p.c, p.ld_c, p.out, p.ld_out, p.out2, p.out2_idx,
+                                     _sched_arg(schedule), ws.data_ptr(), nb, st)
+
+    _run(p, X.device, schedule, ctx, call, workspace)
+    return out, z
+
+
 def spmm_noalloc(row_ptr, col_idx, vals, X, *, schedule: CsrSchedule, out=None,
                  ctx: Optional[Context] = None) -> torch.Tensor:
     """spmm without a workspace (csr_spmm_noalloc): the kernels' scratch lives
@@ -656,18 +709,22 @@ def row_softmax_backward(row_ptr, probs, grad, *, scale: float = 1.0, out=None,
 
 class Transposed(NamedTuple):
     """The CSR pattern of A^T: row_ptr [n_cols + 1], col_idx [nnz] (rows of A)
-    and perm [nnz] (the entry of A behind each entry of A^T)."""
+    and perm [nnz] (the entry of A behind each entry of A^T); inv [nnz] (the
+    position in A^T of each entry of A, perm's inverse) when asked for."""
     row_ptr: torch.Tensor
     col_idx: torch.Tensor
     perm: torch.Tensor
+    inv: Optional[torch.Tensor] = None
 
 
-def transpose(row_ptr, col_idx, n_cols: int, *, ctx: Optional[Context] = None) -> Transposed:
+def transpose(row_ptr, col_idx, n_cols: int, *, inverse: bool = False,
+              ctx: Optional[Context] = None) -> Transposed:
     """CSR of A^T for the pattern (row_ptr, col_idx) with n_cols columns; the
     entries of each column keep their row order (deterministic).  row_ptr is
     checked only on a validating context; without the check, and with col_idx
     in range, a row_ptr that is not monotone still yields rows in
-    [0, n_rows) and a permutation of the entries (which rows is unspecified)."""
+    [0, n_rows) and a permutation of the entries (which rows is unspecified).
+    ``inverse``: also the inverse of perm (csr_inverse_permutation)."""
     n_rows, nnz = _pattern(row_ptr, col_idx)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)
@@ -682,7 +739,21 @@ def transpose(row_ptr, col_idx, n_cols: int, *, ctx: Optional[Context] = None) -
     _check(lib.csr_transpose(ctx.handle, n_rows, n_cols, nnz, row_ptr.data_ptr(), col_idx.data_ptr(),
                              t_rp.data_ptr(), t_ci.data_ptr(), perm.data_ptr(), ws.data_ptr(), nbytes.value,
                              _stream(device)), "csr_transpose", ctx)
-    return Transposed(t_rp, t_ci, perm)
+    return Transposed(t_rp, t_ci, perm, inverse_permutation(perm, ctx=ctx) if inverse else None)
+
+
+def inverse_permutation(perm, *, out=None, ctx: Optional[Context] = None) -> torch.Tensor:
+    """inv[perm[k]] = k for a permutation perm of [0, n) (int32 on the GPU)."""
+    if perm.dtype != torch.int32 or perm.dim() != 1 or not perm.is_contiguous() or not perm.is_cuda:
+        raise ValueError("perm must be a contiguous 1-D int32 GPU tensor")
+    if out is None:
+        out = torch.empty_like(perm)
+    _on(perm.device, out=out)
+    _index_arg(out, "out", perm.numel())
+    ctx = ctx or default_context(perm.device.index)
+    _check(_lib().csr_inverse_permutation(ctx.handle, perm.numel(), perm.data_ptr(), out.data_ptr(),
+                                          _stream(perm.device)), "csr_inverse_permutation", ctx)
+    return out
 
 
 def gather_values(perm, src, *, out=None, ctx: Optional[Context] = None) -> torch.Tensor:
@@ -737,11 +808,21 @@ def attention_backward(row_ptr, col_idx, edge_scores, node_value, d_out, *, scal
                        transposed: Optional[Transposed] = None, fused: bool = True, ctx: Optional[Context] = None):
     """Gradients of out = softmax_row(scale * S) V (scores given): returns
     (d edge_scores, d node_value).  P is recomputed by row_softmax unless given;
-    dP = SDDMM(d_out, V); d scores = row_softmax_backward(P, dP); dV = P^T d_out
-    (P read through the transposed pattern's perm unless ``fused`` is False)."""
-    At = transposed or transpose(row_ptr, col_idx, node_value.shape[0], ctx=ctx)
+    dV = P^T d_out and dP = SDDMM(d_out, V); d scores = row_softmax_backward(P,
+    dP).  ``fused``: dV and dP in one pass over the transposed pattern
+    (spmm_sddmm: each gathered d_out row read once for both, P read through
+    the transposed pattern's perm, dP written in the transposed order), dP
+    gathered back into A's order through perm's inverse, then the softmax
+    backward; otherwise P is gathered into the transposed order, then an SpMM
+    and an SDDMM."""
+    At = transposed or transpose(row_ptr, col_idx, node_value.shape[0], inverse=fused, ctx=ctx)
     P = probs if probs is not None else row_softmax(row_ptr, edge_scores, scale=scale, ctx=ctx)
-    dV = spmm_transposed(At, P, d_out, fused=fused, ctx=ctx)
+    if fused:
+        inv = At.inv if At.inv is not None else inverse_permutation(At.perm, ctx=ctx)
+        dV, dPt = spmm_sddmm(At.row_ptr, At.col_idx, P, d_out, node_value, val_idx=At.perm, ctx=ctx)
+        dP = gather_values(inv, dPt, ctx=ctx)
+        return row_softmax_backward(row_ptr, P, dP, scale=scale, out=dP, ctx=ctx), dV
+    dV = spmm_transposed(At, P, d_out, fused=False, ctx=ctx)
     dP = sddmm(row_ptr, col_idx, d_out, node_value, ctx=ctx)
     dS = row_softmax_backward(row_ptr, P, dP, scale=scale, out=dP, ctx=ctx)
     return dS, dV
@@ -1074,16 +1155,19 @@ def plan_sddmm(pl: Plan, U, V, *, out=None, ctx: Optional[Context] = None,
     return out
 
 
-def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0, val_idx=None) -> CsrProblem:
+def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 1.0, val_idx=None,
+                 z_idx=None) -> CsrProblem:
     """The csr_problem_t of a call, for select() / workspace_size() /
     default_schedule(): op is 'spmm' (vals, X; val_idx: the value index of
-    csr_spmm_perm), 'sddmm' (U, V), 'attention' (edge_scores, node_value),
+    csr_spmm_perm), 'spmm_sddmm' (vals, X, U; val_idx, z_idx), 'sddmm' (U, V), 'attention' (edge_scores, node_value),
     'mha' (Q, K, V) or 'attention_qk' (Q, K, V: the problem that
     csr_attention runs for them)."""
     _pattern(row_ptr, row_ptr if col_idx is None else col_idx)
     n_rows = row_ptr.numel() - 1
-    if val_idx is not None and op != "spmm":
-        raise ValueError("val_idx serves 'spmm'")
+    if val_idx is not None and op not in ("spmm", "spmm_sddmm"):
+        raise ValueError("val_idx serves 'spmm' and 'spmm_sddmm'")
+    if z_idx is not None and op != "spmm_sddmm":
+        raise ValueError("z_idx serves 'spmm_sddmm'")
     if op == "spmm":
         vals, X = operands
         out = out if out is not None else torch.empty((n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
@@ -1091,6 +1175,11 @@ def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 
         if val_idx is not None:
             p.a_idx = val_idx.data_ptr()
         return p, out
+    if op == "spmm_sddmm":
+        vals, X, U = operands
+        out = out if out is not None else torch.empty((n_rows, X.shape[1]), dtype=torch.float32, device=X.device)
+        z = torch.empty(col_idx.numel(), dtype=torch.float32, device=X.device)
+        return _spmm_sddmm_problem(row_ptr, col_idx, vals, X, U, out, z, val_idx, z_idx), out
     if op == "sddmm":
         U, V = operands
         out = out if out is not None else torch.empty(col_idx.numel(), dtype=torch.float32, device=U.device)
@@ -1120,11 +1209,11 @@ def make_problem(op: str, row_ptr, col_idx, *operands, out=None, scale: float = 
 
 
 def select(op: str, row_ptr, col_idx, *operands, mode: str = "auto", scale: float = 1.0, out=None,
-           val_idx=None, ctx: Optional[Context] = None):
+           val_idx=None, z_idx=None, ctx: Optional[Context] = None):
     """Runs the selector for a call; returns (schedule, signature).  With
     mode 'auto' or 'probe' the candidates run on the given operands and write
     ``out``."""
-    p, out = make_problem(op, row_ptr, col_idx, *operands, out=out, scale=scale, val_idx=val_idx)
+    p, out = make_problem(op, row_ptr, col_idx, *operands, out=out, scale=scale, val_idx=val_idx, z_idx=z_idx)
     device = row_ptr.device
     ctx = ctx or default_context(device.index)
     lib = _lib()

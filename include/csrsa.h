@@ -86,7 +86,8 @@ enum csr_op {
     CSR_OP_MHA = 4,       /* multi-head, scores = scale * <Q_i, K_j> per head */
     CSR_OP_ROW_SOFTMAX = 5, /* p_e = softmax over the row's entries of scale * s */
     CSR_OP_SOFTMAX_BWD = 6, /* ds_e = scale * p_e * (g_e - sum over the row of p g) */
-    CSR_OP_ATTENTION_QK = 7 /* one head, scores = scale * <Q_i, K_j> formed in the same pass */
+    CSR_OP_ATTENTION_QK = 7, /* one head, scores = scale * <Q_i, K_j> formed in the same pass */
+    CSR_OP_SPMM_SDDMM = 8   /* Y = A X and z_e = <U[row_e], X[col_e]> from one gather of X */
 };
 
 /* Element types of the dense operands.  bf16 operands are raw bfloat16 bit
@@ -176,6 +177,10 @@ typedef struct csr_schedule_s {
  *                          a = Q [n_rows, ld_a], b = K [n_cols, ld_b], c = V [n_cols, ld_c]
  *                          (all of dtype), width = head_dim (<= 1024), out fp32
  *                          [n_rows, ld_out], scale
+ *   op = CSR_OP_SPMM_SDDMM: a = vals (fp32 [nnz] or NULL = all ones), a_idx (optional),
+ *                          b = X fp32 [n_cols, ld_b], c = U fp32 [n_rows, ld_c],
+ *                          width = F, out = Y fp32 [n_rows, ld_out], out2 = z fp32,
+ *                          out2_idx (optional)
  *   probs (attention ops, optional): the softmax probability of every entry,
  *   at probs[e * probs_stride] (stride 0 means 1); multi-head: [nnz, heads].
  */
@@ -200,7 +205,9 @@ typedef struct csr_problem_s {
     int64_t ld_c;          /* CSR_OP_ATTENTION_QK: leading dimension of c */
     float* probs;          /* attention ops: per-entry probabilities out, or NULL */
     int64_t probs_stride;  /* floats between consecutive entries' probabilities (0: 1) */
-    const int32_t* a_idx;  /* CSR_OP_SPMM: entry e's value is a[a_idx[e]] (NULL: a[e]) */
+    const int32_t* a_idx;  /* CSR_OP_SPMM, CSR_OP_SPMM_SDDMM: entry e's value is a[a_idx[e]] (NULL: a[e]) */
+    float* out2;           /* CSR_OP_SPMM_SDDMM: the per-entry output z */
+    const int32_t* out2_idx; /* CSR_OP_SPMM_SDDMM: z_e is written at out2[out2_idx[e]] (NULL: out2[e]) */
 } csr_problem_t;
 
 /* ---------------------------------------------------------------------------
@@ -262,6 +269,33 @@ int csr_spmm_perm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
                   const int32_t* row_ptr, const int32_t* col_idx, const float* vals, const int32_t* val_idx,
                   const void* X, int32_t x_dtype, int64_t F, int64_t ldx, float* Y, int64_t ldy,
                   const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
+
+/* SpMM and SDDMM on one pattern sharing the gathered operand (AutoSAGE page,
+ * Abstract: CSR SpMM and CSR SDDMM; SparseTIR page, Abstract: sparse
+ * operators of GNN training):
+ *   Y[i, f] = sum over stored entries e of row i of w_e * X[col_idx[e], f]
+ *   z[t_e] = sum over f of U[i, f] * X[col_idx[e], f]   (e a stored entry of row i)
+ * with w_e = vals[val_idx[e]] (val_idx given), vals[e], or 1 (vals NULL), and
+ * t_e = z_idx[e] (z_idx given) or e.  Each gathered row X[col_idx[e], :] is
+ * read once for both products.  On the pattern of A^T (csr_transpose) with
+ * X = dOut, U = V, vals = P, val_idx = z_idx = t_perm, this gives in one pass
+ * the two products of the backward of out = P V that read dOut: dV = P^T dOut
+ * and dP = dOut V^T, the latter at A's entry positions.
+ * X: fp32 [n_cols, ldx]; U: fp32 [n_rows, ldu]; Y: fp32 [n_rows, ldy]
+ * (F <= ldx, ldu, ldy; 1 <= F <= 4096); z: fp32 [nnz].  val_idx, z_idx:
+ * int32 [nnz], every index
+ * in [0, nnz) (checked only with CSR_CTX_VALIDATE: CSR_ERR_INVALID_CSR; an
+ * index out of range otherwise reads or writes outside vals or z); the
+ * entries of z_idx must be distinct (a permutation, as t_perm is): two
+ * entries with one slot leave either value in it.  Operands are fp32 (the
+ * call has no dtype argument); schedules take the row-group or merge-path
+ * mapping and no flags.  Other rules and errors as for csr_spmm. */
+int csr_spmm_sddmm(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                   const int32_t* row_ptr, const int32_t* col_idx, const float* vals,
+                   const int32_t* val_idx, const float* X, int64_t F, int64_t ldx,
+                   const float* U, int64_t ldu, float* Y, int64_t ldy, float* z,
+                   const int32_t* z_idx, const csr_schedule_t* sched, void* workspace,
+                   size_t ws_bytes, void* stream);
 
 /* Scratch capacity (bytes per GPU) of csr_spmm_noalloc. */
 #define CSR_NOALLOC_SCRATCH_BYTES (32u << 20)
@@ -387,6 +421,7 @@ int csr_row_softmax_backward(csr_context_t ctx, int64_t n_rows, int64_t nnz, con
                              const float* probs, const float* grad_probs, float scale, float* grad_scores,
                              const csr_schedule_t* sched, void* workspace, size_t ws_bytes, void* stream);
 
+
 /* Device workspace (bytes) that csr_transpose needs for these sizes.
  * Returns CSR_ERR_SHAPE for negative sizes or sizes beyond int32 indices,
  * CSR_ERR_DEVICE on a host-only context. */
@@ -409,6 +444,14 @@ int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
  * per-entry values (edge values, probabilities, gradients) into the order of
  * a transposed pattern. */
 int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const float* src, float* dst, void* stream);
+
+/* inv[perm[k]] = k for k < n: the inverse of a permutation of [0, n) (for a
+ * transposed pattern's t_perm: the position in A^T of each entry of A).  An
+ * index of perm outside [0, n) is skipped (nothing is written for it); perm
+ * must be a permutation for inv to be complete (not checked).  inv must not
+ * alias perm (CSR_ERR_SHAPE when they are the same array).  CSR_ERR_SHAPE
+ * for n < 0 or n >= 2^31. */
+int csr_inverse_permutation(csr_context_t ctx, int64_t n, const int32_t* perm, int32_t* inv, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Column-part segment format (a composed, "hybrid" format)

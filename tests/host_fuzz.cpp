@@ -45,7 +45,7 @@ static csr_problem_t random_problem()
     static const int64_t widths[] = {-3, 0, 1, 2, 3, 4, 5, 8, 16, 32, 64, 100, 128, 512, 602, 1024, 4096, 4097};
     csr_problem_t p;
     std::memset(&p, 0, sizeof p);
-    p.op = (int32_t)(next() % 9);  // includes invalid ops 0 and 8
+    p.op = (int32_t)(next() % 10);  // includes invalid ops 0 and 9
     p.dtype = (int32_t)(next() % 3);
     p.n_rows = pick(sizes, 11);
     p.n_cols = pick(sizes, 11);
@@ -78,9 +78,9 @@ static csr_problem_t random_problem()
     if (next() % 2) {
         // mostly well-formed: the op's dtype, positive sizes, natural strides
         // and aligned operands, with any width
-        p.op = 1 + (int32_t)(next() % 7);
+        p.op = 1 + (int32_t)(next() % 8);
         const bool lane_group = p.op == CSR_OP_SPMM || p.op == CSR_OP_SDDMM || p.op == CSR_OP_ATTENTION ||
-                                p.op == CSR_OP_ATTENTION_QK;
+                                p.op == CSR_OP_ATTENTION_QK;  // fp32 or bf16; CSR_OP_SPMM_SDDMM: fp32
         p.dtype = (p.op == CSR_OP_MHA || (lane_group && next() % 3 == 0)) ? CSR_DTYPE_BF16 : CSR_DTYPE_F32;
         p.n_rows = 1 + (int64_t)(next() % 3000000);
         p.n_cols = 1 + (int64_t)(next() % 3000000);
@@ -106,8 +106,11 @@ static csr_problem_t random_problem()
                       ? reinterpret_cast<float*>(good[next() % 4]) : nullptr;
         p.probs_stride = 1;
         p.scale = 0.125f;
+        if (p.op == CSR_OP_SPMM_SDDMM) p.out2 = reinterpret_cast<float*>(good[next() % 4]);
     }
     p.a_idx = (next() % 4 == 0) ? static_cast<const int32_t*>(ptr()) : nullptr;
+    if (next() % 4 == 0) p.out2 = static_cast<float*>(ptr());
+    p.out2_idx = (next() % 4 == 0) ? static_cast<const int32_t*>(ptr()) : nullptr;
     return p;
 }
 
@@ -146,8 +149,15 @@ int main(int argc, char** argv)
         random_hist(hist, p);
         if (rc == CSR_OK) {
             ++accepted;
-            CHECK(!p.a_idx || (p.op == CSR_OP_SPMM && ((uintptr_t)p.a_idx % 4) == 0 && (!need_ptrs || p.nnz == 0 || p.a)),
+            CHECK(!p.a_idx || ((p.op == CSR_OP_SPMM || p.op == CSR_OP_SPMM_SDDMM) && ((uintptr_t)p.a_idx % 4) == 0 &&
+                               (!need_ptrs || p.nnz == 0 || p.a)),
                   "value index accepted for op %d\n", p.op);
+            CHECK((!p.out2 && !p.out2_idx) ||
+                      (p.op == CSR_OP_SPMM_SDDMM && ((uintptr_t)p.out2 % 4) == 0 && ((uintptr_t)p.out2_idx % 4) == 0),
+                  "second output accepted for op %d\n", p.op);
+            CHECK(p.op != CSR_OP_SPMM_SDDMM ||
+                      (p.dtype == CSR_DTYPE_F32 && (!need_ptrs || p.nnz == 0 || (p.c && p.out2))),
+                  "SpMM + SDDMM accepted without fp32 operands, U or z\n");
             const csr_schedule_t d = csrh::default_schedule(p);
             CHECK(csrh::check_schedule(p, d, &why) == CSR_OK, "default schedule rejected (op %d F %lld): %s\n",
                   p.op, (long long)p.width, why.c_str());
@@ -213,7 +223,7 @@ int main(int argc, char** argv)
         csr_schedule_t s;
         std::memset(&s, 0, sizeof s);
         s.version = (int32_t)(next() % 3);
-        s.op = (int32_t)(next() % 8);
+        s.op = (int32_t)(next() % 10);
         s.mapping = (int32_t)(next() % 5);
         s.vec = (int32_t)(next() % 10);
         s.group_lanes = (int32_t)(1 << (next() % 8)) - (int32_t)(next() % 2);

@@ -1154,3 +1154,169 @@ def test_attention_heads_given_scores_errors():
         csa.attention(rp, ci, sd, V, out=torch.empty((csr.n_rows, 2, 4), device="cuda"))
     with pytest.raises(ValueError):
         csa.attention(rp, ci, sd, V, probs=torch.empty((2, csr.nnz), device="cuda"))  # probs are [nnz, H]
+
+
+# ---------------------------------------------------------------------------
+# SpMM + SDDMM sharing the gathered rows (csr_spmm_sddmm)
+# ---------------------------------------------------------------------------
+
+def _as_op(s, op):
+    t = csa.CsrSchedule.from_buffer_copy(bytes(s))
+    t.op = op
+    return t
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("F", [1, 5, 32, 64, 100])
+def test_spmm_sddmm_every_schedule(graph, F):
+    """Y = A X and z_e = <U[row_e], X[col_e]> from one pass under every
+    schedule: each against the oracle's SpMM and SDDMM, and bit for bit equal
+    to csr_spmm and csr_sddmm under the same lane layout and mapping (the same
+    sums in the same order)."""
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(640 + F)
+    vals = rng.standard_normal(csr.nnz).astype(np.float32)
+    X = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    U = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    vd, Xd, Ud = dev(vals), dev(X), dev(U)
+    th = oracle.default_threads()
+    refY, magY = oracle.spmm(csr.row_ptr, csr.col_idx, vals, X, threads=th)
+    refZ, magZ = oracle.sddmm(csr.row_ptr, csr.col_idx, U, X, threads=th)
+    p, _ = csa.make_problem("spmm_sddmm", rp, ci, vd, Xd, Ud)
+    scheds = schedules(p)
+    assert any(s.mapping == csa.MAP_ROWGROUP for s in scheds) and any(s.mapping == csa.MAP_MERGEPATH for s in scheds)
+    for s in scheds:
+        Y, z = csa.spmm_sddmm(rp, ci, vd, Xd, Ud, schedule=s)
+        assert_close(Y.cpu().numpy(), refY, magY, TOL_F32, f"Y {sched_id(s)}")
+        assert_close(z.cpu().numpy(), refZ, magZ, TOL_F32, f"z {sched_id(s)}")
+        assert torch.equal(Y, csa.spmm(rp, ci, vd, Xd, schedule=_as_op(s, _ffi.OP_SPMM))), sched_id(s)
+        assert torch.equal(z, csa.sddmm(rp, ci, Ud, Xd, schedule=_as_op(s, _ffi.OP_SDDMM))), sched_id(s)
+    # without values (all ones), automatic selection
+    refY1, magY1 = oracle.spmm(csr.row_ptr, csr.col_idx, np.ones(csr.nnz, np.float32), X, threads=th)
+    Y, z = csa.spmm_sddmm(rp, ci, None, Xd, Ud)
+    assert_close(Y.cpu().numpy(), refY1, magY1, TOL_F32, "ones")
+    assert_close(z.cpu().numpy(), refZ, magZ, TOL_F32, "ones z")
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges"])
+@pytest.mark.parametrize("F", [24, 64])
+def test_spmm_sddmm_transposed(graph, F):
+    """On A^T with A's values read and z written through the transposed
+    pattern's perm: dV = P^T dOut and dP = dOut V^T at A's entry positions
+    (the two products of attention's backward that gather dOut)."""
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(650 + F)
+    P = rng.random(csr.nnz).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    Pd, dOd, Vd = dev(P), dev(dO), dev(V)
+    refV, magV = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P.astype(np.float64), dO, csr.n_cols)
+    refP, magP = oracle.sddmm(csr.row_ptr, csr.col_idx, dO, V, threads=oracle.default_threads())
+    p, _ = csa.make_problem("spmm_sddmm", t.row_ptr, t.col_idx, Pd, dOd, Vd, val_idx=t.perm)
+    for s in schedules(p) + [None]:
+        dV, dP = csa.spmm_sddmm(t.row_ptr, t.col_idx, Pd, dOd, Vd, val_idx=t.perm, z_idx=t.perm, schedule=s)
+        what = "auto" if s is None else sched_id(s)
+        assert_close(dV.cpu().numpy(), refV, magV, TOL_F32, f"dV {what}")
+        assert_close(dP.cpu().numpy(), refP, magP, TOL_F32, f"dP {what}")
+
+
+def test_spmm_sddmm_infinite_features():
+    """An infinite feature gives an infinite dot product, not NaN, also where
+    lanes past the width (F = 5 on 8 lanes) read the row's first features."""
+    csr = dup_graph(11)
+    rng = np.random.default_rng(660)
+    F = 5
+    X = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    U = (rng.random((csr.n_rows, F)) + 0.5).astype(np.float32)
+    X[::7, 0] = np.inf
+    rp, ci = pattern_dev(csr)
+    vd = dev(np.ones(csr.nnz, np.float32))
+    p, _ = csa.make_problem("spmm_sddmm", rp, ci, vd, dev(X), dev(U))
+    want = np.where(np.isin(csr.col_idx, np.arange(0, csr.n_cols, 7)), np.inf, 0.0)
+    for s in schedules(p, thorough=False):
+        _, z = csa.spmm_sddmm(rp, ci, vd, dev(X), dev(U), schedule=s)
+        z = z.cpu().numpy()
+        hot = want == np.inf
+        assert np.all(z[hot] == np.inf), sched_id(s)
+        assert np.all(np.isfinite(z[~hot])), sched_id(s)
+
+
+def test_spmm_sddmm_errors_and_validation():
+    csr = skew_graph(3, n_rows=600, n_cols=4000, giant=3000)
+    rng = np.random.default_rng(661)
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols)
+    vd = dev(rng.standard_normal(csr.nnz).astype(np.float32))
+    X = dev(rng.standard_normal((csr.n_rows, 16)).astype(np.float32))
+    U = dev(rng.standard_normal((csr.n_cols, 16)).astype(np.float32))
+    with pytest.raises(ValueError):
+        csa.spmm_sddmm(t.row_ptr, t.col_idx, None, X, U, val_idx=t.perm)
+    with pytest.raises(ValueError):
+        csa.spmm_sddmm(t.row_ptr, t.col_idx, vd, X, U[1:])
+    with pytest.raises(ValueError):
+        csa.spmm_sddmm(t.row_ptr, t.col_idx, vd, X, U, z=torch.empty(csr.nnz - 1, device="cuda"))
+    with pytest.raises(TypeError):
+        csa.spmm_sddmm(t.row_ptr, t.col_idx, vd, X.to(torch.bfloat16), U)
+    lib = csa.load_library()
+    ctx = csa.Context(0, None)
+    Y = torch.empty((csr.n_cols, 16), device="cuda")
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib.csr_spmm_sddmm(ctx.handle, csr.n_cols, csr.n_rows, csr.nnz, t.row_ptr.data_ptr(), t.col_idx.data_ptr(),
+                            vd.data_ptr(), None, X.data_ptr(), 16, 16, U.data_ptr(), 16, Y.data_ptr(), 16, None,
+                            None, None, ws.data_ptr(), ws.numel(), st)
+    assert rc == -1  # CSR_ERR_NULL: no z
+    ctx.close()
+    # an index out of range is caught on a validating context, before any product runs
+    vctx = csa.Context(0, None, csa.CTX_VALIDATE)
+    for which in ("val_idx", "z_idx"):
+        bad = t.perm.clone()
+        bad[csr.nnz // 2] = csr.nnz
+        kw = {"val_idx": t.perm, "z_idx": t.perm, which: bad}
+        with pytest.raises(csa.CsrError) as ei:
+            csa.spmm_sddmm(t.row_ptr, t.col_idx, vd, X, U, ctx=vctx, **kw)
+        assert "CSR_ERR_INVALID_CSR" in str(ei.value)
+    vctx.close()
+
+
+# ---------------------------------------------------------------------------
+# the inverse permutation (entries of A to their positions in A^T)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges"])
+def test_inverse_permutation_bit_exact(graph):
+    csr = _graphs_for_backward()[graph]
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols, inverse=True)
+    perm = oracle.transpose(csr.row_ptr, csr.col_idx, csr.n_cols)[2]
+    want = np.empty_like(perm)
+    want[perm] = np.arange(perm.size, dtype=perm.dtype)
+    assert np.array_equal(t.inv.cpu().numpy(), want)
+    assert np.array_equal(csa.inverse_permutation(t.perm).cpu().numpy(), want)
+    with pytest.raises(csa.CsrError):
+        csa.inverse_permutation(t.perm, out=t.perm)  # perm and inv alias
+
+
+def test_validating_context_row_softmax_ops():
+    """The row softmax and its backward have no column indices: a validating
+    context checks their row_ptr only (and still catches a bad one)."""
+    csr = dup_graph(12)
+    p, g = _probs_and_grad(csr, 602, 0.5)
+    rp = dev(csr.row_ptr)
+    sc = dev(np.random.default_rng(603).standard_normal(csr.nnz).astype(np.float32))
+    vctx = csa.Context(0, None, csa.CTX_VALIDATE)
+    s, _ = csa.select("row_softmax", rp, None, sc, scale=0.5, mode="estimate")
+    assert torch.equal(csa.row_softmax(rp, sc, scale=0.5, ctx=vctx, schedule=s),
+                       csa.row_softmax(rp, sc, scale=0.5, schedule=s))
+    refb, mag = oracle.softmax_backward(csr.row_ptr, p, g, 0.5)
+    got = csa.row_softmax_backward(rp, dev(p), dev(g), scale=0.5, ctx=vctx)
+    assert_close(got.cpu().numpy(), refb, mag, TOL_F32, "validating context")
+    bad = rp.clone()
+    bad[5] = bad[6] + 1  # not monotone
+    with pytest.raises(csa.CsrError) as ei:
+        csa.row_softmax(bad, sc, scale=0.5, ctx=vctx)
+    assert "CSR_ERR_INVALID_CSR" in str(ei.value)
+    vctx.close()
