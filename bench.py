@@ -40,6 +40,10 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s and GNNZ*F/s per kernel; % of MI355X HBM roofline"
 
 
+# calls without a schedule: per-entry value moves
+NO_SCHEDULE = ("gather", "permute")
+
+
 def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64, esize=4):
     """Algorithmic bytes of one call (index arrays, values, one gathered row
     per stored entry, dense row operands, output); esize = bytes per element
@@ -59,6 +63,9 @@ def b_alg(op, n_rows, nnz, width, heads=8, head_dim=64, esize=4):
         return 4 * (n_rows + 1) + nnz * 12
     if op == "gather":
         return nnz * 12
+    if op == "permute":
+        # two passes: an index, a value and a write each
+        return nnz * 24
     if op == "spmm_sddmm":
         # the SpMM's bytes, the U row per row and the per-entry output
         return 4 * (n_rows + 1) + nnz * 8 + nnz * width * esize + 2 * n_rows * width * 4 + nnz * 4
@@ -277,10 +284,10 @@ def build_workload(name, torch, csa):
     elif name in ("c3bwd", "c3bwd_perm", "c3bwd_gather"):
         # backward of the single-head fp32 attention on the c3 graph (scores
         # given, F = 64): P = row softmax; dV = P^T dOut and dP = dOut V^T;
-        # d scores = softmax backward.  c3bwd: dV and dP in one pass over A^T
-        # (csr_spmm_sddmm, P read through the transposed pattern's perm, dP
-        # written in A^T's order and gathered back through perm's inverse);
-        # c3bwd_perm: SDDMM dP on A, then the
+        # d scores = softmax backward.  c3bwd: P moved into A^T's order by
+        # a two-pass permutation, dV and dP in one pass over A^T
+        # (csr_spmm_sddmm), dP moved back the same way; c3bwd_perm: SDDMM
+        # dP on A, then the
         # SpMM on A^T reading P through the perm; c3bwd_gather: P gathered
         # into A^T's order first.  The transposed pattern is built once,
         # outside the step.
@@ -289,17 +296,17 @@ def build_workload(name, torch, csa):
         S = d(configs.config_dense("c3", "scores", csr) * 3.0)
         Vd = d(configs.config_dense("c3", "X", csr, 64))
         dO = d(configs.config_dense("c3", "V", csr, 64))
-        inverse = name == "c3bwd"  # the fused backward also reads perm's inverse
+        plans = name == "c3bwd"  # the fused backward moves values through two-pass permutation plans
         torch.cuda.synchronize()
         tt = time.perf_counter()
-        At = csa.transpose(rp, ci, csr.n_cols, inverse=inverse)
+        At = csa.transpose(rp, ci, csr.n_cols, plans=plans)
         torch.cuda.synchronize()
         build_workload.transpose_first_ms = (time.perf_counter() - tt) * 1e3
         # again with the buffers already in torch's pool: the build's own time
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         del At
         ev0.record()
-        At = csa.transpose(rp, ci, csr.n_cols, inverse=inverse)
+        At = csa.transpose(rp, ci, csr.n_cols, plans=plans)
         ev1.record()
         ev1.synchronize()
         build_workload.transpose_ms = ev0.elapsed_time(ev1)
@@ -310,13 +317,19 @@ def build_workload(name, torch, csa):
         calls.append(Call("row_softmax", "row_softmax", csa.row_softmax, (rp, S), {"out": P, "scale": 0.125},
                           csr.n_rows, csr.nnz, 1, None))
         if name == "c3bwd":
-            # dP comes out in A^T's order (Pt's buffer) and is gathered back
-            # through perm's inverse; the softmax backward runs in place on it
-            calls.append(Call("spmm_sddmm_dV_dP", "spmm_sddmm", csa.spmm_sddmm, (At.row_ptr, At.col_idx, P, dO, Vd),
-                              {"out": dV, "z": Pt, "val_idx": At.perm}, csr.n_cols, csr.nnz, 64, None))
-            calls[-1].bytes += 4 * csr.nnz  # the value index
-            calls.append(Call("gather_dP", "gather", lambda perm, src, out, schedule=None: csa.gather_values(
-                perm, src, out=out), (At.inv, Pt, dP), {}, csr.n_rows, csr.nnz, 1, None))
+            # P moved into A^T's order and dP back by two-pass permutations;
+            # the softmax backward runs in place on dP
+            dPt = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+            tmp = torch.empty(csr.nnz, dtype=torch.float32, device="cuda")
+
+            def permute(plan, src, out, schedule=None):
+                return csa.permute_values(plan, src, out=out, tmp=tmp)
+
+            calls.append(Call("permute_Pt", "permute", permute, (At.to_t, P, Pt), {}, csr.n_rows, csr.nnz, 1, None))
+            calls.append(Call("spmm_sddmm_dV_dP", "spmm_sddmm", csa.spmm_sddmm, (At.row_ptr, At.col_idx, Pt, dO, Vd),
+                              {"out": dV, "z": dPt}, csr.n_cols, csr.nnz, 64, None))
+            calls.append(Call("permute_dP", "permute", permute, (At.from_t, dPt, dP), {}, csr.n_rows, csr.nnz, 1,
+                              None))
             calls.append(Call("softmax_bwd", "row_softmax_backward", csa.row_softmax_backward, (rp, P, dP),
                               {"out": dP, "scale": 0.125}, csr.n_rows, csr.nnz, 1, None))
             return calls, time.time() - t0
@@ -363,6 +376,10 @@ def check_shapes(calls):
         a = c.args
         if c.op == "gather":
             assert all(t.numel() == c.nnz for t in a), (c.name, "gather operands")
+            continue
+        if c.op == "permute":
+            plan, src, out = a
+            assert all(t.numel() == c.nnz for t in (plan.q1, plan.pos, src, out)), (c.name, "permute operands")
             continue
         assert a[0].numel() == c.n_rows + 1, (c.name, "row_ptr")
         if c.op in ("row_softmax", "row_softmax_backward"):
@@ -462,7 +479,7 @@ def selector_study(calls, torch, csa, rounds=5, per_round=3):
 
     out = {}
     for c in calls:
-        if c.op == "gather":
+        if c.op in NO_SCHEDULE:
             continue
         scale = c.kwargs.get("scale", 1.0)
         args = (c.args[0], None) + tuple(c.args[1:]) if c.op.startswith("row_softmax") else c.args
@@ -823,7 +840,7 @@ def main():
     # cost model, probes) once per call
     sel = {}
     for c in calls:
-        if c.op == "gather":  # no schedule
+        if c.op in NO_SCHEDULE:
             continue
         if c.op in ("spmm", "sddmm") and not args.no_format and "val_idx" not in c.kwargs:
             info = make_plan(c, csa, torch)
@@ -904,7 +921,7 @@ def main():
     for c in calls:
         kernels[c.name]["bytes_compulsory"] = compulsory_bytes(c, torch)
         # counted HBM bytes of the call (committed counter record for these sources, layout and schedule)
-        t = committed_traffic(args.config, c) if c.op != "gather" else None
+        t = committed_traffic(args.config, c) if c.op not in NO_SCHEDULE else None
         kernels[c.name]["traffic_bytes"] = t
         kernels[c.name]["frac_hbm_counted"] = (round(t / (kernels[c.name]["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                                                if t else None)
@@ -939,9 +956,9 @@ def main():
                                 "c3sweep": "CSR SpMM on the log-normal graph at F in {128,256,384,512}: "
                                            "gathered operand of 1.25 to 5.0 GB",
                                 "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "
-                                         "row softmax, dV = P^T dOut and dP = dOut V^T in one pass over A^T "
-                                         "(P read through the transposed pattern's perm, dP in A^T's order), "
-                                         "dP gathered back through the perm's inverse, softmax backward",
+                                         "row softmax, P into A^T's order (two-pass permutation), dV = P^T dOut "
+                                         "and dP = dOut V^T in one pass over A^T, dP back into A's order, "
+                                         "softmax backward",
                                 "c3bwd_perm": "backward of single-head fp32 attention on the log-normal graph, "
                                               "F=64: row softmax, SDDMM dP, softmax backward, SpMM dV on A^T "
                                               "reading P through the transposed pattern's perm",

@@ -46,6 +46,9 @@ from .ops import (  # noqa: E402,F401
     degree_histogram,
     gather_values,
     inverse_permutation,
+    permutation_plan,
+    permute_values,
+    PermutationPlan,
     hybrid_format,
     hybrid_parts,
     hybrid_plan,

@@ -34,7 +34,8 @@ EXPORTS = (
     "csr_context_create", "csr_context_destroy", "csr_status_string", "csr_last_error",
     "csr_spmm", "csr_spmm_perm", "csr_spmm_sddmm", "csr_spmm_noalloc", "csr_sddmm", "csr_attention", "csr_mha_attention", "csr_row_softmax",
     "csr_row_softmax_backward", "csr_transpose_workspace_size", "csr_transpose",
-    "csr_gather_values", "csr_inverse_permutation",
+    "csr_gather_values", "csr_inverse_permutation", "csr_permutation_plan_workspace_size", "csr_permutation_plan",
+    "csr_permute_values",
     "csr_select", "csr_default_schedule", "csr_candidates", "csr_workspace_size", "csr_cache_flush",
     "csr_cache_info", "csr_cache_lookup", "csr_cache_store",
     "csr_degree_histogram", "csr_merge_path_partition", "csr_signature",
@@ -229,6 +230,9 @@ def load() -> ctypes.CDLL:
         "csr_transpose": [P, I64, I64, I64, P, P, P, P, P, P, SZ, P],
         "csr_gather_values": [P, I64, P, P, P, P],
         "csr_inverse_permutation": [P, I64, P, P, P],
+        "csr_permutation_plan_workspace_size": [P, I64, ctypes.POINTER(SZ)],
+        "csr_permutation_plan": [P, I64, P, I32, P, P, P, SZ, P],
+        "csr_permute_values": [P, I64, P, P, P, P, P, P],
         "csr_select": [P, PP, U32, SP, ctypes.POINTER(ctypes.c_uint64)],
         "csr_default_schedule": [P, PP, SP],
         "csr_candidates": [P, PP, ctypes.POINTER(I64), SP, I32, ctypes.POINTER(I32)],

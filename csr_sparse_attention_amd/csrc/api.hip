@@ -1189,6 +1189,56 @@ int csr_inverse_permutation(csr_context_t ctx, int64_t n, const int32_t* perm, i
     return CSR_OK;
 }
 
+static bool perm_size_ok(int64_t n) { return n >= 0 && n < ((int64_t)1 << 31); }
+
+int csr_permutation_plan_workspace_size(csr_context_t ctx, int64_t n, size_t* bytes)
+{
+    if (!ctx || !bytes) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (!perm_size_ok(n)) return set_err(ctx, CSR_ERR_SHAPE, "bad size");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    CSR_HIP(ctx, csrk::permutation_plan_workspace(n, bytes));
+    return CSR_OK;
+}
+
+int csr_permutation_plan(csr_context_t ctx, int64_t n, const int32_t* q, int32_t window_log2, int32_t* q1,
+                         int32_t* pos, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (!perm_size_ok(n) || window_log2 < 8 || window_log2 > 30) return set_err(ctx, CSR_ERR_SHAPE, "bad size or window");
+    if (n > 0 && (!q || !q1 || !pos || !workspace)) return CSR_ERR_NULL;
+    if (n > 0 && ((const void*)q == (const void*)q1 || (const void*)q == (const void*)pos || q1 == pos))
+        return set_err(ctx, CSR_ERR_SHAPE, "q, q1 and pos must not alias");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    size_t need = 0;
+    CSR_HIP(ctx, csrk::permutation_plan_workspace(n, &need));
+    if (ws_bytes < need || (uintptr_t)workspace % csrh::kAlign)
+        return set_err(ctx, CSR_ERR_WORKSPACE, "workspace too small (or not 256-byte aligned) for the plan");
+    CSR_HIP(ctx, csrk::launch_permutation_plan(q, n, window_log2, q1, pos, workspace, ws_bytes,
+                                               static_cast<hipStream_t>(stream)));
+    return CSR_OK;
+}
+
+int csr_permute_values(csr_context_t ctx, int64_t n, const int32_t* q1, const int32_t* pos, const float* src,
+                       float* tmp, float* dst, void* stream)
+{
+    if (!ctx) return CSR_ERR_NULL;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    if (!perm_size_ok(n)) return set_err(ctx, CSR_ERR_SHAPE, "bad size");
+    if (n > 0 && (!q1 || !pos || !src || !tmp || !dst)) return CSR_ERR_NULL;
+    if (n > 0 && (src == tmp || src == dst || tmp == dst))
+        return set_err(ctx, CSR_ERR_SHAPE, "src, tmp and dst must not alias");
+    if (((uintptr_t)q1 | (uintptr_t)pos | (uintptr_t)src | (uintptr_t)tmp | (uintptr_t)dst) % 4)
+        return set_err(ctx, CSR_ERR_ALIGN, "the arrays must be 4-byte aligned");
+    if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
+    DeviceGuard g(ctx->device);
+    CSR_HIP(ctx, csrk::launch_permute(q1, pos, src, tmp, dst, n, static_cast<hipStream_t>(stream)));
+    return CSR_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Column-part segment format
 // ---------------------------------------------------------------------------

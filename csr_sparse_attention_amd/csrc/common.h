@@ -11,6 +11,8 @@
 #define CSR_WAVE 64
 #define CSR_BLOCK 256
 #define CSR_WAVES_PER_BLOCK (CSR_BLOCK / CSR_WAVE)
+// XCDs of an MI355X; a launch's workgroups are dealt to them in turn
+#define CSR_XCDS 8
 
 namespace csrk {
 

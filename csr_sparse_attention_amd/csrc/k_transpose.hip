@@ -73,6 +73,50 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_gather(const int32_t* perm, const
     if (k < n) dst[k] = src[perm[k]];
 }
 
+// One pass of a two-pass permutation: dst[j] = src[idx[j]] (0 for an index
+// outside [0, n)).  Workgroups are dealt to the 8 XCDs in turn, so the grid
+// is laid out XCD-major: workgroup b works on range (b % 8) * per + b / 8 of
+// the n / 256 ranges, and each XCD takes one contiguous eighth of j.  In the
+// first pass j is grouped by the window of src it reads (an XCD then reads
+// a few windows, each into its own L2); in the second, each XCD reads the
+// contiguous runs of every group that its eighth of the output needs.
+// Each thread moves PERM_VEC consecutive entries (one 16-byte index load,
+// PERM_VEC gathers in flight, one 16-byte store); the last partial vector is
+// moved entry by entry.
+constexpr int PERM_VEC = 4;
+// 4 values at a 4-byte aligned address: one 16-byte access (the arrays need
+// not be 16-byte aligned)
+typedef int32_t i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+__global__ __launch_bounds__(CSR_BLOCK) void k_permute_pass(const int32_t* idx, const float* src, float* dst,
+                                                            int64_t n, int64_t per)
+{
+    const int64_t r = (int64_t)(blockIdx.x % CSR_XCDS) * per + blockIdx.x / CSR_XCDS;
+    const int64_t j = (r * CSR_BLOCK + threadIdx.x) * PERM_VEC;
+    if (j >= n) return;
+    if (j + PERM_VEC <= n) {
+        const i32x4_a4 i = *reinterpret_cast<const i32x4_a4*>(idx + j);
+        const int32_t ii[PERM_VEC] = {i.x, i.y, i.z, i.w};
+        float v[PERM_VEC];
+#pragma unroll
+        for (int u = 0; u < PERM_VEC; ++u) v[u] = (ii[u] >= 0 && (int64_t)ii[u] < n) ? src[ii[u]] : 0.f;
+        *reinterpret_cast<f32x4_a4*>(dst + j) = f32x4_a4{v[0], v[1], v[2], v[3]};
+        return;
+    }
+    for (int64_t k = j; k < n; ++k) {
+        const int32_t i = idx[k];
+        dst[k] = (i >= 0 && (int64_t)i < n) ? src[i] : 0.f;
+    }
+}
+
+// keys[e] = q[e] >> wbits (the source window of output e)
+__global__ void k_window_keys(const int32_t* q, int32_t* keys, int64_t n, int wbits)
+{
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+        keys[e] = (int32_t)((uint32_t)q[e] >> wbits);
+}
+
 // inv[perm[k]] = k; indices outside [0, n) are skipped
 __global__ __launch_bounds__(CSR_BLOCK) void k_invert(const int32_t* perm, int32_t* inv, int64_t n)
 {
@@ -149,6 +193,68 @@ hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows
 {
     if (nnz == 0 || n_rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_coo_rows, dim3(full_grid(n_rows)), dim3(CSR_BLOCK), 0, s, row_ptr, n_rows, rows, nnz);
+    return hipGetLastError();
+}
+
+// workgroups of PERM_VEC * CSR_BLOCK entries per XCD
+static int64_t xcd_ranges(int64_t n)
+{
+    const int64_t per_block = (int64_t)CSR_BLOCK * PERM_VEC;
+    return ((n + per_block - 1) / per_block + CSR_XCDS - 1) / CSR_XCDS;
+}
+
+hipError_t permutation_plan_workspace(int64_t n, size_t* bytes)
+{
+    size_t temp = 0;
+    hipError_t e = rocprim::radix_sort_pairs(nullptr, temp, (const int32_t*)nullptr, (int32_t*)nullptr,
+                                             (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned)n, 0, 31);
+    if (e != hipSuccess) return e;
+    *bytes = 4 * up256((size_t)n * 4) + up256(temp);
+    return hipSuccess;
+}
+
+// Plan of dst[e] = src[q[e]] in two passes: the outputs e sorted by the
+// window q[e] >> wbits of the source they read (stable: e ascending within
+// a window) give order; q1[j] = q[order[j]] (pass 1 reads window after
+// window) and pos[order[j]] = j (pass 2 finds output e's value at pos[e]).
+hipError_t launch_permutation_plan(const int32_t* q, int64_t n, int wbits, int32_t* q1, int32_t* pos, void* ws,
+                                   size_t ws_bytes, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    char* w = static_cast<char*>(ws);
+    const size_t arr = up256((size_t)n * 4);
+    int32_t* keys = reinterpret_cast<int32_t*>(w);
+    int32_t* keys_out = reinterpret_cast<int32_t*>(w + arr);
+    int32_t* iota = reinterpret_cast<int32_t*>(w + 2 * arr);
+    int32_t* order = reinterpret_cast<int32_t*>(w + 3 * arr);
+    void* temp = w + 4 * arr;
+    size_t temp_bytes = ws_bytes - 4 * arr;
+    hipLaunchKernelGGL(k_window_keys, dim3(grid_of(n)), dim3(CSR_BLOCK), 0, s, q, keys, n, wbits);
+    hipLaunchKernelGGL(k_iota, dim3(grid_of(n)), dim3(CSR_BLOCK), 0, s, iota, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int bits = key_bits(((n - 1) >> wbits) + 1);
+    size_t need = 0;
+    e = rocprim::radix_sort_pairs(nullptr, need, (const int32_t*)nullptr, (int32_t*)nullptr, (const int32_t*)nullptr,
+                                  (int32_t*)nullptr, (unsigned)n, 0, bits);
+    if (e != hipSuccess) return e;
+    if (need > temp_bytes) return hipErrorInvalidValue;
+    e = rocprim::radix_sort_pairs(temp, temp_bytes, (const int32_t*)keys, keys_out, (const int32_t*)iota, order,
+                                  (unsigned)n, 0, bits, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gather<int32_t>, dim3(full_grid(n)), dim3(CSR_BLOCK), 0, s, (const int32_t*)order, q, q1, n);
+    hipLaunchKernelGGL(k_invert, dim3(full_grid(n)), dim3(CSR_BLOCK), 0, s, (const int32_t*)order, pos, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* q1, const int32_t* pos, const float* src, float* tmp, float* dst, int64_t n,
+                          hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    const int64_t per = xcd_ranges(n);
+    const unsigned grid = (unsigned)(per * CSR_XCDS);
+    hipLaunchKernelGGL(k_permute_pass, dim3(grid), dim3(CSR_BLOCK), 0, s, q1, src, tmp, n, per);
+    hipLaunchKernelGGL(k_permute_pass, dim3(grid), dim3(CSR_BLOCK), 0, s, pos, (const float*)tmp, dst, n, per);
     return hipGetLastError();
 }
 

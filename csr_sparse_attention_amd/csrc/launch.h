@@ -79,6 +79,11 @@ hipError_t launch_transpose(const int32_t* row_ptr, const int32_t* col_idx, int6
                             size_t ws_bytes, hipStream_t s);
 hipError_t launch_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_invert(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s);
+hipError_t permutation_plan_workspace(int64_t n, size_t* bytes);
+hipError_t launch_permutation_plan(const int32_t* q, int64_t n, int wbits, int32_t* q1, int32_t* pos, void* ws,
+                                   size_t ws_bytes, hipStream_t s);
+hipError_t launch_permute(const int32_t* q1, const int32_t* pos, const float* src, float* tmp, float* dst, int64_t n,
+                          hipStream_t s);
 // the COO row array: rows[e] = the row holding entry e
 hipError_t launch_coo_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows, int64_t nnz, hipStream_t s);
 

@@ -453,6 +453,28 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
  * for n < 0 or n >= 2^31. */
 int csr_inverse_permutation(csr_context_t ctx, int64_t n, const int32_t* perm, int32_t* inv, void* stream);
 
+/* A permutation of per-entry values in two passes: dst[e] = src[q[e]] for a
+ * permutation q of [0, n) (q = t_perm moves values of A into A^T's order,
+ * its inverse moves them back).  A direct gather reads a 4-byte value from a
+ * random 128-byte line per entry; the plan groups the outputs by the window
+ * of 2^window_log2 source values they read, so that the first pass reads one
+ * window at a time (from the L2 of the XCD that holds it) and the second
+ * reads the groups in contiguous runs.  The plan is two caller-allocated
+ * int32 [n] device arrays q1 and pos (q1[j] = q[order[j]], pos[order[j]] = j
+ * for the outputs in window order), built once per permutation by
+ * csr_permutation_plan with workspace of csr_permutation_plan_workspace_size
+ * bytes; q must be a permutation (not checked; an index outside [0, n)
+ * makes the plan's results unspecified, never an access outside the
+ * arrays).  window_log2 in [8, 30]; CSR_ERR_SHAPE otherwise or for n < 0 or
+ * n >= 2^31.  csr_permute_values applies a plan: tmp[j] = src[q1[j]], then
+ * dst[e] = tmp[pos[e]] (fp32; tmp [n] is caller scratch; src, tmp and dst
+ * must not alias: CSR_ERR_SHAPE when two are the same array). */
+int csr_permutation_plan_workspace_size(csr_context_t ctx, int64_t n, size_t* bytes);
+int csr_permutation_plan(csr_context_t ctx, int64_t n, const int32_t* q, int32_t window_log2, int32_t* q1,
+                         int32_t* pos, void* workspace, size_t ws_bytes, void* stream);
+int csr_permute_values(csr_context_t ctx, int64_t n, const int32_t* q1, const int32_t* pos, const float* src,
+                       float* tmp, float* dst, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Column-part segment format (a composed, "hybrid" format)
  *

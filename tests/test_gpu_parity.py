@@ -1320,3 +1320,69 @@ def test_validating_context_row_softmax_ops():
         csa.row_softmax(bad, sc, scale=0.5, ctx=vctx)
     assert "CSR_ERR_INVALID_CSR" in str(ei.value)
     vctx.close()
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "short", "edges", "empty"])
+@pytest.mark.parametrize("window_log2", [8, 12, 30])
+def test_permutation_plan_bit_exact(graph, window_log2):
+    """Two-pass permutations of a transposed pattern's perm and its inverse
+    move per-entry values exactly as the direct gathers do, for windows from
+    256 values (many groups) to 2^30 (one group)."""
+    if graph == "empty":
+        csr = CSR(5, 7, np.zeros(6, np.int32), np.zeros(0, np.int32))
+    else:
+        csr = _graphs_for_backward()[graph]
+    rp, ci = pattern_dev(csr)
+    t = csa.transpose(rp, ci, csr.n_cols, inverse=True)
+    vals = dev(np.random.default_rng(670).standard_normal(csr.nnz).astype(np.float32))
+    for q in (t.perm, t.inv):
+        plan = csa.permutation_plan(q, window_log2=window_log2)
+        got = csa.permute_values(plan, vals)
+        want = vals.cpu().numpy()[q.cpu().numpy().astype(np.int64)]
+        assert np.array_equal(got.cpu().numpy(), want)
+        # the plan's arrays: q1 is q in window order, pos its inverse placement
+        q1, pos = plan.q1.cpu().numpy(), plan.pos.cpu().numpy()
+        assert np.array_equal(np.sort(pos), np.arange(csr.nnz))
+        assert np.array_equal(q1[pos], q.cpu().numpy())
+        win = q1.astype(np.int64) >> window_log2
+        assert np.all(np.diff(win) >= 0)
+
+
+def test_permutation_plan_errors():
+    q = torch.arange(1000, dtype=torch.int32, device="cuda")
+    with pytest.raises(csa.CsrError):
+        csa.permutation_plan(q, window_log2=7)
+    with pytest.raises(csa.CsrError):
+        csa.permutation_plan(q, window_log2=31)
+    plan = csa.permutation_plan(q)
+    x = torch.ones(1000, device="cuda")
+    with pytest.raises(csa.CsrError):
+        csa.permute_values(plan, x, out=x)  # src and dst alias
+    with pytest.raises(ValueError):
+        csa.permute_values(plan, torch.ones(999, device="cuda"))
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+def test_attention_backward_through_plans(graph):
+    """attention_backward over a transposed pattern with permutation plans
+    (P into A^T's order and dP back in two passes) against the oracle, and
+    equal to the index-based composition."""
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(671)
+    F = 32
+    sc = (2 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    tp = csa.transpose(rp, ci, csr.n_cols, plans=True)
+    ti = csa.transpose(rp, ci, csr.n_cols, inverse=True)
+    dS, dV = csa.attention_backward(rp, ci, dev(sc), dev(V), dev(dO), scale=0.5, transposed=tp)
+    dS2, dV2 = csa.attention_backward(rp, ci, dev(sc), dev(V), dev(dO), scale=0.5, transposed=ti)
+    assert torch.equal(dS, dS2) and torch.equal(dV, dV2)
+    ref, mag = oracle.attention_backward_scores(csr.row_ptr, csr.col_idx, sc, V, dO, 0.5,
+                                                threads=oracle.default_threads())
+    assert_close(dS.cpu().numpy(), ref, mag, TOL_F32, "d scores")
+    P = oracle.attention(csr.row_ptr, csr.col_idx, sc, np.zeros((csr.n_cols, 1), np.float32), 0.5,
+                         want_probs=True)[2]
+    refV, magV = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P, dO, csr.n_cols)
+    assert_close(dV.cpu().numpy(), refV, magV, TOL_F32, "dV")
