@@ -231,10 +231,10 @@ def test_attention_errors():
     out = torch.empty((n, 16), device="cuda")
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    sc = dev(np.zeros(csr.nnz, np.float32))
-    # given scores serve one head
+    sc = dev(np.zeros((2, csr.nnz), np.float32))  # given scores of 2 heads, head-major
+    # several heads of given scores: a leading dimension of V below heads * head_dim is a shape error
     assert lib.csr_attention(ctx.handle, n, n, csr.nnz, rp.data_ptr(), ci.data_ptr(), sc.data_ptr(), None, None,
-                             Q.data_ptr(), 0, 2, 8, 16, 1.0, out.data_ptr(), 16, None, None, ws.data_ptr(),
+                             Q.data_ptr(), 0, 2, 8, 8, 1.0, out.data_ptr(), 16, None, None, ws.data_ptr(),
                              ws.numel(), st) == -2
     # no queries
     assert lib.csr_attention(ctx.handle, n, n, csr.nnz, rp.data_ptr(), ci.data_ptr(), None, None, Q.data_ptr(),
