@@ -517,3 +517,86 @@ def test_value_index_rules():
     idx = problem(_ffi.OP_SPMM, width=32)
     idx.a_idx = 0x2000
     assert csa.signature(plain, hist) != csa.signature(idx, hist)
+
+
+def _dual(width=64, ld=None, ptr=0x1000):
+    p = problem(_ffi.OP_SPMM_SDDMM, width=width, ld=ld, ptr=ptr)
+    p.ld_c = width if ld is None else ld
+    p.out2 = ptr
+    return p
+
+
+def test_spmm_sddmm_problem_rules():
+    """The SpMM + SDDMM problem: fp32 only, U's leading dimension checked like
+    X's, the per-entry output (and its index) only for this op and 4-byte
+    aligned, schedules on the row-group and merge-path mappings only, the
+    SpMM's workspace, and an output index that changes the signature."""
+    lib = csa.load_library()
+    n = ctypes.c_size_t()
+
+    def ws(p, s=None):
+        return lib.csr_workspace_size(None, ctypes.byref(p), None if s is None else ctypes.byref(s), ctypes.byref(n))
+
+    p = _dual()
+    assert ws(p) == 0
+    d = csa.default_schedule(p)
+    assert d.mapping == _ffi.MAP_MERGEPATH and (d.vec, d.group_lanes, d.passes) == (4, 16, 1)
+    assert ws(p, d) == 0
+    dual_bytes = n.value
+    sd = csa.CsrSchedule.from_buffer_copy(bytes(d))
+    sd.op = _ffi.OP_SPMM
+    assert ws(problem(_ffi.OP_SPMM, width=64), sd) == 0 and n.value == dual_bytes  # the SpMM's carry
+    hist = [0] * 33 + [0] * 33 + [100]
+    cands = csa.candidates(p, hist)
+    assert {c.mapping for c in cands} == {_ffi.MAP_ROWGROUP, _ffi.MAP_MERGEPATH}
+    assert all(c.flags == 0 for c in cands)
+    for c in cands:
+        assert ws(p, c) == 0
+    seg = csa.CsrSchedule.from_buffer_copy(bytes(d))
+    seg.mapping, seg.group_lanes, seg.passes, seg.long_row, seg.chunk_items = _ffi.MAP_SEGSCAN, 1, 16, 0, 512
+    assert ws(p, seg) == -7  # CSR_ERR_SCHEDULE
+    bf = _dual()
+    bf.dtype = _ffi.DTYPE_BF16
+    assert ws(bf) == -3
+    short_u = _dual()
+    short_u.ld_c = 32
+    assert ws(short_u) == -2
+    for op in (_ffi.OP_SPMM, _ffi.OP_SDDMM, _ffi.OP_ATTENTION):
+        q = problem(op, width=32)
+        q.out2 = 0x2000
+        assert ws(q) == -2, op
+    mis = _dual()
+    mis.out2_idx = 0x2002
+    assert ws(mis) == -4
+    h = [0] * 66 + [10]
+    plain, idx = _dual(), _dual()
+    idx.out2_idx = 0x2000
+    assert csa.signature(plain, h) != csa.signature(idx, h)
+
+
+def test_backward_calls_check_arguments_on_the_host():
+    """csr_spmm_sddmm, csr_inverse_permutation and the permutation plans:
+    argument errors before any device work, and a host-only context refuses
+    the device calls."""
+    lib = csa.load_library()
+    ctx = csa.Context(-1, None)
+    h = ctx.handle
+    P = 0x100000
+    # (a missing per-entry output is CSR_ERR_NULL on a device context; the GPU tests check it)
+    assert lib.csr_spmm_sddmm(h, 4, 4, 8, P, P, P, None, P, 16, 16, P, 16, P, 16, P, None, None, P, 1 << 20,
+                              None) == -11
+    assert lib.csr_inverse_permutation(h, -1, P, P + 64, None) == -2
+    assert lib.csr_inverse_permutation(h, 8, P, P, None) == -2  # perm and inv alias
+    assert lib.csr_inverse_permutation(h, 8, P, None, None) == -1
+    assert lib.csr_inverse_permutation(h, 8, P, P + 64, None) == -11
+    n = ctypes.c_size_t()
+    assert lib.csr_permutation_plan_workspace_size(h, 1 << 31, ctypes.byref(n)) == -2
+    assert lib.csr_permutation_plan_workspace_size(h, 100, ctypes.byref(n)) == -11
+    for w in (7, 31):
+        assert lib.csr_permutation_plan(h, 100, P, w, P + 512, P + 1024, P + 2048, 1 << 20, None) == -2
+    assert lib.csr_permutation_plan(h, 100, P, 20, P, P + 1024, P + 2048, 1 << 20, None) == -2  # q and q1 alias
+    assert lib.csr_permutation_plan(h, 100, P, 20, P + 512, P + 1024, P + 2048, 1 << 20, None) == -11
+    assert lib.csr_permute_values(h, 100, P, P + 512, P + 1024, P + 1024, P + 2048, None) == -2  # src and tmp alias
+    assert lib.csr_permute_values(h, 100, P, P + 512, P + 1026, P + 1536, P + 2048, None) == -4  # misaligned
+    assert lib.csr_permute_values(h, 100, P, P + 512, P + 1024, P + 1536, P + 2048, None) == -11
+    ctx.close()
