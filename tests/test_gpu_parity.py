@@ -1386,3 +1386,61 @@ def test_attention_backward_through_plans(graph):
                          want_probs=True)[2]
     refV, magV = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P, dO, csr.n_cols)
     assert_close(dV.cpu().numpy(), refV, magV, TOL_F32, "dV")
+
+
+def test_graph_capture_backward_step():
+    """The attention backward step as library calls with explicit schedules
+    (row softmax, P into A^T's order, the SpMM + SDDMM pass over A^T, dP back,
+    softmax backward in place) captured into one graph: every replay, with
+    eager work between the replays, equals the eager step bit for bit, and
+    the gradients match the oracle."""
+    csr = skew_graph(13, n_rows=1500, n_cols=20000, giant=8000)
+    rng = np.random.default_rng(680)
+    F, scale = 32, 0.5
+    sc = (2 * rng.standard_normal(csr.nnz)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    rp, ci = pattern_dev(csr)
+    S, Vd, dOd = dev(sc), dev(V), dev(dO)
+    t = csa.transpose(rp, ci, csr.n_cols, plans=True)
+    e = lambda: torch.empty(csr.nnz, device="cuda")  # noqa: E731
+    P, Pt, dPt, dP, tmp = e(), e(), e(), e(), e()
+    dV = torch.empty((csr.n_cols, F), device="cuda")
+    s_sm, _ = csa.select("row_softmax", rp, None, S, scale=scale, out=P)
+    csa.row_softmax(rp, S, scale=scale, out=P, schedule=s_sm)
+    csa.permute_values(t.to_t, P, out=Pt, tmp=tmp)
+    s_d, _ = csa.select("spmm_sddmm", t.row_ptr, t.col_idx, Pt, dOd, Vd, out=dV)
+    s_b, _ = csa.select("row_softmax_backward", rp, None, P, dP, scale=scale, out=dP)
+
+    def step():
+        csa.row_softmax(rp, S, scale=scale, out=P, schedule=s_sm)
+        csa.permute_values(t.to_t, P, out=Pt, tmp=tmp)
+        csa.spmm_sddmm(t.row_ptr, t.col_idx, Pt, dOd, Vd, out=dV, z=dPt, schedule=s_d)
+        csa.permute_values(t.from_t, dPt, out=dP, tmp=tmp)
+        csa.row_softmax_backward(rp, P, dP, scale=scale, out=dP, schedule=s_b)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on a side stream, as graph capture requires
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = (dP.clone(), dV.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        dP.fill_(float("nan"))
+        dV.fill_(float("nan"))
+        csa.spmm(rp, ci, None, Vd * (r + 2))  # eager work between the replays (V has the pattern's n_cols rows)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dP, eager[0]) and torch.equal(dV, eager[1]), r
+    ref, mag = oracle.attention_backward_scores(csr.row_ptr, csr.col_idx, sc, V, dO, scale,
+                                                threads=oracle.default_threads())
+    assert_close(dP.cpu().numpy(), ref, mag, TOL_F32, "graph d scores")
+    Pref = oracle.attention(csr.row_ptr, csr.col_idx, sc, np.zeros((csr.n_cols, 1), np.float32), scale,
+                            want_probs=True)[2]
+    refV, magV = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, Pref, dO, csr.n_cols)
+    assert_close(dV.cpu().numpy(), refV, magV, TOL_F32, "graph dV")
