@@ -281,6 +281,56 @@ def build_workload(name, torch, csa):
         else:
             calls.append(Call("attention_F64", "attention", csa.attention, (rp, ci, S, Vd),
                               {"out": Y, "scale": 0.125}, csr.n_rows, csr.nnz, 64, None))
+    elif name == "c3qkbwd":
+        # backward of the one-head fp32 attention from Q, K, V (width 64) on
+        # the c3 graph: scores s = SDDMM(Q, K), P = row softmax, P into A^T's
+        # order, dV and dP in one pass over A^T, dP back, d s = softmax
+        # backward (in place), dQ = A_ds K, d s into A^T's order, dK =
+        # A_ds^T Q.  The transposed pattern and its permutation plans are
+        # built once, outside the step.
+        csr = configs.config_pattern("c3")
+        rp, ci = d(csr.row_ptr), d(csr.col_idx)
+        Q = d(configs.config_dense("c3", "U", csr, 64))
+        K = d(configs.config_dense("c3", "V", csr, 64))
+        Vd = d(configs.config_dense("c3", "X", csr, 64))
+        dO = d(configs.config_dense("c3", "U", csr, 65)[:, :64])
+        torch.cuda.synchronize()
+        tt = time.perf_counter()
+        At = csa.transpose(rp, ci, csr.n_cols, plans=True)
+        torch.cuda.synchronize()
+        build_workload.transpose_first_ms = (time.perf_counter() - tt) * 1e3
+        # again with the buffers already in torch's pool: the build's own time
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        del At
+        ev0.record()
+        At = csa.transpose(rp, ci, csr.n_cols, plans=True)
+        ev1.record()
+        ev1.synchronize()
+        build_workload.transpose_ms = ev0.elapsed_time(ev1)
+        e = lambda: torch.empty(csr.nnz, dtype=torch.float32, device="cuda")  # noqa: E731
+        S, P, Pt, dPt, dP, tmp = e(), e(), e(), e(), e(), e()
+        dV = torch.empty((csr.n_cols, 64), dtype=torch.float32, device="cuda")
+        dQ = torch.empty((csr.n_rows, 64), dtype=torch.float32, device="cuda")
+        dK = torch.empty((csr.n_cols, 64), dtype=torch.float32, device="cuda")
+
+        def permute(plan, src, out, schedule=None):
+            return csa.permute_values(plan, src, out=out, tmp=tmp)
+
+        calls.append(Call("sddmm_S", "sddmm", csa.sddmm, (rp, ci, Q, K), {"out": S}, csr.n_rows, csr.nnz, 64, None))
+        calls.append(Call("row_softmax", "row_softmax", csa.row_softmax, (rp, S), {"out": P, "scale": 0.125},
+                          csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("permute_Pt", "permute", permute, (At.to_t, P, Pt), {}, csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("spmm_sddmm_dV_dP", "spmm_sddmm", csa.spmm_sddmm, (At.row_ptr, At.col_idx, Pt, dO, Vd),
+                          {"out": dV, "z": dPt}, csr.n_cols, csr.nnz, 64, None))
+        calls.append(Call("permute_dP", "permute", permute, (At.from_t, dPt, dP), {}, csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("softmax_bwd", "row_softmax_backward", csa.row_softmax_backward, (rp, P, dP),
+                          {"out": dP, "scale": 0.125}, csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("spmm_dQ", "spmm", csa.spmm, (rp, ci, dP, K), {"out": dQ}, csr.n_rows, csr.nnz, 64, None))
+        calls[-1].step_values = True
+        calls.append(Call("permute_dSt", "permute", permute, (At.to_t, dP, dPt), {}, csr.n_rows, csr.nnz, 1, None))
+        calls.append(Call("spmm_dK", "spmm", csa.spmm, (At.row_ptr, At.col_idx, dPt, Q), {"out": dK}, csr.n_cols,
+                          csr.nnz, 64, None))
+        calls[-1].step_values = True
     elif name in ("c3bwd", "c3bwd_perm", "c3bwd_gather"):
         # backward of the single-head fp32 attention on the c3 graph (scores
         # given, F = 64): P = row softmax; dV = P^T dOut and dP = dOut V^T;
@@ -798,7 +848,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2",
                     help="c2 (default), c1, p4, c3, c4, c5a, c5b, c3pipe, c3fused, c3qk, c3bf16, c3bwd, "
-                         "c3bwd_perm, c3bwd_gather, c3sweep")
+                         "c3bwd_perm, c3bwd_gather, c3qkbwd, c3sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds per pass of the CPU oracle sample")
     ap.add_argument("--no-study", action="store_true", help="skip the selector-vs-fixed-mapping study")
@@ -955,6 +1005,10 @@ def main():
                                           "log-normal graph 2,449,029 rows ~123.7M nnz",
                                 "c3sweep": "CSR SpMM on the log-normal graph at F in {128,256,384,512}: "
                                            "gathered operand of 1.25 to 5.0 GB",
+                                "c3qkbwd": "backward of single-head fp32 attention from Q, K, V (width 64) on "
+                                           "the log-normal graph: SDDMM scores, row softmax, P into A^T's order, "
+                                           "dV and dP in one pass over A^T, dP back, softmax backward, dQ (SpMM), "
+                                           "d scores into A^T's order, dK (SpMM on A^T)",
                                 "c3bwd": "backward of single-head fp32 attention on the log-normal graph, F=64: "
                                          "row softmax, P into A^T's order (two-pass permutation), dV = P^T dOut "
                                          "and dP = dOut V^T in one pass over A^T, dP back into A's order, "

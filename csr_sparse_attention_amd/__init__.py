@@ -38,6 +38,7 @@ from .ops import (  # noqa: E402,F401
     Transposed,
     attention,
     attention_backward,
+    attention_qk_backward,
     attention_pipeline,
     attention_qk,
     candidates,

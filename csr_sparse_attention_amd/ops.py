@@ -9,6 +9,7 @@ libcsrsa.so; there is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import threading
 from typing import NamedTuple, Optional
@@ -882,6 +883,36 @@ def attention_backward(row_ptr, col_idx, edge_scores, node_value, d_out, *, scal
     dP = sddmm(row_ptr, col_idx, d_out, node_value, ctx=ctx)
     dS = row_softmax_backward(row_ptr, P, dP, scale=scale, out=dP, ctx=ctx)
     return dS, dV
+
+
+def attention_qk_backward(row_ptr, col_idx, Q, K, V, d_out, *, scale: Optional[float] = None,
+                          transposed: Optional[Transposed] = None, ctx: Optional[Context] = None):
+    """Gradients of the one-head fp32 attention from queries and keys,
+    out_i = sum over e of p_e V[col_e] with p the row softmax of
+    scale * <Q_i, K[col_e]> (scale 1/sqrt(D) unless given): returns (dQ, dK,
+    dV).  The raw scores s_e = <Q_i, K[col_e]> are recomputed by an SDDMM;
+    dV and d s come from attention_backward (both products that read d_out in
+    one pass over A^T); dQ = dS K (SpMM on A) and dK = dS^T Q (SpMM on A^T
+    over dS moved into A^T's order).  ``transposed`` is built with
+    permutation plans unless given."""
+    n_rows, nnz = _pattern(row_ptr, col_idx)
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("d_out", d_out)):
+        if t.dim() != 2 or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be 2-D float32 (one head)")
+    if Q.shape[0] != n_rows or d_out.shape[0] != n_rows or K.shape[0] != V.shape[0] or K.shape[1] != Q.shape[1] \
+            or d_out.shape[1] != V.shape[1]:
+        raise ValueError("Q, d_out: [n_rows, ...]; K, V: [n_cols, ...]; K as wide as Q, d_out as wide as V")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Q.shape[1])
+    At = transposed or transpose(row_ptr, col_idx, K.shape[0], plans=True, ctx=ctx)
+    S = sddmm(row_ptr, col_idx, Q, K, ctx=ctx)
+    dS, dV = attention_backward(row_ptr, col_idx, S, V, d_out, scale=scale, transposed=At, ctx=ctx)
+    dQ = spmm(row_ptr, col_idx, dS, K, ctx=ctx)
+    if At.to_t is not None:
+        dK = spmm(At.row_ptr, At.col_idx, permute_values(At.to_t, dS, out=S, ctx=ctx), Q, ctx=ctx)
+    else:
+        dK = spmm(At.row_ptr, At.col_idx, dS, Q, val_idx=At.perm, ctx=ctx)
+    return dQ, dK, dV
 
 
 # ---------------------------------------------------------------------------

@@ -1444,3 +1444,37 @@ def test_graph_capture_backward_step():
                             want_probs=True)[2]
     refV, magV = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, Pref, dO, csr.n_cols)
     assert_close(dV.cpu().numpy(), refV, magV, TOL_F32, "graph dV")
+
+
+@pytest.mark.parametrize("graph", ["skew", "dup", "edges"])
+@pytest.mark.parametrize("D,F", [(32, 32), (16, 24)])
+def test_attention_qk_backward(graph, D, F):
+    """dQ, dK, dV of the attention from queries and keys (one head, fp32)
+    against the oracle's composition (SDDMM scores, the scores-given
+    backward, dQ = A_ds K, dK = A_ds^T Q), with error magnitudes carried
+    through the same products."""
+    csr = _graphs_for_backward()[graph]
+    rng = np.random.default_rng(690 + D)
+    Q = rng.standard_normal((csr.n_rows, D)).astype(np.float32)
+    K = rng.standard_normal((csr.n_cols, D)).astype(np.float32)
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+    scale = 0.3
+    rp, ci = pattern_dev(csr)
+    dQ, dK, dV = csa.attention_qk_backward(rp, ci, dev(Q), dev(K), dev(V), dev(dO), scale=scale)
+    th = oracle.default_threads()
+    s, _ = oracle.sddmm(csr.row_ptr, csr.col_idx, Q, K, threads=th)
+    ds, mag_ds = oracle.attention_backward_scores(csr.row_ptr, csr.col_idx, s.astype(np.float32), V, dO, scale,
+                                                  threads=th)
+    refQ, _ = oracle.spmm(csr.row_ptr, csr.col_idx, ds, K, threads=th)
+    magQ, _ = oracle.spmm(csr.row_ptr, csr.col_idx, mag_ds, np.abs(K), threads=th)
+    assert_close(dQ.cpu().numpy(), refQ, magQ, TOL_F32, "dQ")
+    refK, _ = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, ds, Q, csr.n_cols)
+    magK, _ = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, mag_ds, np.abs(Q), csr.n_cols)
+    assert_close(dK.cpu().numpy(), refK, magK, TOL_F32, "dK")
+    P = oracle.attention(csr.row_ptr, csr.col_idx, s.astype(np.float32), np.zeros((csr.n_cols, 1), np.float32),
+                         scale, want_probs=True, threads=th)[2]
+    refV, magV = oracle.spmm_transpose(csr.row_ptr, csr.col_idx, P, dO, csr.n_cols)
+    assert_close(dV.cpu().numpy(), refV, magV, TOL_F32, "dV")
+    with pytest.raises(ValueError):
+        csa.attention_qk_backward(rp, ci, dev(Q), dev(K), dev(V), dev(dO[:-1]))

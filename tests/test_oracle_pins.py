@@ -718,3 +718,40 @@ def test_gpu_error_measure_fails_on_nan():
     with pytest.raises(AssertionError):
         gpu_util.max_err(np.array([np.nan]), np.array([0.0]), np.array([0.0]))  # zero magnitude must be exactly 0
     assert gpu_util.max_err(ref, ref, mag) == 0.0
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_qk_backward_composition_finite_differences(oracle_lib, seed):
+    """The gradients of the attention from queries and keys as the library
+    composes them, written with oracle functions: s = SDDMM(Q, K), d s from
+    the scores-given backward, dQ = A_ds K and dK = A_ds^T Q; against
+    central differences of the oracle's forward in every entry of Q and K."""
+    rng = np.random.default_rng(740 + seed)
+    csr = random_small_graph(7, 8, 0.45, rng, empty_frac=0.15, allow_dup=seed == 2)
+    D, F, scale = 3, 3, [0.5, 1.0, 0.25][seed]
+    grid = lambda shape: (np.round(rng.uniform(-1.5, 1.5, shape) * 256) / 256).astype(np.float32)  # noqa: E731
+    Q, K = grid((csr.n_rows, D)), grid((csr.n_cols, D))
+    V = rng.standard_normal((csr.n_cols, F)).astype(np.float32)
+    dO = rng.standard_normal((csr.n_rows, F)).astype(np.float32)
+
+    def loss(q, k):
+        out = oracle_lib.attention_qk(csr.row_ptr, csr.col_idx, q, k, V, scale)[0]
+        return float(np.sum(dO.astype(np.float64) * out[:, 0, :]))
+
+    s, _ = oracle_lib.sddmm(csr.row_ptr, csr.col_idx, Q, K)
+    ds, mag_ds = oracle_lib.attention_backward_scores(csr.row_ptr, csr.col_idx, s.astype(np.float32), V, dO, scale)
+    dQ, _ = oracle_lib.spmm(csr.row_ptr, csr.col_idx, ds, K)
+    magQ, _ = oracle_lib.spmm(csr.row_ptr, csr.col_idx, mag_ds, np.abs(K))
+    dK, _ = oracle_lib.spmm_transpose(csr.row_ptr, csr.col_idx, ds, Q, csr.n_cols)
+    magK, _ = oracle_lib.spmm_transpose(csr.row_ptr, csr.col_idx, mag_ds, np.abs(Q), csr.n_cols)
+    h = 2.0 ** -10
+    for M, G, mag, which in ((Q, dQ, magQ, 0), (K, dK, magK, 1)):
+        fd = np.empty(M.shape)
+        for idx in np.ndindex(M.shape):
+            mp, mm = M.copy(), M.copy()
+            mp[idx] += np.float32(h)
+            mm[idx] -= np.float32(h)
+            lp = loss(mp, K) if which == 0 else loss(Q, mp)
+            lm = loss(mm, K) if which == 0 else loss(Q, mm)
+            fd[idx] = (lp - lm) / (2 * h)
+        assert rel_err(G, fd, mag + 1e-30) < 1e-4, which
