@@ -1170,6 +1170,8 @@ int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const f
     if (n < 0 || n >= ((int64_t)1 << 31)) return set_err(ctx, CSR_ERR_SHAPE, "bad size");
     if (n > 0 && (!perm || !src || !dst)) return CSR_ERR_NULL;
     if (n > 0 && src == dst) return set_err(ctx, CSR_ERR_SHAPE, "src and dst must not alias");
+    if (((uintptr_t)perm | (uintptr_t)src | (uintptr_t)dst) % 4)
+        return set_err(ctx, CSR_ERR_ALIGN, "the arrays must be 4-byte aligned");
     if (ctx->device < 0) return set_err(ctx, CSR_ERR_DEVICE, "host-only context");
     DeviceGuard g(ctx->device);
     CSR_HIP(ctx, csrk::launch_gather_values(perm, src, dst, n, static_cast<hipStream_t>(stream)));

@@ -265,10 +265,14 @@ hipError_t launch_invert(const int32_t* perm, int32_t* inv, int64_t n, hipStream
     return hipGetLastError();
 }
 
+// the single pass of a permutation's kernel: 4 entries per thread, XCD-major,
+// an index outside [0, n) gives 0
 hipError_t launch_gather_values(const int32_t* perm, const float* src, float* dst, int64_t n, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gather<float>, dim3(full_grid(n)), dim3(CSR_BLOCK), 0, s, perm, src, dst, n);
+    const int64_t per = xcd_ranges(n);
+    hipLaunchKernelGGL(k_permute_pass, dim3((unsigned)(per * CSR_XCDS)), dim3(CSR_BLOCK), 0, s, perm, src, dst, n,
+                       per);
     return hipGetLastError();
 }
 

@@ -440,9 +440,10 @@ int csr_transpose(csr_context_t ctx, int64_t n_rows, int64_t n_cols, int64_t nnz
                   const int32_t* col_idx, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm,
                   void* workspace, size_t ws_bytes, void* stream);
 
-/* dst[k] = src[perm[k]] for k < n (fp32; dst must not alias src): moves
- * per-entry values (edge values, probabilities, gradients) into the order of
- * a transposed pattern. */
+/* dst[k] = src[perm[k]] for k < n (fp32, src and dst of n values; dst must
+ * not alias src; an index outside [0, n) gives 0): moves per-entry values
+ * (edge values, probabilities, gradients) into the order of a transposed
+ * pattern. */
 int csr_gather_values(csr_context_t ctx, int64_t n, const int32_t* perm, const float* src, float* dst, void* stream);
 
 /* inv[perm[k]] = k for k < n: the inverse of a permutation of [0, n) (for a
