@@ -654,22 +654,18 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_rowgroup_wide(Fp32Args a)
             float w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = (i + u < n) ? i + u : 0;
-                const char* xr = row_at(xb, __builtin_amdgcn_readlane(cl, k), row_bytes);
-                w[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+                if (!tail || i + u < n) {
+                    const char* xr = row_at(xb, __builtin_amdgcn_readlane(cl, i + u), row_bytes);
+                    w[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
 #pragma unroll
-                for (int j = 0; j < NV; ++j) xv[u][j] = *reinterpret_cast<const float4_a4*>(xr + lo[j]);
-            }
-            if (tail) {
-                // padded entries (the same for the whole wave) add exact zeros:
-                // weighting their row by 0 would turn an infinite feature into NaN
+                    for (int j = 0; j < NV; ++j) xv[u][j] = *reinterpret_cast<const float4_a4*>(xr + lo[j]);
+                } else {
+                    // padding past the batch's entries (the same for the whole
+                    // wave, so no load is issued for it) adds exact zeros
+                    w[u] = 0.f;
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (i + u >= n) {
-                        w[u] = 0.f;
-#pragma unroll
-                        for (int j = 0; j < NV; ++j) xv[u][j] = float4_a4{0.f, 0.f, 0.f, 0.f};
-                    }
+                    for (int j = 0; j < NV; ++j) xv[u][j] = float4_a4{0.f, 0.f, 0.f, 0.f};
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
