@@ -760,16 +760,25 @@ def vendor_compare(calls, torch, reps=5):
 
 
 def cpu_model():
+    """The host CPU's model name, with its family / model / stepping numbers
+    (virtual machines often report a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block
+                k, _, v = line.partition(":")
+                fields.setdefault(k.strip(), v.strip())
     except OSError:  # pragma: no cover
         pass
-    import platform
+    name = fields.get("model name")
+    if not name:
+        import platform
 
-    return platform.processor() or "unknown"
+        return platform.processor() or "unknown"
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(calls, target_s=8.0, runs=3):

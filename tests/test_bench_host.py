@@ -56,3 +56,15 @@ def test_committed_traffic_records_are_self_consistent():
             for src in r["sources"]:
                 assert os.path.exists(os.path.join(root, src)), src
             assert os.path.exists(os.path.join(root, r["profile"]))
+
+
+def test_cpu_model_names_the_host():
+    """The CPU baseline's model string: /proc/cpuinfo's model name of the
+    first processor, with its family / model / stepping numbers."""
+    name = bench.cpu_model()
+    assert isinstance(name, str) and name
+    if os.path.exists("/proc/cpuinfo"):
+        with open("/proc/cpuinfo") as f:
+            first = [l.split(":", 1)[1].strip() for l in f if l.startswith("model name")][:1]
+        if first:
+            assert name.startswith(first[0]) and "cpu family" in name
