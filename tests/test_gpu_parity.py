@@ -499,6 +499,45 @@ def test_validation_flag_rejects_bad_columns():
     ctx.close()
 
 
+@pytest.mark.parametrize("corrupt", ["start", "end", "order"])
+def test_validation_flag_rejects_bad_row_ptr(corrupt):
+    """A validating context rejects a row_ptr that breaks the CSR invariants
+    (row_ptr[0] = 0, row_ptr[n_rows] = nnz, non-decreasing) before any
+    product kernel runs, for SpMM, SDDMM, attention and the row softmax; the
+    same context then runs the intact pattern."""
+    rng = np.random.default_rng(17)
+    csr = graphs.random_small_graph(200, 300, 0.05, rng)
+    bad = csr.row_ptr.copy()
+    if corrupt == "start":
+        bad[0] = 1
+    elif corrupt == "end":
+        bad[-1] = csr.nnz - 1
+    else:
+        i = int(np.argmax(np.diff(bad) > 0)) + 1  # a row boundary inside the array with a non-empty row before it
+        bad[i] = bad[i - 1] - 1 if bad[i - 1] > 0 else bad[i + 1] + 1
+        assert (np.diff(bad) < 0).any()
+    assert 0 <= bad.min() and bad.max() <= csr.nnz  # every value stays inside the entry arrays
+    rp_bad, rp, ci = dev(bad), dev(csr.row_ptr), dev(csr.col_idx)
+    X = dev(rng.standard_normal((300, 8)).astype(np.float32))
+    U = dev(rng.standard_normal((200, 8)).astype(np.float32))
+    sc = dev(rng.standard_normal(csr.nnz).astype(np.float32))
+    ctx = csa.Context(0, None, flags=csa.CTX_VALIDATE)
+    try:
+        for call in (lambda r: csa.spmm(r, ci, None, X, ctx=ctx),
+                     lambda r: csa.sddmm(r, ci, U, X, ctx=ctx),
+                     lambda r: csa.attention(r, ci, sc, X, ctx=ctx),
+                     lambda r: csa.row_softmax(r, sc, ctx=ctx)):
+            with pytest.raises(csa.CsrError) as ei:
+                call(rp_bad)
+            assert ei.value.code == -6, corrupt
+            call(rp)  # the intact pattern passes the same checks
+        Y = csa.spmm(rp, ci, None, X, ctx=ctx)
+        ref, mag = oracle.spmm(csr.row_ptr, csr.col_idx, None, X.cpu().numpy())
+        assert_close(Y.cpu().numpy(), ref, mag)
+    finally:
+        ctx.close()
+
+
 # ---------------------------------------------------------------------------
 # unfused pipeline: row softmax and SDDMM -> row-softmax -> SpMM
 # ---------------------------------------------------------------------------
