@@ -129,6 +129,9 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_main(SoftmaxArgs a)
 // chunk.  Only row_ptr and the per-row statistics go through LDS.  Every lane
 // then reads the statistics of its rows and writes its p_e.
 // ---------------------------------------------------------------------------
+// 4 floats at a 4-byte aligned address: one 16-byte access
+typedef float sm_f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+
 template <int D>
 struct SmRunShared {
     // chunk row_ptr, then the rows' maxima (float bits); 64 trailing slots take
@@ -208,14 +211,35 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     float t[RMAX];
     float g[BWD ? RMAX : 1];
     // the run's scores, straight from HBM (the wave's loads cover whole lines
-    // between them); read once, so non-temporal
+    // between them); read once, so non-temporal.  Four entries per access
+    // where the run holds them (a lane's run is only 4-byte aligned): an
+    // access costs the address unit about the same whether it moves 4 or 16
+    // bytes per lane, and the lanes' runs are R entries apart.
     const float* srun = a.scores + lo + k0;
     const float* grun = BWD ? a.grad + lo + k0 : nullptr;
 #pragma unroll
-    for (int k = 0; k < RMAX; ++k) {
+    for (int k = 0; k < RMAX; k += 4) {
         if (k >= R) break;
-        t[k] = (k < kn) ? __builtin_nontemporal_load(srun + k) : 0.f;
-        if constexpr (BWD) g[k] = (k < kn) ? __builtin_nontemporal_load(grun + k) : 0.f;
+        if (k + 4 <= kn) {
+            const sm_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const sm_f32x4*>(srun + k));
+            t[k] = v.x;
+            t[k + 1] = v.y;
+            t[k + 2] = v.z;
+            t[k + 3] = v.w;
+            if constexpr (BWD) {
+                const sm_f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const sm_f32x4*>(grun + k));
+                g[k] = w.x;
+                g[k + 1] = w.y;
+                g[k + 2] = w.z;
+                g[k + 3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                t[k + u] = (k + u < kn) ? __builtin_nontemporal_load(srun + k + u) : 0.f;
+                if constexpr (BWD) g[k + u] = (k + u < kn) ? __builtin_nontemporal_load(grun + k + u) : 0.f;
+            }
+        }
     }
     if (active) {
         // row_ptr[x0 .. x0 + nrow]: nrow + 1 <= D + 2 values
@@ -231,7 +255,7 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     }
     __syncthreads();
     // rows of the run's entries and scores in log2 units
-    int ri[RMAX];
+    int ri[RMAX] = {};  // zero past the run's R entries: the result loop reads (and drops) up to 3 more
     {
         int cur = (kn > 0) ? sm_row_search(rp, 0, nrow - 1, lo + k0) : 0;
 #pragma unroll
@@ -334,13 +358,24 @@ __global__ __launch_bounds__(CSR_BLOCK) void k_softmax_run(SoftmaxArgs a)
     const int ks = max(0, ya - lo - k0), ke = min(kn, yb - lo - k0);
     float* prun = a.probs + lo + k0;
 #pragma unroll
-    for (int k = 0; k < RMAX; ++k) {
+    for (int k = 0; k < RMAX; k += 4) {
         if (k >= R) break;
-        if (k >= ks && k < ke) {
+        // the run's results, four at a time (k + u may pass R: those are never stored)
+        float p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
             if constexpr (BWD)
-                prun[k] = a.scale * t[k] * (g[k] - sl[ri[k]]);
+                p[u] = a.scale * t[k + u] * (g[k + u] - sl[ri[k + u]]);
             else
-                prun[k] = __builtin_amdgcn_exp2f(t[k] - __int_as_float(rp[ri[k]])) * __builtin_amdgcn_rcpf(sl[ri[k]]);
+                p[u] = __builtin_amdgcn_exp2f(t[k + u] - __int_as_float(rp[ri[k + u]])) *
+                       __builtin_amdgcn_rcpf(sl[ri[k + u]]);
+        }
+        if (k >= ks && k + 4 <= ke) {
+            *reinterpret_cast<sm_f32x4*>(prun + k) = sm_f32x4{p[0], p[1], p[2], p[3]};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (k + u >= ks && k + u < ke) prun[k + u] = p[u];
         }
     }
 }
